@@ -1,0 +1,270 @@
+"""Model-level pins of the oracle (CPU only).
+
+* HuggingFace's Qwen3 decoder (float64, full causal recompute, no cache) is an
+  independent implementation of the block the oracle reads the pages as
+  describing; the tiny F32 model must agree with it to rounding.
+* The equalities the pages assert for this loop hold bitwise in the oracle:
+  K/V-cached decode == full recompute (qwentts.cpp pipeline-tts.h log, per-layer
+  K/V ring entry: identical output against the pre-cache run), batched ==
+  per-stream (MiniCPM-o optimizations.md, core table, batched Token2Wav row),
+  and the predictor cache reset makes stale rows irrelevant.
+* Q8 blocks == the same weights dequantised by the closed form w = d * q.
+"""
+import dataclasses
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from autoregressive_codebook_tts_frame_amd import synth
+from oracle import Oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f64(m, a):
+    """A stored table / weight as float64 (exact)."""
+    if isinstance(a, tuple):
+        q, d = a
+        return (d.view(np.float16).astype(np.float64).repeat(32, axis=1) * q.astype(np.float64))
+    if a.dtype == np.uint16:
+        return synth.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _hf_stack(m, layers, norm, nlayers, head=None):
+    from transformers import Qwen3Config, Qwen3ForCausalLM
+    cfg = Qwen3Config(vocab_size=m.Vc, hidden_size=m.H, intermediate_size=m.F,
+                      num_hidden_layers=nlayers, num_attention_heads=m.nq,
+                      num_key_value_heads=m.nkv, head_dim=m.hd, rms_norm_eps=m.eps,
+                      max_position_embeddings=m.P, tie_word_embeddings=False,
+                      attention_bias=False,
+                      rope_parameters={"rope_theta": m.theta, "rope_type": "default"})
+    cfg._attn_implementation = "eager"
+    model = Qwen3ForCausalLM(cfg).double().eval()
+    sd = {}
+    for i, L in enumerate(layers):
+        p = f"model.layers.{i}."
+        for ours, theirs in (("wq", "self_attn.q_proj"), ("wk", "self_attn.k_proj"),
+                             ("wv", "self_attn.v_proj"), ("wo", "self_attn.o_proj"),
+                             ("wg", "mlp.gate_proj"), ("wu", "mlp.up_proj"),
+                             ("wd", "mlp.down_proj")):
+            sd[p + theirs + ".weight"] = torch.tensor(_f64(m, L[ours]))
+        sd[p + "self_attn.q_norm.weight"] = torch.tensor(_f64(m, L["q_norm"]))
+        sd[p + "self_attn.k_norm.weight"] = torch.tensor(_f64(m, L["k_norm"]))
+        sd[p + "input_layernorm.weight"] = torch.tensor(_f64(m, L["attn_norm"]))
+        sd[p + "post_attention_layernorm.weight"] = torch.tensor(_f64(m, L["mlp_norm"]))
+    sd["model.norm.weight"] = torch.tensor(_f64(m, norm))
+    if head is not None:
+        sd["lm_head.weight"] = torch.tensor(_f64(m, head))
+    missing = model.load_state_dict(sd, strict=False)
+    assert all("embed_tokens" in k or (head is None and "lm_head" in k) for k in missing.missing_keys)
+    return model
+
+
+def _hf_hidden(model, rows):
+    with torch.no_grad():
+        out = model.model(inputs_embeds=torch.tensor(rows)[None], use_cache=False)
+    return out.last_hidden_state[0].numpy()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _rows(m, w, codes, text):
+    """Talker input rows sum_g E_g[codes[:, g]] + Tx[text] in float64."""
+    E = _f64(m, w["code_emb"])
+    Tx = _f64(m, w["text_emb"])
+    x = Tx[text].copy()
+    for g in range(m.G):
+        x += E[g][codes[:, g]]
+    return x
+
+
+def _run_tiny(m, w, nframes=8):
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_f32_b1"], model=m)
+    o = Oracle(m, w, 1)
+    codes, text = synth.make_prompt(wl, 0)
+    pre = o.prefill(0, codes, text, dump=True)
+    st = o.get_state(0)
+    ov = synth.make_overlays(wl, nframes)
+    out = o.decode(nframes, ov, dump=True)
+    return o, codes, text, ov, pre, st, out
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    m = synth.TINY
+    w = synth.make_weights(m)
+    return (m, w) + _run_tiny(m, w)
+
+
+def test_talker_matches_hf_qwen3(tiny):
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    n = ov.shape[0]
+    T = text.shape[0]
+    seq_codes = np.concatenate([codes, out["codes"][:, 0, :]], 0)
+    seq_text = np.concatenate([text, ov[:, 0]], 0)
+    rows = _rows(m, w, seq_codes, seq_text)
+    hf = _hf_stack(m, w["talker"], w["t_norm"], m.Lt, w["t_head"])
+    hid = _hf_hidden(hf, rows)
+    logits = hid @ _f64(m, w["t_head"]).T
+    assert rel_l2(st[2], hid[T - 1]) < 1e-5
+    assert rel_l2(pre["logits"], logits[T - 1]) < 1e-5
+    for f in range(n):
+        assert rel_l2(out["bridge"][f, 0], hid[T + f]) < 1e-5
+        assert rel_l2(out["talker_logits"][f, 0], logits[T + f]) < 1e-5
+        # code 0 of frame f is the argmax of the talker row before it
+        assert out["codes"][f, 0, 0] == int(np.argmax(logits[T - 1 + f]))
+
+
+def test_predictor_matches_hf_qwen3(tiny):
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    E = _f64(m, w["code_emb"])
+    hf = _hf_stack(m, w["predictor"], w["p_norm"], m.Lp)
+    heads = [_f64(m, h) for h in w["p_heads"]]
+    for f in range(ov.shape[0]):
+        bridge = st[2] if f == 0 else out["bridge"][f - 1, 0]
+        c = out["codes"][f, 0]
+        rows = [bridge.astype(np.float64)] + [E[j][c[j]] for j in range(m.G - 1)]
+        hid = _hf_hidden(hf, np.stack(rows))
+        for j in range(m.G - 1):
+            ref = heads[j] @ hid[j + 1]
+            assert rel_l2(out["pred_logits"][f, 0, j], ref) < 1e-5
+            assert c[j + 1] == int(np.argmax(ref))
+
+
+def test_bf16_model_tracks_float64_reference():
+    """The BF16 storage/rounding policy only perturbs values by bf16 rounding."""
+    m = dataclasses.replace(synth.TINY, model_id=10, lin=synth.LIN_BF16, tab_bf16=True,
+                            kv_bf16=True, act_bf16=True)
+    w = synth.make_weights(m)
+    o, codes, text, ov, pre, st, out = _run_tiny(m, w, nframes=2)
+    T = text.shape[0]
+    forced_rows = _rows(m, w, np.concatenate([codes, out["codes"][:, 0, :]], 0),
+                        np.concatenate([text, ov[:, 0]], 0))
+    hf = _hf_stack(m, w["talker"], w["t_norm"], m.Lt, w["t_head"])
+    hid = _hf_hidden(hf, forced_rows)
+    logits = hid @ _f64(m, w["t_head"]).T
+    for f in range(2):
+        e = rel_l2(out["talker_logits"][f, 0], logits[T + f])
+        assert 1e-5 < e < 3e-2, e  # rounded (so not F32-exact) but close
+
+
+def test_cached_decode_equals_full_recompute_bitwise():
+    for m in (synth.TINY,
+              dataclasses.replace(synth.TINY, model_id=10, lin=synth.LIN_BF16, tab_bf16=True,
+                                  kv_bf16=True, act_bf16=True)):
+        w = synth.make_weights(m)
+        o, codes, text, ov, pre, st, out = _run_tiny(m, w, nframes=5)
+        for n in (1, 3, 5):
+            r = Oracle(m, w, 1)
+            r.prefill(0, np.concatenate([codes, out["codes"][:n, 0, :]], 0),
+                      np.concatenate([text, ov[:n, 0]], 0))
+            pos, c0, br = r.get_state(0)
+            assert pos == text.shape[0] + n
+            assert np.array_equal(br.view(np.uint32), out["bridge"][n - 1, 0].view(np.uint32))
+            if n < 5:
+                assert c0 == out["codes"][n, 0, 0]
+
+
+def test_predictor_cached_equals_recompute_bitwise(tiny):
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    E = w["code_emb"]
+    r = Oracle(m, w, 1)
+    for f in (0, 3):
+        bridge = st[2] if f == 0 else out["bridge"][f - 1, 0]
+        c = out["codes"][f, 0]
+        rows = np.stack([bridge] + [E[j][c[j]].astype(np.float32) for j in range(m.G - 1)])
+        lg = r.predictor_recompute(rows)
+        assert np.array_equal(lg.view(np.uint32), out["pred_logits"][f, 0].view(np.uint32))
+
+
+def test_batched_equals_per_stream_bitwise():
+    m = synth.TINY
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_f32_b1"], batch=3)
+    ob = Oracle(m, w, 3)
+    prompts = [synth.make_prompt(wl, b, T=10 + 3 * b) for b in range(3)]
+    for b, (c, t) in enumerate(prompts):
+        ob.prefill(b, c, t)
+    ov = synth.make_overlays(wl, 4)
+    outb = ob.decode(4, ov, dump=True)
+    for b, (c, t) in enumerate(prompts):
+        o1 = Oracle(m, w, 1)
+        o1.prefill(0, c, t)
+        out1 = o1.decode(4, ov[:, b:b + 1], dump=True)
+        assert np.array_equal(out1["codes"][:, 0], outb["codes"][:, b])
+        for k in ("talker_logits", "pred_logits", "bridge"):
+            assert np.array_equal(out1[k][:, 0].view(np.uint32), outb[k][:, b].view(np.uint32))
+
+
+def test_predictor_reset_ignores_poisoned_cache(tiny):
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    r = Oracle(m, w, 1)
+    r.prefill(0, codes, text)
+    res = []
+    for f in range(3):
+        r.poison_predictor(float("nan"))
+        res.append(r.decode(1, ov[f:f + 1], dump=True))
+    for f in range(3):
+        assert np.array_equal(res[f]["codes"][0], out["codes"][f])
+        assert np.array_equal(res[f]["pred_logits"][0].view(np.uint32),
+                              out["pred_logits"][f].view(np.uint32))
+
+
+def test_teacher_forcing_with_own_codes_is_free_run(tiny):
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    r = Oracle(m, w, 1)
+    r.prefill(0, codes, text)
+    forced = out["codes"].copy()
+    res = r.decode(ov.shape[0], ov, forced=forced, dump=True)
+    assert np.array_equal(res["codes"], out["codes"])
+    assert np.array_equal(res["talker_logits"].view(np.uint32), out["talker_logits"].view(np.uint32))
+
+
+def test_q8_equals_dequantised_weights_bitwise():
+    base = dataclasses.replace(synth.TINY, model_id=11, lin=synth.LIN_Q8, tab_bf16=True,
+                               kv_bf16=True, act_bf16=True)
+    wq = synth.make_weights(base, random_q8_scales=True)
+    deq = dataclasses.replace(base, lin=synth.LIN_F32)
+
+    def dq(a):
+        return _f64(base, a).astype(np.float32) if isinstance(a, tuple) else a
+
+    wd = {k: v for k, v in wq.items()}
+    wd["t_head"] = dq(wq["t_head"])
+    wd["p_heads"] = [dq(h) for h in wq["p_heads"]]
+    for stack in ("talker", "predictor"):
+        wd[stack] = [{k: dq(v) for k, v in L.items()} for L in wq[stack]]
+    _, _, _, _, _, _, a = _run_tiny(base, wq, nframes=3)
+    _, _, _, _, _, _, b = _run_tiny(deq, wd, nframes=3)
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["talker_logits"].view(np.uint32), b["talker_logits"].view(np.uint32))
+
+
+def test_gather_sum_is_exact_sum_rounded(tiny):
+    """x0 = fl(sum of the 16 code rows + overlay row), checked with fsum."""
+    import math
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    E, Tx = w["code_emb"], w["text_emb"]
+    for f in range(2):
+        g = out["gather"][f, 0]
+        assert np.array_equal(g[:m.G], out["codes"][f, 0]) and g[m.G] == ov[f, 0]
+        for i in range(0, m.H, 37):
+            terms = [float(E[j][g[j]][i]) for j in range(m.G)] + [float(Tx[g[m.G]][i])]
+            assert out["x0"][f, 0, i] == np.float32(math.fsum(terms))
+    assert np.array_equal(out["tpos"][:, 0], text.shape[0] + np.arange(ov.shape[0]))
+
+
+def test_frame_schedule_golden(tiny):
+    m, w, o, codes, text, ov, pre, st, out = tiny
+    g = json.load(open(os.path.join(GOLDEN, "frame_schedule.json")))
+    assert out["codes"].shape[2] == g["codes_per_frame"] == m.G
+    assert out["pred_logits"].shape[2] == g["predictor_prefill_rows"] - 1 + g["predictor_decodes"]
+    assert m.Q == g["predictor_cache_positions"]
