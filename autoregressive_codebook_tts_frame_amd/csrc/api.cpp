@@ -1,0 +1,666 @@
+// api.cpp -- host side of libqt: validation, arena layout, frame schedule,
+// hipGraph capture/replay and the C entry points declared in include/qt.h.
+//
+// Sources (page title, section):
+//   [QT-log]   qwentts.cpp, commit log of src/pipeline-tts.h
+//   [QT-tests] qwentts.cpp, commit log of the tests branch
+//   [MC-opt]   MiniCPM-o 4.5 single-GPU engine, docs/optimizations.md
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/qt.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int kPrefillChunk = 32;  // prompt rows per prefill step
+constexpr int kTile = 256;         // talker attention tile (window padding unit)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets of every arena buffer; a pure function of the shapes.
+struct Layout {
+  size_t rope_cos, rope_sin, pos, c0, bridge, ctl, overlay, cin, cout;
+  size_t x, qkv, q, part, o, z, logits_t, logits_p;
+  size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
+  size_t total;
+  int32_t rows;       // activation rows held
+  int32_t max_tiles;  // talker attention tiles
+};
+
+struct Dims {
+  int32_t H, nq, nkv, hd, F, Lt, Lp, G, Vc, Vt, P, Q, qd, kd, nqkv;
+};
+
+Dims dims_of(const qt_model_desc &m) {
+  Dims d;
+  d.H = m.hidden; d.nq = m.n_q_heads; d.nkv = m.n_kv_heads; d.hd = m.head_dim; d.F = m.ffn;
+  d.Lt = m.talker_layers; d.Lp = m.predictor_layers; d.G = m.codebooks; d.Vc = m.codebook_size;
+  d.Vt = m.text_rows; d.P = m.talker_positions; d.Q = m.predictor_positions;
+  d.qd = d.nq * d.hd; d.kd = d.nkv * d.hd; d.nqkv = d.qd + 2 * d.kd;
+  return d;
+}
+
+Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.rows = 2 * B > kPrefillChunk ? 2 * B : kPrefillChunk;
+  L.max_tiles = d.P / kTile;
+  const size_t R = (size_t)L.rows;
+  L.rope_cos = take(sizeof(float) * d.P * (d.hd / 2));
+  L.rope_sin = take(sizeof(float) * d.P * (d.hd / 2));
+  L.pos = take(sizeof(int32_t) * B);
+  L.c0 = take(sizeof(int32_t) * B);
+  L.bridge = take(sizeof(float) * B * d.H);
+  L.ctl = take(64);
+  L.overlay = take(sizeof(int32_t) * (size_t)maxF * B);
+  L.cin = take(sizeof(int32_t) * (size_t)maxF * B * d.G);
+  L.cout = take(sizeof(int32_t) * (size_t)maxF * B * d.G);
+  L.x = take(sizeof(float) * R * d.H);
+  L.qkv = take(sizeof(float) * R * d.nqkv);
+  L.q = take(sizeof(float) * R * d.qd);
+  L.part = take(sizeof(float) * R * d.nq * L.max_tiles * (d.hd + 2));
+  L.o = take(sizeof(float) * R * d.qd);
+  L.z = take(sizeof(float) * R * d.F);
+  L.logits_t = take(sizeof(float) * (R > (size_t)B ? R : B) * d.Vc);
+  L.logits_p = take(sizeof(float) * (size_t)(d.G - 1) * B * d.Vc);
+  L.x0_dump = take(sizeof(float) * B * d.H);
+  L.hidden_dump = take(sizeof(float) * (size_t)d.Lt * B * d.H);
+  L.gather_dump = take(sizeof(int32_t) * B * (d.G + 1));
+  L.tpos_dump = take(sizeof(int32_t) * B);
+  L.pf_codes = take(sizeof(int32_t) * (size_t)d.P * d.G);
+  L.pf_text = take(sizeof(int32_t) * (size_t)d.P);
+  L.total = off;
+  return L;
+}
+
+size_t kv_elem(const qt_model_desc &m) { return m.kv_bf16 ? 2 : 4; }
+
+size_t talker_ring_elems(const Dims &d, int32_t B) {
+  return (size_t)B * d.Lt * 2 * d.kd * d.P;
+}
+size_t pred_ring_elems(const Dims &d, int32_t B) { return (size_t)B * d.Lp * 2 * d.kd * d.Q; }
+
+// Shapes the kernels implement; message on failure.
+const char *unsupported(const qt_model_desc &m) {
+  const Dims d = dims_of(m);
+  if (d.H <= 0 || d.nq <= 0 || d.nkv <= 0 || d.F <= 0 || d.Lt <= 0 || d.Lp <= 0 || d.Vc <= 0 ||
+      d.Vt <= 0)
+    return "non-positive model dimension";
+  if (d.hd != 64 && d.hd != 128) return "head_dim must be 64 or 128";
+  if (d.nq % d.nkv) return "n_kv_heads must divide n_q_heads";
+  const int gq = d.nq / d.nkv;
+  if (!(gq == 1 || gq == 2 || gq == 4) || gq * d.hd > 256) return "GQA group x head_dim must be <= 256 (group 1, 2 or 4)";
+  if (d.G < 2 || d.G > 256) return "codebooks must be in [2, 256]";
+  if (d.Q != d.G) return "predictor_positions must equal codebooks";
+  if (d.P < kTile || d.P % kTile) return "talker_positions must be a positive multiple of 256";
+  if (d.Q > d.P) return "predictor_positions exceeds talker_positions";
+  if (m.lin_type < QT_LIN_F32 || m.lin_type > QT_LIN_Q8) return "unknown lin_type";
+  const int ch = m.lin_type == QT_LIN_F32 ? 4 : (m.lin_type == QT_LIN_BF16 ? 8 : 32);
+  if (d.H % ch || d.F % ch || d.qd % ch) return "hidden, ffn and n_q_heads*head_dim must be multiples of the weight chunk (4 f32, 8 bf16, 32 q8)";
+  if (m.eps <= 0 || m.rope_theta <= 0) return "eps and rope_theta must be positive";
+  return nullptr;
+}
+
+}  // namespace
+
+struct qt_ctx {
+  qt_model_desc md;
+  Dims d;
+  Layout L;
+  int32_t B, K, maxF;
+  uint32_t flags;
+  hipStream_t stream;
+  // weights (device pointers)
+  const void *code_emb, *text_emb, *t_norm, *p_norm;
+  qt_linear t_head;
+  std::vector<qt_linear> p_heads;
+  std::vector<qt_layer_weights> tl, pl;
+  // device memory
+  uint8_t *ring, *arena;
+  // host mirrors and staging
+  std::vector<int32_t> pos_host;
+  std::vector<uint8_t> ready;
+  // pinned staging (int32 elements): every async copy source has its own
+  // region, so no host write can race a copy still in flight
+  int32_t *pin_up = nullptr, *pin_down = nullptr;
+  size_t pin_up_elems = 0, pin_down_elems = 0;
+  size_t pu_ctl = 0, pu_overlay = 0, pu_forced = 0, pu_pf_text = 0, pu_pf_codes = 0, pu_scalar = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  std::string err;
+
+  template <class T> T *A(size_t off) const { return (T *)(arena + off); }
+};
+
+namespace {
+
+int32_t fail(qt_ctx *c, int32_t code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(ctx, expr)                                                              \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(ctx, QT_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+using namespace qtk;
+
+int wtype_of(const qt_model_desc &m) {
+  return m.lin_type == QT_LIN_F32 ? W_F32 : (m.lin_type == QT_LIN_BF16 ? W_BF16 : W_Q8);
+}
+
+Lin lin(const qt_linear &l) { return Lin{l.w, (const uint16_t *)l.scales}; }
+
+// ----------------------------------------------------------------- schedule
+
+struct Stack {
+  const std::vector<qt_layer_weights> *layers;
+  uint8_t *ring;          // (slot 0, layer 0, K) element base
+  int64_t slot_stride;    // elements
+  int64_t layer_stride;
+  int64_t kv_stride;
+  int32_t P;              // positions per head
+  int32_t tile, max_tiles;
+};
+
+Stack talker_stack(const qt_ctx *c) {
+  const Dims &d = c->d;
+  Stack s;
+  s.layers = &c->tl;
+  s.ring = c->ring;
+  s.kv_stride = (int64_t)d.kd * d.P;
+  s.layer_stride = 2 * s.kv_stride;
+  s.slot_stride = s.layer_stride * d.Lt;
+  s.P = d.P;
+  s.tile = kTile;
+  s.max_tiles = c->L.max_tiles;
+  return s;
+}
+
+Stack pred_stack(const qt_ctx *c) {
+  const Dims &d = c->d;
+  Stack s;
+  s.layers = &c->pl;
+  s.ring = c->ring + talker_ring_elems(d, c->B) * kv_elem(c->md);
+  s.kv_stride = (int64_t)d.kd * d.Q;
+  s.layer_stride = 2 * s.kv_stride;
+  s.slot_stride = s.layer_stride * d.Lp;
+  s.P = d.Q;
+  s.tile = d.Q;
+  s.max_tiles = 1;
+  return s;
+}
+
+// One decoder layer over M rows (x in the arena's activation rows).
+hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap &rows,
+                         float *hidden_copy) {
+  const Dims &d = c->d;
+  const qt_model_desc &md = c->md;
+  const qt_layer_weights &w = (*st.layers)[l];
+  const int wt = wtype_of(md);
+  hipStream_t s = c->stream;
+  float *x = c->A<float>(c->L.x);
+  float *qkv = c->A<float>(c->L.qkv);
+  float *q = c->A<float>(c->L.q);
+  float *o = c->A<float>(c->L.o);
+  float *z = c->A<float>(c->L.z);
+  uint8_t *ring_layer = st.ring + (size_t)l * st.layer_stride * kv_elem(md);
+  hipError_t e;
+
+  GemvArgs g = {};
+  g.act_bf16 = md.act_bf16;
+  g.gain_bf16 = md.tab_bf16;
+  g.eps = (float)md.eps;
+
+  // 1. QKV with the attention RMSNorm prologue
+  g.seg[0] = lin(w.wq); g.seg[1] = lin(w.wk); g.seg[2] = lin(w.wv);
+  g.seg_end[0] = d.qd; g.seg_end[1] = d.qd + d.kd; g.seg_end[2] = d.nqkv;
+  g.nseg = 3;
+  g.N = d.nqkv; g.K = d.H;
+  g.x = x; g.x_stride = d.H; g.M = M;
+  g.gain = w.attn_norm;
+  g.y = qkv; g.y_stride = d.nqkv;
+  if ((e = launch_gemv(wt, EPI_STORE, g, s)) != hipSuccess) return e;
+
+  // 2. q/k norm + RoPE + K/V rows into the ring at the row's position
+  QkArgs qa = {};
+  qa.qkv = qkv; qa.M = M; qa.rows = rows; qa.nq = d.nq; qa.nkv = d.nkv;
+  qa.q_gain = w.q_norm; qa.k_gain = w.k_norm; qa.gain_bf16 = md.tab_bf16; qa.eps = (float)md.eps;
+  qa.rope_cos = c->A<float>(c->L.rope_cos); qa.rope_sin = c->A<float>(c->L.rope_sin);
+  qa.q_out = q; qa.ring_layer = ring_layer; qa.slot_stride = st.slot_stride;
+  qa.kv_stride = st.kv_stride; qa.P = st.P;
+  if ((e = launch_qk_rope_kv(d.hd, md.kv_bf16, qa, s)) != hipSuccess) return e;
+
+  // 3. attention over the (padded) window
+  AttnArgs aa = {};
+  aa.q = q; aa.M = M; aa.rows = rows; aa.nq = d.nq; aa.nkv = d.nkv;
+  aa.ring_layer = ring_layer; aa.slot_stride = st.slot_stride; aa.kv_stride = st.kv_stride;
+  aa.P = st.P; aa.tile = st.tile; aa.max_tiles = st.max_tiles;
+  aa.scale = (float)(1.0 / sqrt((double)d.hd));
+  aa.o = o; aa.part = c->A<float>(c->L.part);
+  if ((e = launch_attention(d.hd, md.kv_bf16, aa, st.max_tiles > 1, s)) != hipSuccess) return e;
+
+  // 4. O projection, residual added in the epilogue
+  GemvArgs go = g;
+  go.seg[0] = lin(w.wo); go.nseg = 1; go.seg_end[0] = d.H;
+  go.N = d.H; go.K = d.qd; go.x = o; go.x_stride = d.qd; go.gain = nullptr;
+  go.y = x; go.y_stride = d.H;
+  if ((e = launch_gemv(wt, EPI_RESID, go, s)) != hipSuccess) return e;
+
+  // 5. gate/up with the MLP RMSNorm prologue, SiLU-multiply epilogue
+  GemvArgs gu = g;
+  gu.seg[0] = lin(w.wg); gu.up = lin(w.wu); gu.nseg = 1; gu.seg_end[0] = d.F;
+  gu.N = d.F; gu.K = d.H; gu.x = x; gu.x_stride = d.H; gu.gain = w.mlp_norm;
+  gu.y = z; gu.y_stride = d.F;
+  if ((e = launch_gemv(wt, EPI_GATED, gu, s)) != hipSuccess) return e;
+
+  // 6. down projection, residual added in the epilogue
+  GemvArgs gd = g;
+  gd.seg[0] = lin(w.wd); gd.nseg = 1; gd.seg_end[0] = d.H;
+  gd.N = d.H; gd.K = d.F; gd.x = z; gd.x_stride = d.F; gd.gain = nullptr;
+  gd.y = x; gd.y_stride = d.H;
+  gd.copy_out = hidden_copy; gd.copy_stride = d.H;
+  return launch_gemv(wt, EPI_RESID, gd, s);
+}
+
+// Frame k of a replay: predictor (codes 1..G-1) then the talker step.
+hipError_t enqueue_frame(qt_ctx *c, int k) {
+  const Dims &d = c->d;
+  const qt_model_desc &md = c->md;
+  const int B = c->B;
+  const int wt = wtype_of(md);
+  const bool dump = c->flags & QT_F_DUMP;
+  hipStream_t s = c->stream;
+  float *x = c->A<float>(c->L.x);
+  int32_t *ctl = c->A<int32_t>(c->L.ctl);
+  hipError_t e;
+
+  // predictor prefill rows [bridge, E_0[c0]] ([QT-log] set_rows / bridge entry)
+  PredInArgs pa = {};
+  pa.bridge = c->A<float>(c->L.bridge); pa.code_emb = c->code_emb; pa.tab_bf16 = md.tab_bf16;
+  pa.H = d.H; pa.G = d.G; pa.B = B; pa.c0_state = c->A<int32_t>(c->L.c0); pa.ctl = ctl; pa.k = k;
+  pa.cin = c->A<int32_t>(c->L.cin); pa.cout = c->A<int32_t>(c->L.cout); pa.x = x;
+  if ((e = launch_pred_input(pa, s)) != hipSuccess) return e;
+
+  const Stack ps = pred_stack(c);
+  for (int j = 0; j < d.G - 1; ++j) {
+    // j == 0: two rows per stream at positions 0, 1; else one row at j + 1
+    // ([QT-log] per-layer K/V ring entry: T=2 prefill then single-row decodes)
+    const int M = j == 0 ? 2 * B : B;
+    const RowMap rows = j == 0 ? RowMap{0, 2, 0, nullptr} : RowMap{0, 1, j + 1, nullptr};
+    for (int l = 0; l < d.Lp; ++l)
+      if ((e = enqueue_layer(c, ps, l, M, rows, nullptr)) != hipSuccess) return e;
+    GemvArgs h = {};
+    h.seg[0] = lin(c->p_heads[j]); h.nseg = 1; h.seg_end[0] = d.Vc;
+    h.N = d.Vc; h.K = d.H;
+    h.x = j == 0 ? x + d.H : x; h.x_stride = j == 0 ? 2 * d.H : d.H; h.M = B;
+    h.gain = c->p_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
+    float *lg = c->A<float>(c->L.logits_p) + (size_t)j * B * d.Vc;
+    h.y = lg; h.y_stride = d.Vc;
+    if ((e = launch_gemv(wt, EPI_STORE, h, s)) != hipSuccess) return e;
+    ArgmaxArgs am = {};
+    am.logits = lg; am.Vc = d.Vc; am.M = B; am.mode = AM_PRED; am.j = j; am.ctl = ctl; am.k = k;
+    am.B = B; am.G = d.G; am.cin = pa.cin; am.cout = pa.cout; am.code_emb = c->code_emb;
+    am.tab_bf16 = md.tab_bf16; am.H = d.H; am.x_next = x;
+    if ((e = launch_argmax(am, s)) != hipSuccess) return e;
+  }
+
+  // talker step: gather-sum of the frame's codes + overlay ([QT-log] AR inputs entry)
+  GatherArgs ga = {};
+  ga.code_emb = c->code_emb; ga.text_emb = c->text_emb; ga.tab_bf16 = md.tab_bf16;
+  ga.H = d.H; ga.Vc = d.Vc; ga.G = d.G;
+  ga.codes = c->A<int32_t>(c->L.cin) + (size_t)k * B * d.G; ga.codes_stride = d.G;
+  ga.text = c->A<int32_t>(c->L.overlay) + (size_t)k * B; ga.text_stride = 1;
+  ga.ctl = ctl; ga.frame_stride_codes = B * d.G; ga.frame_stride_text = B;
+  ga.x = x; ga.M = B;
+  ga.x0_dump = dump ? c->A<float>(c->L.x0_dump) : nullptr;
+  ga.gather_dump = dump ? c->A<int32_t>(c->L.gather_dump) : nullptr;
+  if ((e = launch_gather(ga, s)) != hipSuccess) return e;
+
+  const Stack ts = talker_stack(c);
+  const RowMap trows{0, 1, 0, c->A<int32_t>(c->L.pos)};
+  for (int l = 0; l < d.Lt; ++l) {
+    float *hc = dump ? c->A<float>(c->L.hidden_dump) + (size_t)l * B * d.H : nullptr;
+    if ((e = enqueue_layer(c, ts, l, B, trows, hc)) != hipSuccess) return e;
+  }
+  // final norm -> bridge (kept on device), head, argmax -> next c0, pos += 1
+  GemvArgs h = {};
+  h.seg[0] = lin(c->t_head); h.nseg = 1; h.seg_end[0] = d.Vc;
+  h.N = d.Vc; h.K = d.H; h.x = x; h.x_stride = d.H; h.M = B;
+  h.gain = c->t_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
+  h.normed_out = c->A<float>(c->L.bridge);
+  h.y = c->A<float>(c->L.logits_t); h.y_stride = d.Vc;
+  if ((e = launch_gemv(wt, EPI_STORE, h, s)) != hipSuccess) return e;
+  ArgmaxArgs am = {};
+  am.logits = h.y; am.Vc = d.Vc; am.M = B; am.mode = AM_TALKER; am.ctl = ctl; am.k = k;
+  am.B = B; am.G = d.G; am.c0_state = c->A<int32_t>(c->L.c0); am.pos = c->A<int32_t>(c->L.pos);
+  am.tpos_dump = dump ? c->A<int32_t>(c->L.tpos_dump) : nullptr;
+  return launch_argmax(am, s);
+}
+
+hipError_t enqueue_replay(qt_ctx *c) {
+  hipError_t e;
+  for (int k = 0; k < c->K; ++k)
+    if ((e = enqueue_frame(c, k)) != hipSuccess) return e;
+  return launch_advance(c->A<int32_t>(c->L.ctl), c->K, c->stream);
+}
+
+bool ids_ok(const int32_t *p, size_t n, int32_t hi) {
+  for (size_t i = 0; i < n; ++i)
+    if (p[i] < 0 || p[i] >= hi) return false;
+  return true;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- C ABI
+
+extern "C" {
+
+int32_t qt_abi_version(void) { return QT_ABI_VERSION; }
+
+const char *qt_last_error(const qt_ctx *ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t frames_per_replay,
+                       int32_t max_frames_per_call, uint32_t flags, size_t *ring_bytes,
+                       size_t *arena_bytes) {
+  if (!model || !ring_bytes || !arena_bytes) return fail(nullptr, QT_E_ARG, "NULL argument");
+  if (max_batch <= 0 || frames_per_replay <= 0 || max_frames_per_call <= 0)
+    return fail(nullptr, QT_E_ARG, "max_batch, frames_per_replay and max_frames_per_call must be positive");
+  if (max_frames_per_call % frames_per_replay)
+    return fail(nullptr, QT_E_ARG, "max_frames_per_call must be a multiple of frames_per_replay");
+  if (flags & ~(QT_F_DUMP | QT_F_EAGER)) return fail(nullptr, QT_E_ARG, "unknown flags");
+  if (const char *why = unsupported(*model)) return fail(nullptr, QT_E_UNSUPPORTED, "%s", why);
+  const Dims d = dims_of(*model);
+  *ring_bytes = (talker_ring_elems(d, max_batch) + pred_ring_elems(d, max_batch)) * kv_elem(*model);
+  *arena_bytes = layout_of(d, max_batch, max_frames_per_call).total;
+  return QT_OK;
+}
+
+void qt_free(qt_ctx *c) {
+  if (!c) return;
+  if (c->exec) (void)hipGraphExecDestroy(c->exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->pin_up) (void)hipHostFree(c->pin_up);
+  if (c->pin_down) (void)hipHostFree(c->pin_down);
+  delete c;
+}
+
+int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
+  if (!p || !out) return fail(nullptr, QT_E_ARG, "NULL argument");
+  if (p->abi_version < QT_ABI_MIN_VERSION || p->abi_version > QT_ABI_VERSION)
+    return fail(nullptr, QT_E_ABI, "abi_version %u outside [%d, %d]", p->abi_version,
+                QT_ABI_MIN_VERSION, QT_ABI_VERSION);
+  if (p->struct_size != sizeof(qt_init_params))
+    return fail(nullptr, QT_E_ARG, "struct_size %u != %zu", p->struct_size, sizeof(qt_init_params));
+  size_t ring_need, arena_need;
+  int32_t rc = qt_query_sizes(&p->model, p->max_batch, p->frames_per_replay,
+                              p->max_frames_per_call, p->flags, &ring_need, &arena_need);
+  if (rc != QT_OK) return rc;
+  const qt_model_desc &m = p->model;
+  const Dims d = dims_of(m);
+  const qt_weights &w = p->weights;
+  if (!p->ring || !p->arena) return fail(nullptr, QT_E_ARG, "NULL ring or arena");
+  if (((uintptr_t)p->ring | (uintptr_t)p->arena) % kAlign)
+    return fail(nullptr, QT_E_ARG, "ring and arena must be 256-byte aligned");
+  if (p->ring_bytes < ring_need || p->arena_bytes < arena_need)
+    return fail(nullptr, QT_E_SIZE, "ring %zu < %zu or arena %zu < %zu bytes", p->ring_bytes,
+                ring_need, p->arena_bytes, arena_need);
+  if (!p->stream && !(p->flags & QT_F_EAGER))
+    return fail(nullptr, QT_E_ARG, "graph replay needs a non-default stream (or QT_F_EAGER)");
+  if (!w.code_emb || !w.text_emb || !w.talker || !w.talker_norm || !w.talker_head.w ||
+      !w.predictor || !w.predictor_norm || !w.predictor_heads)
+    return fail(nullptr, QT_E_ARG, "NULL weight pointer");
+  const bool q8 = m.lin_type == QT_LIN_Q8;
+  auto lin_ok = [&](const qt_linear &l) {
+    if (!l.w || (q8 && !l.scales)) return false;
+    if ((uintptr_t)l.w % 16) return false;  // 128-bit loads
+    return true;
+  };
+  auto layer_ok = [&](const qt_layer_weights &L) {
+    return L.attn_norm && L.q_norm && L.k_norm && L.mlp_norm && lin_ok(L.wq) && lin_ok(L.wk) &&
+           lin_ok(L.wv) && lin_ok(L.wo) && lin_ok(L.wg) && lin_ok(L.wu) && lin_ok(L.wd);
+  };
+  for (int l = 0; l < d.Lt; ++l)
+    if (!layer_ok(w.talker[l])) return fail(nullptr, QT_E_ARG, "talker layer %d: NULL or unaligned weight", l);
+  for (int l = 0; l < d.Lp; ++l)
+    if (!layer_ok(w.predictor[l])) return fail(nullptr, QT_E_ARG, "predictor layer %d: NULL or unaligned weight", l);
+  if (!lin_ok(w.talker_head)) return fail(nullptr, QT_E_ARG, "talker head: NULL or unaligned");
+  for (int j = 0; j < d.G - 1; ++j)
+    if (!lin_ok(w.predictor_heads[j])) return fail(nullptr, QT_E_ARG, "predictor head %d: NULL or unaligned", j);
+
+  qt_ctx *c = new qt_ctx();
+  c->md = m;
+  c->d = d;
+  c->B = p->max_batch;
+  c->K = p->frames_per_replay;
+  c->maxF = p->max_frames_per_call;
+  c->flags = p->flags;
+  c->stream = (hipStream_t)p->stream;
+  c->L = layout_of(d, c->B, c->maxF);
+  c->code_emb = w.code_emb; c->text_emb = w.text_emb;
+  c->t_norm = w.talker_norm; c->p_norm = w.predictor_norm; c->t_head = w.talker_head;
+  c->tl.assign(w.talker, w.talker + d.Lt);
+  c->pl.assign(w.predictor, w.predictor + d.Lp);
+  c->p_heads.assign(w.predictor_heads, w.predictor_heads + d.G - 1);
+  c->ring = (uint8_t *)p->ring;
+  c->arena = (uint8_t *)p->arena;
+  c->pos_host.assign(c->B, 0);
+  c->ready.assign(c->B, 0);
+
+  auto bail = [&](int32_t code) {
+    g_err = c->err;
+    qt_free(c);
+    return code;
+  };
+  // pinned staging: ctl + overlay + forced codes + prefill ids up; codes down
+  c->pu_ctl = 0;
+  c->pu_overlay = 16;
+  c->pu_forced = c->pu_overlay + (size_t)c->maxF * c->B;
+  c->pu_pf_text = c->pu_forced + (size_t)c->maxF * c->B * d.G;
+  c->pu_pf_codes = c->pu_pf_text + (size_t)d.P;
+  c->pu_scalar = c->pu_pf_codes + (size_t)d.P * d.G;
+  c->pin_up_elems = c->pu_scalar + 16;
+  c->pin_down_elems = (size_t)c->maxF * c->B * d.G;
+  if (hipHostMalloc((void **)&c->pin_up, c->pin_up_elems * 4, hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void **)&c->pin_down, c->pin_down_elems * 4, hipHostMallocDefault) != hipSuccess)
+    return bail(fail(c, QT_E_HIP, "hipHostMalloc of staging buffers failed"));
+
+  // RoPE table: angle p * theta^(-2i/hd) in double, cos/sin rounded to f32
+  {
+    const int h = d.hd / 2;
+    std::vector<float> cs((size_t)d.P * h), sn((size_t)d.P * h);
+    for (int pp = 0; pp < d.P; ++pp)
+      for (int i = 0; i < h; ++i) {
+        const double ang = (double)pp * pow(m.rope_theta, -2.0 * i / (double)d.hd);
+        cs[(size_t)pp * h + i] = (float)cos(ang);
+        sn[(size_t)pp * h + i] = (float)sin(ang);
+      }
+    if (hipMemcpyAsync(c->arena + c->L.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
+        hipMemcpyAsync(c->arena + c->L.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
+        hipStreamSynchronize(c->stream) != hipSuccess)
+      return bail(fail(c, QT_E_HIP, "RoPE table upload failed"));
+  }
+  if (!(c->flags & QT_F_EAGER)) {
+    hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)));
+    hipError_t eq = enqueue_replay(c);
+    e = hipStreamEndCapture(c->stream, &c->graph);
+    if (eq != hipSuccess) return bail(fail(c, QT_E_HIP, "frame capture: %s", hipGetErrorString(eq)));
+    if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e)));
+    e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e)));
+  }
+  *out = c;
+  return QT_OK;
+}
+
+int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, const int32_t *text_ids) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  const Dims &d = c->d;
+  const qt_model_desc &md = c->md;
+  if (slot < 0 || slot >= c->B) return fail(c, QT_E_ARG, "slot %d outside [0, %d)", slot, c->B);
+  if (T <= 0 || !text_ids) return fail(c, QT_E_ARG, "T must be positive and text_ids non-NULL");
+  if (T > d.P) return fail(c, QT_E_CONTEXT_FULL, "prompt of %d rows exceeds %d ring positions", T, d.P);
+  if (!ids_ok(text_ids, T, d.Vt)) return fail(c, QT_E_RANGE, "text id outside [0, %d)", d.Vt);
+  if (codes && !ids_ok(codes, (size_t)T * d.G, d.Vc)) return fail(c, QT_E_RANGE, "code id outside [0, %d)", d.Vc);
+
+  hipStream_t s = c->stream;
+  int32_t *pf_codes = c->A<int32_t>(c->L.pf_codes), *pf_text = c->A<int32_t>(c->L.pf_text);
+  int32_t *up_text = c->pin_up + c->pu_pf_text, *up_codes = c->pin_up + c->pu_pf_codes;
+  memcpy(up_text, text_ids, sizeof(int32_t) * T);
+  if (codes) memcpy(up_codes, codes, sizeof(int32_t) * T * d.G);
+  HIPCHK(c, hipMemcpyAsync(pf_text, up_text, sizeof(int32_t) * T, hipMemcpyHostToDevice, s));
+  if (codes) HIPCHK(c, hipMemcpyAsync(pf_codes, up_codes, sizeof(int32_t) * T * d.G, hipMemcpyHostToDevice, s));
+
+  const int wt = wtype_of(md);
+  float *x = c->A<float>(c->L.x);
+  const Stack ts = talker_stack(c);
+  for (int r0 = 0; r0 < T; r0 += kPrefillChunk) {
+    const int M = T - r0 < kPrefillChunk ? T - r0 : kPrefillChunk;
+    GatherArgs ga = {};
+    ga.code_emb = c->code_emb; ga.text_emb = c->text_emb; ga.tab_bf16 = md.tab_bf16;
+    ga.H = d.H; ga.Vc = d.Vc; ga.G = d.G;
+    ga.codes = codes ? pf_codes + (size_t)r0 * d.G : nullptr; ga.codes_stride = d.G;
+    ga.text = pf_text + r0; ga.text_stride = 1; ga.x = x; ga.M = M;
+    HIPCHK(c, launch_gather(ga, s));
+    // rows of one slot at positions r0 .. r0+M-1, causal through the mask
+    const RowMap rows{slot, M, r0, nullptr};
+    for (int l = 0; l < d.Lt; ++l) HIPCHK(c, enqueue_layer(c, ts, l, M, rows, nullptr));
+    if (r0 + M == T) {
+      GemvArgs h = {};
+      h.seg[0] = lin(c->t_head); h.nseg = 1; h.seg_end[0] = d.Vc;
+      h.N = d.Vc; h.K = d.H; h.x = x + (size_t)(M - 1) * d.H; h.x_stride = d.H; h.M = 1;
+      h.gain = c->t_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
+      h.normed_out = c->A<float>(c->L.bridge) + (size_t)slot * d.H;
+      h.y = c->A<float>(c->L.logits_t) + (size_t)slot * d.Vc; h.y_stride = d.Vc;
+      HIPCHK(c, launch_gemv(wt, EPI_STORE, h, s));
+      ArgmaxArgs am = {};
+      am.logits = h.y; am.Vc = d.Vc; am.M = 1; am.mode = AM_PREFILL; am.slot = slot;
+      am.c0_state = c->A<int32_t>(c->L.c0);
+      HIPCHK(c, launch_argmax(am, s));
+    }
+  }
+  int32_t *up_pos = c->pin_up + c->pu_scalar;
+  up_pos[0] = T;
+  HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.pos) + slot, up_pos, sizeof(int32_t), hipMemcpyHostToDevice, s));
+  HIPCHK(c, hipStreamSynchronize(s));
+  c->pos_host[slot] = T;
+  c->ready[slot] = 1;
+  return QT_OK;
+}
+
+int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
+                        const int32_t *forced) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  const Dims &d = c->d;
+  const int B = c->B;
+  if (n <= 0 || !overlay_ids || !codes_out) return fail(c, QT_E_ARG, "n_frames must be positive, pointers non-NULL");
+  if (n % c->K) return fail(c, QT_E_ARG, "n_frames %d is not a multiple of frames_per_replay %d", n, c->K);
+  for (int b = 0; b < B; ++b) {
+    if (!c->ready[b]) return fail(c, QT_E_STATE, "slot %d not prefilled", b);
+    if (c->pos_host[b] + n > d.P)
+      return fail(c, QT_E_CONTEXT_FULL, "slot %d: position %d + %d frames exceeds %d", b, c->pos_host[b], n, d.P);
+  }
+  if (!ids_ok(overlay_ids, (size_t)n * B, d.Vt)) return fail(c, QT_E_RANGE, "overlay id outside [0, %d)", d.Vt);
+  if (forced && !ids_ok(forced, (size_t)n * B * d.G, d.Vc)) return fail(c, QT_E_RANGE, "forced code outside [0, %d)", d.Vc);
+
+  hipStream_t s = c->stream;
+  int32_t *ctl = c->A<int32_t>(c->L.ctl);
+  for (int f0 = 0; f0 < n; f0 += c->maxF) {
+    const int nf = n - f0 < c->maxF ? n - f0 : c->maxF;
+    // the previous chunk ended with a stream synchronize: staging is free
+    int32_t *up = c->pin_up + c->pu_ctl;
+    memset(up, 0, 16 * sizeof(int32_t));
+    up[0] = 0;                 // frame index base
+    up[1] = forced ? 1 : 0;    // teacher forcing
+    int32_t *ov = c->pin_up + c->pu_overlay;
+    memcpy(ov, overlay_ids + (size_t)f0 * B, sizeof(int32_t) * nf * B);
+    HIPCHK(c, hipMemcpyAsync(ctl, up, 16 * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.overlay), ov, sizeof(int32_t) * nf * B, hipMemcpyHostToDevice, s));
+    if (forced) {
+      int32_t *fu = c->pin_up + c->pu_forced;
+      memcpy(fu, forced + (size_t)f0 * B * d.G, sizeof(int32_t) * nf * B * d.G);
+      HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.cin), fu, sizeof(int32_t) * nf * B * d.G, hipMemcpyHostToDevice, s));
+    }
+    for (int r = 0; r < nf / c->K; ++r) {
+      if (c->exec) HIPCHK(c, hipGraphLaunch(c->exec, s));
+      else HIPCHK(c, enqueue_replay(c));
+    }
+    HIPCHK(c, hipMemcpyAsync(c->pin_down, c->A<int32_t>(c->L.cout), sizeof(int32_t) * nf * B * d.G, hipMemcpyDeviceToHost, s));
+    HIPCHK(c, hipStreamSynchronize(s));
+    memcpy(codes_out + (size_t)f0 * B * d.G, c->pin_down, sizeof(int32_t) * nf * B * d.G);
+    for (int b = 0; b < B; ++b) c->pos_host[b] += nf;
+  }
+  return QT_OK;
+}
+
+int32_t qt_get_slot_state(qt_ctx *c, int32_t slot, int32_t *pos, int32_t *c0, float *bridge) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  if (slot < 0 || slot >= c->B) return fail(c, QT_E_ARG, "slot %d outside [0, %d)", slot, c->B);
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  if (pos) HIPCHK(c, hipMemcpy(pos, c->A<int32_t>(c->L.pos) + slot, 4, hipMemcpyDeviceToHost));
+  if (c0) HIPCHK(c, hipMemcpy(c0, c->A<int32_t>(c->L.c0) + slot, 4, hipMemcpyDeviceToHost));
+  if (bridge)
+    HIPCHK(c, hipMemcpy(bridge, c->A<float>(c->L.bridge) + (size_t)slot * c->d.H, sizeof(float) * c->d.H, hipMemcpyDeviceToHost));
+  return QT_OK;
+}
+
+int32_t qt_set_slot_state(qt_ctx *c, int32_t slot, int32_t pos, int32_t c0, const float *bridge) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  if (slot < 0 || slot >= c->B || !bridge) return fail(c, QT_E_ARG, "bad slot or NULL bridge");
+  if (pos < 1 || pos > c->d.P) return fail(c, QT_E_RANGE, "pos %d outside [1, %d]", pos, c->d.P);
+  if (c0 < 0 || c0 >= c->d.Vc) return fail(c, QT_E_RANGE, "c0 %d outside [0, %d)", c0, c->d.Vc);
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  HIPCHK(c, hipMemcpy(c->A<int32_t>(c->L.pos) + slot, &pos, 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->A<int32_t>(c->L.c0) + slot, &c0, 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->A<float>(c->L.bridge) + (size_t)slot * c->d.H, bridge, sizeof(float) * c->d.H, hipMemcpyHostToDevice));
+  c->pos_host[slot] = pos;
+  c->ready[slot] = 1;
+  return QT_OK;
+}
+
+int32_t qt_read_dump(qt_ctx *c, int32_t kind, void *dst, size_t bytes) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  if (!(c->flags & QT_F_DUMP)) return fail(c, QT_E_STATE, "dump %d needs QT_F_DUMP", kind);
+  if (!dst) return fail(c, QT_E_ARG, "NULL destination");
+  const Dims &d = c->d;
+  const size_t B = c->B;
+  size_t off, need;
+  switch (kind) {
+    case QT_DUMP_TALKER_LOGITS: off = c->L.logits_t; need = 4 * B * d.Vc; break;
+    case QT_DUMP_PRED_LOGITS: off = c->L.logits_p; need = 4 * (size_t)(d.G - 1) * B * d.Vc; break;
+    case QT_DUMP_BRIDGE: off = c->L.bridge; need = 4 * B * d.H; break;
+    case QT_DUMP_X0: off = c->L.x0_dump; need = 4 * B * d.H; break;
+    case QT_DUMP_GATHER: off = c->L.gather_dump; need = 4 * B * (d.G + 1); break;
+    case QT_DUMP_TPOS: off = c->L.tpos_dump; need = 4 * B; break;
+    case QT_DUMP_HIDDEN: off = c->L.hidden_dump; need = 4 * (size_t)d.Lt * B * d.H; break;
+    default: return fail(c, QT_E_ARG, "unknown dump kind %d", kind);
+  }
+  if (bytes != need) return fail(c, QT_E_ARG, "dump %d is %zu bytes, not %zu", kind, need, bytes);
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  HIPCHK(c, hipMemcpy(dst, c->arena + off, need, hipMemcpyDeviceToHost));
+  return QT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// kernels.h -- launch interface of the gfx950 kernels (internal to libqt).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qtk {
+
+enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_GATED = 2 };
+
+// Row r of a step belongs to slot  slot_base + r / rows_per_slot  and sits at
+// position  pos_dev ? pos_dev[slot] : pos_base + r % rows_per_slot.
+struct RowMap {
+  int32_t slot_base;
+  int32_t rows_per_slot;
+  int32_t pos_base;
+  const int32_t *pos_dev;
+};
+
+struct Lin {
+  const void *w;
+  const uint16_t *sc;  // Q8 scales (fp16 bits), else null
+};
+
+// y[m][n] (epilogue) sum_k W[n][k] * x~[m][k]
+//   x~ = act(x * rinv_m * gain)   when gain != null (RMSNorm prologue)
+//   x~ = act(x)                   otherwise
+struct GemvArgs {
+  Lin seg[3];          // row segments (q|k|v) ...
+  int32_t seg_end[3];  // ... rows [seg_end[i-1], seg_end[i]) read seg[i]
+  int32_t nseg;
+  Lin up;              // EPI_GATED: second matrix (u); seg[0] is the gate
+  int32_t N, K;
+  const float *x;
+  int32_t x_stride;
+  int32_t M;
+  const void *gain;
+  int32_t gain_bf16;
+  float eps;
+  int32_t act_bf16;
+  float *y;
+  int32_t y_stride;
+  float *normed_out;   // block 0 stores x * rinv * gain (f32) here, stride K
+  float *copy_out;     // EPI_RESID: also store the updated row here
+  int32_t copy_stride;
+};
+
+struct QkArgs {
+  const float *qkv;  // [M][(nq + 2 nkv) hd]
+  int32_t M;
+  RowMap rows;
+  int32_t nq, nkv;
+  const void *q_gain, *k_gain;
+  int32_t gain_bf16;
+  float eps;
+  const float *rope_cos, *rope_sin;  // [rope_rows][hd/2]
+  float *q_out;                      // [M][nq hd]
+  void *ring_layer;                  // this layer's (slot 0, K) block
+  int64_t slot_stride, kv_stride;    // elements
+  int32_t P;                         // positions per (slot, layer, K|V, head)
+};
+
+struct AttnArgs {
+  const float *q;  // [M][nq hd]
+  int32_t M;
+  RowMap rows;
+  int32_t nq, nkv;
+  const void *ring_layer;
+  int64_t slot_stride, kv_stride;
+  int32_t P;
+  int32_t tile;       // positions per tile (fixed absolute boundaries)
+  int32_t max_tiles;  // grid z
+  float scale;
+  float *o;           // [M][nq hd]
+  float *part;        // [M][nq][max_tiles][hd + 2]
+};
+
+struct GatherArgs {
+  const void *code_emb, *text_emb;
+  int32_t tab_bf16, H, Vc, G;
+  const int32_t *codes;  // row r: codes[r * codes_stride + g]; null: text rows only
+  int32_t codes_stride;
+  const int32_t *text;   // row r: text[r * text_stride]
+  int32_t text_stride;
+  const int32_t *ctl;    // if set, codes/text advance by ctl[0] * frame_stride_*
+  int32_t frame_stride_codes, frame_stride_text;
+  float *x;
+  int32_t M;
+  float *x0_dump;
+  int32_t *gather_dump;  // [M][G+1]
+};
+
+struct PredInArgs {
+  const float *bridge;
+  const void *code_emb;
+  int32_t tab_bf16, H, G, B;
+  const int32_t *c0_state;
+  const int32_t *ctl;  // [0] frame index base, [1] forcing
+  int32_t k;           // frame within the replay
+  int32_t *cin, *cout; // [frames][B][G]
+  float *x;            // rows 2b = bridge[b], 2b+1 = E_0[c0]
+};
+
+enum ArgMode { AM_PRED = 0, AM_TALKER = 1, AM_PREFILL = 2 };
+
+struct ArgmaxArgs {
+  const float *logits;
+  int32_t Vc, M, mode;
+  int32_t j;  // AM_PRED: head index (code j+1)
+  const int32_t *ctl;
+  int32_t k, B, G;
+  int32_t *cin, *cout;
+  int32_t *c0_state, *pos, *tpos_dump;
+  const void *code_emb;
+  int32_t tab_bf16, H;
+  float *x_next;  // AM_PRED: row b <- E_{j+1}[code] when j+1 < G-1
+  int32_t slot;   // AM_PREFILL
+};
+
+hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s);
+hipError_t launch_qk_rope_kv(int hd, int kv_bf16, const QkArgs &a, hipStream_t s);
+hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine, hipStream_t s);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+hipError_t launch_pred_input(const PredInArgs &a, hipStream_t s);
+hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t s);
+hipError_t launch_advance(int32_t *ctl, int32_t K, hipStream_t s);
+
+}  // namespace qtk

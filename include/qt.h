@@ -1,0 +1,215 @@
+/*
+ * qt.h -- C ABI of the MI355X (gfx950) per-frame decode library.
+ *
+ * One codec frame = one talker step + 15 code-predictor micro-steps, decoded
+ * greedily on one GPU.  All compute runs in the library's HIP kernels; the
+ * caller supplies device memory (weights, the K/V ring, a scratch arena) and a
+ * HIP stream, typically from PyTorch.  No entry point allocates device memory.
+ *
+ * Sources (page title, section):
+ *   [QT-log]   qwentts.cpp, commit log of src/pipeline-tts.h
+ *   [QT-tests] qwentts.cpp, commit log of the tests branch
+ *   [MC-opt]   MiniCPM-o 4.5 single-GPU engine, docs/optimizations.md
+ *
+ * Conventions
+ *   - Every entry point returns int32_t status: QT_OK (0) or a negative QT_E_*.
+ *     A failing call changes no state: arguments are validated on the host
+ *     before any launch.  qt_last_error() describes the last failure.
+ *   - "device" pointers are HIP device addresses; "host" pointers are ordinary
+ *     host memory, read or written only during the call.  The library keeps
+ *     device pointers it is given for the lifetime of the context; the caller
+ *     keeps that memory alive and at a fixed address until qt_free().
+ *   - Matrices are row-major [out][in]; "bf16" means IEEE bfloat16 bits.
+ *   - One context is driven by one host thread.
+ */
+#ifndef QT_H
+#define QT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Closed ABI range: a caller built against any version in
+   [QT_ABI_MIN_VERSION, QT_ABI_VERSION] is accepted; both bounds are checked
+   ([QT-tests], codec left context / ABI range entry). */
+#define QT_ABI_MIN_VERSION 1
+#define QT_ABI_VERSION 1
+
+#define QT_OK 0
+#define QT_E_ABI (-1)          /* abi_version outside the closed range (checked first) */
+#define QT_E_ARG (-2)          /* bad argument: NULL, negative count, bad flag, struct_size */
+#define QT_E_SIZE (-3)         /* ring or arena smaller than qt_query_sizes() */
+#define QT_E_RANGE (-4)        /* a code id >= codebook_size or text id >= text_rows */
+#define QT_E_STATE (-5)        /* slot not prefilled, or dump read without QT_F_DUMP */
+#define QT_E_CONTEXT_FULL (-6) /* the talker ring cannot hold the requested positions */
+#define QT_E_HIP (-7)          /* a HIP runtime call failed */
+#define QT_E_UNSUPPORTED (-8)  /* shape outside what the kernels implement */
+
+/* storage of linear (projection and head) weights */
+#define QT_LIN_F32 0
+#define QT_LIN_BF16 1
+#define QT_LIN_Q8 2 /* int8 values [N][K] + fp16 scale per 32 along K: [N][K/32] */
+
+/* context flags */
+#define QT_F_DUMP 1u  /* keep per-step readbacks (logits, bridge, gather ids, hidden) */
+#define QT_F_EAGER 2u /* launch kernels directly instead of replaying a hipGraph */
+
+typedef struct qt_model_desc {
+  int32_t hidden;              /* H: width of talker and predictor */
+  int32_t n_q_heads;           /* nq */
+  int32_t n_kv_heads;          /* nkv (divides nq) */
+  int32_t head_dim;            /* hd: 64 or 128 */
+  int32_t ffn;                 /* F: SiLU-multiply width */
+  int32_t talker_layers;       /* Lt */
+  int32_t predictor_layers;    /* Lp */
+  int32_t codebooks;           /* G: codes per frame (16) */
+  int32_t codebook_size;       /* Vc: entries per codebook = width of every head */
+  int32_t text_rows;           /* Vt: rows of the text / pad overlay table */
+  int32_t talker_positions;    /* P: talker ring positions (multiple of 256) */
+  int32_t predictor_positions; /* Q: predictor cache positions (== G) */
+  int32_t lin_type;            /* QT_LIN_* */
+  int32_t tab_bf16;            /* code / text tables and norm gains: 1 bf16, 0 f32 */
+  int32_t kv_bf16;             /* ring rows: 1 bf16, 0 f32 */
+  int32_t act_bf16;            /* 1: matmul activation operands rounded to bf16 (RNE) */
+  double eps;                  /* RMSNorm epsilon */
+  double rope_theta;           /* RoPE base */
+} qt_model_desc;
+
+typedef struct qt_linear {
+  const void *w;      /* device: f32 / bf16 [N][K], or int8 [N][K] for QT_LIN_Q8 */
+  const void *scales; /* device: QT_LIN_Q8 only, fp16 bits [N][K/32]; else NULL */
+} qt_linear;
+
+/* One decoder layer (pre-norm; [MC-opt] core table: residual add + RMSNorm,
+   q/k norm + RoPE, SiLU-multiply).  Norm gains are [H] or [hd]. */
+typedef struct qt_layer_weights {
+  const void *attn_norm; /* [H] */
+  qt_linear wq;          /* [nq*hd][H] */
+  qt_linear wk;          /* [nkv*hd][H] */
+  qt_linear wv;          /* [nkv*hd][H] */
+  const void *q_norm;    /* [hd], shared by all query heads */
+  const void *k_norm;    /* [hd], shared by all key heads */
+  qt_linear wo;          /* [H][nq*hd] */
+  const void *mlp_norm;  /* [H] */
+  qt_linear wg;          /* [F][H] gate */
+  qt_linear wu;          /* [F][H] up */
+  qt_linear wd;          /* [H][F] down */
+} qt_layer_weights;
+
+typedef struct qt_weights {
+  const void *code_emb;                /* device [G][Vc][H]: table g feeds code g
+                                          ([QT-log] AR inputs entry) */
+  const void *text_emb;                /* device [Vt][H]: text / pad overlay rows */
+  const qt_layer_weights *talker;      /* host array [Lt], read during qt_init */
+  const void *talker_norm;             /* device [H] */
+  qt_linear talker_head;               /* [Vc][H] */
+  const qt_layer_weights *predictor;   /* host array [Lp], read during qt_init */
+  const void *predictor_norm;          /* device [H] */
+  const qt_linear *predictor_heads;    /* host array [G-1], each [Vc][H] */
+} qt_weights;
+
+typedef struct qt_init_params {
+  uint32_t abi_version; /* QT_ABI_VERSION of the caller's header */
+  uint32_t struct_size; /* sizeof(qt_init_params) */
+  qt_model_desc model;
+  qt_weights weights;
+  /* Caller-owned device memory, 256-byte aligned, >= qt_query_sizes():
+     ring  = talker ring [B][Lt][2][nkv][P][hd] then predictor cache
+             [B][Lp][2][nkv][Q][hd] ([2] = K, V), element bf16 or f32 per
+             kv_bf16 ([QT-log] per-layer K/V ring entry).  Row `pos` of a
+             (slot, layer, K|V, head) holds that position's vector.
+     arena = the library's fixed-address scratch (state, activations, io). */
+  void *ring;
+  size_t ring_bytes;
+  void *arena;
+  size_t arena_bytes;
+  int32_t max_batch;           /* B: streams decoded together (slots 0..B-1) */
+  int32_t frames_per_replay;   /* K: frames per graph replay; n_frames % K == 0 */
+  int32_t max_frames_per_call; /* frames staged per upload; longer calls loop */
+  uint32_t flags;              /* QT_F_* */
+  void *stream;                /* hipStream_t, caller-owned; non-default unless QT_F_EAGER */
+} qt_init_params;
+
+typedef struct qt_ctx qt_ctx;
+
+/* ABI version of the loaded library. */
+int32_t qt_abi_version(void);
+
+/* Pure host computation of the device memory a context needs.
+   ring_bytes = B*Lt*2*nkv*P*hd*e + B*Lp*2*nkv*Q*hd*e with e = 2 (bf16) or 4.
+   Errors: QT_E_ARG (NULL outputs, non-positive sizes), QT_E_UNSUPPORTED. */
+int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t frames_per_replay,
+                       int32_t max_frames_per_call, uint32_t flags, size_t *ring_bytes,
+                       size_t *arena_bytes);
+
+/* Validates, binds caller memory, uploads the RoPE table, and (unless
+   QT_F_EAGER) captures the K-frame graph on params->stream.  All slots start
+   un-prefilled.  Errors: QT_E_ABI first, then QT_E_ARG, QT_E_UNSUPPORTED,
+   QT_E_SIZE, QT_E_HIP.  *out is set only on success. */
+int32_t qt_init(const qt_init_params *params, qt_ctx **out);
+
+/* Prefill of one slot with T prompt rows ([QT-log] per-layer K/V ring entry:
+   prefill resets the cache and writes T positions).  Row p's input is
+   sum_g code_emb[g][codes[p][g]] + text_emb[text_ids[p]] (codes may be NULL:
+   text rows only).  Writes ring rows [0, T), sets the slot's bridge (final
+   normed hidden of row T-1), c0 (argmax of the talker head) and pos = T.
+   codes: host [T][G] or NULL; text_ids: host [T].  Synchronous.
+   Errors: QT_E_ARG, QT_E_RANGE, QT_E_CONTEXT_FULL (T > P), QT_E_HIP. */
+int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
+                   const int32_t *text_ids);
+
+/* Decodes n_frames frames for all B slots as n_frames/K graph replays.
+   overlay_ids: host [n][B] (frame f's talker step adds text_emb row
+   overlay_ids[f][b]).  codes_out: host [n][B][G]: codes_out[f][b][0] is the
+   talker's greedy code for frame f, [1..G-1] the predictor's.  forced_codes:
+   NULL, or host [n][B][G] teacher-forcing codes that are fed back instead of
+   the argmax results (codes_out still receives every argmax).  Synchronous:
+   codes are in codes_out on return.  Only ids cross the host boundary per
+   frame ([QT-log] set_rows / hot-loop entry).
+   Errors: QT_E_ARG (n_frames % K, NULLs), QT_E_RANGE, QT_E_STATE (a slot not
+   prefilled), QT_E_CONTEXT_FULL (pos + n_frames > P; checked before any
+   launch), QT_E_HIP. */
+int32_t qt_decode_frame(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_ids,
+                        int32_t *codes_out, const int32_t *forced_codes);
+
+/* Snapshot / restore of a slot's non-ring state: next talker position, the
+   pending code 0, and the bridge (host float [H]).  The ring itself is caller
+   memory at the documented layout.  set marks the slot prefilled.
+   Errors: QT_E_ARG, QT_E_RANGE (pos outside [1, P], c0 outside [0, Vc)). */
+int32_t qt_get_slot_state(qt_ctx *ctx, int32_t slot, int32_t *pos, int32_t *c0, float *bridge);
+int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
+                          const float *bridge);
+
+/* Readbacks of the last decoded frame (QT_F_DUMP only; host readbacks of
+   hidden state exist only in this mode, as in [QT-log] set_rows entry).
+   kind and host layout:
+     QT_DUMP_TALKER_LOGITS f32 [B][Vc]       (after qt_prefill: its last row)
+     QT_DUMP_PRED_LOGITS   f32 [G-1][B][Vc]
+     QT_DUMP_BRIDGE        f32 [B][H]
+     QT_DUMP_X0            f32 [B][H]        talker input gather-sum
+     QT_DUMP_GATHER        i32 [B][G+1]      codes fed to the gather, overlay id
+     QT_DUMP_TPOS          i32 [B]           talker K/V write position
+     QT_DUMP_HIDDEN        f32 [Lt][B][H]    talker residual after each layer
+   bytes must equal the kind's size.  Errors: QT_E_STATE, QT_E_ARG, QT_E_HIP. */
+#define QT_DUMP_TALKER_LOGITS 1
+#define QT_DUMP_PRED_LOGITS 2
+#define QT_DUMP_BRIDGE 3
+#define QT_DUMP_X0 4
+#define QT_DUMP_GATHER 5
+#define QT_DUMP_TPOS 6
+#define QT_DUMP_HIDDEN 7
+int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
+
+/* Destroys graphs and host state; never frees caller memory.  NULL is a no-op. */
+void qt_free(qt_ctx *ctx);
+
+/* Last error text of ctx (of the calling thread when ctx is NULL). */
+const char *qt_last_error(const qt_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QT_H */

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Marked gpu; run on an MI355X.
+
+Sizes: the tiny F32 model (several GEMV tiles per matrix, a ragged 16-row
+prompt against 32-row prefill chunks), a reduced model at the full 1024/3072
+widths, and the full 28-layer BF16 / Q8 models at their real shapes."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+from autoregressive_codebook_tts_frame_amd import synth
+from parity import assert_near_ties_only, code_mismatches, rel_l2, tol_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from autoregressive_codebook_tts_frame_amd import qt  # noqa: E402
+from oracle import Oracle  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None):
+    """Oracle free run, then the GPU teacher-forced with the oracle's codes
+    (one frame per call, dumps read after each) and free-running."""
+    prompts = prompts or [synth.make_prompt(wl, b) for b in range(batch)]
+    ov = synth.make_overlays(wl, nframes, batch)
+    o = Oracle(m, w, batch, pcap=max(len(p[1]) for p in prompts) + nframes + 1)
+    pre_logits = []
+    for b, (c, t) in enumerate(prompts):
+        pre_logits.append(o.prefill(b, c, t, dump=True)["logits"])
+    ostate = [o.get_state(b) for b in range(batch)]
+    oout = o.decode(nframes, ov, dump=True, hidden=dump_hidden)
+
+    d = qt.Decoder(m, w, batch, flags=qt.QT_F_DUMP)
+    for b, (c, t) in enumerate(prompts):
+        d.prefill(b, c, t)
+    gstate = [d.get_state(b) for b in range(batch)]
+    gpre = d.dump(qt.QT_DUMP_TALKER_LOGITS)
+    g = {k: [] for k in ("codes", "talker_logits", "pred_logits", "bridge", "x0", "gather", "tpos", "hidden")}
+    for f in range(nframes):
+        g["codes"].append(d.decode(1, ov[f:f + 1], forced=oout["codes"][f:f + 1])[0])
+        g["talker_logits"].append(d.dump(qt.QT_DUMP_TALKER_LOGITS))
+        g["pred_logits"].append(d.dump(qt.QT_DUMP_PRED_LOGITS).transpose(1, 0, 2))
+        g["bridge"].append(d.dump(qt.QT_DUMP_BRIDGE))
+        g["x0"].append(d.dump(qt.QT_DUMP_X0))
+        g["gather"].append(d.dump(qt.QT_DUMP_GATHER))
+        g["tpos"].append(d.dump(qt.QT_DUMP_TPOS))
+        if dump_hidden:
+            g["hidden"].append(d.dump(qt.QT_DUMP_HIDDEN).transpose(1, 0, 2))
+    g = {k: np.stack(v) for k, v in g.items() if v}
+    return dict(o=o, d=d, ov=ov, prompts=prompts, pre_logits=pre_logits, ostate=ostate,
+                oout=oout, gstate=gstate, gpre=gpre, g=g)
+
+
+def _check(r, m, label, free_run=True):
+    tol = tol_for(m)
+    oout, g = r["oout"], r["g"]
+    B = len(r["prompts"])
+    worst = {}
+    for b in range(B):
+        # prefill: position, bridge, logits
+        assert r["gstate"][b][0] == r["ostate"][b][0]
+        worst["prefill_bridge"] = max(worst.get("prefill_bridge", 0), rel_l2(r["gstate"][b][2], r["ostate"][b][2]))
+        worst["prefill_logits"] = max(worst.get("prefill_logits", 0), rel_l2(r["gpre"][b], r["pre_logits"][b]))
+    for f in range(oout["codes"].shape[0]):
+        for b in range(B):
+            for key in ("talker_logits", "bridge", "x0"):
+                worst[key] = max(worst.get(key, 0), rel_l2(g[key][f, b], oout[key][f, b]))
+            for j in range(m.G - 1):
+                worst["pred_logits"] = max(worst.get("pred_logits", 0),
+                                           rel_l2(g["pred_logits"][f, b, j], oout["pred_logits"][f, b, j]))
+            if "hidden" in g:
+                for l in range(m.Lt):
+                    worst["hidden"] = max(worst.get("hidden", 0), rel_l2(g["hidden"][f, b, l], oout["hidden"][f, b, l]))
+    say(f"[{label}] worst rel-L2 (tol {tol}):", {k: f"{v:.2e}" for k, v in worst.items()})
+    for k, v in worst.items():
+        assert v <= tol, f"{label}: {k} rel-L2 {v} > {tol}"
+    # integer work is bit-exact: gather indices and K/V write positions
+    assert np.array_equal(g["gather"], oout["gather"])
+    assert np.array_equal(g["tpos"], oout["tpos"])
+
+    def ref_logits(f, b, j):
+        if j == 0:
+            return r["pre_logits"][b] if f == 0 else oout["talker_logits"][f - 1, b]
+        return oout["pred_logits"][f, b, j - 1]
+
+    def gpu_logits(f, b, j):
+        if j == 0:
+            return r["gpre"][b] if f == 0 else g["talker_logits"][f - 1, b]
+        return g["pred_logits"][f, b, j - 1]
+
+    bad = code_mismatches(g["codes"], oout["codes"], ref_logits, gpu_logits)
+    say(f"[{label}] teacher-forced decisions differing: {len(bad)} of {g['codes'].size}")
+    assert_near_ties_only(bad, label)
+    if free_run and not bad:
+        # free running from the same prefill must reproduce the oracle's codes
+        d2 = qt.Decoder(m, r["d"].dw, B)
+        for b, (c, t) in enumerate(r["prompts"]):
+            d2.prefill(b, c, t)
+        n = oout["codes"].shape[0]
+        codes = d2.decode(n, r["ov"])
+        assert np.array_equal(codes, oout["codes"]), f"{label}: free-run codes differ"
+        d2.close()
+
+
+# ----------------------------------------------------------------- tiny F32
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    m = synth.TINY
+    wl = synth.WORKLOADS["tiny_f32_b1"]
+    w = synth.make_weights(m)
+    say("[tiny] running oracle + GPU, 8 frames")
+    return m, w, wl, _forced_run(m, w, wl, 8, dump_hidden=True)
+
+
+def test_tiny_f32_parity(tiny):
+    m, w, wl, r = tiny
+    _check(r, m, "tiny_f32")
+    # F32: the oracle's codes come out free-running with no near ties
+    assert np.array_equal(r["g"]["codes"], r["oout"]["codes"])
+
+
+def test_tiny_graph_equals_eager_bitwise(tiny):
+    m, w, wl, r = tiny
+    c, t = r["prompts"][0]
+    outs = []
+    for flags in (qt.QT_F_DUMP, qt.QT_F_DUMP | qt.QT_F_EAGER):
+        d = qt.Decoder(m, r["d"].dw, 1, flags=flags)
+        d.prefill(0, c, t)
+        codes = d.decode(8, r["ov"])
+        outs.append((codes, d.dump(qt.QT_DUMP_TALKER_LOGITS), d.dump(qt.QT_DUMP_PRED_LOGITS),
+                     d.get_state(0)[2]))
+        d.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
+def test_tiny_repeat_runs_identical_and_multi_frame_call(tiny):
+    m, w, wl, r = tiny
+    c, t = r["prompts"][0]
+    runs = []
+    for _ in range(2):
+        d = qt.Decoder(m, r["d"].dw, 1)
+        d.prefill(0, c, t)
+        runs.append(d.decode(8, r["ov"]))
+        d.close()
+    assert np.array_equal(runs[0], runs[1])
+    assert np.array_equal(runs[0], r["oout"]["codes"])
+
+
+def test_tiny_batched_equals_per_stream_and_permutation(tiny):
+    m, w, wl, r = tiny
+    wl3 = dataclasses.replace(wl, batch=3)
+    prompts = [synth.make_prompt(wl3, b, T=9 + 5 * b) for b in range(3)]
+    ov = synth.make_overlays(wl3, 4)
+    d = qt.Decoder(m, r["d"].dw, 3, flags=qt.QT_F_DUMP)
+    for b, (c, t) in enumerate(prompts):
+        d.prefill(b, c, t)
+    cb = d.decode(4, ov)
+    lb = d.dump(qt.QT_DUMP_PRED_LOGITS)
+    # permuted slots give permuted outputs, bit for bit
+    perm = [2, 0, 1]
+    dp = qt.Decoder(m, r["d"].dw, 3, flags=qt.QT_F_DUMP)
+    for s, b in enumerate(perm):
+        dp.prefill(s, *prompts[b])
+    cp = dp.decode(4, ov[:, perm])
+    assert np.array_equal(cp, cb[:, perm])
+    assert np.array_equal(dp.dump(qt.QT_DUMP_PRED_LOGITS).view(np.uint32), lb[:, perm].view(np.uint32))
+    for b in range(3):
+        d1 = qt.Decoder(m, r["d"].dw, 1, flags=qt.QT_F_DUMP)
+        d1.prefill(0, *prompts[b])
+        c1 = d1.decode(4, ov[:, b:b + 1])
+        assert np.array_equal(c1[:, 0], cb[:, b])
+        assert np.array_equal(d1.dump(qt.QT_DUMP_PRED_LOGITS)[:, 0].view(np.uint32), lb[:, b].view(np.uint32))
+        d1.close()
+    # and the oracle agrees on every stream
+    o = Oracle(m, w, 3)
+    for b, (c, t) in enumerate(prompts):
+        o.prefill(b, c, t)
+    assert np.array_equal(o.decode(4, ov)["codes"], cb)
+
+
+def test_tiny_poisoned_ring_tail_and_predictor_cache(tiny):
+    m, w, wl, r = tiny
+    c, t = r["prompts"][0]
+    d = qt.Decoder(m, r["d"].dw, 1)
+    d.prefill(0, c, t)
+    tr = d.talker_ring()
+    tr[0, :, :, :, len(t):, :] = float("nan")   # positions past the context
+    d.predictor_ring()[...] = float("nan")      # stale predictor rows
+    torch.cuda.synchronize()
+    assert np.array_equal(d.decode(8, r["ov"]), r["oout"]["codes"])
+
+
+def test_tiny_errors_leave_state_unchanged(tiny):
+    m, w, wl, r = tiny
+    c, t = r["prompts"][0]
+    d = qt.Decoder(m, r["d"].dw, 1)
+    with pytest.raises(qt.QtError) as e:
+        d.decode(1, r["ov"][:1])
+    assert e.value.code == qt.QT_E_STATE
+    d.prefill(0, c, t)
+    bad = r["ov"][:1].copy()
+    bad[0, 0] = m.Vt
+    with pytest.raises(qt.QtError) as e:
+        d.decode(1, bad)
+    assert e.value.code == qt.QT_E_RANGE
+    with pytest.raises(qt.QtError) as e:
+        d.decode(m.P, np.zeros((m.P, 1), np.int32))
+    assert e.value.code == qt.QT_E_CONTEXT_FULL
+    assert d.get_state(0)[0] == len(t)
+    assert np.array_equal(d.decode(8, r["ov"]), r["oout"]["codes"])
+
+
+# ----------------------------------------------------------------- BF16 / Q8
+
+
+def _reduced(base, **kw):
+    return dataclasses.replace(base, Lt=2, Lp=1, Vt=4096, P=512, model_id=base.model_id + 20, **kw)
+
+
+def test_reduced_bf16_full_width_parity():
+    m = _reduced(synth.BIG)
+    w = synth.make_weights(m)
+    # a 300-row prompt: 10 prefill chunks with a ragged tail, 2 attention tiles
+    wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=300)
+    say("[reduced bf16] prompt 300, 6 frames")
+    _check(_forced_run(m, w, wl, 6, dump_hidden=True), m, "reduced_bf16")
+
+
+def test_reduced_q8_random_scales_parity():
+    m = _reduced(synth.BIG_Q8)
+    w = synth.make_weights(m, random_q8_scales=True)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b1"], model=m, prompt=40)
+    say("[reduced q8 random scales] 4 frames, batch 2")
+    _check(_forced_run(m, w, wl, 4, batch=2), m, "reduced_q8")
+
+
+@pytest.mark.timeout(900)
+def test_full_bf16_b1_parity():
+    m = synth.BIG
+    wl = synth.WORKLOADS["bf16_b1"]
+    say("[bf16_b1] weights")
+    w = synth.make_weights(m)
+    say("[bf16_b1] prefill 128 + 6 frames")
+    _check(_forced_run(m, w, wl, 6), m, "bf16_b1")
