@@ -663,4 +663,44 @@ int32_t qt_read_dump(qt_ctx *c, int32_t kind, void *dst, size_t bytes) {
   return QT_OK;
 }
 
+int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, double *bytes) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  if (kernel != QT_KERNEL_GEMV_GATE_UP || reps <= 0 || !avg_us || !bytes)
+    return fail(c, QT_E_ARG, "unknown kernel or bad arguments");
+  const Dims &d = c->d;
+  const qt_model_desc &md = c->md;
+  const int wt = wtype_of(md);
+  hipStream_t s = c->stream;
+  hipEvent_t e0, e1;
+  HIPCHK(c, hipEventCreate(&e0));
+  HIPCHK(c, hipEventCreate(&e1));
+  std::vector<const qt_layer_weights *> layers;
+  for (auto &L : c->tl) layers.push_back(&L);
+  for (auto &L : c->pl) layers.push_back(&L);
+  GemvArgs gu = {};
+  gu.act_bf16 = md.act_bf16; gu.gain_bf16 = md.tab_bf16; gu.eps = (float)md.eps;
+  gu.nseg = 1; gu.seg_end[0] = d.F; gu.N = d.F; gu.K = d.H;
+  gu.x = c->A<float>(c->L.x); gu.x_stride = d.H; gu.M = c->B;
+  gu.y = c->A<float>(c->L.z); gu.y_stride = d.F;
+  hipError_t err = hipEventRecord(e0, s);
+  int launches = 0;
+  for (int r = 0; r < reps && err == hipSuccess; ++r)
+    for (const qt_layer_weights *L : layers) {
+      gu.seg[0] = lin(L->wg); gu.up = lin(L->wu); gu.gain = L->mlp_norm;
+      if ((err = launch_gemv(wt, EPI_GATED, gu, s)) != hipSuccess) break;
+      ++launches;
+    }
+  if (err == hipSuccess) err = hipEventRecord(e1, s);
+  if (err == hipSuccess) err = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != hipSuccess) return fail(c, QT_E_HIP, "qt_time_kernel: %s", hipGetErrorString(err));
+  const double wbytes = md.lin_type == QT_LIN_F32 ? 4.0 : (md.lin_type == QT_LIN_BF16 ? 2.0 : 34.0 / 32.0);
+  *avg_us = 1000.0 * ms / launches;
+  *bytes = 2.0 * d.F * d.H * wbytes + 4.0 * c->B * (d.H + d.F);
+  return QT_OK;
+}
+
 }  // extern "C"

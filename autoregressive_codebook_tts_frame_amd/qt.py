@@ -29,8 +29,11 @@ QT_F_DUMP, QT_F_EAGER = 1, 2
 (QT_DUMP_TALKER_LOGITS, QT_DUMP_PRED_LOGITS, QT_DUMP_BRIDGE, QT_DUMP_X0, QT_DUMP_GATHER,
  QT_DUMP_TPOS, QT_DUMP_HIDDEN) = range(1, 8)
 
+QT_KERNEL_GEMV_GATE_UP = 1
+
 EXPORTS = ("qt_abi_version", "qt_query_sizes", "qt_init", "qt_prefill", "qt_decode_frame",
-           "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_free", "qt_last_error")
+           "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_time_kernel",
+           "qt_free", "qt_last_error")
 
 
 class qt_model_desc(C.Structure):
@@ -90,6 +93,8 @@ def _load():
     lib.qt_set_slot_state.restype = i32
     lib.qt_read_dump.argtypes = [vp, i32, vp, sz]
     lib.qt_read_dump.restype = i32
+    lib.qt_time_kernel.argtypes = [vp, i32, i32, C.POINTER(C.c_double), C.POINTER(C.c_double)]
+    lib.qt_time_kernel.restype = i32
     lib.qt_free.argtypes = [vp]
     lib.qt_free.restype = None
     lib.qt_last_error.argtypes = [vp]
@@ -173,6 +178,12 @@ def qt_read_dump(ctx, kind: int, out: np.ndarray):
     assert out.flags["C_CONTIGUOUS"]
     _check(lib.qt_read_dump(ctx, kind, out.ctypes.data, out.nbytes), ctx)
     return out
+
+
+def qt_time_kernel(ctx, kernel: int, reps: int):
+    us, nb = C.c_double(), C.c_double()
+    _check(lib.qt_time_kernel(ctx, kernel, reps, C.byref(us), C.byref(nb)), ctx)
+    return us.value, nb.value
 
 
 def qt_free(ctx):
@@ -296,6 +307,9 @@ class Decoder:
         out = np.empty((n, self.B, m.G), np.int32)
         qt_decode_frame(self.ctx, n, ov, out, fc)
         return out
+
+    def time_kernel(self, kernel: int, reps: int):
+        return qt_time_kernel(self.ctx, kernel, reps)
 
     def get_state(self, slot: int):
         return qt_get_slot_state(self.ctx, slot, self.m.H)

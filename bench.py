@@ -1,0 +1,181 @@
+"""Throughput of the per-frame decode step (one talker step + 15 code-predictor
+micro-steps) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bf16_b1]
+
+A step is one qt_decode_frame call of `frames_per_step` frames for every
+stream of the workload, always from the same prefilled state (the slot state
+is restored before each step, so every step decodes the same positions).
+Prints one JSON line.  Inputs are seeded and synthetic (weights N(0, 0.02));
+they are resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def frame_bytes(m, batch: int, mean_len: float) -> float:
+    """Algorithmic bytes of one frame-step for `batch` streams: talker weights
+    once, predictor weights for each of its 15 passes, every head once, K/V
+    reads over valid positions only (talker: mean_len per layer; predictor:
+    2 + 3 + ... + 16 positions per layer), K/V row writes and the gathered
+    table rows.  The padded window tail and norm gains are not counted."""
+    wb = {0: 4.0, 1: 2.0, 2: 34.0 / 32.0}[m.lin]
+    tb = 2.0 if m.tab_bf16 else 4.0
+    kvb = 2.0 if m.kv_bf16 else 4.0
+    layer = (m.nqkv * m.H + m.H * m.nq * m.hd + 3 * m.F * m.H) * wb
+    heads = m.G * m.Vc * m.H * wb
+    weights = m.Lt * layer + (m.G - 1) * m.Lp * layer + heads
+    kv_row = 2 * m.nkv * m.hd * kvb
+    pred_positions = sum(range(2, m.G + 1))
+    kv_read = batch * (m.Lt * mean_len + m.Lp * pred_positions) * kv_row
+    kv_write = batch * (m.Lt + m.Lp * m.G) * kv_row
+    gathers = batch * (m.G + 1 + m.G - 1) * m.H * tb
+    return weights + kv_read + kv_write + gathers
+
+
+def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0):
+    """The oracle as it stands, on the host cores: prefill (untimed) then as
+    many frames as fit in the budget (at least 1)."""
+    from autoregressive_codebook_tts_frame_amd import synth
+    from oracle import Oracle
+
+    o = Oracle(m, w, 1, pcap=wl.prompt + 64 + 1)
+    codes, text = synth.make_prompt(wl, 0)
+    t = time.time()
+    o.prefill(0, codes, text)
+    log(f"cpu baseline: oracle prefill {time.time() - t:.1f}s")
+    ov = synth.make_overlays(wl, 64)
+    n, t0 = 0, time.time()
+    while n < 64:
+        o.decode(1, ov[n:n + 1])
+        n += 1
+        if time.time() - t0 > frames_budget_s:
+            break
+    dt = time.time() - t0
+    threads = o.lib.orc_num_threads()
+    o.close()
+    return {"value": n / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} frames of {wl.name} (batch 1) after an untimed {wl.prompt}-row oracle prefill, "
+                      f"{dt:.1f}s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="bf16_b1")
+    ap.add_argument("--frames", type=int, default=None, help="frames per step (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build decodes on a single MI355X and has no "
+              "multi-GPU path (streams would shard by slot with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from autoregressive_codebook_tts_frame_amd import qt, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    m = wl.model
+    B = wl.batch
+    nf = args.frames or wl.frames
+    log(f"workload {wl.name}: B={B}, prompt {wl.prompt}, {nf} frames/step; drawing weights")
+    t = time.time()
+    w = synth.make_weights(m)
+    log(f"weights drawn in {time.time() - t:.1f}s; uploading")
+    d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf)
+    lens = []
+    for b in range(B):
+        codes, text = synth.make_prompt(wl, b)
+        d.prefill(b, codes, text)
+        lens.append(len(text))
+    states = [d.get_state(b) for b in range(B)]
+    ov = synth.make_overlays(wl, nf, B)
+    log("prefill done; warmup")
+
+    def step():
+        for b, (pos, c0, br) in enumerate(states):
+            d.set_state(b, pos, c0, br)
+        return d.decode(nf, ov)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    ev0.record(d.stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(d.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    frames = B * nf * args.steps
+    ms_per_step = 1e3 * wall / args.steps
+    mean_len = float(np.mean(lens)) + (nf + 1) / 2.0
+    fb = frame_bytes(m, B, mean_len)
+    ms_per_frame_step = 1e3 * wall / (nf * args.steps)
+
+    # dominant kernel: the gate/up GEMV, timed live with HIP events on the
+    # library's stream over every layer's weights
+    reps = 3
+    us, kbytes = d.time_kernel(qt.QT_KERNEL_GEMV_GATE_UP, reps)
+    achieved = kbytes / (us * 1e-6) / 1e9
+    log(f"{frames / wall:.1f} frames/s, {ms_per_frame_step:.3f} ms per frame-step; "
+        f"gate/up GEMV {us:.2f} us/launch = {achieved:.0f} GB/s")
+
+    res = {
+        "metric": "codec frames/s (talker step + 15 predictor steps)",
+        "value": frames / wall,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16"}[m.lin],
+        "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
+        "config": {"workload": wl.name, "batch": B, "prompt": wl.prompt, "frames_per_step": nf,
+                   "frames_per_replay": wl.frames_per_replay, "talker_layers": m.Lt,
+                   "predictor_layers": m.Lp, "hidden": m.H},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemv_kernel<bf16, gated> (RMSNorm + gate/up + SiLU-mul)",
+                     "bytes_per_launch": kbytes, "avg_launch_us": us},
+        "frame_roofline": {"bytes_per_frame_step": fb, "ms_per_frame_step": ms_per_frame_step,
+                           "achieved_gbs": fb / (ms_per_frame_step * 1e-3) / 1e9,
+                           "frac": fb / (ms_per_frame_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "gpu_event_s": gpu_s, "wall_s": wall},
+        "cpu_baseline": None,
+    }
+    d.close()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(m, w, wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

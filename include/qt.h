@@ -203,6 +203,21 @@ int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
 #define QT_DUMP_HIDDEN 7
 int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
 
+/* Measurement hook: launches one kernel of the frame `reps` times, in the
+   launch configuration the frame uses at batch B, between two HIP events on
+   the context's stream, and reports the average duration per launch
+   (microseconds) and the algorithmic bytes one launch moves (weights once,
+   activations in and out).  Successive launches walk every layer's weights
+   (talker then predictor), as the frame does, so no launch finds its weights
+   in a cache a previous launch filled.  Writes only arena scratch; the slots'
+   state is untouched.  Synchronous.
+     QT_KERNEL_GEMV_GATE_UP   RMSNorm + gate/up GEMV + SiLU-multiply (the
+                              largest weight stream of a layer)
+   Errors: QT_E_ARG, QT_E_HIP. */
+#define QT_KERNEL_GEMV_GATE_UP 1
+int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us,
+                       double *bytes_per_launch);
+
 /* Destroys graphs and host state; never frees caller memory.  NULL is a no-op. */
 void qt_free(qt_ctx *ctx);
 

@@ -268,3 +268,29 @@ def test_frame_schedule_golden(tiny):
     assert out["codes"].shape[2] == g["codes_per_frame"] == m.G
     assert out["pred_logits"].shape[2] == g["predictor_prefill_rows"] - 1 + g["predictor_decodes"]
     assert m.Q == g["predictor_cache_positions"]
+
+
+def test_bf16_rounding_noise_floor():
+    """In BF16 models every matmul operand is rounded to bf16, so any change
+    of an F32 activation, however small, flips some roundings and the flips
+    cascade.  A one-ulp change of a single table element moves the oracle's
+    own logits by a few 1e-3 (rel-L2) within two layers: that floor, not
+    kernel error, is what a BF16 parity tolerance of 1e-2 has to absorb."""
+    m = dataclasses.replace(synth.BIG, Lt=2, Lp=2, Vt=512, P=512, model_id=30)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=24)
+    codes, text = synth.make_prompt(wl, 0)
+    ov = synth.make_overlays(wl, 2)
+    a = Oracle(m, w, 1, pcap=64)
+    a.prefill(0, codes, text)
+    ra = a.decode(2, ov, dump=True)
+    w2 = dict(w)
+    tx = w["text_emb"].copy()
+    tx[text[0], 5] ^= 1  # one bf16 ulp, one element
+    w2["text_emb"] = tx
+    b = Oracle(m, w2, 1, pcap=64)
+    b.prefill(0, codes, text)
+    rb = b.decode(2, ov, forced=ra["codes"], dump=True)
+    e_t = rel_l2(rb["talker_logits"], ra["talker_logits"])
+    e_p = rel_l2(rb["pred_logits"], ra["pred_logits"])
+    assert 1e-3 < e_t < 1e-2 and 1e-3 < e_p < 2e-2, (e_t, e_p)
