@@ -29,7 +29,7 @@ def build_library(out: str = LIB, verbose: bool = False) -> str:
     objs = []
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    for src, gpu in (("kernels.hip", True), ("api.cpp", False)):
+    for src, gpu in (("kernels.hip", True), ("frame.hip", True), ("api.cpp", False)):
         obj = os.path.join(build_dir, src + ".o")
         cmd = [HIPCC, *COMMON, *(GPU_FLAGS if gpu else []), "-c", os.path.join(CSRC, src), "-o", obj]
         if gpu:

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "../../include/qt.h"
+#include "frame.h"
 #include "kernels.h"
 
 namespace {
@@ -24,6 +25,7 @@ thread_local std::string g_err;
 constexpr int kPrefillChunk = 32;  // prompt rows per prefill step
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
+constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -32,6 +34,8 @@ struct Layout {
   size_t rope_cos, rope_sin, pos, c0, bridge, ctl, overlay, cin, cout;
   size_t x, qkv, q, part, o, z, logits_t, logits_p;
   size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
+  // persistent frame kernel: weight tables, tagged exchange words, error flag
+  size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_part, f_err, f_trace;
   size_t total;
   int32_t rows;       // activation rows held
   int32_t max_tiles;  // talker attention tiles
@@ -80,6 +84,18 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.tpos_dump = take(sizeof(int32_t) * B);
   L.pf_codes = take(sizeof(int32_t) * (size_t)d.P * d.G);
   L.pf_text = take(sizeof(int32_t) * (size_t)d.P);
+  L.f_tl = take(sizeof(qtk::LayerDev) * d.Lt);
+  L.f_pl = take(sizeof(qtk::LayerDev) * d.Lp);
+  L.f_heads = take(sizeof(void *) * d.G);
+  L.f_heads_sc = take(sizeof(void *) * d.G);
+  L.f_xq = take(8 * 2 * (size_t)d.H);
+  L.f_qkv = take(8 * 2 * (size_t)d.nqkv);
+  L.f_o = take(8 * 2 * (size_t)d.qd);
+  L.f_z = take(8 * 2 * (size_t)d.F);
+  L.f_amax = take(8 * 2 * (size_t)kMaxWG);
+  L.f_part = take(8 * (size_t)d.nq * (d.P / kTile) * (d.hd + 2));
+  L.f_err = take(64);
+  L.f_trace = take(8 * 8 * 1024);
   L.total = off;
   return L;
 }
@@ -138,6 +154,9 @@ struct qt_ctx {
   size_t pu_ctl = 0, pu_overlay = 0, pu_forced = 0, pu_pf_text = 0, pu_pf_codes = 0, pu_scalar = 0;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  int32_t path = QT_PATH_GRAPH;
+  qtk::FrameArgs fa;       // persistent kernel arguments (path == QT_PATH_FRAME)
+  uint32_t tag_base = 1;   // running phase tag of the persistent kernel
   std::string err;
 
   template <class T> T *A(size_t off) const { return (T *)(arena + off); }
@@ -365,6 +384,37 @@ hipError_t enqueue_replay(qt_ctx *c) {
   return launch_advance(c->A<int32_t>(c->L.ctl), c->K, c->stream);
 }
 
+// Work split of each GEMV phase over nwg*4 waves; false if the persistent
+// kernel is not instantiated for it.
+bool frame_splits(const qt_model_desc &m, int nwg, Split (&sp)[SP_COUNT], const char **why) {
+  const Dims d = dims_of(m);
+  const int wt = wtype_of(m);
+  const int ch = wt == W_F32 ? 4 : (wt == W_BF16 ? 8 : 16);
+  const int tw = nwg * 4;
+  const int nk[SP_COUNT][3] = {{d.nqkv, d.H, 1}, {d.H, d.qd, 1}, {d.F, d.H, 2}, {d.H, d.F, 1}, {d.Vc, d.H, 1}};
+  for (int i = 0; i < SP_COUNT; ++i) {
+    const int N = nk[i][0], K = nk[i][1], nm = nk[i][2];
+    if (K % (64 * ch)) { *why = "a GEMV width is not a multiple of 64 lanes x 16 bytes"; return false; }
+    sp[i].rw = (int8_t)((N + tw - 1) / tw);
+    sp[i].nmat = (int8_t)nm;
+    sp[i].cpl = (int8_t)(K / (64 * ch));
+    if (!frame_split_supported(wt, sp[i])) { *why = "GEMV split not instantiated"; return false; }
+  }
+  return true;
+}
+
+const char *frame_unsupported(const qt_model_desc &m, int B) {
+  const Dims d = dims_of(m);
+  if (B != 1) return "the persistent kernel decodes one stream";
+  if (d.nq / d.nkv > 2) return "GQA group > 2";
+  if (d.H > 3072 || d.F > 3072 || d.qd > 3072 || d.hd > 128) return "width above 3072";
+  if (d.G > 32) return "more than 32 codebooks";
+  if (d.Lt + d.Lp > 40) return "more than 40 layers";
+  if (!qtk::frame_variant_supported(wtype_of(m), d.hd, d.nq / d.nkv, m.kv_bf16)) return "no persistent-kernel variant";
+  if (m.lin_type != QT_LIN_F32 && !m.act_bf16) return "bf16/q8 weights with f32 matmul operands";
+  return nullptr;
+}
+
 bool ids_ok(const int32_t *p, size_t n, int32_t hi) {
   for (size_t i = 0; i < n; ++i)
     if (p[i] < 0 || p[i] >= hi) return false;
@@ -379,6 +429,8 @@ extern "C" {
 
 int32_t qt_abi_version(void) { return QT_ABI_VERSION; }
 
+int32_t qt_path(const qt_ctx *ctx) { return ctx ? ctx->path : QT_E_ARG; }
+
 const char *qt_last_error(const qt_ctx *ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
 
 int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t frames_per_replay,
@@ -389,7 +441,7 @@ int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t fr
     return fail(nullptr, QT_E_ARG, "max_batch, frames_per_replay and max_frames_per_call must be positive");
   if (max_frames_per_call % frames_per_replay)
     return fail(nullptr, QT_E_ARG, "max_frames_per_call must be a multiple of frames_per_replay");
-  if (flags & ~(QT_F_DUMP | QT_F_EAGER)) return fail(nullptr, QT_E_ARG, "unknown flags");
+  if (flags & ~(QT_F_DUMP | QT_F_EAGER | QT_F_OPS | QT_F_TRACE)) return fail(nullptr, QT_E_ARG, "unknown flags");
   if (const char *why = unsupported(*model)) return fail(nullptr, QT_E_UNSUPPORTED, "%s", why);
   const Dims d = dims_of(*model);
   *ring_bytes = (talker_ring_elems(d, max_batch) + pred_ring_elems(d, max_batch)) * kv_elem(*model);
@@ -501,7 +553,68 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
         hipStreamSynchronize(c->stream) != hipSuccess)
       return bail(fail(c, QT_E_HIP, "RoPE table upload failed"));
   }
-  if (!(c->flags & QT_F_EAGER)) {
+  // decode path: persistent frame kernel where it applies
+  c->path = (c->flags & QT_F_EAGER) ? QT_PATH_EAGER : QT_PATH_GRAPH;
+  if (!(c->flags & (QT_F_EAGER | QT_F_OPS)) && !frame_unsupported(m, c->B)) {
+    int dev = 0, ncu = 0;
+    const char *why = nullptr;
+    Split sp[SP_COUNT];
+    int lds = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        (size_t)lds >= qtk::frame_lds_bytes() && ncu > 0 && ncu <= kMaxWG && frame_splits(m, ncu, sp, &why)) {
+      qtk::FrameArgs &fa = c->fa;
+      fa = qtk::FrameArgs{};
+      fa.H = d.H; fa.nq = d.nq; fa.nkv = d.nkv; fa.hd = d.hd; fa.F = d.F; fa.Lt = d.Lt; fa.Lp = d.Lp;
+      fa.G = d.G; fa.Vc = d.Vc; fa.Vt = d.Vt; fa.P = d.P; fa.Q = d.Q;
+      fa.wt = wtype_of(m); fa.tab_bf16 = m.tab_bf16; fa.kv_bf16 = m.kv_bf16; fa.act_bf16 = m.act_bf16;
+      fa.eps = (float)m.eps; fa.scale = (float)(1.0 / sqrt((double)d.hd));
+      for (int i = 0; i < SP_COUNT; ++i) fa.split[i] = sp[i];
+      fa.nwg = ncu;
+      // device-side weight tables
+      std::vector<qtk::LayerDev> tl(d.Lt), pl(d.Lp);
+      auto fill = [&](qtk::LayerDev &o, const qt_layer_weights &L) {
+        o.attn_norm = L.attn_norm; o.q_norm = L.q_norm; o.k_norm = L.k_norm; o.mlp_norm = L.mlp_norm;
+        const qt_linear *ls[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+        for (int i = 0; i < 7; ++i) { o.w[i] = ls[i]->w; o.sc[i] = (const uint16_t *)ls[i]->scales; }
+      };
+      for (int l = 0; l < d.Lt; ++l) fill(tl[l], c->tl[l]);
+      for (int l = 0; l < d.Lp; ++l) fill(pl[l], c->pl[l]);
+      std::vector<const void *> hw(d.G), hs(d.G);
+      hw[0] = c->t_head.w; hs[0] = c->t_head.scales;
+      for (int j = 0; j < d.G - 1; ++j) { hw[j + 1] = c->p_heads[j].w; hs[j + 1] = c->p_heads[j].scales; }
+      if (hipMemcpy(c->arena + c->L.f_tl, tl.data(), sizeof(qtk::LayerDev) * d.Lt, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(c->arena + c->L.f_pl, pl.data(), sizeof(qtk::LayerDev) * d.Lp, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(c->arena + c->L.f_heads, hw.data(), sizeof(void *) * d.G, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(c->arena + c->L.f_heads_sc, hs.data(), sizeof(void *) * d.G, hipMemcpyHostToDevice) != hipSuccess)
+        return bail(fail(c, QT_E_HIP, "frame table upload failed"));
+      fa.tl = c->A<qtk::LayerDev>(c->L.f_tl);
+      fa.pl = c->A<qtk::LayerDev>(c->L.f_pl);
+      fa.code_emb = c->code_emb; fa.text_emb = c->text_emb; fa.t_norm = c->t_norm; fa.p_norm = c->p_norm;
+      fa.head_w = c->A<const void *>(c->L.f_heads);
+      fa.head_sc = m.lin_type == QT_LIN_Q8 ? c->A<const uint16_t *>(c->L.f_heads_sc) : nullptr;
+      fa.pos = c->A<int32_t>(c->L.pos); fa.c0 = c->A<int32_t>(c->L.c0); fa.bridge = c->A<float>(c->L.bridge);
+      fa.ctl = c->A<int32_t>(c->L.ctl); fa.cin = c->A<int32_t>(c->L.cin); fa.cout = c->A<int32_t>(c->L.cout);
+      fa.overlay = c->A<int32_t>(c->L.overlay);
+      fa.rope_cos = c->A<float>(c->L.rope_cos); fa.rope_sin = c->A<float>(c->L.rope_sin);
+      fa.ring_t = c->ring;
+      fa.ring_p = c->ring + talker_ring_elems(d, c->B) * kv_elem(m);
+      fa.t_kv_stride = (int64_t)d.kd * d.P; fa.t_layer_stride = 2 * fa.t_kv_stride;
+      fa.p_kv_stride = (int64_t)d.kd * d.Q; fa.p_layer_stride = 2 * fa.p_kv_stride;
+      fa.xq = c->A<uint64_t>(c->L.f_xq); fa.qkvb = c->A<uint64_t>(c->L.f_qkv);
+      fa.ob = c->A<uint64_t>(c->L.f_o); fa.zb = c->A<uint64_t>(c->L.f_z);
+      fa.amax = c->A<uint64_t>(c->L.f_amax); fa.part = c->A<uint64_t>(c->L.f_part);
+      fa.logits_t = c->A<float>(c->L.logits_t); fa.logits_p = c->A<float>(c->L.logits_p);
+      fa.x0_dump = c->A<float>(c->L.x0_dump); fa.hidden_dump = c->A<float>(c->L.hidden_dump);
+      fa.gather_dump = c->A<int32_t>(c->L.gather_dump); fa.tpos_dump = c->A<int32_t>(c->L.tpos_dump);
+      fa.dump = (c->flags & QT_F_DUMP) ? 1 : 0;
+      fa.err = c->A<int32_t>(c->L.f_err);
+      fa.trace = (c->flags & QT_F_TRACE) ? c->A<uint64_t>(c->L.f_trace) : nullptr;
+      c->path = QT_PATH_FRAME;
+    }
+  }
+  if (c->path == QT_PATH_GRAPH) {
     hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
     if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)));
     hipError_t eq = enqueue_replay(c);
@@ -603,12 +716,31 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
       memcpy(fu, forced + (size_t)f0 * B * d.G, sizeof(int32_t) * nf * B * d.G);
       HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.cin), fu, sizeof(int32_t) * nf * B * d.G, hipMemcpyHostToDevice, s));
     }
-    for (int r = 0; r < nf / c->K; ++r) {
-      if (c->exec) HIPCHK(c, hipGraphLaunch(c->exec, s));
-      else HIPCHK(c, enqueue_replay(c));
+    if (c->path == QT_PATH_FRAME) {
+      int32_t *zero = c->pin_up + c->pu_scalar + 4;
+      zero[0] = 0;
+      HIPCHK(c, hipMemcpyAsync(c->fa.err, zero, sizeof(int32_t), hipMemcpyHostToDevice, s));
+      qtk::FrameArgs fa = c->fa;
+      fa.n_frames = nf;
+      fa.tag_base = c->tag_base;
+      // tags are only ever compared for equality: advance past every phase
+      // this launch can number (< 1024 per frame)
+      c->tag_base += (uint32_t)nf * 1024u + 16u;
+      if (c->tag_base < 16u) c->tag_base = 16u;
+      HIPCHK(c, launch_frame_kernel(fa, s));
+    } else {
+      for (int r = 0; r < nf / c->K; ++r) {
+        if (c->exec) HIPCHK(c, hipGraphLaunch(c->exec, s));
+        else HIPCHK(c, enqueue_replay(c));
+      }
     }
     HIPCHK(c, hipMemcpyAsync(c->pin_down, c->A<int32_t>(c->L.cout), sizeof(int32_t) * nf * B * d.G, hipMemcpyDeviceToHost, s));
+    int32_t *errh = c->pin_up + c->pu_scalar + 8;
+    errh[0] = 0;
+    if (c->path == QT_PATH_FRAME)
+      HIPCHK(c, hipMemcpyAsync(errh, c->fa.err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
     HIPCHK(c, hipStreamSynchronize(s));
+    if (errh[0]) return fail(c, QT_E_HIP, "frame kernel: an exchange wait timed out (decode state is undefined)");
     memcpy(codes_out + (size_t)f0 * B * d.G, c->pin_down, sizeof(int32_t) * nf * B * d.G);
     for (int b = 0; b < B; ++b) c->pos_host[b] += nf;
   }
@@ -642,7 +774,8 @@ int32_t qt_set_slot_state(qt_ctx *c, int32_t slot, int32_t pos, int32_t c0, cons
 
 int32_t qt_read_dump(qt_ctx *c, int32_t kind, void *dst, size_t bytes) {
   if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
-  if (!(c->flags & QT_F_DUMP)) return fail(c, QT_E_STATE, "dump %d needs QT_F_DUMP", kind);
+  if (kind == QT_DUMP_TRACE ? !(c->flags & QT_F_TRACE) : !(c->flags & QT_F_DUMP))
+    return fail(c, QT_E_STATE, "dump %d needs QT_F_DUMP (QT_F_TRACE for the trace)", kind);
   if (!dst) return fail(c, QT_E_ARG, "NULL destination");
   const Dims &d = c->d;
   const size_t B = c->B;
@@ -655,6 +788,7 @@ int32_t qt_read_dump(qt_ctx *c, int32_t kind, void *dst, size_t bytes) {
     case QT_DUMP_GATHER: off = c->L.gather_dump; need = 4 * B * (d.G + 1); break;
     case QT_DUMP_TPOS: off = c->L.tpos_dump; need = 4 * B; break;
     case QT_DUMP_HIDDEN: off = c->L.hidden_dump; need = 4 * (size_t)d.Lt * B * d.H; break;
+    case QT_DUMP_TRACE: off = c->L.f_trace; need = 8 * 8 * 1024; break;
     default: return fail(c, QT_E_ARG, "unknown dump kind %d", kind);
   }
   if (bytes != need) return fail(c, QT_E_ARG, "dump %d is %zu bytes, not %zu", kind, need, bytes);

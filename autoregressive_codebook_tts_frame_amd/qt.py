@@ -25,15 +25,16 @@ QT_OK = 0
 QT_E_ABI, QT_E_ARG, QT_E_SIZE, QT_E_RANGE = -1, -2, -3, -4
 QT_E_STATE, QT_E_CONTEXT_FULL, QT_E_HIP, QT_E_UNSUPPORTED = -5, -6, -7, -8
 QT_LIN_F32, QT_LIN_BF16, QT_LIN_Q8 = 0, 1, 2
-QT_F_DUMP, QT_F_EAGER = 1, 2
+QT_F_DUMP, QT_F_EAGER, QT_F_OPS, QT_F_TRACE = 1, 2, 4, 8
+QT_PATH_FRAME, QT_PATH_GRAPH, QT_PATH_EAGER = 1, 2, 3
 (QT_DUMP_TALKER_LOGITS, QT_DUMP_PRED_LOGITS, QT_DUMP_BRIDGE, QT_DUMP_X0, QT_DUMP_GATHER,
- QT_DUMP_TPOS, QT_DUMP_HIDDEN) = range(1, 8)
+ QT_DUMP_TPOS, QT_DUMP_HIDDEN, QT_DUMP_TRACE) = range(1, 9)
 
 QT_KERNEL_GEMV_GATE_UP = 1
 
 EXPORTS = ("qt_abi_version", "qt_query_sizes", "qt_init", "qt_prefill", "qt_decode_frame",
            "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_time_kernel",
-           "qt_free", "qt_last_error")
+           "qt_path", "qt_free", "qt_last_error")
 
 
 class qt_model_desc(C.Structure):
@@ -95,6 +96,8 @@ def _load():
     lib.qt_read_dump.restype = i32
     lib.qt_time_kernel.argtypes = [vp, i32, i32, C.POINTER(C.c_double), C.POINTER(C.c_double)]
     lib.qt_time_kernel.restype = i32
+    lib.qt_path.argtypes = [vp]
+    lib.qt_path.restype = i32
     lib.qt_free.argtypes = [vp]
     lib.qt_free.restype = None
     lib.qt_last_error.argtypes = [vp]
@@ -184,6 +187,10 @@ def qt_time_kernel(ctx, kernel: int, reps: int):
     us, nb = C.c_double(), C.c_double()
     _check(lib.qt_time_kernel(ctx, kernel, reps, C.byref(us), C.byref(nb)), ctx)
     return us.value, nb.value
+
+
+def qt_path(ctx) -> int:
+    return lib.qt_path(ctx)
 
 
 def qt_free(ctx):
@@ -308,6 +315,10 @@ class Decoder:
         qt_decode_frame(self.ctx, n, ov, out, fc)
         return out
 
+    @property
+    def path(self) -> int:
+        return qt_path(self.ctx)
+
     def time_kernel(self, kernel: int, reps: int):
         return qt_time_kernel(self.ctx, kernel, reps)
 
@@ -327,6 +338,7 @@ class Decoder:
             QT_DUMP_GATHER: ((B, m.G + 1), np.int32),
             QT_DUMP_TPOS: ((B,), np.int32),
             QT_DUMP_HIDDEN: ((m.Lt, B, m.H), np.float32),
+            QT_DUMP_TRACE: ((1024, 8), np.uint64),
         }[kind]
         return qt_read_dump(self.ctx, kind, np.empty(shape, dt))
 

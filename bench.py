@@ -81,6 +81,7 @@ def main():
     ap.add_argument("--workload", default="bf16_b1")
     ap.add_argument("--frames", type=int, default=None, help="frames per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ops", action="store_true", help="force the per-op hipGraph path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build decodes on a single MI355X and has no "
@@ -101,7 +102,8 @@ def main():
     t = time.time()
     w = synth.make_weights(m)
     log(f"weights drawn in {time.time() - t:.1f}s; uploading")
-    d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf)
+    d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf,
+                   flags=qt.QT_F_OPS if args.ops else 0)
     lens = []
     for b in range(B):
         codes, text = synth.make_prompt(wl, b)
@@ -136,13 +138,21 @@ def main():
     fb = frame_bytes(m, B, mean_len)
     ms_per_frame_step = 1e3 * wall / (nf * args.steps)
 
-    # dominant kernel: the gate/up GEMV, timed live with HIP events on the
-    # library's stream over every layer's weights
-    reps = 3
-    us, kbytes = d.time_kernel(qt.QT_KERNEL_GEMV_GATE_UP, reps)
+    if d.path == qt.QT_PATH_FRAME:
+        # dominant kernel: the persistent frame kernel, one launch per step;
+        # its average duration from the HIP events on the library's stream
+        # around the timed region (the step's id copies are on the same stream)
+        kname = "frame_kernel (persistent: every phase of a step's frames)"
+        us = gpu_s * 1e6 / args.steps
+        kbytes = fb * nf
+    else:
+        # dominant kernel: the gate/up GEMV, timed live with HIP events on the
+        # library's stream over every layer's weights
+        kname = "gemv_kernel<gated> (RMSNorm + gate/up + SiLU-mul)"
+        us, kbytes = d.time_kernel(qt.QT_KERNEL_GEMV_GATE_UP, 3)
     achieved = kbytes / (us * 1e-6) / 1e9
-    log(f"{frames / wall:.1f} frames/s, {ms_per_frame_step:.3f} ms per frame-step; "
-        f"gate/up GEMV {us:.2f} us/launch = {achieved:.0f} GB/s")
+    log(f"path {d.path}: {frames / wall:.1f} frames/s, {ms_per_frame_step:.3f} ms per frame-step; "
+        f"{kname}: {us:.1f} us/launch = {achieved:.0f} GB/s")
 
     res = {
         "metric": "codec frames/s (talker step + 15 predictor steps)",
@@ -158,11 +168,12 @@ def main():
         "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16"}[m.lin],
         "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
         "config": {"workload": wl.name, "batch": B, "prompt": wl.prompt, "frames_per_step": nf,
+                   "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[d.path],
                    "frames_per_replay": wl.frames_per_replay, "talker_layers": m.Lt,
                    "predictor_layers": m.Lp, "hidden": m.H},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemv_kernel<bf16, gated> (RMSNorm + gate/up + SiLU-mul)",
+                     "kernel": kname,
                      "bytes_per_launch": kbytes, "avg_launch_us": us},
         "frame_roofline": {"bytes_per_frame_step": fb, "ms_per_frame_step": ms_per_frame_step,
                            "achieved_gbs": fb / (ms_per_frame_step * 1e-3) / 1e9,

@@ -56,6 +56,10 @@ extern "C" {
 /* context flags */
 #define QT_F_DUMP 1u  /* keep per-step readbacks (logits, bridge, gather ids, hidden) */
 #define QT_F_EAGER 2u /* launch kernels directly instead of replaying a hipGraph */
+#define QT_F_OPS 4u   /* one kernel per op (hipGraph) even where the persistent
+                         frame kernel applies (single stream); for comparisons */
+#define QT_F_TRACE 8u /* persistent kernel: workgroup 0 stamps every phase of the
+                         first frame of a call (read with QT_DUMP_TRACE) */
 
 typedef struct qt_model_desc {
   int32_t hidden;              /* H: width of talker and predictor */
@@ -161,7 +165,10 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out);
 int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
                    const int32_t *text_ids);
 
-/* Decodes n_frames frames for all B slots as n_frames/K graph replays.
+/* Decodes n_frames frames for all B slots.  With one slot (B = 1) and a shape
+   the persistent kernel implements, one kernel launch runs every phase of the
+   frames (qt_path() reports which path a context uses); otherwise each K-frame
+   block is one replay of a graph of per-op kernels.
    overlay_ids: host [n][B] (frame f's talker step adds text_emb row
    overlay_ids[f][b]).  codes_out: host [n][B][G]: codes_out[f][b][0] is the
    talker's greedy code for frame f, [1..G-1] the predictor's.  forced_codes:
@@ -193,6 +200,10 @@ int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
      QT_DUMP_GATHER        i32 [B][G+1]      codes fed to the gather, overlay id
      QT_DUMP_TPOS          i32 [B]           talker K/V write position
      QT_DUMP_HIDDEN        f32 [Lt][B][H]    talker residual after each layer
+     QT_DUMP_TRACE         u64 [1024][8]     QT_F_TRACE only: per phase (kind | stack << 8 |
+                                             layer << 16 | step << 24, start, inputs in, end,
+                                             prologue done, weights in, dot products done, 0)
+                                             in 100 MHz wall-clock ticks; kind 255 ends it
    bytes must equal the kind's size.  Errors: QT_E_STATE, QT_E_ARG, QT_E_HIP. */
 #define QT_DUMP_TALKER_LOGITS 1
 #define QT_DUMP_PRED_LOGITS 2
@@ -201,6 +212,7 @@ int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
 #define QT_DUMP_GATHER 5
 #define QT_DUMP_TPOS 6
 #define QT_DUMP_HIDDEN 7
+#define QT_DUMP_TRACE 8
 int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
 
 /* Measurement hook: launches one kernel of the frame `reps` times, in the
@@ -213,10 +225,17 @@ int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
    state is untouched.  Synchronous.
      QT_KERNEL_GEMV_GATE_UP   RMSNorm + gate/up GEMV + SiLU-multiply (the
                               largest weight stream of a layer)
-   Errors: QT_E_ARG, QT_E_HIP. */
+   Errors: QT_E_ARG, QT_E_HIP, QT_E_UNSUPPORTED. */
 #define QT_KERNEL_GEMV_GATE_UP 1
 int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us,
                        double *bytes_per_launch);
+
+/* Decode path of a context: QT_PATH_FRAME (persistent frame kernel),
+   QT_PATH_GRAPH (per-op kernels replayed as a hipGraph) or QT_PATH_EAGER. */
+#define QT_PATH_FRAME 1
+#define QT_PATH_GRAPH 2
+#define QT_PATH_EAGER 3
+int32_t qt_path(const qt_ctx *ctx);
 
 /* Destroys graphs and host state; never frees caller memory.  NULL is a no-op. */
 void qt_free(qt_ctx *ctx);

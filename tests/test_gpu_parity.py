@@ -129,6 +129,7 @@ def tiny():
 
 def test_tiny_f32_parity(tiny):
     m, w, wl, r = tiny
+    assert r["d"].path == qt.QT_PATH_FRAME  # one stream: the persistent kernel
     _check(r, m, "tiny_f32")
     # F32: the oracle's codes come out free-running with no near ties
     assert np.array_equal(r["g"]["codes"], r["oout"]["codes"])
@@ -138,8 +139,9 @@ def test_tiny_graph_equals_eager_bitwise(tiny):
     m, w, wl, r = tiny
     c, t = r["prompts"][0]
     outs = []
-    for flags in (qt.QT_F_DUMP, qt.QT_F_DUMP | qt.QT_F_EAGER):
+    for flags in (qt.QT_F_DUMP | qt.QT_F_OPS, qt.QT_F_DUMP | qt.QT_F_EAGER):
         d = qt.Decoder(m, r["d"].dw, 1, flags=flags)
+        assert d.path == (qt.QT_PATH_GRAPH if flags & qt.QT_F_OPS else qt.QT_PATH_EAGER)
         d.prefill(0, c, t)
         codes = d.decode(8, r["ov"])
         outs.append((codes, d.dump(qt.QT_DUMP_TALKER_LOGITS), d.dump(qt.QT_DUMP_PRED_LOGITS),
@@ -182,7 +184,9 @@ def test_tiny_batched_equals_per_stream_and_permutation(tiny):
     assert np.array_equal(cp, cb[:, perm])
     assert np.array_equal(dp.dump(qt.QT_DUMP_PRED_LOGITS).view(np.uint32), lb[:, perm].view(np.uint32))
     for b in range(3):
-        d1 = qt.Decoder(m, r["d"].dw, 1, flags=qt.QT_F_DUMP)
+        # the same per-op kernels at batch 1 (the persistent kernel orders
+        # its reductions differently, so it is compared to the oracle instead)
+        d1 = qt.Decoder(m, r["d"].dw, 1, flags=qt.QT_F_DUMP | qt.QT_F_OPS)
         d1.prefill(0, *prompts[b])
         c1 = d1.decode(4, ov[:, b:b + 1])
         assert np.array_equal(c1[:, 0], cb[:, b])
@@ -193,6 +197,20 @@ def test_tiny_batched_equals_per_stream_and_permutation(tiny):
     for b, (c, t) in enumerate(prompts):
         o.prefill(b, c, t)
     assert np.array_equal(o.decode(4, ov)["codes"], cb)
+
+
+def test_tiny_frame_kernel_equals_op_graph_codes(tiny):
+    m, w, wl, r = tiny
+    c, t = r["prompts"][0]
+    out = {}
+    for flags in (0, qt.QT_F_OPS):
+        d = qt.Decoder(m, r["d"].dw, 1, flags=flags)
+        d.prefill(0, c, t)
+        out[flags] = (d.decode(8, r["ov"]), d.get_state(0))
+        d.close()
+    assert np.array_equal(out[0][0], out[qt.QT_F_OPS][0])
+    assert out[0][1][:2] == out[qt.QT_F_OPS][1][:2]
+    assert rel_l2(out[0][1][2], out[qt.QT_F_OPS][1][2]) < 1e-5
 
 
 def test_tiny_poisoned_ring_tail_and_predictor_cache(tiny):
