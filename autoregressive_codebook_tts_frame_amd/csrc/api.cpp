@@ -156,6 +156,7 @@ struct qt_ctx {
   hipGraphExec_t exec = nullptr;
   int32_t path = QT_PATH_GRAPH;
   qtk::FrameArgs fa;       // persistent kernel arguments (path == QT_PATH_FRAME)
+  int lds_limit = 0;       // LDS per workgroup on the device
   uint32_t tag_base = 1;   // running phase tag of the persistent kernel
   std::string err;
 
@@ -384,34 +385,12 @@ hipError_t enqueue_replay(qt_ctx *c) {
   return launch_advance(c->A<int32_t>(c->L.ctl), c->K, c->stream);
 }
 
-// Work split of each GEMV phase over nwg*4 waves; false if the persistent
-// kernel is not instantiated for it.
-bool frame_splits(const qt_model_desc &m, int nwg, Split (&sp)[SP_COUNT], const char **why) {
-  const Dims d = dims_of(m);
-  const int wt = wtype_of(m);
-  const int ch = wt == W_F32 ? 4 : (wt == W_BF16 ? 8 : 16);
-  const int tw = nwg * 4;
-  const int nk[SP_COUNT][3] = {{d.nqkv, d.H, 1}, {d.H, d.qd, 1}, {d.F, d.H, 2}, {d.H, d.F, 1}, {d.Vc, d.H, 1}};
-  for (int i = 0; i < SP_COUNT; ++i) {
-    const int N = nk[i][0], K = nk[i][1], nm = nk[i][2];
-    if (K % (64 * ch)) { *why = "a GEMV width is not a multiple of 64 lanes x 16 bytes"; return false; }
-    sp[i].rw = (int8_t)((N + tw - 1) / tw);
-    sp[i].nmat = (int8_t)nm;
-    sp[i].cpl = (int8_t)(K / (64 * ch));
-    if (!frame_split_supported(wt, sp[i])) { *why = "GEMV split not instantiated"; return false; }
-  }
-  return true;
-}
-
 const char *frame_unsupported(const qt_model_desc &m, int B) {
   const Dims d = dims_of(m);
   if (B != 1) return "the persistent kernel decodes one stream";
-  if (d.nq / d.nkv > 2) return "GQA group > 2";
-  if (d.H > 3072 || d.F > 3072 || d.qd > 3072 || d.hd > 128) return "width above 3072";
-  if (d.G > 32) return "more than 32 codebooks";
-  if (d.Lt + d.Lp > 40) return "more than 40 layers";
   if (!qtk::frame_variant_supported(wtype_of(m), d.hd, d.nq / d.nkv, m.kv_bf16)) return "no persistent-kernel variant";
-  if (m.lin_type != QT_LIN_F32 && !m.act_bf16) return "bf16/q8 weights with f32 matmul operands";
+  if (m.lin_type != QT_LIN_F32 && !(m.act_bf16 && m.tab_bf16)) return "bf16/q8 weights need bf16 operands and tables";
+  if (m.lin_type == QT_LIN_F32 && (m.act_bf16 || m.tab_bf16)) return "f32 weights need f32 operands and tables";
   return nullptr;
 }
 
@@ -558,20 +537,19 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
   if (!(c->flags & (QT_F_EAGER | QT_F_OPS)) && !frame_unsupported(m, c->B)) {
     int dev = 0, ncu = 0;
     const char *why = nullptr;
-    Split sp[SP_COUNT];
     int lds = 0;
+    qtk::FrameArgs &fa = c->fa;
+    fa = qtk::FrameArgs{};
+    fa.H = d.H; fa.nq = d.nq; fa.nkv = d.nkv; fa.hd = d.hd; fa.F = d.F; fa.Lt = d.Lt; fa.Lp = d.Lp;
+    fa.G = d.G; fa.Vc = d.Vc; fa.Vt = d.Vt; fa.P = d.P; fa.Q = d.Q;
+    fa.wt = wtype_of(m); fa.tab_bf16 = m.tab_bf16; fa.kv_bf16 = m.kv_bf16; fa.act_bf16 = m.act_bf16;
+    // the plan must fit for the longest context the ring holds
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
-        (size_t)lds >= qtk::frame_lds_bytes() && ncu > 0 && ncu <= kMaxWG && frame_splits(m, ncu, sp, &why)) {
-      qtk::FrameArgs &fa = c->fa;
-      fa = qtk::FrameArgs{};
-      fa.H = d.H; fa.nq = d.nq; fa.nkv = d.nkv; fa.hd = d.hd; fa.F = d.F; fa.Lt = d.Lt; fa.Lp = d.Lp;
-      fa.G = d.G; fa.Vc = d.Vc; fa.Vt = d.Vt; fa.P = d.P; fa.Q = d.Q;
-      fa.wt = wtype_of(m); fa.tab_bf16 = m.tab_bf16; fa.kv_bf16 = m.kv_bf16; fa.act_bf16 = m.act_bf16;
+        ncu > 0 && ncu <= kMaxWG && (fa.nwg = ncu, qtk::frame_plan(fa, d.P - 1, lds, &why))) {
+      c->lds_limit = lds;
       fa.eps = (float)m.eps; fa.scale = (float)(1.0 / sqrt((double)d.hd));
-      for (int i = 0; i < SP_COUNT; ++i) fa.split[i] = sp[i];
-      fa.nwg = ncu;
       // device-side weight tables
       std::vector<qtk::LayerDev> tl(d.Lt), pl(d.Lp);
       auto fill = [&](qtk::LayerDev &o, const qt_layer_weights &L) {
@@ -722,6 +700,10 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
       HIPCHK(c, hipMemcpyAsync(c->fa.err, zero, sizeof(int32_t), hipMemcpyHostToDevice, s));
       qtk::FrameArgs fa = c->fa;
       fa.n_frames = nf;
+      fa.pos0 = c->pos_host[0];
+      const char *why = nullptr;
+      if (!qtk::frame_plan(fa, fa.pos0 + nf - 1, c->lds_limit, &why))
+        return fail(c, QT_E_UNSUPPORTED, "frame kernel plan: %s", why);
       fa.tag_base = c->tag_base;
       // tags are only ever compared for equality: advance past every phase
       // this launch can number (< 1024 per frame)

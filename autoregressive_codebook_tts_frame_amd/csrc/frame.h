@@ -1,11 +1,12 @@
 // frame.h -- the persistent frame kernel (internal to libqt).
 //
-// One launch decodes n frames for one stream: every workgroup walks the same
+// One launch decodes n frames of one stream.  Every workgroup walks the same
 // phase schedule (15 code-predictor micro-steps of Lp layers, then the talker
-// step of Lt layers, per frame).  Phases hand data to each other through
-// tagged 64-bit words (tag | value) stored and loaded at agent scope, so a
-// consumer waits on the data itself; each workgroup keeps the next phase's
-// weight slice in flight in registers while it waits.
+// step of Lt layers, per frame).  The first n_attn workgroups run attention
+// only (one KV head and one tile of talker positions each, with that tile's
+// K/V held in LDS); the others run every projection, MLP and head as
+// weight-streaming GEMVs.  Phases hand data to each other through tagged
+// 64-bit words (tag | value) stored and loaded at agent scope.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -19,20 +20,19 @@ struct LayerDev {
 };
 enum { LW_Q = 0, LW_K, LW_V, LW_O, LW_G, LW_U, LW_D };
 
-// GEMV work split of one phase kind: output rows per wave, weight matrices per
-// output row (2 for gate/up), 16-byte chunks per lane per weight row.
-struct Split {
-  int8_t rw, nmat, cpl;
-};
-enum { SP_QKV = 0, SP_O, SP_GU, SP_D, SP_HEAD, SP_COUNT };
-
 struct FrameArgs {
   // shapes
   int32_t H, nq, nkv, hd, F, Lt, Lp, G, Vc, Vt, P, Q;
   int32_t wt, tab_bf16, kv_bf16, act_bf16;
   float eps, scale;
-  Split split[SP_COUNT];
-  int32_t nwg;
+  // launch plan (frame_plan)
+  int32_t nwg;         // workgroups, one per compute unit
+  int32_t n_attn;      // leading attention workgroups: kv head = wg % nkv, tile = wg / nkv
+  int32_t tile;        // talker positions per attention tile
+  int32_t max_tiles;   // tiles per head in the partial buffer
+  int32_t slot_bytes;  // LDS bytes of one weight slot
+  int32_t two_slots;   // 1: the next phase's weights stream in while this phase computes
+  int32_t lds_bytes;   // dynamic LDS per workgroup
   // weights
   const LayerDev *tl, *pl;                  // device arrays [Lt], [Lp]
   const void *code_emb, *text_emb, *t_norm, *p_norm;
@@ -47,13 +47,13 @@ struct FrameArgs {
   const float *rope_cos, *rope_sin;         // [P][hd/2]
   uint8_t *ring_t, *ring_p;                 // (slot 0, layer 0, K) of each stack
   int64_t t_layer_stride, t_kv_stride, p_layer_stride, p_kv_stride;  // elements
-  // tagged exchange buffers
-  uint64_t *xq;    // [2][H]
-  uint64_t *qkvb;  // [2][nqkv]
-  uint64_t *ob;    // [2][nq*hd]
-  uint64_t *zb;    // [2][F]
-  uint64_t *amax;  // [nwg][2]  (value | index) per workgroup
-  uint64_t *part;  // [nq][P/256][hd + 2]
+  // tagged exchange words
+  uint64_t *xq;    // [2][H]        residual stream rows
+  uint64_t *qkvb;  // [2][nqkv]     q | k | v rows
+  uint64_t *ob;    // [2][nq*hd]    attention output (bf16 pairs when act_bf16)
+  uint64_t *zb;    // [2][F]        SiLU-mul output (bf16 pairs when act_bf16)
+  uint64_t *amax;  // [nwg][2]      per-workgroup (value, index) of a head's argmax
+  uint64_t *part;  // [nq][max_tiles][hd + 2]  tile partials (o, max, sum)
   // outputs / dumps
   float *logits_t;  // [Vc]
   float *logits_p;  // [G-1][Vc]
@@ -61,18 +61,18 @@ struct FrameArgs {
   int32_t *gather_dump, *tpos_dump;
   int32_t dump;
   // control
+  int32_t pos0;       // talker position of the launch's first frame (the slot's position)
   int32_t n_frames;
   uint32_t tag_base;  // tags of this launch are tag_base + phase index (> 0)
-  int32_t *err;     // [0] set on a timed-out wait
-  uint64_t *trace;  // optional: [1024][8] phase stamps of workgroup 0, first frame
+  int32_t *err;       // [0] set on a timed-out wait
+  uint64_t *trace;    // optional: [1024][8] stamps (rows < 768: first GEMV workgroup; rest: attention workgroup 0)
 };
 
 hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s);
-// the (rows/wave, matrices, chunks/lane) triples the kernel is instantiated for
-bool frame_split_supported(int wt, const Split &sp);
 // the (weights, head dim, GQA group, bf16 ring) combinations instantiated
 bool frame_variant_supported(int wt, int hd, int g, int kv_bf16);
-// LDS the kernel needs per workgroup (dynamic shared memory)
-size_t frame_lds_bytes();
+// Plan a launch whose talker positions reach max_pos: attention workgroups,
+// tile, weight slots and LDS size.  False (with *why) if it does not fit.
+bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why);
 
 }  // namespace qtk

@@ -5,25 +5,32 @@
 // decodes) and per talker step, each layer is QKV -> attention -> O (+residual)
 // -> gate/up (+SiLU-mul) -> down (+residual), then a head whose argmax picks
 // the next code ([QT-tests] fused codec mode entry: in-graph sampler).  A
-// kernel launch per phase costs more than the phase's own HBM traffic, the
-// failure mode [MC-opt] (closing paragraph) reports for its engine, so one
-// launch runs every phase of n frames:
+// kernel launch per phase costs more than the phase's own HBM traffic (the
+// failure mode [MC-opt] reports in its closing paragraph), so one launch runs
+// every phase of n frames.  At batch 1 each phase is one exchange of a few KB
+// between all compute units, so the design works on exchange latency first:
 //
-//  * Every workgroup walks the same schedule.  A phase's outputs are 64-bit
-//    words (tag | value) written and read at agent scope; a consumer spins on
-//    the words it needs until their tag is the producing phase's, so no
-//    separate barrier or fence is needed.  Every wait is bounded: a timed-out
-//    wait raises a device error flag and the kernel drains.
-//  * Weight slices are prefetched into registers: right after a phase has its
-//    inputs, each lane issues the 16-byte loads of the next phase's slice, so
-//    the HBM stream overlaps the next exchange.
-//  * The argmax of a head is reduced redundantly by every workgroup from the
-//    workgroups' partial maxima, so every workgroup knows every code and builds
-//    the next input row (a code-table row, or the talker's 17-row gather-sum,
-//    [QT-log] AR inputs entry) itself.
-//  * The attention of one (KV head, 256-position tile) always runs on the same
-//    workgroup, so K/V rows a workgroup writes into the ring ([QT-log] set_rows
-//    entry) are only ever read back by that workgroup.
+//  * Two roles.  The first n_attn workgroups only run attention: workgroup
+//    (KV head kh, tile t) keeps the K/V rows of talker positions
+//    [256 t, 256 t + 256) of the layer it serves next in LDS (streamed in from
+//    the ring while the GEMV phases run) and, for t = 0, the 16-position
+//    code-predictor cache of its head.  The other workgroups run every
+//    projection, the MLP and the heads as GEMVs over their rows.
+//  * One exchange per phase.  A phase's outputs are 64-bit words
+//    (tag | value) stored at agent scope; a consumer loads all the words it
+//    needs at once and retries only those whose tag is not yet the producing
+//    phase's.  Every wait is bounded: a timed-out wait raises a device error
+//    flag and the kernel drains.
+//  * Weights stream through LDS.  Right after a GEMV workgroup has its
+//    inputs it issues direct-to-LDS loads of the next GEMV phase's weight
+//    slice (and norm gain) into the other of two slots, so the HBM stream
+//    overlaps this phase's compute and the next exchange.  These loads are
+//    issued from inline assembly: vector-memory counters complete in order,
+//    and the only waits on them are the exchange waits that follow.
+//  * Residuals and gathers stay local.  Each GEMV workgroup keeps the last
+//    residual row it read in LDS (the O and down epilogues add to it) and
+//    accumulates the talker's gather-sum ([QT-log] AR inputs entry) in
+//    registers as the predictor picks each code, in code order.
 #include <math.h>
 
 #include "frame.h"
@@ -33,61 +40,98 @@ namespace qtk {
 namespace {
 
 constexpr int NT = 256;
-constexpr int MAXC = 12;    // 16-byte weight chunks per lane per phase
-constexpr int KMAX = 3072;  // longest activation row
-constexpr int MAXLAYERS = 40;  // talker + predictor layers held in the LDS weight table
+constexpr int MAXLAYERS = 40;
 constexpr int MAXHEADS = 32;
-constexpr int PER = KMAX / NT;
+constexpr int PER = 8;          // tagged words per thread per poll round
+constexpr int HPAIR = 4;        // hidden pairs per thread (H <= 2 * NT * HPAIR)
+constexpr int MAXR = 64;        // GEMV rows per workgroup per phase
+constexpr int TILE = 256;       // talker positions per attention tile
 constexpr uint32_t SPIN_LIMIT = 1u << 21;
 
 enum { PH_QKV = 0, PH_ATTN, PH_COMB, PH_O, PH_GU, PH_D, PH_HEAD, PH_END };
 
 struct Ph {
-  int type, stack, layer, step, frame;  // stack 0 predictor, 1 talker; step = micro-step j
+  int type, stack, layer, step, frame;  // stack 0 predictor, 1 talker; step = micro-step
 };
 
-// Every global access goes through a global-address-space pointer: pointers
-// read out of the argument struct would otherwise be flat, and flat loads
-// also count against the LDS wait counter, which would make every LDS access
-// wait for the in-flight weight prefetch.
+// Every global access goes through a global-address-space pointer: flat
+// accesses would also count against the LDS wait counter.
 #define GAS __attribute__((address_space(1)))
 #define LAS __attribute__((address_space(3)))
 template <class T> __device__ __forceinline__ GAS T *gp(T *p) { return (GAS T *)p; }
 template <class T> __device__ __forceinline__ const GAS T *gp(const T *p) { return (const GAS T *)p; }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7f800000u) == 0x7f800000u) return __uint_as_float((u | ((u & 0x7fffffu) ? 0x400000u : 0u)) & 0xffff0000u);
   u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
   return __uint_as_float(u);
 }
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)(__float_as_uint(bf16_rne(f)) >> 16); }
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return __float_as_uint(bf16_rne(f)) >> 16; }
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+__device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-__device__ __forceinline__ float tab_at(const void *p, int bf16, size_t i) {
-  return bf16 ? __uint_as_float((uint32_t)gp((const uint16_t *)p)[i] << 16) : gp((const float *)p)[i];
+// Cross-lane reductions with DPP row operations (a row is 16 lanes) and
+// readlane for the four row results: a few VALU cycles per step, where a
+// shuffle chain would go through the LDS crossbar once per step.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+__device__ __forceinline__ float row16_sum(float v) {  // every lane gets its row's sum
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
   return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+__device__ __forceinline__ float wave_sum(float v) {  // uniform result
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+// greedy pick: larger value wins, the lower index on ties
+__device__ __forceinline__ void pick(float &bv, int &bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void pick_dpp(float &bv, int &bi) {
+  pick(bv, bi, dpp<CTRL>(bv), __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ void wave_argmax(float &bv, int &bi) {  // uniform result
+  pick_dpp<0xB1>(bv, bi);
+  pick_dpp<0x4E>(bv, bi);
+  pick_dpp<0x124>(bv, bi);
+  pick_dpp<0x128>(bv, bi);
+  float v = lane_f(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
+  pick(v, i, lane_f(bv, 16), __builtin_amdgcn_readlane(bi, 16));
+  pick(v, i, lane_f(bv, 32), __builtin_amdgcn_readlane(bi, 32));
+  pick(v, i, lane_f(bv, 48), __builtin_amdgcn_readlane(bi, 48));
+  bv = v;
+  bi = i;
 }
 
-// phase tags run on across launches (tag_base advances per launch), so a tag
-// is never reused while a buffer could still hold it
-__device__ __forceinline__ uint32_t mktag(uint32_t base, uint32_t seq) { return base + seq; }
-__device__ __forceinline__ void tput(uint64_t *p, float v, uint32_t tag) {
-  __hip_atomic_store(gp(p), ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void tput_u(uint64_t *p, uint32_t v, uint32_t tag) {
+template <class T> __device__ __forceinline__ T ld(const T *p) { return *gp(p); }
+template <class T> __device__ __forceinline__ void st(T *p, T v) { *gp(p) = v; }
+
+// tagged words: tags run on across launches (tag_base advances per launch)
+__device__ __forceinline__ void tput(uint64_t *p, uint32_t v, uint32_t tag) {
   __hip_atomic_store(gp(p), ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void tputf(uint64_t *p, float v, uint32_t tag) { tput(p, __float_as_uint(v), tag); }
 __device__ __forceinline__ uint64_t tget(const uint64_t *p) {
   return __hip_atomic_load(gp(const_cast<uint64_t *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -97,53 +141,110 @@ __device__ __forceinline__ int err_get(const int32_t *e) {
 __device__ __forceinline__ void err_set(int32_t *e) {
   __hip_atomic_store(gp(e), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <class T> __device__ __forceinline__ T ld(const T *p) { return *gp(p); }
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-template <> __device__ __forceinline__ uint4 ld<uint4>(const uint4 *p) {
-  const u32x4 v = *gp((const u32x4 *)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
+// ring rows: 8-byte words at agent scope, so the tile loads below (which
+// bypass the caches the same way) see them
+__device__ __forceinline__ void ring_put(uint8_t *p, uint64_t v) {
+  __hip_atomic_store(gp((uint64_t *)p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <class T> __device__ __forceinline__ void st(T *p, T v) { *gp(p) = v; }
 
-// Weight pointers of every layer and head, copied into LDS at kernel start:
-// computing a weight address must not wait on a vector-memory load, because
-// that wait would also cover (in order) the prefetch loads already in flight.
+// One 16-byte-per-lane direct-to-LDS load: lane l's bytes land at
+// lds_base + 16 l.  coherent: load at agent scope (ring rows).
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(src)
+      : "memory");
+}
+__device__ __forceinline__ void dma16_coherent(const void *src, uint32_t lds_base) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off sc1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(src)
+      : "memory");
+}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const LAS void *)p;
+}
+
+// Weight pointers of every layer and head, copied into LDS at kernel start.
 struct LayerTab {
   const void *w[7];
   const uint16_t *sc[7];
   const void *attn_norm, *q_norm, *k_norm, *mlp_norm;
 };
 
-struct Shared {
-  // next phase's weight slice, loaded straight from HBM into LDS (per wave,
-  // per chunk, per lane) so it never occupies registers while in flight
-  uint4 wbuf[4][MAXC][64];
-  uint16_t sbuf[4][MAXC][64];  // q8 block scales of those chunks
+struct Common {
   LayerTab lt[MAXLAYERS];  // talker layers then predictor layers
   const void *head_w[MAXHEADS];
   const uint16_t *head_sc[MAXHEADS];
-  float x[2][KMAX];   // phase input rows (prologue applied)
-  float bridge[KMAX]; // talker final-normed hidden (next frame's predictor row 0)
-  float q[4][128], k[2][128], v[2][128];
-  float sc[4][256];
   float red[4][8];
-  float stat[4][2];
-  float res[4][24];   // per wave: reduced GEMV outputs
-  float xold[4][8];   // per wave: residual words of its rows
   float amv[4];
   int ami[4];
-  int codes[256];     // codes fed to this frame's gathers
-  int code;           // resolved argmax
+  int codes[MAXHEADS];  // codes fed to this frame's gathers
+  int code;
   int abort;
 };
 
+// Offsets (bytes) of each role's LDS buffers; one function for host and device.
+struct Lds {
+  uint32_t xres, opnd, res, slot0, slot1, g_end;                        // GEMV role
+  uint32_t gq, gk, rc, rs, rowbuf, sc, stat, pvred, comb, kv, a_end;    // attention role
+};
+__host__ __device__ inline uint32_t up16(uint32_t v) { return (v + 15u) & ~15u; }
+__host__ __device__ inline uint32_t up1k(uint32_t v) { return (v + 1023u) & ~1023u; }
+__host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ inline Lds lds_layout(const FrameArgs &a) {
+  Lds L;
+  const uint32_t base = up16(sizeof(Common));
+  // GEMV role
+  const int kop = imax(a.H, imax(a.nq * a.hd, a.F));
+  const int opw = imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg);
+  L.xres = base;
+  L.opnd = up16(L.xres + 2u * a.H * 4u);
+  L.res = up16(L.opnd + 2u * opw * 4u);
+  L.slot0 = up1k(L.res + MAXR * 4u * 4u);
+  L.slot1 = L.slot0 + (a.two_slots ? (uint32_t)a.slot_bytes : 0u);
+  L.g_end = L.slot1 + a.slot_bytes;
+  // attention role (G query heads per KV head)
+  const int g = a.nq / a.nkv, hd = a.hd;
+  const uint32_t rowb = (uint32_t)hd * (a.kv_bf16 ? 2u : 4u);
+  L.gq = base;
+  L.gk = L.gq + hd * 4u;
+  L.rc = L.gk + hd * 4u;
+  L.rs = L.rc + hd * 4u;  // [2][hd/2] each
+  // attention scratch and the tile-merge buffer are never live together
+  L.rowbuf = up16(L.rs + hd * 4u);
+  L.sc = up16(L.rowbuf + 2u * (g + 2) * hd * 4u);
+  L.stat = up16(L.sc + (uint32_t)g * a.tile * 4u);
+  L.pvred = up16(L.stat + 4u * g * 4u);
+  L.comb = L.rowbuf;
+  const uint32_t scratch_end = up16(L.pvred + 4u * g * hd * 4u);
+  const uint32_t comb_end = L.comb + (uint32_t)g * a.max_tiles * (hd + 2) * 4u;
+  L.kv = up1k(scratch_end > comb_end ? scratch_end : comb_end);
+  const uint32_t tile_b = 2u * a.tile * rowb, pc_b = (uint32_t)a.Lp * 2u * a.Q * rowb;
+  L.a_end = L.kv + up1k(tile_b > pc_b ? tile_b : pc_b);
+  return L;
+}
+
 // ------------------------------------------------------------ schedule
 
-__device__ __forceinline__ Ph next_phase(const FrameArgs &a, const Ph &p, bool multi_tile) {
+__device__ __forceinline__ int ntiles_at(int p) { return p / TILE + 1; }
+
+__device__ __forceinline__ Ph next_phase(const FrameArgs &a, const Ph &p, int pos0) {
   Ph n = p;
   switch (p.type) {
     case PH_QKV: n.type = PH_ATTN; break;
-    case PH_ATTN: n.type = (p.stack == 1 && multi_tile) ? PH_COMB : PH_O; break;
+    case PH_ATTN: n.type = (p.stack == 1 && ntiles_at(pos0 + p.frame) > 1) ? PH_COMB : PH_O; break;
     case PH_COMB: n.type = PH_O; break;
     case PH_O: n.type = PH_GU; break;
     case PH_GU: n.type = PH_D; break;
@@ -156,7 +257,7 @@ __device__ __forceinline__ Ph next_phase(const FrameArgs &a, const Ph &p, bool m
       n.type = PH_QKV;
       if (p.stack == 0) {
         if (p.step + 1 < a.G - 1) n.step = p.step + 1;
-        else { n.stack = 1; n.step = -1; }
+        else { n.stack = 1; n.step = 0; }
       } else {
         n.stack = 0; n.step = 0; n.frame = p.frame + 1;
         if (n.frame >= a.n_frames) n.type = PH_END;
@@ -166,29 +267,107 @@ __device__ __forceinline__ Ph next_phase(const FrameArgs &a, const Ph &p, bool m
   }
   return n;
 }
+__device__ __forceinline__ Ph next_gemv_phase(const FrameArgs &a, Ph p, int pos0) {
+  do p = next_phase(a, p, pos0);
+  while (p.type == PH_ATTN || p.type == PH_COMB);
+  return p;
+}
+__device__ __forceinline__ const LayerTab &tab_of(const FrameArgs &a, const Common &cm, int stack, int layer) {
+  return cm.lt[stack ? layer : a.Lt + layer];
+}
 
-__device__ __forceinline__ int split_of(int type) {
-  switch (type) {
-    case PH_QKV: return SP_QKV;
-    case PH_O: return SP_O;
-    case PH_GU: return SP_GU;
-    case PH_D: return SP_D;
-    case PH_HEAD: return SP_HEAD;
-    default: return -1;
+// ------------------------------------------------------------ exchange
+
+// Poll n tagged words (word i at src(i)) until each carries tag; value bits
+// -> *dst(i) (LDS).  All threads; false on timeout.
+template <class Dst, class Src>
+__device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Dst dst, Src src) {
+  for (int b0 = 0; b0 < n; b0 += PER * NT) {
+    uint64_t v[PER];
+    uint32_t pend = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = b0 + (int)threadIdx.x + k * NT;
+      if (i < n) { v[k] = tget(src(i)); pend |= 1u << k; }
+    }
+    for (uint32_t spins = 0;; ++spins) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        if (((pend >> k) & 1u) && (uint32_t)(v[k] >> 32) == tag) {
+          *dst(b0 + threadIdx.x + k * NT) = (uint32_t)v[k];
+          pend &= ~(1u << k);
+        }
+      if (!pend) break;
+      if (spins > SPIN_LIMIT || ((spins & 255u) == 255u && err_get(a.err))) {
+        err_set(a.err);
+        return false;
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        if ((pend >> k) & 1u) v[k] = tget(src(b0 + threadIdx.x + k * NT));
+    }
   }
+  return true;
+}
+__device__ __forceinline__ bool poll_lin(const FrameArgs &a, const uint64_t *src, int n, uint32_t tag, uint32_t *dst) {
+  return poll(a, n, tag, [=](int i) { return dst + i; }, [=](int i) { return src + i; });
+}
+// rows of w words at src (contiguous) into LDS rows of stride dw
+__device__ __forceinline__ bool poll_rows(const FrameArgs &a, const uint64_t *src, int rows, int w, uint32_t tag,
+                                          uint32_t *dst, int dw) {
+  return poll(a, rows * w, tag, [=](int i) { const int m = i / w; return dst + m * dw + (i - m * w); },
+              [=](int i) { return src + i; });
 }
 
-__device__ __forceinline__ const LayerTab &tab_of(const FrameArgs &a, const Shared &sh, const Ph &p) {
-  return sh.lt[p.stack ? p.layer : a.Lt + p.layer];
+__device__ __forceinline__ float block_sum(Common &cm, float v) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) cm.red[wave][0] = v;
+  __syncthreads();
+  return (cm.red[0][0] + cm.red[1][0]) + (cm.red[2][0] + cm.red[3][0]);
 }
 
-// weight row (and its q8 scales) of output row n, matrix mat, for phase p
-__device__ __forceinline__ void row_of(const FrameArgs &a, const Shared &sh, const Ph &p, int n, int mat,
-                                       int K, const uint8_t *&w, const uint16_t *&sc) {
-  const size_t esz = a.wt == W_F32 ? 4 : (a.wt == W_BF16 ? 2 : 1);
-  const LayerTab &T = tab_of(a, sh, p);
-  int which = 0, r = n;
+// ------------------------------------------------------------ GEMV role
+
+// Row share of GEMV workgroup gi among NG: rows [r0, r0 + R), in pairs.
+struct Share {
+  int r0, R, N, K, NM;
+};
+__device__ __forceinline__ Share share_of(const FrameArgs &a, int type, int gi, int NG) {
+  Share s;
+  const int qd = a.nq * a.hd;
+  s.NM = 1;
+  switch (type) {
+    case PH_QKV: s.N = qd + 2 * a.nkv * a.hd; s.K = a.H; break;
+    case PH_O: s.N = a.H; s.K = qd; break;
+    case PH_GU: s.N = a.F; s.K = a.H; s.NM = 2; break;
+    case PH_D: s.N = a.H; s.K = a.F; break;
+    default: s.N = a.Vc; s.K = a.H; break;
+  }
+  const int np = s.N / 2;
+  const int p0 = (int)(((long)np * gi) / NG), p1 = (int)(((long)np * (gi + 1)) / NG);
+  s.r0 = 2 * p0;
+  s.R = 2 * (p1 - p0);
+  return s;
+}
+
+template <int WT> struct WEsz;
+template <> struct WEsz<W_F32> { static constexpr int v = 4; };
+template <> struct WEsz<W_BF16> { static constexpr int v = 2; };
+template <> struct WEsz<W_Q8> { static constexpr int v = 1; };
+
+// weight row (and q8 scale row) of output row n, matrix mat
+__device__ __forceinline__ void wrow_of(const FrameArgs &a, const Common &cm, const Ph &p, int n, int mat,
+                                        int K, int esz, const uint8_t *&w, const uint8_t *&sc) {
   const int qd = a.nq * a.hd, kd = a.nkv * a.hd;
+  int which = 0, r = n;
+  if (p.type == PH_HEAD) {
+    const int hi = p.stack ? 0 : 1 + p.step;
+    w = (const uint8_t *)cm.head_w[hi] + (size_t)n * K * esz;
+    sc = cm.head_sc[hi] ? (const uint8_t *)(cm.head_sc[hi] + (size_t)n * (K / 32)) : nullptr;
+    return;
+  }
   switch (p.type) {
     case PH_QKV:
       if (n < qd) which = LW_Q;
@@ -197,61 +376,57 @@ __device__ __forceinline__ void row_of(const FrameArgs &a, const Shared &sh, con
       break;
     case PH_O: which = LW_O; break;
     case PH_GU: which = mat ? LW_U : LW_G; break;
-    case PH_D: which = LW_D; break;
-    default: {  // head
-      const int hi = p.stack ? 0 : 1 + p.step;
-      w = (const uint8_t *)sh.head_w[hi] + (size_t)n * K * esz;
-      sc = sh.head_sc[hi] ? sh.head_sc[hi] + (size_t)n * (K / 32) : nullptr;
-      return;
-    }
+    default: which = LW_D; break;
   }
+  const LayerTab &T = tab_of(a, cm, p.stack, p.layer);
   w = (const uint8_t *)T.w[which] + (size_t)r * K * esz;
-  sc = T.sc[which] ? T.sc[which] + (size_t)r * (K / 32) : nullptr;
+  sc = T.sc[which] ? (const uint8_t *)(T.sc[which] + (size_t)r * (K / 32)) : nullptr;
+}
+__device__ __forceinline__ const void *gain_of(const FrameArgs &a, const Common &cm, const Ph &p) {
+  if (p.type == PH_QKV) return tab_of(a, cm, p.stack, p.layer).attn_norm;
+  if (p.type == PH_GU) return tab_of(a, cm, p.stack, p.layer).mlp_norm;
+  if (p.type == PH_HEAD) return p.stack ? a.t_norm : a.p_norm;
+  return nullptr;
+}
+// slot layout: weights [R*NM rows], q8 scales [R*NM][K/32] (1 KB aligned), gain [H]
+__device__ __forceinline__ uint32_t scales_off(const Share &s, int esz) { return (uint32_t)(s.R * s.NM) * s.K * esz; }
+__device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool q8) {
+  return scales_off(s, esz) + (q8 ? up1k((uint32_t)(s.R * s.NM) * (s.K / 16)) : 0u);
 }
 
-__device__ __forceinline__ void phase_nk(const FrameArgs &a, int type, int &N, int &K) {
-  const int qd = a.nq * a.hd;
-  switch (type) {
-    case PH_QKV: N = qd + 2 * a.nkv * a.hd; K = a.H; break;
-    case PH_O: N = a.H; K = qd; break;
-    case PH_GU: N = a.F; K = a.H; break;
-    case PH_D: N = a.H; K = a.F; break;
-    default: N = a.Vc; K = a.H; break;
+// Issue the direct-to-LDS loads of phase p's weight slice (+ scales, gain).
+template <int WT>
+__device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, const Ph &p, int gi, int NG,
+                                       uint32_t slot) {
+  constexpr int ESZ = WEsz<WT>::v;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const Share s = share_of(a, p.type, gi, NG);
+  const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
+  int b = 0;
+  for (int u = 0; u < U; ++u) {
+    const uint8_t *w, *sc;
+    wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
+    for (int cb = 0; cb < bpr; ++cb, ++b)
+      if ((b & 3) == wave) dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
   }
-}
-
-// ------------------------------------------------------------ GEMV pieces
-
-template <int WT> struct CHK_;
-template <> struct CHK_<W_F32> { static constexpr int v = 4; };
-template <> struct CHK_<W_BF16> { static constexpr int v = 8; };
-template <> struct CHK_<W_Q8> { static constexpr int v = 16; };
-
-template <int WT, int RW, int NM, int CPL>
-__device__ __forceinline__ void prefetch_t(const FrameArgs &a, Shared &sh, const Ph &p, int gw, int lane) {
-  constexpr int CH = CHK_<WT>::v;
-  const int wave = gw & 3;
-  int N, K;
-  phase_nk(a, p.type, N, K);
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int n = gw * RW + r;  // uniform across the wave
-    if (n >= N) continue;
-#pragma unroll
-    for (int mat = 0; mat < NM; ++mat) {
-      const uint8_t *w;
-      const uint16_t *sc;
-      row_of(a, sh, p, n, mat, K, w, sc);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int i = (r * NM + mat) * CPL + c;
-        const int kc = c * 64 + lane;
-        // lane l's 16 bytes land at wbuf[wave][i][l]
-        __builtin_amdgcn_global_load_lds((const GAS void *)(w + (size_t)kc * 16), (LAS void *)&sh.wbuf[wave][i][0], 16, 0, 0);
-        if constexpr (WT == W_Q8)
-          __builtin_amdgcn_global_load_lds((const GAS void *)(sc + kc * CH / 32), (LAS void *)&sh.sbuf[wave][i][0], 2, 0, 0);
+  if constexpr (WT == W_Q8) {
+    const int spu = s.K / 256, n = U * spu;  // 16-byte scale chunks per row, in all
+    const uint32_t so = scales_off(s, ESZ);
+    for (int sb = 0; sb * 64 < n; ++sb, ++b)
+      if ((b & 3) == wave) {
+        const int idx = min(sb * 64 + lane, n - 1);
+        const int u = idx / spu, k = idx - u * spu;
+        const uint8_t *w, *sc;
+        wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
+        dma16(sc + k * 16, slot + so + (uint32_t)sb * 1024u);
       }
-    }
+  }
+  const void *g = gain_of(a, cm, p);
+  if (g) {
+    const int n = a.H * (a.tab_bf16 ? 2 : 4) / 16;
+    const uint32_t go = gain_off(s, ESZ, WT == W_Q8);
+    for (int gb = 0; gb * 64 < n; ++gb, ++b)
+      if ((b & 3) == wave) dma16((const uint8_t *)g + min(gb * 64 + lane, n - 1) * 16, slot + go + (uint32_t)gb * 1024u);
   }
 }
 
@@ -259,819 +434,772 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), c, false);
 }
-// two int8 (bytes b, b+1 of w) as a bf16 pair (exact: |q| <= 127)
-__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int b) {
+// int8 bytes b, b+1 of w as a bf16 pair (exact: |q| <= 127)
+__device__ __forceinline__ uint32_t i8pair(uint32_t w, int b) {
   const float lo = (float)(int8_t)(w >> (8 * b)), hi = (float)(int8_t)(w >> (8 * b + 8));
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
-// bf16 / q8 weights: the operand row is packed bf16 in LDS (xb), one dot2
-// per weight pair; f32 weights keep the float path
+// 16-byte weight chunk c of a row . operand row (LDS)
 template <int WT>
-__device__ __forceinline__ float chunk_dot2(const uint4 w, const uint32_t *xb, uint32_t s16) {
+__device__ __forceinline__ float chunk_dot(uint4 w, const uint32_t *op, int c, const uint8_t *scl) {
   if constexpr (WT == W_BF16) {
-    const uint4 x = *(const uint4 *)xb;
-    float s = dot2(w.x, x.x, 0.f);
-    s = dot2(w.y, x.y, s);
-    s = dot2(w.z, x.z, s);
-    s = dot2(w.w, x.w, s);
-    return s;
+    const uint4 x = ((const uint4 *)op)[c];
+    return dot2(w.w, x.w, dot2(w.z, x.z, dot2(w.y, x.y, dot2(w.x, x.x, 0.f))));
+  } else if constexpr (WT == W_Q8) {
+    const uint4 x0 = ((const uint4 *)op)[2 * c], x1 = ((const uint4 *)op)[2 * c + 1];
+    float s = dot2(i8pair(w.x, 0), x0.x, 0.f);
+    s = dot2(i8pair(w.x, 2), x0.y, s);
+    s = dot2(i8pair(w.y, 0), x0.z, s);
+    s = dot2(i8pair(w.y, 2), x0.w, s);
+    s = dot2(i8pair(w.z, 0), x1.x, s);
+    s = dot2(i8pair(w.z, 2), x1.y, s);
+    s = dot2(i8pair(w.w, 0), x1.z, s);
+    s = dot2(i8pair(w.w, 2), x1.w, s);
+    return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
   } else {
-    const uint4 x0 = *(const uint4 *)xb, x1 = *(const uint4 *)(xb + 4);
-    float s = dot2(i8pair_bf16(w.x, 0), x0.x, 0.f);
-    s = dot2(i8pair_bf16(w.x, 2), x0.y, s);
-    s = dot2(i8pair_bf16(w.y, 0), x0.z, s);
-    s = dot2(i8pair_bf16(w.y, 2), x0.w, s);
-    s = dot2(i8pair_bf16(w.z, 0), x1.x, s);
-    s = dot2(i8pair_bf16(w.z, 2), x1.y, s);
-    s = dot2(i8pair_bf16(w.w, 0), x1.z, s);
-    s = dot2(i8pair_bf16(w.w, 2), x1.w, s);
-    return s * f16_to_f32(s16);
+    const float4 x = ((const float4 *)op)[c];
+    return __uint_as_float(w.x) * x.x + __uint_as_float(w.y) * x.y + __uint_as_float(w.z) * x.z +
+           __uint_as_float(w.w) * x.w;
   }
 }
 
+// res[u * M + m] = row u of the slot . operand row m; rows spread over the waves
 template <int WT>
-__device__ __forceinline__ float chunk_dot(const uint4 w, const float *x, uint32_t s16) {
-  if constexpr (WT == W_F32) {
-    const float4 xv = *(const float4 *)x;
-    return __uint_as_float(w.x) * xv.x + __uint_as_float(w.y) * xv.y + __uint_as_float(w.z) * xv.z +
-           __uint_as_float(w.w) * xv.w;
-  } else if constexpr (WT == W_BF16) {
-    const float4 x0 = *(const float4 *)x, x1 = *(const float4 *)(x + 4);
-    float s = bf16_lo(w.x) * x0.x;
-    s += bf16_hi(w.x) * x0.y;
-    s += bf16_lo(w.y) * x0.z;
-    s += bf16_hi(w.y) * x0.w;
-    s += bf16_lo(w.z) * x1.x;
-    s += bf16_hi(w.z) * x1.y;
-    s += bf16_lo(w.w) * x1.z;
-    s += bf16_hi(w.w) * x1.w;
-    return s;
-  } else {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 xv = *(const float4 *)(x + 4 * i);
-      s += (float)(int8_t)(ws[i]) * xv.x;
-      s += (float)(int8_t)(ws[i] >> 8) * xv.y;
-      s += (float)(int8_t)(ws[i] >> 16) * xv.z;
-      s += (float)(int8_t)(ws[i] >> 24) * xv.w;
-    }
-    return s * f16_to_f32(s16);
-  }
-}
-
-// reduced results -> sh.res[wave][(r * NM + mat) * M + m] (all lanes hold them)
-template <int WT, int RW, int NM, int CPL, int M>
-__device__ __forceinline__ void gemv_t(Shared &sh, int lane, int wave) {
-  constexpr int CH = CHK_<WT>::v;
-  float acc[RW * NM][M];
-#pragma unroll
-  for (int i = 0; i < RW * NM; ++i)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
-#pragma unroll
-  for (int rm = 0; rm < RW * NM; ++rm)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int i = rm * CPL + c;
-      const int k0 = (c * 64 + lane) * CH;
-      const uint4 wv = sh.wbuf[wave][i][lane];
-      const uint32_t sv = WT == W_Q8 ? (uint32_t)sh.sbuf[wave][i][lane] : 0u;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        if constexpr (WT == W_F32) acc[rm][m] += chunk_dot<WT>(wv, &sh.x[m][k0], sv);
-        else acc[rm][m] += chunk_dot2<WT>(wv, (const uint32_t *)&sh.x[m][0] + k0 / 2, sv);
-      }
-      // keep one chunk's operands live at a time: hoisting every chunk's LDS
-      // reads would spill the prefetched weights of the next phase
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-  for (int rm = 0; rm < RW * NM; ++rm)
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float v = wave_sum(acc[rm][m]);
-      if (lane == 0) sh.res[wave][rm * M + m] = v;
-    }
-}
-
-#define QT_SPLITS(X)                                                                     \
-  X(W_F32, 1, 1, 1) X(W_F32, 1, 2, 1) X(W_F32, 1, 1, 3)                                  \
-  X(W_BF16, 4, 1, 2) X(W_BF16, 1, 1, 4) X(W_BF16, 3, 2, 2) X(W_BF16, 1, 1, 6) X(W_BF16, 2, 1, 2) \
-  X(W_Q8, 4, 1, 1) X(W_Q8, 1, 1, 2) X(W_Q8, 3, 2, 1) X(W_Q8, 1, 1, 3) X(W_Q8, 2, 1, 1)
-
-template <int WT>
-__device__ __forceinline__ void prefetch_any(const FrameArgs &a, Shared &sh, const Ph &p, int gw, int lane) {
-  const int si = split_of(p.type);
-  if (si < 0) return;
-  const Split sp = a.split[si];
-#define X(W, R, N, C) \
-  if (WT == W && sp.rw == R && sp.nmat == N && sp.cpl == C) { prefetch_t<W, R, N, C>(a, sh, p, gw, lane); return; }
-  QT_SPLITS(X)
-#undef X
-}
-
-template <int WT>
-__device__ __forceinline__ void gemv_any(const FrameArgs &a, int type, int M, Shared &sh, int lane, int wave) {
-  const Split sp = a.split[split_of(type)];
-#define X(W, R, N, C)                                                                     \
-  if (WT == W && sp.rw == R && sp.nmat == N && sp.cpl == C) {                            \
-    if (M == 1) gemv_t<W, R, N, C, 1>(sh, lane, wave);                                    \
-    else gemv_t<W, R, N, C, 2>(sh, lane, wave);                                           \
-    return;                                                                              \
-  }
-  QT_SPLITS(X)
-#undef X
-}
-
-// ------------------------------------------------------------ exchange
-
-// n tagged words src[0..n) with tag -> dst (LDS floats); all threads; false on timeout
-__device__ __forceinline__ bool acquire(const FrameArgs &a, const uint64_t *src, int n, uint32_t tag, float *dst) {
-  uint64_t v[PER];
-  uint32_t pend = 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i < n) {
-      v[k] = tget(src + i);
-      pend |= 1u << k;
-    }
-  }
-  for (uint32_t spins = 0;; ++spins) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-      if ((pend >> k) & 1u) {
-        if ((uint32_t)(v[k] >> 32) == tag) {
-          dst[threadIdx.x + k * NT] = __uint_as_float((uint32_t)v[k]);
-          pend &= ~(1u << k);
-        }
-      }
-    if (!pend) return true;
-    if (spins > SPIN_LIMIT || ((spins & 1023u) == 1023u && err_get(a.err))) {
-      err_set(a.err);
-      return false;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-      if ((pend >> k) & 1u) v[k] = tget(src + threadIdx.x + k * NT);
-  }
-}
-
-// one tagged word (single lane); false on timeout
-__device__ __forceinline__ bool acquire1(const FrameArgs &a, const uint64_t *src, uint32_t tag, uint32_t &out) {
-  uint64_t v = tget(src);
-  for (uint32_t spins = 0; (uint32_t)(v >> 32) != tag; ++spins) {
-    if (spins > SPIN_LIMIT || ((spins & 1023u) == 1023u && err_get(a.err))) {
-      err_set(a.err);
-      return false;
-    }
-    v = tget(src);
-  }
-  out = (uint32_t)v;
-  return true;
-}
-
-// block-wide sum of per-thread values (fixed order)
-__device__ __forceinline__ float block_sum(Shared &sh, float v, int slot) {
-  v = wave_sum(v);
+__device__ __forceinline__ void gemv_slice(const uint8_t *slot, const uint32_t *opnd, int opw, const Share &s, int M,
+                                        float *res) {
+  constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) sh.red[wave][slot] = v;
-  __syncthreads();
-  return (sh.red[0][slot] + sh.red[1][slot]) + (sh.red[2][slot] + sh.red[3][slot]);
-}
-
-// RMSNorm rows of sh.x in place: x <- act(x / rms(x) * g); keep optional f32 copy
-__device__ __forceinline__ void norm_rows(const FrameArgs &a, Shared &sh, int M, int K, const void *gain, float *keep) {
-  for (int m = 0; m < M; ++m) {
-    float s = 0.f;
-    for (int i = threadIdx.x; i < K; i += NT) s += sh.x[m][i] * sh.x[m][i];
-    s = block_sum(sh, s, m);
-    const float r = 1.0f / sqrtf(s / (float)K + a.eps);
-    for (int i = threadIdx.x; i < K; i += NT) {
-      const float y = sh.x[m][i] * r * tab_at(gain, a.tab_bf16, i);
-      if (keep) keep[i] = y;
-      sh.x[m][i] = a.act_bf16 ? bf16_rne(y) : y;
+  const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
+  const uint8_t *scb = slot + scales_off(s, ESZ);
+  for (int u = wave; u < U; u += 4) {
+    const uint8_t *wr = slot + (size_t)u * rowb;
+    const uint8_t *scl = scb + (size_t)u * (s.K / 16);
+    float a0 = 0.f, a1 = 0.f;
+    for (int cb = 0; cb < bpr; ++cb) {
+      const int c = cb * 64 + lane;
+      const uint4 w = ((const uint4 *)wr)[c];
+      a0 += chunk_dot<WT>(w, opnd, c, scl);
+      if (M > 1) a1 += chunk_dot<WT>(w, opnd + opw, c, scl);
+    }
+    a0 = wave_sum(a0);
+    if (M > 1) a1 = wave_sum(a1);
+    if (lane == 0) {
+      res[u * M] = a0;
+      if (M > 1) res[u * M + 1] = a1;
     }
   }
-  __syncthreads();
 }
 
-__device__ __forceinline__ void act_rows(const FrameArgs &a, Shared &sh, int M, int K) {
-  if (a.act_bf16)
-    for (int m = 0; m < M; ++m)
-      for (int i = threadIdx.x; i < K; i += NT) sh.x[m][i] = bf16_rne(sh.x[m][i]);
-  __syncthreads();
-}
-
-// ------------------------------------------------------------ attention
-
-// Ring rows are read and written as 8-byte words at agent scope (4 bf16 or 2
-// f32 per word): the code-predictor cache is rewritten every frame by the same
-// workgroup that reads it, and these accesses never see a stale cached line.
-template <bool KVB>
-__device__ __forceinline__ void unpack8(uint64_t w, float *v) {
-  if constexpr (KVB) {
-    v[0] = __uint_as_float((uint32_t)(w << 16) & 0xffff0000u);
-    v[1] = __uint_as_float((uint32_t)w & 0xffff0000u);
-    v[2] = __uint_as_float((uint32_t)(w >> 16) & 0xffff0000u);
-    v[3] = __uint_as_float((uint32_t)(w >> 32) & 0xffff0000u);
-  } else {
-    v[0] = __uint_as_float((uint32_t)w);
-    v[1] = __uint_as_float((uint32_t)(w >> 32));
-  }
-}
-template <bool KVB>
-__device__ __forceinline__ uint64_t pack8(const float *v) {
-  if constexpr (KVB)
-    return (uint64_t)bf16_bits(v[0]) | ((uint64_t)bf16_bits(v[1]) << 16) |
-           ((uint64_t)bf16_bits(v[2]) << 32) | ((uint64_t)bf16_bits(v[3]) << 48);
-  else
-    return (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
-}
-__device__ __forceinline__ void ring_put(uint64_t *p, uint64_t v) {
-  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One (KV head kh, tile t) attention unit for rows at positions pos0, pos1
-// (M <= 2).  HD head dim, G query heads per KV head, KVB bf16 ring.
-template <int HD, int G, bool KVB>
-__device__ __forceinline__ bool attention_unit(const FrameArgs &a, Shared &sh, const Ph &p, int kh,
-                                               int t, int M, int pos0, int pos1, uint32_t tag_in,
-                                               uint32_t tag_out, int ntiles, int tile) {
-  constexpr int VPW = KVB ? 4 : 2;   // values per 8-byte word
-  constexpr int WPR = HD / VPW;      // words per ring row
-  constexpr int NGRP = NT / WPR;     // position groups of the P.V loop
-  constexpr int HALF = HD / 2;
-  const int qd = a.nq * HD, kd = a.nkv * HD;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int P = p.stack ? a.P : a.Q;
-  const int64_t kvs_w = (p.stack ? a.t_kv_stride : a.p_kv_stride) / VPW;
-  uint64_t *ring = (uint64_t *)((p.stack ? a.ring_t : a.ring_p) +
-                                (size_t)p.layer * (p.stack ? a.t_layer_stride : a.p_layer_stride) * (KVB ? 2 : 4));
-  const size_t head_w = (size_t)kh * P * WPR;
-  const LayerTab &T = tab_of(a, sh, p);
-  const void *qn = T.q_norm, *kn = T.k_norm;
-  const int nqkv = qd + 2 * kd;
-  for (int m = 0; m < M; ++m) {
-    const int pm = m ? pos1 : pos0;
-    const int j0 = t * tile;
-    if (j0 > pm) continue;  // uniform across the block
-    const int jn = min(tile, pm + 1 - j0);
-    // q (G heads), k, v of this KV head, row m
-    const uint64_t *row = a.qkvb + (size_t)m * nqkv;
-    bool ok = acquire(a, row + kh * G * HD, G * HD, tag_in, &sh.sc[0][0]);
-    ok = ok && acquire(a, row + qd + kh * HD, HD, tag_in, &sh.sc[2][0]);
-    ok = ok && acquire(a, row + qd + kd + kh * HD, HD, tag_in, &sh.sc[3][0]);
-    if (!ok) sh.abort = 1;
-    __syncthreads();
-    if (sh.abort) return false;
-    // q/k norm + RoPE: wave w < G handles q head w, wave G the k head; lanes own pairs
-    if (wave <= G) {
-      const float *src = wave < G ? &sh.sc[0][wave * HD] : &sh.sc[2][0];
-      const void *gain = wave < G ? qn : kn;
-      const bool act = lane < HALF;
-      const float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + HALF] : 0.f;
-      const float s = wave_sum(x0 * x0 + x1 * x1);
-      const float rv = 1.0f / sqrtf(s / (float)HD + a.eps);
-      if (act) {
-        const float y0 = x0 * rv * tab_at(gain, a.tab_bf16, lane);
-        const float y1 = x1 * rv * tab_at(gain, a.tab_bf16, lane + HALF);
-        const float c = ld(a.rope_cos + (size_t)pm * HALF + lane), sn = ld(a.rope_sin + (size_t)pm * HALF + lane);
-        const float o0 = y0 * c - y1 * sn, o1 = y1 * c + y0 * sn;
-        float *dst = wave < G ? sh.q[wave] : sh.k[0];
-        dst[lane] = o0;
-        dst[lane + HALF] = o1;
-      }
-    }
-    for (int i = tid; i < HD; i += NT) sh.v[0][i] = sh.sc[3][i];
-    __syncthreads();
-    // the tile holding this row's position writes its K/V rows (set_rows)
-    if (pm < j0 + tile && tid < 2 * WPR) {
-      const int wi = tid % WPR;
-      const bool isv = tid >= WPR;
-      ring_put(ring + head_w + (isv ? kvs_w : 0) + (size_t)pm * WPR + wi,
-               pack8<KVB>((isv ? sh.v[0] : sh.k[0]) + wi * VPW));
-    }
-    __syncthreads();
-    // scores: one thread per position of the tile; positions past pm are
-    // excluded by select and their rows never read
-    if (tid < tile) {
-      if (tid < jn) {
-        const uint64_t *kr = ring + head_w + (size_t)(j0 + tid) * WPR;
-        uint64_t kw[WPR];
+// RMSNorm of residual row x (LDS f32) with gain g (LDS, table type) -> operand
+// row (bf16 pairs or f32); y kept in yk[] (pair layout) when asked
+template <int WT>
+__device__ __forceinline__ void norm_row(const FrameArgs &a, Common &cm, const float *x, const uint8_t *g,
+                                         uint32_t *op, float (&yk)[2 * HPAIR], bool keep) {
+  const int H = a.H, tid = threadIdx.x;
+  float ss = 0.f;
+  for (int i = tid; i < H; i += NT) ss += x[i] * x[i];
+  ss = block_sum(cm, ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + a.eps);
 #pragma unroll
-        for (int wi = 0; wi < WPR; ++wi) kw[wi] = tget(kr + wi);
-        float s[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[g] = 0.f;
-#pragma unroll
-        for (int wi = 0; wi < WPR; ++wi) {
-          float kv[4];
-          unpack8<KVB>(kw[wi], kv);
-#pragma unroll
-          for (int i = 0; i < VPW; ++i)
-#pragma unroll
-            for (int g = 0; g < G; ++g) s[g] += sh.q[g][wi * VPW + i] * kv[i];
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) sh.sc[g][tid] = s[g] * a.scale;
+  for (int k = 0; k < HPAIR; ++k) {
+    const int pi = tid + k * NT;
+    if (2 * pi < H) {
+      float g0, g1;
+      if (a.tab_bf16) {
+        const uint32_t gw = ((const uint32_t *)g)[pi];
+        g0 = lo16(gw); g1 = hi16(gw);
       } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) sh.sc[g][tid] = -INFINITY;
+        g0 = ((const float *)g)[2 * pi]; g1 = ((const float *)g)[2 * pi + 1];
+      }
+      const float y0 = x[2 * pi] * r * g0, y1 = x[2 * pi + 1] * r * g1;
+      if (keep) { yk[2 * k] = y0; yk[2 * k + 1] = y1; }
+      if constexpr (WT == W_F32) {
+        ((float *)op)[2 * pi] = a.act_bf16 ? bf16_rne(y0) : y0;
+        ((float *)op)[2 * pi + 1] = a.act_bf16 ? bf16_rne(y1) : y1;
+      } else {
+        op[pi] = pack2(y0, y1);
       }
     }
-    __syncthreads();
+  }
+}
+
+// table row (bf16 or f32) element pairs of this thread -> v[2 * HPAIR]
+__device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, size_t row, float *v) {
+  const int tid = threadIdx.x;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float v = tid < tile ? sh.sc[g][tid] : -INFINITY;
-      v = wave_max(v);
-      if (lane == 0) sh.red[wave][g] = v;
+  for (int k = 0; k < HPAIR; ++k) {
+    const int pi = tid + k * NT;
+    if (2 * pi < a.H) {
+      if (a.tab_bf16) {
+        const uint32_t w = ld((const uint32_t *)((const uint16_t *)tab + row * a.H) + pi);
+        v[2 * k] = lo16(w); v[2 * k + 1] = hi16(w);
+      } else {
+        const uint64_t f = ld((const uint64_t *)((const float *)tab + row * a.H) + pi);
+        v[2 * k] = __uint_as_float((uint32_t)f); v[2 * k + 1] = __uint_as_float((uint32_t)(f >> 32));
+      }
     }
-    __syncthreads();
-    if (tid < G) sh.stat[tid][0] = fmaxf(fmaxf(sh.red[0][tid], sh.red[1][tid]), fmaxf(sh.red[2][tid], sh.red[3][tid]));
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float e = 0.f;
-      if (tid < jn) e = expf(sh.sc[g][tid] - sh.stat[g][0]);
-      if (tid < tile) sh.sc[g][tid] = e;
-      e = wave_sum(e);
-      if (lane == 0) sh.red[wave][4 + g] = e;
+  }
+}
+
+// argmax over the workgroups' partial maxima of the head with tag; lowest index wins ties
+__device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uint32_t *scratch, int NG, uint32_t tag) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool ok = poll_lin(a, a.amax, 2 * NG, tag, scratch);
+  __syncthreads();  // each thread reduces words other threads polled
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if (ok)
+    for (int w = tid; w < NG; w += NT) {
+      const float fv = __uint_as_float(scratch[2 * w]);
+      const int ix = (int)scratch[2 * w + 1];
+      if (fv > bv || (fv == bv && ix < bi)) { bv = fv; bi = ix; }
     }
+  wave_argmax(bv, bi);
+  if (lane == 0) { cm.amv[wave] = bv; cm.ami[wave] = bi; }
+  if (!ok) cm.abort = 1;
+  __syncthreads();
+  if (tid == 0) {
+    float b2 = cm.amv[0];
+    int i2 = cm.ami[0];
+    for (int w = 1; w < 4; ++w)
+      if (cm.amv[w] > b2 || (cm.amv[w] == b2 && cm.ami[w] < i2)) { b2 = cm.amv[w]; i2 = cm.ami[w]; }
+    cm.code = i2 == 0x7fffffff ? 0 : i2;
+  }
+  __syncthreads();
+  return !cm.abort;
+}
+
+template <int WT>
+__device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *smem) {
+  constexpr int ESZ = WEsz<WT>::v;
+  Common &cm = *reinterpret_cast<Common *>(smem);
+  const Lds L = lds_layout(a);
+  float *xres = (float *)(smem + L.xres);   // [2][H] residual rows
+  uint32_t *opnd = (uint32_t *)(smem + L.opnd);
+  float *res = (float *)(smem + L.res);
+  const uint32_t slot_lds0 = lds_addr(smem + L.slot0), slot_lds1 = lds_addr(smem + L.slot1);
+  const int kop = imax(a.H, imax(a.nq * a.hd, a.F));
+  const int opw = imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg);  // words per operand row
+  const int tid = threadIdx.x;
+  const int gi = (int)blockIdx.x - a.n_attn, NG = a.nwg - a.n_attn;
+  const int H = a.H, G = a.G;
+  const int force = ld(a.ctl + 1);
+  const int pos0 = a.pos0;
+  int c0 = ld(a.c0);
+  const bool lead = gi == 0;  // writes state, codes and dumps
+
+  float brg[2 * HPAIR], tacc[2 * HPAIR], trow[2 * HPAIR];
+#pragma unroll
+  for (int k = 0; k < 2 * HPAIR; ++k) { brg[k] = 0.f; tacc[k] = 0.f; trow[k] = 0.f; }
+#pragma unroll
+  for (int k = 0; k < HPAIR; ++k) {
+    const int pi = tid + k * NT;
+    if (2 * pi < H) { brg[2 * k] = ld(a.bridge + 2 * pi); brg[2 * k + 1] = ld(a.bridge + 2 * pi + 1); }
+  }
+
+  Ph cur{PH_QKV, 0, 0, 0, 0};
+  uint32_t seq = 1;
+  int slot = 0;
+  bool pending = false;  // the previous GEMV phase was a head
+  int pending_idx = 0;   // the code index it decides (0: next frame's code 0)
+  int ntr = 0;
+  bool first = true;
+
+  while (cur.type != PH_END) {
+    const Ph nxt = next_phase(a, cur, pos0);
+    if (cur.type == PH_ATTN || cur.type == PH_COMB) { ++seq; cur = nxt; continue; }
+    const bool tracing = a.trace && lead && cur.frame == 0 && ntr < 767;
+    uint64_t t0 = tracing ? wall_clock64() : 0;
+    const uint32_t tag = a.tag_base + seq, tagp = tag - 1;
+    const int f = cur.frame;
+    const int pos = pos0 + f;
+    const int M = (cur.stack == 0 && cur.step == 0 && cur.type != PH_HEAD) ? 2 : 1;
+    const Share s = share_of(a, cur.type, gi, NG);
+    const Ph ng = next_gemv_phase(a, cur, pos0);
+    // inputs of this phase -> xres (residual rows) or opnd (operand rows)
+    auto inputs = [&]() -> bool {
+      bool ok = true;
+      if (cur.type == PH_QKV && cur.layer == 0) {
+        if (pending) {
+          if (!resolve_code(a, cm, opnd, NG, tagp)) return false;
+          const int c = cm.code;
+          if (pending_idx == 0) c0 = c;
+          else {
+            int32_t *ci = a.cin + (size_t)f * G + pending_idx;
+            if (lead && tid == 0) {
+              st(a.cout + (size_t)f * G + pending_idx, c);
+              if (!force) st(ci, c);
+            }
+            if (tid == 0) cm.codes[pending_idx] = force ? ld(ci) : c;
+          }
+          pending = false;
+        }
+        float row[2 * HPAIR];
+        if (cur.stack == 0 && cur.step == 0) {
+          // frame start: code 0 of the frame, rows [bridge, E_0[code 0]]
+          int32_t *ci = a.cin + (size_t)f * G;
+          if (lead && tid == 0) {
+            st(a.cout + (size_t)f * G, c0);
+            if (!force) st(ci, c0);
+          }
+          if (tid == 0) cm.codes[0] = force ? ld(ci) : c0;
+          __syncthreads();
+          tab_pairs(a, a.code_emb, (size_t)cm.codes[0], row);
+          tab_pairs(a, a.text_emb, (size_t)ld(a.overlay + f), trow);
+  #pragma unroll
+          for (int k = 0; k < HPAIR; ++k) {
+            const int pi = tid + k * NT;
+            if (2 * pi < H) {
+              xres[2 * pi] = brg[2 * k]; xres[2 * pi + 1] = brg[2 * k + 1];
+              xres[H + 2 * pi] = row[2 * k]; xres[H + 2 * pi + 1] = row[2 * k + 1];
+            }
+            tacc[2 * k] = 0.f + row[2 * k];
+            tacc[2 * k + 1] = 0.f + row[2 * k + 1];
+          }
+        } else if (cur.stack == 0) {
+          __syncthreads();
+          tab_pairs(a, a.code_emb, (size_t)cur.step * a.Vc + cm.codes[cur.step], row);
+  #pragma unroll
+          for (int k = 0; k < HPAIR; ++k) {
+            const int pi = tid + k * NT;
+            if (2 * pi < H) { xres[2 * pi] = row[2 * k]; xres[2 * pi + 1] = row[2 * k + 1]; }
+            tacc[2 * k] += row[2 * k];
+            tacc[2 * k + 1] += row[2 * k + 1];
+          }
+        } else {
+          // talker input: the frame's G code rows, then the overlay row, in order
+          __syncthreads();
+          tab_pairs(a, a.code_emb, (size_t)(G - 1) * a.Vc + cm.codes[G - 1], row);
+  #pragma unroll
+          for (int k = 0; k < HPAIR; ++k) {
+            const int pi = tid + k * NT;
+            const float v0 = (tacc[2 * k] + row[2 * k]) + trow[2 * k];
+            const float v1 = (tacc[2 * k + 1] + row[2 * k + 1]) + trow[2 * k + 1];
+            if (2 * pi < H) {
+              xres[2 * pi] = v0; xres[2 * pi + 1] = v1;
+              if (a.dump && lead) { st(a.x0_dump + 2 * pi, v0); st(a.x0_dump + 2 * pi + 1, v1); }
+            }
+          }
+          if (a.dump && lead && tid <= G) st(a.gather_dump + tid, tid < G ? cm.codes[tid] : ld(a.overlay + f));
+          if (a.dump && lead && tid == 0) st(a.tpos_dump, pos);
+        }
+      } else if (cur.type == PH_QKV || cur.type == PH_GU) {
+        ok = poll_lin(a, a.xq, M * H, tagp, (uint32_t *)xres);
+      } else if (cur.type == PH_HEAD) {
+        const int mrow = cur.stack == 0 && cur.step == 0 ? 1 : 0;
+        ok = poll_lin(a, a.xq + (size_t)mrow * H, H, tagp, (uint32_t *)xres);
+      } else if (cur.type == PH_O) {
+        const int w = a.act_bf16 ? a.nq * a.hd / 2 : a.nq * a.hd;
+        ok = poll_rows(a, a.ob, M, w, tagp, opnd, opw);
+      } else {  // PH_D
+        const int w = a.act_bf16 ? a.F / 2 : a.F;
+        ok = poll_rows(a, a.zb, M, w, tagp, opnd, opw);
+      }
+      return ok;
+    };
+    // Weight slices: with two slots, the first phase loads its own slice
+    // before its inputs and every phase loads the next one's right after its
+    // inputs are in; with one slot, each phase loads its own before its inputs.
+    bool ok = true;
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool before = pass == 0;
+      const bool go = before ? (first || !a.two_slots) : (a.two_slots && ng.type != PH_END);
+      const bool to_slot1 = before ? slot != 0 : slot == 0;  // this phase's slot, else the other one
+      if (go) dma_slice<WT>(a, cm, before ? cur : ng, gi, NG, to_slot1 ? slot_lds1 : slot_lds0);
+      if (!before) break;
+      ok = inputs();
+      if (!ok) cm.abort = 1;
+      wait_vm();  // this phase's slice (usually landed long before: the polls waited in order)
+      __syncthreads();
+      if (cm.abort) return;
+    }
+    first = false;
+    const uint64_t t1 = tracing ? wall_clock64() : 0;
+    const uint64_t c1 = tracing ? __builtin_amdgcn_s_memtime() : 0;
+
+    // ---- prologue: RMSNorm into the operand rows
+    const uint8_t *sp = smem + (slot ? L.slot1 : L.slot0);
+    if (cur.type == PH_QKV || cur.type == PH_GU || cur.type == PH_HEAD) {
+      const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
+      const bool talker_head = cur.type == PH_HEAD && cur.stack == 1;
+      for (int m = 0; m < M; ++m) norm_row<WT>(a, cm, xres + m * H, gain, opnd + m * opw, brg, talker_head);
+      if (talker_head && lead) {
+#pragma unroll
+        for (int k = 0; k < HPAIR; ++k) {
+          const int pi = tid + k * NT;
+          if (2 * pi < H) { st(a.bridge + 2 * pi, brg[2 * k]); st(a.bridge + 2 * pi + 1, brg[2 * k + 1]); }
+        }
+      }
+      __syncthreads();
+    }
+    const uint64_t t2 = tracing ? wall_clock64() : 0;
+    const uint64_t c2 = tracing ? __builtin_amdgcn_s_memtime() : 0;
+    gemv_slice<WT>(sp, opnd, opw, s, M, res);
     __syncthreads();
-    if (tid < G) sh.stat[tid][1] = (sh.red[0][4 + tid] + sh.red[1][4 + tid]) + (sh.red[2][4 + tid] + sh.red[3][4 + tid]);
-    // P.V: thread (group, word) accumulates positions j = group, group+NGRP, ...
-    {
-      const int wi = tid % WPR, grp = tid / WPR;
-      float acc[G][VPW];
+    const uint64_t t3 = tracing ? wall_clock64() : 0;
+
+    // ---- epilogue: publish this workgroup's rows
+    if (cur.type == PH_QKV) {
+      const int N = s.N;
+      for (int i = tid; i < s.R * M; i += NT) {
+        const int j = i / M, m = i - j * M;
+        tputf(a.qkvb + (size_t)m * N + s.r0 + j, res[j * M + m], tag);
+      }
+    } else if (cur.type == PH_O || cur.type == PH_D) {
+      for (int i = tid; i < s.R * M; i += NT) {
+        const int j = i / M, m = i - j * M, n = s.r0 + j;
+        const float v = xres[m * H + n] + res[j * M + m];
+        tputf(a.xq + (size_t)m * H + n, v, tag);
+        if (cur.type == PH_D && cur.stack == 1 && a.dump) st(a.hidden_dump + (size_t)cur.layer * H + n, v);
+      }
+    } else if (cur.type == PH_GU) {
+      // z = SiLU(g) * u, rounded as the down projection's operand
+      if (a.act_bf16) {
+        for (int i = tid; i < (s.R / 2) * M; i += NT) {
+          const int pp = i / M, m = i - pp * M;
+          float z[2];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+          for (int e = 0; e < 2; ++e) {
+            const int j = 2 * pp + e;
+            const float g = res[(2 * j) * M + m], u = res[(2 * j + 1) * M + m];
+            z[e] = g / (1.0f + expf(-g)) * u;
+          }
+          tput(a.zb + (size_t)m * (a.F / 2) + s.r0 / 2 + pp, pack2(z[0], z[1]), tag);
+        }
+      } else {
+        for (int i = tid; i < s.R * M; i += NT) {
+          const int j = i / M, m = i - j * M;
+          const float g = res[(2 * j) * M + m], u = res[(2 * j + 1) * M + m];
+          tputf(a.zb + (size_t)m * a.F + s.r0 + j, g / (1.0f + expf(-g)) * u, tag);
+        }
+      }
+    } else {  // PH_HEAD: logits and this workgroup's partial argmax
+      float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      if (tid < 64) {
+        for (int j = tid; j < s.R; j += 64) {
+          const float v = res[j];
+          st(lg + s.r0 + j, v);
+          if (v > bv || (v == bv && s.r0 + j < bi)) { bv = v; bi = s.r0 + j; }
+        }
+        wave_argmax(bv, bi);
+        if (tid == 0) {
+          tputf(a.amax + 2 * gi, bv, tag);
+          tput(a.amax + 2 * gi + 1, (uint32_t)bi, tag);
+        }
+      }
+      pending = true;
+      pending_idx = cur.stack ? 0 : cur.step + 1;
+    }
+    if (tracing && tid == 0) {
+      uint64_t *tr = a.trace + 8 * ntr;
+      st(tr, (uint64_t)cur.type | ((uint64_t)cur.stack << 8) | ((uint64_t)cur.layer << 16) |
+                 ((uint64_t)(cur.step & 0xff) << 24));
+      st(tr + 1, t0);
+      st(tr + 2, t1);
+      st(tr + 3, (uint64_t)wall_clock64());
+      st(tr + 4, t2);
+      st(tr + 5, t3);
+      st(tr + 6, c1);  // shader-clock cycles around the norm
+      st(tr + 7, c2);
+    }
+    if (tracing) ++ntr;
+    if (a.two_slots) slot ^= 1;
+    ++seq;
+    cur = nxt;
+  }
+  if (a.trace && lead && tid == 0) st(a.trace + 8 * ntr, (uint64_t)255);
+  // the code picked by the last talker head becomes the slot's pending code 0
+  if (lead) {
+    if (pending) {
+      if (!resolve_code(a, cm, opnd, NG, a.tag_base + seq - 1)) return;
+      if (tid == 0) st(a.c0, cm.code);
+    }
+    if (tid == 0) st(a.pos, pos0 + a.n_frames);
+  }
+}
+
+// ------------------------------------------------------------ attention role
+
+// An attention event of workgroup (kh, t): predictor (frame, step, layer) or
+// talker (frame, layer).
+struct Ev {
+  int valid, stack, frame, step, layer;
+};
+__device__ __forceinline__ Ev first_event(const FrameArgs &a, int t, int pos0) {
+  if (t == 0) return Ev{1, 0, 0, 0, 0};
+  const int f = imax(0, t * TILE - pos0);
+  return Ev{f < a.n_frames, 1, f, 0, 0};
+}
+__device__ __forceinline__ Ev next_event(const FrameArgs &a, Ev e, int t) {
+  if (e.stack == 0) {
+    if (e.layer + 1 < a.Lp) { ++e.layer; return e; }
+    if (e.step + 1 < a.G - 1) { ++e.step; e.layer = 0; return e; }
+    e.stack = 1; e.layer = 0; e.step = 0;
+    return e;
+  }
+  if (e.layer + 1 < a.Lt) { ++e.layer; return e; }
+  e.frame += 1;
+  e.layer = 0;
+  e.valid = e.frame < a.n_frames;
+  if (t == 0) e.stack = 0;
+  return e;
+}
+
+template <bool KVB> struct KvT;
+template <> struct KvT<true> { static constexpr int esz = 2; };
+template <> struct KvT<false> { static constexpr int esz = 4; };
+
+// K/V chunk (16 bytes) -> floats
+template <bool KVB>
+__device__ __forceinline__ void unpack16(uint4 w, float *v) {
+  if constexpr (KVB) {
+    v[0] = lo16(w.x); v[1] = hi16(w.x); v[2] = lo16(w.y); v[3] = hi16(w.y);
+    v[4] = lo16(w.z); v[5] = hi16(w.z); v[6] = lo16(w.w); v[7] = hi16(w.w);
+  } else {
+    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+  }
+}
+
+template <int HD, int GQ, bool KVB>
+__device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *smem) {
+  constexpr int ESZ = KvT<KVB>::esz;
+  constexpr int ROWB = HD * ESZ;           // bytes per K/V row
+  constexpr int DPC = 16 / ESZ;            // dims per 16-byte chunk
+  constexpr int CPR = HD / DPC;            // chunks per row (lanes per position)
+  constexpr int PG = NT / CPR;             // position groups
+  constexpr int W = (GQ + 2) * HD;         // q | k | v words of one row
+  static_assert(CPR == 16, "K/V rows of 256 bytes");
+  Common &cm = *reinterpret_cast<Common *>(smem);
+  const Lds L = lds_layout(a);
+  float *rowbuf = (float *)(smem + L.rowbuf);  // [2][GQ + 2][HD]
+  float *gq = (float *)(smem + L.gq), *gk = (float *)(smem + L.gk);
+  float *rc = (float *)(smem + L.rc), *rs = (float *)(smem + L.rs);  // [2][HD/2]
+  float *sc = (float *)(smem + L.sc);          // [GQ][tile]
+  float *stat = (float *)(smem + L.stat);      // [GQ][2] max, sum
+  float *pvred = (float *)(smem + L.pvred);    // [4][GQ][HD]
+  uint8_t *kv = smem + L.kv;
+  const uint32_t kv_lds = lds_addr(kv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wg = blockIdx.x;
+  const int kh = wg % a.nkv, t = wg / a.nkv, ts = t * TILE;
+  const int qd = a.nq * HD, kd = a.nkv * HD, nqkv = qd + 2 * kd;
+  const int pos0 = a.pos0;
+  const int maxT = a.max_tiles;
+  const int pg = tid / CPR, cc = tid % CPR;
+
+  // load gains and RoPE rows for event e, then (talker) its K/V tile
+  auto prep = [&](const Ev &e) {
+    const LayerTab &T = tab_of(a, cm, e.stack, e.layer);
+    for (int i = tid; i < HD; i += NT) {
+      gq[i] = a.tab_bf16 ? lo16((uint32_t)ld((const uint16_t *)T.q_norm + i)) : ld((const float *)T.q_norm + i);
+      gk[i] = a.tab_bf16 ? lo16((uint32_t)ld((const uint16_t *)T.k_norm + i)) : ld((const float *)T.k_norm + i);
+    }
+    const int p0 = e.stack ? pos0 + e.frame : (e.step == 0 ? 0 : e.step + 1);
+    for (int i = tid; i < HD; i += NT) {
+      const int m = i / (HD / 2), d = i % (HD / 2);
+      const int pm = m ? 1 : p0;
+      rc[i] = ld(a.rope_cos + (size_t)pm * (HD / 2) + d);
+      rs[i] = ld(a.rope_sin + (size_t)pm * (HD / 2) + d);
+    }
+    wait_vm();
+    __syncthreads();
+    if (e.stack == 1) {
+      // rows [ts, min(p, ts + tile)) of the layer's K and V for this head
+      const int p = pos0 + e.frame;
+      const int nv = min(p, ts + TILE) - ts;
+      if (nv > 0) {
+        const size_t hoff = (size_t)e.layer * a.t_layer_stride + (size_t)kh * a.P * HD + (size_t)ts * HD;
+        const uint8_t *srcK = a.ring_t + hoff * ESZ;
+        const uint8_t *srcV = a.ring_t + (hoff + a.t_kv_stride) * ESZ;
+        const int n = nv * ROWB / 16;  // chunks per matrix
+        for (int b = wave; b * 64 < n; b += 4) {
+          const int idx = min(b * 64 + lane, n - 1);
+          dma16_coherent(srcK + (size_t)idx * 16, kv_lds + (uint32_t)b * 1024u);
+          dma16_coherent(srcV + (size_t)idx * 16, kv_lds + (uint32_t)(TILE * ROWB) + (uint32_t)b * 1024u);
+        }
+      }
+    }
+  };
+
+  Ev ev = first_event(a, t, pos0);
+  if (ev.valid) prep(ev);
+  Ph cur{PH_QKV, 0, 0, 0, 0};
+  uint32_t seq = 1;
+  int ntr = 0;
+  while (cur.type != PH_END) {
+    const Ph nxt = next_phase(a, cur, pos0);
+    const uint32_t tag = a.tag_base + seq, tagp = tag - 1;
+    const bool mine = ev.valid && cur.type == PH_ATTN && cur.stack == ev.stack && cur.frame == ev.frame &&
+                      cur.layer == ev.layer && (cur.stack == 1 || cur.step == ev.step);
+    if (mine) {
+      const bool tracing = a.trace && wg == 0 && cur.frame == 0 && ntr < 255;
+      const uint64_t t0 = tracing ? wall_clock64() : 0;
+      const int p = pos0 + cur.frame;
+      const int M = (cur.stack == 0 && cur.step == 0) ? 2 : 1;
+      const int ntile = cur.stack ? ntiles_at(p) : 1;
+      // ---- q | k | v rows of this KV head
+      uint32_t *rb = (uint32_t *)rowbuf;
+      const bool ok = poll(a, M * W, tagp, [=](int i) { return rb + i; }, [=](int i) {
+        const int m = i / W, r = i - m * W;
+        const int off = r < GQ * HD ? kh * GQ * HD + r
+                        : r < (GQ + 1) * HD ? qd + kh * HD + (r - GQ * HD)
+                                            : qd + kd + kh * HD + (r - (GQ + 1) * HD);
+        return a.qkvb + (size_t)m * nqkv + off;
+      });
+      if (!ok) cm.abort = 1;
+      wait_vm();  // the tile's loads (long landed: the poll waited in order)
+      __syncthreads();
+      if (cm.abort) return;
+      const uint64_t t1 = tracing ? wall_clock64() : 0;
+      // ---- q/k RMSNorm + RoPE (NeoX halves): one wave per (row, head)
+      for (int it = wave; it < M * (GQ + 1); it += 4) {
+        const int m = it / (GQ + 1), h = it % (GQ + 1);
+        float *v = rowbuf + (size_t)m * W + h * HD;
+        const float *g = h < GQ ? gq : gk;
+        const bool act = lane < HD / 2;
+        const float x0 = act ? v[lane] : 0.f, x1 = act ? v[lane + HD / 2] : 0.f;
+        const float ssum = wave_sum(x0 * x0 + x1 * x1);
+        const float r = 1.0f / sqrtf(ssum / (float)HD + a.eps);
+        if (act) {
+          const float y0 = x0 * r * g[lane], y1 = x1 * r * g[lane + HD / 2];
+          const float c = rc[m * (HD / 2) + lane], sn = rs[m * (HD / 2) + lane];
+          v[lane] = y0 * c - y1 * sn;
+          v[lane + HD / 2] = y1 * c + y0 * sn;
+        }
+      }
+      __syncthreads();
+      // ---- the new K/V rows (set_rows) into LDS and the ring
+      uint8_t *kbase, *vbase;
+      int base;  // position of LDS row 0
+      if (cur.stack) {
+        kbase = kv; vbase = kv + TILE * ROWB; base = ts;
+      } else {
+        kbase = kv + (size_t)cur.layer * 2 * a.Q * ROWB; vbase = kbase + (size_t)a.Q * ROWB; base = 0;
+      }
+      const bool owner = cur.stack == 0 || p < ts + TILE;
+      if (owner) {
+        for (int i = tid; i < M * 2 * (ROWB / 8); i += NT) {
+          const int m = i / (2 * (ROWB / 8)), r = i % (2 * (ROWB / 8));
+          const int isv = r >= ROWB / 8, wi = r % (ROWB / 8);
+          const int pm = cur.stack ? p : (cur.step == 0 ? m : cur.step + 1);
+          const float *src = rowbuf + (size_t)m * W + (GQ + isv) * HD + wi * (8 / ESZ);
+          uint64_t word;
+          if constexpr (KVB)
+            word = (uint64_t)pack2(src[0], src[1]) | ((uint64_t)pack2(src[2], src[3]) << 32);
+          else
+            word = (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32);
+          *(uint64_t *)((isv ? vbase : kbase) + (size_t)(pm - base) * ROWB + wi * 8) = word;
+          uint8_t *ring;
+          if (cur.stack)
+            ring = a.ring_t + ((size_t)cur.layer * a.t_layer_stride + (size_t)isv * a.t_kv_stride +
+                               (size_t)kh * a.P * HD + (size_t)pm * HD) * ESZ;
+          else
+            ring = a.ring_p + ((size_t)cur.layer * a.p_layer_stride + (size_t)isv * a.p_kv_stride +
+                               (size_t)kh * a.Q * HD + (size_t)pm * HD) * ESZ;
+          ring_put(ring + wi * 8, word);
+        }
+      }
+      __syncthreads();
+      for (int m = 0; m < M; ++m) {
+        const int pm = cur.stack ? p : (cur.step == 0 ? m : cur.step + 1);
+        const int n = min(pm - base + 1, cur.stack ? TILE : a.Q);  // valid rows of this tile
+        const float *qrow = rowbuf + (size_t)m * W;
+        // scores: lanes (pg, chunk cc); 16-lane reduction per position
+        float qr[GQ][DPC];
 #pragma unroll
-        for (int i = 0; i < VPW; ++i) acc[g][i] = 0.f;
-      const uint64_t *vr = ring + head_w + kvs_w + (size_t)j0 * WPR + wi;
-      int j = grp;
-      for (; j + 3 * NGRP < jn; j += 4 * NGRP) {
-        uint64_t vw[4];
+        for (int g = 0; g < GQ; ++g)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) vw[u] = tget(vr + (size_t)(j + u * NGRP) * WPR);
+          for (int e = 0; e < DPC; ++e) qr[g][e] = qrow[g * HD + cc * DPC + e];
+        for (int j0 = 0; j0 < n; j0 += PG) {
+          const int j = j0 + pg;
+          float kf[DPC];
+          unpack16<KVB>(j < n ? *(const uint4 *)(kbase + (size_t)j * ROWB + cc * 16) : make_uint4(0, 0, 0, 0), kf);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float vv[4];
-          unpack8<KVB>(vw[u], vv);
+          for (int g = 0; g < GQ; ++g) {
+            float d = 0.f;
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float e = sh.sc[g][j + u * NGRP];
-#pragma unroll
-            for (int i = 0; i < VPW; ++i) acc[g][i] += e * vv[i];
+            for (int e = 0; e < DPC; ++e) d += qr[g][e] * kf[e];
+            d = row16_sum(d);  // the 16 lanes of a position form one DPP row
+            if (cc == 0 && j < n) sc[g * TILE + j] = d * a.scale;
           }
         }
-      }
-      for (; j < jn; j += NGRP) {
-        float vv[4];
-        unpack8<KVB>(tget(vr + (size_t)j * WPR), vv);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float e = sh.sc[g][j];
-#pragma unroll
-          for (int i = 0; i < VPW; ++i) acc[g][i] += e * vv[i];
+        __syncthreads();
+        // softmax statistics: one wave per head
+        if (wave < GQ) {
+          float mx = -INFINITY;
+          for (int j = lane; j < n; j += 64) mx = fmaxf(mx, sc[wave * TILE + j]);
+          mx = wave_max(mx);
+          float sum = 0.f;
+          for (int j = lane; j < n; j += 64) {
+            const float e = expf(sc[wave * TILE + j] - mx);
+            sc[wave * TILE + j] = e;
+            sum += e;
+          }
+          sum = wave_sum(sum);
+          if (lane == 0) { stat[wave * 2] = mx; stat[wave * 2 + 1] = sum; }
         }
+        __syncthreads();
+        // P.V: lanes (pg, chunk cc) accumulate their positions
+        float acc[GQ][DPC];
+#pragma unroll
+        for (int g = 0; g < GQ; ++g)
+#pragma unroll
+          for (int e = 0; e < DPC; ++e) acc[g][e] = 0.f;
+        for (int j = pg; j < n; j += PG) {
+          float vf[DPC];
+          unpack16<KVB>(*(const uint4 *)(vbase + (size_t)j * ROWB + cc * 16), vf);
+#pragma unroll
+          for (int g = 0; g < GQ; ++g) {
+            const float e = sc[g * TILE + j];
+#pragma unroll
+            for (int d = 0; d < DPC; ++d) acc[g][d] += e * vf[d];
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < GQ; ++g)
+#pragma unroll
+          for (int d = 0; d < DPC; ++d) {
+            float v = acc[g][d];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[g][d] = v;
+          }
+        if (lane < CPR)
+#pragma unroll
+          for (int g = 0; g < GQ; ++g)
+#pragma unroll
+            for (int d = 0; d < DPC; ++d) pvred[(wave * GQ + g) * HD + cc * DPC + d] = acc[g][d];
+        __syncthreads();
+        // publish: normalised output (one tile) or the tile's partial
+        if (ntile == 1) {
+          if (a.act_bf16) {
+            for (int i = tid; i < GQ * HD / 2; i += NT) {
+              const int g = i / (HD / 2), d = 2 * (i % (HD / 2));
+              float o[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int k = g * HD + d + e;
+                o[e] = ((pvred[k] + pvred[GQ * HD + k]) + (pvred[2 * GQ * HD + k] + pvred[3 * GQ * HD + k])) / stat[g * 2 + 1];
+              }
+              tput(a.ob + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, pack2(o[0], o[1]), tag);
+            }
+          } else {
+            for (int i = tid; i < GQ * HD; i += NT) {
+              const int g = i / HD;
+              const float o = ((pvred[i] + pvred[GQ * HD + i]) + (pvred[2 * GQ * HD + i] + pvred[3 * GQ * HD + i])) / stat[g * 2 + 1];
+              tputf(a.ob + (size_t)m * qd + kh * GQ * HD + i, o, tag);
+            }
+          }
+        } else {
+          for (int i = tid; i < GQ * (HD + 2); i += NT) {
+            const int g = i / (HD + 2), d = i % (HD + 2);
+            uint64_t *pp = a.part + ((size_t)(kh * GQ + g) * maxT + t) * (HD + 2);
+            float v;
+            if (d < HD) {
+              const int k = g * HD + d;
+              v = (pvred[k] + pvred[GQ * HD + k]) + (pvred[2 * GQ * HD + k] + pvred[3 * GQ * HD + k]);
+            } else {
+              v = stat[g * 2 + (d - HD)];
+            }
+            tputf(pp + d, v, tag);
+          }
+        }
+        __syncthreads();
       }
-      // partials by group -> LDS (sh.x as scratch: [grp][g][HD])
-      float *scr = &sh.x[0][0];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < VPW; ++i) scr[((size_t)grp * G + g) * HD + wi * VPW + i] = acc[g][i];
-    }
-    __syncthreads();
-    if (tid < G * HD) {
-      const int g = tid / HD, d = tid % HD;
-      const float *scr = &sh.x[0][0];
-      float acc = 0.f;
-#pragma unroll
-      for (int grp = 0; grp < NGRP; ++grp) acc += scr[((size_t)grp * G + g) * HD + d];
-      const int h = kh * G + g;
-      if (ntiles == 1) {
-        tput(a.ob + (size_t)m * qd + (size_t)h * HD + d, acc / sh.stat[g][1], tag_out);
+      if (tracing && tid == 0) {
+        uint64_t *tr = a.trace + 8 * (768 + ntr);
+        st(tr, (uint64_t)cur.type | ((uint64_t)cur.stack << 8) | ((uint64_t)cur.layer << 16) |
+                   ((uint64_t)(cur.step & 0xff) << 24));
+        st(tr + 1, t0);
+        st(tr + 2, t1);
+        st(tr + 3, (uint64_t)wall_clock64());
+        ++ntr;
+      }
+      ev = next_event(a, ev, t);
+      if (ev.valid) prep(ev);
+    } else if (cur.type == PH_COMB && t == 0) {
+      // merge the tile partials of this head's query heads (talker, one row)
+      const int ntile = ntiles_at(pos0 + cur.frame);
+      uint32_t *buf = (uint32_t *)(smem + L.comb);  // [GQ][ntile][HD + 2]
+      const int per = ntile * (HD + 2);
+      const bool ok = poll(a, GQ * per, tagp, [=](int i) { return buf + i; }, [=](int i) {
+        const int g = i / per;
+        return a.part + ((size_t)(kh * GQ + g) * maxT) * (HD + 2) + (i - g * per);
+      });
+      if (!ok) cm.abort = 1;
+      __syncthreads();
+      if (cm.abort) return;
+      const float *pb = (const float *)buf;
+      if (a.act_bf16) {
+        for (int i = tid; i < GQ * HD / 2; i += NT) {
+          const int g = i / (HD / 2), d = 2 * (i % (HD / 2));
+          const float *hp = pb + (size_t)g * ntile * (HD + 2);
+          float mx = -INFINITY;
+          for (int tt = 0; tt < ntile; ++tt) mx = fmaxf(mx, hp[tt * (HD + 2) + HD]);
+          float Ls = 0.f, O0 = 0.f, O1 = 0.f;
+          for (int tt = 0; tt < ntile; ++tt) {
+            const float w = expf(hp[tt * (HD + 2) + HD] - mx);
+            Ls += hp[tt * (HD + 2) + HD + 1] * w;
+            O0 += hp[tt * (HD + 2) + d] * w;
+            O1 += hp[tt * (HD + 2) + d + 1] * w;
+          }
+          tput(a.ob + ((kh * GQ + g) * HD + d) / 2, pack2(O0 / Ls, O1 / Ls), tag);
+        }
       } else {
-        uint64_t *pp = a.part + ((size_t)h * (a.P / 256) + t) * (HD + 2);
-        tput(pp + d, acc, tag_out);
-        if (d == 0) {
-          tput(pp + HD, sh.stat[g][0], tag_out);
-          tput(pp + HD + 1, sh.stat[g][1], tag_out);
+        for (int i = tid; i < GQ * HD; i += NT) {
+          const int g = i / HD, d = i % HD;
+          const float *hp = pb + (size_t)g * ntile * (HD + 2);
+          float mx = -INFINITY;
+          for (int tt = 0; tt < ntile; ++tt) mx = fmaxf(mx, hp[tt * (HD + 2) + HD]);
+          float Ls = 0.f, O = 0.f;
+          for (int tt = 0; tt < ntile; ++tt) {
+            const float w = expf(hp[tt * (HD + 2) + HD] - mx);
+            Ls += hp[tt * (HD + 2) + HD + 1] * w;
+            O += hp[tt * (HD + 2) + d] * w;
+          }
+          tputf(a.ob + (size_t)(kh * GQ + g) * HD + d, O / Ls, tag);
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
+    ++seq;
+    cur = nxt;
   }
-  return true;
-}
-
-// merge the tile partials of query head h (talker, one row)
-__device__ __forceinline__ bool combine_unit(const FrameArgs &a, Shared &sh, int h, int ntiles, uint32_t tag_in,
-                             uint32_t tag_out) {
-  const int hd = a.hd, tid = threadIdx.x;
-  const uint64_t *base = a.part + (size_t)h * (a.P / 256) * (hd + 2);
-  // stage all partials: ntiles * (hd + 2) words <= 16 * 130
-  const int n = ntiles * (hd + 2);
-  if (!acquire(a, base, n, tag_in, &sh.x[0][0])) sh.abort = 1;
-  __syncthreads();
-  if (sh.abort) return false;
-  if (tid < hd) {
-    float mx = -INFINITY;
-    for (int t = 0; t < ntiles; ++t) mx = fmaxf(mx, sh.x[0][t * (hd + 2) + hd]);
-    float Lsum = 0.f, O = 0.f;
-    for (int t = 0; t < ntiles; ++t) {
-      const float w = expf(sh.x[0][t * (hd + 2) + hd] - mx);
-      Lsum += sh.x[0][t * (hd + 2) + hd + 1] * w;
-      O += sh.x[0][t * (hd + 2) + tid] * w;
-    }
-    tput(a.ob + (size_t)h * hd + tid, O / Lsum, tag_out);
-  }
-  __syncthreads();
-  return true;
+  if (a.trace && wg == 0 && tid == 0) st(a.trace + 8 * (768 + ntr), (uint64_t)255);
 }
 
 // ------------------------------------------------------------ the kernel
 
 template <int WT, int HD, int GQ, bool KVB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void frame_kernel(FrameArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  Shared &sh = *reinterpret_cast<Shared *>(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wg = blockIdx.x;
-  const int gw = wg * 4 + wave;
-  const int H = a.H, qd = a.nq * a.hd;
-  const int force = ld(a.ctl + 1);
-  const int tiles_max = a.P / 256;
-
-  int pos = ld(a.pos);
-  int c0 = ld(a.c0);
-  if (tid == 0) sh.abort = 0;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  Common &cm = *reinterpret_cast<Common *>(smem);
+  const int tid = threadIdx.x;
+  if (tid == 0) cm.abort = 0;
   for (int l = tid; l < a.Lt + a.Lp; l += NT) {
     const LayerDev *src = l < a.Lt ? a.tl + l : a.pl + (l - a.Lt);
-    LayerTab &T = sh.lt[l];
+    LayerTab &T = cm.lt[l];
     for (int i = 0; i < 7; ++i) { T.w[i] = ld(&src->w[i]); T.sc[i] = ld(&src->sc[i]); }
     T.attn_norm = ld(&src->attn_norm); T.q_norm = ld(&src->q_norm);
     T.k_norm = ld(&src->k_norm); T.mlp_norm = ld(&src->mlp_norm);
   }
   for (int i = tid; i < a.G; i += NT) {
-    sh.head_w[i] = ld(a.head_w + i);
-    sh.head_sc[i] = a.head_sc ? ld(a.head_sc + i) : nullptr;
+    cm.head_w[i] = ld(a.head_w + i);
+    cm.head_sc[i] = a.head_sc ? ld(a.head_sc + i) : nullptr;
   }
-  for (int i = tid; i < H; i += NT) sh.bridge[i] = ld(a.bridge + i);
   __syncthreads();
-
-  uint32_t seq = 1, x_seq = 0;
-  // the weight slice of a phase sits in sh.wbuf: a phase consumes it, then
-  // loads the next phase's slice there before its stores and the next wait
-  __syncthreads();
-
-  Ph cur{PH_QKV, 0, 0, 0, 0};
-  bool pending_code = false;     // the previous phase was a head
-  int pending_idx = 0;           // code index it decides (0 = next frame's c0)
-  prefetch_any<WT>(a, sh, cur, gw, lane);
-
-  int ntr = 0;
-  uint64_t t_start = 0;
-  while (cur.type != PH_END) {
-    const bool tracing = a.trace && wg == 0 && cur.frame == 0 && ntr < 1023;  // [1024][8] words
-    if (tracing) t_start = wall_clock64();
-    const uint32_t tag = mktag(a.tag_base, seq);
-    const uint32_t tag_prev = mktag(a.tag_base, seq - 1);
-    const bool multi = ((pos + 256) / 256) > 1;
-
-    // ---- resolve the code picked by the previous head (every workgroup)
-    if (pending_code) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int w = tid; w < a.nwg; w += NT) {
-        uint32_t v, ix;
-        bool ok = acquire1(a, a.amax + 2 * w, tag_prev, v) && acquire1(a, a.amax + 2 * w + 1, tag_prev, ix);
-        if (!ok) { sh.abort = 1; break; }
-        const float fv = __uint_as_float(v);
-        if (fv > bv || (fv == bv && (int)ix < bi)) { bv = fv; bi = (int)ix; }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (lane == 0) { sh.amv[wave] = bv; sh.ami[wave] = bi; }
-      __syncthreads();
-      if (sh.abort) return;
-      if (tid == 0) {
-        float b2 = sh.amv[0];
-        int i2 = sh.ami[0];
-        for (int w = 1; w < 4; ++w)
-          if (sh.amv[w] > b2 || (sh.amv[w] == b2 && sh.ami[w] < i2)) { b2 = sh.amv[w]; i2 = sh.ami[w]; }
-        sh.code = i2 == 0x7fffffff ? 0 : i2;
-      }
-      __syncthreads();
-      const int c = sh.code;
-      if (pending_idx == 0) {
-        c0 = c;  // next frame's code 0 (the talker's pick)
-      } else {
-        const int f = cur.frame;  // same frame as the predictor head
-        int32_t *ci = a.cin + (size_t)f * a.G + pending_idx;
-        if (wg == 0 && tid == 0) {
-          st(a.cout + (size_t)f * a.G + pending_idx, c);
-          if (!force) st(ci, c);
-        }
-        if (tid == 0) sh.codes[pending_idx] = force ? ld(ci) : c;
-      }
-      pending_code = false;
-      __syncthreads();
-    }
-
-    const int f = cur.frame;
-    if (cur.type == PH_END) break;
-
-    // ---- inputs of this phase
-    int M = 1;
-    bool ok = true;
-    int pos0 = 0, pos1 = 0;
-    if (cur.stack == 0) {
-      if (cur.step == 0) { M = 2; pos0 = 0; pos1 = 1; }
-      else pos0 = cur.step + 1;
-    } else {
-      pos0 = pos;
-    }
-
-    if (cur.type == PH_QKV && cur.layer == 0) {
-      // build the stack's input rows locally
-      if (cur.stack == 0 && cur.step == 0) {
-        // frame start: code 0 of the frame, then rows [bridge, E_0[c0]]
-        int32_t *ci = a.cin + (size_t)f * a.G;
-        if (wg == 0 && tid == 0) {
-          st(a.cout + (size_t)f * a.G, c0);
-          if (!force) st(ci, c0);
-        }
-        if (tid == 0) sh.codes[0] = force ? ld(ci) : c0;
-        __syncthreads();
-        const int cc = sh.codes[0];
-        for (int i = tid; i < H; i += NT) {
-          sh.x[0][i] = sh.bridge[i];
-          sh.x[1][i] = tab_at(a.code_emb, a.tab_bf16, (size_t)cc * H + i);
-        }
-      } else if (cur.stack == 0) {
-        const int cc = sh.codes[cur.step];
-        for (int i = tid; i < H; i += NT)
-          sh.x[0][i] = tab_at(a.code_emb, a.tab_bf16, ((size_t)cur.step * a.Vc + cc) * H + i);
-      } else {
-        // talker input: sum of the G code rows + the overlay row, left to right
-        const int ov = ld(a.overlay + f);
-        for (int i = tid; i < H; i += NT) {
-          float acc = 0.f;
-          for (int g = 0; g < a.G; ++g)
-            acc += tab_at(a.code_emb, a.tab_bf16, ((size_t)g * a.Vc + sh.codes[g]) * H + i);
-          acc += tab_at(a.text_emb, a.tab_bf16, (size_t)ov * H + i);
-          sh.x[0][i] = acc;
-          if (a.dump && wg == 0) st(a.x0_dump + i, acc);
-        }
-        if (a.dump && wg == 0 && tid <= a.G) st(a.gather_dump + tid, tid < a.G ? sh.codes[tid] : ov);
-        if (a.dump && wg == 0 && tid == 0) st(a.tpos_dump, pos);
-      }
-      __syncthreads();
-      // publish the rows for the residual adds: element i by workgroup i % nwg
-      for (int m = 0; m < M; ++m)
-        for (int i = wg + a.nwg * tid; i < H; i += a.nwg * NT) tput(a.xq + (size_t)m * H + i, sh.x[m][i], tag);
-      x_seq = seq;
-    } else if (cur.type == PH_QKV || cur.type == PH_GU || cur.type == PH_HEAD) {
-      const int mrow = (cur.type == PH_HEAD && cur.stack == 0 && cur.step == 0) ? 1 : 0;
-      if (cur.type == PH_HEAD) M = 1;
-      for (int m = 0; m < M; ++m)
-        ok = ok && acquire(a, a.xq + (size_t)(m + mrow) * H, H, mktag(a.tag_base, x_seq), sh.x[m]);
-    } else if (cur.type == PH_O) {
-      for (int m = 0; m < M; ++m) ok = ok && acquire(a, a.ob + (size_t)m * qd, qd, tag_prev, sh.x[m]);
-    } else if (cur.type == PH_D) {
-      for (int m = 0; m < M; ++m) ok = ok && acquire(a, a.zb + (size_t)m * a.F, a.F, tag_prev, sh.x[m]);
-    }
-    // residual words of this wave's rows
-    if (ok && (cur.type == PH_O || cur.type == PH_D)) {
-      const Split sp = a.split[split_of(cur.type)];
-      if (lane < sp.rw * M) {
-        const int r = lane / M, m = lane % M;
-        const int n = gw * sp.rw + r;
-        if (n < H) {
-          uint32_t v;
-          if (!acquire1(a, a.xq + (size_t)m * H + n, mktag(a.tag_base, x_seq), v)) ok = false;
-          else sh.xold[wave][lane] = __uint_as_float(v);
-        }
-      }
-    }
-    if (!ok) sh.abort = 1;
-    __syncthreads();
-    if (sh.abort) return;
-
-    uint64_t t_in = 0, t_pro = 0, t_w = 0, t_mm = 0;
-    if (tracing) t_in = wall_clock64();
-    // ---- prologue: norm / operand rounding
-    const LayerTab &Lc = tab_of(a, sh, cur);
-    if (cur.type == PH_QKV) norm_rows(a, sh, M, H, Lc.attn_norm, nullptr);
-    else if (cur.type == PH_GU) norm_rows(a, sh, M, H, Lc.mlp_norm, nullptr);
-    else if (cur.type == PH_HEAD) {
-      const bool talker = cur.stack == 1;
-      norm_rows(a, sh, 1, H, talker ? a.t_norm : a.p_norm, talker ? sh.bridge : nullptr);
-      if (talker && wg == 0)
-        for (int i = tid; i < H; i += NT) st(a.bridge + i, sh.bridge[i]);
-    } else if (cur.type == PH_O) act_rows(a, sh, M, qd);
-    else if (cur.type == PH_D) act_rows(a, sh, M, a.F);
-    if constexpr (WT != W_F32) {
-      // GEMV operand rows -> packed bf16 pairs in place (values are already
-      // bf16-rounded, so this is exact)
-      if (cur.type != PH_ATTN && cur.type != PH_COMB) {
-        int N_, K_;
-        phase_nk(a, cur.type, N_, K_);
-        const int Mg = cur.type == PH_HEAD ? 1 : M;
-        uint32_t pk[2][KMAX / (2 * NT)];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int k = 0; k < KMAX / (2 * NT); ++k) {
-            const int pi = tid + k * NT;
-            pk[m][k] = 0;
-            if (m < Mg && 2 * pi < K_)
-              pk[m][k] = (__float_as_uint(sh.x[m][2 * pi]) >> 16) | (__float_as_uint(sh.x[m][2 * pi + 1]) & 0xffff0000u);
-          }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int k = 0; k < KMAX / (2 * NT); ++k) {
-            const int pi = tid + k * NT;
-            if (m < Mg && 2 * pi < K_) ((uint32_t *)&sh.x[m][0])[pi] = pk[m][k];
-          }
-        __syncthreads();
-      }
-    }
-
-    if (tracing) t_pro = wall_clock64();
-    const Ph nxt = next_phase(a, cur, multi);
-    // workgroups with attention work issue the next prefetch after it (their
-    // waits for q/k/v would otherwise also wait for the prefetch, in order)
-    const bool attn_busy =
-        (cur.type == PH_ATTN && wg < a.nkv * (cur.stack ? tiles_max : 1)) || (cur.type == PH_COMB && wg < a.nq);
-
-    // ---- compute + epilogue
-    if (attn_busy) {
-      // attention first: the next phase's weights are not in flight meanwhile
-      if (cur.type == PH_ATTN) {
-        const int tile = cur.stack ? 256 : a.Q;
-        const int ntiles = cur.stack ? (pos + 256) / 256 : 1;
-        const int units = a.nkv * (cur.stack ? tiles_max : 1);
-        for (int u = wg; u < units; u += a.nwg) {
-          const int kh = cur.stack ? u / tiles_max : u;
-          const int t = cur.stack ? u % tiles_max : 0;
-          if (!attention_unit<HD, GQ, KVB>(a, sh, cur, kh, t, M, pos0, pos1, tag_prev, tag, ntiles, tile)) return;
-        }
-      } else {
-        const int ntiles = (pos + 256) / 256;
-        for (int h = wg; h < a.nq; h += a.nwg)
-          if (!combine_unit(a, sh, h, ntiles, tag_prev, tag)) return;
-      }
-      prefetch_any<WT>(a, sh, nxt, gw, lane);
-    } else if (cur.type == PH_ATTN || cur.type == PH_COMB) {
-      prefetch_any<WT>(a, sh, nxt, gw, lane);
-    }
-    if (cur.type != PH_ATTN && cur.type != PH_COMB) {
-      int N, K;
-      phase_nk(a, cur.type, N, K);
-      // the slice's LDS-direct loads count as vector-memory operations: wait
-      // for them (long done after the input exchange, which waited in order)
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-      if (tracing) t_w = wall_clock64();
-      gemv_any<WT>(a, cur.type, M, sh, lane, wave);
-      if (tracing) t_mm = wall_clock64();
-      // each wave reads back only its own slice, so the next phase's loads
-      // may land once this wave's reads are done
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      prefetch_any<WT>(a, sh, nxt, gw, lane);
-      const Split sp = a.split[split_of(cur.type)];
-      const int nout = sp.rw * M;
-      if (cur.type == PH_HEAD) {
-        // logits (kept for readback) and this workgroup's partial argmax
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
-        if (lane < sp.rw) {
-          const int n = gw * sp.rw + lane;
-          if (n < N) {
-            bv = sh.res[wave][lane];
-            bi = n;
-            st(lg + n, bv);
-          }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float ov = __shfl_xor(bv, o, 64);
-          const int oi = __shfl_xor(bi, o, 64);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        if (lane == 0) { sh.amv[wave] = bv; sh.ami[wave] = bi; }
-        __syncthreads();
-        if (tid == 0) {
-          float b2 = sh.amv[0];
-          int i2 = sh.ami[0];
-          for (int w = 1; w < 4; ++w)
-            if (sh.amv[w] > b2 || (sh.amv[w] == b2 && sh.ami[w] < i2)) { b2 = sh.amv[w]; i2 = sh.ami[w]; }
-          tput(a.amax + 2 * wg, b2, tag);
-          tput_u(a.amax + 2 * wg + 1, (uint32_t)i2, tag);
-        }
-        pending_code = true;
-        pending_idx = cur.stack ? 0 : cur.step + 1;
-        if (cur.stack == 1) {
-          if (wg == 0 && tid == 0) st(a.pos, pos + 1);
-          pos += 1;
-        }
-      } else if (lane < nout) {
-        const int r = lane / M, m = lane % M;
-        const int n = gw * sp.rw + r;
-        if (n < N) {
-          if (cur.type == PH_QKV) {
-            tput(a.qkvb + (size_t)m * N + n, sh.res[wave][r * M + m], tag);
-          } else if (cur.type == PH_GU) {
-            const float g = sh.res[wave][(r * 2) * M + m], u = sh.res[wave][(r * 2 + 1) * M + m];
-            tput(a.zb + (size_t)m * N + n, g / (1.0f + expf(-g)) * u, tag);
-          } else {
-            const float nv = sh.xold[wave][lane] + sh.res[wave][r * M + m];
-            tput(a.xq + (size_t)m * H + n, nv, tag);
-            if (cur.type == PH_D && cur.stack == 1 && a.dump)
-              st(a.hidden_dump + (size_t)cur.layer * H + n, nv);
-          }
-        }
-      }
-      if (cur.type == PH_O || cur.type == PH_D) x_seq = seq;
-    }
-    __syncthreads();
-    if (tracing && tid == 0) {
-      uint64_t *tr = a.trace + 8 * ntr;
-      st(tr, (uint64_t)cur.type | ((uint64_t)cur.stack << 8) | ((uint64_t)cur.layer << 16) |
-                 ((uint64_t)(cur.step & 0xff) << 24));
-      st(tr + 1, t_start);
-      st(tr + 2, t_in);
-      st(tr + 3, (uint64_t)wall_clock64());
-      st(tr + 4, t_pro);
-      st(tr + 5, t_w);
-      st(tr + 6, t_mm);
-    }
-    if (tracing) ++ntr;
-    ++seq;
-    cur = nxt;
-  }
-  if (a.trace && wg == 0 && tid == 0) st(a.trace + 8 * ntr, (uint64_t)255);
-  // the code picked by the last talker head becomes the slot's pending code 0
-  if (pending_code) {
-    const uint32_t tag_prev = mktag(a.tag_base, seq - 1);
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    bool ok = true;
-    for (int w = tid; w < a.nwg; w += NT) {
-      uint32_t v, ix;
-      if (!(acquire1(a, a.amax + 2 * w, tag_prev, v) && acquire1(a, a.amax + 2 * w + 1, tag_prev, ix))) { ok = false; break; }
-      const float fv = __uint_as_float(v);
-      if (fv > bv || (fv == bv && (int)ix < bi)) { bv = fv; bi = (int)ix; }
-    }
-    if (!ok) sh.abort = 1;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == 0) { sh.amv[wave] = bv; sh.ami[wave] = bi; }
-    __syncthreads();
-    if (sh.abort) return;
-    if (wg == 0 && tid == 0) {
-      float b2 = sh.amv[0];
-      int i2 = sh.ami[0];
-      for (int w = 1; w < 4; ++w)
-        if (sh.amv[w] > b2 || (sh.amv[w] == b2 && sh.ami[w] < i2)) { b2 = sh.amv[w]; i2 = sh.ami[w]; }
-      st(a.c0, i2 == 0x7fffffff ? 0 : i2);
-    }
-  }
-}
-
-}  // namespace
-
-bool frame_split_supported(int wt, const Split &sp) {
-#define X(W, R, N, C) \
-  if (wt == W && sp.rw == R && sp.nmat == N && sp.cpl == C) return true;
-  QT_SPLITS(X)
-#undef X
-  return false;
+  if ((int)blockIdx.x < a.n_attn) attn_role<HD, GQ, KVB>(a, smem);
+  else gemv_role<WT>(a, smem);
 }
 
 // (weights, head dim, GQA group, bf16 ring) combinations instantiated
-#define QT_FRAME_VARIANTS(X)                                   \
-  X(W_F32, 64, 2, false) X(W_F32, 128, 2, false)               \
-  X(W_BF16, 128, 2, true) X(W_BF16, 128, 1, true) X(W_BF16, 64, 2, true) \
-  X(W_Q8, 128, 2, true) X(W_Q8, 128, 1, true)
+#define QT_FRAME_VARIANTS(X) X(W_F32, 64, 2, false) X(W_BF16, 128, 2, true) X(W_Q8, 128, 2, true)
+
+}  // namespace
 
 bool frame_variant_supported(int wt, int hd, int g, int kvb) {
 #define X(W, HD_, G_, K_) if (wt == W && hd == HD_ && g == G_ && (kvb != 0) == K_) return true;
@@ -1080,16 +1208,52 @@ bool frame_variant_supported(int wt, int hd, int g, int kvb) {
   return false;
 }
 
-size_t frame_lds_bytes() { return sizeof(Shared); }
+bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
+  const int esz = a.wt == W_F32 ? 4 : (a.wt == W_BF16 ? 2 : 1);
+  const int qd = a.nq * a.hd;
+  a.tile = TILE;
+  a.max_tiles = a.P / TILE;
+  if (a.P % TILE) { *why = "talker positions not a multiple of 256"; return false; }
+  if (a.hd * (a.kv_bf16 ? 2 : 4) != 256) { *why = "K/V rows must be 256 bytes"; return false; }
+  if (a.H > 2 * NT * HPAIR || a.H % 2) { *why = "hidden width above 2048"; return false; }
+  if (a.Lt + a.Lp > MAXLAYERS || a.G > MAXHEADS) { *why = "too many layers or codebooks"; return false; }
+  if (a.nwg > 1024) { *why = "more than 1024 workgroups"; return false; }
+  a.n_attn = a.nkv * (max_pos / TILE + 1);
+  const int NG = a.nwg - a.n_attn;
+  if (NG < 16) { *why = "too few GEMV workgroups"; return false; }
+  const int NK[5][3] = {{qd + 2 * a.nkv * a.hd, a.H, 1}, {a.H, qd, 1}, {a.F, a.H, 2}, {a.H, a.F, 1}, {a.Vc, a.H, 1}};
+  int slot = 0;
+  for (int i = 0; i < 5; ++i) {
+    const int N = NK[i][0], K = NK[i][1], nm = NK[i][2];
+    if ((K * esz) % 1024 || N % 2 || (a.wt == W_Q8 && K % 256)) { *why = "GEMV width not a multiple of 1 KB"; return false; }
+    if (K > 3072) { *why = "GEMV width above 3072"; return false; }
+    const int R = 2 * ((N / 2 + NG - 1) / NG);
+    if (R * nm > MAXR) { *why = "too many rows per workgroup"; return false; }
+    int b = R * nm * K * esz;
+    if (a.wt == W_Q8) b += (int)up1k((uint32_t)(R * nm * (K / 16)));
+    if (i == 0 || i == 2 || i == 4) b += (int)up1k((uint32_t)(a.H * (a.tab_bf16 ? 2 : 4)));
+    slot = imax(slot, (int)up1k((uint32_t)b));
+  }
+  a.slot_bytes = slot;
+  a.two_slots = 1;
+  Lds L = lds_layout(a);
+  if ((int)L.g_end > lds_limit) {
+    a.two_slots = 0;
+    L = lds_layout(a);
+  }
+  a.lds_bytes = (int)(L.g_end > L.a_end ? L.g_end : L.a_end);
+  if (a.lds_bytes > lds_limit) { *why = "LDS plan above the device limit"; return false; }
+  return true;
+}
 
 hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s) {
   const int g = a.nq / a.nkv;
 #define X(W, HD_, G_, K_)                                                                         \
   if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_) {                          \
     hipError_t e = hipFuncSetAttribute((const void *)frame_kernel<W, HD_, G_, K_>,                \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Shared)); \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes); \
     if (e != hipSuccess) return e;                                                               \
-    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_>), dim3(a.nwg), dim3(NT), sizeof(Shared), s, a); \
+    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_>), dim3(a.nwg), dim3(NT), a.lds_bytes, s, a); \
     return hipGetLastError();                                                                    \
   }
   QT_FRAME_VARIANTS(X)

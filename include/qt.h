@@ -200,10 +200,13 @@ int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
      QT_DUMP_GATHER        i32 [B][G+1]      codes fed to the gather, overlay id
      QT_DUMP_TPOS          i32 [B]           talker K/V write position
      QT_DUMP_HIDDEN        f32 [Lt][B][H]    talker residual after each layer
-     QT_DUMP_TRACE         u64 [1024][8]     QT_F_TRACE only: per phase (kind | stack << 8 |
-                                             layer << 16 | step << 24, start, inputs in, end,
-                                             prologue done, weights in, dot products done, 0)
-                                             in 100 MHz wall-clock ticks; kind 255 ends it
+     QT_DUMP_TRACE         u64 [1024][8]     QT_F_TRACE only: rows 0..767 per GEMV phase of the
+                                             first GEMV workgroup (kind | stack << 8 | layer << 16 |
+                                             step << 24, start, inputs in, end, norm done, GEMV done,
+                                             then two shader-clock stamps around the norm); rows
+                                             768.. per attention event of workgroup 0 (kind word,
+                                             start, inputs in, end).  Wall-clock stamps are 100 MHz
+                                             ticks; kind 255 ends each part
    bytes must equal the kind's size.  Errors: QT_E_STATE, QT_E_ARG, QT_E_HIP. */
 #define QT_DUMP_TALKER_LOGITS 1
 #define QT_DUMP_PRED_LOGITS 2
