@@ -39,11 +39,14 @@
 namespace qtk {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NW = 7;            // compute waves of a GEMV workgroup
+constexpr int NT = 64 * NW;      // their threads
+constexpr int NTB = NT + 64;     // plus the loader wave: two waves per SIMD
+constexpr int ANT = 256;         // threads of an attention workgroup
 constexpr int MAXLAYERS = 40;
 constexpr int MAXHEADS = 32;
 constexpr int PER = 8;          // tagged words per thread per poll round
-constexpr int HPAIR = 4;        // hidden pairs per thread (H <= 2 * NT * HPAIR)
+constexpr int HPAIR = 3;        // hidden pairs per thread (H <= 2 * NT * HPAIR)
 constexpr int MAXR = 64;        // GEMV rows per workgroup per phase
 constexpr int TILE = 256;       // talker positions per attention tile
 constexpr uint32_t SPIN_LIMIT = 1u << 21;
@@ -187,12 +190,13 @@ struct Common {
   LayerTab lt[MAXLAYERS];  // talker layers then predictor layers
   const void *head_w[MAXHEADS];
   const uint16_t *head_sc[MAXHEADS];
-  float red[4][8];
-  float amv[4];
-  int ami[4];
+  float amv[NW];
+  int ami[NW];
   int codes[MAXHEADS];  // codes fed to this frame's gathers
   int code;
   int abort;
+  uint32_t cbar;   // compute-wave barrier arrivals
+  uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
 };
 
 // Offsets (bytes) of each role's LDS buffers; one function for host and device.
@@ -280,21 +284,21 @@ __device__ __forceinline__ const LayerTab &tab_of(const FrameArgs &a, const Comm
 
 // Poll n tagged words (word i at src(i)) until each carries tag; value bits
 // -> *dst(i) (LDS).  All threads; false on timeout.
-template <class Dst, class Src>
+template <int TH = NT, class Dst, class Src>
 __device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Dst dst, Src src) {
-  for (int b0 = 0; b0 < n; b0 += PER * NT) {
+  for (int b0 = 0; b0 < n; b0 += PER * TH) {
     uint64_t v[PER];
     uint32_t pend = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = b0 + (int)threadIdx.x + k * NT;
+      const int i = b0 + (int)threadIdx.x + k * TH;
       if (i < n) { v[k] = tget(src(i)); pend |= 1u << k; }
     }
     for (uint32_t spins = 0;; ++spins) {
 #pragma unroll
       for (int k = 0; k < PER; ++k)
         if (((pend >> k) & 1u) && (uint32_t)(v[k] >> 32) == tag) {
-          *dst(b0 + threadIdx.x + k * NT) = (uint32_t)v[k];
+          *dst(b0 + threadIdx.x + k * TH) = (uint32_t)v[k];
           pend &= ~(1u << k);
         }
       if (!pend) break;
@@ -304,28 +308,20 @@ __device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Ds
       }
 #pragma unroll
       for (int k = 0; k < PER; ++k)
-        if ((pend >> k) & 1u) v[k] = tget(src(b0 + threadIdx.x + k * NT));
+        if ((pend >> k) & 1u) v[k] = tget(src(b0 + threadIdx.x + k * TH));
     }
   }
   return true;
 }
+template <int TH = NT>
 __device__ __forceinline__ bool poll_lin(const FrameArgs &a, const uint64_t *src, int n, uint32_t tag, uint32_t *dst) {
-  return poll(a, n, tag, [=](int i) { return dst + i; }, [=](int i) { return src + i; });
+  return poll<TH>(a, n, tag, [=](int i) { return dst + i; }, [=](int i) { return src + i; });
 }
 // rows of w words at src (contiguous) into LDS rows of stride dw
 __device__ __forceinline__ bool poll_rows(const FrameArgs &a, const uint64_t *src, int rows, int w, uint32_t tag,
                                           uint32_t *dst, int dw) {
   return poll(a, rows * w, tag, [=](int i) { const int m = i / w; return dst + m * dw + (i - m * w); },
               [=](int i) { return src + i; });
-}
-
-__device__ __forceinline__ float block_sum(Common &cm, float v) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) cm.red[wave][0] = v;
-  __syncthreads();
-  return (cm.red[0][0] + cm.red[1][0]) + (cm.red[2][0] + cm.red[3][0]);
 }
 
 // ------------------------------------------------------------ GEMV role
@@ -395,38 +391,37 @@ __device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool q8) {
 }
 
 // Issue the direct-to-LDS loads of phase p's weight slice (+ scales, gain).
+// Called by the loader wave only: every 1 KB block is one instruction of it.
 template <int WT>
 __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, const Ph &p, int gi, int NG,
-                                       uint32_t slot) {
+                                          uint32_t slot) {
   constexpr int ESZ = WEsz<WT>::v;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const Share s = share_of(a, p.type, gi, NG);
   const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
   int b = 0;
   for (int u = 0; u < U; ++u) {
     const uint8_t *w, *sc;
     wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
-    for (int cb = 0; cb < bpr; ++cb, ++b)
-      if ((b & 3) == wave) dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
+    for (int cb = 0; cb < bpr; ++cb, ++b) dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
   }
   if constexpr (WT == W_Q8) {
     const int spu = s.K / 256, n = U * spu;  // 16-byte scale chunks per row, in all
     const uint32_t so = scales_off(s, ESZ);
-    for (int sb = 0; sb * 64 < n; ++sb, ++b)
-      if ((b & 3) == wave) {
-        const int idx = min(sb * 64 + lane, n - 1);
-        const int u = idx / spu, k = idx - u * spu;
-        const uint8_t *w, *sc;
-        wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
-        dma16(sc + k * 16, slot + so + (uint32_t)sb * 1024u);
-      }
+    for (int sb = 0; sb * 64 < n; ++sb) {
+      const int idx = min(sb * 64 + lane, n - 1);
+      const int u = idx / spu, k = idx - u * spu;
+      const uint8_t *w, *sc;
+      wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
+      dma16(sc + k * 16, slot + so + (uint32_t)sb * 1024u);
+    }
   }
   const void *g = gain_of(a, cm, p);
   if (g) {
     const int n = a.H * (a.tab_bf16 ? 2 : 4) / 16;
     const uint32_t go = gain_off(s, ESZ, WT == W_Q8);
-    for (int gb = 0; gb * 64 < n; ++gb, ++b)
-      if ((b & 3) == wave) dma16((const uint8_t *)g + min(gb * 64 + lane, n - 1) * 16, slot + go + (uint32_t)gb * 1024u);
+    for (int gb = 0; gb * 64 < n; ++gb)
+      dma16((const uint8_t *)g + min(gb * 64 + lane, n - 1) * 16, slot + go + (uint32_t)gb * 1024u);
   }
 }
 
@@ -464,42 +459,36 @@ __device__ __forceinline__ float chunk_dot(uint4 w, const uint32_t *op, int c, c
   }
 }
 
-// res[u * M + m] = row u of the slot . operand row m; rows spread over the waves
-template <int WT>
-__device__ __forceinline__ void gemv_slice(const uint8_t *slot, const uint32_t *opnd, int opw, const Share &s, int M,
-                                        float *res) {
-  constexpr int ESZ = WEsz<WT>::v;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
-  const uint8_t *scb = slot + scales_off(s, ESZ);
-  for (int u = wave; u < U; u += 4) {
-    const uint8_t *wr = slot + (size_t)u * rowb;
-    const uint8_t *scl = scb + (size_t)u * (s.K / 16);
-    float a0 = 0.f, a1 = 0.f;
-    for (int cb = 0; cb < bpr; ++cb) {
-      const int c = cb * 64 + lane;
-      const uint4 w = ((const uint4 *)wr)[c];
-      a0 += chunk_dot<WT>(w, opnd, c, scl);
-      if (M > 1) a1 += chunk_dot<WT>(w, opnd + opw, c, scl);
+// Barrier of the compute waves (the loader wave never joins it): an arrival
+// counter in LDS; gen counts this wave's barriers times NW.
+__device__ __forceinline__ bool cbar(const FrameArgs &a, Common &cm, uint32_t &gen) {
+  gen += NW;
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(&cm.cbar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (uint32_t spins = 0; __hip_atomic_load(&cm.cbar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < gen; ++spins) {
+    if (spins > SPIN_LIMIT) {
+      err_set(a.err);
+      return false;
     }
-    a0 = wave_sum(a0);
-    if (M > 1) a1 = wave_sum(a1);
-    if (lane == 0) {
-      res[u * M] = a0;
-      if (M > 1) res[u * M + 1] = a1;
-    }
+    __builtin_amdgcn_s_sleep(1);
   }
+  return true;
 }
 
 // RMSNorm of residual row x (LDS f32) with gain g (LDS, table type) -> operand
-// row (bf16 pairs or f32); y kept in yk[] (pair layout) when asked
+// row (bf16 pairs or f32), this thread's pairs; every wave forms the full sum
+// of squares itself.  y kept in yk[] (pair layout) when asked.
 template <int WT>
-__device__ __forceinline__ void norm_row(const FrameArgs &a, Common &cm, const float *x, const uint8_t *g,
-                                         uint32_t *op, float (&yk)[2 * HPAIR], bool keep) {
-  const int H = a.H, tid = threadIdx.x;
+__device__ __forceinline__ void norm_row(const FrameArgs &a, const float *x, const uint8_t *g, uint32_t *op,
+                                         float (&yk)[2 * HPAIR], bool keep) {
+  const int H = a.H, tid = threadIdx.x, lane = tid & 63;
+  float4 xv[8];  // H <= 2048, a multiple of 256: eight float4 per lane
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    xv[k] = 256 * k < H ? *(const float4 *)(x + 4 * lane + 256 * k) : make_float4(0.f, 0.f, 0.f, 0.f);
   float ss = 0.f;
-  for (int i = tid; i < H; i += NT) ss += x[i] * x[i];
-  ss = block_sum(cm, ss);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss += (xv[k].x * xv[k].x + xv[k].y * xv[k].y) + (xv[k].z * xv[k].z + xv[k].w * xv[k].w);
+  ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)H + a.eps);
 #pragma unroll
   for (int k = 0; k < HPAIR; ++k) {
@@ -542,32 +531,114 @@ __device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, s
   }
 }
 
-// argmax over the workgroups' partial maxima of the head with tag; lowest index wins ties
-__device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uint32_t *scratch, int NG, uint32_t tag) {
+// argmax over the workgroups' partial maxima of the head with tag; lowest
+// index wins ties.  Compute waves; false on timeout.
+__device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uint32_t &gen, uint32_t *scratch,
+                                             int NG, uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool ok = poll_lin(a, a.amax, 2 * NG, tag, scratch);
-  __syncthreads();  // each thread reduces words other threads polled
+  if (!poll_lin(a, a.amax, 2 * NG, tag, scratch)) cm.abort = 1;
+  if (!cbar(a, cm, gen) || cm.abort) return false;  // each thread reduces words other threads polled
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  if (ok)
-    for (int w = tid; w < NG; w += NT) {
-      const float fv = __uint_as_float(scratch[2 * w]);
-      const int ix = (int)scratch[2 * w + 1];
-      if (fv > bv || (fv == bv && ix < bi)) { bv = fv; bi = ix; }
-    }
+  for (int w = tid; w < NG; w += NT) pick(bv, bi, __uint_as_float(scratch[2 * w]), (int)scratch[2 * w + 1]);
   wave_argmax(bv, bi);
   if (lane == 0) { cm.amv[wave] = bv; cm.ami[wave] = bi; }
-  if (!ok) cm.abort = 1;
-  __syncthreads();
-  if (tid == 0) {
-    float b2 = cm.amv[0];
-    int i2 = cm.ami[0];
-    for (int w = 1; w < 4; ++w)
-      if (cm.amv[w] > b2 || (cm.amv[w] == b2 && cm.ami[w] < i2)) { b2 = cm.amv[w]; i2 = cm.ami[w]; }
-    cm.code = i2 == 0x7fffffff ? 0 : i2;
+  if (!cbar(a, cm, gen)) return false;
+  float b2 = cm.amv[0];
+  int i2 = cm.ami[0];
+  for (int w = 1; w < NW; ++w) pick(b2, i2, cm.amv[w], cm.ami[w]);
+  cm.code = i2 == 0x7fffffff ? 0 : i2;  // every thread writes the same value
+  return true;
+}
+
+// One wave's GEMV items of the slice (UPI weight rows each: 1, or the gate and
+// up rows of a row pair), round-robin over the compute waves; the results of
+// item it go to out(it, acc) as uniform values.  A row is at most MAXB 1 KB
+// blocks; an item's weight chunks are all loaded before its dot products.
+template <int WT, int UPI, int MAXB, class Out>
+__device__ __forceinline__ void gemv_items(const uint8_t *slot, const uint32_t *opnd, int opw, const Share &s, int M,
+                                           Out out) {
+  constexpr int ESZ = WEsz<WT>::v;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rowb = s.K * ESZ, bpr = rowb >> 10;
+  const int nitems = s.R * s.NM / UPI;
+  const uint8_t *scb = slot + scales_off(s, ESZ);
+  for (int it = wave; it < nitems; it += NW) {
+    uint4 w[UPI][MAXB];
+#pragma unroll
+    for (int q = 0; q < UPI; ++q)
+#pragma unroll
+      for (int cb = 0; cb < MAXB; ++cb)
+        if (cb < bpr) w[q][cb] = ((const uint4 *)(slot + (size_t)(it * UPI + q) * rowb))[cb * 64 + lane];
+    float acc[UPI][2];
+#pragma unroll
+    for (int q = 0; q < UPI; ++q) acc[q][0] = acc[q][1] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < MAXB; ++cb) {
+      if (cb >= bpr) break;
+      const int c = cb * 64 + lane;
+#pragma unroll
+      for (int q = 0; q < UPI; ++q) {
+        const uint8_t *scl = scb + (size_t)(it * UPI + q) * (s.K / 16);
+        acc[q][0] += chunk_dot<WT>(w[q][cb], opnd, c, scl);
+        if (M > 1) acc[q][1] += chunk_dot<WT>(w[q][cb], opnd + opw, c, scl);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < UPI; ++q) {
+      acc[q][0] = wave_sum(acc[q][0]);
+      if (M > 1) acc[q][1] = wave_sum(acc[q][1]);
+    }
+    out(it, acc);
   }
-  __syncthreads();
-  return !cm.abort;
+}
+
+// The loader wave: streams each GEMV phase's weight slice into its LDS slot
+// one phase ahead and meets the compute waves once per phase, right after
+// their inputs are in.
+template <int WT>
+__device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, const Lds &L, unsigned char *smem) {
+  const int gi = (int)blockIdx.x - a.n_attn, NG = a.nwg - a.n_attn;
+  const uint32_t s0 = lds_addr(smem + L.slot0), s1 = lds_addr(smem + L.slot1);
+  Ph cur{PH_QKV, 0, 0, 0, 0};
+  dma_slice<WT>(a, cm, cur, gi, NG, s0);
+  wait_vm();
+  int slot = 0;
+  uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
+  bool have_next = false;     // the next phase's slice is already in its slot
+  // until every compute wave has finished the current phase's GEMV
+  auto wait_gemv = [&]() -> bool {
+    for (uint32_t spins = 0; __hip_atomic_load(&cm.gdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < done;
+         ++spins) {
+      if (spins > SPIN_LIMIT) { err_set(a.err); return false; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+  };
+  while (cur.type != PH_END) {
+    const Ph ng = next_gemv_phase(a, cur, a.pos0);
+    __syncthreads();  // the compute waves have this phase's inputs (and are done with the last phase's slot)
+    if (cm.abort) return;
+    done += NW;
+    if (ng.type != PH_END && !have_next) {
+      if (!a.two_slots && !wait_gemv()) return;  // one slot: it is free once this phase's GEMV is done
+      dma_slice<WT>(a, cm, ng, gi, NG, a.two_slots && !slot ? s1 : s0);
+    }
+    have_next = false;
+    if (a.two_slots && cur.type == PH_QKV && ng.type == PH_O) {
+      // The attention window: the compute waves only poll until attention is
+      // done, so the gate/up slice (the largest) streams into this phase's
+      // slot as soon as its GEMV is done, instead of competing later with the
+      // exchange before the gate/up phase.
+      const Ph n2 = next_gemv_phase(a, ng, a.pos0);
+      if (!wait_gemv()) return;
+      dma_slice<WT>(a, cm, n2, gi, NG, slot ? s1 : s0);
+      have_next = true;  // skipped at the O phase's meeting
+    }
+    wait_vm();
+    if (a.two_slots) slot ^= 1;
+    cur = ng;
+  }
 }
 
 template <int WT>
@@ -575,19 +646,22 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   constexpr int ESZ = WEsz<WT>::v;
   Common &cm = *reinterpret_cast<Common *>(smem);
   const Lds L = lds_layout(a);
+  if (threadIdx.x >= NT) {
+    loader_role<WT>(a, cm, L, smem);
+    return;
+  }
   float *xres = (float *)(smem + L.xres);   // [2][H] residual rows
   uint32_t *opnd = (uint32_t *)(smem + L.opnd);
-  float *res = (float *)(smem + L.res);
-  const uint32_t slot_lds0 = lds_addr(smem + L.slot0), slot_lds1 = lds_addr(smem + L.slot1);
   const int kop = imax(a.H, imax(a.nq * a.hd, a.F));
   const int opw = imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg);  // words per operand row
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gi = (int)blockIdx.x - a.n_attn, NG = a.nwg - a.n_attn;
   const int H = a.H, G = a.G;
   const int force = ld(a.ctl + 1);
   const int pos0 = a.pos0;
   int c0 = ld(a.c0);
   const bool lead = gi == 0;  // writes state, codes and dumps
+  uint32_t gen = 0;           // compute-wave barrier count
 
   float brg[2 * HPAIR], tacc[2 * HPAIR], trow[2 * HPAIR];
 #pragma unroll
@@ -604,25 +678,26 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   bool pending = false;  // the previous GEMV phase was a head
   int pending_idx = 0;   // the code index it decides (0: next frame's code 0)
   int ntr = 0;
-  bool first = true;
 
   while (cur.type != PH_END) {
     const Ph nxt = next_phase(a, cur, pos0);
     if (cur.type == PH_ATTN || cur.type == PH_COMB) { ++seq; cur = nxt; continue; }
     const bool tracing = a.trace && lead && cur.frame == 0 && ntr < 767;
-    uint64_t t0 = tracing ? wall_clock64() : 0;
+    const uint64_t t0 = tracing ? wall_clock64() : 0;
     const uint32_t tag = a.tag_base + seq, tagp = tag - 1;
     const int f = cur.frame;
     const int pos = pos0 + f;
     const int M = (cur.stack == 0 && cur.step == 0 && cur.type != PH_HEAD) ? 2 : 1;
     const Share s = share_of(a, cur.type, gi, NG);
-    const Ph ng = next_gemv_phase(a, cur, pos0);
-    // inputs of this phase -> xres (residual rows) or opnd (operand rows)
-    auto inputs = [&]() -> bool {
-      bool ok = true;
-      if (cur.type == PH_QKV && cur.layer == 0) {
-        if (pending) {
-          if (!resolve_code(a, cm, opnd, NG, tagp)) return false;
+    // every compute wave is done with the last phase's operand and residual rows
+    if (!cbar(a, cm, gen)) return;
+
+    // ---- inputs -> xres (residual rows) or opnd (operand rows)
+    bool ok = true;
+    if (cur.type == PH_QKV && cur.layer == 0) {
+      if (pending) {
+        if (!resolve_code(a, cm, gen, opnd, NG, tagp)) { cm.abort = 1; ok = false; }
+        else {
           const int c = cm.code;
           if (pending_idx == 0) c0 = c;
           else {
@@ -631,10 +706,12 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
               st(a.cout + (size_t)f * G + pending_idx, c);
               if (!force) st(ci, c);
             }
-            if (tid == 0) cm.codes[pending_idx] = force ? ld(ci) : c;
+            cm.codes[pending_idx] = force ? ld(ci) : c;  // same value from every thread
           }
-          pending = false;
         }
+        pending = false;
+      }
+      if (ok) {
         float row[2 * HPAIR];
         if (cur.stack == 0 && cur.step == 0) {
           // frame start: code 0 of the frame, rows [bridge, E_0[code 0]]
@@ -643,11 +720,11 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             st(a.cout + (size_t)f * G, c0);
             if (!force) st(ci, c0);
           }
-          if (tid == 0) cm.codes[0] = force ? ld(ci) : c0;
-          __syncthreads();
-          tab_pairs(a, a.code_emb, (size_t)cm.codes[0], row);
+          const int code0 = force ? ld(ci) : c0;
+          cm.codes[0] = code0;
+          tab_pairs(a, a.code_emb, (size_t)code0, row);
           tab_pairs(a, a.text_emb, (size_t)ld(a.overlay + f), trow);
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
             if (2 * pi < H) {
@@ -658,9 +735,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             tacc[2 * k + 1] = 0.f + row[2 * k + 1];
           }
         } else if (cur.stack == 0) {
-          __syncthreads();
           tab_pairs(a, a.code_emb, (size_t)cur.step * a.Vc + cm.codes[cur.step], row);
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
             if (2 * pi < H) { xres[2 * pi] = row[2 * k]; xres[2 * pi + 1] = row[2 * k + 1]; }
@@ -669,9 +745,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           }
         } else {
           // talker input: the frame's G code rows, then the overlay row, in order
-          __syncthreads();
           tab_pairs(a, a.code_emb, (size_t)(G - 1) * a.Vc + cm.codes[G - 1], row);
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
             const float v0 = (tacc[2 * k] + row[2 * k]) + trow[2 * k];
@@ -684,37 +759,22 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           if (a.dump && lead && tid <= G) st(a.gather_dump + tid, tid < G ? cm.codes[tid] : ld(a.overlay + f));
           if (a.dump && lead && tid == 0) st(a.tpos_dump, pos);
         }
-      } else if (cur.type == PH_QKV || cur.type == PH_GU) {
-        ok = poll_lin(a, a.xq, M * H, tagp, (uint32_t *)xres);
-      } else if (cur.type == PH_HEAD) {
-        const int mrow = cur.stack == 0 && cur.step == 0 ? 1 : 0;
-        ok = poll_lin(a, a.xq + (size_t)mrow * H, H, tagp, (uint32_t *)xres);
-      } else if (cur.type == PH_O) {
-        const int w = a.act_bf16 ? a.nq * a.hd / 2 : a.nq * a.hd;
-        ok = poll_rows(a, a.ob, M, w, tagp, opnd, opw);
-      } else {  // PH_D
-        const int w = a.act_bf16 ? a.F / 2 : a.F;
-        ok = poll_rows(a, a.zb, M, w, tagp, opnd, opw);
       }
-      return ok;
-    };
-    // Weight slices: with two slots, the first phase loads its own slice
-    // before its inputs and every phase loads the next one's right after its
-    // inputs are in; with one slot, each phase loads its own before its inputs.
-    bool ok = true;
-    for (int pass = 0; pass < 2; ++pass) {
-      const bool before = pass == 0;
-      const bool go = before ? (first || !a.two_slots) : (a.two_slots && ng.type != PH_END);
-      const bool to_slot1 = before ? slot != 0 : slot == 0;  // this phase's slot, else the other one
-      if (go) dma_slice<WT>(a, cm, before ? cur : ng, gi, NG, to_slot1 ? slot_lds1 : slot_lds0);
-      if (!before) break;
-      ok = inputs();
-      if (!ok) cm.abort = 1;
-      wait_vm();  // this phase's slice (usually landed long before: the polls waited in order)
-      __syncthreads();
-      if (cm.abort) return;
+    } else if (cur.type == PH_QKV || cur.type == PH_GU) {
+      ok = poll_lin(a, a.xq, M * H, tagp, (uint32_t *)xres);
+    } else if (cur.type == PH_HEAD) {
+      const int mrow = cur.stack == 0 && cur.step == 0 ? 1 : 0;
+      ok = poll_lin(a, a.xq + (size_t)mrow * H, H, tagp, (uint32_t *)xres);
+    } else if (cur.type == PH_O) {
+      const int w = a.act_bf16 ? a.nq * a.hd / 2 : a.nq * a.hd;
+      ok = poll_rows(a, a.ob, M, w, tagp, opnd, opw);
+    } else {  // PH_D
+      const int w = a.act_bf16 ? a.F / 2 : a.F;
+      ok = poll_rows(a, a.zb, M, w, tagp, opnd, opw);
     }
-    first = false;
+    if (!ok) cm.abort = 1;
+    __syncthreads();  // with the loader wave: inputs in LDS, this phase's slice landed
+    if (cm.abort) return;
     const uint64_t t1 = tracing ? wall_clock64() : 0;
     const uint64_t c1 = tracing ? __builtin_amdgcn_s_memtime() : 0;
 
@@ -723,7 +783,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     if (cur.type == PH_QKV || cur.type == PH_GU || cur.type == PH_HEAD) {
       const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
       const bool talker_head = cur.type == PH_HEAD && cur.stack == 1;
-      for (int m = 0; m < M; ++m) norm_row<WT>(a, cm, xres + m * H, gain, opnd + m * opw, brg, talker_head);
+      for (int m = 0; m < M; ++m) norm_row<WT>(a, xres + m * H, gain, opnd + m * opw, brg, talker_head);
       if (talker_head && lead) {
 #pragma unroll
         for (int k = 0; k < HPAIR; ++k) {
@@ -731,68 +791,64 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           if (2 * pi < H) { st(a.bridge + 2 * pi, brg[2 * k]); st(a.bridge + 2 * pi + 1, brg[2 * k + 1]); }
         }
       }
-      __syncthreads();
+      if (!cbar(a, cm, gen)) return;
     }
     const uint64_t t2 = tracing ? wall_clock64() : 0;
     const uint64_t c2 = tracing ? __builtin_amdgcn_s_memtime() : 0;
-    gemv_slice<WT>(sp, opnd, opw, s, M, res);
-    __syncthreads();
-    const uint64_t t3 = tracing ? wall_clock64() : 0;
 
-    // ---- epilogue: publish this workgroup's rows
-    if (cur.type == PH_QKV) {
-      const int N = s.N;
-      for (int i = tid; i < s.R * M; i += NT) {
-        const int j = i / M, m = i - j * M;
-        tputf(a.qkvb + (size_t)m * N + s.r0 + j, res[j * M + m], tag);
-      }
-    } else if (cur.type == PH_O || cur.type == PH_D) {
-      for (int i = tid; i < s.R * M; i += NT) {
-        const int j = i / M, m = i - j * M, n = s.r0 + j;
-        const float v = xres[m * H + n] + res[j * M + m];
-        tputf(a.xq + (size_t)m * H + n, v, tag);
-        if (cur.type == PH_D && cur.stack == 1 && a.dump) st(a.hidden_dump + (size_t)cur.layer * H + n, v);
-      }
-    } else if (cur.type == PH_GU) {
-      // z = SiLU(g) * u, rounded as the down projection's operand
-      if (a.act_bf16) {
-        for (int i = tid; i < (s.R / 2) * M; i += NT) {
-          const int pp = i / M, m = i - pp * M;
-          float z[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int j = 2 * pp + e;
-            const float g = res[(2 * j) * M + m], u = res[(2 * j + 1) * M + m];
-            z[e] = g / (1.0f + expf(-g)) * u;
+    // ---- GEMV; each wave publishes the rows it computed
+    if (cur.type == PH_GU) {
+      // item = row pair (2 p, 2 p + 1): z = SiLU(g) * u, rounded as the down projection's operand
+      gemv_items<WT, 4, 2>(sp, opnd, opw, s, M, [&](int it, float (&acc)[4][2]) {
+        for (int m = 0; m < M; ++m) {
+          const float z0 = acc[0][m] / (1.0f + expf(-acc[0][m])) * acc[1][m];
+          const float z1 = acc[2][m] / (1.0f + expf(-acc[2][m])) * acc[3][m];
+          if (a.act_bf16) {
+            if (lane == 0) tput(a.zb + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
+          } else if (lane < 2) {
+            tputf(a.zb + (size_t)m * a.F + s.r0 + 2 * it + lane, lane ? z1 : z0, tag);
           }
-          tput(a.zb + (size_t)m * (a.F / 2) + s.r0 / 2 + pp, pack2(z[0], z[1]), tag);
         }
-      } else {
-        for (int i = tid; i < s.R * M; i += NT) {
-          const int j = i / M, m = i - j * M;
-          const float g = res[(2 * j) * M + m], u = res[(2 * j + 1) * M + m];
-          tputf(a.zb + (size_t)m * a.F + s.r0 + j, g / (1.0f + expf(-g)) * u, tag);
-        }
-      }
-    } else {  // PH_HEAD: logits and this workgroup's partial argmax
+      });
+    } else if (cur.type == PH_HEAD) {
+      // logits and the wave's running argmax, then the workgroup's
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      if (tid < 64) {
-        for (int j = tid; j < s.R; j += 64) {
-          const float v = res[j];
-          st(lg + s.r0 + j, v);
-          if (v > bv || (v == bv && s.r0 + j < bi)) { bv = v; bi = s.r0 + j; }
-        }
-        wave_argmax(bv, bi);
-        if (tid == 0) {
-          tputf(a.amax + 2 * gi, bv, tag);
-          tput(a.amax + 2 * gi + 1, (uint32_t)bi, tag);
-        }
+      gemv_items<WT, 1, 2>(sp, opnd, opw, s, 1, [&](int it, float (&acc)[1][2]) {
+        const int n = s.r0 + it;
+        if (lane == 0) st(lg + n, acc[0][0]);
+        pick(bv, bi, acc[0][0], n);
+      });
+      if (lane == 0) { cm.amv[wave] = bv; cm.ami[wave] = bi; }
+      if (!cbar(a, cm, gen)) return;
+      if (tid == 0) {
+        for (int w = 1; w < NW; ++w) pick(bv, bi, cm.amv[w], cm.ami[w]);
+        tputf(a.amax + 2 * gi, bv, tag);
+        tput(a.amax + 2 * gi + 1, (uint32_t)bi, tag);
       }
       pending = true;
       pending_idx = cur.stack ? 0 : cur.step + 1;
+    } else {
+      const int type = cur.type, N = s.N;
+      const bool hid = type == PH_D && cur.stack == 1 && a.dump;
+      gemv_items<WT, 1, 6>(sp, opnd, opw, s, M, [&](int it, float (&acc)[1][2]) {
+        const int n = s.r0 + it;
+        if (lane < M) {
+          const float v = lane ? acc[0][1] : acc[0][0];
+          if (type == PH_QKV) {
+            tputf(a.qkvb + (size_t)lane * N + n, v, tag);
+          } else {
+            const float x = xres[lane * H + n] + v;
+            tputf(a.xq + (size_t)lane * H + n, x, tag);
+            if (hid) st(a.hidden_dump + (size_t)cur.layer * H + n, x);
+          }
+        }
+      });
     }
+    if (lane == 0)  // this wave is done with the phase's slot
+      __hip_atomic_fetch_add(&cm.gdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t t3 = tracing ? wall_clock64() : 0;
     if (tracing && tid == 0) {
       uint64_t *tr = a.trace + 8 * ntr;
       st(tr, (uint64_t)cur.type | ((uint64_t)cur.stack << 8) | ((uint64_t)cur.layer << 16) |
@@ -814,7 +870,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   // the code picked by the last talker head becomes the slot's pending code 0
   if (lead) {
     if (pending) {
-      if (!resolve_code(a, cm, opnd, NG, a.tag_base + seq - 1)) return;
+      if (!cbar(a, cm, gen) || !resolve_code(a, cm, gen, opnd, NG, a.tag_base + seq - 1)) return;
       if (tid == 0) st(a.c0, cm.code);
     }
     if (tid == 0) st(a.pos, pos0 + a.n_frames);
@@ -870,7 +926,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
   constexpr int ROWB = HD * ESZ;           // bytes per K/V row
   constexpr int DPC = 16 / ESZ;            // dims per 16-byte chunk
   constexpr int CPR = HD / DPC;            // chunks per row (lanes per position)
-  constexpr int PG = NT / CPR;             // position groups
+  constexpr int PG = ANT / CPR;             // position groups
   constexpr int W = (GQ + 2) * HD;         // q | k | v words of one row
   static_assert(CPR == 16, "K/V rows of 256 bytes");
   Common &cm = *reinterpret_cast<Common *>(smem);
@@ -894,12 +950,12 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
   // load gains and RoPE rows for event e, then (talker) its K/V tile
   auto prep = [&](const Ev &e) {
     const LayerTab &T = tab_of(a, cm, e.stack, e.layer);
-    for (int i = tid; i < HD; i += NT) {
+    for (int i = tid; i < HD; i += ANT) {
       gq[i] = a.tab_bf16 ? lo16((uint32_t)ld((const uint16_t *)T.q_norm + i)) : ld((const float *)T.q_norm + i);
       gk[i] = a.tab_bf16 ? lo16((uint32_t)ld((const uint16_t *)T.k_norm + i)) : ld((const float *)T.k_norm + i);
     }
     const int p0 = e.stack ? pos0 + e.frame : (e.step == 0 ? 0 : e.step + 1);
-    for (int i = tid; i < HD; i += NT) {
+    for (int i = tid; i < HD; i += ANT) {
       const int m = i / (HD / 2), d = i % (HD / 2);
       const int pm = m ? 1 : p0;
       rc[i] = ld(a.rope_cos + (size_t)pm * (HD / 2) + d);
@@ -943,7 +999,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
       const int ntile = cur.stack ? ntiles_at(p) : 1;
       // ---- q | k | v rows of this KV head
       uint32_t *rb = (uint32_t *)rowbuf;
-      const bool ok = poll(a, M * W, tagp, [=](int i) { return rb + i; }, [=](int i) {
+      const bool ok = poll<ANT>(a, M * W, tagp, [=](int i) { return rb + i; }, [=](int i) {
         const int m = i / W, r = i - m * W;
         const int off = r < GQ * HD ? kh * GQ * HD + r
                         : r < (GQ + 1) * HD ? qd + kh * HD + (r - GQ * HD)
@@ -982,7 +1038,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
       }
       const bool owner = cur.stack == 0 || p < ts + TILE;
       if (owner) {
-        for (int i = tid; i < M * 2 * (ROWB / 8); i += NT) {
+        for (int i = tid; i < M * 2 * (ROWB / 8); i += ANT) {
           const int m = i / (2 * (ROWB / 8)), r = i % (2 * (ROWB / 8));
           const int isv = r >= ROWB / 8, wi = r % (ROWB / 8);
           const int pm = cur.stack ? p : (cur.step == 0 ? m : cur.step + 1);
@@ -1077,7 +1133,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
         // publish: normalised output (one tile) or the tile's partial
         if (ntile == 1) {
           if (a.act_bf16) {
-            for (int i = tid; i < GQ * HD / 2; i += NT) {
+            for (int i = tid; i < GQ * HD / 2; i += ANT) {
               const int g = i / (HD / 2), d = 2 * (i % (HD / 2));
               float o[2];
 #pragma unroll
@@ -1088,14 +1144,14 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
               tput(a.ob + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, pack2(o[0], o[1]), tag);
             }
           } else {
-            for (int i = tid; i < GQ * HD; i += NT) {
+            for (int i = tid; i < GQ * HD; i += ANT) {
               const int g = i / HD;
               const float o = ((pvred[i] + pvred[GQ * HD + i]) + (pvred[2 * GQ * HD + i] + pvred[3 * GQ * HD + i])) / stat[g * 2 + 1];
               tputf(a.ob + (size_t)m * qd + kh * GQ * HD + i, o, tag);
             }
           }
         } else {
-          for (int i = tid; i < GQ * (HD + 2); i += NT) {
+          for (int i = tid; i < GQ * (HD + 2); i += ANT) {
             const int g = i / (HD + 2), d = i % (HD + 2);
             uint64_t *pp = a.part + ((size_t)(kh * GQ + g) * maxT + t) * (HD + 2);
             float v;
@@ -1126,7 +1182,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
       const int ntile = ntiles_at(pos0 + cur.frame);
       uint32_t *buf = (uint32_t *)(smem + L.comb);  // [GQ][ntile][HD + 2]
       const int per = ntile * (HD + 2);
-      const bool ok = poll(a, GQ * per, tagp, [=](int i) { return buf + i; }, [=](int i) {
+      const bool ok = poll<ANT>(a, GQ * per, tagp, [=](int i) { return buf + i; }, [=](int i) {
         const int g = i / per;
         return a.part + ((size_t)(kh * GQ + g) * maxT) * (HD + 2) + (i - g * per);
       });
@@ -1135,7 +1191,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
       if (cm.abort) return;
       const float *pb = (const float *)buf;
       if (a.act_bf16) {
-        for (int i = tid; i < GQ * HD / 2; i += NT) {
+        for (int i = tid; i < GQ * HD / 2; i += ANT) {
           const int g = i / (HD / 2), d = 2 * (i % (HD / 2));
           const float *hp = pb + (size_t)g * ntile * (HD + 2);
           float mx = -INFINITY;
@@ -1150,7 +1206,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
           tput(a.ob + ((kh * GQ + g) * HD + d) / 2, pack2(O0 / Ls, O1 / Ls), tag);
         }
       } else {
-        for (int i = tid; i < GQ * HD; i += NT) {
+        for (int i = tid; i < GQ * HD; i += ANT) {
           const int g = i / HD, d = i % HD;
           const float *hp = pb + (size_t)g * ntile * (HD + 2);
           float mx = -INFINITY;
@@ -1175,11 +1231,15 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
 // ------------------------------------------------------------ the kernel
 
 template <int WT, int HD, int GQ, bool KVB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void frame_kernel(FrameArgs a) {
+__global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   Common &cm = *reinterpret_cast<Common *>(smem);
   const int tid = threadIdx.x;
-  if (tid == 0) cm.abort = 0;
+  if (tid == 0) {
+    cm.abort = 0;
+    cm.cbar = 0;
+    cm.gdone = 0;
+  }
   for (int l = tid; l < a.Lt + a.Lp; l += NT) {
     const LayerDev *src = l < a.Lt ? a.tl + l : a.pl + (l - a.Lt);
     LayerTab &T = cm.lt[l];
@@ -1192,8 +1252,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     cm.head_sc[i] = a.head_sc ? ld(a.head_sc + i) : nullptr;
   }
   __syncthreads();
-  if ((int)blockIdx.x < a.n_attn) attn_role<HD, GQ, KVB>(a, smem);
-  else gemv_role<WT>(a, smem);
+  if ((int)blockIdx.x < a.n_attn) {
+    if (tid < ANT) attn_role<HD, GQ, KVB>(a, smem);  // the other waves end here
+  } else {
+    gemv_role<WT>(a, smem);
+  }
 }
 
 // (weights, head dim, GQA group, bf16 ring) combinations instantiated
@@ -1215,9 +1278,12 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   a.max_tiles = a.P / TILE;
   if (a.P % TILE) { *why = "talker positions not a multiple of 256"; return false; }
   if (a.hd * (a.kv_bf16 ? 2 : 4) != 256) { *why = "K/V rows must be 256 bytes"; return false; }
-  if (a.H > 2 * NT * HPAIR || a.H % 2) { *why = "hidden width above 2048"; return false; }
+  if (a.H > 2048 || a.H % 256) { *why = "hidden width above 2048 or not a multiple of 256"; return false; }
   if (a.Lt + a.Lp > MAXLAYERS || a.G > MAXHEADS) { *why = "too many layers or codebooks"; return false; }
   if (a.nwg > 1024) { *why = "more than 1024 workgroups"; return false; }
+  // GEMV rows held in registers per item: hidden-wide rows (gate/up pairs, heads)
+  // up to 2 KB, the others up to 6 KB
+  if (a.H * esz > 2048 || qd * esz > 6144 || a.F * esz > 6144) { *why = "GEMV rows too wide"; return false; }
   a.n_attn = a.nkv * (max_pos / TILE + 1);
   const int NG = a.nwg - a.n_attn;
   if (NG < 16) { *why = "too few GEMV workgroups"; return false; }
@@ -1253,7 +1319,7 @@ hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void *)frame_kernel<W, HD_, G_, K_>,                \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes); \
     if (e != hipSuccess) return e;                                                               \
-    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_>), dim3(a.nwg), dim3(NT), a.lds_bytes, s, a); \
+    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_>), dim3(a.nwg), dim3(NTB), a.lds_bytes, s, a); \
     return hipGetLastError();                                                                    \
   }
   QT_FRAME_VARIANTS(X)
