@@ -42,7 +42,8 @@ namespace {
 constexpr int NW = 7;            // compute waves of a GEMV workgroup
 constexpr int NT = 64 * NW;      // their threads
 constexpr int NTB = NT + 64;     // plus the loader wave: two waves per SIMD
-constexpr int ANT = 256;         // threads of an attention workgroup
+constexpr int ANT = 512;         // threads of an attention workgroup
+constexpr int ANW = ANT / 64;    // its waves
 constexpr int MAXLAYERS = 40;
 constexpr int MAXHEADS = 32;
 constexpr int PER = 8;          // tagged words per thread per poll round
@@ -232,7 +233,7 @@ __host__ __device__ inline Lds lds_layout(const FrameArgs &a) {
   L.stat = up16(L.sc + (uint32_t)g * a.tile * 4u);
   L.pvred = up16(L.stat + 4u * g * 4u);
   L.comb = L.rowbuf;
-  const uint32_t scratch_end = up16(L.pvred + 4u * g * hd * 4u);
+  const uint32_t scratch_end = up16(L.pvred + (uint32_t)ANW * g * hd * 4u);
   const uint32_t comb_end = L.comb + (uint32_t)g * a.max_tiles * (hd + 2) * 4u;
   L.kv = up1k(scratch_end > comb_end ? scratch_end : comb_end);
   const uint32_t tile_b = 2u * a.tile * rowb, pc_b = (uint32_t)a.Lp * 2u * a.Q * rowb;
@@ -936,7 +937,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
   float *rc = (float *)(smem + L.rc), *rs = (float *)(smem + L.rs);  // [2][HD/2]
   float *sc = (float *)(smem + L.sc);          // [GQ][tile]
   float *stat = (float *)(smem + L.stat);      // [GQ][2] max, sum
-  float *pvred = (float *)(smem + L.pvred);    // [4][GQ][HD]
+  float *pvred = (float *)(smem + L.pvred);    // [ANW][GQ][HD]
   uint8_t *kv = smem + L.kv;
   const uint32_t kv_lds = lds_addr(kv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -972,7 +973,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
         const uint8_t *srcK = a.ring_t + hoff * ESZ;
         const uint8_t *srcV = a.ring_t + (hoff + a.t_kv_stride) * ESZ;
         const int n = nv * ROWB / 16;  // chunks per matrix
-        for (int b = wave; b * 64 < n; b += 4) {
+        for (int b = wave; b * 64 < n; b += ANW) {
           const int idx = min(b * 64 + lane, n - 1);
           dma16_coherent(srcK + (size_t)idx * 16, kv_lds + (uint32_t)b * 1024u);
           dma16_coherent(srcV + (size_t)idx * 16, kv_lds + (uint32_t)(TILE * ROWB) + (uint32_t)b * 1024u);
@@ -1012,7 +1013,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
       if (cm.abort) return;
       const uint64_t t1 = tracing ? wall_clock64() : 0;
       // ---- q/k RMSNorm + RoPE (NeoX halves): one wave per (row, head)
-      for (int it = wave; it < M * (GQ + 1); it += 4) {
+      for (int it = wave; it < M * (GQ + 1); it += ANW) {
         const int m = it / (GQ + 1), h = it % (GQ + 1);
         float *v = rowbuf + (size_t)m * W + h * HD;
         const float *g = h < GQ ? gq : gk;
@@ -1130,6 +1131,13 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
 #pragma unroll
             for (int d = 0; d < DPC; ++d) pvred[(wave * GQ + g) * HD + cc * DPC + d] = acc[g][d];
         __syncthreads();
+        // sum of the waves' partials, element k of [GQ][HD]
+        auto pv = [&](int k) {
+          float v = 0.f;
+#pragma unroll
+          for (int w = 0; w < ANW; ++w) v += pvred[w * GQ * HD + k];
+          return v;
+        };
         // publish: normalised output (one tile) or the tile's partial
         if (ntile == 1) {
           if (a.act_bf16) {
@@ -1139,14 +1147,14 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
                 const int k = g * HD + d + e;
-                o[e] = ((pvred[k] + pvred[GQ * HD + k]) + (pvred[2 * GQ * HD + k] + pvred[3 * GQ * HD + k])) / stat[g * 2 + 1];
+                o[e] = pv(k) / stat[g * 2 + 1];
               }
               tput(a.ob + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, pack2(o[0], o[1]), tag);
             }
           } else {
             for (int i = tid; i < GQ * HD; i += ANT) {
               const int g = i / HD;
-              const float o = ((pvred[i] + pvred[GQ * HD + i]) + (pvred[2 * GQ * HD + i] + pvred[3 * GQ * HD + i])) / stat[g * 2 + 1];
+              const float o = pv(i) / stat[g * 2 + 1];
               tputf(a.ob + (size_t)m * qd + kh * GQ * HD + i, o, tag);
             }
           }
@@ -1157,7 +1165,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
             float v;
             if (d < HD) {
               const int k = g * HD + d;
-              v = (pvred[k] + pvred[GQ * HD + k]) + (pvred[2 * GQ * HD + k] + pvred[3 * GQ * HD + k]);
+              v = pv(k);
             } else {
               v = stat[g * 2 + (d - HD)];
             }
