@@ -33,6 +33,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t rope_cos, rope_sin, pos, c0, bridge, ctl, overlay, cin, cout;
   size_t x, qkv, q, part, o, z, logits_t, logits_p;
+  size_t ssq, gpart, gcnt;  // batched projections: row sums of squares, split-K partials, tile counters
+  size_t gcnt_bytes;
   size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
   // persistent frame kernel: weight tables, tagged exchange words, error flag
   size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_part, f_err, f_trace;
@@ -76,6 +78,19 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.part = take(sizeof(float) * R * d.nq * L.max_tiles * (d.hd + 2));
   L.o = take(sizeof(float) * R * d.qd);
   L.z = take(sizeof(float) * R * d.F);
+  L.ssq = take(sizeof(float) * R * (d.H / 32 > 0 ? d.H / 32 : 1));
+  {
+    // split-K partials of the largest projection: (K / 256) slices x 64 rows x columns
+    const size_t a1 = (size_t)(d.H / 256) * (d.nqkv > 2 * d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (2 * d.F > d.Vc ? 2 * d.F : d.Vc));
+    const size_t a2 = (size_t)(d.qd / 256) * d.H, a3 = (size_t)(d.F / 256) * d.H;
+    const size_t mx = a1 > a2 ? (a1 > a3 ? a1 : a3) : (a2 > a3 ? a2 : a3);
+    L.gpart = take(sizeof(float) * 64 * (mx > 0 ? mx : 1));
+  }
+  {
+    const int nmax = d.nqkv > d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (d.F > d.Vc ? d.F : d.Vc);
+    L.gcnt_bytes = sizeof(uint32_t) * (size_t)(nmax / 32 + 1 + (d.H / 32));  // tiles of every projection
+    L.gcnt = take(L.gcnt_bytes);
+  }
   L.logits_t = take(sizeof(float) * (R > (size_t)B ? R : B) * d.Vc);
   L.logits_p = take(sizeof(float) * (size_t)(d.G - 1) * B * d.Vc);
   L.x0_dump = take(sizeof(float) * B * d.H);
@@ -232,6 +247,35 @@ Stack pred_stack(const qt_ctx *c) {
 }
 
 // One decoder layer over M rows (x in the arena's activation rows).
+// Batched rows (4..64, bf16 or q8 weights with bf16 operands) go through the
+// MFMA GEMM; fewer rows through the GEMV.  All projections of one layer see the
+// same M, so a layer runs entirely on one of the two.
+bool use_gemm(const qt_ctx *c, int M, int K) {
+  const qt_model_desc &md = c->md;
+  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 4 && M <= 64 && K % 256 == 0 && c->d.H % 32 == 0;
+}
+
+// One projection.  ssq_in: the input rows' sums of squares in 32-column slots
+// (row m at ssq_in + m * ssq_stride), needed by the GEMM's RMSNorm; ssq_out:
+// where a residual epilogue leaves the new rows' sums.
+hipError_t project(qt_ctx *c, int epi, const GemvArgs &g, const float *ssq_in, int ssq_stride, float *ssq_out) {
+  const int wt = wtype_of(c->md);
+  if (!use_gemm(c, g.M, g.K)) return launch_gemv(wt, epi, g, c->stream);
+  GemmArgs a = {};
+  for (int i = 0; i < 3; ++i) { a.seg[i] = g.seg[i]; a.seg_end[i] = g.seg_end[i]; }
+  a.nseg = g.nseg; a.up = g.up;
+  a.N = g.N; a.K = g.K; a.M = g.M;
+  a.x = g.x; a.x_stride = g.x_stride;
+  a.gain = g.gain; a.gain_bf16 = g.gain_bf16; a.eps = g.eps;
+  a.ssq = ssq_in; a.ssq_stride = ssq_stride;
+  a.y = g.y; a.y_stride = g.y_stride;
+  a.ssq_out = ssq_out; a.normed_out = g.normed_out;
+  a.copy_out = g.copy_out; a.copy_stride = g.copy_stride;
+  a.part = c->A<float>(c->L.gpart);
+  a.cnt = c->A<uint32_t>(c->L.gcnt);
+  return launch_gemm(wt, epi, a, c->stream);
+}
+
 hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap &rows,
                          float *hidden_copy) {
   const Dims &d = c->d;
@@ -260,7 +304,9 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   g.x = x; g.x_stride = d.H; g.M = M;
   g.gain = w.attn_norm;
   g.y = qkv; g.y_stride = d.nqkv;
-  if ((e = launch_gemv(wt, EPI_STORE, g, s)) != hipSuccess) return e;
+  float *ssq = c->A<float>(c->L.ssq);
+  const int ss = d.H / 32;
+  if ((e = project(c, EPI_STORE, g, ssq, ss, nullptr)) != hipSuccess) return e;
 
   // 2. q/k norm + RoPE + K/V rows into the ring at the row's position
   QkArgs qa = {};
@@ -285,14 +331,14 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   go.seg[0] = lin(w.wo); go.nseg = 1; go.seg_end[0] = d.H;
   go.N = d.H; go.K = d.qd; go.x = o; go.x_stride = d.qd; go.gain = nullptr;
   go.y = x; go.y_stride = d.H;
-  if ((e = launch_gemv(wt, EPI_RESID, go, s)) != hipSuccess) return e;
+  if ((e = project(c, EPI_RESID, go, nullptr, 0, ssq)) != hipSuccess) return e;
 
   // 5. gate/up with the MLP RMSNorm prologue, SiLU-multiply epilogue
   GemvArgs gu = g;
   gu.seg[0] = lin(w.wg); gu.up = lin(w.wu); gu.nseg = 1; gu.seg_end[0] = d.F;
   gu.N = d.F; gu.K = d.H; gu.x = x; gu.x_stride = d.H; gu.gain = w.mlp_norm;
   gu.y = z; gu.y_stride = d.F;
-  if ((e = launch_gemv(wt, EPI_GATED, gu, s)) != hipSuccess) return e;
+  if ((e = project(c, EPI_GATED, gu, ssq, ss, nullptr)) != hipSuccess) return e;
 
   // 6. down projection, residual added in the epilogue
   GemvArgs gd = g;
@@ -300,7 +346,7 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   gd.N = d.H; gd.K = d.F; gd.x = z; gd.x_stride = d.F; gd.gain = nullptr;
   gd.y = x; gd.y_stride = d.H;
   gd.copy_out = hidden_copy; gd.copy_stride = d.H;
-  return launch_gemv(wt, EPI_RESID, gd, s);
+  return project(c, EPI_RESID, gd, nullptr, 0, ssq);
 }
 
 // Frame k of a replay: predictor (codes 1..G-1) then the talker step.
@@ -320,6 +366,9 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
   pa.bridge = c->A<float>(c->L.bridge); pa.code_emb = c->code_emb; pa.tab_bf16 = md.tab_bf16;
   pa.H = d.H; pa.G = d.G; pa.B = B; pa.c0_state = c->A<int32_t>(c->L.c0); pa.ctl = ctl; pa.k = k;
   pa.cin = c->A<int32_t>(c->L.cin); pa.cout = c->A<int32_t>(c->L.cout); pa.x = x;
+  float *ssq = c->A<float>(c->L.ssq);
+  const int ss = d.H / 32;
+  pa.ssq = ssq;
   if ((e = launch_pred_input(pa, s)) != hipSuccess) return e;
 
   const Stack ps = pred_stack(c);
@@ -337,11 +386,11 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
     h.gain = c->p_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
     float *lg = c->A<float>(c->L.logits_p) + (size_t)j * B * d.Vc;
     h.y = lg; h.y_stride = d.Vc;
-    if ((e = launch_gemv(wt, EPI_STORE, h, s)) != hipSuccess) return e;
+    if ((e = project(c, EPI_STORE, h, j == 0 ? ssq + ss : ssq, j == 0 ? 2 * ss : ss, nullptr)) != hipSuccess) return e;
     ArgmaxArgs am = {};
     am.logits = lg; am.Vc = d.Vc; am.M = B; am.mode = AM_PRED; am.j = j; am.ctl = ctl; am.k = k;
     am.B = B; am.G = d.G; am.cin = pa.cin; am.cout = pa.cout; am.code_emb = c->code_emb;
-    am.tab_bf16 = md.tab_bf16; am.H = d.H; am.x_next = x;
+    am.tab_bf16 = md.tab_bf16; am.H = d.H; am.x_next = x; am.ssq = ssq;
     if ((e = launch_argmax(am, s)) != hipSuccess) return e;
   }
 
@@ -355,6 +404,7 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
   ga.x = x; ga.M = B;
   ga.x0_dump = dump ? c->A<float>(c->L.x0_dump) : nullptr;
   ga.gather_dump = dump ? c->A<int32_t>(c->L.gather_dump) : nullptr;
+  ga.ssq = ssq;
   if ((e = launch_gather(ga, s)) != hipSuccess) return e;
 
   const Stack ts = talker_stack(c);
@@ -370,7 +420,7 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
   h.gain = c->t_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
   h.normed_out = c->A<float>(c->L.bridge);
   h.y = c->A<float>(c->L.logits_t); h.y_stride = d.Vc;
-  if ((e = launch_gemv(wt, EPI_STORE, h, s)) != hipSuccess) return e;
+  if ((e = project(c, EPI_STORE, h, ssq, ss, nullptr)) != hipSuccess) return e;
   ArgmaxArgs am = {};
   am.logits = h.y; am.Vc = d.Vc; am.M = B; am.mode = AM_TALKER; am.ctl = ctl; am.k = k;
   am.B = B; am.G = d.G; am.c0_state = c->A<int32_t>(c->L.c0); am.pos = c->A<int32_t>(c->L.pos);
@@ -532,6 +582,11 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
         hipStreamSynchronize(c->stream) != hipSuccess)
       return bail(fail(c, QT_E_HIP, "RoPE table upload failed"));
   }
+  // the batched projections' tile counters start at zero (their last workgroup resets them);
+  // cleared here, before any capture
+  if (hipMemsetAsync(c->arena + c->L.gcnt, 0, c->L.gcnt_bytes, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return bail(fail(c, QT_E_HIP, "counter clear failed"));
   // decode path: persistent frame kernel where it applies
   c->path = (c->flags & QT_F_EAGER) ? QT_PATH_EAGER : QT_PATH_GRAPH;
   if (!(c->flags & (QT_F_EAGER | QT_F_OPS)) && !frame_unsupported(m, c->B)) {
@@ -634,6 +689,7 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
     ga.H = d.H; ga.Vc = d.Vc; ga.G = d.G;
     ga.codes = codes ? pf_codes + (size_t)r0 * d.G : nullptr; ga.codes_stride = d.G;
     ga.text = pf_text + r0; ga.text_stride = 1; ga.x = x; ga.M = M;
+    ga.ssq = c->A<float>(c->L.ssq);
     HIPCHK(c, launch_gather(ga, s));
     // rows of one slot at positions r0 .. r0+M-1, causal through the mask
     const RowMap rows{slot, M, r0, nullptr};

@@ -88,6 +88,7 @@ struct GatherArgs {
   int32_t M;
   float *x0_dump;
   int32_t *gather_dump;  // [M][G+1]
+  float *ssq;            // optional: row sums of squares in 32-column slots [M][H/32]
 };
 
 struct PredInArgs {
@@ -99,6 +100,7 @@ struct PredInArgs {
   int32_t k;           // frame within the replay
   int32_t *cin, *cout; // [frames][B][G]
   float *x;            // rows 2b = bridge[b], 2b+1 = E_0[c0]
+  float *ssq;          // optional: row sums of squares in 32-column slots [2B][H/32]
 };
 
 enum ArgMode { AM_PRED = 0, AM_TALKER = 1, AM_PREFILL = 2 };
@@ -114,8 +116,38 @@ struct ArgmaxArgs {
   const void *code_emb;
   int32_t tab_bf16, H;
   float *x_next;  // AM_PRED: row b <- E_{j+1}[code] when j+1 < G-1
+  float *ssq;     // optional: x_next row sums of squares in 32-column slots [M][H/32]
   int32_t slot;   // AM_PREFILL
 };
+
+// Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 64 rows,
+// bf16 or q8 weights with bf16 operands.  Tiles of 32 output columns (gated:
+// 32 gate + 32 up rows) x all rows x 256-wide K slices; the last workgroup of
+// a tile to finish sums the K slices' partials in order and applies the
+// epilogue.
+struct GemmArgs {
+  Lin seg[3];          // row segments (q|k|v) ...
+  int32_t seg_end[3];  // ... rows [seg_end[i-1], seg_end[i]) read seg[i]
+  int32_t nseg;
+  Lin up;              // EPI_GATED: the up matrix (seg[0] is the gate)
+  int32_t N, K, M;
+  const float *x;
+  int32_t x_stride;
+  const void *gain;    // RMSNorm gain, or null: no norm
+  int32_t gain_bf16;
+  float eps;
+  const float *ssq;    // with gain: row m's sums of squares at ssq[m * ssq_stride + i], i < K / 32
+  int32_t ssq_stride;
+  float *y;
+  int32_t y_stride;
+  float *ssq_out;      // EPI_RESID: new rows' sums of squares in 32-column slots [M][N/32]
+  float *normed_out;   // optional: f32 normed rows [M][K] (the talker bridge)
+  float *copy_out;     // EPI_RESID: also store the new row here
+  int32_t copy_stride;
+  float *part;         // [K/256][M][N or 2N] split-K partials
+  uint32_t *cnt;       // [tiles] arrival counters, zero between launches
+};
+hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s);
 
 hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s);
 hipError_t launch_qk_rope_kv(int hd, int kv_bf16, const QkArgs &a, hipStream_t s);

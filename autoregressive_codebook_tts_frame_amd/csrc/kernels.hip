@@ -488,6 +488,219 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------------ batched projections (MFMA)
+//
+// y[M][N] = epi(x~ . W^T) for M <= 64 rows: x~ = bf16(x * rinv * gain) (or
+// bf16(x)); weight rows in their storage format (bf16, or q8 converted exactly
+// to bf16 with the 32-wide block scale applied to each block's product).
+// v_mfma_f32_16x16x32_bf16 lane layout (checked on the device): A[16][32]
+// row l%16, k (l/16)*8..+8; B[32][16] k (l/16)*8..+8, column l%16; D[16][16]
+// c[j] at row (l/16)*4+j, column l%16.  A = 16 weight rows, B = 16 activation
+// rows (transposed), so D[j] is the partial of y[m = l%16][n = (l/16)*4 + j].
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int GT = 32;        // output columns per tile
+constexpr int GBK = 256;      // K slice per workgroup
+constexpr int GXS = GBK + 8;  // LDS row stride (bf16) of the staged operand: conflict-free B reads
+
+template <int WT>
+__device__ __forceinline__ const uint8_t *gemm_row(const GemmArgs &a, int mat, int n, const uint16_t *&sc) {
+  constexpr size_t esz = WT == W_BF16 ? 2 : 1;
+  const Lin *L = &a.up;
+  int r = n;
+  if (mat == 0) {
+    int s = 0, base = 0;
+    while (s + 1 < a.nseg && n >= a.seg_end[s]) { base = a.seg_end[s]; ++s; }
+    L = &a.seg[s];
+    r = n - base;
+  }
+  sc = L->sc ? L->sc + (size_t)r * (a.K / 32) : nullptr;
+  return (const uint8_t *)L->w + (size_t)r * a.K * esz;
+}
+
+__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int b) {
+  const float lo = (float)(int8_t)(w >> (8 * b)), hi = (float)(int8_t)(w >> (8 * b + 8));
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+template <int WT, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+  constexpr int NSUB = EPI == EPI_GATED ? 4 : 2;  // 16-row weight blocks per tile
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * GXS];
+  __shared__ float rinv[64];
+  __shared__ int last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tn = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
+  const int M = a.M, K = a.K, N = a.N;
+  const int MT = (M + 15) / 16;
+  const int k0 = ks * GBK;
+  const int NP = EPI == EPI_GATED ? 2 * N : N;  // partial columns (gated: gate then up)
+
+  // RMSNorm row scales from the producers' sums of squares
+  if (tid < 64) {
+    float r = 1.f;
+    if (a.gain && tid < M) {
+      float sq = 0.f;
+      for (int i = 0; i < K / 32; ++i) sq += a.ssq[(size_t)tid * a.ssq_stride + i];
+      r = 1.0f / sqrtf(sq / (float)K + a.eps);
+    }
+    rinv[tid] = r;
+  }
+  __syncthreads();
+  // operand slice in LDS: rows < MT * 16 (zero past M), eight columns per item
+  for (int e = tid; e < MT * 16 * (GBK / 8); e += 256) {
+    const int m = e / (GBK / 8), c = e % (GBK / 8);
+    const int k = k0 + 8 * c;
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
+    if (m < M) {
+      const float *xr = a.x + (size_t)m * a.x_stride + k;
+      const float4 v0 = *(const float4 *)xr, v1 = *(const float4 *)(xr + 4);
+      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if (a.gain) {
+        const float r = rinv[m];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] * r * tab_at(a.gain, a.gain_bf16, k + i);
+        if (a.normed_out && tn == 0)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a.normed_out[(size_t)m * K + k + i] = v[i];
+      }
+      o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+      o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+      o.z = (uint32_t)bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
+      o.w = (uint32_t)bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
+    }
+    *(uint4 *)&xs[m * GXS + 8 * c] = o;
+  }
+  __syncthreads();
+
+  // products: wave w takes (weight block nb, row block mt) pairs p = w, w + 4, ...
+  for (int p = wave; p < NSUB * MT; p += 4) {
+    const int nb = p % NSUB, mt = p / NSUB;
+    const int mat = EPI == EPI_GATED ? nb / 2 : 0;
+    const int nrow0 = tn * GT + (EPI == EPI_GATED ? (nb % 2) : nb) * 16;
+    const int n = nrow0 + (lane & 15);  // the weight row this lane loads
+    const uint16_t *sc;
+    const uint8_t *wr = gemm_row<WT>(a, mat, n < N ? n : 0, sc);
+    const uint16_t *scj[4];  // q8: scale rows of this lane's four outputs
+    if constexpr (WT == W_Q8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int nj = nrow0 + (lane >> 4) * 4 + j;
+        const uint16_t *s2;
+        (void)gemm_row<WT>(a, mat, nj < N ? nj : 0, s2);
+        scj[j] = s2;
+      }
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int st = 0; st < GBK / 32; ++st) {
+      const int k = k0 + st * 32 + (lane >> 4) * 8;
+      const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + st * 32 + (lane >> 4) * 8];
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bx);
+      if constexpr (WT == W_BF16) {
+        const uint4 w = *(const uint4 *)(wr + (size_t)k * 2);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), bv, acc, 0, 0, 0);
+      } else {
+        const uint2 w = *(const uint2 *)(wr + k);
+        const uint4 wq = make_uint4(i8pair_bf16(w.x, 0), i8pair_bf16(w.x, 2), i8pair_bf16(w.y, 0), i8pair_bf16(w.y, 2));
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wq), bv, zero, 0, 0, 0);
+        const int blk = (k0 + st * 32) / 32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += t[j] * f16_to_f32(scj[j][blk]);
+      }
+    }
+    // partials at agent scope, so the tile's last workgroup reads them from any XCD
+    const int m = mt * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nj = nrow0 + (lane >> 4) * 4 + j;
+      if (m < M && nj < N)
+        __hip_atomic_store(a.part + ((size_t)ks * M + m) * NP + (mat ? N : 0) + nj, acc[j], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(a.cnt + tn, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == (uint32_t)(KS - 1);
+    if (last) __hip_atomic_store(a.cnt + tn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+
+  // the tile's last workgroup: sum the K slices in order, then the epilogue;
+  // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile
+  const int m = tid >> 2, c0 = (tid & 3) * 8;
+  float sq = 0.f;
+  if (m < M) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = tn * GT + c0 + i;
+      if (n >= N) break;
+      float g = 0.f, u = 0.f;
+      for (int q = 0; q < KS; ++q) {
+        const float *pr = a.part + ((size_t)q * M + m) * NP;
+        g += __hip_atomic_load(pr + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (EPI == EPI_GATED) u += __hip_atomic_load(pr + N + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float *yp = a.y + (size_t)m * a.y_stride + n;
+      if constexpr (EPI == EPI_STORE) {
+        *yp = g;
+      } else if constexpr (EPI == EPI_RESID) {
+        const float v = *yp + g;
+        *yp = v;
+        if (a.copy_out) a.copy_out[(size_t)m * a.copy_stride + n] = v;
+        sq += v * v;
+      } else {
+        *yp = silu(g) * u;
+      }
+    }
+  }
+  if (EPI == EPI_RESID && a.ssq_out) {
+    sq += __shfl_xor(sq, 1, 64);
+    sq += __shfl_xor(sq, 2, 64);
+    if ((tid & 3) == 0 && m < M) a.ssq_out[(size_t)m * (N / 32) + tn] = sq;
+  }
+}
+
+template <int WT>
+static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
+  const dim3 grid((a.N + GT - 1) / GT, a.K / GBK);
+  if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE>), grid, dim3(256), 0, s, a);
+  else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
+  if (a.M < 1 || a.M > 64 || a.K % GBK) return hipErrorInvalidValue;
+  if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);
+  if (wtype == W_Q8) return gemm_wt<W_Q8>(epi, a, s);
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ row sums of squares
+//
+// Producers of residual rows also leave the rows' sums of squares in 32-column
+// slots ([row][H/32]) for the batched projections' RMSNorm.  A block covering
+// columns [c0, c0 + n) writes its sum into slot c0/32 and zeros into the other
+// slots it covers.
+__device__ __forceinline__ void put_ssq(float *ssq, int H, int row, int c0, int n, float v) {
+  __shared__ float red[4];
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int ns = (n + 31) / 32;
+  if ((int)threadIdx.x < ns)
+    ssq[(size_t)row * (H / 32) + c0 / 32 + threadIdx.x] =
+        threadIdx.x == 0 ? (red[0] + red[1]) + (red[2] + red[3]) : 0.f;
+}
+
 // ------------------------------------------------------------------ gather-sum
 //
 // Talker input: sum of the G code rows plus the overlay row, accumulated in
@@ -507,6 +720,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     acc += tab_at(a.text_emb, a.tab_bf16, (size_t)text * a.H + i);
     a.x[(size_t)r * a.H + i] = acc;
     if (a.x0_dump) a.x0_dump[(size_t)r * a.H + i] = acc;
+  }
+  if (a.ssq) {
+    float v = 0.f;
+    if (i < a.H) v = a.x[(size_t)r * a.H + i];
+    put_ssq(a.ssq, a.H, r, blockIdx.y * 256, min(256, a.H - (int)blockIdx.y * 256), v * v);
   }
   if (a.gather_dump && blockIdx.y == 0 && threadIdx.x <= a.G) {
     const int g = threadIdx.x;
@@ -533,9 +751,18 @@ __global__ __launch_bounds__(256) void pred_input_kernel(PredInArgs a) {
   int32_t *cin = a.cin + ((size_t)f * a.B + b) * a.G;
   int32_t *cout = a.cout + ((size_t)f * a.B + b) * a.G;
   const int c = force ? cin[0] : a.c0_state[b];
+  float v0 = 0.f, v1 = 0.f;
   if (i < a.H) {
-    a.x[(size_t)(2 * b) * a.H + i] = a.bridge[(size_t)b * a.H + i];
-    a.x[(size_t)(2 * b + 1) * a.H + i] = tab_at(a.code_emb, a.tab_bf16, (size_t)c * a.H + i);
+    v0 = a.bridge[(size_t)b * a.H + i];
+    v1 = tab_at(a.code_emb, a.tab_bf16, (size_t)c * a.H + i);
+    a.x[(size_t)(2 * b) * a.H + i] = v0;
+    a.x[(size_t)(2 * b + 1) * a.H + i] = v1;
+  }
+  if (a.ssq) {
+    const int n = min(256, a.H - (int)blockIdx.y * 256);
+    put_ssq(a.ssq, a.H, 2 * b, blockIdx.y * 256, n, v0 * v0);
+    __syncthreads();
+    put_ssq(a.ssq, a.H, 2 * b + 1, blockIdx.y * 256, n, v1 * v1);
   }
   if (blockIdx.y == 0 && threadIdx.x == 0) {
     cout[0] = a.c0_state[b];
@@ -600,7 +827,13 @@ __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
     __syncthreads();
     const int c = code;
     const size_t base = ((size_t)(a.j + 1) * a.Vc + c) * a.H;
-    for (int i = tid; i < a.H; i += 256) a.x_next[(size_t)r * a.H + i] = tab_at(a.code_emb, a.tab_bf16, base + i);
+    float sq = 0.f;
+    for (int i = tid; i < a.H; i += 256) {
+      const float v = tab_at(a.code_emb, a.tab_bf16, base + i);
+      a.x_next[(size_t)r * a.H + i] = v;
+      sq += v * v;
+    }
+    if (a.ssq) put_ssq(a.ssq, a.H, r, 0, a.H, sq);
   }
 }
 

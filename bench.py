@@ -133,8 +133,9 @@ def main():
     d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf,
                    flags=qt.QT_F_OPS if args.ops else 0)
     lens = []
+    ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
     for b in range(B):
-        codes, text = synth.make_prompt(wl, b)
+        codes, text = synth.make_prompt(wl, b, T=int(ctx[b]))
         d.prefill(b, codes, text)
         lens.append(len(text))
     states = [d.get_state(b) for b in range(B)]

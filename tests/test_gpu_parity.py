@@ -269,6 +269,24 @@ def test_reduced_q8_random_scales_parity():
     _check(_forced_run(m, w, wl, 4, batch=2), m, "reduced_q8")
 
 
+def test_reduced_bf16_batched_parity():
+    # eight streams: the projections run on the batched MFMA GEMM (8- and
+    # 16-row predictor steps, 8-row talker steps, 32-row prefill chunks)
+    m = _reduced(synth.BIG)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
+    say("[reduced bf16 batched] 4 frames, batch 8")
+    _check(_forced_run(m, w, wl, 4, batch=8), m, "reduced_bf16_b8")
+
+
+def test_reduced_q8_batched_parity():
+    m = _reduced(synth.BIG_Q8)
+    w = synth.make_weights(m, random_q8_scales=True)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
+    say("[reduced q8 batched] 3 frames, batch 8")
+    _check(_forced_run(m, w, wl, 3, batch=8), m, "reduced_q8_b8")
+
+
 @pytest.mark.timeout(900)
 def test_full_bf16_b1_parity():
     m = synth.BIG
