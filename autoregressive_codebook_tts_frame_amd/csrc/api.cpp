@@ -252,7 +252,9 @@ Stack pred_stack(const qt_ctx *c) {
 // same M, so a layer runs entirely on one of the two.
 bool use_gemm(const qt_ctx *c, int M, int K) {
   const qt_model_desc &md = c->md;
-  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 4 && M <= 64 && K % 256 == 0 && c->d.H % 32 == 0;
+  const Dims &d = c->d;
+  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 4 && M <= 64 && K % 256 == 0 && d.H % 32 == 0 &&
+         d.nqkv % 32 == 0 && d.F % 32 == 0 && d.Vc % 32 == 0;
 }
 
 // One projection.  ssq_in: the input rows' sums of squares in 32-column slots
@@ -854,12 +856,15 @@ int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, 
   gu.nseg = 1; gu.seg_end[0] = d.F; gu.N = d.F; gu.K = d.H;
   gu.x = c->A<float>(c->L.x); gu.x_stride = d.H; gu.M = c->B;
   gu.y = c->A<float>(c->L.z); gu.y_stride = d.F;
+  // as the per-op decode path runs it: the GEMV at batch <= 3, the MFMA GEMM
+  // for 4..64 rows (its row norms read the sums of squares the last decode left)
+  (void)wt;
   hipError_t err = hipEventRecord(e0, s);
   int launches = 0;
   for (int r = 0; r < reps && err == hipSuccess; ++r)
     for (const qt_layer_weights *L : layers) {
       gu.seg[0] = lin(L->wg); gu.up = lin(L->wu); gu.gain = L->mlp_norm;
-      if ((err = launch_gemv(wt, EPI_GATED, gu, s)) != hipSuccess) break;
+      if ((err = project(c, EPI_GATED, gu, c->A<float>(c->L.ssq), d.H / 32, nullptr)) != hipSuccess) break;
       ++launches;
     }
   if (err == hipSuccess) err = hipEventRecord(e1, s);

@@ -345,8 +345,44 @@ hipError_t launch_qk_rope_kv(int hd, int kv_bf16, const QkArgs &a, hipStream_t s
 // read.  One tile: the block normalises and writes o; several: it writes
 // (max, sum, acc) partials that the combine kernel merges in tile order.
 
+// Row sums over groups of L lanes (L = 8, 16 or 32); every lane of a group
+// gets its group's sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <>
+__device__ __forceinline__ float group_sum<16>(float v) {  // one DPP row
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, true));
+  return v;
+}
+
+// 16-byte K/V chunk -> floats
+template <bool KVB>
+__device__ __forceinline__ void kv_unpack(uint4 w, float *v) {
+  if constexpr (KVB) {
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  } else {
+    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+  }
+}
+
+// Lanes work in groups of CPR = one K/V row (16-byte chunk each): a row is one
+// coalesced read, PG = 256 / CPR rows per pass, and every chunk a thread needs
+// is requested before it is used.
 template <int HD, int G, bool KVB>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
+  constexpr int ESZ = KVB ? 2 : 4;
+  constexpr int DPC = 16 / ESZ;   // values per chunk
+  constexpr int CPR = HD / DPC;   // chunks per row
+  constexpr int PG = 256 / CPR;   // rows per pass
+  constexpr int NP = 256 / PG;    // passes over a full tile
   const int r = blockIdx.x, kh = blockIdx.y, t = blockIdx.z;
   const int slot = row_slot(a.rows, r), pos = row_pos(a.rows, r);
   const int j0 = t * a.tile;
@@ -354,86 +390,117 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   const int jn = min(a.tile, pos + 1 - j0);
   const int ntiles = (pos + a.tile) / a.tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pg = tid / CPR, cc = tid % CPR;
 
   __shared__ float qs[G][HD];
   __shared__ float sc[G][256];
-  __shared__ float red[G][4];
   __shared__ float stat[G][2];
+  __shared__ float red[4][G][HD];
 
   for (int i = tid; i < G * HD; i += 256)
     qs[i / HD][i % HD] = a.q[(size_t)r * a.nq * HD + (size_t)kh * G * HD + i];
   __syncthreads();
 
   const size_t head_off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD;
-  // scores: one thread per position
-  if (tid < a.tile) {
-    if (tid < jn) {
-      float s[G];
+  const uint8_t *kbase = (const uint8_t *)a.ring_layer + (head_off + (size_t)j0 * HD) * ESZ;
+  const uint8_t *vbase = (const uint8_t *)a.ring_layer + (head_off + a.kv_stride + (size_t)j0 * HD) * ESZ;
+
+  // scores
+  {
+    uint4 kc[NP];
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = 0.f;
-      const size_t roff = head_off + (size_t)(j0 + tid) * HD;
-      for (int d = 0; d < HD; d += 8) {
-        float kv[8];
-        if constexpr (KVB) {
-          const uint4 w = *(const uint4 *)((const uint16_t *)a.ring_layer + roff + d);
-          kv[0] = bf16_lo(w.x); kv[1] = bf16_hi(w.x); kv[2] = bf16_lo(w.y); kv[3] = bf16_hi(w.y);
-          kv[4] = bf16_lo(w.z); kv[5] = bf16_hi(w.z); kv[6] = bf16_lo(w.w); kv[7] = bf16_hi(w.w);
-        } else {
-          const float4 v0 = *(const float4 *)((const float *)a.ring_layer + roff + d);
-          const float4 v1 = *(const float4 *)((const float *)a.ring_layer + roff + d + 4);
-          kv[0] = v0.x; kv[1] = v0.y; kv[2] = v0.z; kv[3] = v0.w;
-          kv[4] = v1.x; kv[5] = v1.y; kv[6] = v1.z; kv[7] = v1.w;
-        }
+    for (int p = 0; p < NP; ++p) {
+      const int j = p * PG + pg;
+      kc[p] = j < jn ? *(const uint4 *)(kbase + (size_t)j * HD * ESZ + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float qr[G][DPC];
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s[g] += qs[g][d + i] * kv[i];
+      for (int e = 0; e < DPC; ++e) qr[g][e] = qs[g][cc * DPC + e];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (p * PG >= jn) break;
+      const int j = p * PG + pg;
+      float kf[8];
+      kv_unpack<KVB>(kc[p], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) d += qr[g][e] * kf[e];
+        d = group_sum<CPR>(d);
+        if (cc == 0 && j < jn) sc[g][j] = d * a.scale;
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g) sc[g][tid] = s[g] * a.scale;
-    } else {
-#pragma unroll
-      for (int g = 0; g < G; ++g) sc[g][tid] = -INFINITY;
     }
   }
   __syncthreads();
-
-  // per query head: max, exp, sum (block tree in fixed order)
-  for (int g = 0; g < G; ++g) {
-    float v = (tid < a.tile) ? sc[g][tid] : -INFINITY;
-    v = wave_max(v);
-    if (lane == 0) red[g][wave] = v;
-  }
-  __syncthreads();
-  if (tid < G) stat[tid][0] = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    float e = 0.f;
-    if (tid < jn) e = expf(sc[g][tid] - stat[g][0]);
-    if (tid < a.tile) sc[g][tid] = e;
-    e = wave_sum(e);
-    if (lane == 0) red[g][wave] = e;
-  }
-  __syncthreads();
-  if (tid < G) stat[tid][1] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
-  __syncthreads();
-
-  // P.V: thread (g, d)
-  if (tid < G * HD) {
-    const int g = tid / HD, d = tid % HD;
-    float acc = 0.f;
-    const size_t voff = head_off + a.kv_stride + (size_t)j0 * HD + d;
-    for (int j = 0; j < jn; ++j) {
-      const float v = KVB ? bf16_at((const uint16_t *)a.ring_layer, voff + (size_t)j * HD)
-                          : ((const float *)a.ring_layer)[voff + (size_t)j * HD];
-      acc += sc[g][j] * v;
+  // softmax statistics: one wave per query head
+  for (int g = wave; g < G; g += 4) {
+    float mx = -INFINITY;
+    for (int j = lane; j < jn; j += 64) mx = fmaxf(mx, sc[g][j]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int j = lane; j < jn; j += 64) {
+      const float e = expf(sc[g][j] - mx);
+      sc[g][j] = e;
+      sum += e;
     }
+    sum = wave_sum(sum);
+    if (lane == 0) { stat[g][0] = mx; stat[g][1] = sum; }
+  }
+  __syncthreads();
+  // P.V: lanes (pg, chunk cc) accumulate their rows
+  {
+    uint4 vc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int j = p * PG + pg;
+      vc[p] = j < jn ? *(const uint4 *)(vbase + (size_t)j * HD * ESZ + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float acc[G][DPC];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < DPC; ++e) acc[g][e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (p * PG >= jn) break;
+      const int j = p * PG + pg;
+      if (j < jn) {
+        float vf[8];
+        kv_unpack<KVB>(vc[p], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float e = sc[g][j];
+#pragma unroll
+          for (int d = 0; d < DPC; ++d) acc[g][d] += e * vf[d];
+        }
+      }
+    }
+    // row groups inside the wave (lanes cc, cc + CPR, ...), then across waves
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int d = 0; d < DPC; ++d)
+#pragma unroll
+        for (int o = CPR; o < 64; o <<= 1) acc[g][d] += __shfl_xor(acc[g][d], o, 64);
+    if (lane < CPR)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DPC; ++d) red[wave][g][cc * DPC + d] = acc[g][d];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * HD; i += 256) {
+    const int g = i / HD, d = i % HD;
+    const float o = (red[0][g][d] + red[1][g][d]) + (red[2][g][d] + red[3][g][d]);
     const int h = kh * G + g;
     if (ntiles == 1) {
-      a.o[(size_t)r * a.nq * HD + (size_t)h * HD + d] = acc / stat[g][1];
+      a.o[(size_t)r * a.nq * HD + (size_t)h * HD + d] = o / stat[g][1];
     } else {
       float *p = a.part + (((size_t)r * a.nq + h) * a.max_tiles + t) * (HD + 2);
-      p[d] = acc;
+      p[d] = o;
       if (d == 0) {
         p[HD] = stat[g][0];
         p[HD + 1] = stat[g][1];
@@ -526,11 +593,22 @@ __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int b) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
+// split-K partials are written and read back with 16-byte buffer accesses at
+// agent scope (cache policy sc1), so the tile's last workgroup, on any XCD,
+// reads what the others wrote
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0x7fffffff, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+
 template <int WT, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int NSUB = EPI == EPI_GATED ? 4 : 2;  // 16-row weight blocks per tile
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * GXS];
   __shared__ float rinv[64];
+  __shared__ float gs[GBK];
   __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tn = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
@@ -538,6 +616,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int MT = (M + 15) / 16;
   const int k0 = ks * GBK;
   const int NP = EPI == EPI_GATED ? 2 * N : N;  // partial columns (gated: gate then up)
+  const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.part);
 
   // RMSNorm row scales from the producers' sums of squares
   if (tid < 64) {
@@ -549,23 +628,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
     rinv[tid] = r;
   }
+  gs[tid] = a.gain ? tab_at(a.gain, a.gain_bf16, k0 + tid) : 1.f;  // GBK == blockDim
   __syncthreads();
-  // operand slice in LDS: rows < MT * 16 (zero past M), eight columns per item
-  for (int e = tid; e < MT * 16 * (GBK / 8); e += 256) {
-    const int m = e / (GBK / 8), c = e % (GBK / 8);
-    const int k = k0 + 8 * c;
+  // operand slice in LDS: rows < MT * 16 (zero past M), eight columns per item;
+  // a thread's (at most eight) items load first, then convert
+  constexpr int IT = 64 * (GBK / 8) / 256;
+  float4 xv[IT][2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
+    xv[it][0] = xv[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m < M) {
+      const float *xr = a.x + (size_t)m * a.x_stride + k0 + 8 * c;
+      xv[it][0] = *(const float4 *)xr;
+      xv[it][1] = *(const float4 *)(xr + 4);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
+    if (m >= MT * 16) break;
+    float v[8] = {xv[it][0].x, xv[it][0].y, xv[it][0].z, xv[it][0].w,
+                  xv[it][1].x, xv[it][1].y, xv[it][1].z, xv[it][1].w};
     uint4 o = make_uint4(0u, 0u, 0u, 0u);
     if (m < M) {
-      const float *xr = a.x + (size_t)m * a.x_stride + k;
-      const float4 v0 = *(const float4 *)xr, v1 = *(const float4 *)(xr + 4);
-      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if (a.gain) {
         const float r = rinv[m];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] * r * tab_at(a.gain, a.gain_bf16, k + i);
+        for (int i = 0; i < 8; ++i) v[i] = v[i] * r * gs[8 * c + i];
         if (a.normed_out && tn == 0)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a.normed_out[(size_t)m * K + k + i] = v[i];
+          for (int i = 0; i < 8; ++i) a.normed_out[(size_t)m * K + k0 + 8 * c + i] = v[i];
       }
       o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
       o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
@@ -595,7 +688,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       }
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll
     for (int st = 0; st < GBK / 32; ++st) {
       const int k = k0 + st * 32 + (lane >> 4) * 8;
       const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + st * 32 + (lane >> 4) * 8];
@@ -613,15 +706,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         for (int j = 0; j < 4; ++j) acc[j] += t[j] * f16_to_f32(scj[j][blk]);
       }
     }
-    // partials at agent scope, so the tile's last workgroup reads them from any XCD
+    // this lane's four partials are four consecutive columns of row m
     const int m = mt * 16 + (lane & 15);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nj = nrow0 + (lane >> 4) * 4 + j;
-      if (m < M && nj < N)
-        __hip_atomic_store(a.part + ((size_t)ks * M + m) * NP + (mat ? N : 0) + nj, acc[j], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const int nj = nrow0 + (lane >> 4) * 4;
+    if (m < M && nj < N)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc), prs,
+                                             (int)((((size_t)ks * M + m) * NP + (mat ? N : 0) + nj) * 4), 0, CPOL_SC1);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
   __syncthreads();
@@ -636,18 +726,39 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // the tile's last workgroup: sum the K slices in order, then the epilogue;
   // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile
   const int m = tid >> 2, c0 = (tid & 3) * 8;
+  const int nb0 = tn * GT + c0;
   float sq = 0.f;
-  if (m < M) {
+  if (m < M && nb0 < N) {
+    float g8[8], u8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g8[i] = u8[i] = 0.f;
+    // slices four at a time: every load of a group in flight before the sums
+    for (int q0 = 0; q0 < KS; q0 += 4) {
+      f32x4v_t lg[4][2], lu[4][2];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        if (q0 + qq < KS) {
+          const int off = (int)((((size_t)(q0 + qq) * M + m) * NP + nb0) * 4);
+          lg[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, CPOL_SC1));
+          lg[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16, 0, CPOL_SC1));
+          if (EPI == EPI_GATED) {
+            lu[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4, 0, CPOL_SC1));
+            lu[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4 + 16, 0, CPOL_SC1));
+          }
+        }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        if (q0 + qq < KS)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            g8[i] += lg[qq][i >> 2][i & 3];
+            if (EPI == EPI_GATED) u8[i] += lu[qq][i >> 2][i & 3];
+          }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int n = tn * GT + c0 + i;
-      if (n >= N) break;
-      float g = 0.f, u = 0.f;
-      for (int q = 0; q < KS; ++q) {
-        const float *pr = a.part + ((size_t)q * M + m) * NP;
-        g += __hip_atomic_load(pr + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (EPI == EPI_GATED) u += __hip_atomic_load(pr + N + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      const int n = nb0 + i;
+      const float g = g8[i], u = u8[i];
       float *yp = a.y + (size_t)m * a.y_stride + n;
       if constexpr (EPI == EPI_STORE) {
         *yp = g;
@@ -678,7 +789,7 @@ static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
-  if (a.M < 1 || a.M > 64 || a.K % GBK) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 64 || a.K % GBK || a.N % GT) return hipErrorInvalidValue;
   if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);
   if (wtype == W_Q8) return gemm_wt<W_Q8>(epi, a, s);
   return hipErrorInvalidValue;

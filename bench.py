@@ -177,7 +177,9 @@ def main():
     else:
         # dominant kernel: the gate/up GEMV, timed live with HIP events on the
         # library's stream over every layer's weights
-        kname = "gemv_kernel<gated> (RMSNorm + gate/up + SiLU-mul)"
+        batched = B >= 4 and m.lin != 0 and m.act_bf16
+        kname = ("gemm_kernel<gated> (MFMA: RMSNorm + gate/up + SiLU-mul, %d rows)" % B if batched
+                 else "gemv_kernel<gated> (RMSNorm + gate/up + SiLU-mul)")
         us, kbytes = d.time_kernel(qt.QT_KERNEL_GEMV_GATE_UP, 3)
     achieved = kbytes / (us * 1e-6) / 1e9
     log(f"path {d.path}: {frames / wall:.1f} frames/s, {ms_per_frame_step:.3f} ms per frame-step; "
