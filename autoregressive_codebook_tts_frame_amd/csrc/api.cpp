@@ -26,6 +26,7 @@ constexpr int kPrefillChunk = 32;  // prompt rows per prefill step
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
+constexpr int kXchRep = 8;         // copies of the frame kernel's broadcast rows
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -38,6 +39,7 @@ struct Layout {
   size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
   // persistent frame kernel: weight tables, tagged exchange words, error flag
   size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_part, f_err, f_trace;
+  size_t xch_words;  // words between copies of the exchange rows
   size_t total;
   int32_t rows;       // activation rows held
   int32_t max_tiles;  // talker attention tiles
@@ -103,10 +105,13 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.f_pl = take(sizeof(qtk::LayerDev) * d.Lp);
   L.f_heads = take(sizeof(void *) * d.G);
   L.f_heads_sc = take(sizeof(void *) * d.G);
-  L.f_xq = take(8 * 2 * (size_t)d.H);
+  // rows every GEMV workgroup reads (residual, attention output, SiLU-mul
+  // output) exist kXchRep times, one copy per group of readers
+  L.xch_words = 2 * (size_t)d.H + 2 * (size_t)d.qd + 2 * (size_t)d.F + 32;
+  L.f_xq = take(8 * kXchRep * L.xch_words);
+  L.f_o = L.f_xq + 8 * 2 * (size_t)d.H;
+  L.f_z = L.f_o + 8 * 2 * (size_t)d.qd;
   L.f_qkv = take(8 * 2 * (size_t)d.nqkv);
-  L.f_o = take(8 * 2 * (size_t)d.qd);
-  L.f_z = take(8 * 2 * (size_t)d.F);
   L.f_amax = take(8 * 2 * (size_t)kMaxWG);
   L.f_part = take(8 * (size_t)d.nq * (d.P / kTile) * (d.hd + 2));
   L.f_err = take(64);
@@ -600,6 +605,7 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
     fa.H = d.H; fa.nq = d.nq; fa.nkv = d.nkv; fa.hd = d.hd; fa.F = d.F; fa.Lt = d.Lt; fa.Lp = d.Lp;
     fa.G = d.G; fa.Vc = d.Vc; fa.Vt = d.Vt; fa.P = d.P; fa.Q = d.Q;
     fa.wt = wtype_of(m); fa.tab_bf16 = m.tab_bf16; fa.kv_bf16 = m.kv_bf16; fa.act_bf16 = m.act_bf16;
+    fa.rep = kXchRep; fa.rep_stride = (int64_t)c->L.xch_words;
     // the plan must fit for the longest context the ring holds
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&

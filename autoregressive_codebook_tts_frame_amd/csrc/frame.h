@@ -54,6 +54,11 @@ struct FrameArgs {
   uint64_t *zb;    // [2][F]        SiLU-mul output (bf16 pairs when act_bf16)
   uint64_t *amax;  // [nwg][2]      per-workgroup (value, index) of a head's argmax
   uint64_t *part;  // [nq][max_tiles][hd + 2]  tile partials (o, max, sum)
+  // xq, ob and zb exist rep times, rep_stride words apart: producers write
+  // every copy, workgroup b reads copy b % rep, so that the readers of one
+  // row spread over rep places in memory
+  int32_t rep;
+  int64_t rep_stride;
   // outputs / dumps
   float *logits_t;  // [Vc]
   float *logits_p;  // [G-1][Vc]

@@ -65,14 +65,17 @@ struct Ph {
 template <class T> __device__ __forceinline__ GAS T *gp(T *p) { return (GAS T *)p; }
 template <class T> __device__ __forceinline__ const GAS T *gp(const T *p) { return (const GAS T *)p; }
 
+// float -> nearest bf16 (ties to even; the hardware conversion), kept in a float
 __device__ __forceinline__ float bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return __uint_as_float((u | ((u & 0x7fffffu) ? 0x400000u : 0u)) & 0xffff0000u);
-  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
-  return __uint_as_float(u);
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f) << 16);
 }
-__device__ __forceinline__ uint32_t bf16_bits(float f) { return __float_as_uint(bf16_rne(f)) >> 16; }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// nearest bf16 pair of (lo, hi), lo in the low half: one packed conversion
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
@@ -176,6 +179,7 @@ __device__ __forceinline__ void dma16_coherent(const void *src, uint32_t lds_bas
       : "memory");
 }
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const LAS void *)p;
 }
@@ -187,17 +191,25 @@ struct LayerTab {
   const void *attn_norm, *q_norm, *k_norm, *mlp_norm;
 };
 
+// GEMV rows [r0, r0 + R) of N, width K, NM matrices (2: gate and up)
+struct Share {
+  int r0, R, N, K, NM;
+};
+
 struct Common {
   LayerTab lt[MAXLAYERS];  // talker layers then predictor layers
   const void *head_w[MAXHEADS];
   const uint16_t *head_sc[MAXHEADS];
   float amv[NW];
   int ami[NW];
+  float pss[2][NW];     // per-wave partial sums of squares of the residual rows
   int codes[MAXHEADS];  // codes fed to this frame's gathers
   int code;
   int abort;
   uint32_t cbar;   // compute-wave barrier arrivals
   uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
+  uint64_t ltime;  // tracing: when the loader wave's last slice had landed
+  Share sh[PH_END];  // this GEMV workgroup's rows, per phase type
 };
 
 // Offsets (bytes) of each role's LDS buffers; one function for host and device.
@@ -285,8 +297,13 @@ __device__ __forceinline__ const LayerTab &tab_of(const FrameArgs &a, const Comm
 
 // Poll n tagged words (word i at src(i)) until each carries tag; value bits
 // -> *dst(i) (LDS).  All threads; false on timeout.
-template <int TH = NT, class Dst, class Src>
-__device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Dst dst, Src src) {
+struct NoTap {
+  __device__ __forceinline__ void operator()(int, uint32_t) const {}
+};
+// Wait for n tagged words src(i) and store their values at dst(i); every
+// value also goes to tap(i, v), in this thread's order.
+template <int TH = NT, class Dst, class Src, class Tap = NoTap>
+__device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Dst dst, Src src, Tap tap = Tap()) {
   for (int b0 = 0; b0 < n; b0 += PER * TH) {
     uint64_t v[PER];
     uint32_t pend = 0;
@@ -300,11 +317,19 @@ __device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Ds
       for (int k = 0; k < PER; ++k)
         if (((pend >> k) & 1u) && (uint32_t)(v[k] >> 32) == tag) {
           *dst(b0 + threadIdx.x + k * TH) = (uint32_t)v[k];
+          tap(b0 + threadIdx.x + k * TH, (uint32_t)v[k]);
           pend &= ~(1u << k);
         }
-      if (!pend) break;
+      if (!pend) {
+        // Nothing is in flight now, but the compiler cannot see it: without
+        // this it waits for all memory operations before every later write
+        // to these registers, serialising the next poll's loads.
+        wait_vm();
+        break;
+      }
       if (spins > SPIN_LIMIT || ((spins & 255u) == 255u && err_get(a.err))) {
         err_set(a.err);
+        wait_vm();  // leave no load in flight into registers the caller reuses
         return false;
       }
 #pragma unroll
@@ -314,24 +339,24 @@ __device__ __forceinline__ bool poll(const FrameArgs &a, int n, uint32_t tag, Ds
   }
   return true;
 }
-template <int TH = NT>
-__device__ __forceinline__ bool poll_lin(const FrameArgs &a, const uint64_t *src, int n, uint32_t tag, uint32_t *dst) {
-  return poll<TH>(a, n, tag, [=](int i) { return dst + i; }, [=](int i) { return src + i; });
+template <int TH = NT, class Tap = NoTap>
+__device__ __forceinline__ bool poll_lin(const FrameArgs &a, const uint64_t *src, int n, uint32_t tag, uint32_t *dst,
+                                         Tap tap = Tap()) {
+  return poll<TH>(a, n, tag, [=](int i) { return dst + i; }, [=](int i) { return src + i; }, tap);
 }
-// rows of w words at src (contiguous) into LDS rows of stride dw
+// one or two rows of w words at src (contiguous) into LDS rows of stride dw
+template <class Tap = NoTap>
 __device__ __forceinline__ bool poll_rows(const FrameArgs &a, const uint64_t *src, int rows, int w, uint32_t tag,
-                                          uint32_t *dst, int dw) {
-  return poll(a, rows * w, tag, [=](int i) { const int m = i / w; return dst + m * dw + (i - m * w); },
-              [=](int i) { return src + i; });
+                                          uint32_t *dst, int dw, Tap tap = Tap()) {
+  return poll(a, rows * w, tag, [=](int i) { return dst + (i < w ? i : i - w + dw); },
+              [=](int i) { return src + i; }, tap);
 }
 
 // ------------------------------------------------------------ GEMV role
 
-// Row share of GEMV workgroup gi among NG: rows [r0, r0 + R), in pairs.
-struct Share {
-  int r0, R, N, K, NM;
-};
-__device__ __forceinline__ Share share_of(const FrameArgs &a, int type, int gi, int NG) {
+// Row share of GEMV workgroup gi among NG: rows [r0, r0 + R) (computed once
+// per phase type at the start, then read from LDS).
+__device__ __forceinline__ Share share_calc(const FrameArgs &a, int type, int gi, int NG) {
   Share s;
   const int qd = a.nq * a.hd;
   s.NM = 1;
@@ -342,10 +367,13 @@ __device__ __forceinline__ Share share_of(const FrameArgs &a, int type, int gi, 
     case PH_D: s.N = a.H; s.K = a.F; break;
     default: s.N = a.Vc; s.K = a.H; break;
   }
-  const int np = s.N / 2;
-  const int p0 = (int)(((long)np * gi) / NG), p1 = (int)(((long)np * (gi + 1)) / NG);
-  s.r0 = 2 * p0;
-  s.R = 2 * (p1 - p0);
+  // gate/up rows go in pairs (one packed bf16 pair of SiLU-mul outputs each);
+  // the others one by one, so that no workgroup gets more than one row above
+  // the mean (the slowest workgroup sets every phase's pace)
+  const int g = type == PH_GU ? 2 : 1, nu = s.N / g;
+  const int p0 = (int)(((long)nu * gi) / NG), p1 = (int)(((long)nu * (gi + 1)) / NG);
+  s.r0 = g * p0;
+  s.R = g * (p1 - p0);
   return s;
 }
 
@@ -353,6 +381,9 @@ template <int WT> struct WEsz;
 template <> struct WEsz<W_F32> { static constexpr int v = 4; };
 template <> struct WEsz<W_BF16> { static constexpr int v = 2; };
 template <> struct WEsz<W_Q8> { static constexpr int v = 1; };
+// 1 KB blocks a weight row of width H may span: its normalized operand lives
+// in registers (a q8 chunk takes twice the operand words of a bf16 one)
+__host__ __device__ constexpr int nb_hidden(int wt) { return wt == W_Q8 ? 1 : 2; }
 
 // weight row (and q8 scale row) of output row n, matrix mat
 __device__ __forceinline__ void wrow_of(const FrameArgs &a, const Common &cm, const Ph &p, int n, int mat,
@@ -394,11 +425,10 @@ __device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool q8) {
 // Issue the direct-to-LDS loads of phase p's weight slice (+ scales, gain).
 // Called by the loader wave only: every 1 KB block is one instruction of it.
 template <int WT>
-__device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, const Ph &p, int gi, int NG,
-                                          uint32_t slot) {
+__device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, const Ph &p, uint32_t slot) {
   constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63;
-  const Share s = share_of(a, p.type, gi, NG);
+  const Share s = cm.sh[p.type];
   const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
   int b = 0;
   for (int u = 0; u < U; ++u) {
@@ -426,9 +456,8 @@ __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, 
   }
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), c, false);
 }
 // int8 bytes b, b+1 of w as a bf16 pair (exact: |q| <= 127)
 __device__ __forceinline__ uint32_t i8pair(uint32_t w, int b) {
@@ -436,27 +465,43 @@ __device__ __forceinline__ uint32_t i8pair(uint32_t w, int b) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
-// 16-byte weight chunk c of a row . operand row (LDS)
+// The operand elements that meet one 16-byte weight chunk: 8 bf16 pairs for
+// q8 (a, b), 4 pairs for bf16 (a), 4 floats for f32 (a).
+struct OpC {
+  uint4 a, b;
+};
+// chunk c of an operand row in LDS
 template <int WT>
-__device__ __forceinline__ float chunk_dot(uint4 w, const uint32_t *op, int c, const uint8_t *scl) {
+__device__ __forceinline__ OpC op_lds(const uint32_t *op, int c) {
+  OpC x;
+  if constexpr (WT == W_Q8) {
+    x.a = ((const uint4 *)op)[2 * c];
+    x.b = ((const uint4 *)op)[2 * c + 1];
+  } else {
+    x.a = ((const uint4 *)op)[c];
+    x.b = x.a;
+  }
+  return x;
+}
+
+// 16-byte weight chunk c of a row . its operand elements
+template <int WT>
+__device__ __forceinline__ float chunk_dot(uint4 w, const OpC &x, int c, const uint8_t *scl) {
   if constexpr (WT == W_BF16) {
-    const uint4 x = ((const uint4 *)op)[c];
-    return dot2(w.w, x.w, dot2(w.z, x.z, dot2(w.y, x.y, dot2(w.x, x.x, 0.f))));
+    return dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
   } else if constexpr (WT == W_Q8) {
-    const uint4 x0 = ((const uint4 *)op)[2 * c], x1 = ((const uint4 *)op)[2 * c + 1];
-    float s = dot2(i8pair(w.x, 0), x0.x, 0.f);
-    s = dot2(i8pair(w.x, 2), x0.y, s);
-    s = dot2(i8pair(w.y, 0), x0.z, s);
-    s = dot2(i8pair(w.y, 2), x0.w, s);
-    s = dot2(i8pair(w.z, 0), x1.x, s);
-    s = dot2(i8pair(w.z, 2), x1.y, s);
-    s = dot2(i8pair(w.w, 0), x1.z, s);
-    s = dot2(i8pair(w.w, 2), x1.w, s);
+    float s = dot2(i8pair(w.x, 0), x.a.x, 0.f);
+    s = dot2(i8pair(w.x, 2), x.a.y, s);
+    s = dot2(i8pair(w.y, 0), x.a.z, s);
+    s = dot2(i8pair(w.y, 2), x.a.w, s);
+    s = dot2(i8pair(w.z, 0), x.b.x, s);
+    s = dot2(i8pair(w.z, 2), x.b.y, s);
+    s = dot2(i8pair(w.w, 0), x.b.z, s);
+    s = dot2(i8pair(w.w, 2), x.b.w, s);
     return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
   } else {
-    const float4 x = ((const float4 *)op)[c];
-    return __uint_as_float(w.x) * x.x + __uint_as_float(w.y) * x.y + __uint_as_float(w.z) * x.z +
-           __uint_as_float(w.w) * x.w;
+    return __uint_as_float(w.x) * __uint_as_float(x.a.x) + __uint_as_float(w.y) * __uint_as_float(x.a.y) +
+           __uint_as_float(w.z) * __uint_as_float(x.a.z) + __uint_as_float(w.w) * __uint_as_float(x.a.w);
   }
 }
 
@@ -475,43 +520,55 @@ __device__ __forceinline__ bool cbar(const FrameArgs &a, Common &cm, uint32_t &g
   return true;
 }
 
-// RMSNorm of residual row x (LDS f32) with gain g (LDS, table type) -> operand
-// row (bf16 pairs or f32), this thread's pairs; every wave forms the full sum
-// of squares itself.  y kept in yk[] (pair layout) when asked.
-template <int WT>
-__device__ __forceinline__ void norm_row(const FrameArgs &a, const float *x, const uint8_t *g, uint32_t *op,
-                                         float (&yk)[2 * HPAIR], bool keep) {
-  const int H = a.H, tid = threadIdx.x, lane = tid & 63;
-  float4 xv[8];  // H <= 2048, a multiple of 256: eight float4 per lane
+// 1 / RMS of a row from the compute waves' partial sums of squares (LDS).
+__device__ __forceinline__ float rms_inv(const FrameArgs &a, const float *pss) {
+  float ss = pss[0];
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    xv[k] = 256 * k < H ? *(const float4 *)(x + 4 * lane + 256 * k) : make_float4(0.f, 0.f, 0.f, 0.f);
-  float ss = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) ss += (xv[k].x * xv[k].x + xv[k].y * xv[k].y) + (xv[k].z * xv[k].z + xv[k].w * xv[k].w);
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)H + a.eps);
-#pragma unroll
-  for (int k = 0; k < HPAIR; ++k) {
-    const int pi = tid + k * NT;
-    if (2 * pi < H) {
-      float g0, g1;
-      if (a.tab_bf16) {
-        const uint32_t gw = ((const uint32_t *)g)[pi];
-        g0 = lo16(gw); g1 = hi16(gw);
-      } else {
-        g0 = ((const float *)g)[2 * pi]; g1 = ((const float *)g)[2 * pi + 1];
-      }
-      const float y0 = x[2 * pi] * r * g0, y1 = x[2 * pi + 1] * r * g1;
-      if (keep) { yk[2 * k] = y0; yk[2 * k + 1] = y1; }
-      if constexpr (WT == W_F32) {
-        ((float *)op)[2 * pi] = a.act_bf16 ? bf16_rne(y0) : y0;
-        ((float *)op)[2 * pi + 1] = a.act_bf16 ? bf16_rne(y1) : y1;
-      } else {
-        op[pi] = pack2(y0, y1);
-      }
-    }
+  for (int w = 1; w < NW; ++w) ss += pss[w];
+  return 1.0f / sqrtf(ss / (float)a.H + a.eps);
+}
+// gain element e of a norm table (bf16 or f32) staged in LDS
+__device__ __forceinline__ float gain_at(const FrameArgs &a, const uint8_t *g, int e) {
+  return a.tab_bf16 ? __uint_as_float((uint32_t)((const uint16_t *)g)[e] << 16) : ((const float *)g)[e];
+}
+// bf16 pairs of RMSNorm(x) * g for elements e0 .. e0 + 7
+__device__ __forceinline__ uint4 norm8(const FrameArgs &a, const float *x, const uint8_t *g, float r, int e0) {
+  const float4 x0 = *(const float4 *)(x + e0), x1 = *(const float4 *)(x + e0 + 4);
+  float g8[8];
+  if (a.tab_bf16) {
+    const uint4 gw = *(const uint4 *)(g + 2 * e0);
+    g8[0] = lo16(gw.x); g8[1] = hi16(gw.x); g8[2] = lo16(gw.y); g8[3] = hi16(gw.y);
+    g8[4] = lo16(gw.z); g8[5] = hi16(gw.z); g8[6] = lo16(gw.w); g8[7] = hi16(gw.w);
+  } else {
+    const float4 g0 = *(const float4 *)(g + 4 * e0), g1 = *(const float4 *)(g + 4 * e0 + 16);
+    g8[0] = g0.x; g8[1] = g0.y; g8[2] = g0.z; g8[3] = g0.w;
+    g8[4] = g1.x; g8[5] = g1.y; g8[6] = g1.z; g8[7] = g1.w;
   }
+  return make_uint4(pack2(x0.x * r * g8[0], x0.y * r * g8[1]), pack2(x0.z * r * g8[2], x0.w * r * g8[3]),
+                    pack2(x1.x * r * g8[4], x1.y * r * g8[5]), pack2(x1.z * r * g8[6], x1.w * r * g8[7]));
+}
+// The operand elements of weight chunk c for a row of width H: RMSNorm(x) * g,
+// rounded as an operand row would be, built in registers from the residual row.
+template <int WT>
+__device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, const uint8_t *g, float r, int c) {
+  OpC o;
+  if constexpr (WT == W_Q8) {
+    o.a = norm8(a, x, g, r, 16 * c);
+    o.b = norm8(a, x, g, r, 16 * c + 8);
+  } else if constexpr (WT == W_BF16) {
+    o.a = norm8(a, x, g, r, 8 * c);
+    o.b = o.a;
+  } else {
+    const int e0 = 4 * c;
+    const float4 xv = *(const float4 *)(x + e0);
+    float y[4] = {xv.x * r * gain_at(a, g, e0), xv.y * r * gain_at(a, g, e0 + 1), xv.z * r * gain_at(a, g, e0 + 2),
+                  xv.w * r * gain_at(a, g, e0 + 3)};
+    if (a.act_bf16)
+      for (int j = 0; j < 4; ++j) y[j] = bf16_rne(y[j]);
+    o.a = make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3]));
+    o.b = o.a;
+  }
+  return o;
 }
 
 // table row (bf16 or f32) element pairs of this thread -> v[2 * HPAIR]
@@ -556,9 +613,9 @@ __device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uin
 // up rows of a row pair), round-robin over the compute waves; the results of
 // item it go to out(it, acc) as uniform values.  A row is at most MAXB 1 KB
 // blocks; an item's weight chunks are all loaded before its dot products.
-template <int WT, int UPI, int MAXB, class Out>
-__device__ __forceinline__ void gemv_items(const uint8_t *slot, const uint32_t *opnd, int opw, const Share &s, int M,
-                                           Out out) {
+// op(m, cb, c) gives operand row m's elements for chunk c (block cb).
+template <int WT, int UPI, int MAXB, class Op, class Out>
+__device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int M, Out out) {
   constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rowb = s.K * ESZ, bpr = rowb >> 10;
@@ -578,11 +635,14 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, const uint32_t *
     for (int cb = 0; cb < MAXB; ++cb) {
       if (cb >= bpr) break;
       const int c = cb * 64 + lane;
+      const OpC x0 = op(0, cb, c);
+      OpC x1;
+      if (M > 1) x1 = op(1, cb, c);
 #pragma unroll
       for (int q = 0; q < UPI; ++q) {
         const uint8_t *scl = scb + (size_t)(it * UPI + q) * (s.K / 16);
-        acc[q][0] += chunk_dot<WT>(w[q][cb], opnd, c, scl);
-        if (M > 1) acc[q][1] += chunk_dot<WT>(w[q][cb], opnd + opw, c, scl);
+        acc[q][0] += chunk_dot<WT>(w[q][cb], x0, c, scl);
+        if (M > 1) acc[q][1] += chunk_dot<WT>(w[q][cb], x1, c, scl);
       }
     }
 #pragma unroll
@@ -599,11 +659,11 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, const uint32_t *
 // their inputs are in.
 template <int WT>
 __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, const Lds &L, unsigned char *smem) {
-  const int gi = (int)blockIdx.x - a.n_attn, NG = a.nwg - a.n_attn;
   const uint32_t s0 = lds_addr(smem + L.slot0), s1 = lds_addr(smem + L.slot1);
   Ph cur{PH_QKV, 0, 0, 0, 0};
-  dma_slice<WT>(a, cm, cur, gi, NG, s0);
+  dma_slice<WT>(a, cm, cur, s0);
   wait_vm();
+  if (a.trace) cm.ltime = wall_clock64();
   int slot = 0;
   uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
   bool have_next = false;     // the next phase's slice is already in its slot
@@ -623,7 +683,7 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     done += NW;
     if (ng.type != PH_END && !have_next) {
       if (!a.two_slots && !wait_gemv()) return;  // one slot: it is free once this phase's GEMV is done
-      dma_slice<WT>(a, cm, ng, gi, NG, a.two_slots && !slot ? s1 : s0);
+      dma_slice<WT>(a, cm, ng, a.two_slots && !slot ? s1 : s0);
     }
     have_next = false;
     if (a.two_slots && cur.type == PH_QKV && ng.type == PH_O) {
@@ -633,10 +693,11 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
       // exchange before the gate/up phase.
       const Ph n2 = next_gemv_phase(a, ng, a.pos0);
       if (!wait_gemv()) return;
-      dma_slice<WT>(a, cm, n2, gi, NG, slot ? s1 : s0);
+      dma_slice<WT>(a, cm, n2, slot ? s1 : s0);
       have_next = true;  // skipped at the O phase's meeting
     }
     wait_vm();
+    if (a.trace) cm.ltime = wall_clock64();
     if (a.two_slots) slot ^= 1;
     cur = ng;
   }
@@ -662,6 +723,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   const int pos0 = a.pos0;
   int c0 = ld(a.c0);
   const bool lead = gi == 0;  // writes state, codes and dumps
+  const size_t rsel = (size_t)(blockIdx.x % a.rep) * a.rep_stride;  // the exchange copy this workgroup reads
+  const uint64_t *xq = a.xq + rsel;
   uint32_t gen = 0;           // compute-wave barrier count
 
   float brg[2 * HPAIR], tacc[2 * HPAIR], trow[2 * HPAIR];
@@ -672,6 +735,10 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     const int pi = tid + k * NT;
     if (2 * pi < H) { brg[2 * k] = ld(a.bridge + 2 * pi); brg[2 * k + 1] = ld(a.bridge + 2 * pi + 1); }
   }
+  // Loop-carried values must not enter the phase loop with loads in flight:
+  // the compiler would then wait for every outstanding memory operation
+  // (the last phase's stores included) at each of their copies in the loop.
+  wait_vm();
 
   Ph cur{PH_QKV, 0, 0, 0, 0};
   uint32_t seq = 1;
@@ -689,7 +756,9 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     const int f = cur.frame;
     const int pos = pos0 + f;
     const int M = (cur.stack == 0 && cur.step == 0 && cur.type != PH_HEAD) ? 2 : 1;
-    const Share s = share_of(a, cur.type, gi, NG);
+    const Share s = cm.sh[cur.type];
+    const bool normed = cur.type == PH_QKV || cur.type == PH_GU || cur.type == PH_HEAD;
+    float ss0 = 0.f, ss1 = 0.f;  // this thread's squares of residual rows 0 and 1
     // every compute wave is done with the last phase's operand and residual rows
     if (!cbar(a, cm, gen)) return;
 
@@ -731,6 +800,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             if (2 * pi < H) {
               xres[2 * pi] = brg[2 * k]; xres[2 * pi + 1] = brg[2 * k + 1];
               xres[H + 2 * pi] = row[2 * k]; xres[H + 2 * pi + 1] = row[2 * k + 1];
+              ss0 += brg[2 * k] * brg[2 * k] + brg[2 * k + 1] * brg[2 * k + 1];
+              ss1 += row[2 * k] * row[2 * k] + row[2 * k + 1] * row[2 * k + 1];
             }
             tacc[2 * k] = 0.f + row[2 * k];
             tacc[2 * k + 1] = 0.f + row[2 * k + 1];
@@ -740,7 +811,10 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
 #pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
-            if (2 * pi < H) { xres[2 * pi] = row[2 * k]; xres[2 * pi + 1] = row[2 * k + 1]; }
+            if (2 * pi < H) {
+              xres[2 * pi] = row[2 * k]; xres[2 * pi + 1] = row[2 * k + 1];
+              ss0 += row[2 * k] * row[2 * k] + row[2 * k + 1] * row[2 * k + 1];
+            }
             tacc[2 * k] += row[2 * k];
             tacc[2 * k + 1] += row[2 * k + 1];
           }
@@ -754,6 +828,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             const float v1 = (tacc[2 * k + 1] + row[2 * k + 1]) + trow[2 * k + 1];
             if (2 * pi < H) {
               xres[2 * pi] = v0; xres[2 * pi + 1] = v1;
+              ss0 += v0 * v0 + v1 * v1;
               if (a.dump && lead) { st(a.x0_dump + 2 * pi, v0); st(a.x0_dump + 2 * pi + 1, v1); }
             }
           }
@@ -761,53 +836,81 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           if (a.dump && lead && tid == 0) st(a.tpos_dump, pos);
         }
       }
-    } else if (cur.type == PH_QKV || cur.type == PH_GU) {
-      ok = poll_lin(a, a.xq, M * H, tagp, (uint32_t *)xres);
-    } else if (cur.type == PH_HEAD) {
-      const int mrow = cur.stack == 0 && cur.step == 0 ? 1 : 0;
-      ok = poll_lin(a, a.xq + (size_t)mrow * H, H, tagp, (uint32_t *)xres);
-    } else if (cur.type == PH_O) {
-      const int w = a.act_bf16 ? a.nq * a.hd / 2 : a.nq * a.hd;
-      ok = poll_rows(a, a.ob, M, w, tagp, opnd, opw);
-    } else {  // PH_D
-      const int w = a.act_bf16 ? a.F / 2 : a.F;
-      ok = poll_rows(a, a.zb, M, w, tagp, opnd, opw);
+    } else {
+      // residual rows (normed phases) or operand rows (O: attention output, D: SiLU-mul output)
+      const uint64_t *src = xq;
+      int rows = M, w = H, dw = H;
+      uint32_t *dst = (uint32_t *)xres;
+      if (cur.type == PH_HEAD) {
+        if (cur.stack == 0 && cur.step == 0) src += H;  // the code row of the pair
+      } else if (cur.type == PH_O || cur.type == PH_D) {
+        src = (cur.type == PH_O ? a.ob : a.zb) + rsel;
+        const int k = cur.type == PH_O ? a.nq * a.hd : a.F;
+        w = a.act_bf16 ? k / 2 : k;
+        dst = opnd;
+        dw = opw;
+      }
+      ok = poll_rows(a, src, rows, w, tagp, dst, dw, [&](int i, uint32_t v) {
+        const float x = __uint_as_float(v);  // squares feed the RMSNorm of the residual rows
+        if (i < w) ss0 += x * x;
+        else ss1 += x * x;
+      });
     }
+    const uint64_t tp = tracing ? wall_clock64() : 0;
     if (!ok) cm.abort = 1;
+    if (normed) {
+      ss0 = wave_sum(ss0);
+      if (M > 1) ss1 = wave_sum(ss1);
+      if (lane == 0) { cm.pss[0][wave] = ss0; cm.pss[1][wave] = ss1; }
+    }
     __syncthreads();  // with the loader wave: inputs in LDS, this phase's slice landed
     if (cm.abort) return;
     const uint64_t t1 = tracing ? wall_clock64() : 0;
-    const uint64_t c1 = tracing ? __builtin_amdgcn_s_memtime() : 0;
+    const uint64_t tl = tracing ? cm.ltime : 0;
 
-    // ---- prologue: RMSNorm into the operand rows
+    // ---- prologue: the normalized operand rows, each lane its own chunks
     const uint8_t *sp = smem + (slot ? L.slot1 : L.slot0);
-    if (cur.type == PH_QKV || cur.type == PH_GU || cur.type == PH_HEAD) {
+    constexpr int NBH = nb_hidden(WT);
+    OpC xo[2][NBH];  // [row][block]
+    if (normed) {
       const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
-      const bool talker_head = cur.type == PH_HEAD && cur.stack == 1;
-      for (int m = 0; m < M; ++m) norm_row<WT>(a, xres + m * H, gain, opnd + m * opw, brg, talker_head);
-      if (talker_head && lead) {
+      const int bpr = H * ESZ >> 10;
+      const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
+#pragma unroll
+      for (int cb = 0; cb < NBH; ++cb)
+        if (cb < bpr) {
+          xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, cb * 64 + lane);
+          if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + H, gain, r1, cb * 64 + lane);
+        }
+      if (cur.type == PH_HEAD && cur.stack == 1) {
+        // the talker's normed output row, kept (unrounded) as the next frame's bridge
 #pragma unroll
         for (int k = 0; k < HPAIR; ++k) {
           const int pi = tid + k * NT;
-          if (2 * pi < H) { st(a.bridge + 2 * pi, brg[2 * k]); st(a.bridge + 2 * pi + 1, brg[2 * k + 1]); }
+          if (2 * pi < H) {
+            brg[2 * k] = xres[2 * pi] * r0 * gain_at(a, gain, 2 * pi);
+            brg[2 * k + 1] = xres[2 * pi + 1] * r0 * gain_at(a, gain, 2 * pi + 1);
+            if (lead) { st(a.bridge + 2 * pi, brg[2 * k]); st(a.bridge + 2 * pi + 1, brg[2 * k + 1]); }
+          }
         }
       }
-      if (!cbar(a, cm, gen)) return;
     }
+    auto op_reg = [&](int m, int cb, int) -> OpC { return xo[m][cb]; };
+    auto op_row = [&](int m, int, int c) -> OpC { return op_lds<WT>(opnd + m * opw, c); };
     const uint64_t t2 = tracing ? wall_clock64() : 0;
-    const uint64_t c2 = tracing ? __builtin_amdgcn_s_memtime() : 0;
 
     // ---- GEMV; each wave publishes the rows it computed
     if (cur.type == PH_GU) {
       // item = row pair (2 p, 2 p + 1): z = SiLU(g) * u, rounded as the down projection's operand
-      gemv_items<WT, 4, 2>(sp, opnd, opw, s, M, [&](int it, float (&acc)[4][2]) {
+      gemv_items<WT, 4, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[4][2]) {
         for (int m = 0; m < M; ++m) {
           const float z0 = acc[0][m] / (1.0f + expf(-acc[0][m])) * acc[1][m];
           const float z1 = acc[2][m] / (1.0f + expf(-acc[2][m])) * acc[3][m];
           if (a.act_bf16) {
-            if (lane == 0) tput(a.zb + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
-          } else if (lane < 2) {
-            tputf(a.zb + (size_t)m * a.F + s.r0 + 2 * it + lane, lane ? z1 : z0, tag);
+            if (lane < a.rep) tput(a.zb + lane * a.rep_stride + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
+          } else if (lane < 2 * a.rep) {
+            const int e = lane & 1;
+            tputf(a.zb + (lane >> 1) * a.rep_stride + (size_t)m * a.F + s.r0 + 2 * it + e, e ? z1 : z0, tag);
           }
         }
       });
@@ -816,7 +919,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      gemv_items<WT, 1, 2>(sp, opnd, opw, s, 1, [&](int it, float (&acc)[1][2]) {
+      gemv_items<WT, 1, NBH>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2]) {
         const int n = s.r0 + it;
         if (lane == 0) st(lg + n, acc[0][0]);
         pick(bv, bi, acc[0][0], n);
@@ -833,19 +936,21 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     } else {
       const int type = cur.type, N = s.N;
       const bool hid = type == PH_D && cur.stack == 1 && a.dump;
-      gemv_items<WT, 1, 6>(sp, opnd, opw, s, M, [&](int it, float (&acc)[1][2]) {
-        const int n = s.r0 + it;
-        if (lane < M) {
-          const float v = lane ? acc[0][1] : acc[0][0];
-          if (type == PH_QKV) {
-            tputf(a.qkvb + (size_t)lane * N + n, v, tag);
-          } else {
-            const float x = xres[lane * H + n] + v;
-            tputf(a.xq + (size_t)lane * H + n, x, tag);
-            if (hid) st(a.hidden_dump + (size_t)cur.layer * H + n, x);
+      if (type == PH_QKV) {
+        gemv_items<WT, 1, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[1][2]) {
+          if (lane < M) tputf(a.qkvb + (size_t)lane * N + s.r0 + it, lane ? acc[0][1] : acc[0][0], tag);
+        });
+      } else {
+        gemv_items<WT, 1, 6>(sp, op_row, s, M, [&](int it, float (&acc)[1][2]) {
+          const int n = s.r0 + it;
+          if (lane < M * a.rep) {  // lane: copy lane / M of row lane % M
+            const int m = M > 1 ? lane & 1 : 0, r = M > 1 ? lane >> 1 : lane;
+            const float x = xres[m * H + n] + (m ? acc[0][1] : acc[0][0]);
+            tputf(a.xq + r * a.rep_stride + (size_t)m * H + n, x, tag);
+            if (hid && r == 0) st(a.hidden_dump + (size_t)cur.layer * H + n, x);
           }
-        }
-      });
+        });
+      }
     }
     if (lane == 0)  // this wave is done with the phase's slot
       __hip_atomic_fetch_add(&cm.gdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -859,8 +964,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       st(tr + 3, (uint64_t)wall_clock64());
       st(tr + 4, t2);
       st(tr + 5, t3);
-      st(tr + 6, c1);  // shader-clock cycles around the norm
-      st(tr + 7, c2);
+      st(tr + 6, tp);  // this wave's inputs were in
+      st(tr + 7, tl);  // the phase's weight slice had landed
     }
     if (tracing) ++ntr;
     if (a.two_slots) slot ^= 1;
@@ -1149,13 +1254,15 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
                 const int k = g * HD + d + e;
                 o[e] = pv(k) / stat[g * 2 + 1];
               }
-              tput(a.ob + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, pack2(o[0], o[1]), tag);
+              const uint32_t v = pack2(o[0], o[1]);
+              for (int r = 0; r < a.rep; ++r)
+                tput(a.ob + r * a.rep_stride + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, v, tag);
             }
           } else {
             for (int i = tid; i < GQ * HD; i += ANT) {
               const int g = i / HD;
               const float o = pv(i) / stat[g * 2 + 1];
-              tputf(a.ob + (size_t)m * qd + kh * GQ * HD + i, o, tag);
+              for (int r = 0; r < a.rep; ++r) tputf(a.ob + r * a.rep_stride + (size_t)m * qd + kh * GQ * HD + i, o, tag);
             }
           }
         } else {
@@ -1211,7 +1318,8 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
             O0 += hp[tt * (HD + 2) + d] * w;
             O1 += hp[tt * (HD + 2) + d + 1] * w;
           }
-          tput(a.ob + ((kh * GQ + g) * HD + d) / 2, pack2(O0 / Ls, O1 / Ls), tag);
+          const uint32_t v = pack2(O0 / Ls, O1 / Ls);
+          for (int r = 0; r < a.rep; ++r) tput(a.ob + r * a.rep_stride + ((kh * GQ + g) * HD + d) / 2, v, tag);
         }
       } else {
         for (int i = tid; i < GQ * HD; i += ANT) {
@@ -1225,7 +1333,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
             Ls += hp[tt * (HD + 2) + HD + 1] * w;
             O += hp[tt * (HD + 2) + d] * w;
           }
-          tputf(a.ob + (size_t)(kh * GQ + g) * HD + d, O / Ls, tag);
+          for (int r = 0; r < a.rep; ++r) tputf(a.ob + r * a.rep_stride + (size_t)(kh * GQ + g) * HD + d, O / Ls, tag);
         }
       }
       __syncthreads();
@@ -1259,6 +1367,8 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
     cm.head_w[i] = ld(a.head_w + i);
     cm.head_sc[i] = a.head_sc ? ld(a.head_sc + i) : nullptr;
   }
+  if (tid < PH_END && (int)blockIdx.x >= a.n_attn)
+    cm.sh[tid] = share_calc(a, tid, (int)blockIdx.x - a.n_attn, a.nwg - a.n_attn);
   __syncthreads();
   if ((int)blockIdx.x < a.n_attn) {
     if (tid < ANT) attn_role<HD, GQ, KVB>(a, smem);  // the other waves end here
@@ -1289,9 +1399,13 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   if (a.H > 2048 || a.H % 256) { *why = "hidden width above 2048 or not a multiple of 256"; return false; }
   if (a.Lt + a.Lp > MAXLAYERS || a.G > MAXHEADS) { *why = "too many layers or codebooks"; return false; }
   if (a.nwg > 1024) { *why = "more than 1024 workgroups"; return false; }
+  if (a.rep < 1 || a.rep > 32) { *why = "exchange copies outside 1..32"; return false; }
   // GEMV rows held in registers per item: hidden-wide rows (gate/up pairs, heads)
   // up to 2 KB, the others up to 6 KB
-  if (a.H * esz > 2048 || qd * esz > 6144 || a.F * esz > 6144) { *why = "GEMV rows too wide"; return false; }
+  if (a.H * esz > 1024 * nb_hidden(a.wt) || qd * esz > 6144 || a.F * esz > 6144) {
+    *why = "GEMV rows too wide";
+    return false;
+  }
   a.n_attn = a.nkv * (max_pos / TILE + 1);
   const int NG = a.nwg - a.n_attn;
   if (NG < 16) { *why = "too few GEMV workgroups"; return false; }
@@ -1301,7 +1415,8 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
     const int N = NK[i][0], K = NK[i][1], nm = NK[i][2];
     if ((K * esz) % 1024 || N % 2 || (a.wt == W_Q8 && K % 256)) { *why = "GEMV width not a multiple of 1 KB"; return false; }
     if (K > 3072) { *why = "GEMV width above 3072"; return false; }
-    const int R = 2 * ((N / 2 + NG - 1) / NG);
+    const int g = nm;  // gate/up (nm = 2) rows go in pairs
+    const int R = g * ((N / g + NG - 1) / NG);
     if (R * nm > MAXR) { *why = "too many rows per workgroup"; return false; }
     int b = R * nm * K * esz;
     if (a.wt == W_Q8) b += (int)up1k((uint32_t)(R * nm * (K / 16)));

@@ -25,12 +25,9 @@ __device__ __forceinline__ float bf16_at(const uint16_t *p, size_t i) {
 
 // float -> nearest bf16 (ties to even), kept in a float
 __device__ __forceinline__ float bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return __uint_as_float((u | ((u & 0x7fffffu) ? 0x400000u : 0u)) & 0xffff0000u);
-  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
-  return __uint_as_float(u);
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f) << 16);
 }
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)(__float_as_uint(bf16_rne(f)) >> 16); }
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);

@@ -203,7 +203,7 @@ int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
      QT_DUMP_TRACE         u64 [1024][8]     QT_F_TRACE only: rows 0..767 per GEMV phase of the
                                              first GEMV workgroup (kind | stack << 8 | layer << 16 |
                                              step << 24, start, inputs in, end, norm done, GEMV done,
-                                             then two shader-clock stamps around the norm); rows
+                                             the first wave's poll done, the weight slice landed); rows
                                              768.. per attention event of workgroup 0 (kind word,
                                              start, inputs in, end).  Wall-clock stamps are 100 MHz
                                              ticks; kind 255 ends each part
