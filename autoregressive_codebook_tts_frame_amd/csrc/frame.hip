@@ -214,7 +214,7 @@ struct Common {
 
 // Offsets (bytes) of each role's LDS buffers; one function for host and device.
 struct Lds {
-  uint32_t xres, opnd, res, slot0, slot1, g_end;                        // GEMV role
+  uint32_t xres, opnd, res, brg, tacc, slot0, slot1, g_end;            // GEMV role
   uint32_t gq, gk, rc, rs, rowbuf, sc, stat, pvred, comb, kv, a_end;    // attention role
 };
 __host__ __device__ inline uint32_t up16(uint32_t v) { return (v + 15u) & ~15u; }
@@ -229,7 +229,9 @@ __host__ __device__ inline Lds lds_layout(const FrameArgs &a) {
   L.xres = base;
   L.opnd = up16(L.xres + 2u * a.H * 4u);
   L.res = up16(L.opnd + 2u * opw * 4u);
-  L.slot0 = up1k(L.res + MAXR * 4u * 4u);
+  L.brg = up16(L.res + MAXR * 4u * 4u);
+  L.tacc = L.brg + a.H * 4u;
+  L.slot0 = up1k(L.tacc + a.H * 4u);
   L.slot1 = L.slot0 + (a.two_slots ? (uint32_t)a.slot_bytes : 0u);
   L.g_end = L.slot1 + a.slot_bytes;
   // attention role (G query heads per KV head)
@@ -354,9 +356,8 @@ __device__ __forceinline__ bool poll_rows(const FrameArgs &a, const uint64_t *sr
 
 // ------------------------------------------------------------ GEMV role
 
-// Row share of GEMV workgroup gi among NG: rows [r0, r0 + R) (computed once
-// per phase type at the start, then read from LDS).
-__device__ __forceinline__ Share share_calc(const FrameArgs &a, int type, int gi, int NG) {
+// Rows of phase type `type`: count N, width K, NM matrices (2: gate and up).
+__device__ __forceinline__ Share shape_of(const FrameArgs &a, int type) {
   Share s;
   const int qd = a.nq * a.hd;
   s.NM = 1;
@@ -367,13 +368,27 @@ __device__ __forceinline__ Share share_calc(const FrameArgs &a, int type, int gi
     case PH_D: s.N = a.H; s.K = a.F; break;
     default: s.N = a.Vc; s.K = a.H; break;
   }
-  // gate/up rows go in pairs (one packed bf16 pair of SiLU-mul outputs each);
-  // the others one by one, so that no workgroup gets more than one row above
-  // the mean (the slowest workgroup sets every phase's pace)
-  const int g = type == PH_GU ? 2 : 1, nu = s.N / g;
-  const int p0 = (int)(((long)nu * gi) / NG), p1 = (int)(((long)nu * (gi + 1)) / NG);
-  s.r0 = g * p0;
-  s.R = g * (p1 - p0);
+  return s;
+}
+// Row share of GEMV workgroup gi among NG: rows [r0, r0 + R), computed once
+// per phase type at the start, then read from LDS.  Gate/up rows go in pairs
+// (one packed bf16 pair of SiLU-mul outputs each), the others one by one, so
+// no workgroup gets more than one unit above the mean.  The workgroups that
+// get that extra unit are dealt round-robin across the phase types in their
+// order within a layer: a workgroup with an extra row in every phase type
+// would fall further behind each phase and pace the whole frame.
+__device__ __forceinline__ Share share_calc(const FrameArgs &a, int type, int gi, int NG) {
+  Share s = shape_of(a, type);
+  const int order[5] = {PH_QKV, PH_O, PH_GU, PH_D, PH_HEAD};
+  int off = 0;  // extra units dealt to the phase types before this one
+  for (int k = 0; k < 5 && order[k] != type; ++k) {
+    const Share o = shape_of(a, order[k]);
+    off += (o.N / o.NM) % NG;
+  }
+  const int g = s.NM, nu = s.N / g, base = nu / NG, extra = nu % NG;
+  const int v = ((gi - off) % NG + NG) % NG;
+  s.r0 = g * (v * base + min(v, extra));
+  s.R = g * (base + (v < extra ? 1 : 0));
   return s;
 }
 
@@ -727,13 +742,19 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   const uint64_t *xq = a.xq + rsel;
   uint32_t gen = 0;           // compute-wave barrier count
 
-  float brg[2 * HPAIR], tacc[2 * HPAIR], trow[2 * HPAIR];
-#pragma unroll
-  for (int k = 0; k < 2 * HPAIR; ++k) { brg[k] = 0.f; tacc[k] = 0.f; trow[k] = 0.f; }
+  // Row state kept across phases, each thread its own element pairs (so no
+  // barrier guards them): the bridge row and the frame's running sum of code
+  // embedding rows.  They live in LDS, not registers, so that the phase loop
+  // carries no register arrays.
+  float *brg = (float *)(smem + L.brg), *tacc = (float *)(smem + L.tacc);
 #pragma unroll
   for (int k = 0; k < HPAIR; ++k) {
     const int pi = tid + k * NT;
-    if (2 * pi < H) { brg[2 * k] = ld(a.bridge + 2 * pi); brg[2 * k + 1] = ld(a.bridge + 2 * pi + 1); }
+    if (2 * pi < H) {
+      const uint64_t b = ld((const uint64_t *)a.bridge + pi);
+      brg[2 * pi] = __uint_as_float((uint32_t)b);
+      brg[2 * pi + 1] = __uint_as_float((uint32_t)(b >> 32));
+    }
   }
   // Loop-carried values must not enter the phase loop with loads in flight:
   // the compiler would then wait for every outstanding memory operation
@@ -793,18 +814,18 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           const int code0 = force ? ld(ci) : c0;
           cm.codes[0] = code0;
           tab_pairs(a, a.code_emb, (size_t)code0, row);
-          tab_pairs(a, a.text_emb, (size_t)ld(a.overlay + f), trow);
 #pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
             if (2 * pi < H) {
-              xres[2 * pi] = brg[2 * k]; xres[2 * pi + 1] = brg[2 * k + 1];
+              const float b0 = brg[2 * pi], b1 = brg[2 * pi + 1];
+              xres[2 * pi] = b0; xres[2 * pi + 1] = b1;
               xres[H + 2 * pi] = row[2 * k]; xres[H + 2 * pi + 1] = row[2 * k + 1];
-              ss0 += brg[2 * k] * brg[2 * k] + brg[2 * k + 1] * brg[2 * k + 1];
+              ss0 += b0 * b0 + b1 * b1;
               ss1 += row[2 * k] * row[2 * k] + row[2 * k + 1] * row[2 * k + 1];
+              tacc[2 * pi] = 0.f + row[2 * k];
+              tacc[2 * pi + 1] = 0.f + row[2 * k + 1];
             }
-            tacc[2 * k] = 0.f + row[2 * k];
-            tacc[2 * k + 1] = 0.f + row[2 * k + 1];
           }
         } else if (cur.stack == 0) {
           tab_pairs(a, a.code_emb, (size_t)cur.step * a.Vc + cm.codes[cur.step], row);
@@ -814,19 +835,21 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             if (2 * pi < H) {
               xres[2 * pi] = row[2 * k]; xres[2 * pi + 1] = row[2 * k + 1];
               ss0 += row[2 * k] * row[2 * k] + row[2 * k + 1] * row[2 * k + 1];
+              tacc[2 * pi] += row[2 * k];
+              tacc[2 * pi + 1] += row[2 * k + 1];
             }
-            tacc[2 * k] += row[2 * k];
-            tacc[2 * k + 1] += row[2 * k + 1];
           }
         } else {
           // talker input: the frame's G code rows, then the overlay row, in order
+          float trow[2 * HPAIR];
           tab_pairs(a, a.code_emb, (size_t)(G - 1) * a.Vc + cm.codes[G - 1], row);
+          tab_pairs(a, a.text_emb, (size_t)ld(a.overlay + f), trow);
 #pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
-            const float v0 = (tacc[2 * k] + row[2 * k]) + trow[2 * k];
-            const float v1 = (tacc[2 * k + 1] + row[2 * k + 1]) + trow[2 * k + 1];
             if (2 * pi < H) {
+              const float v0 = (tacc[2 * pi] + row[2 * k]) + trow[2 * k];
+              const float v1 = (tacc[2 * pi + 1] + row[2 * k + 1]) + trow[2 * k + 1];
               xres[2 * pi] = v0; xres[2 * pi + 1] = v1;
               ss0 += v0 * v0 + v1 * v1;
               if (a.dump && lead) { st(a.x0_dump + 2 * pi, v0); st(a.x0_dump + 2 * pi + 1, v1); }
@@ -888,9 +911,11 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
         for (int k = 0; k < HPAIR; ++k) {
           const int pi = tid + k * NT;
           if (2 * pi < H) {
-            brg[2 * k] = xres[2 * pi] * r0 * gain_at(a, gain, 2 * pi);
-            brg[2 * k + 1] = xres[2 * pi + 1] * r0 * gain_at(a, gain, 2 * pi + 1);
-            if (lead) { st(a.bridge + 2 * pi, brg[2 * k]); st(a.bridge + 2 * pi + 1, brg[2 * k + 1]); }
+            const float b0 = xres[2 * pi] * r0 * gain_at(a, gain, 2 * pi);
+            const float b1 = xres[2 * pi + 1] * r0 * gain_at(a, gain, 2 * pi + 1);
+            brg[2 * pi] = b0;
+            brg[2 * pi + 1] = b1;
+            if (lead) { st(a.bridge + 2 * pi, b0); st(a.bridge + 2 * pi + 1, b1); }
           }
         }
       }
