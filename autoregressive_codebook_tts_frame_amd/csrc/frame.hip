@@ -1059,7 +1059,9 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
   constexpr int CPR = HD / DPC;            // chunks per row (lanes per position)
   constexpr int PG = ANT / CPR;             // position groups
   constexpr int W = (GQ + 2) * HD;         // q | k | v words of one row
+  constexpr int NS = ANW / GQ;              // position subsets of P.V
   static_assert(CPR == 16, "K/V rows of 256 bytes");
+  static_assert(ANW % GQ == 0 && 2 * 64 >= HD, "P.V wave layout");
   Common &cm = *reinterpret_cast<Common *>(smem);
   const Lds L = lds_layout(a);
   float *rowbuf = (float *)(smem + L.rowbuf);  // [2][GQ + 2][HD]
@@ -1230,64 +1232,53 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
           if (lane == 0) { stat[wave * 2] = mx; stat[wave * 2 + 1] = sum; }
         }
         __syncthreads();
-        // P.V: lanes (pg, chunk cc) accumulate their positions
-        float acc[GQ][DPC];
-#pragma unroll
-        for (int g = 0; g < GQ; ++g)
-#pragma unroll
-          for (int e = 0; e < DPC; ++e) acc[g][e] = 0.f;
-        for (int j = pg; j < n; j += PG) {
-          float vf[DPC];
-          unpack16<KVB>(*(const uint4 *)(vbase + (size_t)j * ROWB + cc * 16), vf);
-#pragma unroll
-          for (int g = 0; g < GQ; ++g) {
-            const float e = sc[g * TILE + j];
-#pragma unroll
-            for (int d = 0; d < DPC; ++d) acc[g][d] += e * vf[d];
+        // P.V: wave w takes query head w % GQ and the positions j = w / GQ
+        // (mod NS); each lane two adjacent dims, so no cross-lane reduction
+        {
+          const int g = wave % GQ, sub = wave / GQ;
+          if (2 * lane < HD) {
+            float o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+            for (int j = sub; j < n; j += NS) {
+              const float pj = sc[g * TILE + j];
+              float v0, v1;
+              if constexpr (KVB) {
+                const uint32_t w2 = *(const uint32_t *)(vbase + (size_t)j * ROWB + 4 * lane);
+                v0 = lo16(w2); v1 = hi16(w2);
+              } else {
+                const float2 f2 = *(const float2 *)(vbase + (size_t)j * ROWB + 8 * lane);
+                v0 = f2.x; v1 = f2.y;
+              }
+              o0 += pj * v0;
+              o1 += pj * v1;
+            }
+            *(float2 *)(pvred + (sub * GQ + g) * HD + 2 * lane) = make_float2(o0, o1);
           }
         }
-#pragma unroll
-        for (int g = 0; g < GQ; ++g)
-#pragma unroll
-          for (int d = 0; d < DPC; ++d) {
-            float v = acc[g][d];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[g][d] = v;
-          }
-        if (lane < CPR)
-#pragma unroll
-          for (int g = 0; g < GQ; ++g)
-#pragma unroll
-            for (int d = 0; d < DPC; ++d) pvred[(wave * GQ + g) * HD + cc * DPC + d] = acc[g][d];
         __syncthreads();
-        // sum of the waves' partials, element k of [GQ][HD]
+        // sum of the position subsets' partials, element k of [GQ][HD]
         auto pv = [&](int k) {
           float v = 0.f;
 #pragma unroll
-          for (int w = 0; w < ANW; ++w) v += pvred[w * GQ * HD + k];
+          for (int w = 0; w < NS; ++w) v += pvred[w * GQ * HD + k];
           return v;
         };
         // publish: normalised output (one tile) or the tile's partial
         if (ntile == 1) {
+          // every (word, copy) pair once, spread over the threads
           if (a.act_bf16) {
-            for (int i = tid; i < GQ * HD / 2; i += ANT) {
-              const int g = i / (HD / 2), d = 2 * (i % (HD / 2));
-              float o[2];
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                const int k = g * HD + d + e;
-                o[e] = pv(k) / stat[g * 2 + 1];
-              }
-              const uint32_t v = pack2(o[0], o[1]);
-              for (int r = 0; r < a.rep; ++r)
-                tput(a.ob + r * a.rep_stride + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, v, tag);
+            for (int i = tid; i < GQ * HD / 2 * a.rep; i += ANT) {
+              const int wi = i % (GQ * HD / 2), r = i / (GQ * HD / 2);
+              const int g = wi / (HD / 2), d = 2 * (wi % (HD / 2));
+              const float inv = 1.0f / stat[g * 2 + 1];
+              const uint32_t v = pack2(pv(g * HD + d) * inv, pv(g * HD + d + 1) * inv);
+              tput(a.ob + r * a.rep_stride + (size_t)m * (qd / 2) + ((kh * GQ + g) * HD + d) / 2, v, tag);
             }
           } else {
-            for (int i = tid; i < GQ * HD; i += ANT) {
-              const int g = i / HD;
-              const float o = pv(i) / stat[g * 2 + 1];
-              for (int r = 0; r < a.rep; ++r) tputf(a.ob + r * a.rep_stride + (size_t)m * qd + kh * GQ * HD + i, o, tag);
+            for (int i = tid; i < GQ * HD * a.rep; i += ANT) {
+              const int wi = i % (GQ * HD), r = i / (GQ * HD);
+              const float o = pv(wi) / stat[(wi / HD) * 2 + 1];
+              tputf(a.ob + r * a.rep_stride + (size_t)m * qd + kh * GQ * HD + wi, o, tag);
             }
           }
         } else {
