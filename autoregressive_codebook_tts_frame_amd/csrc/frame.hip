@@ -540,7 +540,9 @@ __device__ __forceinline__ float rms_inv(const FrameArgs &a, const float *pss) {
   float ss = pss[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) ss += pss[w];
-  return 1.0f / sqrtf(ss / (float)a.H + a.eps);
+  // mean by the hardware reciprocal of H (exact for a power of two) and
+  // v_rsq_f32 (1 ulp): a handful of instructions on the critical path
+  return __builtin_amdgcn_rsqf(ss * __builtin_amdgcn_rcpf((float)a.H) + a.eps);
 }
 // gain element e of a norm table (bf16 or f32) staged in LDS
 __device__ __forceinline__ float gain_at(const FrameArgs &a, const uint8_t *g, int e) {
@@ -929,8 +931,9 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       // item = row pair (2 p, 2 p + 1): z = SiLU(g) * u, rounded as the down projection's operand
       gemv_items<WT, 4, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[4][2]) {
         for (int m = 0; m < M; ++m) {
-          const float z0 = acc[0][m] / (1.0f + expf(-acc[0][m])) * acc[1][m];
-          const float z1 = acc[2][m] / (1.0f + expf(-acc[2][m])) * acc[3][m];
+          // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
+          const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
+          const float z1 = acc[2][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[2][m])) * acc[3][m];
           if (a.act_bf16) {
             if (lane < a.rep) tput(a.zb + lane * a.rep_stride + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
           } else if (lane < 2 * a.rep) {
@@ -1152,7 +1155,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
         const bool act = lane < HD / 2;
         const float x0 = act ? v[lane] : 0.f, x1 = act ? v[lane + HD / 2] : 0.f;
         const float ssum = wave_sum(x0 * x0 + x1 * x1);
-        const float r = 1.0f / sqrtf(ssum / (float)HD + a.eps);
+        const float r = __builtin_amdgcn_rsqf(ssum / (float)HD + a.eps);
         if (act) {
           const float y0 = x0 * r * g[lane], y1 = x1 * r * g[lane + HD / 2];
           const float c = rc[m * (HD / 2) + lane], sn = rs[m * (HD / 2) + lane];
@@ -1224,7 +1227,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
           mx = wave_max(mx);
           float sum = 0.f;
           for (int j = lane; j < n; j += 64) {
-            const float e = expf(sc[wave * TILE + j] - mx);
+            const float e = __expf(sc[wave * TILE + j] - mx);
             sc[wave * TILE + j] = e;
             sum += e;
           }
