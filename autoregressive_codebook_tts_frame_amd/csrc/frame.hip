@@ -399,6 +399,9 @@ template <> struct WEsz<W_Q8> { static constexpr int v = 1; };
 // 1 KB blocks a weight row of width H may span: its normalized operand lives
 // in registers (a q8 chunk takes twice the operand words of a bf16 one)
 __host__ __device__ constexpr int nb_hidden(int wt) { return wt == W_Q8 ? 1 : 2; }
+// 1 KB blocks of the O and down rows (widths nq*hd and F), whose operand
+// chunks are also held in registers per item
+__host__ __device__ constexpr int nb_wide(int wt) { return wt == W_Q8 ? 4 : 6; }
 
 // weight row (and q8 scale row) of output row n, matrix mat
 __device__ __forceinline__ void wrow_of(const FrameArgs &a, const Common &cm, const Ph &p, int n, int mat,
@@ -630,9 +633,14 @@ __device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uin
 // up rows of a row pair), round-robin over the compute waves; the results of
 // item it go to out(it, acc) as uniform values.  A row is at most MAXB 1 KB
 // blocks; an item's weight chunks are all loaded before its dot products.
-// op(m, cb, c) gives operand row m's elements for chunk c (block cb).
-template <int WT, int UPI, int MAXB, class Op, class Out>
-__device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int M, Out out) {
+// op(m, cb, c) gives operand row m's elements for chunk c (block cb);
+// pre(it) is read when item it starts and handed to out(it, acc, pre).
+struct NoPre {
+  __device__ __forceinline__ float operator()(int) const { return 0.f; }
+};
+template <int WT, int UPI, int MAXB, class Op, class Out, class Pre = NoPre>
+__device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int M, Out out,
+                                           Pre pre = Pre()) {
   constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rowb = s.K * ESZ, bpr = rowb >> 10;
@@ -645,6 +653,16 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
 #pragma unroll
       for (int cb = 0; cb < MAXB; ++cb)
         if (cb < bpr) w[q][cb] = ((const uint4 *)(slot + (size_t)(it * UPI + q) * rowb))[cb * 64 + lane];
+    const float pv = pre(it);
+    // the operand chunks too, before any dot product (from LDS they would
+    // otherwise wait one LDS round trip per block)
+    OpC x[2][MAXB];
+#pragma unroll
+    for (int cb = 0; cb < MAXB; ++cb)
+      if (cb < bpr) {
+        x[0][cb] = op(0, cb, cb * 64 + lane);
+        if (M > 1) x[1][cb] = op(1, cb, cb * 64 + lane);
+      }
     float acc[UPI][2];
 #pragma unroll
     for (int q = 0; q < UPI; ++q) acc[q][0] = acc[q][1] = 0.f;
@@ -652,14 +670,11 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
     for (int cb = 0; cb < MAXB; ++cb) {
       if (cb >= bpr) break;
       const int c = cb * 64 + lane;
-      const OpC x0 = op(0, cb, c);
-      OpC x1;
-      if (M > 1) x1 = op(1, cb, c);
 #pragma unroll
       for (int q = 0; q < UPI; ++q) {
         const uint8_t *scl = scb + (size_t)(it * UPI + q) * (s.K / 16);
-        acc[q][0] += chunk_dot<WT>(w[q][cb], x0, c, scl);
-        if (M > 1) acc[q][1] += chunk_dot<WT>(w[q][cb], x1, c, scl);
+        acc[q][0] += chunk_dot<WT>(w[q][cb], x[0][cb], c, scl);
+        if (M > 1) acc[q][1] += chunk_dot<WT>(w[q][cb], x[1][cb], c, scl);
       }
     }
 #pragma unroll
@@ -667,7 +682,7 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
       acc[q][0] = wave_sum(acc[q][0]);
       if (M > 1) acc[q][1] = wave_sum(acc[q][1]);
     }
-    out(it, acc);
+    out(it, acc, pv);
   }
 }
 
@@ -929,7 +944,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     // ---- GEMV; each wave publishes the rows it computed
     if (cur.type == PH_GU) {
       // item = row pair (2 p, 2 p + 1): z = SiLU(g) * u, rounded as the down projection's operand
-      gemv_items<WT, 4, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[4][2]) {
+      gemv_items<WT, 4, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[4][2], float) {
         for (int m = 0; m < M; ++m) {
           // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
           const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
@@ -947,7 +962,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      gemv_items<WT, 1, NBH>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2]) {
+      gemv_items<WT, 1, NBH>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2], float) {
         const int n = s.r0 + it;
         if (lane == 0) st(lg + n, acc[0][0]);
         pick(bv, bi, acc[0][0], n);
@@ -965,19 +980,22 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       const int type = cur.type, N = s.N;
       const bool hid = type == PH_D && cur.stack == 1 && a.dump;
       if (type == PH_QKV) {
-        gemv_items<WT, 1, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[1][2]) {
+        gemv_items<WT, 1, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[1][2], float) {
           if (lane < M) tputf(a.qkvb + (size_t)lane * N + s.r0 + it, lane ? acc[0][1] : acc[0][0], tag);
         });
       } else {
-        gemv_items<WT, 1, 6>(sp, op_row, s, M, [&](int it, float (&acc)[1][2]) {
+        // the residual element (lane: copy lane / M of row lane % M) is read
+        // when the item starts, off the path after the reduction
+        const int rm = M > 1 ? lane & 1 : 0, rr = M > 1 ? lane >> 1 : lane;
+        gemv_items<WT, 1, nb_wide(WT)>(sp, op_row, s, M, [&](int it, float (&acc)[1][2], float res) {
           const int n = s.r0 + it;
-          if (lane < M * a.rep) {  // lane: copy lane / M of row lane % M
-            const int m = M > 1 ? lane & 1 : 0, r = M > 1 ? lane >> 1 : lane;
-            const float x = xres[m * H + n] + (m ? acc[0][1] : acc[0][0]);
+          if (lane < M * a.rep) {
+            const int m = rm, r = rr;
+            const float x = res + (m ? acc[0][1] : acc[0][0]);
             tputf(a.xq + r * a.rep_stride + (size_t)m * H + n, x, tag);
             if (hid && r == 0) st(a.hidden_dump + (size_t)cur.layer * H + n, x);
           }
-        });
+        }, [&](int it) { return lane < M * a.rep ? xres[rm * H + s.r0 + it] : 0.f; });
       }
     }
     if (lane == 0)  // this wave is done with the phase's slot
@@ -1420,8 +1438,8 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   if (a.nwg > 1024) { *why = "more than 1024 workgroups"; return false; }
   if (a.rep < 1 || a.rep > 32) { *why = "exchange copies outside 1..32"; return false; }
   // GEMV rows held in registers per item: hidden-wide rows (gate/up pairs, heads)
-  // up to 2 KB, the others up to 6 KB
-  if (a.H * esz > 1024 * nb_hidden(a.wt) || qd * esz > 6144 || a.F * esz > 6144) {
+  // up to 2 KB (q8: 1 KB), the O and down rows up to 6 KB (q8: 4 KB)
+  if (a.H * esz > 1024 * nb_hidden(a.wt) || qd * esz > 1024 * nb_wide(a.wt) || a.F * esz > 1024 * nb_wide(a.wt)) {
     *why = "GEMV rows too wide";
     return false;
   }
