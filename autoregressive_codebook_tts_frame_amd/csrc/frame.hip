@@ -39,9 +39,10 @@
 namespace qtk {
 namespace {
 
-constexpr int NW = 7;            // compute waves of a GEMV workgroup
+constexpr int NW = 5;            // compute waves of a GEMV workgroup
 constexpr int NT = 64 * NW;      // their threads
-constexpr int NTB = NT + 64;     // plus the loader wave: two waves per SIMD
+constexpr int NLW = 3;           // loader waves (each keeps its own loads in flight)
+constexpr int NTB = NT + 64 * NLW;  // two waves per SIMD
 constexpr int ANT = 512;         // threads of an attention workgroup
 constexpr int ANW = ANT / 64;    // its waves
 constexpr int MAXLAYERS = 40;
@@ -208,7 +209,7 @@ struct Common {
   int abort;
   uint32_t cbar;   // compute-wave barrier arrivals
   uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
-  uint64_t ltime;  // tracing: when the loader wave's last slice had landed
+  uint64_t ltime;  // tracing: when a loader wave's part of the last slice had landed
   Share sh[PH_END];  // this GEMV workgroup's rows, per phase type
 };
 
@@ -440,20 +441,27 @@ __device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool q8) {
   return scales_off(s, esz) + (q8 ? up1k((uint32_t)(s.R * s.NM) * (s.K / 16)) : 0u);
 }
 
-// Issue the direct-to-LDS loads of phase p's weight slice (+ scales, gain).
-// Called by the loader wave only: every 1 KB block is one instruction of it.
+// Issue this loader wave's part of the direct-to-LDS loads of phase p's
+// weight slice: loader wave li takes weight blocks [li nb / NLW, (li + 1) nb /
+// NLW) and the last one also the q8 scales and the norm gain.  Every 1 KB
+// block is one instruction.  A wave can keep only a limited number of these
+// loads in flight, so several loader waves land a slice sooner.
 template <int WT>
 __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, const Ph &p, uint32_t slot) {
   constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63;
+  const int li = (int)(threadIdx.x >> 6) - NW;
   const Share s = cm.sh[p.type];
   const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
-  int b = 0;
-  for (int u = 0; u < U; ++u) {
+  const int nb = U * bpr, b1 = (li + 1) * nb / NLW;
+  for (int b = li * nb / NLW; b < b1;) {
+    const int u = b / bpr;
     const uint8_t *w, *sc;
     wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
-    for (int cb = 0; cb < bpr; ++cb, ++b) dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
+    for (int cb = b - u * bpr; cb < bpr && b < b1; ++cb, ++b)
+      dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
   }
+  if (li != NLW - 1) return;
   if constexpr (WT == W_Q8) {
     const int spu = s.K / 256, n = U * spu;  // 16-byte scale chunks per row, in all
     const uint32_t so = scales_off(s, ESZ);
@@ -523,7 +531,7 @@ __device__ __forceinline__ float chunk_dot(uint4 w, const OpC &x, int c, const u
   }
 }
 
-// Barrier of the compute waves (the loader wave never joins it): an arrival
+// Barrier of the compute waves (the loader waves never join it): an arrival
 // counter in LDS; gen counts this wave's barriers times NW.
 __device__ __forceinline__ bool cbar(const FrameArgs &a, Common &cm, uint32_t &gen) {
   gen += NW;
@@ -686,9 +694,9 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
   }
 }
 
-// The loader wave: streams each GEMV phase's weight slice into its LDS slot
-// one phase ahead and meets the compute waves once per phase, right after
-// their inputs are in.
+// The loader waves: stream each GEMV phase's weight slice (a part each) into
+// its LDS slot one phase ahead and meet the compute waves once per phase,
+// right after their inputs are in.
 template <int WT>
 __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, const Lds &L, unsigned char *smem) {
   const uint32_t s0 = lds_addr(smem + L.slot0), s1 = lds_addr(smem + L.slot1);
@@ -903,7 +911,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       if (M > 1) ss1 = wave_sum(ss1);
       if (lane == 0) { cm.pss[0][wave] = ss0; cm.pss[1][wave] = ss1; }
     }
-    __syncthreads();  // with the loader wave: inputs in LDS, this phase's slice landed
+    __syncthreads();  // with the loader waves: inputs in LDS, this phase's slice landed
     if (cm.abort) return;
     const uint64_t t1 = tracing ? wall_clock64() : 0;
     const uint64_t tl = tracing ? cm.ltime : 0;
@@ -1433,7 +1441,10 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   a.max_tiles = a.P / TILE;
   if (a.P % TILE) { *why = "talker positions not a multiple of 256"; return false; }
   if (a.hd * (a.kv_bf16 ? 2 : 4) != 256) { *why = "K/V rows must be 256 bytes"; return false; }
-  if (a.H > 2048 || a.H % 256) { *why = "hidden width above 2048 or not a multiple of 256"; return false; }
+  if (a.H > 2 * NT * HPAIR || a.H % 256) {
+    *why = "hidden width above 1920 or not a multiple of 256";
+    return false;
+  }
   if (a.Lt + a.Lp > MAXLAYERS || a.G > MAXHEADS) { *why = "too many layers or codebooks"; return false; }
   if (a.nwg > 1024) { *why = "more than 1024 workgroups"; return false; }
   if (a.rep < 1 || a.rep > 32) { *why = "exchange copies outside 1..32"; return false; }
