@@ -646,15 +646,16 @@ __device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uin
 struct NoPre {
   __device__ __forceinline__ float operator()(int) const { return 0.f; }
 };
+// Items go round-robin: this wave takes items wv, wv + nwv, ...
 template <int WT, int UPI, int MAXB, class Op, class Out, class Pre = NoPre>
 __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int M, Out out,
-                                           Pre pre = Pre()) {
+                                           Pre pre = Pre(), int wv = -1, int nwv = NW) {
   constexpr int ESZ = WEsz<WT>::v;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int rowb = s.K * ESZ, bpr = rowb >> 10;
   const int nitems = s.R * s.NM / UPI;
   const uint8_t *scb = slot + scales_off(s, ESZ);
-  for (int it = wave; it < nitems; it += NW) {
+  for (int it = wv < 0 ? (int)(threadIdx.x >> 6) : wv; it < nitems; it += nwv) {
     uint4 w[UPI][MAXB];
 #pragma unroll
     for (int q = 0; q < UPI; ++q)
@@ -694,6 +695,45 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
   }
 }
 
+// The gate/up phase's items of one wave (index wv of nwv): the normalized
+// operand built in registers, gate and up rows, z = SiLU(g) * u
+// published as the down projection's operand.  With two weight slots the
+// loader waves take items too (the gate/up slice is the largest and its row
+// pairs do not divide evenly over the compute waves).
+template <int WT>
+__device__ __forceinline__ void gu_items(const FrameArgs &a, const Common &cm, const float *xres, const uint8_t *sp,
+                                         int M, uint32_t tag, int wv, int nwv) {
+  constexpr int ESZ = WEsz<WT>::v;
+  constexpr int NBH = nb_hidden(WT);
+  const int lane = threadIdx.x & 63;
+  const Share s = cm.sh[PH_GU];
+  const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
+  const int bpr = a.H * ESZ >> 10;
+  const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
+  OpC xo[2][NBH];
+#pragma unroll
+  for (int cb = 0; cb < NBH; ++cb)
+    if (cb < bpr) {
+      xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, cb * 64 + lane);
+      if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + a.H, gain, r1, cb * 64 + lane);
+    }
+  // item = row pair (2 p, 2 p + 1)
+  gemv_items<WT, 4, NBH>(sp, [&](int m, int cb, int) -> OpC { return xo[m][cb]; }, s, M,
+                         [&](int it, float (&acc)[4][2], float) {
+    for (int m = 0; m < M; ++m) {
+      // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
+      const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
+      const float z1 = acc[2][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[2][m])) * acc[3][m];
+      if (a.act_bf16) {
+        if (lane < a.rep) tput(a.zb + lane * a.rep_stride + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
+      } else if (lane < 2 * a.rep) {
+        const int e = lane & 1;
+        tputf(a.zb + (lane >> 1) * a.rep_stride + (size_t)m * a.F + s.r0 + 2 * it + e, e ? z1 : z0, tag);
+      }
+    }
+  }, NoPre(), wv, nwv);
+}
+
 // The loader waves: stream each GEMV phase's weight slice (a part each) into
 // its LDS slot one phase ahead and meet the compute waves once per phase,
 // right after their inputs are in.
@@ -706,6 +746,7 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
   if (a.trace) cm.ltime = wall_clock64();
   int slot = 0;
   uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
+  uint32_t seq = 1;           // phase index of cur + 1 (its tag is tag_base + seq)
   bool have_next = false;     // the next phase's slice is already in its slot
   // until every compute wave has finished the current phase's GEMV
   auto wait_gemv = [&]() -> bool {
@@ -721,6 +762,13 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     __syncthreads();  // the compute waves have this phase's inputs (and are done with the last phase's slot)
     if (cm.abort) return;
     done += NW;
+    if (a.two_slots && cur.type == PH_GU) {
+      // its gate/up items first (the down phase waits for every one of them),
+      // then the down slice
+      const int M = cur.stack == 0 && cur.step == 0 ? 2 : 1;
+      gu_items<WT>(a, cm, (const float *)(smem + L.xres), smem + (slot ? L.slot1 : L.slot0), M, a.tag_base + seq,
+                   (int)(threadIdx.x >> 6), NW + NLW);
+    }
     if (ng.type != PH_END && !have_next) {
       if (!a.two_slots && !wait_gemv()) return;  // one slot: it is free once this phase's GEMV is done
       dma_slice<WT>(a, cm, ng, a.two_slots && !slot ? s1 : s0);
@@ -739,6 +787,10 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     wait_vm();
     if (a.trace) cm.ltime = wall_clock64();
     if (a.two_slots) slot ^= 1;
+    for (Ph q = next_phase(a, cur, a.pos0); ; q = next_phase(a, q, a.pos0)) {  // the phase index of ng
+      ++seq;
+      if (q.type != PH_ATTN && q.type != PH_COMB) break;
+    }
     cur = ng;
   }
 }
@@ -920,7 +972,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     const uint8_t *sp = smem + (slot ? L.slot1 : L.slot0);
     constexpr int NBH = nb_hidden(WT);
     OpC xo[2][NBH];  // [row][block]
-    if (normed) {
+    if (normed && cur.type != PH_GU) {  // (gate/up: inside gu_items)
       const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
       const int bpr = H * ESZ >> 10;
       const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
@@ -951,20 +1003,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
 
     // ---- GEMV; each wave publishes the rows it computed
     if (cur.type == PH_GU) {
-      // item = row pair (2 p, 2 p + 1): z = SiLU(g) * u, rounded as the down projection's operand
-      gemv_items<WT, 4, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[4][2], float) {
-        for (int m = 0; m < M; ++m) {
-          // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
-          const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
-          const float z1 = acc[2][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[2][m])) * acc[3][m];
-          if (a.act_bf16) {
-            if (lane < a.rep) tput(a.zb + lane * a.rep_stride + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
-          } else if (lane < 2 * a.rep) {
-            const int e = lane & 1;
-            tputf(a.zb + (lane >> 1) * a.rep_stride + (size_t)m * a.F + s.r0 + 2 * it + e, e ? z1 : z0, tag);
-          }
-        }
-      });
+      gu_items<WT>(a, cm, xres, sp, M, tag, wave, a.two_slots ? NW + NLW : NW);
     } else if (cur.type == PH_HEAD) {
       // logits and the wave's running argmax, then the workgroup's
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
