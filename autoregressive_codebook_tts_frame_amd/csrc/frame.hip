@@ -695,18 +695,18 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
   }
 }
 
-// The gate/up phase's items of one wave (index wv of nwv): the normalized
-// operand built in registers, gate and up rows, z = SiLU(g) * u
-// published as the down projection's operand.  With two weight slots the
-// loader waves take items too (the gate/up slice is the largest and its row
-// pairs do not divide evenly over the compute waves).
+// The QKV or gate/up phase's items of one wave (index wv of nwv): the
+// normalized operand built in registers from the residual rows, then QKV rows
+// (published as they are) or gate/up row pairs (z = SiLU(g) * u published as
+// the down projection's operand).  With two weight slots the loader waves take
+// items too: these slices' rows do not divide evenly over the compute waves.
 template <int WT>
-__device__ __forceinline__ void gu_items(const FrameArgs &a, const Common &cm, const float *xres, const uint8_t *sp,
-                                         int M, uint32_t tag, int wv, int nwv) {
+__device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &cm, int type, const float *xres,
+                                             const uint8_t *sp, int M, uint32_t tag, int wv, int nwv) {
   constexpr int ESZ = WEsz<WT>::v;
   constexpr int NBH = nb_hidden(WT);
   const int lane = threadIdx.x & 63;
-  const Share s = cm.sh[PH_GU];
+  const Share s = cm.sh[type];
   const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
   const int bpr = a.H * ESZ >> 10;
   const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
@@ -717,8 +717,15 @@ __device__ __forceinline__ void gu_items(const FrameArgs &a, const Common &cm, c
       xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, cb * 64 + lane);
       if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + a.H, gain, r1, cb * 64 + lane);
     }
+  auto op = [&](int m, int cb, int) -> OpC { return xo[m][cb]; };
+  if (type == PH_QKV) {
+    gemv_items<WT, 1, NBH>(sp, op, s, M, [&](int it, float (&acc)[1][2], float) {
+      if (lane < M) tputf(a.qkvb + (size_t)lane * s.N + s.r0 + it, lane ? acc[0][1] : acc[0][0], tag);
+    }, NoPre(), wv, nwv);
+    return;
+  }
   // item = row pair (2 p, 2 p + 1)
-  gemv_items<WT, 4, NBH>(sp, [&](int m, int cb, int) -> OpC { return xo[m][cb]; }, s, M,
+  gemv_items<WT, 4, NBH>(sp, op, s, M,
                          [&](int it, float (&acc)[4][2], float) {
     for (int m = 0; m < M; ++m) {
       // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
@@ -762,12 +769,12 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     __syncthreads();  // the compute waves have this phase's inputs (and are done with the last phase's slot)
     if (cm.abort) return;
     done += NW;
-    if (a.two_slots && cur.type == PH_GU) {
-      // its gate/up items first (the down phase waits for every one of them),
-      // then the down slice
+    if (a.two_slots && (cur.type == PH_GU || cur.type == PH_QKV)) {
+      // its items first (the next phase waits for every one of them), then
+      // the next slice
       const int M = cur.stack == 0 && cur.step == 0 ? 2 : 1;
-      gu_items<WT>(a, cm, (const float *)(smem + L.xres), smem + (slot ? L.slot1 : L.slot0), M, a.tag_base + seq,
-                   (int)(threadIdx.x >> 6), NW + NLW);
+      normed_items<WT>(a, cm, cur.type, (const float *)(smem + L.xres), smem + (slot ? L.slot1 : L.slot0), M,
+                       a.tag_base + seq, (int)(threadIdx.x >> 6), NW + NLW);
     }
     if (ng.type != PH_END && !have_next) {
       if (!a.two_slots && !wait_gemv()) return;  // one slot: it is free once this phase's GEMV is done
@@ -972,7 +979,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     const uint8_t *sp = smem + (slot ? L.slot1 : L.slot0);
     constexpr int NBH = nb_hidden(WT);
     OpC xo[2][NBH];  // [row][block]
-    if (normed && cur.type != PH_GU) {  // (gate/up: inside gu_items)
+    if (normed && !(cur.type == PH_GU || (cur.type == PH_QKV && a.two_slots))) {  // (else inside normed_items)
       const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
       const int bpr = H * ESZ >> 10;
       const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
@@ -1002,8 +1009,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     const uint64_t t2 = tracing ? wall_clock64() : 0;
 
     // ---- GEMV; each wave publishes the rows it computed
-    if (cur.type == PH_GU) {
-      gu_items<WT>(a, cm, xres, sp, M, tag, wave, a.two_slots ? NW + NLW : NW);
+    if (cur.type == PH_GU || (cur.type == PH_QKV && a.two_slots)) {
+      normed_items<WT>(a, cm, cur.type, xres, sp, M, tag, wave, a.two_slots ? NW + NLW : NW);
     } else if (cur.type == PH_HEAD) {
       // logits and the wave's running argmax, then the workgroup's
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
