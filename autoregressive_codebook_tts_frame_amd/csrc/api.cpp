@@ -26,7 +26,7 @@ constexpr int kPrefillChunk = 32;  // prompt rows per prefill step
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
-constexpr int kXchRep = 8;         // copies of the frame kernel's broadcast rows
+constexpr int kXchRep = 1;         // copies of the frame kernel's broadcast rows (1-8 measured alike)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
