@@ -600,11 +600,15 @@ __device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, co
 }
 
 // table row (bf16 or f32) element pairs of this thread -> v[2 * HPAIR]
+// (zero beyond the row: every element is written, so no value is carried
+// over from an earlier phase)
 __device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, size_t row, float *v) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < HPAIR; ++k) {
     const int pi = tid + k * NT;
+    v[2 * k] = 0.f;
+    v[2 * k + 1] = 0.f;
     if (2 * pi < a.H) {
       if (a.tab_bf16) {
         const uint32_t w = ld((const uint32_t *)((const uint16_t *)tab + row * a.H) + pi);
@@ -943,6 +947,10 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           if (a.dump && lead && tid == 0) st(a.tpos_dump, pos);
         }
       }
+      // The table loads above are all consumed; saying so here keeps the
+      // compiler from waiting on every memory operation (the last phase's
+      // stores included) at the top of each later phase.
+      wait_vm();
     } else {
       // residual rows (normed phases) or operand rows (O: attention output, D: SiLU-mul output)
       const uint64_t *src = xq;
