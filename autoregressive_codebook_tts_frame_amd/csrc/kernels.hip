@@ -12,6 +12,7 @@
 #include "kernels.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace qtk {
 
@@ -570,19 +571,25 @@ constexpr int GT = 32;        // output columns per tile
 constexpr int GBK = 256;      // K slice per workgroup
 constexpr int GXS = GBK + 8;  // LDS row stride (bf16) of the staged operand: conflict-free B reads
 
+// Weight row n of matrix `mat` (0: the segmented q|k|v or single matrix, 1:
+// up).  The segment is chosen with selects on the kernel arguments: indexing
+// a.seg[] with a computed index would read the argument block from memory
+// before the first weight load could issue.
 template <int WT>
 __device__ __forceinline__ const uint8_t *gemm_row(const GemmArgs &a, int mat, int n, const uint16_t *&sc) {
   constexpr size_t esz = WT == W_BF16 ? 2 : 1;
-  const Lin *L = &a.up;
+  const void *w = a.up.w;
+  const uint16_t *scb = a.up.sc;
   int r = n;
   if (mat == 0) {
-    int s = 0, base = 0;
-    while (s + 1 < a.nseg && n >= a.seg_end[s]) { base = a.seg_end[s]; ++s; }
-    L = &a.seg[s];
-    r = n - base;
+    const bool s1 = a.nseg > 1 && n >= a.seg_end[0];
+    const bool s2 = a.nseg > 2 && n >= a.seg_end[1];
+    w = s2 ? a.seg[2].w : s1 ? a.seg[1].w : a.seg[0].w;
+    scb = s2 ? a.seg[2].sc : s1 ? a.seg[1].sc : a.seg[0].sc;
+    r = n - (s2 ? a.seg_end[1] : s1 ? a.seg_end[0] : 0);
   }
-  sc = L->sc ? L->sc + (size_t)r * (a.K / 32) : nullptr;
-  return (const uint8_t *)L->w + (size_t)r * a.K * esz;
+  sc = scb ? scb + (size_t)r * (a.K / 32) : nullptr;
+  return (const uint8_t *)w + (size_t)r * a.K * esz;
 }
 
 __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int b) {
@@ -602,10 +609,19 @@ constexpr int CPOL_SC1 = 16;
 
 template <int WT, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  constexpr int NSUB = EPI == EPI_GATED ? 4 : 2;  // 16-row weight blocks per tile
+  // The tile's weight rows form NSUB blocks of 16; each block's K slice is
+  // split over WPB waves, so every wave owns SPW 32-wide steps of one block
+  // and loads them exactly once, then applies them to every 16-row activation
+  // block.
+  constexpr int NSUB = EPI == EPI_GATED ? 4 : 2;
+  constexpr int WPB = 4 / NSUB;
+  constexpr int SPW = GBK / 32 / WPB;
+  constexpr int NBLK = GBK / 32;  // q8 scale blocks per weight row in the slice
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * GXS];
   __shared__ float rinv[64];
   __shared__ float gs[GBK];
+  __shared__ float scl[WT == W_Q8 ? NSUB * 16 * NBLK : 1];
+  __shared__ __attribute__((aligned(16))) f32x4_t red[WPB > 1 ? 4 * 64 * (NSUB * (WPB - 1)) : 1];
   __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tn = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
@@ -614,33 +630,85 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int k0 = ks * GBK;
   const int NP = EPI == EPI_GATED ? 2 * N : N;  // partial columns (gated: gate then up)
   const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.part);
+  const int nb = wave / WPB, kq = wave % WPB;
+  const int mat = EPI == EPI_GATED ? nb / 2 : 0;
+  const int nrow0 = tn * GT + (EPI == EPI_GATED ? (nb % 2) : nb) * 16;
 
-  // RMSNorm row scales from the producers' sums of squares
-  if (tid < 64) {
-    float r = 1.f;
-    if (a.gain && tid < M) {
-      float sq = 0.f;
-      for (int i = 0; i < K / 32; ++i) sq += a.ssq[(size_t)tid * a.ssq_stride + i];
-      r = 1.0f / sqrtf(sq / (float)K + a.eps);
-    }
-    rinv[tid] = r;
-  }
-  gs[tid] = a.gain ? tab_at(a.gain, a.gain_bf16, k0 + tid) : 1.f;  // GBK == blockDim
-  __syncthreads();
-  // operand slice in LDS: rows < MT * 16 (zero past M), eight columns per item;
-  // a thread's (at most eight) items load first, then convert
+  // Loads first, in the order they are consumed, so that waiting for the
+  // operand does not wait for the weights: the rows' sums of squares (thread
+  // t sums row t / 4's slots t % 4, t % 4 + 4, ...), the gain, the operand
+  // slice (eight columns per item), q8 scales, then the weights.  Every load
+  // is unconditional, from a clamped in-bounds address, and masked where it is
+  // used: a load under a branch makes the compiler wait for it at the join.
+  const int sm = tid >> 2, sq4 = tid & 3;
+  const bool norm_row = a.gain && sm < M;
+  const float *ssp = a.gain ? a.ssq + (size_t)min(sm, M - 1) * a.ssq_stride : a.x;
+  float sqv[8];  // slots sq4 + 4 i, i < 8 (hidden widths up to 1024; wider rows add a loop)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sqv[i] = ssp[min(sq4 + 4 * i, K / 32 - 1)];
+  // the gain element as two 16-bit loads (bf16: the same half twice); without
+  // a norm, row 0 of x stands in as an in-bounds address
+  const uint16_t *gp = (const uint16_t *)(a.gain ? a.gain : (const void *)a.x);
+  const size_t gi = a.gain_bf16 ? (size_t)(k0 + tid) : 2 * (size_t)(k0 + tid);  // GBK == blockDim
+  const uint16_t glo = gp[gi], ghi = gp[a.gain_bf16 ? gi : gi + 1];
   constexpr int IT = 64 * (GBK / 8) / 256;
   float4 xv[IT][2];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
-    xv[it][0] = xv[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (m < M) {
-      const float *xr = a.x + (size_t)m * a.x_stride + k0 + 8 * c;
-      xv[it][0] = *(const float4 *)xr;
-      xv[it][1] = *(const float4 *)(xr + 4);
+    if (it * 256 >= MT * 16 * (GBK / 8)) break;  // rows past the last 16-row block
+    const float *xr = a.x + (size_t)min(m, M - 1) * a.x_stride + k0 + 8 * c;
+    xv[it][0] = *(const float4 *)xr;
+    xv[it][1] = *(const float4 *)(xr + 4);
+  }
+  constexpr int NSC = NSUB * 16 * NBLK / 256;  // q8 scales per thread
+  static_assert(NSUB * 16 * NBLK % 256 == 0 && 64 % NBLK == 0, "a wave's scales lie in one weight block");
+  uint16_t sv[NSC];
+  if constexpr (WT == W_Q8) {
+    // entry e: tile row r = e / NBLK (block r / 16, row r % 16 of it), scale
+    // block e % NBLK; a wave's 64 entries are rows of one block
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) {
+      const int e = tid + 256 * q, r = e / NBLK, b = e % NBLK;
+      const int rb = __builtin_amdgcn_readfirstlane(r / 16);
+      const int rn0 = tn * GT + (EPI == EPI_GATED ? (rb % 2) : rb) * 16;
+      const uint16_t *sp;
+      (void)gemm_row<WT>(a, EPI == EPI_GATED ? rb / 2 : 0, rn0, sp);
+      sv[q] = sp[(size_t)(r % 16) * (K / 32) + k0 / 32 + b];
     }
   }
+  typedef typename std::conditional<WT == W_BF16, uint4, uint2>::type WVec;
+  WVec wv[SPW];
+  {
+    // the block's 16 rows lie in one segment (segment ends are multiples of 16)
+    const int n0 = __builtin_amdgcn_readfirstlane(nrow0);
+    const uint16_t *sc;
+    const uint8_t *wr = gemm_row<WT>(a, __builtin_amdgcn_readfirstlane(mat), n0, sc);
+    const int n = n0 + (lane & 15);  // the weight row this lane loads
+    constexpr size_t esz = WT == W_BF16 ? 2 : 1;
+    wr += (size_t)(n < N ? lane & 15 : 0) * K * esz;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int k = k0 + (kq * SPW + s) * 32 + (lane >> 4) * 8;
+      wv[s] = *(const WVec *)(wr + (size_t)k * esz);
+    }
+  }
+
+  // RMSNorm row scales, gain and q8 scales to LDS
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sq += norm_row && sq4 + 4 * i < K / 32 ? sqv[i] : 0.f;
+  if (norm_row)
+    for (int i = sq4 + 32; i < K / 32; i += 4) sq += ssp[i];
+  sq += __shfl_xor(sq, 1, 64);
+  sq += __shfl_xor(sq, 2, 64);
+  if (sq4 == 0) rinv[sm] = a.gain ? 1.0f / sqrtf(sq / (float)K + a.eps) : 1.f;
+  gs[tid] = !a.gain ? 1.f : __uint_as_float(a.gain_bf16 ? (uint32_t)glo << 16 : ((uint32_t)ghi << 16) | glo);
+  if constexpr (WT == W_Q8)
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) scl[tid + 256 * q] = f16_to_f32(sv[q]);
+  __syncthreads();
+  // operand slice in LDS as bf16: rows < MT * 16 (zero past M)
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
@@ -666,49 +734,62 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
   __syncthreads();
 
-  // products: wave w takes (weight block nb, row block mt) pairs p = w, w + 4, ...
-  for (int p = wave; p < NSUB * MT; p += 4) {
-    const int nb = p % NSUB, mt = p / NSUB;
-    const int mat = EPI == EPI_GATED ? nb / 2 : 0;
-    const int nrow0 = tn * GT + (EPI == EPI_GATED ? (nb % 2) : nb) * 16;
-    const int n = nrow0 + (lane & 15);  // the weight row this lane loads
-    const uint16_t *sc;
-    const uint8_t *wr = gemm_row<WT>(a, mat, n < N ? n : 0, sc);
-    const uint16_t *scj[4];  // q8: scale rows of this lane's four outputs
-    if constexpr (WT == W_Q8) {
+  // products of this wave's steps with every activation block
+  f32x4_t acc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int nj = nrow0 + (lane >> 4) * 4 + j;
-        const uint16_t *s2;
-        (void)gemm_row<WT>(a, mat, nj < N ? nj : 0, s2);
-        scj[j] = s2;
-      }
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int kl = (kq * SPW + s) * 32;  // step's offset in the slice
+    bf16x8_t av;
+    if constexpr (WT == W_BF16) {
+      av = __builtin_bit_cast(bf16x8_t, wv[s]);
+    } else {
+      const uint4 wq = make_uint4(i8pair_bf16(wv[s].x, 0), i8pair_bf16(wv[s].x, 2), i8pair_bf16(wv[s].y, 0),
+                                  i8pair_bf16(wv[s].y, 2));
+      av = __builtin_bit_cast(bf16x8_t, wq);
     }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < GBK / 32; ++st) {
-      const int k = k0 + st * 32 + (lane >> 4) * 8;
-      const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + st * 32 + (lane >> 4) * 8];
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= MT) break;
+      const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + kl + (lane >> 4) * 8];
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bx);
       if constexpr (WT == W_BF16) {
-        const uint4 w = *(const uint4 *)(wr + (size_t)k * 2);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), bv, acc, 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mt], 0, 0, 0);
       } else {
-        const uint2 w = *(const uint2 *)(wr + k);
-        const uint4 wq = make_uint4(i8pair_bf16(w.x, 0), i8pair_bf16(w.x, 2), i8pair_bf16(w.y, 0), i8pair_bf16(w.y, 2));
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wq), bv, zero, 0, 0, 0);
-        const int blk = (k0 + st * 32) / 32;
+        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero, 0, 0, 0);
+        const float *sr = &scl[(nb * 16 + (lane >> 4) * 4) * NBLK + kl / 32];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += t[j] * f16_to_f32(scj[j][blk]);
+        for (int j = 0; j < 4; ++j) acc[mt][j] += t[j] * sr[j * NBLK];
       }
     }
-    // this lane's four partials are four consecutive columns of row m
-    const int m = mt * 16 + (lane & 15);
+  }
+  // waves of one block sum their K parts (lower K part first)
+  if constexpr (WPB > 1) {
+    if (kq > 0)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        if (mt < MT) red[((nb * (WPB - 1) + kq - 1) * 4 + mt) * 64 + lane] = acc[mt];
+    __syncthreads();
+    if (kq == 0)
+#pragma unroll
+      for (int q = 1; q < WPB; ++q)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if (mt < MT) acc[mt] += red[((nb * (WPB - 1) + q - 1) * 4 + mt) * 64 + lane];
+  }
+  // this lane's four partials are four consecutive columns of row m
+  if (kq == 0) {
     const int nj = nrow0 + (lane >> 4) * 4;
-    if (m < M && nj < N)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc), prs,
-                                             (int)((((size_t)ks * M + m) * NP + (mat ? N : 0) + nj) * 4), 0, CPOL_SC1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int m = mt * 16 + (lane & 15);
+      if (mt < MT && m < M && nj < N)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc[mt]), prs,
+                                               (int)((((size_t)ks * M + m) * NP + (mat ? N : 0) + nj) * 4), 0,
+                                               CPOL_SC1);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
   __syncthreads();
@@ -724,7 +805,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile
   const int m = tid >> 2, c0 = (tid & 3) * 8;
   const int nb0 = tn * GT + c0;
-  float sq = 0.f;
+  sq = 0.f;
   if (m < M && nb0 < N) {
     float g8[8], u8[8];
 #pragma unroll
@@ -786,7 +867,9 @@ static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
-  if (a.M < 1 || a.M > 64 || a.K % GBK || a.N % GT) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 64 || a.K % GBK || a.N % GT || a.nseg < 1 || a.nseg > 3) return hipErrorInvalidValue;
+  for (int i = 0; i + 1 < a.nseg; ++i)  // a 16-row weight block never straddles two segments
+    if (a.seg_end[i] % 16) return hipErrorInvalidValue;
   if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);
   if (wtype == W_Q8) return gemm_wt<W_Q8>(epi, a, s);
   return hipErrorInvalidValue;
