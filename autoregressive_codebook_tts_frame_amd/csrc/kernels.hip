@@ -802,51 +802,57 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   if (!last) return;
 
   // the tile's last workgroup: sum the K slices in order, then the epilogue;
-  // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile
+  // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile.  The
+  // residual row and every slice of a group (all of them for K <= 3072) are
+  // requested before the first sum, so the epilogue waits for one round trip.
   const int m = tid >> 2, c0 = (tid & 3) * 8;
   const int nb0 = tn * GT + c0;
   sq = 0.f;
   if (m < M && nb0 < N) {
+    float *yr = a.y + (size_t)m * a.y_stride + nb0;
+    float yv[8];
+    if constexpr (EPI == EPI_RESID)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[i] = yr[i];
     float g8[8], u8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) g8[i] = u8[i] = 0.f;
-    // slices four at a time: every load of a group in flight before the sums
-    for (int q0 = 0; q0 < KS; q0 += 4) {
-      f32x4v_t lg[4][2], lu[4][2];
+    constexpr int QG = EPI == EPI_GATED ? 6 : 12;  // slices per group
+    for (int q0 = 0; q0 < KS; q0 += QG) {
+      f32x4v_t lg[QG][2], lu[EPI == EPI_GATED ? QG : 1][2];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
+      for (int qq = 0; qq < QG; ++qq)
         if (q0 + qq < KS) {
           const int off = (int)((((size_t)(q0 + qq) * M + m) * NP + nb0) * 4);
           lg[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, CPOL_SC1));
           lg[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16, 0, CPOL_SC1));
-          if (EPI == EPI_GATED) {
+          if constexpr (EPI == EPI_GATED) {
             lu[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4, 0, CPOL_SC1));
             lu[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4 + 16, 0, CPOL_SC1));
           }
         }
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
+      for (int qq = 0; qq < QG; ++qq)
         if (q0 + qq < KS)
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             g8[i] += lg[qq][i >> 2][i & 3];
-            if (EPI == EPI_GATED) u8[i] += lu[qq][i >> 2][i & 3];
+            if constexpr (EPI == EPI_GATED) u8[i] += lu[qq][i >> 2][i & 3];
           }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int n = nb0 + i;
       const float g = g8[i], u = u8[i];
-      float *yp = a.y + (size_t)m * a.y_stride + n;
       if constexpr (EPI == EPI_STORE) {
-        *yp = g;
+        yr[i] = g;
       } else if constexpr (EPI == EPI_RESID) {
-        const float v = *yp + g;
-        *yp = v;
+        const float v = yv[i] + g;
+        yr[i] = v;
         if (a.copy_out) a.copy_out[(size_t)m * a.copy_stride + n] = v;
         sq += v * v;
       } else {
-        *yp = silu(g) * u;
+        yr[i] = silu(g) * u;
       }
     }
   }
@@ -975,12 +981,22 @@ hipError_t launch_pred_input(const PredInArgs &a, hipStream_t s) {
 __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *lg = a.logits + (size_t)r * a.Vc;
+  // Eight logits per thread in flight at a time (a plain loop waits on each
+  // load); the first group is outside any loop.
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = tid; i < a.Vc; i += 256) {
-    const float v = lg[i];
-    if (v > best) { best = v; bi = i; }   // increasing i: first max kept
-  }
+  auto scan = [&](int i0) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = lg[min(i0 + u * 256 + tid, a.Vc - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < a.Vc && v[u] > best) { best = v[u]; bi = i; }  // increasing i: first max kept
+    }
+  };
+  scan(0);
+  for (int i0 = 8 * 256; i0 < a.Vc; i0 += 8 * 256) scan(i0);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(best, o, 64);
@@ -1019,10 +1035,18 @@ __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
     const int c = code;
     const size_t base = ((size_t)(a.j + 1) * a.Vc + c) * a.H;
     float sq = 0.f;
-    for (int i = tid; i < a.H; i += 256) {
-      const float v = tab_at(a.code_emb, a.tab_bf16, base + i);
-      a.x_next[(size_t)r * a.H + i] = v;
-      sq += v * v;
+    for (int i0 = 0; i0 < a.H; i0 += 4 * 256) {  // four loads in flight per thread
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = tab_at(a.code_emb, a.tab_bf16, base + min(i0 + u * 256 + tid, a.H - 1));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 256 + tid;
+        if (i < a.H) {
+          a.x_next[(size_t)r * a.H + i] = v[u];
+          sq += v[u] * v[u];
+        }
+      }
     }
     if (a.ssq) put_ssq(a.ssq, a.H, r, 0, a.H, sq);
   }
