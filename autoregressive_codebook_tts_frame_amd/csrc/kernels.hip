@@ -390,32 +390,42 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pg = tid / CPR, cc = tid % CPR;
 
-  __shared__ float qs[G][HD];
   __shared__ float sc[G][256];
   __shared__ float stat[G][2];
   __shared__ float red[4][G][HD];
 
-  for (int i = tid; i < G * HD; i += 256)
-    qs[i / HD][i % HD] = a.q[(size_t)r * a.nq * HD + (size_t)kh * G * HD + i];
-  __syncthreads();
-
+  // This thread's q chunks, then the tile's K rows, then its V rows, all
+  // requested before the first use of any of them (in that order, so each use
+  // waits only for what it needs).  The loads are unconditional: rows past
+  // the context read the tile's row 0 and are never used (a load skipped by
+  // a branch would make the compiler wait for every load at the join).
+  float qr[G][DPC];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float *qp = a.q + (size_t)r * a.nq * HD + (size_t)(kh * G + g) * HD + cc * DPC;
+#pragma unroll
+    for (int e = 0; e < DPC; e += 4) {
+      const float4 v = *(const float4 *)(qp + e);
+      qr[g][e] = v.x; qr[g][e + 1] = v.y; qr[g][e + 2] = v.z; qr[g][e + 3] = v.w;
+    }
+  }
   const size_t head_off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD;
   const uint8_t *kbase = (const uint8_t *)a.ring_layer + (head_off + (size_t)j0 * HD) * ESZ;
   const uint8_t *vbase = (const uint8_t *)a.ring_layer + (head_off + a.kv_stride + (size_t)j0 * HD) * ESZ;
+  uint4 kc[NP], vc[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int j = p * PG + pg;
+    kc[p] = *(const uint4 *)(kbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int j = p * PG + pg;
+    vc[p] = *(const uint4 *)(vbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
+  }
 
   // scores
   {
-    uint4 kc[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int j = p * PG + pg;
-      kc[p] = j < jn ? *(const uint4 *)(kbase + (size_t)j * HD * ESZ + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    float qr[G][DPC];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < DPC; ++e) qr[g][e] = qs[g][cc * DPC + e];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       if (p * PG >= jn) break;
@@ -450,12 +460,6 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   __syncthreads();
   // P.V: lanes (pg, chunk cc) accumulate their rows
   {
-    uint4 vc[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int j = p * PG + pg;
-      vc[p] = j < jn ? *(const uint4 *)(vbase + (size_t)j * HD * ESZ + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
     float acc[G][DPC];
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -514,14 +518,38 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
   const int ntiles = (pos + a.tile) / a.tile;
   if (ntiles == 1) return;
   const float *p = a.part + ((size_t)r * a.nq + h) * a.max_tiles * (HD + 2);
-  float mx = -INFINITY;
-  for (int t = 0; t < ntiles; ++t) mx = fmaxf(mx, p[(size_t)t * (HD + 2) + HD]);
-  float L = 0.f, O = 0.f;
-  for (int t = 0; t < ntiles; ++t) {
-    const float *pt = p + (size_t)t * (HD + 2);
-    const float w = expf(pt[HD] - mx);
-    L += pt[HD + 1] * w;
-    O += pt[d] * w;
+  // Tiles in groups of 16 with every load of a group in flight at once.  Up
+  // to 16 tiles (2,048 positions) this is the plain two-pass merge: the
+  // group's maximum, then its weighted sums in tile order; later groups are
+  // merged online (the running sums rescaled to the new maximum).
+  constexpr int TG = 16;
+  float mx = -INFINITY, L = 0.f, O = 0.f;
+  for (int t0 = 0; t0 < ntiles; t0 += TG) {
+    float mv[TG], lv[TG], ov[TG];
+#pragma unroll
+    for (int u = 0; u < TG; ++u) {
+      const float *pt = p + (size_t)min(t0 + u, ntiles - 1) * (HD + 2);
+      mv[u] = pt[HD];
+      lv[u] = pt[HD + 1];
+      ov[u] = pt[d];
+    }
+    float cm = mx;
+#pragma unroll
+    for (int u = 0; u < TG; ++u)
+      if (t0 + u < ntiles) cm = fmaxf(cm, mv[u]);
+    if (t0 > 0) {
+      const float sc = expf(mx - cm);
+      L *= sc;
+      O *= sc;
+    }
+#pragma unroll
+    for (int u = 0; u < TG; ++u)
+      if (t0 + u < ntiles) {
+        const float w = expf(mv[u] - cm);
+        L += lv[u] * w;
+        O += ov[u] * w;
+      }
+    mx = cm;
   }
   a.o[(size_t)r * a.nq * HD + (size_t)h * HD + d] = O / L;
 }
