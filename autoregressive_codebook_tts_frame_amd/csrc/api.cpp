@@ -315,17 +315,28 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   const int ss = d.H / 32;
   if ((e = project(c, EPI_STORE, g, ssq, ss, nullptr)) != hipSuccess) return e;
 
-  // 2. q/k norm + RoPE + K/V rows into the ring at the row's position
-  QkArgs qa = {};
-  qa.qkv = qkv; qa.M = M; qa.rows = rows; qa.nq = d.nq; qa.nkv = d.nkv;
-  qa.q_gain = w.q_norm; qa.k_gain = w.k_norm; qa.gain_bf16 = md.tab_bf16; qa.eps = (float)md.eps;
-  qa.rope_cos = c->A<float>(c->L.rope_cos); qa.rope_sin = c->A<float>(c->L.rope_sin);
-  qa.q_out = q; qa.ring_layer = ring_layer; qa.slot_stride = st.slot_stride;
-  qa.kv_stride = st.kv_stride; qa.P = st.P;
-  if ((e = launch_qk_rope_kv(d.hd, md.kv_bf16, qa, s)) != hipSuccess) return e;
+  // 2. q/k norm + RoPE + K/V rows into the ring at the row's position: the
+  // attention tile's prologue for the predictor's decode steps (one tile per
+  // row, latency-bound); a kernel of its own for prefill chunks and for the
+  // talker, whose long tiles stream K/V at a higher occupancy without it
+  const bool fused = rows.rows_per_slot <= 2 && st.max_tiles == 1;
+  if (!fused) {
+    QkArgs qa = {};
+    qa.qkv = qkv; qa.M = M; qa.rows = rows; qa.nq = d.nq; qa.nkv = d.nkv;
+    qa.q_gain = w.q_norm; qa.k_gain = w.k_norm; qa.gain_bf16 = md.tab_bf16; qa.eps = (float)md.eps;
+    qa.rope_cos = c->A<float>(c->L.rope_cos); qa.rope_sin = c->A<float>(c->L.rope_sin);
+    qa.q_out = q; qa.ring_layer = ring_layer; qa.slot_stride = st.slot_stride;
+    qa.kv_stride = st.kv_stride; qa.P = st.P;
+    if ((e = launch_qk_rope_kv(d.hd, md.kv_bf16, qa, s)) != hipSuccess) return e;
+  }
 
   // 3. attention over the (padded) window
   AttnArgs aa = {};
+  if (fused) {
+    aa.qkv = qkv;
+    aa.q_gain = w.q_norm; aa.k_gain = w.k_norm; aa.gain_bf16 = md.tab_bf16; aa.eps = (float)md.eps;
+    aa.rope_cos = c->A<float>(c->L.rope_cos); aa.rope_sin = c->A<float>(c->L.rope_sin);
+  }
   aa.q = q; aa.M = M; aa.rows = rows; aa.nq = d.nq; aa.nkv = d.nkv;
   aa.ring_layer = ring_layer; aa.slot_stride = st.slot_stride; aa.kv_stride = st.kv_stride;
   aa.P = st.P; aa.tile = st.tile; aa.max_tiles = st.max_tiles;

@@ -73,6 +73,15 @@ struct AttnArgs {
   float scale;
   float *o;           // [M][nq hd]
   float *part;        // [M][nq][max_tiles][hd + 2]
+  // Fused q/k norm + RoPE + set_rows (rows_per_slot <= 2): q is built from
+  // qkv instead of read from q, and the K/V rows of the step's new positions
+  // are built in the workgroup and written to the ring by the row they
+  // belong to.  qkv null: q holds the rotated queries and the ring the rows.
+  const float *qkv;   // [M][(nq + 2 nkv) hd]
+  const void *q_gain, *k_gain;
+  int32_t gain_bf16;
+  float eps;
+  const float *rope_cos, *rope_sin;  // [rope_rows][hd/2]
 };
 
 struct GatherArgs {

@@ -275,6 +275,22 @@ hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s) {
 // does not depend on the position ([QT-log] set_rows entry; [MC-opt] core
 // table, q/k norm + RoPE + v copy).
 
+// Per-head RMSNorm then NeoX RoPE of one head vector, one wave per vector:
+// lane i < HD/2 holds the pair (x0, x1) = (x_i, x_{i+HD/2}) (the other lanes
+// hold zeros and take part in the norm's sum only), its gains g0, g1 and the
+// position's cos / sin, and gets the rotated pair in o0, o1.  Shared by the
+// separate kernel and the fused attention prologue, so both round alike.
+template <int HD>
+__device__ __forceinline__ void qk_norm_rope(float x0, float x1, float g0, float g1, float c, float sn, float eps,
+                                             float &o0, float &o1) {
+  const float s = wave_sum(x0 * x0 + x1 * x1);
+  const float rv = 1.0f / sqrtf(s / (float)HD + eps);
+  const float y0 = x0 * rv * g0;
+  const float y1 = x1 * rv * g1;
+  o0 = y0 * c - y1 * sn;
+  o1 = y1 * c + y0 * sn;
+}
+
 template <int HD, bool KVB>
 __global__ __launch_bounds__(64) void qk_rope_kv_kernel(QkArgs a) {
   constexpr int HALF = HD / 2;
@@ -287,15 +303,12 @@ __global__ __launch_bounds__(64) void qk_rope_kv_kernel(QkArgs a) {
   const float *src = isq ? row + h * HD : row + qd + kh * HD;
   const void *gain = isq ? a.q_gain : a.k_gain;
   const bool act = lane < HALF;
-  float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + HALF] : 0.f;
-  const float s = wave_sum(x0 * x0 + x1 * x1);
-  const float rv = 1.0f / sqrtf(s / (float)HD + a.eps);
+  const float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + HALF] : 0.f;
+  const int ln = act ? lane : 0;  // idle lanes read pair 0 (in bounds) and discard it
+  float o0, o1;
+  qk_norm_rope<HD>(x0, x1, tab_at(gain, a.gain_bf16, ln), tab_at(gain, a.gain_bf16, ln + HALF),
+                   a.rope_cos[(size_t)pos * HALF + ln], a.rope_sin[(size_t)pos * HALF + ln], a.eps, o0, o1);
   if (!act) return;
-  const float y0 = x0 * rv * tab_at(gain, a.gain_bf16, lane);
-  const float y1 = x1 * rv * tab_at(gain, a.gain_bf16, lane + HALF);
-  const float c = a.rope_cos[(size_t)pos * HALF + lane], sn = a.rope_sin[(size_t)pos * HALF + lane];
-  const float o0 = y0 * c - y1 * sn;
-  const float o1 = y1 * c + y0 * sn;
   if (isq) {
     float *dst = a.q_out + (size_t)r * qd + h * HD;
     dst[lane] = o0;
@@ -360,6 +373,15 @@ __device__ __forceinline__ float group_sum<16>(float v) {  // one DPP row
   return v;
 }
 
+// Workgroup barrier for data in LDS only: each wave's LDS operations are
+// complete, while its global loads and stores stay in flight (the fence of
+// __syncthreads also covers global memory, so it would wait for all of them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 16-byte K/V chunk -> floats
 template <bool KVB>
 __device__ __forceinline__ void kv_unpack(uint4 w, float *v) {
@@ -374,7 +396,7 @@ __device__ __forceinline__ void kv_unpack(uint4 w, float *v) {
 // Lanes work in groups of CPR = one K/V row (16-byte chunk each): a row is one
 // coalesced read, PG = 256 / CPR rows per pass, and every chunk a thread needs
 // is requested before it is used.
-template <int HD, int G, bool KVB>
+template <int HD, int G, bool KVB, bool FUSED>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   constexpr int ESZ = KVB ? 2 : 4;
   constexpr int DPC = 16 / ESZ;   // values per chunk
@@ -393,20 +415,63 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   __shared__ float sc[G][256];
   __shared__ float stat[G][2];
   __shared__ float red[4][G][HD];
+  __shared__ float qs[FUSED ? G : 1][HD];                                       // rotated queries
+  __shared__ __attribute__((aligned(16))) uint32_t nrow[FUSED ? 2 : 1][2][HD * ESZ / 4];  // new K, V rows
 
-  // This thread's q chunks, then the tile's K rows, then its V rows, all
-  // requested before the first use of any of them (in that order, so each use
-  // waits only for what it needs).  The loads are unconditional: rows past
-  // the context read the tile's row 0 and are never used (a load skipped by
-  // a branch would make the compiler wait for every load at the join).
+  // Fused prologue (decode steps: one or two rows per slot).  Items, one wave
+  // each: the G query heads of row r, then the K rows of head kh at the
+  // slot's new positions that fall in this tile (a slot's second row also
+  // attends to its first row's position).  Their inputs are requested first,
+  // then the ring rows, so the prologue waits only for its own loads.
+  constexpr int HALF = HD / 2;
+  const int qd = a.nq * HD, kd = a.nkv * HD;
+  int rs0 = r, p0 = pos, p1 = pos;
+  bool need0 = false, need1 = false;
+  constexpr int NS = (G + 2 + 3) / 4;  // prologue items per wave
+  float fx0[NS], fx1[NS], fg0[NS], fg1[NS], fc[NS], fs[NS], fv0[NS], fv1[NS];
+  if constexpr (FUSED) {
+    const int rps = a.rows.rows_per_slot;
+    rs0 = r - r % rps;
+    p0 = row_pos(a.rows, rs0);
+    p1 = rps > 1 ? row_pos(a.rows, rs0 + 1) : pos;
+    need0 = p0 >= j0 && p0 - j0 < jn;  // inside this tile, at or before pos
+    need1 = rps > 1 && p1 >= j0 && p1 - j0 < jn;
+    const int ln = lane & (HALF - 1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int it = wave + 4 * s, i = it - G;
+      const bool isq = it < G, isk = (i == 0 && need0) || (i == 1 && need1);
+      const int rr = isk ? rs0 + i : r, pp = isk ? (i ? p1 : p0) : pos;
+      const float *row = a.qkv + (size_t)rr * (qd + 2 * kd);
+      const float *src = isk ? row + qd + kh * HD : row + (kh * G + (isq ? it : 0)) * HD;
+      const void *gain = isk ? a.k_gain : a.q_gain;
+      fx0[s] = src[ln];
+      fx1[s] = src[ln + HALF];
+      fg0[s] = tab_at(gain, a.gain_bf16, ln);
+      fg1[s] = tab_at(gain, a.gain_bf16, ln + HALF);
+      fc[s] = a.rope_cos[(size_t)pp * HALF + ln];
+      fs[s] = a.rope_sin[(size_t)pp * HALF + ln];
+      fv0[s] = row[qd + kd + kh * HD + ln];
+      fv1[s] = row[qd + kd + kh * HD + ln + HALF];
+    }
+  }
+
+  // This thread's q chunks (unfused), then the tile's K rows, then its V
+  // rows, all requested before the first use of any of them (in that order,
+  // so each use waits only for what it needs).  The loads are unconditional:
+  // rows past the context read the tile's row 0 and are never used (a load
+  // skipped by a branch would make the compiler wait for every load at the
+  // join).
   float qr[G][DPC];
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float *qp = a.q + (size_t)r * a.nq * HD + (size_t)(kh * G + g) * HD + cc * DPC;
+    for (int g = 0; g < G; ++g) {
+      const float *qp = a.q + (size_t)r * a.nq * HD + (size_t)(kh * G + g) * HD + cc * DPC;
 #pragma unroll
-    for (int e = 0; e < DPC; e += 4) {
-      const float4 v = *(const float4 *)(qp + e);
-      qr[g][e] = v.x; qr[g][e + 1] = v.y; qr[g][e + 2] = v.z; qr[g][e + 3] = v.w;
+      for (int e = 0; e < DPC; e += 4) {
+        const float4 v = *(const float4 *)(qp + e);
+        qr[g][e] = v.x; qr[g][e + 1] = v.y; qr[g][e + 2] = v.z; qr[g][e + 3] = v.w;
+      }
     }
   }
   const size_t head_off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD;
@@ -418,11 +483,66 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
     const int j = p * PG + pg;
     kc[p] = *(const uint4 *)(kbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
   }
+
+  if constexpr (FUSED) {
+    const bool act = lane < HALF;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int it = wave + 4 * s, i = it - G;
+      const bool isq = it < G, isk = (i == 0 && need0) || (i == 1 && need1);
+      if (!isq && !isk) continue;  // wave-uniform
+      float o0, o1;
+      qk_norm_rope<HD>(act ? fx0[s] : 0.f, act ? fx1[s] : 0.f, fg0[s], fg1[s], fc[s], fs[s], a.eps, o0, o1);
+      if (!act) continue;
+      if (isq) {
+        qs[it][lane] = o0;
+        qs[it][lane + HALF] = o1;
+        continue;
+      }
+      const float v0 = fv0[s], v1 = fv1[s];
+      // the row in its storage format, as the ring holds it
+      if constexpr (KVB) {
+        uint16_t *kr = (uint16_t *)nrow[i][0], *vr = (uint16_t *)nrow[i][1];
+        kr[lane] = bf16_bits(o0); kr[lane + HALF] = bf16_bits(o1);
+        vr[lane] = bf16_bits(v0); vr[lane + HALF] = bf16_bits(v1);
+      } else {
+        float *kr = (float *)nrow[i][0], *vr = (float *)nrow[i][1];
+        kr[lane] = o0; kr[lane + HALF] = o1;
+        vr[lane] = v0; vr[lane + HALF] = v1;
+      }
+      if (rs0 + i == r) {
+        // set_rows: the row's own workgroup (its last tile) writes its K/V row
+        const size_t off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD + (size_t)pos * HD;
+        if constexpr (KVB) {
+          uint16_t *kr = (uint16_t *)a.ring_layer + off, *vr = kr + a.kv_stride;
+          kr[lane] = bf16_bits(o0); kr[lane + HALF] = bf16_bits(o1);
+          vr[lane] = bf16_bits(v0); vr[lane + HALF] = bf16_bits(v1);
+        } else {
+          float *kr = (float *)a.ring_layer + off, *vr = kr + a.kv_stride;
+          kr[lane] = o0; kr[lane + HALF] = o1;
+          vr[lane] = v0; vr[lane + HALF] = v1;
+        }
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < DPC; ++e) qr[g][e] = qs[g][cc * DPC + e];
+  }
+  // V rows, requested after the prologue (whose inputs are dead by now)
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int j = p * PG + pg;
     vc[p] = *(const uint4 *)(vbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
   }
+
+  // Rows of the step's new positions come from the workgroup, not from the
+  // ring: the loops below skip them, and they are added after each loop.  A
+  // new position is the last valid row of its lane group (at most two
+  // consecutive new positions, at least 8 rows per pass), so the sums keep
+  // their order.
+  auto is_new = [&](int j) { return FUSED && ((need0 && j0 + j == p0) || (need1 && j0 + j == p1)); };
 
   // scores
   {
@@ -438,9 +558,25 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < DPC; ++e) d += qr[g][e] * kf[e];
         d = group_sum<CPR>(d);
-        if (cc == 0 && j < jn) sc[g][j] = d * a.scale;
+        if (cc == 0 && j < jn && !is_new(j)) sc[g][j] = d * a.scale;
       }
     }
+    if constexpr (FUSED)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int jl = (i ? p1 : p0) - j0;
+        if (!(i ? need1 : need0) || pg != jl % PG) continue;  // uniform over the lane group
+        float kf[8];
+        kv_unpack<KVB>(((const uint4 *)nrow[i][0])[cc], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < DPC; ++e) d += qr[g][e] * kf[e];
+          d = group_sum<CPR>(d);
+          if (cc == 0) sc[g][jl] = d * a.scale;
+        }
+      }
   }
   __syncthreads();
   // softmax statistics: one wave per query head
@@ -469,7 +605,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
     for (int p = 0; p < NP; ++p) {
       if (p * PG >= jn) break;
       const int j = p * PG + pg;
-      if (j < jn) {
+      if (j < jn && !is_new(j)) {
         float vf[8];
         kv_unpack<KVB>(vc[p], vf);
 #pragma unroll
@@ -480,6 +616,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
         }
       }
     }
+    if constexpr (FUSED)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int jl = (i ? p1 : p0) - j0;
+        if (!(i ? need1 : need0) || pg != jl % PG) continue;
+        float vf[8];
+        kv_unpack<KVB>(((const uint4 *)nrow[i][1])[cc], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float e = sc[g][jl];
+#pragma unroll
+          for (int d = 0; d < DPC; ++d) acc[g][d] += e * vf[d];
+        }
+      }
     // row groups inside the wave (lanes cc, cc + CPR, ...), then across waves
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -557,8 +707,13 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
 template <int HD, int G>
 static void attn_tile_g(int kv_bf16, const AttnArgs &a, hipStream_t s) {
   const dim3 grid(a.M, a.nkv, a.max_tiles);
-  if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false>), grid, dim3(256), 0, s, a);
+  if (a.qkv) {
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false>), grid, dim3(256), 0, s, a);
+  }
 }
 
 template <int HD>
