@@ -1,0 +1,39 @@
+"""Per-kernel summary of one replay of a rocprofv3 kernel trace (the last
+replay before the last advance_kernel), split into predictor and talker
+stages.  Usage: python -m autoregressive_codebook_tts_frame_amd.trace_summary <rocprofv3 output dir>"""
+import collections
+import glob
+import sqlite3
+import sys
+
+
+def main(d: str) -> None:
+    db = glob.glob(d + "/**/*.db", recursive=True)[0]
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, start, end, grid_x, workgroup_x, grid_y, grid_z from kernels order by start").fetchall()
+    adv = [i for i, r in enumerate(rows) if "advance_kernel" in r[0]]
+    seg = rows[adv[-2] + 1:adv[-1] + 1]
+    frames = sum(1 for r in seg if "gather_kernel" in r[0])
+    stage, agg = "pred", collections.defaultdict(lambda: [0, 0.0])
+    for r in seg:
+        n = r[0]
+        if "pred_input" in n:
+            stage = "predictor"
+        if "gather_kernel" in n:
+            stage = "talker"
+        key = (stage, n.split("(")[0].replace("void ", ""), "%dx%dx%d" % (r[3] // r[4], r[5], r[6]))
+        agg[key][0] += 1
+        agg[key][1] += (r[2] - r[1]) / 1e3
+    print("| stage | kernel | grid | calls per frame-step | avg us | us per frame-step |")
+    print("|---|---|---|---:|---:|---:|")
+    tot = 0.0
+    for k, (n, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
+        tot += t
+        print("| %s | `%s` | %s | %g | %.2f | %.1f |" % (k[0], k[1], k[2], n / frames, t / n, t / frames))
+    span = (seg[-1][2] - seg[0][1]) / 1e3
+    print("\nKernels per replay: %d over %d frame-steps; kernel time %.1f us and span %.1f us per frame-step."
+          % (len(seg), frames, tot / frames, span / frames))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1])
