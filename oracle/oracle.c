@@ -7,7 +7,8 @@
  * header, table or constant generator with the HIP library; both sides only
  * receive the same seeded input arrays.
  *
- * What it computes: greedy decoding with two pre-norm decoder-only stacks.
+ * What it computes: greedy (or, with a temperature, sampled: see "sampling")
+ * decoding with two pre-norm decoder-only stacks.
  * Every technique the pages apply to this loop (K/V caching in a per-layer
  * ring, a window padded to 256 with a -inf tail, gather-sums assembled on the
  * device, fixed arenas, graph replay, batching) is an exact reorganisation of
@@ -148,6 +149,8 @@ typedef struct {
   float *bridge; /* [B][H] */
   float *rope_cos, *rope_sin; /* [max(Pcap,Q)][hd/2] */
   int32_t rope_rows;
+  float inv_temp; /* sampling: float(1/T), 0 = greedy */
+  uint64_t seed;
 } orc_sess;
 
 static double tab_get(const orc_model *m, const void *p, size_t i) {
@@ -230,6 +233,60 @@ static void rope(const orc_sess *s, float *v, int32_t p) {
 }
 
 static float kv_store(const orc_model *m, float v) { return m->kv_bf16 ? orc_bf16_round(v) : v; }
+
+/* ----------------------------------------------------------------------- */
+/* sampling                                                                 */
+/*
+ * The pages decode greedily and keep the sampler inside the graph
+ * (qwentts.cpp tests-branch log, "fused codec mode removed" entry), but they
+ * define no distribution, so this one is our own: temperature sampling by the
+ * Gumbel-max rule.  For a head's logits l and temperature T > 0 the code is
+ *     argmax_n ( l_n * (1/T) + g_n ),   the lowest index winning ties,
+ * with g_n = -log(-log(u_n)) standard Gumbel variates; the argmax of
+ * Gumbel-perturbed scores is a draw from softmax(l / T).  u_n is the first
+ * output word x of Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC'11) at counter (n, j, q, slot) and
+ * key (seed, 0), mapped to ((x >> 11) + 0.5) * 2^-53 in (0, 1).  j is the
+ * code's index in its frame (0 = the talker's code), q the frame's talker
+ * position (a talker head at position p decides frame q = p + 1; the
+ * predictor of the frame at position q decides codes 1..G-1), slot the
+ * stream.  1/T is rounded to float once; g is computed in double and rounded
+ * to float once; the product and the sum are float operations.  T = 0 is the
+ * greedy argmax.
+ */
+#define ORC_PHILOX_M0 0xD2E7470EE14C6C93ULL
+#define ORC_PHILOX_M1 0xCA5A826395121157ULL
+#define ORC_PHILOX_W0 0x9E3779B97F4A7C15ULL /* golden ratio */
+#define ORC_PHILOX_W1 0xBB67AE8584CAA73BULL /* sqrt(3) - 1 */
+
+/* Philox4x64 with 10 rounds: each round multiplies words 0 and 2 by the two
+   multipliers (128-bit products), crosses the high halves with words 1, 3 and
+   the round key, and the key advances by the Weyl constants between rounds. */
+void orc_prim_philox4x64(const uint64_t *ctr, const uint64_t *key, uint64_t *out) {
+  uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += ORC_PHILOX_W0; k1 += ORC_PHILOX_W1; }
+    const unsigned __int128 p0 = (unsigned __int128)ORC_PHILOX_M0 * c0;
+    const unsigned __int128 p1 = (unsigned __int128)ORC_PHILOX_M1 * c2;
+    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Gumbel variate of logit n of code j of frame q, stream slot */
+float orc_prim_gumbel(uint64_t seed, int32_t slot, int32_t q, int32_t j, int32_t n) {
+  const uint64_t ctr[4] = {(uint64_t)n, (uint64_t)j, (uint64_t)q, (uint64_t)slot};
+  const uint64_t key[2] = {seed, 0};
+  uint64_t x[4];
+  orc_prim_philox4x64(ctr, key, x);
+  const double u = ((double)(x[0] >> 11) + 0.5) * 0x1p-53;
+  return (float)(-log(-log(u)));
+}
 
 /* argmax over n logits; the lowest index wins ties. */
 static int32_t argmax(const float *x, int32_t n) {
@@ -474,11 +531,34 @@ static void gather_sum(const orc_sess *s, const int32_t *codes, int32_t text_id,
   }
 }
 
-/* talker final norm -> bridge, head -> logits, argmax -> code 0 */
-static int32_t talker_tail(const orc_sess *s, const float *x, float *bridge, float *logits) {
+/* The code a head's logits decide: greedy argmax, or with a temperature the
+   Gumbel-max draw of code j of frame q for stream slot (see "sampling"). */
+static int32_t choose(const orc_sess *s, const float *logits, int32_t n, int32_t slot, int32_t q, int32_t j) {
+  if (s->inv_temp == 0.f) return argmax(logits, n);
+  float best = -INFINITY;
+  int32_t bi = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const float scaled = logits[i] * s->inv_temp;
+    const float v = scaled + orc_prim_gumbel(s->seed, slot, q, j, i);
+    if (v > best) { best = v; bi = i; }
+  }
+  return bi;
+}
+
+/* talker final norm -> bridge, head -> logits, code 0 of frame q (the next one) */
+static int32_t talker_tail(const orc_sess *s, const float *x, float *bridge, float *logits, int32_t slot,
+                           int32_t q) {
   rmsnorm(&s->m, x, s->t_norm, s->m.H, bridge);
   mm(&s->m, &s->t_head, 1, bridge, s->m.H, logits, s->m.Vc);
-  return argmax(logits, s->m.Vc);
+  return choose(s, logits, s->m.Vc, slot, q, 0);
+}
+
+/* Sampling from now on: temperature T (0: greedy) and the Philox key seed. */
+int32_t orc_set_sampler(orc_sess *s, float temperature, uint64_t seed) {
+  if (!(temperature >= 0.f) || isinf(temperature)) return ORC_E_ARG;
+  s->inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
+  s->seed = seed;
+  return ORC_OK;
 }
 
 /*
@@ -514,7 +594,7 @@ int32_t orc_prefill(orc_sess *s, int32_t b, int32_t T, const int32_t *codes, con
     layer_fwd(s, &s->tl[l], T, x, rows);
   }
   float *logits = (float *)malloc(sizeof(float) * m->Vc);
-  s->c0[b] = talker_tail(s, x + (size_t)(T - 1) * m->H, s->bridge + (size_t)b * m->H, logits);
+  s->c0[b] = talker_tail(s, x + (size_t)(T - 1) * m->H, s->bridge + (size_t)b * m->H, logits, b, T);
   if (dump_logits) memcpy(dump_logits, logits, sizeof(float) * m->Vc);
   s->pos[b] = T;
   s->ready[b] = 1;
@@ -594,7 +674,7 @@ int32_t orc_decode(orc_sess *s, int32_t n, const int32_t *overlay, const int32_t
     for (int32_t b = 0; b < B; ++b) {
       rmsnorm(m, x + (size_t)(2 * b + 1) * H, s->p_norm, H, hn);
       mm(m, &s->p_heads[0], 1, hn, H, logits, Vc);
-      const int32_t c = argmax(logits, Vc);
+      const int32_t c = choose(s, logits, Vc, b, s->pos[b], 1);
       cf[(size_t)b * G + 1] = c;
       cin[(size_t)b * G + 1] = ff ? ff[(size_t)b * G + 1] : c;
       if (dump && dump->pred_logits)
@@ -618,7 +698,7 @@ int32_t orc_decode(orc_sess *s, int32_t n, const int32_t *overlay, const int32_t
       for (int32_t b = 0; b < B; ++b) {
         rmsnorm(m, x + (size_t)b * H, s->p_norm, H, hn);
         mm(m, &s->p_heads[j], 1, hn, H, logits, Vc);
-        const int32_t c = argmax(logits, Vc);
+        const int32_t c = choose(s, logits, Vc, b, s->pos[b], j + 1);
         cf[(size_t)b * G + j + 1] = c;
         cin[(size_t)b * G + j + 1] = ff ? ff[(size_t)b * G + j + 1] : c;
         if (dump && dump->pred_logits)
@@ -651,7 +731,7 @@ int32_t orc_decode(orc_sess *s, int32_t n, const int32_t *overlay, const int32_t
                  sizeof(float) * H);
     }
     for (int32_t b = 0; b < B; ++b) {
-      s->c0[b] = talker_tail(s, x + (size_t)b * H, s->bridge + (size_t)b * H, logits);
+      s->c0[b] = talker_tail(s, x + (size_t)b * H, s->bridge + (size_t)b * H, logits, b, s->pos[b] + 1);
       if (dump && dump->talker_logits)
         memcpy(dump->talker_logits + ((size_t)f * B + b) * Vc, logits, sizeof(float) * Vc);
       if (dump && dump->bridge)
@@ -760,6 +840,15 @@ void orc_prim_mm(const orc_model *m, const void *w, const uint16_t *d, int32_t N
 }
 
 int32_t orc_prim_argmax(const float *x, int32_t n) { return argmax(x, n); }
+
+/* The sampler's choice for one head's logits (temperature 0: greedy). */
+int32_t orc_prim_sample(const float *x, int32_t n, float temperature, uint64_t seed, int32_t slot, int32_t q,
+                        int32_t j) {
+  orc_sess s;
+  memset(&s, 0, sizeof(s));
+  if (orc_set_sampler(&s, temperature, seed) != ORC_OK) return ORC_E_ARG;
+  return choose(&s, x, n, slot, q, j);
+}
 
 int32_t orc_prim_talker_window(int32_t p) { return talker_window(p); }
 

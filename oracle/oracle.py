@@ -87,6 +87,13 @@ def load_library():
     lib.orc_num_threads.restype = i32
     lib.orc_predictor_recompute.argtypes = [vp, i32, vp, vp]
     lib.orc_predictor_recompute.restype = i32
+    lib.orc_set_sampler.argtypes = [vp, C.c_float, C.c_uint64]
+    lib.orc_set_sampler.restype = i32
+    lib.orc_prim_philox4x64.argtypes = [vp, vp, vp]
+    lib.orc_prim_gumbel.argtypes = [C.c_uint64, i32, i32, i32, i32]
+    lib.orc_prim_gumbel.restype = C.c_float
+    lib.orc_prim_sample.argtypes = [vp, i32, C.c_float, C.c_uint64, i32, i32, i32]
+    lib.orc_prim_sample.restype = i32
     _lib = lib
     return lib
 
@@ -234,5 +241,45 @@ class Oracle:
             raise RuntimeError(f"orc_predictor_recompute failed: {rc}")
         return lg
 
+    def set_sampler(self, temperature: float, seed: int = 0):
+        """Temperature sampling from now on (0: greedy); seed keys the Philox
+        counters of every draw."""
+        rc = self.lib.orc_set_sampler(self.h, float(temperature), int(seed))
+        if rc != 0:
+            raise ValueError(f"orc_set_sampler: {rc}")
+
     def poison_predictor(self, value: float = float("nan")):
         self.lib.orc_poison_predictor(self.h, value)
+
+
+def philox4x64(ctr, key) -> np.ndarray:
+    """Philox4x64-10 block at counter ctr[4], key key[2] (uint64)."""
+    lib = load_library()
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    lib.orc_prim_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def gumbel(seed: int, slot: int, q: int, j: int, n: int) -> np.float32:
+    """The Gumbel variate of logit n of code j of frame q of a stream."""
+    return np.float32(load_library().orc_prim_gumbel(int(seed), int(slot), int(q), int(j), int(n)))
+
+
+def sample_scores(logits: np.ndarray, temperature: float, seed: int, slot: int, q: int, j: int) -> np.ndarray:
+    """Float32 scores whose argmax (lowest index on ties) is the sampled code:
+    logits * float(1/T) + g, as the sampler computes them; greedy: the logits."""
+    lg = np.asarray(logits, dtype=np.float32)
+    if temperature == 0:
+        return lg.copy()
+    inv = np.float32(1.0 / float(np.float32(temperature)))
+    g = np.array([gumbel(seed, slot, q, j, n) for n in range(lg.shape[-1])], dtype=np.float32)
+    return (lg * inv).astype(np.float32) + g
+
+
+def sample(logits: np.ndarray, temperature: float, seed: int, slot: int, q: int, j: int) -> int:
+    """The oracle sampler's code for one head's logits (float32 [Vc])."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    return int(load_library().orc_prim_sample(_ptr(lg), lg.shape[0], float(temperature), int(seed),
+                                              int(slot), int(q), int(j)))
