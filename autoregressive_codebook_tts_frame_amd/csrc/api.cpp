@@ -178,6 +178,8 @@ struct qt_ctx {
   qtk::FrameArgs fa;       // persistent kernel arguments (path == QT_PATH_FRAME)
   int lds_limit = 0;       // LDS per workgroup on the device
   uint32_t tag_base = 1;   // running phase tag of the persistent kernel
+  float inv_temp = 0.f;    // sampling: float(1/T), 0 = greedy (sampler.h)
+  uint64_t seed = 0;
   std::string err;
 
   template <class T> T *A(size_t off) const { return (T *)(arena + off); }
@@ -407,6 +409,7 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
     if ((e = project(c, EPI_STORE, h, j == 0 ? ssq + ss : ssq, j == 0 ? 2 * ss : ss, nullptr)) != hipSuccess) return e;
     ArgmaxArgs am = {};
     am.logits = lg; am.Vc = d.Vc; am.M = B; am.mode = AM_PRED; am.j = j; am.ctl = ctl; am.k = k;
+    am.pos = c->A<int32_t>(c->L.pos);
     am.B = B; am.G = d.G; am.cin = pa.cin; am.cout = pa.cout; am.code_emb = c->code_emb;
     am.tab_bf16 = md.tab_bf16; am.H = d.H; am.x_next = x; am.ssq = ssq;
     if ((e = launch_argmax(am, s)) != hipSuccess) return e;
@@ -477,6 +480,15 @@ extern "C" {
 int32_t qt_abi_version(void) { return QT_ABI_VERSION; }
 
 int32_t qt_path(const qt_ctx *ctx) { return ctx ? ctx->path : QT_E_ARG; }
+
+int32_t qt_set_sampler(qt_ctx *c, float temperature, uint64_t seed) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  if (!(temperature >= 0.f) || isinf(temperature))
+    return fail(c, QT_E_ARG, "temperature must be finite and >= 0");
+  c->inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
+  c->seed = seed;
+  return QT_OK;
+}
 
 const char *qt_last_error(const qt_ctx *ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
 
@@ -724,6 +736,7 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
       ArgmaxArgs am = {};
       am.logits = h.y; am.Vc = d.Vc; am.M = 1; am.mode = AM_PREFILL; am.slot = slot;
       am.c0_state = c->A<int32_t>(c->L.c0);
+      am.inv_temp = c->inv_temp; am.seed = c->seed; am.q_prefill = T;
       HIPCHK(c, launch_argmax(am, s));
     }
   }
@@ -760,6 +773,9 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
     memset(up, 0, 16 * sizeof(int32_t));
     up[0] = 0;                 // frame index base
     up[1] = forced ? 1 : 0;    // teacher forcing
+    memcpy(&up[2], &c->inv_temp, sizeof(float));  // sampler (argmax_kernel)
+    up[3] = (int32_t)(uint32_t)c->seed;
+    up[4] = (int32_t)(uint32_t)(c->seed >> 32);
     int32_t *ov = c->pin_up + c->pu_overlay;
     memcpy(ov, overlay_ids + (size_t)f0 * B, sizeof(int32_t) * nf * B);
     HIPCHK(c, hipMemcpyAsync(ctl, up, 16 * sizeof(int32_t), hipMemcpyHostToDevice, s));
@@ -780,6 +796,8 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
       if (!qtk::frame_plan(fa, fa.pos0 + nf - 1, c->lds_limit, &why))
         return fail(c, QT_E_UNSUPPORTED, "frame kernel plan: %s", why);
       fa.tag_base = c->tag_base;
+      fa.inv_temp = c->inv_temp;
+      fa.seed = c->seed;
       // tags are only ever compared for equality: advance past every phase
       // this launch can number (< 1024 per frame)
       c->tag_base += (uint32_t)nf * 1024u + 16u;

@@ -71,6 +71,8 @@ struct FrameArgs {
   uint32_t tag_base;  // tags of this launch are tag_base + phase index (> 0)
   int32_t *err;       // [0] set on a timed-out wait
   uint64_t *trace;    // optional: [1024][8] stamps (rows < 768: first GEMV workgroup; rest: attention workgroup 0)
+  float inv_temp;     // sampling (sampler.h): float(1/T), 0 = greedy
+  uint64_t seed;
 };
 
 hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s);

@@ -35,6 +35,7 @@
 
 #include "frame.h"
 #include "kernels.h"
+#include "sampler.h"
 
 namespace qtk {
 namespace {
@@ -806,7 +807,9 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
   }
 }
 
-template <int WT>
+// SMP: the heads' codes are sampled (sampler.h), else greedy; a compile-time
+// switch, so the greedy kernel carries no sampling code.
+template <int WT, bool SMP>
 __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *smem) {
   constexpr int ESZ = WEsz<WT>::v;
   Common &cm = *reinterpret_cast<Common *>(smem);
@@ -1024,10 +1027,15 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
+      // sampling key: a talker head decides the next frame's code 0, head
+      // j of the predictor code j + 1 of this frame (stream slot 0)
+      const int sq = cur.stack ? pos + 1 : pos, sj = cur.stack ? 0 : cur.step + 1;
+      (void)sq; (void)sj;
       gemv_items<WT, 1, NBH>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2], float) {
         const int n = s.r0 + it;
         if (lane == 0) st(lg + n, acc[0][0]);
-        pick(bv, bi, acc[0][0], n);
+        if constexpr (SMP) pick(bv, bi, sample_score(acc[0][0], a.inv_temp, a.seed, 0, sq, sj, n), n);
+        else pick(bv, bi, acc[0][0], n);
       });
       if (lane == 0) { cm.amv[wave] = bv; cm.ami[wave] = bi; }
       if (!cbar(a, cm, gen)) return;
@@ -1445,7 +1453,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
 
 // ------------------------------------------------------------ the kernel
 
-template <int WT, int HD, int GQ, bool KVB>
+template <int WT, int HD, int GQ, bool KVB, bool SMP>
 __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   Common &cm = *reinterpret_cast<Common *>(smem);
@@ -1472,7 +1480,7 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
   if ((int)blockIdx.x < a.n_attn) {
     if (tid < ANT) attn_role<HD, GQ, KVB>(a, smem);  // the other waves end here
   } else {
-    gemv_role<WT>(a, smem);
+    gemv_role<WT, SMP>(a, smem);
   }
 }
 
@@ -1539,16 +1547,19 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
 
 hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s) {
   const int g = a.nq / a.nkv;
-#define X(W, HD_, G_, K_)                                                                         \
-  if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_) {                          \
-    hipError_t e = hipFuncSetAttribute((const void *)frame_kernel<W, HD_, G_, K_>,                \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes); \
-    if (e != hipSuccess) return e;                                                               \
-    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_>), dim3(a.nwg), dim3(NTB), a.lds_bytes, s, a); \
-    return hipGetLastError();                                                                    \
+  const bool smp = a.inv_temp != 0.f;
+#define X1(W, HD_, G_, K_, S_)                                                                       \
+  if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_ && smp == S_) {                \
+    hipError_t e = hipFuncSetAttribute((const void *)frame_kernel<W, HD_, G_, K_, S_>,               \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);    \
+    if (e != hipSuccess) return e;                                                                  \
+    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_, S_>), dim3(a.nwg), dim3(NTB), a.lds_bytes, s, a); \
+    return hipGetLastError();                                                                       \
   }
+#define X(W, HD_, G_, K_) X1(W, HD_, G_, K_, false) X1(W, HD_, G_, K_, true)
   QT_FRAME_VARIANTS(X)
 #undef X
+#undef X1
   return hipErrorInvalidValue;
 }
 

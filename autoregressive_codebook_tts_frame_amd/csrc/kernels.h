@@ -127,6 +127,12 @@ struct ArgmaxArgs {
   float *x_next;  // AM_PRED: row b <- E_{j+1}[code] when j+1 < G-1
   float *ssq;     // optional: x_next row sums of squares in 32-column slots [M][H/32]
   int32_t slot;   // AM_PREFILL
+  // Sampling (sampler.h).  AM_PRED / AM_TALKER read it from the per-call
+  // control words: ctl[2] = float bits of 1/T (0: greedy), ctl[3], ctl[4] =
+  // seed low, high.  AM_PREFILL takes it here, with q = the prompt length.
+  float inv_temp;
+  uint64_t seed;
+  int32_t q_prefill;
 };
 
 // Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 64 rows,

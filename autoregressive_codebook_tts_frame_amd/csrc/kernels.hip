@@ -10,6 +10,7 @@
 //   [QT-log] qwentts.cpp, commit log of src/pipeline-tts.h
 //   [MC-opt] MiniCPM-o 4.5 single-GPU engine, docs/optimizations.md
 #include "kernels.h"
+#include "sampler.h"
 
 #include <math.h>
 #include <type_traits>
@@ -1164,6 +1165,18 @@ hipError_t launch_pred_input(const PredInArgs &a, hipStream_t s) {
 __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *lg = a.logits + (size_t)r * a.Vc;
+  // The code's sampling key: stream, frame position, index in the frame
+  float inv_temp = a.inv_temp;
+  uint64_t seed = a.seed;
+  int slot = a.slot, q = a.q_prefill, jc = 0;
+  if (a.mode != AM_PREFILL) {
+    inv_temp = __int_as_float(a.ctl[2]);
+    seed = (uint64_t)(uint32_t)a.ctl[3] | ((uint64_t)(uint32_t)a.ctl[4] << 32);
+    slot = r;
+    q = a.mode == AM_PRED ? a.pos[r] : a.pos[r] + 1;
+    jc = a.mode == AM_PRED ? a.j + 1 : 0;
+  }
+  const bool sampled = inv_temp != 0.f;
   // Eight logits per thread in flight at a time (a plain loop waits on each
   // load); the first group is outside any loop.
   float best = -INFINITY;
@@ -1175,7 +1188,8 @@ __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * 256 + tid;
-      if (i < a.Vc && v[u] > best) { best = v[u]; bi = i; }  // increasing i: first max kept
+      const float s = sampled ? sample_score(v[u], inv_temp, seed, slot, q, jc, i) : v[u];
+      if (i < a.Vc && s > best) { best = s; bi = i; }  // increasing i: first max kept
     }
   };
   scan(0);

@@ -1,6 +1,11 @@
-"""Per-kernel summary of one replay of a rocprofv3 kernel trace (the last
-replay before the last advance_kernel), split into predictor and talker
-stages.  Usage: python -m autoregressive_codebook_tts_frame_amd.trace_summary <rocprofv3 output dir>"""
+"""Per-kernel summaries of a rocprofv3 kernel trace.
+
+    python -m autoregressive_codebook_tts_frame_amd.trace_summary DIR          one replay of the per-op graph
+    python -m autoregressive_codebook_tts_frame_amd.trace_summary --stats DIR  every kernel of the trace
+
+The replay summary takes the last replay before the last advance_kernel and
+splits it into predictor and talker stages; --stats lists calls, total and
+average duration and share per kernel over the whole trace."""
 import collections
 import glob
 import sqlite3
@@ -35,5 +40,22 @@ def main(d: str) -> None:
           % (len(seg), frames, tot / frames, span / frames))
 
 
+def stats(d: str) -> None:
+    db = glob.glob(d + "/**/*.db", recursive=True)[0]
+    c = sqlite3.connect(db)
+    agg = collections.defaultdict(lambda: [0, 0.0])
+    for name, start, end in c.execute("select name, start, end from kernels"):
+        agg[name][0] += 1
+        agg[name][1] += (end - start) / 1e3
+    tot = sum(t for _, t in agg.values())
+    print("| kernel | calls | total (us) | average (us) | % |")
+    print("|---|---:|---:|---:|---:|")
+    for k, (n, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
+        print("| `%s` | %d | %.1f | %.1f | %.2f |" % (k[:110], n, t, t / n, 100 * t / tot))
+
+
 if __name__ == "__main__":
-    main(sys.argv[1])
+    if sys.argv[1] == "--stats":
+        stats(sys.argv[2])
+    else:
+        main(sys.argv[1])

@@ -72,13 +72,15 @@ def frame_bytes(m, batch: int, mean_len: float) -> float:
     return weights + kv_read + kv_write + gathers
 
 
-def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0):
+def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0, temperature: float = 0.0, seed: int = 0):
     """The oracle as it stands, on the host cores: prefill (untimed) then as
     many frames as fit in the budget (at least 1)."""
     from autoregressive_codebook_tts_frame_amd import synth
     from oracle import Oracle
 
     o = Oracle(m, w, 1, pcap=wl.prompt + 64 + 1)
+    if temperature:
+        o.set_sampler(temperature, seed)
     codes, text = synth.make_prompt(wl, 0)
     t = time.time()
     o.prefill(0, codes, text)
@@ -107,6 +109,9 @@ def main():
     ap.add_argument("--frames", type=int, default=None, help="frames per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", action="store_true", help="force the per-op hipGraph path")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="sample every code at this temperature (0: greedy, the default)")
+    ap.add_argument("--seed", type=int, default=42, help="sampler seed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device three times (a plain copy kernel "
                          "of known size, to scale hardware byte counters against)")
@@ -132,6 +137,8 @@ def main():
     log(f"weights drawn in {time.time() - t:.1f}s; uploading")
     d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf,
                    flags=qt.QT_F_OPS if args.ops else 0)
+    if args.temperature:
+        d.set_sampler(args.temperature, args.seed)
     lens = []
     ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
     for b in range(B):
@@ -201,7 +208,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "prompt": wl.prompt, "frames_per_step": nf,
                    "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[d.path],
                    "frames_per_replay": wl.frames_per_replay, "talker_layers": m.Lt,
-                   "predictor_layers": m.Lp, "hidden": m.H},
+                   "predictor_layers": m.Lp, "hidden": m.H,
+                   "sampler": f"temperature {args.temperature}, seed {args.seed}" if args.temperature else "greedy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name, nf) if d.path == qt.QT_PATH_FRAME else None,
@@ -225,7 +233,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(m, w, wl)
+        res["cpu_baseline"] = cpu_baseline(m, w, wl, temperature=args.temperature, seed=args.seed)
     print(json.dumps(res), flush=True)
 
 

@@ -2,7 +2,7 @@
  * qt.h -- C ABI of the MI355X (gfx950) per-frame decode library.
  *
  * One codec frame = one talker step + 15 code-predictor micro-steps, decoded
- * greedily on one GPU.  All compute runs in the library's HIP kernels; the
+ * greedily (or by temperature sampling, qt_set_sampler) on one GPU.  All compute runs in the library's HIP kernels; the
  * caller supplies device memory (weights, the K/V ring, a scratch arena) and a
  * HIP stream, typically from PyTorch.  No entry point allocates device memory.
  *
@@ -36,7 +36,7 @@ extern "C" {
    [QT_ABI_MIN_VERSION, QT_ABI_VERSION] is accepted; both bounds are checked
    ([QT-tests], codec left context / ABI range entry). */
 #define QT_ABI_MIN_VERSION 1
-#define QT_ABI_VERSION 1
+#define QT_ABI_VERSION 2 /* 2: qt_set_sampler */
 
 #define QT_OK 0
 #define QT_E_ABI (-1)          /* abi_version outside the closed range (checked first) */
@@ -176,6 +176,7 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
    the argmax results (codes_out still receives every argmax).  Synchronous:
    codes are in codes_out on return.  Only ids cross the host boundary per
    frame ([QT-log] set_rows / hot-loop entry).
+   With a sampler set (qt_set_sampler) codes_out holds the sampled codes.
    Errors: QT_E_ARG (n_frames % K, NULLs), QT_E_RANGE, QT_E_STATE (a slot not
    prefilled), QT_E_CONTEXT_FULL (pos + n_frames > P; checked before any
    launch), QT_E_HIP. */
@@ -235,6 +236,22 @@ int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
 #define QT_KERNEL_GEMV_GATE_UP 1
 int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us,
                        double *bytes_per_launch);
+
+/* Sampler of every later qt_prefill / qt_decode_frame call of ctx (the pages
+   keep the sampler inside the decode graph: [QT-tests] fused codec mode removed
+   entry; the distribution is this library's definition).  temperature 0 (the
+   default) is the greedy argmax.  temperature T > 0: each code is
+   argmax_n (l_n * (1/T) + g_n), lowest index on ties, over its head's f32
+   logits l; 1/T is rounded to float once, the product and sum are float
+   operations, g_n = -log(-log(u_n)) (double, rounded to float once) with
+   u_n = ((x >> 11) + 0.5) * 2^-53 and x the first word of Philox4x64-10
+   (Salmon et al., SC'11) at counter (n, j, q, slot), key (seed, 0); j is the
+   code's index in its frame (0: the talker's), q the frame's talker position
+   (a talker head at position p decides frame p + 1; qt_prefill of T rows
+   decides frame T), slot the stream.  This draws each code from
+   softmax(l / T).  Host only: no GPU call, no graph recapture.
+   Errors: QT_E_ARG (NULL ctx, temperature negative, NaN or infinite). */
+int32_t qt_set_sampler(qt_ctx *ctx, float temperature, uint64_t seed);
 
 /* Decode path of a context: QT_PATH_FRAME (persistent frame kernel),
    QT_PATH_GRAPH (per-op kernels replayed as a hipGraph) or QT_PATH_EAGER. */

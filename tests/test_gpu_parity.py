@@ -21,6 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 from autoregressive_codebook_tts_frame_amd import qt  # noqa: E402
 from oracle import Oracle  # noqa: E402
+from oracle.oracle import sample_scores  # noqa: E402
 
 
 def say(*a):
@@ -28,19 +29,24 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None):
+def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None, sampler=None, flags=0):
     """Oracle free run, then the GPU teacher-forced with the oracle's codes
-    (one frame per call, dumps read after each) and free-running."""
+    (one frame per call, dumps read after each) and free-running.
+    sampler: (temperature, seed) set on both sides before the prefill."""
     prompts = prompts or [synth.make_prompt(wl, b) for b in range(batch)]
     ov = synth.make_overlays(wl, nframes, batch)
     o = Oracle(m, w, batch, pcap=max(len(p[1]) for p in prompts) + nframes + 1)
+    if sampler:
+        o.set_sampler(*sampler)
     pre_logits = []
     for b, (c, t) in enumerate(prompts):
         pre_logits.append(o.prefill(b, c, t, dump=True)["logits"])
     ostate = [o.get_state(b) for b in range(batch)]
     oout = o.decode(nframes, ov, dump=True, hidden=dump_hidden)
 
-    d = qt.Decoder(m, w, batch, flags=qt.QT_F_DUMP)
+    d = qt.Decoder(m, w, batch, flags=qt.QT_F_DUMP | flags)
+    if sampler:
+        d.set_sampler(*sampler)
     for b, (c, t) in enumerate(prompts):
         d.prefill(b, c, t)
     gstate = [d.get_state(b) for b in range(batch)]
@@ -58,7 +64,8 @@ def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None):
             g["hidden"].append(d.dump(qt.QT_DUMP_HIDDEN).transpose(1, 0, 2))
     g = {k: np.stack(v) for k, v in g.items() if v}
     return dict(o=o, d=d, ov=ov, prompts=prompts, pre_logits=pre_logits, ostate=ostate,
-                oout=oout, gstate=gstate, gpre=gpre, g=g)
+                oout=oout, gstate=gstate, gpre=gpre, g=g, sampler=sampler, flags=flags,
+                q0=[len(t) for _, t in prompts])
 
 
 def _oracle_from_states(m, w, states, lengths, pcap):
@@ -169,15 +176,23 @@ def _check(r, m, label, free_run=True):
 
     # (code 0 of the first frame comes from the prefill, or is the injected
     # state's on both sides)
+    # the values a decision maximises: the logits, or under a sampler the
+    # scores logits * (1/T) + Gumbel noise of the code's key
+    def scores(lg, f, b, j):
+        if not r.get("sampler"):
+            return lg
+        temp, seed = r["sampler"]
+        return sample_scores(lg, temp, seed, b, r["q0"][b] + f, j)
+
     def ref_logits(f, b, j):
         if j == 0:
-            return r["pre_logits"][b] if f == 0 else oout["talker_logits"][f - 1, b]
-        return oout["pred_logits"][f, b, j - 1]
+            return scores(r["pre_logits"][b] if f == 0 else oout["talker_logits"][f - 1, b], f, b, j)
+        return scores(oout["pred_logits"][f, b, j - 1], f, b, j)
 
     def gpu_logits(f, b, j):
         if j == 0:
-            return r["gpre"][b] if f == 0 else g["talker_logits"][f - 1, b]
-        return g["pred_logits"][f, b, j - 1]
+            return scores(r["gpre"][b] if f == 0 else g["talker_logits"][f - 1, b], f, b, j)
+        return scores(g["pred_logits"][f, b, j - 1], f, b, j)
 
     bad = code_mismatches(g["codes"], oout["codes"], ref_logits, gpu_logits)
     say(f"[{label}] teacher-forced decisions differing: {len(bad)} of {g['codes'].size}")
@@ -187,7 +202,9 @@ def _check(r, m, label, free_run=True):
         if "fresh" in r:
             d2 = r["fresh"](0)
         else:
-            d2 = qt.Decoder(m, r["d"].dw, B)
+            d2 = qt.Decoder(m, r["d"].dw, B, flags=r.get("flags", 0))
+            if r.get("sampler"):
+                d2.set_sampler(*r["sampler"])
             for b, (c, t) in enumerate(r["prompts"]):
                 d2.prefill(b, c, t)
         n = oout["codes"].shape[0]
@@ -326,6 +343,48 @@ def test_tiny_errors_leave_state_unchanged(tiny):
     assert np.array_equal(d.decode(8, r["ov"]), r["oout"]["codes"])
 
 
+# ----------------------------------------------------------------- sampling
+
+
+@pytest.mark.parametrize("flags", [0, qt.QT_F_OPS])
+def test_tiny_sampled_parity(tiny, flags):
+    # temperature sampling in the persistent kernel and the per-op graph: F32
+    # codes equal the oracle's free-running, teacher-forced values in tolerance
+    m, w, wl, r = tiny
+    say(f"[tiny sampled] flags {flags}, 8 frames, T = 1.0")
+    rs = _forced_run(m, w, wl, 8, sampler=(1.0, 77), flags=flags)
+    assert rs["d"].path == (qt.QT_PATH_GRAPH if flags else qt.QT_PATH_FRAME)
+    _check(rs, m, "tiny_sampled")
+    assert np.array_equal(rs["g"]["codes"], rs["oout"]["codes"])
+    # sampling at T = 1 on these logits is not the greedy decode
+    assert np.mean(rs["oout"]["codes"] != r["oout"]["codes"]) > 0.5
+
+
+def test_tiny_sampled_batched_keys_by_slot(tiny):
+    m, w, wl, r = tiny
+    wl3 = dataclasses.replace(wl, batch=3)
+    prompts = [synth.make_prompt(wl3, 0, T=12)] * 3  # one prompt in every slot
+    ov = np.repeat(synth.make_overlays(wl3, 4)[:, :1], 3, axis=1)
+    d = qt.Decoder(m, r["d"].dw, 3)
+    d.set_sampler(0.7, 5)
+    for b, (c, t) in enumerate(prompts):
+        d.prefill(b, c, t)
+    cb = d.decode(4, ov)
+    o = Oracle(m, w, 3)
+    o.set_sampler(0.7, 5)
+    for b, (c, t) in enumerate(prompts):
+        o.prefill(b, c, t)
+    assert np.array_equal(o.decode(4, ov)["codes"], cb)
+    # identical inputs, different slots: different draws
+    assert not np.array_equal(cb[:, 0], cb[:, 1])
+    with pytest.raises(qt.QtError) as e:
+        d.set_sampler(-1.0, 0)
+    assert e.value.code == qt.QT_E_ARG
+    with pytest.raises(qt.QtError) as e:
+        d.set_sampler(float("nan"), 0)
+    assert e.value.code == qt.QT_E_ARG
+
+
 # ----------------------------------------------------------------- BF16 / Q8
 
 
@@ -340,6 +399,16 @@ def test_reduced_bf16_full_width_parity():
     wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=300)
     say("[reduced bf16] prompt 300, 6 frames")
     _check(_forced_run(m, w, wl, 6, dump_hidden=True), m, "reduced_bf16")
+
+
+def test_reduced_bf16_sampled_parity():
+    # full widths, one stream (persistent kernel) and eight (MFMA GEMM path)
+    m = _reduced(synth.BIG)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
+    for batch in (1, 8):
+        say(f"[reduced bf16 sampled] 4 frames, batch {batch}, T = 0.8")
+        _check(_forced_run(m, w, wl, 4, batch=batch, sampler=(0.8, 2024)), m, f"reduced_bf16_sampled_b{batch}")
 
 
 def test_reduced_q8_random_scales_parity():
@@ -376,6 +445,17 @@ def test_full_bf16_b1_parity():
     w = synth.make_weights(m)
     say("[bf16_b1] prefill 128 + 6 frames")
     _check(_forced_run(m, w, wl, 6), m, "bf16_b1")
+
+
+@pytest.mark.timeout(900)
+def test_full_bf16_b1_sampled_parity():
+    m = synth.BIG
+    wl = synth.WORKLOADS["bf16_b1"]
+    w = synth.make_weights(m)
+    say("[bf16_b1 sampled] prefill 128 + 4 frames, T = 0.9")
+    r = _forced_run(m, w, wl, 4, sampler=(0.9, 99))
+    assert r["d"].path == qt.QT_PATH_FRAME
+    _check(r, m, "bf16_b1_sampled")
 
 
 @pytest.mark.timeout(900)
