@@ -374,15 +374,6 @@ __device__ __forceinline__ float group_sum<16>(float v) {  // one DPP row
   return v;
 }
 
-// Workgroup barrier for data in LDS only: each wave's LDS operations are
-// complete, while its global loads and stores stay in flight (the fence of
-// __syncthreads also covers global memory, so it would wait for all of them).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // 16-byte K/V chunk -> floats
 template <bool KVB>
 __device__ __forceinline__ void kv_unpack(uint4 w, float *v) {
@@ -525,7 +516,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
         }
       }
     }
-    lds_barrier();
+    __syncthreads();  // K/V loads stay in flight: the barrier waits for LDS operations only
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
