@@ -22,7 +22,7 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kPrefillChunk = 32;  // prompt rows per prefill step
+constexpr int kPrefillChunk = 64;  // prompt rows per prefill step (the batched GEMM takes up to 64)
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)

@@ -395,7 +395,7 @@ def _reduced(base, **kw):
 def test_reduced_bf16_full_width_parity():
     m = _reduced(synth.BIG)
     w = synth.make_weights(m)
-    # a 300-row prompt: 10 prefill chunks with a ragged tail, 2 attention tiles
+    # a 300-row prompt: 5 prefill chunks with a ragged tail, 2 attention tiles
     wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=300)
     say("[reduced bf16] prompt 300, 6 frames")
     _check(_forced_run(m, w, wl, 6, dump_hidden=True), m, "reduced_bf16")
