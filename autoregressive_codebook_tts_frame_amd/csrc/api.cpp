@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -342,9 +343,13 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   aa.q = q; aa.M = M; aa.rows = rows; aa.nq = d.nq; aa.nkv = d.nkv;
   aa.ring_layer = ring_layer; aa.slot_stride = st.slot_stride; aa.kv_stride = st.kv_stride;
   aa.P = st.P; aa.tile = st.tile; aa.max_tiles = st.max_tiles;
+  // rows with host-known positions (prefill chunks, the predictor) launch only
+  // the tiles up to their last position, and skip the merge when that is one
+  aa.grid_tiles = rows.pos_dev ? st.max_tiles
+                               : std::min(st.max_tiles, (rows.pos_base + rows.rows_per_slot - 1) / st.tile + 1);
   aa.scale = (float)(1.0 / sqrt((double)d.hd));
   aa.o = o; aa.part = c->A<float>(c->L.part);
-  if ((e = launch_attention(d.hd, md.kv_bf16, aa, st.max_tiles > 1, s)) != hipSuccess) return e;
+  if ((e = launch_attention(d.hd, md.kv_bf16, aa, aa.grid_tiles > 1, s)) != hipSuccess) return e;
 
   // 4. O projection, residual added in the epilogue
   GemvArgs go = g;

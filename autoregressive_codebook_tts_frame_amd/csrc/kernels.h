@@ -69,7 +69,8 @@ struct AttnArgs {
   int64_t slot_stride, kv_stride;
   int32_t P;
   int32_t tile;       // positions per tile (fixed absolute boundaries)
-  int32_t max_tiles;  // grid z
+  int32_t max_tiles;  // tiles per row in the partial buffer
+  int32_t grid_tiles; // grid z: tiles launched (rows' positions known to stay below grid_tiles * tile), or 0: max_tiles
   float scale;
   float *o;           // [M][nq hd]
   float *part;        // [M][nq][max_tiles][hd + 2]

@@ -698,7 +698,7 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
 
 template <int HD, int G>
 static void attn_tile_g(int kv_bf16, const AttnArgs &a, hipStream_t s) {
-  const dim3 grid(a.M, a.nkv, a.max_tiles);
+  const dim3 grid(a.M, a.nkv, a.grid_tiles > 0 ? a.grid_tiles : a.max_tiles);
   if (a.qkv) {
     if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, true>), grid, dim3(256), 0, s, a);
