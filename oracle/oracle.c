@@ -150,6 +150,7 @@ typedef struct {
   float *rope_cos, *rope_sin; /* [max(Pcap,Q)][hd/2] */
   int32_t rope_rows;
   float inv_temp; /* sampling: float(1/T), 0 = greedy */
+  int32_t top_k;  /* sampling: only the top_k largest logits compete (0: all) */
   uint64_t seed;
 } orc_sess;
 
@@ -252,7 +253,9 @@ static float kv_store(const orc_model *m, float v) { return m->kv_bf16 ? orc_bf1
  * predictor of the frame at position q decides codes 1..G-1), slot the
  * stream.  1/T is rounded to float once; g is computed in double and rounded
  * to float once; the product and the sum are float operations.  T = 0 is the
- * greedy argmax.
+ * greedy argmax.  With top_k = k > 0 only the k largest logits compete (the
+ * draw is from softmax(l / T) restricted to them); among equal logits at the
+ * boundary the lower indices are the larger, as in the argmax.
  */
 #define ORC_PHILOX_M0 0xD2E7470EE14C6C93ULL
 #define ORC_PHILOX_M1 0xCA5A826395121157ULL
@@ -533,11 +536,22 @@ static void gather_sum(const orc_sess *s, const int32_t *codes, int32_t text_id,
 
 /* The code a head's logits decide: greedy argmax, or with a temperature the
    Gumbel-max draw of code j of frame q for stream slot (see "sampling"). */
+/* logit a ranks above logit b: larger value, or equal value and lower index */
+static int ranks_above(const float *x, int32_t a, int32_t b) {
+  return x[a] > x[b] || (x[a] == x[b] && a < b);
+}
+
 static int32_t choose(const orc_sess *s, const float *logits, int32_t n, int32_t slot, int32_t q, int32_t j) {
   if (s->inv_temp == 0.f) return argmax(logits, n);
   float best = -INFINITY;
   int32_t bi = 0;
   for (int32_t i = 0; i < n; ++i) {
+    if (s->top_k > 0 && s->top_k < n) {
+      /* member of the top k: fewer than k logits rank above it */
+      int32_t above = 0;
+      for (int32_t t = 0; t < n && above < s->top_k; ++t) above += ranks_above(logits, t, i);
+      if (above >= s->top_k) continue;
+    }
     const float scaled = logits[i] * s->inv_temp;
     const float v = scaled + orc_prim_gumbel(s->seed, slot, q, j, i);
     if (v > best) { best = v; bi = i; }
@@ -553,10 +567,12 @@ static int32_t talker_tail(const orc_sess *s, const float *x, float *bridge, flo
   return choose(s, logits, s->m.Vc, slot, q, 0);
 }
 
-/* Sampling from now on: temperature T (0: greedy) and the Philox key seed. */
-int32_t orc_set_sampler(orc_sess *s, float temperature, uint64_t seed) {
-  if (!(temperature >= 0.f) || isinf(temperature)) return ORC_E_ARG;
+/* Sampling from now on: temperature T (0: greedy), top_k (0: every logit)
+   and the Philox key seed. */
+int32_t orc_set_sampler(orc_sess *s, float temperature, int32_t top_k, uint64_t seed) {
+  if (!(temperature >= 0.f) || isinf(temperature) || top_k < 0) return ORC_E_ARG;
   s->inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
+  s->top_k = top_k;
   s->seed = seed;
   return ORC_OK;
 }
@@ -842,11 +858,11 @@ void orc_prim_mm(const orc_model *m, const void *w, const uint16_t *d, int32_t N
 int32_t orc_prim_argmax(const float *x, int32_t n) { return argmax(x, n); }
 
 /* The sampler's choice for one head's logits (temperature 0: greedy). */
-int32_t orc_prim_sample(const float *x, int32_t n, float temperature, uint64_t seed, int32_t slot, int32_t q,
-                        int32_t j) {
+int32_t orc_prim_sample(const float *x, int32_t n, float temperature, int32_t top_k, uint64_t seed, int32_t slot,
+                        int32_t q, int32_t j) {
   orc_sess s;
   memset(&s, 0, sizeof(s));
-  if (orc_set_sampler(&s, temperature, seed) != ORC_OK) return ORC_E_ARG;
+  if (orc_set_sampler(&s, temperature, top_k, seed) != ORC_OK) return ORC_E_ARG;
   return choose(&s, x, n, slot, q, j);
 }
 

@@ -87,12 +87,12 @@ def load_library():
     lib.orc_num_threads.restype = i32
     lib.orc_predictor_recompute.argtypes = [vp, i32, vp, vp]
     lib.orc_predictor_recompute.restype = i32
-    lib.orc_set_sampler.argtypes = [vp, C.c_float, C.c_uint64]
+    lib.orc_set_sampler.argtypes = [vp, C.c_float, i32, C.c_uint64]
     lib.orc_set_sampler.restype = i32
     lib.orc_prim_philox4x64.argtypes = [vp, vp, vp]
     lib.orc_prim_gumbel.argtypes = [C.c_uint64, i32, i32, i32, i32]
     lib.orc_prim_gumbel.restype = C.c_float
-    lib.orc_prim_sample.argtypes = [vp, i32, C.c_float, C.c_uint64, i32, i32, i32]
+    lib.orc_prim_sample.argtypes = [vp, i32, C.c_float, i32, C.c_uint64, i32, i32, i32]
     lib.orc_prim_sample.restype = i32
     _lib = lib
     return lib
@@ -241,10 +241,10 @@ class Oracle:
             raise RuntimeError(f"orc_predictor_recompute failed: {rc}")
         return lg
 
-    def set_sampler(self, temperature: float, seed: int = 0):
-        """Temperature sampling from now on (0: greedy); seed keys the Philox
-        counters of every draw."""
-        rc = self.lib.orc_set_sampler(self.h, float(temperature), int(seed))
+    def set_sampler(self, temperature: float, seed: int = 0, top_k: int = 0):
+        """Temperature sampling from now on (0: greedy), among the top_k
+        largest logits (0: all); seed keys the Philox counters of every draw."""
+        rc = self.lib.orc_set_sampler(self.h, float(temperature), int(top_k), int(seed))
         if rc != 0:
             raise ValueError(f"orc_set_sampler: {rc}")
 
@@ -267,19 +267,27 @@ def gumbel(seed: int, slot: int, q: int, j: int, n: int) -> np.float32:
     return np.float32(load_library().orc_prim_gumbel(int(seed), int(slot), int(q), int(j), int(n)))
 
 
-def sample_scores(logits: np.ndarray, temperature: float, seed: int, slot: int, q: int, j: int) -> np.ndarray:
+def sample_scores(logits: np.ndarray, temperature: float, seed: int, slot: int, q: int, j: int,
+                  top_k: int = 0) -> np.ndarray:
     """Float32 scores whose argmax (lowest index on ties) is the sampled code:
-    logits * float(1/T) + g, as the sampler computes them; greedy: the logits."""
+    logits * float(1/T) + g, as the sampler computes them, -inf outside the
+    top_k largest logits (ties ranked by index); greedy: the logits."""
     lg = np.asarray(logits, dtype=np.float32)
     if temperature == 0:
         return lg.copy()
     inv = np.float32(1.0 / float(np.float32(temperature)))
     g = np.array([gumbel(seed, slot, q, j, n) for n in range(lg.shape[-1])], dtype=np.float32)
-    return (lg * inv).astype(np.float32) + g
+    sc = (lg * inv).astype(np.float32) + g
+    if 0 < top_k < lg.shape[-1]:
+        order = np.lexsort((np.arange(lg.shape[-1]), -lg.astype(np.float64)))  # value desc, index asc
+        keep = np.zeros(lg.shape[-1], bool)
+        keep[order[:top_k]] = True
+        sc = np.where(keep, sc, np.float32(-np.inf)).astype(np.float32)
+    return sc
 
 
-def sample(logits: np.ndarray, temperature: float, seed: int, slot: int, q: int, j: int) -> int:
+def sample(logits: np.ndarray, temperature: float, seed: int, slot: int, q: int, j: int, top_k: int = 0) -> int:
     """The oracle sampler's code for one head's logits (float32 [Vc])."""
     lg = np.ascontiguousarray(logits, dtype=np.float32)
-    return int(load_library().orc_prim_sample(_ptr(lg), lg.shape[0], float(temperature), int(seed),
+    return int(load_library().orc_prim_sample(_ptr(lg), lg.shape[0], float(temperature), int(top_k), int(seed),
                                               int(slot), int(q), int(j)))

@@ -111,3 +111,48 @@ def test_sampled_decode_teacher_forcing_and_vanishing_temperature():
     t.set_sampler(1e-6, 1234)
     t.prefill(0, codes, text)
     np.testing.assert_array_equal(t.decode(6, ov)["codes"], greedy)
+
+
+# ------------------------------------------------------------------ top-k
+
+
+def test_top_k_one_is_greedy_and_k_at_least_n_is_unrestricted():
+    rng = np.random.default_rng(12)
+    for q in range(40):
+        lg = rng.normal(size=50).astype(np.float32)
+        assert sample(lg, 1.3, 4, 0, q, 2, top_k=1) == int(np.argmax(lg))
+        assert sample(lg, 1.3, 4, 0, q, 2, top_k=50) == sample(lg, 1.3, 4, 0, q, 2)
+        assert sample(lg, 1.3, 4, 0, q, 2, top_k=77) == sample(lg, 1.3, 4, 0, q, 2)
+
+
+def test_top_k_draws_follow_the_restricted_softmax():
+    logits = np.array([0.3, -1.2, 1.1, 0.0, 0.45, -0.2, 0.8, -0.6], dtype=np.float32)
+    k, temperature, n = 4, 0.9, 40000
+    counts = np.bincount([sample(logits, temperature, 8, 1, q, 5, top_k=k) for q in range(n)], minlength=8)
+    top = np.argsort(-logits.astype(np.float64), kind="stable")[:k]
+    assert counts[np.setdiff1d(np.arange(8), top)].sum() == 0  # nothing outside the top k
+    z = logits[top].astype(np.float64) / np.float64(np.float32(temperature))
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    chi2 = float(((counts[top] - n * p) ** 2 / (n * p)).sum())
+    assert chi2 < 21.1, (chi2, counts[top], n * p)  # df = 3, p = 1e-4
+
+
+def test_top_k_boundary_ties_go_to_lower_indices():
+    lg = np.array([1.0, 5.0, 3.0, 3.0, 3.0, 0.0], dtype=np.float32)
+    drawn = {sample(lg, 50.0, 3, 0, q, 1, top_k=3) for q in range(3000)}
+    assert drawn == {1, 2, 3}  # a high temperature reaches every member; index 4 is not one
+    for q in range(300):  # the scores mirror used by the parity tests agrees
+        assert int(np.argmax(sample_scores(lg, 50.0, 3, 0, q, 1, top_k=3))) == sample(lg, 50.0, 3, 0, q, 1, top_k=3)
+
+
+def test_top_k_whole_model_teacher_forcing():
+    wl, m, w, codes, text = _tiny()
+    ov = synth.make_overlays(wl, 4)
+    runs = []
+    for forced in (None, "free"):
+        o = Oracle(m, w, 1)
+        o.set_sampler(1.0, 99, top_k=5)
+        o.prefill(0, codes, text)
+        runs.append(o.decode(4, ov, forced=None if forced is None else runs[0])["codes"])
+    np.testing.assert_array_equal(runs[0], runs[1])
