@@ -180,6 +180,7 @@ struct qt_ctx {
   int lds_limit = 0;       // LDS per workgroup on the device
   uint32_t tag_base = 1;   // running phase tag of the persistent kernel
   float inv_temp = 0.f;    // sampling: float(1/T), 0 = greedy (sampler.h)
+  int32_t top_k = 0;       // sampling: the k largest logits compete (0: all)
   uint64_t seed = 0;
   std::string err;
 
@@ -486,11 +487,18 @@ int32_t qt_abi_version(void) { return QT_ABI_VERSION; }
 
 int32_t qt_path(const qt_ctx *ctx) { return ctx ? ctx->path : QT_E_ARG; }
 
-int32_t qt_set_sampler(qt_ctx *c, float temperature, uint64_t seed) {
+int32_t qt_set_sampler(qt_ctx *c, float temperature, int32_t top_k, uint64_t seed) {
   if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
   if (!(temperature >= 0.f) || isinf(temperature))
     return fail(c, QT_E_ARG, "temperature must be finite and >= 0");
+  if (top_k < 0) return fail(c, QT_E_ARG, "top_k must be >= 0");
+  if (top_k > 0 && top_k < c->d.Vc) {
+    if (c->path == QT_PATH_FRAME)
+      return fail(c, QT_E_UNSUPPORTED, "top-k needs the per-op path (a context with QT_F_OPS or several streams)");
+    if (c->d.Vc > 2048) return fail(c, QT_E_UNSUPPORTED, "top-k supports codebooks of at most 2048 entries");
+  }
   c->inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
+  c->top_k = top_k;
   c->seed = seed;
   return QT_OK;
 }
@@ -741,7 +749,7 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
       ArgmaxArgs am = {};
       am.logits = h.y; am.Vc = d.Vc; am.M = 1; am.mode = AM_PREFILL; am.slot = slot;
       am.c0_state = c->A<int32_t>(c->L.c0);
-      am.inv_temp = c->inv_temp; am.seed = c->seed; am.q_prefill = T;
+      am.inv_temp = c->inv_temp; am.seed = c->seed; am.top_k = c->top_k; am.q_prefill = T;
       HIPCHK(c, launch_argmax(am, s));
     }
   }
@@ -781,6 +789,7 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
     memcpy(&up[2], &c->inv_temp, sizeof(float));  // sampler (argmax_kernel)
     up[3] = (int32_t)(uint32_t)c->seed;
     up[4] = (int32_t)(uint32_t)(c->seed >> 32);
+    up[5] = c->top_k;
     int32_t *ov = c->pin_up + c->pu_overlay;
     memcpy(ov, overlay_ids + (size_t)f0 * B, sizeof(int32_t) * nf * B);
     HIPCHK(c, hipMemcpyAsync(ctl, up, 16 * sizeof(int32_t), hipMemcpyHostToDevice, s));

@@ -130,9 +130,11 @@ struct ArgmaxArgs {
   int32_t slot;   // AM_PREFILL
   // Sampling (sampler.h).  AM_PRED / AM_TALKER read it from the per-call
   // control words: ctl[2] = float bits of 1/T (0: greedy), ctl[3], ctl[4] =
-  // seed low, high.  AM_PREFILL takes it here, with q = the prompt length.
+  // seed low, high, ctl[5] = top_k (0: all; needs Vc <= 2048).  AM_PREFILL
+  // takes it here, with q = the prompt length.
   float inv_temp;
   uint64_t seed;
+  int32_t top_k;
   int32_t q_prefill;
 };
 

@@ -1153,38 +1153,131 @@ hipError_t launch_pred_input(const PredInArgs &a, hipStream_t s) {
 // entry: in-graph sampler).  Predictor heads also gather the next micro-step's
 // input row; the talker head advances the slot's position.
 
+// Logit -> unsigned key in the same order (-0 and +0 equal, as they compare).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x == 0.f ? 0.f : x);
+  return b ^ ((b >> 31) ? 0xffffffffu : 0x80000000u);
+}
+
+// This thread's best sampled score among the top_k largest of Vc <= 2048
+// logits (logit i = u * 256 + tid is value u of the thread): the k-th largest
+// key by a radix select, 8 bits per pass from the top, over LDS histograms;
+// logits equal to it count in index order, lower indices first (the argmax's
+// tie rule).  Every other logit scores -inf.  256 threads, all of them.
+__device__ __forceinline__ void top_k_scan(const float *lg, int Vc, int k, float inv_temp, uint64_t seed, int slot,
+                                           int q, int jc, float &best, int &bi) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel[2];      // key prefix found so far, members still to place
+  __shared__ uint32_t eqc[8][4];   // logits equal to the threshold per (value slot, wave)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float v[8];
+  uint32_t key[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    v[u] = lg[min(u * 256 + tid, Vc - 1)];
+    key[u] = order_key(v[u]);
+  }
+  uint32_t prefix = 0, need = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass ? 0xffffffffu << (shift + 8) : 0u;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u * 256 + tid < Vc && (key[u] & hmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 255 - 4l .. 252 - 4l (descending); inclusive scan over lanes
+      uint32_t c[4], c4 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { c[e] = hist[255 - 4 * lane - e]; c4 += c[e]; }
+      uint32_t cum = c4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(cum, o, 64);
+        if (lane >= o) cum += t;
+      }
+      const uint64_t hit = __ballot(cum >= need);
+      if (lane == (int)__ffsll((unsigned long long)hit) - 1) {  // the lane whose bins reach the k-th
+        uint32_t run = cum - c4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (run + c[e] >= need) {
+            sel[0] = prefix | ((uint32_t)(255 - 4 * lane - e) << shift);
+            sel[1] = need - run;
+            break;
+          }
+          run += c[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix = sel[0];
+    need = sel[1];
+  }
+  // logits equal to the threshold key: the first `need` in index order are members
+  if (lane == 0)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) eqc[u][wave] = 0;
+  uint64_t eqm[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    eqm[u] = __ballot(u * 256 + tid < Vc && key[u] == prefix);
+    if (lane == 0) eqc[u][wave] = (uint32_t)__popcll(eqm[u]);
+  }
+  __syncthreads();
+  uint32_t before = 0;  // equal logits at lower indices than value slot u of this thread
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = u * 256 + tid;
+    uint32_t rank = before;
+    for (int w = 0; w < wave; ++w) rank += eqc[u][w];
+    rank += (uint32_t)__popcll(eqm[u] & ((1ull << lane) - 1ull));
+    for (int w = 0; w < 4; ++w) before += eqc[u][w];
+    const bool member = i < Vc && (key[u] > prefix || (key[u] == prefix && rank < need));
+    const float s = member ? sample_score(v[u], inv_temp, seed, slot, q, jc, i) : -INFINITY;
+    if (member && s > best) { best = s; bi = i; }
+  }
+}
+
 __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *lg = a.logits + (size_t)r * a.Vc;
   // The code's sampling key: stream, frame position, index in the frame
   float inv_temp = a.inv_temp;
   uint64_t seed = a.seed;
-  int slot = a.slot, q = a.q_prefill, jc = 0;
+  int slot = a.slot, q = a.q_prefill, jc = 0, top_k = a.top_k;
   if (a.mode != AM_PREFILL) {
     inv_temp = __int_as_float(a.ctl[2]);
     seed = (uint64_t)(uint32_t)a.ctl[3] | ((uint64_t)(uint32_t)a.ctl[4] << 32);
+    top_k = a.ctl[5];
     slot = r;
     q = a.mode == AM_PRED ? a.pos[r] : a.pos[r] + 1;
     jc = a.mode == AM_PRED ? a.j + 1 : 0;
   }
   const bool sampled = inv_temp != 0.f;
-  // Eight logits per thread in flight at a time (a plain loop waits on each
-  // load); the first group is outside any loop.
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  auto scan = [&](int i0) {
-    float v[8];
+  if (sampled && top_k > 0 && top_k < a.Vc) {
+    top_k_scan(lg, a.Vc, top_k, inv_temp, seed, slot, q, jc, best, bi);
+  } else {
+    // Eight logits per thread in flight at a time (a plain loop waits on each
+    // load); the first group is outside any loop.
+    auto scan = [&](int i0) {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = lg[min(i0 + u * 256 + tid, a.Vc - 1)];
+      for (int u = 0; u < 8; ++u) v[u] = lg[min(i0 + u * 256 + tid, a.Vc - 1)];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * 256 + tid;
-      const float s = sampled ? sample_score(v[u], inv_temp, seed, slot, q, jc, i) : v[u];
-      if (i < a.Vc && s > best) { best = s; bi = i; }  // increasing i: first max kept
-    }
-  };
-  scan(0);
-  for (int i0 = 8 * 256; i0 < a.Vc; i0 += 8 * 256) scan(i0);
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + tid;
+        const float s = sampled ? sample_score(v[u], inv_temp, seed, slot, q, jc, i) : v[u];
+        if (i < a.Vc && s > best) { best = s; bi = i; }  // increasing i: first max kept
+      }
+    };
+    scan(0);
+    for (int i0 = 8 * 256; i0 < a.Vc; i0 += 8 * 256) scan(i0);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(best, o, 64);

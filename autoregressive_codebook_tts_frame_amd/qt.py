@@ -98,7 +98,7 @@ def _load():
     lib.qt_time_kernel.restype = i32
     lib.qt_path.argtypes = [vp]
     lib.qt_path.restype = i32
-    lib.qt_set_sampler.argtypes = [vp, C.c_float, C.c_uint64]
+    lib.qt_set_sampler.argtypes = [vp, C.c_float, i32, C.c_uint64]
     lib.qt_set_sampler.restype = i32
     lib.qt_free.argtypes = [vp]
     lib.qt_free.restype = None
@@ -191,8 +191,8 @@ def qt_time_kernel(ctx, kernel: int, reps: int):
     return us.value, nb.value
 
 
-def qt_set_sampler(ctx, temperature: float, seed: int = 0):
-    _check(lib.qt_set_sampler(ctx, float(temperature), int(seed)), ctx)
+def qt_set_sampler(ctx, temperature: float, top_k: int = 0, seed: int = 0):
+    _check(lib.qt_set_sampler(ctx, float(temperature), int(top_k), int(seed)), ctx)
 
 
 def qt_path(ctx) -> int:
@@ -313,8 +313,8 @@ class Decoder:
     def prefill(self, slot: int, codes, text):
         qt_prefill(self.ctx, slot, codes, text)
 
-    def set_sampler(self, temperature: float, seed: int = 0):
-        qt_set_sampler(self.ctx, temperature, seed)
+    def set_sampler(self, temperature: float, seed: int = 0, top_k: int = 0):
+        qt_set_sampler(self.ctx, temperature, top_k, seed)
 
     def decode(self, n: int, overlay: np.ndarray, forced: Optional[np.ndarray] = None) -> np.ndarray:
         m = self.m

@@ -72,7 +72,7 @@ def frame_bytes(m, batch: int, mean_len: float) -> float:
     return weights + kv_read + kv_write + gathers
 
 
-def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0, temperature: float = 0.0, seed: int = 0):
+def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0, temperature: float = 0.0, seed: int = 0, top_k: int = 0):
     """The oracle as it stands, on the host cores: prefill (untimed) then as
     many frames as fit in the budget (at least 1)."""
     from autoregressive_codebook_tts_frame_amd import synth
@@ -80,7 +80,7 @@ def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0, temperature: float = 0
 
     o = Oracle(m, w, 1, pcap=wl.prompt + 64 + 1)
     if temperature:
-        o.set_sampler(temperature, seed)
+        o.set_sampler(temperature, seed, top_k)
     codes, text = synth.make_prompt(wl, 0)
     t = time.time()
     o.prefill(0, codes, text)
@@ -171,6 +171,8 @@ def main():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="sample every code at this temperature (0: greedy, the default)")
     ap.add_argument("--seed", type=int, default=42, help="sampler seed")
+    ap.add_argument("--top-k", type=int, default=0, help="with --temperature: only the k largest logits compete "
+                                                          "(per-op path: use with --ops for one stream)")
     ap.add_argument("--ttfa", action="store_true",
                     help="time to first frame instead: a step is the prompt prefill of every stream plus "
                          "one decoded frame")
@@ -200,7 +202,7 @@ def main():
     d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf,
                    flags=qt.QT_F_OPS if args.ops else 0)
     if args.temperature:
-        d.set_sampler(args.temperature, args.seed)
+        d.set_sampler(args.temperature, args.seed, top_k=args.top_k)
     lens = []
     ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
     for b in range(B):
@@ -275,7 +277,8 @@ def main():
                    "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[d.path],
                    "frames_per_replay": wl.frames_per_replay, "talker_layers": m.Lt,
                    "predictor_layers": m.Lp, "hidden": m.H,
-                   "sampler": f"temperature {args.temperature}, seed {args.seed}" if args.temperature else "greedy"},
+                   "sampler": (f"temperature {args.temperature}, seed {args.seed}"
+                               + (f", top-k {args.top_k}" if args.top_k else "")) if args.temperature else "greedy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name, nf) if d.path == qt.QT_PATH_FRAME else None,
@@ -299,7 +302,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(m, w, wl, temperature=args.temperature, seed=args.seed)
+        res["cpu_baseline"] = cpu_baseline(m, w, wl, temperature=args.temperature, seed=args.seed, top_k=args.top_k)
     print(json.dumps(res), flush=True)
 
 

@@ -249,9 +249,14 @@ int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us
    code's index in its frame (0: the talker's), q the frame's talker position
    (a talker head at position p decides frame p + 1; qt_prefill of T rows
    decides frame T), slot the stream.  This draws each code from
-   softmax(l / T).  Host only: no GPU call, no graph recapture.
-   Errors: QT_E_ARG (NULL ctx, temperature negative, NaN or infinite). */
-int32_t qt_set_sampler(qt_ctx *ctx, float temperature, uint64_t seed);
+   softmax(l / T).  top_k > 0: only the top_k largest logits compete (the draw
+   is from softmax(l / T) restricted to them); equal logits at the boundary
+   rank by lower index, as in the argmax.  top_k = 0 (or >= codebook_size):
+   every logit.  Host only: no GPU call, no graph recapture.
+   Errors: QT_E_ARG (NULL ctx, temperature negative, NaN or infinite, top_k
+   negative), QT_E_UNSUPPORTED (top-k on a context whose decode path is
+   QT_PATH_FRAME, or codebook_size > 2048). */
+int32_t qt_set_sampler(qt_ctx *ctx, float temperature, int32_t top_k, uint64_t seed);
 
 /* Decode path of a context: QT_PATH_FRAME (persistent frame kernel),
    QT_PATH_GRAPH (per-op kernels replayed as a hipGraph) or QT_PATH_EAGER. */
