@@ -871,6 +871,19 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     const Share s = cm.sh[cur.type];
     const bool normed = cur.type == PH_QKV || cur.type == PH_GU || cur.type == PH_HEAD;
     float ss0 = 0.f, ss1 = 0.f;  // this thread's squares of residual rows 0 and 1
+    // Sampling: the Gumbel noise of the head's rows does not depend on the
+    // logits, so each lane draws it for one of its wave's items (items
+    // wave, wave + NW, ...) before the inputs arrive, while the exchange is
+    // in flight; the head phase reads it back by lane.  A talker head decides
+    // the next frame's code 0, predictor head j code j + 1 of this frame.
+    float gnoise = 0.f;
+    if constexpr (SMP) {
+      if (cur.type == PH_HEAD) {
+        const int item = wave + lane * NW;
+        gnoise = gumbel_noise(a.seed, 0, cur.stack ? pos + 1 : pos, cur.stack ? 0 : cur.step + 1,
+                              s.r0 + (item < s.R ? item : s.R - 1));
+      }
+    }
     // every compute wave is done with the last phase's operand and residual rows
     if (!cbar(a, cm, gen)) return;
 
@@ -1027,15 +1040,16 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      // sampling key: a talker head decides the next frame's code 0, head
-      // j of the predictor code j + 1 of this frame (stream slot 0)
-      const int sq = cur.stack ? pos + 1 : pos, sj = cur.stack ? 0 : cur.step + 1;
-      (void)sq; (void)sj;
       gemv_items<WT, 1, NBH>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2], float) {
         const int n = s.r0 + it;
         if (lane == 0) st(lg + n, acc[0][0]);
-        if constexpr (SMP) pick(bv, bi, sample_score(acc[0][0], a.inv_temp, a.seed, 0, sq, sj, n), n);
-        else pick(bv, bi, acc[0][0], n);
+        if constexpr (SMP) {
+          // item it is this wave's ((it - wave) / NW)-th: its noise sits in that lane
+          const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gnoise), (it - wave) / NW));
+          pick(bv, bi, __fadd_rn(__fmul_rn(acc[0][0], a.inv_temp), g), n);
+        } else {
+          pick(bv, bi, acc[0][0], n);
+        }
       });
       if (lane == 0) { cm.amv[wave] = bv; cm.ami[wave] = bi; }
       if (!cbar(a, cm, gen)) return;

@@ -37,14 +37,18 @@ __device__ __forceinline__ uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, u
   return c0;
 }
 
+// Gumbel variate of logit n of code j of frame q, stream slot.
+__device__ __forceinline__ float gumbel_noise(uint64_t seed, int slot, int q, int j, int n) {
+  const uint64_t x = philox4x64_word0((uint64_t)n, (uint64_t)j, (uint64_t)q, (uint64_t)slot, seed, 0);
+  const double u = ((double)(x >> 11) + 0.5) * 0x1p-53;
+  return (float)(-log(-log(u)));
+}
 // Score of logit n of code j of frame q, stream slot: its argmax over n is the
 // sampled code.
 __device__ __forceinline__ float sample_score(float logit, float inv_temp, uint64_t seed, int slot, int q, int j,
                                               int n) {
-  const uint64_t x = philox4x64_word0((uint64_t)n, (uint64_t)j, (uint64_t)q, (uint64_t)slot, seed, 0);
-  const double u = ((double)(x >> 11) + 0.5) * 0x1p-53;
-  const float g = (float)(-log(-log(u)));
-  return __fadd_rn(__fmul_rn(logit, inv_temp), g);
+  return __fadd_rn(__fmul_rn(logit, inv_temp), gumbel_noise(seed, slot, q, j, n));
 }
+
 
 }  // namespace qtk
