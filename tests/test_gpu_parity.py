@@ -534,6 +534,26 @@ def test_full_bf16_long_context_parity():
 
 
 @pytest.mark.timeout(900)
+def test_full_bf16_max_context_parity():
+    # the ring's last positions: a 4,088-position state decoded to position
+    # 4,093 of 4,096; the frame kernel runs 128 attention workgroups (16 tiles
+    # per head) beside 128 GEMV workgroups with one weight slot
+    m = synth.BIG
+    wl = synth.WORKLOADS["bf16_long_b1"]
+    w = synth.make_weights(m)
+    say("[bf16_max_context] state of 4088 positions, 6 frames")
+    r = _injected_state_run(m, w, wl, 6, [4088])
+    assert r["path"] == qt.QT_PATH_FRAME
+    _check(r, m, "bf16_max_context")
+    # one more frame than the ring holds is refused before any launch
+    d = r["fresh"](0)
+    with pytest.raises(qt.QtError) as e:
+        d.decode(9, r["ov"][:1].repeat(9, axis=0))
+    assert e.value.code == qt.QT_E_CONTEXT_FULL
+    d.close()
+
+
+@pytest.mark.timeout(900)
 def test_full_bf16_b32_sampled_parity():
     # 32 streams with the ragged contexts the batched workload uses, decoded
     # four frames per graph replay as the bench times them; the oracle
