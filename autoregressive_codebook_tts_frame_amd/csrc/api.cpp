@@ -23,7 +23,7 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kPrefillChunk = 64;  // prompt rows per prefill step (the batched GEMM takes up to 64)
+constexpr int kPrefillChunk = 128;  // prompt rows per prefill step (the batched GEMM takes up to 128)
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
@@ -83,11 +83,11 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.z = take(sizeof(float) * R * d.F);
   L.ssq = take(sizeof(float) * R * (d.H / 32 > 0 ? d.H / 32 : 1));
   {
-    // split-K partials of the largest projection: (K / 256) slices x 64 rows x columns
+    // split-K partials of the largest projection: (K / 256) slices x 128 rows x columns
     const size_t a1 = (size_t)(d.H / 256) * (d.nqkv > 2 * d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (2 * d.F > d.Vc ? 2 * d.F : d.Vc));
     const size_t a2 = (size_t)(d.qd / 256) * d.H, a3 = (size_t)(d.F / 256) * d.H;
     const size_t mx = a1 > a2 ? (a1 > a3 ? a1 : a3) : (a2 > a3 ? a2 : a3);
-    L.gpart = take(sizeof(float) * 64 * (mx > 0 ? mx : 1));
+    L.gpart = take(sizeof(float) * 128 * (mx > 0 ? mx : 1));
   }
   {
     const int nmax = d.nqkv > d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (d.F > d.Vc ? d.F : d.Vc);
@@ -256,13 +256,13 @@ Stack pred_stack(const qt_ctx *c) {
 }
 
 // One decoder layer over M rows (x in the arena's activation rows).
-// Batched rows (4..64, bf16 or q8 weights with bf16 operands) go through the
+// Batched rows (4..128, bf16 or q8 weights with bf16 operands) go through the
 // MFMA GEMM; fewer rows through the GEMV.  All projections of one layer see the
 // same M, so a layer runs entirely on one of the two.
 bool use_gemm(const qt_ctx *c, int M, int K) {
   const qt_model_desc &md = c->md;
   const Dims &d = c->d;
-  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 4 && M <= 64 && K % 256 == 0 && d.H % 32 == 0 &&
+  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 4 && M <= 128 && K % 256 == 0 && d.H % 32 == 0 &&
          d.nqkv % 32 == 0 && d.F % 32 == 0 && d.Vc % 32 == 0;
 }
 
@@ -906,7 +906,7 @@ int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, 
   gu.x = c->A<float>(c->L.x); gu.x_stride = d.H; gu.M = c->B;
   gu.y = c->A<float>(c->L.z); gu.y_stride = d.F;
   // as the per-op decode path runs it: the GEMV at batch <= 3, the MFMA GEMM
-  // for 4..64 rows (its row norms read the sums of squares the last decode left)
+  // for 4..128 rows (its row norms read the sums of squares the last decode left)
   (void)wt;
   hipError_t err = hipEventRecord(e0, s);
   int launches = 0;

@@ -138,7 +138,7 @@ struct ArgmaxArgs {
   int32_t q_prefill;
 };
 
-// Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 64 rows,
+// Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 128 rows (two 64-row halves),
 // bf16 or q8 weights with bf16 operands.  Tiles of 32 output columns (gated:
 // 32 gate + 32 up rows) x all rows x 256-wide K slices; the last workgroup of
 // a tile to finish sums the K slices' partials in order and applies the

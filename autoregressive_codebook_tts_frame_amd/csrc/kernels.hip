@@ -731,7 +731,7 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
 
 // ------------------------------------------------------------------ batched projections (MFMA)
 //
-// y[M][N] = epi(x~ . W^T) for M <= 64 rows: x~ = bf16(x * rinv * gain) (or
+// y[M][N] = epi(x~ . W^T) for M <= 128 rows (in 64-row halves): x~ = bf16(x * rinv * gain) (or
 // bf16(x)); weight rows in their storage format (bf16, or q8 converted exactly
 // to bf16 with the 32-wide block scale applied to each block's product).
 // v_mfma_f32_16x16x32_bf16 lane layout (checked on the device): A[16][32]
@@ -782,7 +782,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float *p) {
 }
 constexpr int CPOL_SC1 = 16;
 
-template <int WT, int EPI>
+// MH: 64-row halves of the activation rows (1: up to 64 rows; 2: up to 128,
+// the second half staged and multiplied after the first with the same
+// weights, which stay in registers).
+template <int WT, int EPI, int MH>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // The tile's weight rows form NSUB blocks of 16; each block's K slice is
   // split over WPB waves, so every wave owns SPW 32-wide steps of one block
@@ -801,7 +804,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tn = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
   const int M = a.M, K = a.K, N = a.N;
-  const int MT = (M + 15) / 16;
+  const int M0 = M < 64 ? M : 64;  // rows of the first half
+  const int MT = (M0 + 15) / 16;
   const int k0 = ks * GBK;
   const int NP = EPI == EPI_GATED ? 2 * N : N;  // partial columns (gated: gate then up)
   const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.part);
@@ -816,8 +820,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // is unconditional, from a clamped in-bounds address, and masked where it is
   // used: a load under a branch makes the compiler wait for it at the join.
   const int sm = tid >> 2, sq4 = tid & 3;
-  const bool norm_row = a.gain && sm < M;
-  const float *ssp = a.gain ? a.ssq + (size_t)min(sm, M - 1) * a.ssq_stride : a.x;
+  const bool norm_row = a.gain && sm < M0;
+  const float *ssp = a.gain ? a.ssq + (size_t)min(sm, M0 - 1) * a.ssq_stride : a.x;
   float sqv[8];  // slots sq4 + 4 i, i < 8 (hidden widths up to 1024; wider rows add a loop)
 #pragma unroll
   for (int i = 0; i < 8; ++i) sqv[i] = ssp[min(sq4 + 4 * i, K / 32 - 1)];
@@ -832,7 +836,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   for (int it = 0; it < IT; ++it) {
     const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
     if (it * 256 >= MT * 16 * (GBK / 8)) break;  // rows past the last 16-row block
-    const float *xr = a.x + (size_t)min(m, M - 1) * a.x_stride + k0 + 8 * c;
+    const float *xr = a.x + (size_t)min(m, M0 - 1) * a.x_stride + k0 + 8 * c;
     xv[it][0] = *(const float4 *)xr;
     xv[it][1] = *(const float4 *)(xr + 4);
   }
@@ -891,7 +895,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     float v[8] = {xv[it][0].x, xv[it][0].y, xv[it][0].z, xv[it][0].w,
                   xv[it][1].x, xv[it][1].y, xv[it][1].z, xv[it][1].w};
     uint4 o = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M) {
+    if (m < M0) {
       if (a.gain) {
         const float r = rinv[m];
 #pragma unroll
@@ -960,10 +964,119 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int m = mt * 16 + (lane & 15);
-      if (mt < MT && m < M && nj < N)
+      if (mt < MT && m < M0 && nj < N)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc[mt]), prs,
                                                (int)((((size_t)ks * M + m) * NP + (mat ? N : 0) + nj) * 4), 0,
                                                CPOL_SC1);
+    }
+  }
+  if constexpr (MH == 2) {
+    if (M > 64) {
+      // rows 64 .. M-1: their sums of squares and operand slice, then the
+      // same steps as above through the weights still in registers
+      const int M1 = M - 64, MT1 = (M1 + 15) / 16;
+      const bool norm_row1 = a.gain && sm < M1;
+      const float *ssp1 = a.gain ? a.ssq + (size_t)(64 + min(sm, M1 - 1)) * a.ssq_stride : a.x;
+      float sqv1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sqv1[i] = ssp1[min(sq4 + 4 * i, K / 32 - 1)];
+      float4 xv1[IT][2];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
+        if (it * 256 >= MT1 * 16 * (GBK / 8)) break;
+        const float *xr = a.x + (size_t)(64 + min(m, M1 - 1)) * a.x_stride + k0 + 8 * c;
+        xv1[it][0] = *(const float4 *)xr;
+        xv1[it][1] = *(const float4 *)(xr + 4);
+      }
+      float sq1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sq1 += norm_row1 && sq4 + 4 * i < K / 32 ? sqv1[i] : 0.f;
+      if (norm_row1)
+        for (int i = sq4 + 32; i < K / 32; i += 4) sq1 += ssp1[i];
+      sq1 += __shfl_xor(sq1, 1, 64);
+      sq1 += __shfl_xor(sq1, 2, 64);
+      __syncthreads();  // every wave is done with the first half's xs, rinv and red
+      if (sq4 == 0) rinv[sm] = a.gain ? 1.0f / sqrtf(sq1 / (float)K + a.eps) : 1.f;
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
+        if (m >= MT1 * 16) break;
+        float v[8] = {xv1[it][0].x, xv1[it][0].y, xv1[it][0].z, xv1[it][0].w,
+                      xv1[it][1].x, xv1[it][1].y, xv1[it][1].z, xv1[it][1].w};
+        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M1) {
+          if (a.gain) {
+            const float r = rinv[m];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = v[i] * r * gs[8 * c + i];
+            if (a.normed_out && tn == 0)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) a.normed_out[(size_t)(64 + m) * K + k0 + 8 * c + i] = v[i];
+          }
+          o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+          o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+          o.z = (uint32_t)bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
+          o.w = (uint32_t)bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
+        }
+        *(uint4 *)&xs[m * GXS + 8 * c] = o;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+        const int kl = (kq * SPW + s) * 32;
+        bf16x8_t av;
+        if constexpr (WT == W_BF16) {
+          av = __builtin_bit_cast(bf16x8_t, wv[s]);
+        } else {
+          const uint4 wq = make_uint4(i8pair_bf16(wv[s].x, 0), i8pair_bf16(wv[s].x, 2), i8pair_bf16(wv[s].y, 0),
+                                      i8pair_bf16(wv[s].y, 2));
+          av = __builtin_bit_cast(bf16x8_t, wq);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          if (mt >= MT1) break;
+          const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + kl + (lane >> 4) * 8];
+          const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bx);
+          if constexpr (WT == W_BF16) {
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mt], 0, 0, 0);
+          } else {
+            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero, 0, 0, 0);
+            const float *sr = &scl[(nb * 16 + (lane >> 4) * 4) * NBLK + kl / 32];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mt][j] += t[j] * sr[j * NBLK];
+          }
+        }
+      }
+      if constexpr (WPB > 1) {
+        if (kq > 0)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            if (mt < MT1) red[((nb * (WPB - 1) + kq - 1) * 4 + mt) * 64 + lane] = acc[mt];
+        __syncthreads();
+        if (kq == 0)
+#pragma unroll
+          for (int q = 1; q < WPB; ++q)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              if (mt < MT1) acc[mt] += red[((nb * (WPB - 1) + q - 1) * 4 + mt) * 64 + lane];
+      }
+      // row 64 + m
+      if (kq == 0) {
+        const int nj = nrow0 + (lane >> 4) * 4;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int m = mt * 16 + (lane & 15);
+          if (mt < MT1 && m < M1 && nj < N)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc[mt]), prs,
+                                                   (int)((((size_t)ks * M + 64 + m) * NP + (mat ? N : 0) + nj) * 4), 0,
+                                                   CPOL_SC1);
+        }
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
@@ -980,7 +1093,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile.  The
   // residual row and every slice of a group (all of them for K <= 3072) are
   // requested before the first sum, so the epilogue waits for one round trip.
-  const int m = tid >> 2, c0 = (tid & 3) * 8;
+  for (int h = 0; h < MH; ++h) {  // 64-row halves
+  const int m = h * 64 + (tid >> 2), c0 = (tid & 3) * 8;
   const int nb0 = tn * GT + c0;
   sq = 0.f;
   if (m < M && nb0 < N) {
@@ -1036,19 +1150,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     sq += __shfl_xor(sq, 2, 64);
     if ((tid & 3) == 0 && m < M) a.ssq_out[(size_t)m * (N / 32) + tn] = sq;
   }
+  }
 }
 
 template <int WT>
 static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
   const dim3 grid((a.N + GT - 1) / GT, a.K / GBK);
-  if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE>), grid, dim3(256), 0, s, a);
-  else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED>), grid, dim3(256), 0, s, a);
+  if (a.M <= 64) {
+    if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE, 1>), grid, dim3(256), 0, s, a);
+    else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED, 1>), grid, dim3(256), 0, s, a);
+  } else {
+    if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE, 2>), grid, dim3(256), 0, s, a);
+    else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED, 2>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
-  if (a.M < 1 || a.M > 64 || a.K % GBK || a.N % GT || a.nseg < 1 || a.nseg > 3) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 128 || a.K % GBK || a.N % GT || a.nseg < 1 || a.nseg > 3) return hipErrorInvalidValue;
   for (int i = 0; i + 1 < a.nseg; ++i)  // a 16-row weight block never straddles two segments
     if (a.seg_end[i] % 16) return hipErrorInvalidValue;
   if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);

@@ -109,7 +109,7 @@ def talker_weight_bytes(m) -> float:
 
 def ttfa(args, d, m, wl, B):
     """Time to first frame: qt_prefill of each stream's prompt (per-op path,
-    chunks of 64 rows on the MFMA GEMM) then one qt_decode_frame.  Host wall
+    chunks of 128 rows on the MFMA GEMM) then one qt_decode_frame.  Host wall
     clock around each step (both calls are synchronous)."""
     import numpy as np
     from autoregressive_codebook_tts_frame_amd import synth
@@ -129,7 +129,7 @@ def ttfa(args, d, m, wl, B):
         t0 = time.perf_counter()
         step()
         times.append(time.perf_counter() - t0)
-    # the prefill alone, for its roofline: the talker weights once per 64-row chunk
+    # the prefill alone, for its roofline: the talker weights once per 128-row chunk
     pre = []
     for _ in range(args.steps):
         t0 = time.perf_counter()
@@ -137,7 +137,7 @@ def ttfa(args, d, m, wl, B):
             d.prefill(b, c, t)
         pre.append(time.perf_counter() - t0)
     T = len(prompts[0][1])
-    chunks = B * ((T + 63) // 64)
+    chunks = B * ((T + 127) // 128)
     wbytes = talker_weight_bytes(m)
     ms = 1e3 * float(np.median(times))
     pre_ms = 1e3 * float(np.median(pre))
@@ -147,13 +147,13 @@ def ttfa(args, d, m, wl, B):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16"}[m.lin],
         "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
-        "config": {"workload": wl.name + "_ttfa", "batch": B, "prompt": T, "prefill_chunk": 64,
+        "config": {"workload": wl.name + "_ttfa", "batch": B, "prompt": T, "prefill_chunk": 128,
                    "path": "per-op prefill + " + {1: "persistent frame kernel", 2: "per-op hipGraph",
                                                   3: "per-op eager"}[d.path]},
         "prefill_ms": pre_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "prefill (talker weights streamed once per 64-row chunk)",
+                     "kernel": "prefill (talker weights streamed once per 128-row chunk)",
                      "bytes_per_launch": chunks * wbytes, "avg_launch_us": pre_ms * 1e3},
         "cpu_baseline": None,
     }
