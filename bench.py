@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--seed", type=int, default=42, help="sampler seed")
     ap.add_argument("--top-k", type=int, default=0, help="with --temperature: only the k largest logits compete "
                                                           "(per-op path: use with --ops for one stream)")
+    ap.add_argument("--frames-per-replay", type=int, default=None,
+                    help="frames per graph replay on the per-op path (default: the workload's)")
     ap.add_argument("--ttfa", action="store_true",
                     help="time to first frame instead: a step is the prompt prefill of every stream plus "
                          "one decoded frame")
@@ -199,6 +201,9 @@ def main():
     t = time.time()
     w = synth.make_weights(m)
     log(f"weights drawn in {time.time() - t:.1f}s; uploading")
+    if args.frames_per_replay:
+        import dataclasses
+        wl = dataclasses.replace(wl, frames_per_replay=args.frames_per_replay)
     d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf,
                    flags=qt.QT_F_OPS if args.ops else 0)
     if args.temperature:
