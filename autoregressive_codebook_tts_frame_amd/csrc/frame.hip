@@ -561,10 +561,13 @@ __device__ __forceinline__ float gain_at(const FrameArgs &a, const uint8_t *g, i
   return a.tab_bf16 ? __uint_as_float((uint32_t)((const uint16_t *)g)[e] << 16) : ((const float *)g)[e];
 }
 // bf16 pairs of RMSNorm(x) * g for elements e0 .. e0 + 7
+// (bf16 and q8 weights run with bf16 tables and gains, f32 weights with f32
+// ones: the kernel's weight type fixes the gains' format at compile time)
+template <bool TB>
 __device__ __forceinline__ uint4 norm8(const FrameArgs &a, const float *x, const uint8_t *g, float r, int e0) {
   const float4 x0 = *(const float4 *)(x + e0), x1 = *(const float4 *)(x + e0 + 4);
   float g8[8];
-  if (a.tab_bf16) {
+  if constexpr (TB) {
     const uint4 gw = *(const uint4 *)(g + 2 * e0);
     g8[0] = lo16(gw.x); g8[1] = hi16(gw.x); g8[2] = lo16(gw.y); g8[3] = hi16(gw.y);
     g8[4] = lo16(gw.z); g8[5] = hi16(gw.z); g8[6] = lo16(gw.w); g8[7] = hi16(gw.w);
@@ -582,10 +585,10 @@ template <int WT>
 __device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, const uint8_t *g, float r, int c) {
   OpC o;
   if constexpr (WT == W_Q8) {
-    o.a = norm8(a, x, g, r, 16 * c);
-    o.b = norm8(a, x, g, r, 16 * c + 8);
+    o.a = norm8<true>(a, x, g, r, 16 * c);
+    o.b = norm8<true>(a, x, g, r, 16 * c + 8);
   } else if constexpr (WT == W_BF16) {
-    o.a = norm8(a, x, g, r, 8 * c);
+    o.a = norm8<true>(a, x, g, r, 8 * c);
     o.b = o.a;
   } else {
     const int e0 = 4 * c;
@@ -603,6 +606,8 @@ __device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, co
 // table row (bf16 or f32) element pairs of this thread -> v[2 * HPAIR]
 // (zero beyond the row: every element is written, so no value is carried
 // over from an earlier phase)
+// (TB: bf16 tables, which the bf16 and q8 kernels always have)
+template <bool TB>
 __device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, size_t row, float *v) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -611,7 +616,7 @@ __device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, s
     v[2 * k] = 0.f;
     v[2 * k + 1] = 0.f;
     if (2 * pi < a.H) {
-      if (a.tab_bf16) {
+      if constexpr (TB) {
         const uint32_t w = ld((const uint32_t *)((const uint16_t *)tab + row * a.H) + pi);
         v[2 * k] = lo16(w); v[2 * k + 1] = hi16(w);
       } else {
@@ -736,7 +741,7 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
       // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
       const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
       const float z1 = acc[2][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[2][m])) * acc[3][m];
-      if (a.act_bf16) {
+      if constexpr (WT != W_F32) {  // bf16 operands (the bf16 and q8 kernels always have them)
         if (lane < a.rep) tput(a.zb + lane * a.rep_stride + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
       } else if (lane < 2 * a.rep) {
         const int e = lane & 1;
@@ -917,7 +922,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
           }
           const int code0 = force ? ld(ci) : c0;
           cm.codes[0] = code0;
-          tab_pairs(a, a.code_emb, (size_t)code0, row);
+          tab_pairs<WT != W_F32>(a, a.code_emb, (size_t)code0, row);
 #pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
@@ -932,7 +937,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             }
           }
         } else if (cur.stack == 0) {
-          tab_pairs(a, a.code_emb, (size_t)cur.step * a.Vc + cm.codes[cur.step], row);
+          tab_pairs<WT != W_F32>(a, a.code_emb, (size_t)cur.step * a.Vc + cm.codes[cur.step], row);
 #pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
@@ -946,8 +951,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
         } else {
           // talker input: the frame's G code rows, then the overlay row, in order
           float trow[2 * HPAIR];
-          tab_pairs(a, a.code_emb, (size_t)(G - 1) * a.Vc + cm.codes[G - 1], row);
-          tab_pairs(a, a.text_emb, (size_t)ld(a.overlay + f), trow);
+          tab_pairs<WT != W_F32>(a, a.code_emb, (size_t)(G - 1) * a.Vc + cm.codes[G - 1], row);
+          tab_pairs<WT != W_F32>(a, a.text_emb, (size_t)ld(a.overlay + f), trow);
 #pragma unroll
           for (int k = 0; k < HPAIR; ++k) {
             const int pi = tid + k * NT;
