@@ -657,9 +657,11 @@ struct NoPre {
   __device__ __forceinline__ float operator()(int) const { return 0.f; }
 };
 // Items go round-robin: this wave takes items wv, wv + nwv, ...
-template <int WT, int UPI, int MAXB, class Op, class Out, class Pre = NoPre>
-__device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int M, Out out,
+// MC: the operand row count at compile time (1 or 2; 0: the run-time M)
+template <int WT, int UPI, int MAXB, int MC, class Op, class Out, class Pre = NoPre>
+__device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int Mrt, Out out,
                                            Pre pre = Pre(), int wv = -1, int nwv = NW) {
+  const int M = MC ? MC : Mrt;
   constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63;
   const int rowb = s.K * ESZ, bpr = rowb >> 10;
@@ -729,14 +731,15 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
     }
   auto op = [&](int m, int cb, int) -> OpC { return xo[m][cb]; };
   if (type == PH_QKV) {
-    gemv_items<WT, 1, NBH>(sp, op, s, M, [&](int it, float (&acc)[1][2], float) {
+    auto out = [&](int it, float (&acc)[1][2], float) {
       if (lane < M) tputf(a.qkvb + (size_t)lane * s.N + s.r0 + it, lane ? acc[0][1] : acc[0][0], tag);
-    }, NoPre(), wv, nwv);
+    };
+    if (M > 1) gemv_items<WT, 1, NBH, 2>(sp, op, s, M, out, NoPre(), wv, nwv);
+    else gemv_items<WT, 1, NBH, 1>(sp, op, s, M, out, NoPre(), wv, nwv);
     return;
   }
   // item = row pair (2 p, 2 p + 1)
-  gemv_items<WT, 4, NBH>(sp, op, s, M,
-                         [&](int it, float (&acc)[4][2], float) {
+  auto out = [&](int it, float (&acc)[4][2], float) {
     for (int m = 0; m < M; ++m) {
       // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
       const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
@@ -748,7 +751,9 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
         tputf(a.zb + (lane >> 1) * a.rep_stride + (size_t)m * a.F + s.r0 + 2 * it + e, e ? z1 : z0, tag);
       }
     }
-  }, NoPre(), wv, nwv);
+  };
+  if (M > 1) gemv_items<WT, 4, NBH, 2>(sp, op, s, M, out, NoPre(), wv, nwv);
+  else gemv_items<WT, 4, NBH, 1>(sp, op, s, M, out, NoPre(), wv, nwv);
 }
 
 // The loader waves: stream each GEMV phase's weight slice (a part each) into
@@ -1045,7 +1050,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       float *lg = cur.stack ? a.logits_t : a.logits_p + (size_t)cur.step * a.Vc;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      gemv_items<WT, 1, NBH>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2], float) {
+      gemv_items<WT, 1, NBH, 1>(sp, op_reg, s, 1, [&](int it, float (&acc)[1][2], float) {
         const int n = s.r0 + it;
         if (lane == 0) st(lg + n, acc[0][0]);
         if constexpr (SMP) {
@@ -1069,14 +1074,16 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       const int type = cur.type, N = s.N;
       const bool hid = type == PH_D && cur.stack == 1 && a.dump;
       if (type == PH_QKV) {
-        gemv_items<WT, 1, NBH>(sp, op_reg, s, M, [&](int it, float (&acc)[1][2], float) {
+        auto out = [&](int it, float (&acc)[1][2], float) {
           if (lane < M) tputf(a.qkvb + (size_t)lane * N + s.r0 + it, lane ? acc[0][1] : acc[0][0], tag);
-        });
+        };
+        if (M > 1) gemv_items<WT, 1, NBH, 2>(sp, op_reg, s, M, out);
+        else gemv_items<WT, 1, NBH, 1>(sp, op_reg, s, M, out);
       } else {
         // the residual element (lane: copy lane / M of row lane % M) is read
         // when the item starts, off the path after the reduction
         const int rm = M > 1 ? lane & 1 : 0, rr = M > 1 ? lane >> 1 : lane;
-        gemv_items<WT, 1, nb_wide(WT)>(sp, op_row, s, M, [&](int it, float (&acc)[1][2], float res) {
+        auto out = [&](int it, float (&acc)[1][2], float res) {
           const int n = s.r0 + it;
           if (lane < M * a.rep) {
             const int m = rm, r = rr;
@@ -1084,7 +1091,10 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             tputf(a.xq + r * a.rep_stride + (size_t)m * H + n, x, tag);
             if (hid && r == 0) st(a.hidden_dump + (size_t)cur.layer * H + n, x);
           }
-        }, [&](int it) { return lane < M * a.rep ? xres[rm * H + s.r0 + it] : 0.f; });
+        };
+        auto pre = [&](int it) { return lane < M * a.rep ? xres[rm * H + s.r0 + it] : 0.f; };
+        if (M > 1) gemv_items<WT, 1, nb_wide(WT), 2>(sp, op_row, s, M, out, pre);
+        else gemv_items<WT, 1, nb_wide(WT), 1>(sp, op_row, s, M, out, pre);
       }
     }
     if (lane == 0)  // this wave is done with the phase's slot
