@@ -668,22 +668,25 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
   const int nitems = s.R * s.NM / UPI;
   const uint8_t *scb = slot + scales_off(s, ESZ);
   for (int it = wv < 0 ? (int)(threadIdx.x >> 6) : wv; it < nitems; it += nwv) {
+    // Every block's loads are unconditional, from block min(cb, bpr - 1)
+    // past the row's end (read, never used): a load under a branch makes the
+    // compiler wait for all outstanding LDS operations where the branch joins.
     uint4 w[UPI][MAXB];
 #pragma unroll
     for (int q = 0; q < UPI; ++q)
 #pragma unroll
       for (int cb = 0; cb < MAXB; ++cb)
-        if (cb < bpr) w[q][cb] = ((const uint4 *)(slot + (size_t)(it * UPI + q) * rowb))[cb * 64 + lane];
+        w[q][cb] = ((const uint4 *)(slot + (size_t)(it * UPI + q) * rowb))[min(cb, bpr - 1) * 64 + lane];
     const float pv = pre(it);
     // the operand chunks too, before any dot product (from LDS they would
     // otherwise wait one LDS round trip per block)
     OpC x[2][MAXB];
 #pragma unroll
-    for (int cb = 0; cb < MAXB; ++cb)
-      if (cb < bpr) {
-        x[0][cb] = op(0, cb, cb * 64 + lane);
-        if (M > 1) x[1][cb] = op(1, cb, cb * 64 + lane);
-      }
+    for (int cb = 0; cb < MAXB; ++cb) {
+      const int c = min(cb, bpr - 1) * 64 + lane;  // (register operands take cb itself)
+      x[0][cb] = op(0, cb, c);
+      if (M > 1) x[1][cb] = op(1, cb, c);
+    }
     float acc[UPI][2];
 #pragma unroll
     for (int q = 0; q < UPI; ++q) acc[q][0] = acc[q][1] = 0.f;
@@ -712,9 +715,10 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
 // (published as they are) or gate/up row pairs (z = SiLU(g) * u published as
 // the down projection's operand).  With two weight slots the loader waves take
 // items too: these slices' rows do not divide evenly over the compute waves.
-template <int WT>
-__device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &cm, int type, const float *xres,
-                                             const uint8_t *sp, int M, uint32_t tag, int wv, int nwv) {
+template <int WT, int MC>
+__device__ __forceinline__ void normed_items_m(const FrameArgs &a, const Common &cm, int type, const float *xres,
+                                               const uint8_t *sp, uint32_t tag, int wv, int nwv) {
+  constexpr int M = MC;  // operand rows, at compile time
   constexpr int ESZ = WEsz<WT>::v;
   constexpr int NBH = nb_hidden(WT);
   const int lane = threadIdx.x & 63;
@@ -724,11 +728,11 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
   const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
   OpC xo[2][NBH];
 #pragma unroll
-  for (int cb = 0; cb < NBH; ++cb)
-    if (cb < bpr) {
-      xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, cb * 64 + lane);
-      if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + a.H, gain, r1, cb * 64 + lane);
-    }
+  for (int cb = 0; cb < NBH; ++cb) {  // unconditional loads (see gemv_items)
+    const int c = min(cb, bpr - 1) * 64 + lane;
+    xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, c);
+    if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + a.H, gain, r1, c);
+  }
   auto op = [&](int m, int cb, int) -> OpC { return xo[m][cb]; };
   if (type == PH_QKV) {
     auto out = [&](int it, float (&acc)[1][2], float) {
@@ -754,6 +758,14 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
   };
   if (M > 1) gemv_items<WT, 4, NBH, 2>(sp, op, s, M, out, NoPre(), wv, nwv);
   else gemv_items<WT, 4, NBH, 1>(sp, op, s, M, out, NoPre(), wv, nwv);
+}
+
+// one or two operand rows (two only in the predictor's first step), at compile time
+template <int WT>
+__device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &cm, int type, const float *xres,
+                                             const uint8_t *sp, int M, uint32_t tag, int wv, int nwv) {
+  if (M > 1) normed_items_m<WT, 2>(a, cm, type, xres, sp, tag, wv, nwv);
+  else normed_items_m<WT, 1>(a, cm, type, xres, sp, tag, wv, nwv);
 }
 
 // The loader waves: stream each GEMV phase's weight slice (a part each) into
