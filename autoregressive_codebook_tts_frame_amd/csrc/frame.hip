@@ -1030,11 +1030,11 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       const int bpr = H * ESZ >> 10;
       const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
 #pragma unroll
-      for (int cb = 0; cb < NBH; ++cb)
-        if (cb < bpr) {
-          xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, cb * 64 + lane);
-          if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + H, gain, r1, cb * 64 + lane);
-        }
+      for (int cb = 0; cb < NBH; ++cb) {  // unconditional loads (see gemv_items)
+        const int c = min(cb, bpr - 1) * 64 + lane;
+        xo[0][cb] = norm_chunk<WT>(a, xres, gain, r0, c);
+        if (M > 1) xo[1][cb] = norm_chunk<WT>(a, xres + H, gain, r1, c);
+      }
       if (cur.type == PH_HEAD && cur.stack == 1) {
         // the talker's normed output row, kept (unrounded) as the next frame's bridge
 #pragma unroll
@@ -1104,7 +1104,10 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
             if (hid && r == 0) st(a.hidden_dump + (size_t)cur.layer * H + n, x);
           }
         };
-        auto pre = [&](int it) { return lane < M * a.rep ? xres[rm * H + s.r0 + it] : 0.f; };
+        auto pre = [&](int it) {  // every lane loads (in bounds), the publishing lanes use it
+          const float v = xres[rm * H + s.r0 + it];
+          return lane < M * a.rep ? v : 0.f;
+        };
         if (M > 1) gemv_items<WT, 1, nb_wide(WT), 2>(sp, op_row, s, M, out, pre);
         else gemv_items<WT, 1, nb_wide(WT), 1>(sp, op_row, s, M, out, pre);
       }
