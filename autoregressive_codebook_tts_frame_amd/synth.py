@@ -9,7 +9,7 @@ scales) happen here because the drawn tensors *are* stored in those formats.
 
 Shapes follow the five workloads of the decode step: a tiny F32 model, the
 28-layer BF16 model at batch 1, the same model at long context, at 32 ragged
-streams, and with Q8_0-style block-quantised linear weights.  The talker /
+streams, and with Q8_0-style or 4-bit block-quantised linear weights.  The talker /
 code-predictor split, the 16 codebooks and the one text-or-pad overlay row
 per frame are those of the qwentts.cpp pipeline-tts.h commit log (entries on
 assembling the AR inputs on device and on the per-layer K/V ring).
@@ -30,7 +30,7 @@ import numpy as np
 # ---------------------------------------------------------------------------
 # storage formats
 
-LIN_F32, LIN_BF16, LIN_Q8 = 0, 1, 2
+LIN_F32, LIN_BF16, LIN_Q8, LIN_Q4 = 0, 1, 2, 3
 Q8_BLOCK = 32
 
 
@@ -109,6 +109,7 @@ BIG = Model("bf16_28L", 1, H=1024, nq=16, nkv=8, hd=128, F=3072, Lt=28, Lp=5,
             G=16, Vc=2048, Vt=151936, P=4096, Q=16, lin=LIN_BF16,
             tab_bf16=True, kv_bf16=True, act_bf16=True)
 BIG_Q8 = dataclasses.replace(BIG, name="q8_28L", model_id=4, lin=LIN_Q8)
+BIG_Q4 = dataclasses.replace(BIG, name="q4_28L", model_id=5, lin=LIN_Q4)
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny_f32_b1": Workload(0, "tiny_f32_b1", TINY, batch=1, prompt=16, frames=8,
@@ -122,6 +123,10 @@ WORKLOADS: Dict[str, Workload] = {
     "q8_b1": Workload(4, "q8_b1", BIG_Q8, batch=1, prompt=128, frames=64,
                       frames_per_replay=1),
     "q8_b8": Workload(4, "q8_b8", BIG_Q8, batch=8, prompt=128, frames=64,
+                      frames_per_replay=1),
+    "q4_b1": Workload(5, "q4_b1", BIG_Q4, batch=1, prompt=128, frames=64,
+                      frames_per_replay=1),
+    "q4_b8": Workload(5, "q4_b8", BIG_Q4, batch=8, prompt=128, frames=64,
                       frames_per_replay=1),
 }
 
@@ -169,9 +174,19 @@ def _store_linear(m: Model, rng: np.random.Generator, shape, random_scales: bool
         return _normal(rng, shape, 0.02)
     if m.lin == LIN_BF16:
         return f32_to_bf16_bits(_normal(rng, shape, 0.02))
-    # Q8_0-style: 32 int8 values per block along the input dim + one fp16 scale
     n, k = shape
     assert k % Q8_BLOCK == 0
+    if m.lin == LIN_Q4:
+        # 4-bit blocks: codes 0..15 (value c - 8), two per byte, even index in
+        # the low nibble; one fp16 scale per 32 weights along the input dim
+        c = rng.integers(0, 16, size=shape, dtype=np.uint8)
+        packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        if random_scales:
+            d = (rng.uniform(0.5, 1.5, size=(n, k // Q8_BLOCK)) * (0.02 / 8.0)).astype(np.float16)
+        else:
+            d = np.full((n, k // Q8_BLOCK), 0.02 / 8.0, dtype=np.float16)
+        return (packed, d.view(np.uint16))
+    # Q8_0-style: 32 int8 values per block along the input dim + one fp16 scale
     q = rng.integers(-127, 128, size=shape, dtype=np.int8)
     if random_scales:
         s = rng.uniform(0.5, 1.5, size=(n, k // Q8_BLOCK)) * (0.02 / 127.0)
@@ -190,7 +205,8 @@ def make_weights(m: Model, random_q8_scales: bool = False, literal_gains: bool =
     code_emb [G][Vc][H], text_emb [Vt][H], t_norm [H], t_head [Vc][H],
     p_norm [H], p_heads (G-1 x [Vc][H]), talker / predictor: lists of per-layer
     dicts keyed by LAYER_KEYS.  Linear weights are float32, bf16 bits (uint16)
-    or a (int8 [N][K], fp16-bits uint16 [N][K/32]) pair.
+    or a (int8 [N][K], fp16-bits uint16 [N][K/32]) pair (q4: uint8 [N][K/2]
+    of packed 4-bit codes instead of the int8 values).
     """
     tid = iter(range(1 << 30))
 

@@ -58,7 +58,7 @@ def frame_bytes(m, batch: int, mean_len: float) -> float:
     reads over valid positions only (talker: mean_len per layer; predictor:
     2 + 3 + ... + 16 positions per layer), K/V row writes and the gathered
     table rows.  The padded window tail and norm gains are not counted."""
-    wb = {0: 4.0, 1: 2.0, 2: 34.0 / 32.0}[m.lin]
+    wb = {0: 4.0, 1: 2.0, 2: 34.0 / 32.0, 3: 18.0 / 32.0}[m.lin]
     tb = 2.0 if m.tab_bf16 else 4.0
     kvb = 2.0 if m.kv_bf16 else 4.0
     layer = (m.nqkv * m.H + m.H * m.nq * m.hd + 3 * m.F * m.H) * wb
@@ -102,7 +102,7 @@ def cpu_baseline(m, w, wl, frames_budget_s: float = 15.0, temperature: float = 0
 
 def talker_weight_bytes(m) -> float:
     """Talker projection weights plus its head: what one prefill chunk streams."""
-    wb = {0: 4.0, 1: 2.0, 2: 34.0 / 32.0}[m.lin]
+    wb = {0: 4.0, 1: 2.0, 2: 34.0 / 32.0, 3: 18.0 / 32.0}[m.lin]
     layer = (m.nqkv * m.H + m.H * m.nq * m.hd + 3 * m.F * m.H) * wb
     return m.Lt * layer + m.Vc * m.H * wb
 
@@ -145,7 +145,7 @@ def ttfa(args, d, m, wl, B):
     return {
         "metric": f"time to first frame (prefill of {T} rows + 1 frame)", "value": ms, "unit": "ms",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16"}[m.lin],
+        "scaling": "weak", "vs_baseline": None, "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16", 3: "q4+bf16"}[m.lin],
         "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
         "config": {"workload": wl.name + "_ttfa", "batch": B, "prompt": T, "prefill_chunk": 128,
                    "path": "per-op prefill + " + {1: "persistent frame kernel", 2: "per-op hipGraph",
@@ -276,7 +276,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16"}[m.lin],
+        "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16", 3: "q4+bf16"}[m.lin],
         "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
         "config": {"workload": wl.name, "batch": B, "prompt": wl.prompt, "frames_per_step": nf,
                    "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[d.path],

@@ -34,6 +34,11 @@
  * SiLU-multiply MLP, no biases, untied heads) are listed in the design doc and
  * pinned in tests/ against HuggingFace's Qwen3 implementation.
  *
+ * Linear-weight formats: F32, BF16, Q8 (32 int8 + one fp16 scale) and Q4.
+ * The qwentts.cpp commit log's TTFA table lists a 4-bit column without
+ * defining its block; Q4 here is our own: 32 weights per fp16 scale d, two
+ * 4-bit codes c per byte (even index in the low nibble), w = d * (c - 8).
+ *
  * Arithmetic: every dot product, sum and elementwise function is evaluated in
  * double, sequentially in index order, and rounded to the storage precision of
  * the tensor it produces: float32 for activations, hidden states and logits;
@@ -58,8 +63,8 @@
 /* ----------------------------------------------------------------------- */
 /* storage formats                                                          */
 
-enum { ORC_LIN_F32 = 0, ORC_LIN_BF16 = 1, ORC_LIN_Q8 = 2 };
-#define ORC_Q8_BLOCK 32
+enum { ORC_LIN_F32 = 0, ORC_LIN_BF16 = 1, ORC_LIN_Q8 = 2, ORC_LIN_Q4 = 3 };
+#define ORC_Q8_BLOCK 32 /* weights per scale, for both block formats */
 
 typedef struct {
   int32_t H, nq, nkv, hd, F;
@@ -125,8 +130,9 @@ float orc_f16_to_f32(uint16_t h) {
 #define ORC_LAYER_SLOTS 18
 
 typedef struct {
-  const void *w;     /* float[N][K], bf16 bits[N][K] or int8[N][K] */
-  const uint16_t *d; /* q8 only: fp16 bits [N][K/32] */
+  const void *w;     /* float[N][K], bf16 bits[N][K], int8[N][K] (q8) or
+                        uint8[N][K/2] (q4: weight k in byte k/2, low nibble for even k) */
+  const uint16_t *d; /* q8 / q4 only: fp16 bits [N][K/32] */
   int32_t N, K;
 } orc_lin;
 
@@ -159,7 +165,7 @@ static double tab_get(const orc_model *m, const void *p, size_t i) {
                      : (double)((const float *)p)[i];
 }
 
-/* one row of a linear weight as doubles (Q8: w = f32(d) * q, exact) */
+/* one row of a linear weight as doubles (Q8: w = f32(d) * q; Q4: w = f32(d) * (c - 8); exact) */
 static void lin_row(const orc_model *m, const orc_lin *L, int32_t n, double *out) {
   size_t base = (size_t)n * L->K;
   if (m->lin == ORC_LIN_F32) {
@@ -168,6 +174,14 @@ static void lin_row(const orc_model *m, const orc_lin *L, int32_t n, double *out
   } else if (m->lin == ORC_LIN_BF16) {
     const uint16_t *w = (const uint16_t *)L->w + base;
     for (int32_t k = 0; k < L->K; ++k) out[k] = bf16_to_f32(w[k]);
+  } else if (m->lin == ORC_LIN_Q4) {
+    /* 4-bit blocks of our own definition: code c in 0..15 stands for c - 8 */
+    const uint8_t *q = (const uint8_t *)L->w + base / 2;
+    const uint16_t *d = L->d + (size_t)n * (L->K / ORC_Q8_BLOCK);
+    for (int32_t k = 0; k < L->K; ++k) {
+      const int c = k % 2 ? q[k / 2] >> 4 : q[k / 2] & 15;
+      out[k] = (double)orc_f16_to_f32(d[k / ORC_Q8_BLOCK]) * (double)(c - 8);
+    }
   } else {
     const int8_t *q = (const int8_t *)L->w + base;
     const uint16_t *d = L->d + (size_t)n * (L->K / ORC_Q8_BLOCK);
@@ -465,7 +479,8 @@ orc_sess *orc_new(const orc_model *m, const void *const *t, int32_t n_tensors, i
   if (!m || !t || B <= 0 || Pcap <= 0 || Pcap > m->P) return NULL;
   if (n_tensors != orc_num_tensors(m)) return NULL;
   if (m->hd % 2 || m->nq % m->nkv || m->G < 2 || m->Q < m->G) return NULL;
-  if (m->lin == ORC_LIN_Q8 && (m->H % ORC_Q8_BLOCK || m->F % ORC_Q8_BLOCK ||
+  if (m->lin < ORC_LIN_F32 || m->lin > ORC_LIN_Q4) return NULL;
+  if (m->lin >= ORC_LIN_Q8 && (m->H % ORC_Q8_BLOCK || m->F % ORC_Q8_BLOCK ||
                                (m->nq * m->hd) % ORC_Q8_BLOCK))
     return NULL;
   orc_sess *s = (orc_sess *)calloc(1, sizeof(orc_sess));

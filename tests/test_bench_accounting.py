@@ -36,6 +36,8 @@ def _expected(weight_bytes_per_param: float, batch: int, mean_context: float) ->
     ("bf16_b32", 32, 1088.5, 2.0, 7406.7),       # 32 streams, mean context 1,088.5
     ("q8_b1", 1, 160.5, 34 / 32, 1778.6),         # 32 int8 + one fp16 scale per 32 weights
     ("q8_b8", 8, 160.5, 34 / 32, 1930.4),
+    ("q4_b1", 1, 160.5, 18 / 32, 951.8),          # 32 4-bit codes (16 bytes) + one fp16 scale per 32
+    ("q4_b8", 8, 160.5, 18 / 32, 1103.6),
 ])
 def test_frame_bytes_match_the_shapes(workload, batch, mean_context, wb, mb):
     m = synth.WORKLOADS[workload].model

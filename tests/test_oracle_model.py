@@ -8,7 +8,8 @@
   K/V ring entry: identical output against the pre-cache run), batched ==
   per-stream (MiniCPM-o optimizations.md, core table, batched Token2Wav row),
   and the predictor cache reset makes stale rows irrelevant.
-* Q8 blocks == the same weights dequantised by the closed form w = d * q.
+* Q8 / Q4 blocks == the same weights dequantised by the closed forms w = d * q,
+  w = d * (c - 8).
 """
 import dataclasses
 import json
@@ -28,6 +29,11 @@ def _f64(m, a):
     """A stored table / weight as float64 (exact)."""
     if isinstance(a, tuple):
         q, d = a
+        if m.lin == synth.LIN_Q4:  # two 4-bit codes per byte, even index low, value c - 8
+            c = np.empty((q.shape[0], 2 * q.shape[1]), np.float64)
+            c[:, 0::2] = q & 15
+            c[:, 1::2] = q >> 4
+            q = c - 8
         return (d.view(np.float16).astype(np.float64).repeat(32, axis=1) * q.astype(np.float64))
     if a.dtype == np.uint16:
         return synth.bf16_bits_to_f32(a).astype(np.float64)
@@ -228,8 +234,9 @@ def test_teacher_forcing_with_own_codes_is_free_run(tiny):
     assert np.array_equal(res["talker_logits"].view(np.uint32), out["talker_logits"].view(np.uint32))
 
 
-def test_q8_equals_dequantised_weights_bitwise():
-    base = dataclasses.replace(synth.TINY, model_id=11, lin=synth.LIN_Q8, tab_bf16=True,
+@pytest.mark.parametrize("lin,mid", [(synth.LIN_Q8, 11), (synth.LIN_Q4, 12)])
+def test_block_quant_equals_dequantised_weights_bitwise(lin, mid):
+    base = dataclasses.replace(synth.TINY, model_id=mid, lin=lin, tab_bf16=True,
                                kv_bf16=True, act_bf16=True)
     wq = synth.make_weights(base, random_q8_scales=True)
     deq = dataclasses.replace(base, lin=synth.LIN_F32)

@@ -252,6 +252,29 @@ def test_mm_q8_block_scales_closed_form():
         assert np.array_equal(out, ref)
 
 
+def test_mm_q4_codes_closed_form():
+    """4-bit blocks: code c of weight k sits in byte k/2 (low nibble for even
+    k) and stands for d * (c - 8); a swapped nibble, a wrong block or a missing
+    offset fails one of the one-hot columns."""
+    m = _model(lin=synth.LIN_Q4, act_bf16=False)
+    N, K = 3, 96
+    rng = np.random.default_rng(12)
+    c = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    c[0, :2] = (0, 15)  # the two extremes next to each other
+    packed = np.zeros((N, K // 2), np.uint8)
+    for n in range(N):
+        for k in range(K):
+            packed[n, k // 2] |= c[n, k] << (4 * (k % 2))
+    d = (rng.uniform(0.5, 1.5, (N, K // 32)) * 1e-3).astype(np.float16)
+    for k in (0, 1, 2, 31, 32, 33, 63, 95):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        out = _mm(m, packed, d.view(np.uint16), N, K, x)[0]
+        ref = d[:, k // 32].astype(np.float32) * (c[:, k].astype(np.float32) - 8)
+        assert np.array_equal(out, ref), k
+    assert _mm(m, packed, d.view(np.uint16), N, K, np.eye(1, K, 0, np.float32))[0, 0] == -8 * np.float32(d[0, 0])
+
+
 def test_argmax_lowest_index_on_ties():
     x = np.array([1.0, 5.0, 2.0, 5.0, 5.0], np.float32)
     assert lib.orc_prim_argmax(_p(x), 5) == 1 == int(np.argmax(x))
