@@ -142,9 +142,9 @@ const char *unsupported(const qt_model_desc &m) {
   if (d.Q != d.G) return "predictor_positions must equal codebooks";
   if (d.P < kTile || d.P % kTile) return "talker_positions must be a positive multiple of 256";
   if (d.Q > d.P) return "predictor_positions exceeds talker_positions";
-  if (m.lin_type < QT_LIN_F32 || m.lin_type > QT_LIN_Q8) return "unknown lin_type";
+  if (m.lin_type < QT_LIN_F32 || m.lin_type > QT_LIN_Q4) return "unknown lin_type";
   const int ch = m.lin_type == QT_LIN_F32 ? 4 : (m.lin_type == QT_LIN_BF16 ? 8 : 32);
-  if (d.H % ch || d.F % ch || d.qd % ch) return "hidden, ffn and n_q_heads*head_dim must be multiples of the weight chunk (4 f32, 8 bf16, 32 q8)";
+  if (d.H % ch || d.F % ch || d.qd % ch) return "hidden, ffn and n_q_heads*head_dim must be multiples of the weight chunk (4 f32, 8 bf16, 32 q8 / q4)";
   if (m.eps <= 0 || m.rope_theta <= 0) return "eps and rope_theta must be positive";
   return nullptr;
 }
@@ -210,7 +210,7 @@ int32_t fail(qt_ctx *c, int32_t code, const char *fmt, ...) {
 using namespace qtk;
 
 int wtype_of(const qt_model_desc &m) {
-  return m.lin_type == QT_LIN_F32 ? W_F32 : (m.lin_type == QT_LIN_BF16 ? W_BF16 : W_Q8);
+  return m.lin_type == QT_LIN_F32 ? W_F32 : m.lin_type == QT_LIN_BF16 ? W_BF16 : m.lin_type == QT_LIN_Q8 ? W_Q8 : W_Q4;
 }
 
 Lin lin(const qt_linear &l) { return Lin{l.w, (const uint16_t *)l.scales}; }
@@ -465,6 +465,7 @@ hipError_t enqueue_replay(qt_ctx *c) {
 const char *frame_unsupported(const qt_model_desc &m, int B) {
   const Dims d = dims_of(m);
   if (B != 1) return "the persistent kernel decodes one stream";
+  if (m.lin_type == QT_LIN_Q4) return "4-bit weights run on the per-op path";
   if (!qtk::frame_variant_supported(wtype_of(m), d.hd, d.nq / d.nkv, m.kv_bf16)) return "no persistent-kernel variant";
   if (m.lin_type != QT_LIN_F32 && !(m.act_bf16 && m.tab_bf16)) return "bf16/q8 weights need bf16 operands and tables";
   if (m.lin_type == QT_LIN_F32 && (m.act_bf16 || m.tab_bf16)) return "f32 weights need f32 operands and tables";
@@ -555,9 +556,9 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
   if (!w.code_emb || !w.text_emb || !w.talker || !w.talker_norm || !w.talker_head.w ||
       !w.predictor || !w.predictor_norm || !w.predictor_heads)
     return fail(nullptr, QT_E_ARG, "NULL weight pointer");
-  const bool q8 = m.lin_type == QT_LIN_Q8;
+  const bool blocked = m.lin_type == QT_LIN_Q8 || m.lin_type == QT_LIN_Q4;
   auto lin_ok = [&](const qt_linear &l) {
-    if (!l.w || (q8 && !l.scales)) return false;
+    if (!l.w || (blocked && !l.scales)) return false;
     if ((uintptr_t)l.w % 16) return false;  // 128-bit loads
     return true;
   };
@@ -923,7 +924,8 @@ int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, 
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (err != hipSuccess) return fail(c, QT_E_HIP, "qt_time_kernel: %s", hipGetErrorString(err));
-  const double wbytes = md.lin_type == QT_LIN_F32 ? 4.0 : (md.lin_type == QT_LIN_BF16 ? 2.0 : 34.0 / 32.0);
+  const double wbytes = md.lin_type == QT_LIN_F32 ? 4.0 : md.lin_type == QT_LIN_BF16 ? 2.0
+                        : md.lin_type == QT_LIN_Q8 ? 34.0 / 32.0 : 18.0 / 32.0;
   *avg_us = 1000.0 * ms / launches;
   *bytes = 2.0 * d.F * d.H * wbytes + 4.0 * c->B * (d.H + d.F);
   return QT_OK;

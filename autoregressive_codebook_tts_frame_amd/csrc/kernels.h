@@ -5,7 +5,10 @@
 
 namespace qtk {
 
-enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
+enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2, W_Q4 = 3 };
+// block formats carry one fp16 scale per 32 weights along K; Q4 packs two
+// 4-bit codes c per byte (even index in the low nibble), w = d * (c - 8)
+__host__ __device__ constexpr bool w_blocked(int wt) { return wt == W_Q8 || wt == W_Q4; }
 enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_GATED = 2 };
 
 // Row r of a step belongs to slot  slot_base + r / rows_per_slot  and sits at

@@ -60,7 +60,7 @@ __device__ __forceinline__ int row_pos(const RowMap &m, int r) {
 // ------------------------------------------------------------------ GEMV
 //
 // One wave computes RW output rows; its 64 lanes split K into 16-byte chunks
-// (8 bf16, 4 f32 or 16 int8 weights).  Activation rows are processed in
+// (8 bf16, 4 f32, 16 int8 or 32 4-bit weights: half a q8 block, one q4 block).  Activation rows are processed in
 // groups of up to 8 held in registers, so each weight chunk is loaded once per
 // group.
 
@@ -68,6 +68,7 @@ template <int WT> struct WT_;
 template <> struct WT_<W_F32> { static constexpr int CH = 4; };
 template <> struct WT_<W_BF16> { static constexpr int CH = 8; };
 template <> struct WT_<W_Q8> { static constexpr int CH = 16; };
+template <> struct WT_<W_Q4> { static constexpr int CH = 32; };
 
 // dot of one 16-byte weight chunk with CH activations
 template <int WT>
@@ -85,7 +86,7 @@ __device__ __forceinline__ float chunk_dot(const uint4 w, const float *xv, float
     s += bf16_lo(w.w) * xv[6];
     s += bf16_hi(w.w) * xv[7];
     return s;
-  } else {
+  } else if constexpr (WT == W_Q8) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     float s = 0.f;
 #pragma unroll
@@ -94,13 +95,28 @@ __device__ __forceinline__ float chunk_dot(const uint4 w, const float *xv, float
       for (int b = 0; b < 4; ++b) s += (float)(int8_t)(ws[i] >> (8 * b)) * xv[4 * i + b];
     }
     return s * scale;
+  } else {
+    // nibble b of word i is weight 8 i + b
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) s += (float)((int)((ws[i] >> (4 * b)) & 15u) - 8) * xv[8 * i + b];
+    }
+    return s * scale;
   }
+}
+
+// bytes of one weight row of K weights (block scales are stored apart)
+template <int WT>
+__device__ __forceinline__ size_t row_bytes(int K) {
+  return WT == W_F32 ? (size_t)K * 4 : WT == W_BF16 ? (size_t)K * 2 : WT == W_Q8 ? (size_t)K : (size_t)K / 2;
 }
 
 template <int WT>
 __device__ __forceinline__ const uint8_t *row_ptr(const Lin &L, int n, int K) {
-  constexpr size_t esz = WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1);
-  return (const uint8_t *)L.w + (size_t)n * K * esz;
+  return (const uint8_t *)L.w + (size_t)n * row_bytes<WT>(K);
 }
 
 template <int WT, int EPI, int RW>
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       for (int r = 0; r < NW; ++r) {
         wv[r] = *(const uint4 *)(wp[r] + (size_t)c * 16);
         scl[r] = 1.f;
-        if constexpr (WT == W_Q8) scl[r] = f16_to_f32(sp[r][k0 / 32]);
+        if constexpr (w_blocked(WT)) scl[r] = f16_to_f32(sp[r][k0 / 32]);
       }
       float g[CH];
       if (a.gain) {
@@ -265,7 +281,9 @@ static hipError_t gemv_epi(int epi, const GemvArgs &a, hipStream_t s) {
 hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s) {
   if (wtype == W_F32) return gemv_epi<W_F32>(epi, a, s);
   if (wtype == W_BF16) return gemv_epi<W_BF16>(epi, a, s);
-  return gemv_epi<W_Q8>(epi, a, s);
+  if (wtype == W_Q8) return gemv_epi<W_Q8>(epi, a, s);
+  if (wtype == W_Q4) return gemv_epi<W_Q4>(epi, a, s);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------ q/k norm + RoPE + set_rows
@@ -752,7 +770,6 @@ constexpr int GXS = GBK + 8;  // LDS row stride (bf16) of the staged operand: co
 // before the first weight load could issue.
 template <int WT>
 __device__ __forceinline__ const uint8_t *gemm_row(const GemmArgs &a, int mat, int n, const uint16_t *&sc) {
-  constexpr size_t esz = WT == W_BF16 ? 2 : 1;
   const void *w = a.up.w;
   const uint16_t *scb = a.up.sc;
   int r = n;
@@ -764,12 +781,39 @@ __device__ __forceinline__ const uint8_t *gemm_row(const GemmArgs &a, int mat, i
     r = n - (s2 ? a.seg_end[1] : s1 ? a.seg_end[0] : 0);
   }
   sc = scb ? scb + (size_t)r * (a.K / 32) : nullptr;
-  return (const uint8_t *)w + (size_t)r * a.K * esz;
+  return (const uint8_t *)w + (size_t)r * row_bytes<WT>(a.K);
 }
 
 __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int b) {
   const float lo = (float)(int8_t)(w >> (8 * b)), hi = (float)(int8_t)(w >> (8 * b + 8));
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// 4-bit codes b and b + 1 of w as a bf16 pair (c - 8 is exact in bf16)
+__device__ __forceinline__ uint32_t q4pair_bf16(uint32_t w, int b) {
+  const float lo = (float)((int)((w >> (4 * b)) & 15u) - 8), hi = (float)((int)((w >> (4 * b + 4)) & 15u) - 8);
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// a lane's 8 consecutive weights of one 32-wide step: 16 bytes of bf16, 8 of
+// int8 or 4 of 4-bit codes, and the same 8 as the MFMA's bf16 operand (block
+// formats unscaled: the scale is applied to the product)
+template <int WT> struct GemmW;
+template <> struct GemmW<W_BF16> { typedef uint4 V; };
+template <> struct GemmW<W_Q8> { typedef uint2 V; };
+template <> struct GemmW<W_Q4> { typedef uint32_t V; };
+
+template <int WT>
+__device__ __forceinline__ bf16x8_t gemm_w_bf16(const typename GemmW<WT>::V w) {
+  if constexpr (WT == W_BF16) {
+    return __builtin_bit_cast(bf16x8_t, w);
+  } else if constexpr (WT == W_Q8) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(i8pair_bf16(w.x, 0), i8pair_bf16(w.x, 2),
+                                                   i8pair_bf16(w.y, 0), i8pair_bf16(w.y, 2)));
+  } else {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(q4pair_bf16(w, 0), q4pair_bf16(w, 2),
+                                                   q4pair_bf16(w, 4), q4pair_bf16(w, 6)));
+  }
 }
 
 // split-K partials are written and read back with 16-byte buffer accesses at
@@ -798,7 +842,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * GXS];
   __shared__ float rinv[64];
   __shared__ float gs[GBK];
-  __shared__ float scl[WT == W_Q8 ? NSUB * 16 * NBLK : 1];
+  __shared__ float scl[w_blocked(WT) ? NSUB * 16 * NBLK : 1];
   __shared__ __attribute__((aligned(16))) f32x4_t red[WPB > 1 ? 4 * 64 * (NSUB * (WPB - 1)) : 1];
   __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -843,7 +887,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int NSC = NSUB * 16 * NBLK / 256;  // q8 scales per thread
   static_assert(NSUB * 16 * NBLK % 256 == 0 && 64 % NBLK == 0, "a wave's scales lie in one weight block");
   uint16_t sv[NSC];
-  if constexpr (WT == W_Q8) {
+  if constexpr (w_blocked(WT)) {
     // entry e: tile row r = e / NBLK (block r / 16, row r % 16 of it), scale
     // block e % NBLK; a wave's 64 entries are rows of one block
 #pragma unroll
@@ -856,7 +900,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       sv[q] = sp[(size_t)(r % 16) * (K / 32) + k0 / 32 + b];
     }
   }
-  typedef typename std::conditional<WT == W_BF16, uint4, uint2>::type WVec;
+  typedef typename GemmW<WT>::V WVec;
   WVec wv[SPW];
   {
     // the block's 16 rows lie in one segment (segment ends are multiples of 16)
@@ -864,12 +908,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const uint16_t *sc;
     const uint8_t *wr = gemm_row<WT>(a, __builtin_amdgcn_readfirstlane(mat), n0, sc);
     const int n = n0 + (lane & 15);  // the weight row this lane loads
-    constexpr size_t esz = WT == W_BF16 ? 2 : 1;
-    wr += (size_t)(n < N ? lane & 15 : 0) * K * esz;
+    wr += (size_t)(n < N ? lane & 15 : 0) * row_bytes<WT>(K);
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const int k = k0 + (kq * SPW + s) * 32 + (lane >> 4) * 8;
-      wv[s] = *(const WVec *)(wr + (size_t)k * esz);
+      wv[s] = *(const WVec *)(wr + row_bytes<WT>(k));
     }
   }
 
@@ -883,7 +926,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   sq += __shfl_xor(sq, 2, 64);
   if (sq4 == 0) rinv[sm] = a.gain ? 1.0f / sqrtf(sq / (float)K + a.eps) : 1.f;
   gs[tid] = !a.gain ? 1.f : __uint_as_float(a.gain_bf16 ? (uint32_t)glo << 16 : ((uint32_t)ghi << 16) | glo);
-  if constexpr (WT == W_Q8)
+  if constexpr (w_blocked(WT))
 #pragma unroll
     for (int q = 0; q < NSC; ++q) scl[tid + 256 * q] = f16_to_f32(sv[q]);
   __syncthreads();
@@ -920,14 +963,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int kl = (kq * SPW + s) * 32;  // step's offset in the slice
-    bf16x8_t av;
-    if constexpr (WT == W_BF16) {
-      av = __builtin_bit_cast(bf16x8_t, wv[s]);
-    } else {
-      const uint4 wq = make_uint4(i8pair_bf16(wv[s].x, 0), i8pair_bf16(wv[s].x, 2), i8pair_bf16(wv[s].y, 0),
-                                  i8pair_bf16(wv[s].y, 2));
-      av = __builtin_bit_cast(bf16x8_t, wq);
-    }
+    const bf16x8_t av = gemm_w_bf16<WT>(wv[s]);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= MT) break;
@@ -1028,14 +1064,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
         const int kl = (kq * SPW + s) * 32;
-        bf16x8_t av;
-        if constexpr (WT == W_BF16) {
-          av = __builtin_bit_cast(bf16x8_t, wv[s]);
-        } else {
-          const uint4 wq = make_uint4(i8pair_bf16(wv[s].x, 0), i8pair_bf16(wv[s].x, 2), i8pair_bf16(wv[s].y, 0),
-                                      i8pair_bf16(wv[s].y, 2));
-          av = __builtin_bit_cast(bf16x8_t, wq);
-        }
+        const bf16x8_t av = gemm_w_bf16<WT>(wv[s]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           if (mt >= MT1) break;
@@ -1174,6 +1203,7 @@ hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
     if (a.seg_end[i] % 16) return hipErrorInvalidValue;
   if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);
   if (wtype == W_Q8) return gemm_wt<W_Q8>(epi, a, s);
+  if (wtype == W_Q4) return gemm_wt<W_Q4>(epi, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -24,7 +24,7 @@ QT_ABI_VERSION = 2
 QT_OK = 0
 QT_E_ABI, QT_E_ARG, QT_E_SIZE, QT_E_RANGE = -1, -2, -3, -4
 QT_E_STATE, QT_E_CONTEXT_FULL, QT_E_HIP, QT_E_UNSUPPORTED = -5, -6, -7, -8
-QT_LIN_F32, QT_LIN_BF16, QT_LIN_Q8 = 0, 1, 2
+QT_LIN_F32, QT_LIN_BF16, QT_LIN_Q8, QT_LIN_Q4 = 0, 1, 2, 3
 QT_F_DUMP, QT_F_EAGER, QT_F_OPS, QT_F_TRACE = 1, 2, 4, 8
 QT_PATH_FRAME, QT_PATH_GRAPH, QT_PATH_EAGER = 1, 2, 3
 (QT_DUMP_TALKER_LOGITS, QT_DUMP_PRED_LOGITS, QT_DUMP_BRIDGE, QT_DUMP_X0, QT_DUMP_GATHER,

@@ -52,6 +52,12 @@ extern "C" {
 #define QT_LIN_F32 0
 #define QT_LIN_BF16 1
 #define QT_LIN_Q8 2 /* int8 values [N][K] + fp16 scale per 32 along K: [N][K/32] */
+/* 4-bit blocks of this library's own definition (the qwentts.cpp commit log's
+   TTFA table lists a 4-bit column but defines no block): uint8 [N][K/2], weight
+   k in byte k/2, low nibble for even k, code c in 0..15 standing for c - 8; fp16
+   scale d per 32 along K: [N][K/32]; w = d * (c - 8).  Decoded on the per-op
+   path at any batch size (the persistent frame kernel does not take it). */
+#define QT_LIN_Q4 3
 
 /* context flags */
 #define QT_F_DUMP 1u  /* keep per-step readbacks (logits, bridge, gather ids, hidden) */
@@ -83,8 +89,8 @@ typedef struct qt_model_desc {
 } qt_model_desc;
 
 typedef struct qt_linear {
-  const void *w;      /* device: f32 / bf16 [N][K], or int8 [N][K] for QT_LIN_Q8 */
-  const void *scales; /* device: QT_LIN_Q8 only, fp16 bits [N][K/32]; else NULL */
+  const void *w;      /* device: f32 / bf16 [N][K], int8 [N][K] (QT_LIN_Q8) or uint8 [N][K/2] (QT_LIN_Q4) */
+  const void *scales; /* device: QT_LIN_Q8 / QT_LIN_Q4 only, fp16 bits [N][K/32]; else NULL */
 } qt_linear;
 
 /* One decoder layer (pre-norm; [MC-opt] core table: residual add + RMSNorm,

@@ -96,6 +96,18 @@ def test_unsupported_shapes_and_bad_sizes():
         assert e.value.code == qt.QT_E_ARG
 
 
+def test_block_formats_need_scales_and_whole_blocks():
+    # a 4-bit model is accepted by the size query; its hidden width must hold whole
+    # 32-weight blocks, and the persistent kernel leaves it to the per-op path
+    qt.qt_query_sizes(qt.model_desc(synth.BIG_Q4), 1)
+    with pytest.raises(qt.QtError) as e:
+        qt.qt_query_sizes(qt.model_desc(dataclasses.replace(synth.BIG_Q4, F=3072 + 16)), 1)
+    assert e.value.code == qt.QT_E_UNSUPPORTED
+    with pytest.raises(qt.QtError) as e:
+        qt.qt_query_sizes(qt.model_desc(dataclasses.replace(synth.BIG_Q4, lin=4)), 1)
+    assert e.value.code == qt.QT_E_UNSUPPORTED
+
+
 def test_null_context_calls_fail_cleanly():
     assert qt.lib.qt_prefill(None, 0, 1, None, None) == qt.QT_E_ARG
     assert qt.lib.qt_decode_frame(None, 1, None, None, None) == qt.QT_E_ARG

@@ -3,7 +3,7 @@ same seeded inputs.  Marked gpu; run on an MI355X.
 
 Sizes: the tiny F32 model (several GEMV tiles per matrix, a ragged 16-row
 prompt against 32-row prefill chunks), a reduced model at the full 1024/3072
-widths, and the full 28-layer BF16 / Q8 models at their real shapes."""
+widths, and the full 28-layer BF16 / Q8 / Q4 models at their real shapes."""
 import dataclasses
 import sys
 
@@ -487,6 +487,39 @@ def test_reduced_q8_batched_parity():
     wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
     say("[reduced q8 batched] 3 frames, batch 8")
     _check(_forced_run(m, w, wl, 3, batch=8), m, "reduced_q8_b8")
+
+
+def test_reduced_q4_parity():
+    # 4-bit blocks run on the per-op path: one and two streams on the GEMV,
+    # a 358-row prompt's prefill chunks (128, 128, 102 rows) on the MFMA GEMM
+    m = _reduced(synth.BIG_Q4)
+    w = synth.make_weights(m, random_q8_scales=True)
+    wl = dataclasses.replace(synth.WORKLOADS["q4_b1"], model=m, prompt=358)
+    for batch in (1, 2):
+        say(f"[reduced q4 random scales] prompt 358, 4 frames, batch {batch}")
+        r = _forced_run(m, w, wl, 4, batch=batch)
+        assert r["d"].path == qt.QT_PATH_GRAPH
+        _check(r, m, f"reduced_q4_b{batch}")
+
+
+def test_reduced_q4_batched_parity():
+    m = _reduced(synth.BIG_Q4)
+    w = synth.make_weights(m, random_q8_scales=True)
+    wl = dataclasses.replace(synth.WORKLOADS["q4_b8"], model=m, prompt=40)
+    say("[reduced q4 batched] 3 frames, batch 8")
+    _check(_forced_run(m, w, wl, 3, batch=8), m, "reduced_q4_b8")
+    say("[reduced q4 batched sampled] 3 frames, batch 8, T = 0.8")
+    _check(_forced_run(m, w, wl, 3, batch=8, sampler=(0.8, 7)), m, "reduced_q4_b8_sampled")
+
+
+@pytest.mark.timeout(900)
+def test_full_q4_b1_parity():
+    m = synth.BIG_Q4
+    wl = synth.WORKLOADS["q4_b1"]
+    say("[q4_b1] weights")
+    w = synth.make_weights(m)
+    say("[q4_b1] prefill 128 + 4 frames")
+    _check(_forced_run(m, w, wl, 4), m, "q4_b1")
 
 
 @pytest.mark.timeout(900)
