@@ -256,18 +256,17 @@ Stack pred_stack(const qt_ctx *c) {
 }
 
 // One decoder layer over M rows (x in the arena's activation rows).
-// Batched rows (4..128, bf16 or q8 weights with bf16 operands) go through the
-// MFMA GEMM; fewer rows through the GEMV.  Q4 weights take the GEMM from one
-// row: a 1,024-wide Q4 row is only 32 of the GEMV's 16-byte chunks, half a
-// wave, while the GEMM spreads each row's K over its split-K workgroups.  All
+// With bf16, q8 or q4 weights and bf16 operands, every projection of 1..128
+// rows goes through the split-K MFMA GEMM: even at one row it spreads each
+// weight row's K over its workgroups, where the GEMV gives a row to one wave
+// (a 1,024-wide q4 row fills only half of it).  F32 models use the GEMV.  All
 // projections of one layer see the same M, so a layer runs entirely on one of
 // the two.
 bool use_gemm(const qt_ctx *c, int M, int K) {
   const qt_model_desc &md = c->md;
   const Dims &d = c->d;
-  const int min_rows = md.lin_type == QT_LIN_Q4 ? 1 : 4;
-  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= min_rows && M <= 128 && K % 256 == 0 &&
-         d.H % 32 == 0 && d.nqkv % 32 == 0 && d.F % 32 == 0 && d.Vc % 32 == 0;
+  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 1 && M <= 128 && K % 256 == 0 && d.H % 32 == 0 &&
+         d.nqkv % 32 == 0 && d.F % 32 == 0 && d.Vc % 32 == 0;
 }
 
 // One projection.  ssq_in: the input rows' sums of squares in 32-column slots

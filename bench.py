@@ -257,7 +257,7 @@ def main():
     else:
         # dominant kernel: the gate/up GEMV, timed live with HIP events on the
         # library's stream over every layer's weights
-        batched = (B >= 4 or m.lin == 3) and m.lin != 0 and m.act_bf16  # q4 takes the GEMM from one row
+        batched = m.lin != 0 and m.act_bf16  # bf16 / q8 / q4 projections take the GEMM at any row count
         kname = ("gemm_kernel<gated> (MFMA: RMSNorm + gate/up + SiLU-mul, %d rows)" % B if batched
                  else "gemv_kernel<gated> (RMSNorm + gate/up + SiLU-mul)")
         us, kbytes = d.time_kernel(qt.QT_KERNEL_GEMV_GATE_UP, 3)
