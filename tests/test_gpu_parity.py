@@ -364,6 +364,16 @@ def test_tiny_errors_leave_state_unchanged(tiny):
     with pytest.raises(qt.QtError) as e:
         d.decode(m.P, np.zeros((m.P, 1), np.int32))
     assert e.value.code == qt.QT_E_CONTEXT_FULL
+    # empty calls and a prompt longer than the ring are refused before any launch
+    with pytest.raises(qt.QtError) as e:
+        d.decode(0, np.zeros((0, 1), np.int32))
+    assert e.value.code == qt.QT_E_ARG
+    with pytest.raises(qt.QtError) as e:
+        d.prefill(0, np.zeros((0, m.G), np.int32), np.zeros((0,), np.int32))
+    assert e.value.code == qt.QT_E_ARG
+    with pytest.raises(qt.QtError) as e:
+        d.prefill(0, np.zeros((m.P + 1, m.G), np.int32), np.zeros((m.P + 1,), np.int32))
+    assert e.value.code == qt.QT_E_CONTEXT_FULL
     assert d.get_state(0)[0] == len(t)
     assert np.array_equal(d.decode(8, r["ov"]), r["oout"]["codes"])
 
