@@ -470,7 +470,7 @@ const char *frame_unsupported(const qt_model_desc &m, int B) {
   if (B != 1) return "the persistent kernel decodes one stream";
   if (m.lin_type == QT_LIN_Q4) return "4-bit weights run on the per-op path";
   if (!qtk::frame_variant_supported(wtype_of(m), d.hd, d.nq / d.nkv, m.kv_bf16)) return "no persistent-kernel variant";
-  if (m.lin_type != QT_LIN_F32 && !(m.act_bf16 && m.tab_bf16)) return "bf16/q8 weights need bf16 operands and tables";
+  if (m.lin_type != QT_LIN_F32 && !(m.act_bf16 && m.tab_bf16)) return "bf16/q8/q4 weights need bf16 operands and tables";
   if (m.lin_type == QT_LIN_F32 && (m.act_bf16 || m.tab_bf16)) return "f32 weights need f32 operands and tables";
   return nullptr;
 }

@@ -22,7 +22,7 @@ struct RowMap {
 
 struct Lin {
   const void *w;
-  const uint16_t *sc;  // Q8 scales (fp16 bits), else null
+  const uint16_t *sc;  // Q8 / Q4 block scales (fp16 bits), else null
 };
 
 // y[m][n] (epilogue) sum_k W[n][k] * x~[m][k]
@@ -142,7 +142,7 @@ struct ArgmaxArgs {
 };
 
 // Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 128 rows (two 64-row halves),
-// bf16 or q8 weights with bf16 operands.  Tiles of 32 output columns (gated:
+// bf16, q8 or q4 weights with bf16 operands.  Tiles of 32 output columns (gated:
 // 32 gate + 32 up rows) x all rows x 256-wide K slices; the last workgroup of
 // a tile to finish sums the K slices' partials in order and applies the
 // epilogue.

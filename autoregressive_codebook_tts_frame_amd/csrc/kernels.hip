@@ -60,9 +60,9 @@ __device__ __forceinline__ int row_pos(const RowMap &m, int r) {
 // ------------------------------------------------------------------ GEMV
 //
 // One wave computes RW output rows; its 64 lanes split K into 16-byte chunks
-// (8 bf16, 4 f32, 16 int8 or 32 4-bit weights: half a q8 block, one q4 block).  Activation rows are processed in
-// groups of up to 8 held in registers, so each weight chunk is loaded once per
-// group.
+// (8 bf16, 4 f32, 16 int8 or 32 4-bit weights: half a q8 block, one q4
+// block).  Activation rows are processed in groups of up to 8 held in
+// registers, so each weight chunk is loaded once per group.
 
 template <int WT> struct WT_;
 template <> struct WT_<W_F32> { static constexpr int CH = 4; };
@@ -750,8 +750,9 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
 // ------------------------------------------------------------------ batched projections (MFMA)
 //
 // y[M][N] = epi(x~ . W^T) for M <= 128 rows (in 64-row halves): x~ = bf16(x * rinv * gain) (or
-// bf16(x)); weight rows in their storage format (bf16, or q8 converted exactly
-// to bf16 with the 32-wide block scale applied to each block's product).
+// bf16(x)); weight rows in their storage format (bf16, or q8 / q4 codes
+// converted exactly to bf16 with the 32-wide block scale applied to each
+// block's product).
 // v_mfma_f32_16x16x32_bf16 lane layout (checked on the device): A[16][32]
 // row l%16, k (l/16)*8..+8; B[32][16] k (l/16)*8..+8, column l%16; D[16][16]
 // c[j] at row (l/16)*4+j, column l%16.  A = 16 weight rows, B = 16 activation
@@ -838,7 +839,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int NSUB = EPI == EPI_GATED ? 4 : 2;
   constexpr int WPB = 4 / NSUB;
   constexpr int SPW = GBK / 32 / WPB;
-  constexpr int NBLK = GBK / 32;  // q8 scale blocks per weight row in the slice
+  constexpr int NBLK = GBK / 32;  // q8 / q4 scale blocks per weight row in the slice
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * GXS];
   __shared__ float rinv[64];
   __shared__ float gs[GBK];
@@ -860,7 +861,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // Loads first, in the order they are consumed, so that waiting for the
   // operand does not wait for the weights: the rows' sums of squares (thread
   // t sums row t / 4's slots t % 4, t % 4 + 4, ...), the gain, the operand
-  // slice (eight columns per item), q8 scales, then the weights.  Every load
+  // slice (eight columns per item), block scales, then the weights.  Every load
   // is unconditional, from a clamped in-bounds address, and masked where it is
   // used: a load under a branch makes the compiler wait for it at the join.
   const int sm = tid >> 2, sq4 = tid & 3;
@@ -884,7 +885,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     xv[it][0] = *(const float4 *)xr;
     xv[it][1] = *(const float4 *)(xr + 4);
   }
-  constexpr int NSC = NSUB * 16 * NBLK / 256;  // q8 scales per thread
+  constexpr int NSC = NSUB * 16 * NBLK / 256;  // block scales per thread
   static_assert(NSUB * 16 * NBLK % 256 == 0 && 64 % NBLK == 0, "a wave's scales lie in one weight block");
   uint16_t sv[NSC];
   if constexpr (w_blocked(WT)) {
@@ -916,7 +917,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
   }
 
-  // RMSNorm row scales, gain and q8 scales to LDS
+  // RMSNorm row scales, gain and block scales to LDS
   float sq = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) sq += norm_row && sq4 + 4 * i < K / 32 ? sqv[i] : 0.f;
