@@ -522,6 +522,22 @@ def test_reduced_q4_batched_parity():
     _check(_forced_run(m, w, wl, 3, batch=8, sampler=(0.8, 7)), m, "reduced_q4_b8_sampled")
 
 
+@pytest.mark.parametrize("base", [synth.BIG, synth.BIG_Q8, synth.BIG_Q4], ids=["bf16", "q8", "q4"])
+def test_gemv_widths_parity(base):
+    # hidden 320 and ffn 960 (not multiples of the GEMM's 256-wide K slice):
+    # every projection over them runs on the GEMV, the O projection
+    # (K = 2,048) on the GEMM, at one and two streams; the persistent kernel
+    # does not take 640-byte rows, so the per-op path decodes
+    m = dataclasses.replace(base, Lt=2, Lp=1, Vt=4096, P=512, model_id=base.model_id + 30, H=320, F=960)
+    w = synth.make_weights(m, random_q8_scales=True)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b1"], model=m, prompt=40)
+    for batch in (1, 2):
+        say(f"[gemv widths {base.name}] H 320, F 960, prompt 40, 3 frames, batch {batch}")
+        r = _forced_run(m, w, wl, 3, batch=batch)
+        assert r["d"].path == qt.QT_PATH_GRAPH
+        _check(r, m, f"gemv_widths_{base.name}_b{batch}")
+
+
 @pytest.mark.timeout(900)
 def test_full_q4_b1_parity():
     m = synth.BIG_Q4
