@@ -236,8 +236,9 @@ int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
      QT_KERNEL_GEMV_GATE_UP   RMSNorm + gate/up projection + SiLU-multiply (the
                               largest weight stream of a layer) as the per-op
                               decode path runs it for the context's batch: the
-                              GEMV for up to 3 rows, the split-K MFMA GEMM for
-                              4..128 rows (bf16 / q8 weights)
+                              split-K MFMA GEMM for 1..128 rows with bf16, q8 or
+                              q4 weights, the GEMV for f32 weights or widths the
+                              GEMM does not take
    Errors: QT_E_ARG, QT_E_HIP, QT_E_UNSUPPORTED. */
 #define QT_KERNEL_GEMV_GATE_UP 1
 int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us,
