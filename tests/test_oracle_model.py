@@ -146,7 +146,11 @@ def test_predictor_matches_hf_qwen3(tiny):
 
 
 def test_bf16_model_tracks_float64_reference():
-    """The BF16 storage/rounding policy only perturbs values by bf16 rounding."""
+    """The BF16 storage/rounding policy perturbs values by bf16 rounding only:
+    against HF's float64 Qwen3 with no rounding at all, the talker logits sit
+    at ~3e-3 (operand and K/V roundings of relative size 2^-9).  The policy
+    itself -- where each rounding happens -- is pinned tightly in
+    test_oracle_bf16_policy.py."""
     m = dataclasses.replace(synth.TINY, model_id=10, lin=synth.LIN_BF16, tab_bf16=True,
                             kv_bf16=True, act_bf16=True)
     w = synth.make_weights(m)
@@ -159,7 +163,7 @@ def test_bf16_model_tracks_float64_reference():
     logits = hid @ _f64(m, w["t_head"]).T
     for f in range(2):
         e = rel_l2(out["talker_logits"][f, 0], logits[T + f])
-        assert 1e-5 < e < 3e-2, e  # rounded (so not F32-exact) but close
+        assert 5e-4 < e < 1e-2, e  # rounded (so not F32-exact) but close
 
 
 def test_cached_decode_equals_full_recompute_bitwise():
