@@ -41,6 +41,7 @@ struct Layout {
   // persistent frame kernel: weight tables, tagged exchange words, error flag
   size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_part, f_err, f_trace;
   size_t xch_words;  // words between copies of the exchange rows
+  size_t f_xch_begin;
   size_t total;
   int32_t rows;       // activation rows held
   int32_t max_tiles;  // talker attention tiles
@@ -109,6 +110,7 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   // rows every GEMV workgroup reads (residual, attention output, SiLU-mul
   // output) exist kXchRep times, one copy per group of readers
   L.xch_words = 2 * (size_t)d.H + 2 * (size_t)d.qd + 2 * (size_t)d.F + 32;
+  L.f_xch_begin = off;  // every tagged exchange word lies in [f_xch_begin, f_err)
   L.f_xq = take(8 * kXchRep * L.xch_words);
   L.f_o = L.f_xq + 8 * 2 * (size_t)d.H;
   L.f_z = L.f_o + 8 * 2 * (size_t)d.qd;
@@ -259,22 +261,24 @@ Stack pred_stack(const qt_ctx *c) {
 // With bf16, q8 or q4 weights and bf16 operands, every projection of 1..128
 // rows goes through the split-K MFMA GEMM: even at one row it spreads each
 // weight row's K over its workgroups, where the GEMV gives a row to one wave
-// (a 1,024-wide q4 row fills only half of it).  F32 models use the GEMV.  All
-// projections of one layer see the same M, so a layer runs entirely on one of
-// the two.
-bool use_gemm(const qt_ctx *c, int M, int K) {
-  const qt_model_desc &md = c->md;
-  const Dims &d = c->d;
-  return md.lin_type != QT_LIN_F32 && md.act_bf16 && M >= 1 && M <= 128 && K % 256 == 0 && d.H % 32 == 0 &&
-         d.nqkv % 32 == 0 && d.F % 32 == 0 && d.Vc % 32 == 0;
+// (a 1,024-wide q4 row fills only half of it).  F32 models use the GEMV.
+// The choice is made once per model, never per projection: the GEMM's
+// RMSNorm reads the row sums of squares that the GEMM's residual epilogues
+// (and the gather / argmax kernels) leave, which the GEMV's residual epilogue
+// does not write, so a model whose hidden, attention or FFN width is not a
+// multiple of the GEMM's 256-wide K slice runs every projection on the GEMV.
+bool model_uses_gemm(const qt_model_desc &md, const Dims &d) {
+  return md.lin_type != QT_LIN_F32 && md.act_bf16 && d.H % 256 == 0 && d.qd % 256 == 0 && d.F % 256 == 0 &&
+         d.nqkv % 32 == 0 && d.Vc % 32 == 0;
 }
+bool use_gemm(const qt_ctx *c, int M) { return model_uses_gemm(c->md, c->d) && M >= 1 && M <= 128; }
 
 // One projection.  ssq_in: the input rows' sums of squares in 32-column slots
 // (row m at ssq_in + m * ssq_stride), needed by the GEMM's RMSNorm; ssq_out:
 // where a residual epilogue leaves the new rows' sums.
 hipError_t project(qt_ctx *c, int epi, const GemvArgs &g, const float *ssq_in, int ssq_stride, float *ssq_out) {
   const int wt = wtype_of(c->md);
-  if (!use_gemm(c, g.M, g.K)) return launch_gemv(wt, epi, g, c->stream);
+  if (!use_gemm(c, g.M)) return launch_gemv(wt, epi, g, c->stream);
   GemmArgs a = {};
   for (int i = 0; i < 3; ++i) { a.seg[i] = g.seg[i]; a.seg_end[i] = g.seg_end[i]; }
   a.nseg = g.nseg; a.up = g.up;
@@ -475,6 +479,9 @@ const char *frame_unsupported(const qt_model_desc &m, int B) {
   return nullptr;
 }
 
+int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
+                      const int32_t *forced);
+
 bool ids_ok(const int32_t *p, size_t n, int32_t hi) {
   for (size_t i = 0; i < n; ++i)
     if (p[i] < 0 || p[i] >= hi) return false;
@@ -650,7 +657,8 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
-        ncu > 0 && ncu <= kMaxWG && (fa.nwg = ncu, qtk::frame_plan(fa, d.P - 1, lds, &why))) {
+        ncu > 0 && ncu <= kMaxWG && (fa.nwg = ncu, qtk::frame_plan(fa, d.P - 1, lds, &why)) &&
+        qtk::frame_coresident(fa, ncu)) {
       c->lds_limit = lds;
       fa.eps = (float)m.eps; fa.scale = (float)(1.0 / sqrt((double)d.hd));
       // device-side weight tables
@@ -720,6 +728,9 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
   if (codes && !ids_ok(codes, (size_t)T * d.G, d.Vc)) return fail(c, QT_E_RANGE, "code id outside [0, %d)", d.Vc);
 
   hipStream_t s = c->stream;
+  // from the first launch on the slot's ring rows change: it counts as
+  // prefilled again only once the whole prompt has run
+  c->ready[slot] = 0;
   int32_t *pf_codes = c->A<int32_t>(c->L.pf_codes), *pf_text = c->A<int32_t>(c->L.pf_text);
   int32_t *up_text = c->pin_up + c->pu_pf_text, *up_codes = c->pin_up + c->pu_pf_codes;
   memcpy(up_text, text_ids, sizeof(int32_t) * T);
@@ -781,6 +792,22 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
   if (!ids_ok(overlay_ids, (size_t)n * B, d.Vt)) return fail(c, QT_E_RANGE, "overlay id outside [0, %d)", d.Vt);
   if (forced && !ids_ok(forced, (size_t)n * B * d.G, d.Vc)) return fail(c, QT_E_RANGE, "forced code outside [0, %d)", d.Vc);
 
+  const int32_t rc = decode_chunks(c, n, overlay_ids, codes_out, forced);
+  if (rc == QT_E_HIP)
+    // work was launched: the slots may hold partial results (ring rows,
+    // bridge, position), so they must be restored before the next decode
+    for (int b = 0; b < B; ++b) c->ready[b] = 0;
+  return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
+                      const int32_t *forced) {
+  const Dims &d = c->d;
+  const int B = c->B;
   hipStream_t s = c->stream;
   int32_t *ctl = c->A<int32_t>(c->L.ctl);
   for (int f0 = 0; f0 < n; f0 += c->maxF) {
@@ -813,13 +840,20 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
       const char *why = nullptr;
       if (!qtk::frame_plan(fa, fa.pos0 + nf - 1, c->lds_limit, &why))
         return fail(c, QT_E_UNSUPPORTED, "frame kernel plan: %s", why);
+      // Tags are only ever compared for equality, and each launch numbers
+      // fewer than 1024 phases per frame.  When the 32-bit tag space would
+      // wrap, every exchange word is cleared (tag 0, which no phase uses)
+      // and numbering restarts: no word can then carry a tag of the coming
+      // launch before that launch writes it.
+      const uint64_t span = (uint64_t)nf * 1024u + 16u;
+      if ((uint64_t)c->tag_base + span > 0xffffffffull) {
+        HIPCHK(c, hipMemsetAsync(c->arena + c->L.f_xch_begin, 0, c->L.f_err - c->L.f_xch_begin, s));
+        c->tag_base = 16u;
+      }
       fa.tag_base = c->tag_base;
       fa.inv_temp = c->inv_temp;
       fa.seed = c->seed;
-      // tags are only ever compared for equality: advance past every phase
-      // this launch can number (< 1024 per frame)
-      c->tag_base += (uint32_t)nf * 1024u + 16u;
-      if (c->tag_base < 16u) c->tag_base = 16u;
+      c->tag_base += (uint32_t)span;
       HIPCHK(c, launch_frame_kernel(fa, s));
     } else {
       for (int r = 0; r < nf / c->K; ++r) {
@@ -833,12 +867,18 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
     if (c->path == QT_PATH_FRAME)
       HIPCHK(c, hipMemcpyAsync(errh, c->fa.err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
     HIPCHK(c, hipStreamSynchronize(s));
-    if (errh[0]) return fail(c, QT_E_HIP, "frame kernel: an exchange wait timed out (decode state is undefined)");
+    if (errh[0])
+      return fail(c, QT_E_HIP, "frame kernel: an exchange wait timed out (the slot must be restored by "
+                                "qt_prefill or qt_set_slot_state)");
     memcpy(codes_out + (size_t)f0 * B * d.G, c->pin_down, sizeof(int32_t) * nf * B * d.G);
     for (int b = 0; b < B; ++b) c->pos_host[b] += nf;
   }
   return QT_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int32_t qt_get_slot_state(qt_ctx *c, int32_t slot, int32_t *pos, int32_t *c0, float *bridge) {
   if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
@@ -856,6 +896,7 @@ int32_t qt_set_slot_state(qt_ctx *c, int32_t slot, int32_t pos, int32_t c0, cons
   if (slot < 0 || slot >= c->B || !bridge) return fail(c, QT_E_ARG, "bad slot or NULL bridge");
   if (pos < 1 || pos > c->d.P) return fail(c, QT_E_RANGE, "pos %d outside [1, %d]", pos, c->d.P);
   if (c0 < 0 || c0 >= c->d.Vc) return fail(c, QT_E_RANGE, "c0 %d outside [0, %d)", c0, c->d.Vc);
+  c->ready[slot] = 0;  // until every part of the state is written
   HIPCHK(c, hipStreamSynchronize(c->stream));
   HIPCHK(c, hipMemcpy(c->A<int32_t>(c->L.pos) + slot, &pos, 4, hipMemcpyHostToDevice));
   HIPCHK(c, hipMemcpy(c->A<int32_t>(c->L.c0) + slot, &c0, 4, hipMemcpyHostToDevice));
@@ -909,8 +950,10 @@ int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, 
   gu.nseg = 1; gu.seg_end[0] = d.F; gu.N = d.F; gu.K = d.H;
   gu.x = c->A<float>(c->L.x); gu.x_stride = d.H; gu.M = c->B;
   gu.y = c->A<float>(c->L.z); gu.y_stride = d.F;
-  // as the per-op decode path runs it: the GEMV at batch <= 3, the MFMA GEMM
-  // for 4..128 rows (its row norms read the sums of squares the last decode left)
+  // as the per-op decode path runs it (project(): the split-K MFMA GEMM for
+  // bf16, q8 and q4 models whose widths are multiples of 256, at 1..128 rows,
+  // its row norms reading the sums of squares the last decode left; else the
+  // GEMV)
   (void)wt;
   hipError_t err = hipEventRecord(e0, s);
   int launches = 0;
@@ -931,6 +974,34 @@ int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, 
                         : md.lin_type == QT_LIN_Q8 ? 34.0 / 32.0 : 18.0 / 32.0;
   *avg_us = 1000.0 * ms / launches;
   *bytes = 2.0 * d.F * d.H * wbytes + 4.0 * c->B * (d.H + d.F);
+  return QT_OK;
+}
+
+int32_t qt_stream_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, int32_t reps, void *stream,
+                       double *avg_us) {
+  if (!src || !sink || !avg_us || reps <= 0) return fail(nullptr, QT_E_ARG, "NULL pointer or reps <= 0");
+  if (bytes < (1u << 20) || bytes % 16 || ((uintptr_t)src | (uintptr_t)sink) % 16)
+    return fail(nullptr, QT_E_ARG, "bytes must be >= 1 MiB and a multiple of 16; pointers 16-byte aligned");
+  if (sink_bytes < (size_t)kStreamGrid * 256 * 4)
+    return fail(nullptr, QT_E_SIZE, "sink needs %zu bytes", (size_t)kStreamGrid * 256 * 4);
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return fail(nullptr, QT_E_HIP, "hipEventCreate failed");
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(nullptr, QT_E_HIP, "hipEventCreate failed");
+  }
+  hipError_t err = launch_stream_read(src, bytes, sink, s);  // untimed first pass
+  if (err == hipSuccess) err = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch_stream_read(src, bytes, sink, s);
+  if (err == hipSuccess) err = hipEventRecord(e1, s);
+  if (err == hipSuccess) err = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != hipSuccess) return fail(nullptr, QT_E_HIP, "qt_stream_read: %s", hipGetErrorString(err));
+  *avg_us = 1000.0 * ms / reps;
   return QT_OK;
 }
 

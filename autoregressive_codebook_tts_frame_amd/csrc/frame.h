@@ -75,7 +75,11 @@ struct FrameArgs {
   uint64_t seed;
 };
 
+// Cooperative launch: every workgroup is resident at once, or the launch fails.
 hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s);
+// True if a.nwg workgroups of the planned kernel (a.lds_bytes of LDS each)
+// fit on the ncu compute units at once, by the occupancy query.
+bool frame_coresident(const FrameArgs &a, int ncu);
 // the (weights, head dim, GQA group, bf16 ring) combinations instantiated
 bool frame_variant_supported(int wt, int hd, int g, int kv_bf16);
 // Plan a launch whose talker positions reach max_pos: attention workgroups,

@@ -1589,22 +1589,40 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   return true;
 }
 
-hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s) {
+// The kernel instantiation of a plan (null if none).
+static const void *frame_fn(const FrameArgs &a, bool smp) {
   const int g = a.nq / a.nkv;
-  const bool smp = a.inv_temp != 0.f;
-#define X1(W, HD_, G_, K_, S_)                                                                       \
-  if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_ && smp == S_) {                \
-    hipError_t e = hipFuncSetAttribute((const void *)frame_kernel<W, HD_, G_, K_, S_>,               \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);    \
-    if (e != hipSuccess) return e;                                                                  \
-    hipLaunchKernelGGL((frame_kernel<W, HD_, G_, K_, S_>), dim3(a.nwg), dim3(NTB), a.lds_bytes, s, a); \
-    return hipGetLastError();                                                                       \
-  }
+#define X1(W, HD_, G_, K_, S_) \
+  if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_ && smp == S_) return (const void *)frame_kernel<W, HD_, G_, K_, S_>;
 #define X(W, HD_, G_, K_) X1(W, HD_, G_, K_, false) X1(W, HD_, G_, K_, true)
   QT_FRAME_VARIANTS(X)
 #undef X
 #undef X1
-  return hipErrorInvalidValue;
+  return nullptr;
+}
+
+bool frame_coresident(const FrameArgs &a, int ncu) {
+  for (const bool smp : {false, true}) {
+    const void *fn = frame_fn(a, smp);
+    int per_cu = 0;
+    if (!fn || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTB, a.lds_bytes) != hipSuccess ||
+        (long long)per_cu * ncu < a.nwg)
+      return false;
+  }
+  return true;
+}
+
+hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s) {
+  const void *fn = frame_fn(a, a.inv_temp != 0.f);
+  if (!fn) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
+  if (e != hipSuccess) return e;
+  FrameArgs arg = a;
+  void *params[] = {&arg};
+  // every workgroup waits on the others' exchange words: they must all be
+  // resident together, which a cooperative launch guarantees (or refuses)
+  return hipLaunchCooperativeKernel(fn, dim3(a.nwg), dim3(NTB), params, (unsigned)a.lds_bytes, s);
 }
 
 }  // namespace qtk

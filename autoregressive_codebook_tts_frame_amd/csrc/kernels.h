@@ -177,5 +177,9 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_pred_input(const PredInArgs &a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t s);
 hipError_t launch_advance(int32_t *ctl, int32_t K, hipStream_t s);
+// streaming read of `bytes` (a multiple of 16) at src; writes kStreamGrid *
+// 256 words to sink
+constexpr int kStreamGrid = 2048;
+hipError_t launch_stream_read(const void *src, size_t bytes, void *sink, hipStream_t s);
 
 }  // namespace qtk

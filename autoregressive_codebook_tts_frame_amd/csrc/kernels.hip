@@ -1499,4 +1499,30 @@ hipError_t launch_advance(int32_t *ctl, int32_t K, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Plain streaming read of n16 16-byte chunks: a grid-stride loop with four
+// 16-byte loads in flight per thread, the words folded by xor so the loads
+// stay live; each thread stores its fold to sink (the achievable-bandwidth
+// reference the frame kernels are measured against).
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ src, size_t n16,
+                                                          uint32_t *__restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void *src, size_t bytes, void *sink, hipStream_t s) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamGrid), dim3(256), 0, s, (const uint4 *)src, bytes / 16,
+                     (uint32_t *)sink);
+  return hipGetLastError();
+}
+
 }  // namespace qtk

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqt.so")
 
 QT_ABI_MIN_VERSION = 1
-QT_ABI_VERSION = 2
+QT_ABI_VERSION = 3
 QT_OK = 0
 QT_E_ABI, QT_E_ARG, QT_E_SIZE, QT_E_RANGE = -1, -2, -3, -4
 QT_E_STATE, QT_E_CONTEXT_FULL, QT_E_HIP, QT_E_UNSUPPORTED = -5, -6, -7, -8
@@ -34,7 +34,7 @@ QT_KERNEL_GEMV_GATE_UP = 1
 
 EXPORTS = ("qt_abi_version", "qt_query_sizes", "qt_init", "qt_prefill", "qt_decode_frame",
            "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_time_kernel",
-           "qt_set_sampler", "qt_path", "qt_free", "qt_last_error")
+           "qt_set_sampler", "qt_path", "qt_free", "qt_last_error", "qt_stream_read")
 
 
 class qt_model_desc(C.Structure):
@@ -98,6 +98,8 @@ def _load():
     lib.qt_time_kernel.restype = i32
     lib.qt_path.argtypes = [vp]
     lib.qt_path.restype = i32
+    lib.qt_stream_read.argtypes = [vp, sz, vp, sz, i32, vp, C.POINTER(C.c_double)]
+    lib.qt_stream_read.restype = i32
     lib.qt_set_sampler.argtypes = [vp, C.c_float, i32, C.c_uint64]
     lib.qt_set_sampler.restype = i32
     lib.qt_free.argtypes = [vp]
@@ -189,6 +191,15 @@ def qt_time_kernel(ctx, kernel: int, reps: int):
     us, nb = C.c_double(), C.c_double()
     _check(lib.qt_time_kernel(ctx, kernel, reps, C.byref(us), C.byref(nb)), ctx)
     return us.value, nb.value
+
+
+def qt_stream_read(src: torch.Tensor, sink: torch.Tensor, reps: int, stream=None) -> float:
+    """Average microseconds per streaming-read pass over the device tensor src."""
+    us = C.c_double()
+    st = (stream or torch.cuda.current_stream(src.device)).cuda_stream
+    _check(lib.qt_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                              sink.numel() * sink.element_size(), reps, st, C.byref(us)), None)
+    return us.value
 
 
 def qt_set_sampler(ctx, temperature: float, top_k: int = 0, seed: int = 0):

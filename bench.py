@@ -159,6 +159,52 @@ def ttfa(args, d, m, wl, B):
     }
 
 
+def setup(qt, synth, wl, dw, nf, flags, args):
+    """A decoder for wl with every stream prefilled from its seeded prompt;
+    returns it, the context lengths, the slot states and the overlay ids."""
+    B = wl.batch
+    d = qt.Decoder(wl.model, dw, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf, flags=flags)
+    if args.temperature:
+        d.set_sampler(args.temperature, args.seed, top_k=args.top_k)
+    lens = []
+    ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
+    for b in range(B):
+        codes, text = synth.make_prompt(wl, b, T=int(ctx[b]))
+        d.prefill(b, codes, text)
+        lens.append(len(text))
+    states = [d.get_state(b) for b in range(B)]
+    ov = synth.make_overlays(wl, nf, B)
+    log("prefill done")
+    return d, lens, states, ov
+
+
+def time_steps(d, states, ov, nf, steps, warmup):
+    """Warm up, then time `steps` steps between HIP events on the library's
+    stream and the host clock; a step restores every slot's state and
+    decodes nf frames.  Returns (wall seconds, event seconds)."""
+    import torch
+
+    def step():
+        for b, (pos, c0, br) in enumerate(states):
+            d.set_state(b, pos, c0, br)
+        return d.decode(nf, ov)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    ev0.record(d.stream)
+    for _ in range(steps):
+        step()
+    ev1.record(d.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1e3
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +224,8 @@ def main():
     ap.add_argument("--ttfa", action="store_true",
                     help="time to first frame instead: a step is the prompt prefill of every stream plus "
                          "one decoded frame")
+    ap.add_argument("--no-b32", action="store_true",
+                    help="skip the 32-stream leg that the default run times after the batch-1 workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device three times (a plain copy kernel "
                          "of known size, to scale hardware byte counters against)")
@@ -204,50 +252,22 @@ def main():
     if args.frames_per_replay:
         import dataclasses
         wl = dataclasses.replace(wl, frames_per_replay=args.frames_per_replay)
-    d = qt.Decoder(m, w, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf,
-                   flags=qt.QT_F_OPS if args.ops else 0)
-    if args.temperature:
-        d.set_sampler(args.temperature, args.seed, top_k=args.top_k)
-    lens = []
-    ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
-    for b in range(B):
-        codes, text = synth.make_prompt(wl, b, T=int(ctx[b]))
-        d.prefill(b, codes, text)
-        lens.append(len(text))
-    states = [d.get_state(b) for b in range(B)]
-    ov = synth.make_overlays(wl, nf, B)
-    log("prefill done; warmup")
+    dw = qt.DeviceWeights(m, w, "cuda")
+    d, lens, states, ov = setup(qt, synth, wl, dw, nf, qt.QT_F_OPS if args.ops else 0, args)
     if args.ttfa:
         print(json.dumps(ttfa(args, d, m, wl, B)), flush=True)
         d.close()
         return
 
-    def step():
-        for b, (pos, c0, br) in enumerate(states):
-            d.set_state(b, pos, c0, br)
-        return d.decode(nf, ov)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    ev0.record(d.stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(d.stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    wall, gpu_s = time_steps(d, states, ov, nf, args.steps, args.warmup)
     frames = B * nf * args.steps
     ms_per_step = 1e3 * wall / args.steps
     mean_len = float(np.mean(lens)) + (nf + 1) / 2.0
     fb = frame_bytes(m, B, mean_len)
     ms_per_frame_step = 1e3 * wall / (nf * args.steps)
 
-    if d.path == qt.QT_PATH_FRAME:
+    path = d.path
+    if path == qt.QT_PATH_FRAME:
         # dominant kernel: the persistent frame kernel, one launch per step;
         # its average duration from the HIP events on the library's stream
         # around the timed region (the step's id copies are on the same stream)
@@ -255,15 +275,51 @@ def main():
         us = gpu_s * 1e6 / args.steps
         kbytes = fb * nf
     else:
-        # dominant kernel: the gate/up GEMV, timed live with HIP events on the
-        # library's stream over every layer's weights
+        # dominant kernel: the gate/up projection, timed live with HIP events
+        # on the library's stream over every layer's weights
         batched = m.lin != 0 and m.act_bf16  # bf16 / q8 / q4 projections take the GEMM at any row count
         kname = ("gemm_kernel<gated> (MFMA: RMSNorm + gate/up + SiLU-mul, %d rows)" % B if batched
                  else "gemv_kernel<gated> (RMSNorm + gate/up + SiLU-mul)")
         us, kbytes = d.time_kernel(qt.QT_KERNEL_GEMV_GATE_UP, 3)
     achieved = kbytes / (us * 1e-6) / 1e9
-    log(f"path {d.path}: {frames / wall:.1f} frames/s, {ms_per_frame_step:.3f} ms per frame-step; "
+    log(f"path {path}: {frames / wall:.1f} frames/s, {ms_per_frame_step:.3f} ms per frame-step; "
         f"{kname}: {us:.1f} us/launch = {achieved:.0f} GB/s")
+    d.close()
+
+    # the achievable HBM read bandwidth, measured in the same run: a plain
+    # streaming-read kernel over 4 GiB (far above the 256 MB last-level cache)
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2 << 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sread_us = qt.qt_stream_read(src, sink, 5)
+    achievable = src.numel() / (sread_us * 1e-6) / 1e9
+    del src, sink
+    log(f"streaming read: {achievable:.0f} GB/s ({achievable / HBM_PEAK_GBS:.3f} of the 8 TB/s peak)")
+
+    # the 32-stream workload, timed in the same run (the metric is quoted at
+    # batch 1 and at 32 streams)
+    b32 = None
+    if args.workload == "bf16_b1" and not args.no_b32 and not args.frames:
+        wl32 = synth.WORKLOADS["bf16_b32"]
+        nf32 = wl32.frames
+        log(f"workload {wl32.name}: B={wl32.batch}, ragged contexts, {nf32} frames/step, "
+            f"{wl32.frames_per_replay} frames per graph replay")
+        d32, lens32, states32, ov32 = setup(qt, synth, wl32, dw, nf32, 0, args)
+        wall32, gpu32 = time_steps(d32, states32, ov32, nf32, args.steps, args.warmup)
+        fb32 = frame_bytes(m, wl32.batch, float(np.mean(lens32)) + (nf32 + 1) / 2.0)
+        ms32 = 1e3 * wall32 / (nf32 * args.steps)
+        b32 = {"workload": wl32.name, "value": wl32.batch * nf32 * args.steps / wall32, "unit": "frames/s",
+               "ms_per_frame_step": ms32, "steps": args.steps, "warmup": args.warmup,
+               "batch": wl32.batch, "frames_per_step": nf32, "frames_per_replay": wl32.frames_per_replay,
+               "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[d32.path],
+               "mean_context": float(np.mean(lens32)),
+               "frame_roofline": {"bytes_per_frame_step": fb32, "achieved_gbs": fb32 / (ms32 * 1e-3) / 1e9,
+                                  "frac": fb32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "frac_of_achievable": fb32 / (ms32 * 1e-3) / 1e9 / achievable},
+               "gpu_event_s": gpu32, "wall_s": wall32}
+        log(f"{wl32.name}: {b32['value']:.1f} frames/s, {ms32:.3f} ms per frame-step, "
+            f"{b32['frame_roofline']['frac']:.3f} of HBM peak")
+        d32.close()
 
     res = {
         "metric": "codec frames/s (talker step + 15 predictor steps)",
@@ -279,23 +335,24 @@ def main():
         "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16", 3: "q4+bf16"}[m.lin],
         "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
         "config": {"workload": wl.name, "batch": B, "prompt": wl.prompt, "frames_per_step": nf,
-                   "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[d.path],
+                   "path": {1: "persistent frame kernel", 2: "per-op hipGraph", 3: "per-op eager"}[path],
                    "frames_per_replay": wl.frames_per_replay, "talker_layers": m.Lt,
                    "predictor_layers": m.Lp, "hidden": m.H,
                    "sampler": (f"temperature {args.temperature}, seed {args.seed}"
                                + (f", top-k {args.top_k}" if args.top_k else "")) if args.temperature else "greedy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(wl.name, nf) if d.path == qt.QT_PATH_FRAME else None,
+                     "traffic": measured_traffic(wl.name, nf) if path == qt.QT_PATH_FRAME else None,
                      "kernel": kname,
-                     "bytes_per_launch": kbytes, "avg_launch_us": us},
+                     "bytes_per_launch": kbytes, "avg_launch_us": us,
+                     "achievable_gbs": achievable, "frac_of_achievable": achieved / achievable},
         "frame_roofline": {"bytes_per_frame_step": fb, "ms_per_frame_step": ms_per_frame_step,
                            "achieved_gbs": fb / (ms_per_frame_step * 1e-3) / 1e9,
                            "frac": fb / (ms_per_frame_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "gpu_event_s": gpu_s, "wall_s": wall},
         "cpu_baseline": None,
+        "b32": b32,
     }
-    d.close()
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -14,7 +14,15 @@
  * Conventions
  *   - Every entry point returns int32_t status: QT_OK (0) or a negative QT_E_*.
  *     A failing call changes no state: arguments are validated on the host
- *     before any launch.  qt_last_error() describes the last failure.
+ *     before any launch.  The one exception is QT_E_HIP from a call that had
+ *     already launched work (a HIP runtime failure, or a timed-out wait of
+ *     the persistent kernel): the slots that call was decoding may hold
+ *     partial results, so they are marked un-prefilled and the next
+ *     qt_decode_frame returns QT_E_STATE until qt_prefill or
+ *     qt_set_slot_state restores them.  No failure is silent: an empty or
+ *     partial result always comes with an error status ([QT-log], clone-mode
+ *     entry: an encoder pass that returned empty without an error).
+ *     qt_last_error() describes the last failure.
  *   - "device" pointers are HIP device addresses; "host" pointers are ordinary
  *     host memory, read or written only during the call.  The library keeps
  *     device pointers it is given for the lifetime of the context; the caller
@@ -34,9 +42,10 @@ extern "C" {
 
 /* Closed ABI range: a caller built against any version in
    [QT_ABI_MIN_VERSION, QT_ABI_VERSION] is accepted; both bounds are checked
-   ([QT-tests], codec left context / ABI range entry). */
+   ([QT-tests], codec left context / ABI range entry: the range check rejects
+   a version past either bound). */
 #define QT_ABI_MIN_VERSION 1
-#define QT_ABI_VERSION 2 /* 2: qt_set_sampler */
+#define QT_ABI_VERSION 3 /* 2: qt_set_sampler; 3: qt_stream_read */
 
 #define QT_OK 0
 #define QT_E_ABI (-1)          /* abi_version outside the closed range (checked first) */
@@ -121,6 +130,9 @@ typedef struct qt_weights {
   const qt_linear *predictor_heads;    /* host array [G-1], each [Vc][H] */
 } qt_weights;
 
+/* Everything a context is built from, read once by qt_init ([QT-tests],
+   codec left context / ABI range entry: an init-params struct resolved once
+   at load, versioned by the closed ABI range above). */
 typedef struct qt_init_params {
   uint32_t abi_version; /* QT_ABI_VERSION of the caller's header */
   uint32_t struct_size; /* sizeof(qt_init_params) */
@@ -145,10 +157,14 @@ typedef struct qt_init_params {
 
 typedef struct qt_ctx qt_ctx;
 
-/* ABI version of the loaded library. */
+/* ABI version of the loaded library (the library's own query). */
 int32_t qt_abi_version(void);
 
-/* Pure host computation of the device memory a context needs.
+/* Pure host computation of the device memory a context needs (the
+   library's own helper: the ring is sized once for P positions, as the
+   [QT-log] per-layer K/V ring entry sizes its buffer at init for the
+   longest sequence; the arena holds the fixed-address buffers of the
+   [QT-log] persistent-arena entry).
    ring_bytes = B*Lt*2*nkv*P*hd*e + B*Lp*2*nkv*Q*hd*e with e = 2 (bf16) or 4.
    Errors: QT_E_ARG (NULL outputs, non-positive sizes), QT_E_UNSUPPORTED. */
 int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t frames_per_replay,
@@ -156,9 +172,18 @@ int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t fr
                        size_t *arena_bytes);
 
 /* Validates, binds caller memory, uploads the RoPE table, and (unless
-   QT_F_EAGER) captures the K-frame graph on params->stream.  All slots start
-   un-prefilled.  Errors: QT_E_ABI first, then QT_E_ARG, QT_E_UNSUPPORTED,
-   QT_E_SIZE, QT_E_HIP.  *out is set only on success. */
+   QT_F_EAGER) captures the K-frame graph on params->stream.  Everything a
+   context needs is fixed here, once, from qt_init_params ([QT-tests], codec
+   left context / ABI range entry: settings move into the init params and
+   are resolved once at load); every later call reuses the same device
+   addresses ([QT-log], persistent-arena entry: fixed tensor addresses let a
+   captured graph replay without an update).  All slots start un-prefilled.
+   The persistent frame kernel is chosen only where every one of its
+   workgroups fits on the device at once (one per compute unit, checked with
+   the occupancy query); it is launched cooperatively, so the runtime either
+   makes them all resident together or refuses the launch.
+   Errors: QT_E_ABI first, then QT_E_ARG, QT_E_UNSUPPORTED, QT_E_SIZE,
+   QT_E_HIP.  *out is set only on success. */
 int32_t qt_init(const qt_init_params *params, qt_ctx **out);
 
 /* Prefill of one slot with T prompt rows ([QT-log] per-layer K/V ring entry:
@@ -189,9 +214,12 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
 int32_t qt_decode_frame(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_ids,
                         int32_t *codes_out, const int32_t *forced_codes);
 
-/* Snapshot / restore of a slot's non-ring state: next talker position, the
-   pending code 0, and the bridge (host float [H]).  The ring itself is caller
-   memory at the documented layout.  set marks the slot prefilled.
+/* Snapshot / restore of a slot's non-ring state (the library's own calls,
+   used to restart a decode from a saved or injected state): next talker
+   position, the pending code 0, and the bridge (host float [H]; the bridge
+   is the [QT-log] set_rows entry's device-resident talker hidden).  The
+   ring itself is caller memory at the documented layout.  set marks the slot
+   prefilled.
    Errors: QT_E_ARG, QT_E_RANGE (pos outside [1, P], c0 outside [0, Vc)). */
 int32_t qt_get_slot_state(qt_ctx *ctx, int32_t slot, int32_t *pos, int32_t *c0, float *bridge);
 int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
@@ -225,7 +253,8 @@ int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
 #define QT_DUMP_TRACE 8
 int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
 
-/* Measurement hook: launches one kernel of the frame `reps` times, in the
+/* Measurement hook (the library's own): launches one kernel of the frame
+   `reps` times, in the
    launch configuration the frame uses at batch B, between two HIP events on
    the context's stream, and reports the average duration per launch
    (microseconds) and the algorithmic bytes one launch moves (weights once,
@@ -265,17 +294,33 @@ int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us
    QT_PATH_FRAME, or codebook_size > 2048). */
 int32_t qt_set_sampler(qt_ctx *ctx, float temperature, int32_t top_k, uint64_t seed);
 
-/* Decode path of a context: QT_PATH_FRAME (persistent frame kernel),
+/* Measurement hook (the library's own): the achievable HBM read bandwidth
+   that the decode kernels are compared with.  Reads `bytes` at src (device,
+   16-byte aligned, a multiple of 16 and at least 1 MiB; pass well above the
+   256 MB last-level cache for an HBM figure) with a plain streaming-read
+   kernel, once untimed and then `reps` times between two HIP events on
+   `stream` (hipStream_t; NULL: the default stream), and reports the average
+   duration per pass in microseconds.  sink: device scratch of sink_bytes >=
+   2 MiB that the kernel overwrites.  Synchronous.  Needs no context.
+   Errors: QT_E_ARG, QT_E_SIZE (sink too small), QT_E_HIP. */
+int32_t qt_stream_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, int32_t reps, void *stream,
+                       double *avg_us);
+
+/* Decode path of a context (the library's own query): QT_PATH_FRAME
+   (persistent frame kernel),
    QT_PATH_GRAPH (per-op kernels replayed as a hipGraph) or QT_PATH_EAGER. */
 #define QT_PATH_FRAME 1
 #define QT_PATH_GRAPH 2
 #define QT_PATH_EAGER 3
 int32_t qt_path(const qt_ctx *ctx);
 
-/* Destroys graphs and host state; never frees caller memory.  NULL is a no-op. */
+/* Destroys graphs and host state; never frees caller memory (the caller
+   owns it, as in the [QT-log] clone-mode entry the caller holds its buffers
+   until the library returns).  NULL is a no-op. */
 void qt_free(qt_ctx *ctx);
 
-/* Last error text of ctx (of the calling thread when ctx is NULL). */
+/* Last error text of ctx (of the calling thread when ctx is NULL): every
+   failure carries one ([QT-log], clone-mode entry: no silent failures). */
 const char *qt_last_error(const qt_ctx *ctx);
 
 #ifdef __cplusplus

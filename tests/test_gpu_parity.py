@@ -68,77 +68,56 @@ def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None, sam
                 q0=[len(t) for _, t in prompts])
 
 
-def _oracle_from_states(m, w, states, lengths, pcap):
-    o = Oracle(m, w, len(states), pcap=pcap)
-    for b, (k, v, br, c0) in enumerate(states):
-        kf = synth.bf16_bits_to_f32(k) if m.kv_bf16 else k
-        vf = synth.bf16_bits_to_f32(v) if m.kv_bf16 else v
-        for layer in range(m.Lt):  # ring [nkv][L][hd] -> oracle [L][nkv][hd]
-            o.set_cache(b, layer, 0, kf[layer].transpose(1, 0, 2), vf[layer].transpose(1, 0, 2))
-        o.set_state(b, int(lengths[b]), c0, br)
-    return o
+def _read_state(d, b, length):
+    """Slot b's decode state after a GPU prefill: talker K/V of positions
+    [0, length) as float32 [Lt][length][nkv][hd] (the oracle's layout), and
+    (pos, c0, bridge)."""
+    m = d.m
+    ring = d.talker_ring()[b, :, :, :, :length, :].cpu().numpy()  # [Lt][2][nkv][L][hd]
+    if m.kv_bf16:
+        ring = synth.bf16_bits_to_f32(ring.view(np.uint16))
+    kv = np.ascontiguousarray(ring.transpose(0, 1, 3, 2, 4))  # [Lt][2][L][nkv][hd]
+    return kv, d.get_state(b)
 
 
-def _state_noise_floor(m, w, state, length, ov, out):
-    """The oracle against itself from a synthetic state: one key element
-    changed by one bf16 ulp, teacher-forced with the unchanged run's codes.
-    Returns, per tensor, the largest rel-L2 over the frames: the rounding
-    noise floor of this regime (synthetic states sit about twice as high as
-    prefilled ones)."""
-    k, v, br, c0 = state
-    k2 = k.copy()
-    k2[min(3, m.Lt - 1), 0, length // 2, 7] ^= 1
-    n = ov.shape[0]
-    o = _oracle_from_states(m, w, [(k2, v, br, c0)], [length], length + n + 1)
-    p = o.decode(n, ov, forced=out["codes"], dump=True)
-    return {key: max(rel_l2(p[key][f, 0], out[key][f, 0]) for f in range(n))
-            for key in ("talker_logits", "bridge", "pred_logits")}
-
-
-def _injected_state_run(m, w, wl, nframes, lengths):
-    """Like _forced_run, but each stream starts from a seeded synthetic decode
-    state (talker K/V of `lengths[b]` positions, bridge, code 0) written into
-    the ring and the oracle's cache instead of a prefill."""
-    B = len(lengths)
-    states = [synth.make_synthetic_state(wl, b, int(L)) for b, L in enumerate(lengths)]
+def _prefilled_state_run(m, w, wl, nframes, prompts, sample, frames_per_replay=1):
+    """The GPU prefills every stream's prompt (qt_prefill); the decode state
+    of the streams in `sample` (ring rows, position, code 0, bridge) is read
+    back and given to the oracle, so both sides start the decode from one
+    bitwise state (the long-context and multi-stream workloads' contexts are
+    prefilled from seeded prompts).  Then the oracle decodes free-running and
+    the GPU decodes teacher-forced with the oracle's codes, one frame per call
+    with the dumps read after each frame."""
+    B = len(prompts)
     ov = synth.make_overlays(wl, nframes, B)
-    o = _oracle_from_states(m, w, states, lengths, int(max(lengths)) + nframes + 1)
-    oout = o.decode(nframes, ov, dump=True)
-    floor = None
-    if tol_for(m) > TOL_F32_CHECK:  # bf16 models: a tolerance from this regime's own floor
-        floor = _state_noise_floor(m, w, states[0], int(lengths[0]), ov[:, :1],
-                                   {k: v[:, :1] for k, v in oout.items()})
-
-    def fresh(flags):
-        d = qt.Decoder(m, w, B, flags=flags)
-        for b, (k, v, br, c0) in enumerate(states):
-            d.inject_talker_state(b, k, v, br, c0)
-        return d
-
-    d = fresh(qt.QT_F_DUMP)
+    d = qt.Decoder(m, w, B, frames_per_replay=frames_per_replay, flags=qt.QT_F_DUMP)
+    for b, (c, t) in enumerate(prompts):
+        d.prefill(b, c, t)
+    torch.cuda.synchronize()
+    lengths = [len(prompts[b][1]) for b in sample]
+    o = Oracle(m, w, len(sample), pcap=max(lengths) + nframes + 1)
+    gstate = {}
+    for i, b in enumerate(sample):
+        kv, (pos, c0, br) = _read_state(d, b, lengths[i])
+        for layer in range(m.Lt):
+            o.set_cache(i, layer, 0, kv[layer, 0], kv[layer, 1])
+        o.set_state(i, pos, c0, br)
+        gstate[b] = (pos, c0, br)
+    oout = o.decode(nframes, ov[:, sample], dump=True)
+    forced = np.zeros((nframes, B, m.G), np.int32)
+    forced[:, sample] = oout["codes"]
     g = {k: [] for k in ("codes", "talker_logits", "pred_logits", "bridge", "x0", "gather", "tpos")}
     for f in range(nframes):
-        g["codes"].append(d.decode(1, ov[f:f + 1], forced=oout["codes"][f:f + 1])[0])
-        g["talker_logits"].append(d.dump(qt.QT_DUMP_TALKER_LOGITS))
-        g["pred_logits"].append(d.dump(qt.QT_DUMP_PRED_LOGITS).transpose(1, 0, 2))
-        g["bridge"].append(d.dump(qt.QT_DUMP_BRIDGE))
-        g["x0"].append(d.dump(qt.QT_DUMP_X0))
-        g["gather"].append(d.dump(qt.QT_DUMP_GATHER))
-        g["tpos"].append(d.dump(qt.QT_DUMP_TPOS))
+        g["codes"].append(d.decode(1, ov[f:f + 1], forced=forced[f:f + 1])[0][sample])
+        g["talker_logits"].append(d.dump(qt.QT_DUMP_TALKER_LOGITS)[sample])
+        g["pred_logits"].append(d.dump(qt.QT_DUMP_PRED_LOGITS).transpose(1, 0, 2)[sample])
+        g["bridge"].append(d.dump(qt.QT_DUMP_BRIDGE)[sample])
+        g["x0"].append(d.dump(qt.QT_DUMP_X0)[sample])
+        g["gather"].append(d.dump(qt.QT_DUMP_GATHER)[sample])
+        g["tpos"].append(d.dump(qt.QT_DUMP_TPOS)[sample])
     g = {k: np.stack(v) for k, v in g.items()}
-    return dict(o=o, d=d, ov=ov, prompts=[None] * B, pre_logits=None, fresh=fresh, oout=oout, g=g,
-                states=states, path=d.path, floor=floor)
-
-
-TOL_F32_CHECK = 1e-3
-
-
-def _tol_map(m, r):
-    """Per-tensor tolerance: rel-L2 1e-2 for BF16/Q8 (1e-4 for F32), raised
-    to 2.5x the oracle's own rounding noise floor where a test measured it."""
-    base = tol_for(m)
-    floor = r.get("floor") or {}
-    return lambda key: max(base, 2.5 * floor[key]) if key in floor else base
+    return dict(o=o, d=d, ov=ov, prompts=[None] * len(sample), pre_logits=None, oout=oout, g=g,
+                sample=sample, pstate=gstate, lengths=lengths)
 
 
 def _check(r, m, label, free_run=True):
@@ -157,19 +136,15 @@ def _check(r, m, label, free_run=True):
             # step's predictor logits [G-1][Vc] (what the dump returns per stream)
             for key in ("talker_logits", "bridge", "x0", "pred_logits"):
                 worst[key] = max(worst.get(key, 0), rel_l2(g[key][f, b], oout[key][f, b]))
-            for j in range(m.G - 1):  # reported, not gated: a single head's row
-                worst["pred_head_row (info)"] = max(worst.get("pred_head_row (info)", 0),
-                                                    rel_l2(g["pred_logits"][f, b, j], oout["pred_logits"][f, b, j]))
+            for j in range(m.G - 1):  # and each predictor head's row on its own
+                worst["pred_head_row"] = max(worst.get("pred_head_row", 0),
+                                             rel_l2(g["pred_logits"][f, b, j], oout["pred_logits"][f, b, j]))
             if "hidden" in g:
                 for l in range(m.Lt):
                     worst["hidden"] = max(worst.get("hidden", 0), rel_l2(g["hidden"][f, b, l], oout["hidden"][f, b, l]))
-    tk = _tol_map(m, r)
-    if r.get("floor"):
-        say(f"[{label}] oracle noise floor:", {k: f"{v:.2e}" for k, v in r["floor"].items()})
-    say(f"[{label}] worst rel-L2 (tol {tol}, or 2.5x the floor):", {k: f"{v:.2e}" for k, v in worst.items()})
+    say(f"[{label}] worst rel-L2 (tol {tol}):", {k: f"{v:.2e}" for k, v in worst.items()})
     for k, v in worst.items():
-        if "(info)" not in k:
-            assert v <= tk(k), f"{label}: {k} rel-L2 {v} > {tk(k)}"
+        assert v <= tol, f"{label}: {k} rel-L2 {v} > {tol}"
     # integer work is bit-exact: gather indices and K/V write positions
     assert np.array_equal(g["gather"], oout["gather"])
     assert np.array_equal(g["tpos"], oout["tpos"])
@@ -222,16 +197,23 @@ def _check(r, m, label, free_run=True):
         bad = code_mismatches(g["codes"], oout["codes"], ref_logits, gpu_logits)
         say(f"[{label}] teacher-forced decisions differing: {len(bad)} of {g['codes'].size}")
         assert_near_ties_only(bad, label)
-    if free_run and not bad:
-        # free running from the same prefill (or state) must reproduce the oracle's codes
-        if "fresh" in r:
-            d2 = r["fresh"](0)
-        else:
-            d2 = qt.Decoder(m, r["d"].dw, B, flags=r.get("flags", 0))
-            if r.get("sampler"):
-                d2.set_sampler(*r["sampler"])
-            for b, (c, t) in enumerate(r["prompts"]):
-                d2.prefill(b, c, t)
+    if free_run and not bad and "pstate" in r:
+        # free running from the same prefilled state reproduces the oracle's
+        # codes (the sampled streams restart from their state; the ring rows
+        # past it are rewritten at the same positions before they are read)
+        d2 = r["d"]
+        for b, st in r["pstate"].items():
+            d2.set_state(b, *st)
+        n = oout["codes"].shape[0]
+        codes = d2.decode(n, r["ov"])[:, r["sample"]]
+        assert np.array_equal(codes, oout["codes"]), f"{label}: free-run codes differ"
+    elif free_run and not bad:
+        # free running from the same prefill reproduces the oracle's codes
+        d2 = qt.Decoder(m, r["d"].dw, B, flags=r.get("flags", 0))
+        if r.get("sampler"):
+            d2.set_sampler(*r["sampler"])
+        for b, (c, t) in enumerate(r["prompts"]):
+            d2.prefill(b, c, t)
         n = oout["codes"].shape[0]
         codes = d2.decode(n, r["ov"])
         assert np.array_equal(codes, oout["codes"]), f"{label}: free-run codes differ"
@@ -581,32 +563,36 @@ def test_full_q8_b1_parity():
 
 @pytest.mark.timeout(900)
 def test_full_bf16_long_context_parity():
-    # a 2,044-position context from a synthetic state: the frame kernel runs
-    # 64 attention workgroups (8 tiles per head) with one weight slot, and the
-    # free run crosses the 2,048-position tile boundary inside one launch
+    # the long-context workload as configured: a seeded 2,048-row prompt
+    # prefilled through the 28-layer model on the GPU, its state handed to
+    # the oracle, then decoding across position 2,048 -- the window grows from
+    # 2,048 to 2,304 positions (9 attention tiles) at the first frame; the
+    # frame kernel runs 72 attention workgroups with one weight slot
     m = synth.BIG
     wl = synth.WORKLOADS["bf16_long_b1"]
     w = synth.make_weights(m)
-    say("[bf16_long] state of 2044 positions, 6 frames")
-    r = _injected_state_run(m, w, wl, 6, [2044])
-    assert r["path"] == qt.QT_PATH_FRAME
+    say("[bf16_long] GPU prefill of 2048 rows, oracle from its state, 6 frames")
+    r = _prefilled_state_run(m, w, wl, 6, [synth.make_prompt(wl, 0)], [0])
+    assert r["d"].path == qt.QT_PATH_FRAME
+    assert r["lengths"] == [2048]
     _check(r, m, "bf16_long")
 
 
 @pytest.mark.timeout(900)
 def test_full_bf16_max_context_parity():
-    # the ring's last positions: a 4,088-position state decoded to position
-    # 4,093 of 4,096; the frame kernel runs 128 attention workgroups (16 tiles
-    # per head) beside 128 GEMV workgroups with one weight slot
+    # the ring's last positions: a 4,088-row prompt prefilled on the GPU,
+    # decoded to position 4,093 of 4,096; the frame kernel runs 128
+    # attention workgroups (16 tiles per head) beside 128 GEMV workgroups
     m = synth.BIG
     wl = synth.WORKLOADS["bf16_long_b1"]
     w = synth.make_weights(m)
-    say("[bf16_max_context] state of 4088 positions, 6 frames")
-    r = _injected_state_run(m, w, wl, 6, [4088])
-    assert r["path"] == qt.QT_PATH_FRAME
+    say("[bf16_max_context] GPU prefill of 4088 rows, oracle from its state, 6 frames")
+    r = _prefilled_state_run(m, w, wl, 6, [synth.make_prompt(wl, 0, T=4088)], [0])
+    assert r["d"].path == qt.QT_PATH_FRAME
     _check(r, m, "bf16_max_context")
     # one more frame than the ring holds is refused before any launch
-    d = r["fresh"](0)
+    d = r["d"]
+    d.set_state(0, *r["pstate"][0])
     with pytest.raises(qt.QtError) as e:
         d.decode(9, r["ov"][:1].repeat(9, axis=0))
     assert e.value.code == qt.QT_E_CONTEXT_FULL
@@ -614,61 +600,169 @@ def test_full_bf16_max_context_parity():
 
 
 @pytest.mark.timeout(900)
-def test_full_bf16_b32_sampled_parity():
-    # 32 streams with the ragged contexts the batched workload uses, decoded
-    # four frames per graph replay as the bench times them; the oracle
-    # computes four of the streams (streams are independent)
+def test_full_bf16_b32_parity():
+    # the multi-stream workload as the bench runs it: 32 streams whose seeded
+    # prompts have the ragged context lengths (uniform in [64, 2048]), each
+    # prefilled through the model on the GPU; six streams' states go to the
+    # oracle and every frame of those streams is compared (teacher-forced,
+    # one frame per call), then the free run
     m = synth.BIG
     wl = synth.WORKLOADS["bf16_b32"]
     w = synth.make_weights(m)
-    B, K, n = wl.batch, wl.frames_per_replay, 4
     lens = synth.make_context_lengths(wl)
-    sample = [0, 9, 22, 31]
+    prompts = [synth.make_prompt(wl, b, T=int(lens[b])) for b in range(wl.batch)]
+    sample = [0, 5, 9, 22, 27, 31]
     say("[bf16_b32] contexts", lens.tolist(), "checking streams", sample)
-    ov = synth.make_overlays(wl, n, B)
-    states = {b: synth.make_synthetic_state(wl, b, int(lens[b])) for b in sample}
-    o = _oracle_from_states(m, w, [states[b] for b in sample], lens[sample], int(lens[sample].max()) + n + 1)
-    oout = o.decode(n, ov[:, sample], dump=True)
-    floor = _state_noise_floor(m, w, states[sample[0]], int(lens[sample[0]]), ov[:, sample[:1]],
-                               {k: v[:, :1] for k, v in oout.items()})
-    say("[bf16_b32] oracle done; noise floor", {k: f"{v:.2e}" for k, v in floor.items()})
-    tk = _tol_map(m, {"floor": floor})
-    d = qt.Decoder(m, w, B, frames_per_replay=K, flags=qt.QT_F_DUMP)
-    ring = d.talker_ring()
-    gen = torch.Generator(device=ring.device).manual_seed(1234)
-    for b in range(B):
-        if b in sample:
-            d.inject_talker_state(b, *states[b])
-        else:  # the other streams: a state of the same length drawn on the device
-            L = int(lens[b])
-            kv = torch.randn((m.Lt, 2, m.nkv, L, m.hd), generator=gen, device=ring.device)
-            ring[b, :, :, :, :L, :] = kv.to(torch.bfloat16).view(torch.int16)
-            d.set_state(b, L, b % m.Vc, np.ones((m.H,), np.float32))
-    torch.cuda.synchronize()
-    forced = np.zeros((n, B, m.G), np.int32)
-    forced[:, sample] = oout["codes"]
-    codes = d.decode(n, ov, forced=forced)[:, sample]
-    gl = d.dump(qt.QT_DUMP_TALKER_LOGITS)[sample]
-    gp = d.dump(qt.QT_DUMP_PRED_LOGITS).transpose(1, 0, 2)[sample]
-    gb = d.dump(qt.QT_DUMP_BRIDGE)[sample]
-    worst = {}
-    for i in range(len(sample)):  # the last frame's dumps
-        worst["talker_logits"] = max(worst.get("talker_logits", 0), rel_l2(gl[i], oout["talker_logits"][n - 1, i]))
-        worst["pred_logits"] = max(worst.get("pred_logits", 0), rel_l2(gp[i], oout["pred_logits"][n - 1, i]))
-        worst["bridge"] = max(worst.get("bridge", 0), rel_l2(gb[i], oout["bridge"][n - 1, i]))
-    say("[bf16_b32] worst rel-L2 of the last frame:", {k: f"{v:.2e}" for k, v in worst.items()})
+    r = _prefilled_state_run(m, w, wl, 4, prompts, sample)
+    assert r["d"].path == qt.QT_PATH_GRAPH
+    _check(r, m, "bf16_b32")
+    r["d"].close()
+
+
+@pytest.mark.timeout(900)
+def test_full_bf16_b32_replay_of_four_frames_equals_one():
+    # four frames per graph replay (as the bench times the workload) decode
+    # the same codes and last-frame logits as one frame per replay, bit for bit
+    m = synth.BIG
+    wl = synth.WORKLOADS["bf16_b32"]
+    w = synth.make_weights(m)
+    lens = synth.make_context_lengths(wl)
+    prompts = [synth.make_prompt(wl, b, T=int(lens[b])) for b in range(wl.batch)]
+    ov = synth.make_overlays(wl, 8)
+    dw = qt.DeviceWeights(m, w, "cuda")
+    out = {}
+    for K in (1, 4):
+        say(f"[bf16_b32 replay] K = {K}: 32 prefills, 8 frames")
+        d = qt.Decoder(m, dw, wl.batch, frames_per_replay=K, flags=qt.QT_F_DUMP)
+        for b, (c, t) in enumerate(prompts):
+            d.prefill(b, c, t)
+        out[K] = (d.decode(8, ov), d.dump(qt.QT_DUMP_TALKER_LOGITS), d.dump(qt.QT_DUMP_PRED_LOGITS))
+        d.close()
+    assert np.array_equal(out[1][0], out[4][0])
+    assert np.array_equal(out[1][1].view(np.uint32), out[4][1].view(np.uint32))
+    assert np.array_equal(out[1][2].view(np.uint32), out[4][2].view(np.uint32))
+
+
+@pytest.mark.timeout(900)
+def test_reduced_long_prefill_parity():
+    # the 2,048-row prefill itself against the oracle's own prefill, on the
+    # full widths with two talker layers: 16 chunks of 128 rows, causal tiles
+    # across 8 attention tiles; last-row logits, bridge, code 0 and every
+    # cached K/V row
+    m = dataclasses.replace(_reduced(synth.BIG), P=4096)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["bf16_long_b1"], model=m)
+    codes, text = synth.make_prompt(wl, 0)
+    say("[reduced long prefill] oracle prefill of 2048 rows (2 layers)")
+    o = Oracle(m, w, 1, pcap=2048 + 1)
+    pre = o.prefill(0, codes, text, dump=True)
+    opos, oc0, obr = o.get_state(0)
+    d = qt.Decoder(m, w, 1, flags=qt.QT_F_DUMP)
+    d.prefill(0, codes, text)
+    pos, c0, br = d.get_state(0)
+    gl = d.dump(qt.QT_DUMP_TALKER_LOGITS)[0]
+    kv, _ = _read_state(d, 0, 2048)
+    worst = {"logits": rel_l2(gl, pre["logits"]), "bridge": rel_l2(br, obr)}
+    for layer in range(m.Lt):
+        ok, ov_ = o.get_cache(0, layer, 0, 2048)
+        worst[f"k{layer}"] = rel_l2(kv[layer, 0], ok)
+        worst[f"v{layer}"] = rel_l2(kv[layer, 1], ov_)
+    say("[reduced long prefill] rel-L2:", {k: f"{v:.2e}" for k, v in worst.items()})
+    assert pos == opos == 2048
     for k, v in worst.items():
-        assert v <= tk(k), f"bf16_b32: {k} rel-L2 {v} > {tk(k)}"
-    # teacher-forced decisions: a difference is only allowed at a near tie,
-    # judged with the logit error measured on the dumped last frame
-    err = {i: max(float(np.max(np.abs(gl[i] - oout["talker_logits"][n - 1, i]))),
-                  float(np.max(np.abs(gp[i] - oout["pred_logits"][n - 1, i])))) for i in range(len(sample))}
-    diff = list(zip(*np.nonzero(codes != oout["codes"])))
-    say(f"[bf16_b32] teacher-forced decisions differing: {len(diff)} of {codes.size}")
-    for f, i, j in diff:
-        rl = (oout["talker_logits"][f - 1, i] if f > 0 else None) if j == 0 else oout["pred_logits"][f, i, j - 1]
-        assert rl is not None, "code 0 of the first frame is the injected state's"
-        mg = margin(rl)
-        say(f"[bf16_b32] code flip frame {f} stream {sample[i]} code {j}: oracle margin {mg:.3e}, err {err[i]:.3e}")
-        assert mg <= 4 * err[i], f"bf16_b32: decision differs with margin {mg} > 4 x {err[i]}"
+        assert v <= 1e-2, f"reduced long prefill: {k} rel-L2 {v}"
+    if c0 != oc0:  # only at a near tie of the last row's logits
+        assert margin(pre["logits"]) <= 4 * float(np.max(np.abs(gl - pre["logits"])))
+
+
+@pytest.mark.parametrize("base", [synth.BIG, synth.BIG_Q8], ids=["bf16", "q8"])
+def test_ffn_width_not_multiple_of_256_parity(base):
+    # hidden 1,024 but FFN 2,080: the model takes the GEMV for every
+    # projection (the GEMM's row norms need sums of squares that only its own
+    # residual epilogue writes), at one and two streams on the per-op path
+    m = dataclasses.replace(base, Lt=2, Lp=1, Vt=4096, P=512, model_id=base.model_id + 40, F=2080)
+    w = synth.make_weights(m, random_q8_scales=True)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b1"], model=m, prompt=40)
+    for batch in (1, 2):
+        say(f"[ffn 2080 {base.name}] prompt 40, 3 frames, batch {batch}")
+        r = _forced_run(m, w, wl, 3, batch=batch)
+        assert r["d"].path == qt.QT_PATH_GRAPH
+        _check(r, m, f"ffn2080_{base.name}_b{batch}")
+
+
+def _tied_heads(m, w, wl, prompt):
+    """Weights whose heads tie exactly at the decisions of the oracle's first
+    frame: row 0 of each head becomes a copy of the row the oracle picked
+    there (when that row is not 0).  Decoded with the first frame's codes fed
+    back (teacher forcing), every head then sees the inputs it saw before, so
+    each of those logits is the maximum twice -- at 0 and at a row that the
+    persistent kernel gives another workgroup -- and the lowest index must
+    win.  Returns the weights, the first frame's codes (code 0 from the
+    prefill) and the indices of the tied decisions."""
+    o = Oracle(m, w, 1)
+    o.prefill(0, *prompt)
+    ov = synth.make_overlays(wl, 1, 1)
+    codes = o.decode(1, ov)["codes"]
+    w2 = dict(w)
+    w2["t_head"] = w["t_head"].copy()
+    w2["p_heads"] = [h.copy() for h in w["p_heads"]]
+    tied = []
+    for j in range(m.G):
+        c = int(codes[0, 0, j])
+        if c:
+            tab = w2["t_head"] if j == 0 else w2["p_heads"][j - 1]
+            tab[0] = (w["t_head"] if j == 0 else w["p_heads"][j - 1])[c]
+            tied.append(j)
+    return w2, codes, ov, tied
+
+
+@pytest.mark.parametrize("flags", [0, qt.QT_F_OPS], ids=["frame", "ops"])
+def test_exact_ties_pick_the_lowest_index(flags):
+    m = synth.TINY
+    wl = synth.WORKLOADS["tiny_f32_b1"]
+    w = synth.make_weights(m)
+    prompt = synth.make_prompt(wl, 0)
+    w2, codes, ov, tied = _tied_heads(m, w, wl, prompt)
+    assert len(tied) >= 8
+    o = Oracle(m, w2, 1)
+    o.prefill(0, *prompt)
+    oc = o.decode(1, ov, forced=codes)["codes"]
+    d = qt.Decoder(m, w2, 1, flags=flags)
+    assert d.path == (qt.QT_PATH_GRAPH if flags else qt.QT_PATH_FRAME)
+    d.prefill(0, *prompt)
+    gc = d.decode(1, ov, forced=codes)
+    say(f"[ties {flags}] tied decisions {tied}; codes", gc[0, 0].tolist())
+    assert all(oc[0, 0, j] == 0 for j in tied)  # the oracle's rule: lowest index
+    assert np.array_equal(gc, oc)                # F32: every decision equal
     d.close()
+
+
+def test_exact_ties_bf16_full_width():
+    # the same on the 1,024-wide bf16 model: 2,048-way heads spread over the
+    # persistent kernel's workgroups (one stream), and the MFMA GEMM + argmax
+    # kernel (two streams); the tied decisions must be 0 exactly, the others
+    # may differ from the oracle only at a near tie
+    m = _reduced(synth.BIG)
+    wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=40)
+    w = synth.make_weights(m)
+    prompt = synth.make_prompt(wl, 0)
+    w2, codes, ov, tied = _tied_heads(m, w, wl, prompt)
+    assert len(tied) >= 8
+    o = Oracle(m, w2, 1)
+    o.prefill(0, *prompt)
+    oout = o.decode(1, ov, forced=codes, dump=True)
+    for batch in (1, 2):
+        d = qt.Decoder(m, w2, batch, flags=qt.QT_F_DUMP)
+        for b in range(batch):
+            d.prefill(b, *prompt)
+        gc = d.decode(1, np.repeat(ov, batch, axis=1), forced=np.repeat(codes, batch, axis=1))
+        gl = d.dump(qt.QT_DUMP_PRED_LOGITS)
+        say(f"[ties bf16 b{batch}] tied {tied}; codes", gc[0, 0].tolist())
+        for b in range(batch):
+            assert all(gc[0, b, j] == 0 for j in tied), "a tie went to a higher index"
+            for j in range(1, m.G):
+                if gc[0, b, j] != oout["codes"][0, 0, j]:
+                    rl = oout["pred_logits"][0, 0, j - 1]
+                    err = float(np.max(np.abs(gl[j - 1, b] - rl)))
+                    assert margin(rl) <= 4 * err, f"code {j} differs away from a near tie"
+        d.close()
