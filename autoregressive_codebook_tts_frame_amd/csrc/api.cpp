@@ -181,6 +181,7 @@ struct qt_ctx {
   qtk::FrameArgs fa;       // persistent kernel arguments (path == QT_PATH_FRAME)
   int lds_limit = 0;       // LDS per workgroup on the device
   uint32_t tag_base = 1;   // running phase tag of the persistent kernel
+  void *scratch = nullptr; // this device's static exchange region (qt_decode_frame_noalloc)
   float inv_temp = 0.f;    // sampling: float(1/T), 0 = greedy (sampler.h)
   int32_t top_k = 0;       // sampling: the k largest logits compete (0: all)
   uint64_t seed = 0;
@@ -480,7 +481,9 @@ const char *frame_unsupported(const qt_model_desc &m, int B) {
 }
 
 int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
-                      const int32_t *forced);
+                      const int32_t *forced, bool static_scratch);
+int32_t decode_entry(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out, const int32_t *forced,
+                     bool static_scratch);
 
 bool ids_ok(const int32_t *p, size_t n, int32_t hi) {
   for (size_t i = 0; i < n; ++i)
@@ -701,6 +704,10 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
       fa.err = c->A<int32_t>(c->L.f_err);
       fa.trace = (c->flags & QT_F_TRACE) ? c->A<uint64_t>(c->L.f_trace) : nullptr;
       c->path = QT_PATH_FRAME;
+      // the device address of this device's static exchange region, for
+      // qt_decode_frame_noalloc (looked up here, once per device; a failure
+      // only disables that entry point)
+      if (qtk::frame_scratch_address(&c->scratch) != hipSuccess) c->scratch = nullptr;
     }
   }
   if (c->path == QT_PATH_GRAPH) {
@@ -779,6 +786,28 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
 
 int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
                         const int32_t *forced) {
+  return decode_entry(c, n, overlay_ids, codes_out, forced, false);
+}
+
+int32_t qt_decode_frame_noalloc(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
+                                const int32_t *forced) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  if (c->path != QT_PATH_FRAME)
+    return fail(c, QT_E_UNSUPPORTED, "qt_decode_frame_noalloc needs the persistent frame kernel (one stream)");
+  const size_t need = c->L.f_err + 64 - c->L.f_xch_begin;
+  if (need > qtk::kFrameScratchBytes)
+    return fail(c, QT_E_SIZE, "the exchange region needs %zu bytes, above the static maximum of %zu", need,
+                qtk::kFrameScratchBytes);
+  if (!c->scratch) return fail(c, QT_E_HIP, "the static scratch address was not found at qt_init");
+  return decode_entry(c, n, overlay_ids, codes_out, forced, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t decode_entry(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out, const int32_t *forced,
+                     bool static_scratch) {
   if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
   const Dims &d = c->d;
   const int B = c->B;
@@ -792,7 +821,7 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
   if (!ids_ok(overlay_ids, (size_t)n * B, d.Vt)) return fail(c, QT_E_RANGE, "overlay id outside [0, %d)", d.Vt);
   if (forced && !ids_ok(forced, (size_t)n * B * d.G, d.Vc)) return fail(c, QT_E_RANGE, "forced code outside [0, %d)", d.Vc);
 
-  const int32_t rc = decode_chunks(c, n, overlay_ids, codes_out, forced);
+  const int32_t rc = decode_chunks(c, n, overlay_ids, codes_out, forced, static_scratch);
   if (rc == QT_E_HIP)
     // work was launched: the slots may hold partial results (ring rows,
     // bridge, position), so they must be restored before the next decode
@@ -800,12 +829,8 @@ int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_
   return rc;
 }
 
-}  // extern "C"
-
-namespace {
-
 int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
-                      const int32_t *forced) {
+                      const int32_t *forced, bool static_scratch) {
   const Dims &d = c->d;
   const int B = c->B;
   hipStream_t s = c->stream;
@@ -830,11 +855,25 @@ int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t 
       memcpy(fu, forced + (size_t)f0 * B * d.G, sizeof(int32_t) * nf * B * d.G);
       HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.cin), fu, sizeof(int32_t) * nf * B * d.G, hipMemcpyHostToDevice, s));
     }
-    if (c->path == QT_PATH_FRAME) {
+    qtk::FrameArgs fa = c->fa;
+    if (c->path == QT_PATH_FRAME && static_scratch) {
+      // The exchange words and the error flag live in this device's static
+      // region, at their arena offsets.  Other contexts' calls leave their
+      // own tags there, so the region is cleared first (tag 0 is never a
+      // phase's tag): no word can match a tag of this launch before this
+      // launch writes it.  (Calls that overlap on one device race.)
+      uint8_t *base = (uint8_t *)c->scratch - c->L.f_xch_begin;
+      fa.xq = (uint64_t *)(base + c->L.f_xq); fa.qkvb = (uint64_t *)(base + c->L.f_qkv);
+      fa.ob = (uint64_t *)(base + c->L.f_o); fa.zb = (uint64_t *)(base + c->L.f_z);
+      fa.amax = (uint64_t *)(base + c->L.f_amax); fa.part = (uint64_t *)(base + c->L.f_part);
+      fa.err = (int32_t *)(base + c->L.f_err);
+      HIPCHK(c, hipMemsetAsync(c->scratch, 0, c->L.f_err + 64 - c->L.f_xch_begin, s));
+    } else if (c->path == QT_PATH_FRAME) {
       int32_t *zero = c->pin_up + c->pu_scalar + 4;
       zero[0] = 0;
-      HIPCHK(c, hipMemcpyAsync(c->fa.err, zero, sizeof(int32_t), hipMemcpyHostToDevice, s));
-      qtk::FrameArgs fa = c->fa;
+      HIPCHK(c, hipMemcpyAsync(fa.err, zero, sizeof(int32_t), hipMemcpyHostToDevice, s));
+    }
+    if (c->path == QT_PATH_FRAME) {
       fa.n_frames = nf;
       fa.pos0 = c->pos_host[0];
       const char *why = nullptr;
@@ -865,7 +904,7 @@ int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t 
     int32_t *errh = c->pin_up + c->pu_scalar + 8;
     errh[0] = 0;
     if (c->path == QT_PATH_FRAME)
-      HIPCHK(c, hipMemcpyAsync(errh, c->fa.err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+      HIPCHK(c, hipMemcpyAsync(errh, fa.err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
     HIPCHK(c, hipStreamSynchronize(s));
     if (errh[0])
       return fail(c, QT_E_HIP, "frame kernel: an exchange wait timed out (the slot must be restored by "

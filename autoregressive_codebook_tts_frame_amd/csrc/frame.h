@@ -80,6 +80,11 @@ hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s);
 // True if a.nwg workgroups of the planned kernel (a.lds_bytes of LDS each)
 // fit on the ncu compute units at once, by the occupancy query.
 bool frame_coresident(const FrameArgs &a, int ncu);
+// Device address of this device's static scratch array (kFrameScratchBytes),
+// looked up once per device with that device current.
+constexpr size_t kFrameScratchBytes = 512u << 10;
+constexpr int kMaxDevices = 64;
+hipError_t frame_scratch_address(void **ptr);
 // the (weights, head dim, GQA group, bf16 ring) combinations instantiated
 bool frame_variant_supported(int wt, int hd, int g, int kv_bf16);
 // Plan a launch whose talker positions reach max_pos: attention workgroups,

@@ -33,6 +33,8 @@
 //    registers as the predictor picks each code, in code order.
 #include <math.h>
 
+#include <mutex>
+
 #include "frame.h"
 #include "kernels.h"
 #include "sampler.h"
@@ -1532,6 +1534,30 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
 #define QT_FRAME_VARIANTS(X) X(W_F32, 64, 2, false) X(W_BF16, 128, 2, true) X(W_Q8, 128, 2, true)
 
 }  // namespace
+
+// The persistent kernel's exchange words and error flag for callers that
+// cannot allocate (qt_decode_frame_noalloc): one array per device, held until
+// the process ends.  In host code its name is only a stand-in for the device
+// symbol; the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kFrameScratchBytes];
+
+hipError_t frame_scratch_address(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 bool frame_variant_supported(int wt, int hd, int g, int kvb) {
 #define X(W, HD_, G_, K_) if (wt == W && hd == HD_ && g == G_ && (kvb != 0) == K_) return true;

@@ -34,7 +34,8 @@ QT_KERNEL_GEMV_GATE_UP = 1
 
 EXPORTS = ("qt_abi_version", "qt_query_sizes", "qt_init", "qt_prefill", "qt_decode_frame",
            "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_time_kernel",
-           "qt_set_sampler", "qt_path", "qt_free", "qt_last_error", "qt_stream_read")
+           "qt_set_sampler", "qt_path", "qt_free", "qt_last_error", "qt_stream_read",
+           "qt_decode_frame_noalloc")
 
 
 class qt_model_desc(C.Structure):
@@ -88,6 +89,8 @@ def _load():
     lib.qt_prefill.restype = i32
     lib.qt_decode_frame.argtypes = [vp, i32, vp, vp, vp]
     lib.qt_decode_frame.restype = i32
+    lib.qt_decode_frame_noalloc.argtypes = [vp, i32, vp, vp, vp]
+    lib.qt_decode_frame_noalloc.restype = i32
     lib.qt_get_slot_state.argtypes = [vp, i32, vp, vp, vp]
     lib.qt_get_slot_state.restype = i32
     lib.qt_set_slot_state.argtypes = [vp, i32, i32, i32, vp]
@@ -167,6 +170,12 @@ def qt_decode_frame(ctx, n_frames: int, overlay_ids: np.ndarray, codes_out: np.n
                     forced_codes: Optional[np.ndarray] = None):
     _check(lib.qt_decode_frame(ctx, n_frames, _np_ptr(overlay_ids), _np_ptr(codes_out),
                                _np_ptr(forced_codes)), ctx)
+
+
+def qt_decode_frame_noalloc(ctx, n_frames: int, overlay_ids: np.ndarray, codes_out: np.ndarray,
+                            forced_codes: Optional[np.ndarray] = None):
+    _check(lib.qt_decode_frame_noalloc(ctx, n_frames, _np_ptr(overlay_ids), _np_ptr(codes_out),
+                                       _np_ptr(forced_codes)), ctx)
 
 
 def qt_get_slot_state(ctx, slot: int, hidden: int):
@@ -327,12 +336,14 @@ class Decoder:
     def set_sampler(self, temperature: float, seed: int = 0, top_k: int = 0):
         qt_set_sampler(self.ctx, temperature, top_k, seed)
 
-    def decode(self, n: int, overlay: np.ndarray, forced: Optional[np.ndarray] = None) -> np.ndarray:
+    def decode(self, n: int, overlay: np.ndarray, forced: Optional[np.ndarray] = None,
+               noalloc: bool = False) -> np.ndarray:
+        """qt_decode_frame (qt_decode_frame_noalloc with noalloc=True)."""
         m = self.m
         ov = np.ascontiguousarray(overlay, dtype=np.int32).reshape(n, self.B)
         fc = None if forced is None else np.ascontiguousarray(forced, dtype=np.int32).reshape(n, self.B, m.G)
         out = np.empty((n, self.B, m.G), np.int32)
-        qt_decode_frame(self.ctx, n, ov, out, fc)
+        (qt_decode_frame_noalloc if noalloc else qt_decode_frame)(self.ctx, n, ov, out, fc)
         return out
 
     @property

@@ -214,6 +214,24 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
 int32_t qt_decode_frame(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_ids,
                         int32_t *codes_out, const int32_t *forced_codes);
 
+/* For callers that cannot allocate device memory (code that must not call
+   hipMalloc: tight serving loops, harnesses that forbid allocation): the same
+   decode as qt_decode_frame, with the same arguments, results and errors,
+   but the persistent kernel's scratch -- its tagged exchange words and its
+   error flag -- lives in a static device array of the library (512 KiB, one
+   per device, held until the process ends) instead of the context's arena.
+   The call allocates nothing: it clears the used part of that array on the
+   context's stream (other contexts' calls leave their tags there), launches,
+   and copies the codes back through the pinned staging that qt_init made.
+   Every context on a device shares that device's array: calls that overlap
+   on one device race and must be serialised by the caller.
+   Errors: those of qt_decode_frame; QT_E_UNSUPPORTED if the context does not
+   decode on the persistent kernel (qt_path() != QT_PATH_FRAME); QT_E_SIZE if
+   the model's exchange region exceeds 512 KiB (the 28-layer, 1,024-wide
+   model needs 436 KiB). */
+int32_t qt_decode_frame_noalloc(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_ids,
+                                int32_t *codes_out, const int32_t *forced_codes);
+
 /* Snapshot / restore of a slot's non-ring state (the library's own calls,
    used to restart a decode from a saved or injected state): next talker
    position, the pending code 0, and the bridge (host float [H]; the bridge
