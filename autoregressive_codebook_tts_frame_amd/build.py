@@ -25,19 +25,32 @@ def _run(cmd):
         raise RuntimeError("hipcc failed")
 
 
+BUILD_DIR = os.path.join(HERE, "_build")
+PROBE = os.path.join(BUILD_DIR, "exchange_probe")
+
+
 def build_library(out: str = LIB, verbose: bool = False) -> str:
-    objs = []
-    build_dir = os.path.join(HERE, "_build")
-    os.makedirs(build_dir, exist_ok=True)
+    """libqt.so from the three sources (compiled in parallel), and the
+    exchange-latency probe program beside the objects."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cmds, objs = [], []
     for src, gpu in (("kernels.hip", True), ("frame.hip", True), ("api.cpp", False)):
-        obj = os.path.join(build_dir, src + ".o")
+        obj = os.path.join(BUILD_DIR, src + ".o")
         cmd = [HIPCC, *COMMON, *(GPU_FLAGS if gpu else []), "-c", os.path.join(CSRC, src), "-o", obj]
         if gpu:
             cmd[1:1] = ["-x", "hip"]
-        if verbose:
-            print(" ".join(cmd))
-        _run(cmd)
+        cmds.append(cmd)
         objs.append(obj)
+    cmds.append([HIPCC, "-x", "hip", "-O3", "-std=c++17", *GPU_FLAGS, os.path.join(HERE, "exchange_probe.hip"),
+                 "-o", PROBE + ".tmp"])
+    if verbose:
+        for c in cmds:
+            print(" ".join(c))
+    with ThreadPoolExecutor(len(cmds)) as ex:
+        list(ex.map(_run, cmds))
+    os.replace(PROBE + ".tmp", PROBE)
     tmp = out + ".tmp"
     _run([HIPCC, "-shared", *GPU_FLAGS, "-o", tmp, *objs])
     os.replace(tmp, out)
