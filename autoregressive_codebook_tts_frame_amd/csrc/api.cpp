@@ -473,7 +473,6 @@ hipError_t enqueue_replay(qt_ctx *c) {
 const char *frame_unsupported(const qt_model_desc &m, int B) {
   const Dims d = dims_of(m);
   if (B != 1) return "the persistent kernel decodes one stream";
-  if (m.lin_type == QT_LIN_Q4) return "4-bit weights run on the per-op path";
   if (!qtk::frame_variant_supported(wtype_of(m), d.hd, d.nq / d.nkv, m.kv_bf16)) return "no persistent-kernel variant";
   if (m.lin_type != QT_LIN_F32 && !(m.act_bf16 && m.tab_bf16)) return "bf16/q8/q4 weights need bf16 operands and tables";
   if (m.lin_type == QT_LIN_F32 && (m.act_bf16 || m.tab_bf16)) return "f32 weights need f32 operands and tables";
@@ -685,7 +684,7 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
       fa.pl = c->A<qtk::LayerDev>(c->L.f_pl);
       fa.code_emb = c->code_emb; fa.text_emb = c->text_emb; fa.t_norm = c->t_norm; fa.p_norm = c->p_norm;
       fa.head_w = c->A<const void *>(c->L.f_heads);
-      fa.head_sc = m.lin_type == QT_LIN_Q8 ? c->A<const uint16_t *>(c->L.f_heads_sc) : nullptr;
+      fa.head_sc = (m.lin_type == QT_LIN_Q8 || m.lin_type == QT_LIN_Q4) ? c->A<const uint16_t *>(c->L.f_heads_sc) : nullptr;
       fa.pos = c->A<int32_t>(c->L.pos); fa.c0 = c->A<int32_t>(c->L.c0); fa.bridge = c->A<float>(c->L.bridge);
       fa.ctl = c->A<int32_t>(c->L.ctl); fa.cin = c->A<int32_t>(c->L.cin); fa.cout = c->A<int32_t>(c->L.cout);
       fa.overlay = c->A<int32_t>(c->L.overlay);

@@ -45,6 +45,7 @@ namespace {
 constexpr int NW = 5;            // compute waves of a GEMV workgroup
 constexpr int NT = 64 * NW;      // their threads
 constexpr int NLW = 3;           // loader waves (each keeps its own loads in flight)
+constexpr int MAXWB = 16;        // q4: 1 KB raw blocks per loader wave and slice
 constexpr int NTB = NT + 64 * NLW;  // two waves per SIMD
 constexpr int ANT = 512;         // threads of an attention workgroup
 constexpr int ANW = ANT / 64;    // its waves
@@ -212,6 +213,7 @@ struct Common {
   int abort;
   uint32_t cbar;   // compute-wave barrier arrivals
   uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
+  uint32_t lbar;   // loader-wave barrier arrivals (q4 widening)
   uint64_t ltime;  // tracing: when a loader wave's part of the last slice had landed
   Share sh[PH_END];  // this GEMV workgroup's rows, per phase type
 };
@@ -396,25 +398,33 @@ __device__ __forceinline__ Share share_calc(const FrameArgs &a, int type, int gi
   return s;
 }
 
-template <int WT> struct WEsz;
-template <> struct WEsz<W_F32> { static constexpr int v = 4; };
-template <> struct WEsz<W_BF16> { static constexpr int v = 2; };
-template <> struct WEsz<W_Q8> { static constexpr int v = 1; };
-// 1 KB blocks a weight row of width H may span: its normalized operand lives
-// in registers (a q8 chunk takes twice the operand words of a bf16 one)
+// Bytes per weight in a weight slot in LDS: f32, bf16 and q8 rows stay as
+// they are in HBM (q8 codes are widened to bf16 pairs in registers, by the
+// GEMV); q4 rows are widened to bf16 by the loader waves once they land
+// (exact: |c - 8| <= 8).  The block scales stay beside the weights and are
+// applied to each chunk's dot product.
+template <int WT> struct WEsz { static constexpr int v = WT == W_F32 ? 4 : WT == W_Q8 ? 1 : 2; };
+// q4 slices are widened in LDS
+__host__ __device__ constexpr bool w_widened(int wt) { return wt == W_Q4; }
+// Bytes of a weight row of width K as stored in HBM.
+__host__ __device__ constexpr int raw_rowb(int wt, int K) {
+  return wt == W_F32 ? 4 * K : wt == W_BF16 ? 2 * K : wt == W_Q8 ? K : K / 2;
+}
+// 1 KB blocks a weight row of width H may span in LDS: its normalized operand
+// lives in registers (a q8 chunk takes twice the operand words of a bf16 one)
 __host__ __device__ constexpr int nb_hidden(int wt) { return wt == W_Q8 ? 1 : 2; }
 // 1 KB blocks of the O and down rows (widths nq*hd and F), whose operand
 // chunks are also held in registers per item
 __host__ __device__ constexpr int nb_wide(int wt) { return wt == W_Q8 ? 4 : 6; }
 
-// weight row (and q8 scale row) of output row n, matrix mat
+// weight row (bytes rb in HBM) and block-scale row of output row n, matrix mat
 __device__ __forceinline__ void wrow_of(const FrameArgs &a, const Common &cm, const Ph &p, int n, int mat,
-                                        int K, int esz, const uint8_t *&w, const uint8_t *&sc) {
+                                        int K, int rb, const uint8_t *&w, const uint8_t *&sc) {
   const int qd = a.nq * a.hd, kd = a.nkv * a.hd;
   int which = 0, r = n;
   if (p.type == PH_HEAD) {
     const int hi = p.stack ? 0 : 1 + p.step;
-    w = (const uint8_t *)cm.head_w[hi] + (size_t)n * K * esz;
+    w = (const uint8_t *)cm.head_w[hi] + (size_t)n * rb;
     sc = cm.head_sc[hi] ? (const uint8_t *)(cm.head_sc[hi] + (size_t)n * (K / 32)) : nullptr;
     return;
   }
@@ -429,7 +439,7 @@ __device__ __forceinline__ void wrow_of(const FrameArgs &a, const Common &cm, co
     default: which = LW_D; break;
   }
   const LayerTab &T = tab_of(a, cm, p.stack, p.layer);
-  w = (const uint8_t *)T.w[which] + (size_t)r * K * esz;
+  w = (const uint8_t *)T.w[which] + (size_t)r * rb;
   sc = T.sc[which] ? (const uint8_t *)(T.sc[which] + (size_t)r * (K / 32)) : nullptr;
 }
 __device__ __forceinline__ const void *gain_of(const FrameArgs &a, const Common &cm, const Ph &p) {
@@ -438,15 +448,24 @@ __device__ __forceinline__ const void *gain_of(const FrameArgs &a, const Common 
   if (p.type == PH_HEAD) return p.stack ? a.t_norm : a.p_norm;
   return nullptr;
 }
-// slot layout: weights [R*NM rows], q8 scales [R*NM][K/32] (1 KB aligned), gain [H]
+// slot layout: weights [R*NM rows] (in their LDS format), block scales
+// [R*NM][K/32] (q8 / q4, 1 KB aligned), gain [H].  A q4 slice lands in the
+// tail of the weight area (raw_off) and is widened in place.
 __device__ __forceinline__ uint32_t scales_off(const Share &s, int esz) { return (uint32_t)(s.R * s.NM) * s.K * esz; }
-__device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool q8) {
-  return scales_off(s, esz) + (q8 ? up1k((uint32_t)(s.R * s.NM) * (s.K / 16)) : 0u);
+__device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool blocked) {
+  return scales_off(s, esz) + (blocked ? up1k((uint32_t)(s.R * s.NM) * (s.K / 16)) : 0u);
+}
+// q4 rows land 1 KB-padded (raw row stride bpr KB), at the end of the weight
+// area; the frame kernel's K (a multiple of 512) keeps that inside it
+template <int WT>
+__device__ __forceinline__ uint32_t raw_off(const Share &s) {
+  if constexpr (!w_widened(WT)) return 0u;
+  return (uint32_t)(s.R * s.NM) * (s.K * WEsz<WT>::v - ((raw_rowb(WT, s.K) + 1023) & ~1023));
 }
 
 // Issue this loader wave's part of the direct-to-LDS loads of phase p's
 // weight slice: loader wave li takes weight blocks [li nb / NLW, (li + 1) nb /
-// NLW) and the last one also the q8 scales and the norm gain.  Every 1 KB
+// NLW) and the last one also the block scales and the norm gain.  Every 1 KB
 // block is one instruction.  A wave can keep only a limited number of these
 // loads in flight, so several loader waves land a slice sooner.
 template <int WT>
@@ -455,31 +474,37 @@ __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, 
   const int lane = threadIdx.x & 63;
   const int li = (int)(threadIdx.x >> 6) - NW;
   const Share s = cm.sh[p.type];
-  const int rowb = s.K * ESZ, bpr = rowb >> 10, U = s.R * s.NM;
+  // rows of rb bytes in 1 KB blocks, block b at raw_off + b KB; in a row's
+  // last block lanes past its end load its last chunk again (so that every
+  // lane of every load is on: a lane mask here slows the whole slice's issue)
+  const int rb = raw_rowb(WT, s.K), bpr = (rb + 1023) >> 10, U = s.R * s.NM;
+  const uint32_t ro = slot + raw_off<WT>(s);
   const int nb = U * bpr, b1 = (li + 1) * nb / NLW;
   for (int b = li * nb / NLW; b < b1;) {
     const int u = b / bpr;
     const uint8_t *w, *sc;
-    wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
-    for (int cb = b - u * bpr; cb < bpr && b < b1; ++cb, ++b)
-      dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
+    wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, rb, w, sc);
+    for (int cb = b - u * bpr; cb < bpr && b < b1; ++cb, ++b) {
+      if constexpr (w_widened(WT)) dma16(w + min(cb * 1024 + lane * 16, rb - 16), ro + (uint32_t)b * 1024u);
+      else dma16(w + cb * 1024 + lane * 16, ro + (uint32_t)b * 1024u);
+    }
   }
   if (li != NLW - 1) return;
-  if constexpr (WT == W_Q8) {
+  if constexpr (w_blocked(WT)) {
     const int spu = s.K / 256, n = U * spu;  // 16-byte scale chunks per row, in all
     const uint32_t so = scales_off(s, ESZ);
     for (int sb = 0; sb * 64 < n; ++sb) {
       const int idx = min(sb * 64 + lane, n - 1);
       const int u = idx / spu, k = idx - u * spu;
       const uint8_t *w, *sc;
-      wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, ESZ, w, sc);
+      wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, rb, w, sc);
       dma16(sc + k * 16, slot + so + (uint32_t)sb * 1024u);
     }
   }
   const void *g = gain_of(a, cm, p);
   if (g) {
     const int n = a.H * (a.tab_bf16 ? 2 : 4) / 16;
-    const uint32_t go = gain_off(s, ESZ, WT == W_Q8);
+    const uint32_t go = gain_off(s, ESZ, w_blocked(WT));
     for (int gb = 0; gb * 64 < n; ++gb)
       dma16((const uint8_t *)g + min(gb * 64 + lane, n - 1) * 16, slot + go + (uint32_t)gb * 1024u);
   }
@@ -488,14 +513,15 @@ __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), c, false);
 }
-// int8 bytes b, b+1 of w as a bf16 pair (exact: |q| <= 127)
+// int8 bytes b, b+1 of w as a bf16 pair (exact: |q| <= 128)
 __device__ __forceinline__ uint32_t i8pair(uint32_t w, int b) {
   const float lo = (float)(int8_t)(w >> (8 * b)), hi = (float)(int8_t)(w >> (8 * b + 8));
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
-// The operand elements that meet one 16-byte weight chunk: 8 bf16 pairs for
-// q8 (a, b), 4 pairs for bf16 (a), 4 floats for f32 (a).
+// The operand elements that meet one 16-byte weight chunk in LDS: 8 bf16
+// pairs for q8 (a, b), 4 pairs for bf16 and widened q4 (a), 4 floats for
+// f32 (a).
 struct OpC {
   uint4 a, b;
 };
@@ -513,11 +539,14 @@ __device__ __forceinline__ OpC op_lds(const uint32_t *op, int c) {
   return x;
 }
 
-// 16-byte weight chunk c of a row . its operand elements
+// 16-byte weight chunk c of a row (in LDS) . its operand elements: a q8
+// chunk is 16 codes of half a block, a (widened) q4 chunk 8 bf16 weights of
+// a quarter block; the block scale multiplies the chunk's dot product
 template <int WT>
 __device__ __forceinline__ float chunk_dot(uint4 w, const OpC &x, int c, const uint8_t *scl) {
-  if constexpr (WT == W_BF16) {
-    return dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
+  if constexpr (WT == W_F32) {
+    return __uint_as_float(w.x) * __uint_as_float(x.a.x) + __uint_as_float(w.y) * __uint_as_float(x.a.y) +
+           __uint_as_float(w.z) * __uint_as_float(x.a.z) + __uint_as_float(w.w) * __uint_as_float(x.a.w);
   } else if constexpr (WT == W_Q8) {
     float s = dot2(i8pair(w.x, 0), x.a.x, 0.f);
     s = dot2(i8pair(w.x, 2), x.a.y, s);
@@ -529,8 +558,71 @@ __device__ __forceinline__ float chunk_dot(uint4 w, const OpC &x, int c, const u
     s = dot2(i8pair(w.w, 2), x.b.w, s);
     return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
   } else {
-    return __uint_as_float(w.x) * __uint_as_float(x.a.x) + __uint_as_float(w.y) * __uint_as_float(x.a.y) +
-           __uint_as_float(w.z) * __uint_as_float(x.a.z) + __uint_as_float(w.w) * __uint_as_float(x.a.w);
+    const float d = dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
+    if constexpr (w_blocked(WT)) return d * f16_to_f32(((const uint16_t *)scl)[c >> 2]);
+    return d;
+  }
+}
+
+// Barrier of the loader waves alone (an LDS counter; gen counts arrivals)
+__device__ __forceinline__ bool loader_barrier(const FrameArgs &a, Common &cm, uint32_t &gen) {
+  gen += NLW;
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(&cm.lbar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (uint32_t spins = 0; __hip_atomic_load(&cm.lbar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < gen; ++spins) {
+    if (spins > SPIN_LIMIT) { err_set(a.err); return false; }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Widen a landed q4 slice to bf16 rows in place (loader waves, each after
+// waiting for its own loads).  Each loader lane reads back the raw
+// 16-byte chunks that its own direct-to-LDS loads wrote (dma_slice's block
+// split), all of them before the one loader barrier, then writes each one's
+// weights as bf16: the chunk at byte o of raw row u becomes bf16 chunks
+// 4 (u rb + o) / 16 .. + 3 (rb raw row bytes).  The raw rows lie in the tail of the weight area, so these writes
+// overwrite raw bytes, but only after every lane has read its own.
+template <int WT>
+__device__ __forceinline__ bool widen_slice(const FrameArgs &a, Common &cm, const Ph &p, uint8_t *slot,
+                                            uint32_t &gen) {
+  if constexpr (!w_widened(WT)) {
+    return true;
+  } else {
+    constexpr int RHO = 4;  // bf16 chunks per raw chunk
+    const int lane = threadIdx.x & 63;
+    const int li = (int)(threadIdx.x >> 6) - NW;
+    const Share s = cm.sh[p.type];
+    const int rb = raw_rowb(WT, s.K), bpr = (rb + 1023) >> 10, nb = s.R * s.NM * bpr;
+    const int b0 = li * nb / NLW, n = (li + 1) * nb / NLW - b0;  // n <= MAXWB (frame_plan)
+    const uint8_t *raw = slot + raw_off<WT>(s);
+    uint4 v[MAXWB];
+    int off[MAXWB];  // unpadded raw offset u rb + o of this lane's chunk of each block (-1: none)
+#pragma unroll
+    for (int i = 0; i < MAXWB; ++i) {
+      const int bb = b0 + min(i, n - 1), u = bb / bpr, cb = bb - u * bpr;
+      const int o = cb * 1024 + lane * 16;
+      off[i] = i < n && o < rb ? u * rb + o : -1;
+      v[i] = *(const uint4 *)(raw + (bb < 0 ? 0 : bb * 1024 + lane * 16));
+    }
+    if (!loader_barrier(a, cm, gen)) return false;  // every lane's raw chunks are in registers
+#pragma unroll
+    for (int i = 0; i < MAXWB; ++i) {
+      if (off[i] < 0) continue;
+      const uint32_t r[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint4 *dst = (uint4 *)(slot + RHO * off[i]);
+#pragma unroll
+      for (int h = 0; h < RHO; ++h) {
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // byte k of word h: codes of weights 8 h + 2 k (low nibble) and 8 h + 2 k + 1, as c - 8
+          const uint32_t byte = (r[h] >> (8 * k)) & 0xffu;
+          o[k] = pack2((float)((int)(byte & 15u) - 8), (float)((int)(byte >> 4) - 8));
+        }
+        dst[h] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    return true;
   }
 }
 
@@ -563,7 +655,7 @@ __device__ __forceinline__ float gain_at(const FrameArgs &a, const uint8_t *g, i
   return a.tab_bf16 ? __uint_as_float((uint32_t)((const uint16_t *)g)[e] << 16) : ((const float *)g)[e];
 }
 // bf16 pairs of RMSNorm(x) * g for elements e0 .. e0 + 7
-// (bf16 and q8 weights run with bf16 tables and gains, f32 weights with f32
+// (bf16, q8 and q4 weights run with bf16 tables and gains, f32 weights with f32
 // ones: the kernel's weight type fixes the gains' format at compile time)
 template <bool TB>
 __device__ __forceinline__ uint4 norm8(const FrameArgs &a, const float *x, const uint8_t *g, float r, int e0) {
@@ -589,7 +681,7 @@ __device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, co
   if constexpr (WT == W_Q8) {
     o.a = norm8<true>(a, x, g, r, 16 * c);
     o.b = norm8<true>(a, x, g, r, 16 * c + 8);
-  } else if constexpr (WT == W_BF16) {
+  } else if constexpr (WT != W_F32) {
     o.a = norm8<true>(a, x, g, r, 8 * c);
     o.b = o.a;
   } else {
@@ -608,7 +700,7 @@ __device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, co
 // table row (bf16 or f32) element pairs of this thread -> v[2 * HPAIR]
 // (zero beyond the row: every element is written, so no value is carried
 // over from an earlier phase)
-// (TB: bf16 tables, which the bf16 and q8 kernels always have)
+// (TB: bf16 tables, which every kernel but the f32 one has)
 template <bool TB>
 __device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, size_t row, float *v) {
   const int tid = threadIdx.x;
@@ -725,7 +817,7 @@ __device__ __forceinline__ void normed_items_m(const FrameArgs &a, const Common 
   constexpr int NBH = nb_hidden(WT);
   const int lane = threadIdx.x & 63;
   const Share s = cm.sh[type];
-  const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
+  const uint8_t *gain = sp + gain_off(s, ESZ, w_blocked(WT));
   const int bpr = a.H * ESZ >> 10;
   const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
   OpC xo[2][NBH];
@@ -750,7 +842,7 @@ __device__ __forceinline__ void normed_items_m(const FrameArgs &a, const Common 
       // SiLU(g) * u with the hardware exp and reciprocal (a few ulp)
       const float z0 = acc[0][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[0][m])) * acc[1][m];
       const float z1 = acc[2][m] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[2][m])) * acc[3][m];
-      if constexpr (WT != W_F32) {  // bf16 operands (the bf16 and q8 kernels always have them)
+      if constexpr (WT != W_F32) {  // bf16 operands (every kernel but the f32 one has them)
         if (lane < a.rep) tput(a.zb + lane * a.rep_stride + (size_t)m * (a.F / 2) + s.r0 / 2 + it, pack2(z0, z1), tag);
       } else if (lane < 2 * a.rep) {
         const int e = lane & 1;
@@ -771,19 +863,21 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
 }
 
 // The loader waves: stream each GEMV phase's weight slice (a part each) into
-// its LDS slot one phase ahead and meet the compute waves once per phase,
-// right after their inputs are in.
+// its LDS slot one phase ahead, widen q4 slices to bf16 once they land,
+// and meet the compute waves once per phase, right after their inputs are in.
 template <int WT>
 __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, const Lds &L, unsigned char *smem) {
-  const uint32_t s0 = lds_addr(smem + L.slot0), s1 = lds_addr(smem + L.slot1);
+  uint8_t *const p0 = smem + L.slot0, *const p1 = smem + L.slot1;
   Ph cur{PH_QKV, 0, 0, 0, 0};
-  dma_slice<WT>(a, cm, cur, s0);
+  uint32_t lgen = 0;  // loader-barrier arrivals counted so far
+  dma_slice<WT>(a, cm, cur, lds_addr(p0));
   wait_vm();
+  if (!widen_slice<WT>(a, cm, cur, p0, lgen)) return;
   if (a.trace) cm.ltime = wall_clock64();
   int slot = 0;
   uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
   uint32_t seq = 1;           // phase index of cur + 1 (its tag is tag_base + seq)
-  bool have_next = false;     // the next phase's slice is already in its slot
+  bool have_next = false;     // the next phase's slice was issued during the last phase
   // until every compute wave has finished the current phase's GEMV
   auto wait_gemv = [&]() -> bool {
     for (uint32_t spins = 0; __hip_atomic_load(&cm.gdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < done;
@@ -796,18 +890,19 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
   while (cur.type != PH_END) {
     const Ph ng = next_gemv_phase(a, cur, a.pos0);
     __syncthreads();  // the compute waves have this phase's inputs (and are done with the last phase's slot)
-    if (cm.abort) return;
+    if (cm.abort) break;
     done += NW;
+    uint8_t *const cslot = slot ? p1 : p0, *const nslot = a.two_slots && !slot ? p1 : p0;
     if (a.two_slots && (cur.type == PH_GU || cur.type == PH_QKV)) {
       // its items first (the next phase waits for every one of them), then
       // the next slice
       const int M = cur.stack == 0 && cur.step == 0 ? 2 : 1;
-      normed_items<WT>(a, cm, cur.type, (const float *)(smem + L.xres), smem + (slot ? L.slot1 : L.slot0), M,
-                       a.tag_base + seq, (int)(threadIdx.x >> 6), NW + NLW);
+      normed_items<WT>(a, cm, cur.type, (const float *)(smem + L.xres), cslot, M, a.tag_base + seq,
+                       (int)(threadIdx.x >> 6), NW + NLW);
     }
     if (ng.type != PH_END && !have_next) {
-      if (!a.two_slots && !wait_gemv()) return;  // one slot: it is free once this phase's GEMV is done
-      dma_slice<WT>(a, cm, ng, a.two_slots && !slot ? s1 : s0);
+      if (!a.two_slots && !wait_gemv()) break;  // one slot: it is free once this phase's GEMV is done
+      dma_slice<WT>(a, cm, ng, lds_addr(nslot));
     }
     have_next = false;
     if (a.two_slots && cur.type == PH_QKV && ng.type == PH_O) {
@@ -816,11 +911,14 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
       // slot as soon as its GEMV is done, instead of competing later with the
       // exchange before the gate/up phase.
       const Ph n2 = next_gemv_phase(a, ng, a.pos0);
-      if (!wait_gemv()) return;
-      dma_slice<WT>(a, cm, n2, slot ? s1 : s0);
-      have_next = true;  // skipped at the O phase's meeting
+      if (!wait_gemv()) break;
+      dma_slice<WT>(a, cm, n2, lds_addr(cslot));
+      have_next = true;  // not loaded again at the O phase's meeting; widened there (q4)
     }
     wait_vm();
+    // ng's slice (loaded now, or during the last phase) to bf16; a gate/up
+    // slice loaded ahead waits for the next iteration
+    if (ng.type != PH_END && !widen_slice<WT>(a, cm, ng, nslot, lgen)) break;
     if (a.trace) cm.ltime = wall_clock64();
     if (a.two_slots) slot ^= 1;
     for (Ph q = next_phase(a, cur, a.pos0); ; q = next_phase(a, q, a.pos0)) {  // the phase index of ng
@@ -829,6 +927,7 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     }
     cur = ng;
   }
+  wait_vm();  // no load left in flight at exit (after an abort)
 }
 
 // SMP: the heads' codes are sampled (sampler.h), else greedy; a compile-time
@@ -1028,7 +1127,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     constexpr int NBH = nb_hidden(WT);
     OpC xo[2][NBH];  // [row][block]
     if (normed && !(cur.type == PH_GU || (cur.type == PH_QKV && a.two_slots))) {  // (else inside normed_items)
-      const uint8_t *gain = sp + gain_off(s, ESZ, WT == W_Q8);
+      const uint8_t *gain = sp + gain_off(s, ESZ, w_blocked(WT));
       const int bpr = H * ESZ >> 10;
       const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
 #pragma unroll
@@ -1508,6 +1607,7 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
     cm.abort = 0;
     cm.cbar = 0;
     cm.gdone = 0;
+    cm.lbar = 0;
   }
   for (int l = tid; l < a.Lt + a.Lp; l += NT) {
     const LayerDev *src = l < a.Lt ? a.tl + l : a.pl + (l - a.Lt);
@@ -1531,7 +1631,8 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
 }
 
 // (weights, head dim, GQA group, bf16 ring) combinations instantiated
-#define QT_FRAME_VARIANTS(X) X(W_F32, 64, 2, false) X(W_BF16, 128, 2, true) X(W_Q8, 128, 2, true)
+#define QT_FRAME_VARIANTS(X) \
+  X(W_F32, 64, 2, false) X(W_BF16, 128, 2, true) X(W_Q8, 128, 2, true) X(W_Q4, 128, 2, true)
 
 }  // namespace
 
@@ -1567,7 +1668,8 @@ bool frame_variant_supported(int wt, int hd, int g, int kvb) {
 }
 
 bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
-  const int esz = a.wt == W_F32 ? 4 : (a.wt == W_BF16 ? 2 : 1);
+  const int esz = a.wt == W_F32 ? 4 : a.wt == W_Q8 ? 1 : 2;  // bytes per weight in LDS (q4 rows widened to bf16)
+  const bool blocked = a.wt == W_Q8 || a.wt == W_Q4;
   const int qd = a.nq * a.hd;
   a.tile = TILE;
   a.max_tiles = a.P / TILE;
@@ -1593,13 +1695,18 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   int slot = 0;
   for (int i = 0; i < 5; ++i) {
     const int N = NK[i][0], K = NK[i][1], nm = NK[i][2];
-    if ((K * esz) % 1024 || N % 2 || (a.wt == W_Q8 && K % 256)) { *why = "GEMV width not a multiple of 1 KB"; return false; }
+    if ((K * esz) % 1024 || N % 2 || (blocked && K % 256)) { *why = "GEMV width not a multiple of 1 KB"; return false; }
     if (K > 3072) { *why = "GEMV width above 3072"; return false; }
     const int g = nm;  // gate/up (nm = 2) rows go in pairs
     const int R = g * ((N / g + NG - 1) / NG);
     if (R * nm > MAXR) { *why = "too many rows per workgroup"; return false; }
     int b = R * nm * K * esz;
-    if (a.wt == W_Q8) b += (int)up1k((uint32_t)(R * nm * (K / 16)));
+    if (blocked) b += (int)up1k((uint32_t)(R * nm * (K / 16)));
+    if (w_widened(a.wt)) {
+      const int bpr = (raw_rowb(a.wt, K) + 1023) / 1024;  // raw blocks per row, widened from registers
+      if ((R * nm * bpr + NLW - 1) / NLW > MAXWB) { *why = "too many q4 blocks per loader wave"; return false; }
+      if (bpr * 1024 > 2 * K) { *why = "q4 rows narrower than 512"; return false; }  // (raw_off)
+    }
     if (i == 0 || i == 2 || i == 4) b += (int)up1k((uint32_t)(a.H * (a.tab_bf16 ? 2 : 4)));
     slot = imax(slot, (int)up1k((uint32_t)b));
   }

@@ -64,8 +64,8 @@ extern "C" {
 /* 4-bit blocks of this library's own definition (the qwentts.cpp commit log's
    TTFA table lists a 4-bit column but defines no block): uint8 [N][K/2], weight
    k in byte k/2, low nibble for even k, code c in 0..15 standing for c - 8; fp16
-   scale d per 32 along K: [N][K/32]; w = d * (c - 8).  Decoded on the per-op
-   path at any batch size (the persistent frame kernel does not take it). */
+   scale d per 32 along K: [N][K/32]; w = d * (c - 8).  Decoded by both paths,
+   like QT_LIN_Q8. */
 #define QT_LIN_Q4 3
 
 /* context flags */

@@ -456,11 +456,16 @@ def test_reduced_bf16_sampled_parity():
 
 
 def test_reduced_q8_random_scales_parity():
+    # one stream on the persistent kernel (its loader waves widen the int8
+    # rows to bf16 in LDS), two on the per-op GEMV
     m = _reduced(synth.BIG_Q8)
     w = synth.make_weights(m, random_q8_scales=True)
     wl = dataclasses.replace(synth.WORKLOADS["q8_b1"], model=m, prompt=40)
-    say("[reduced q8 random scales] 4 frames, batch 2")
-    _check(_forced_run(m, w, wl, 4, batch=2), m, "reduced_q8")
+    for batch in (1, 2):
+        say(f"[reduced q8 random scales] 4 frames, batch {batch}")
+        r = _forced_run(m, w, wl, 4, batch=batch)
+        assert r["d"].path == (qt.QT_PATH_FRAME if batch == 1 else qt.QT_PATH_GRAPH)
+        _check(r, m, f"reduced_q8_b{batch}")
 
 
 def test_reduced_bf16_batched_parity():
@@ -481,16 +486,18 @@ def test_reduced_q8_batched_parity():
     _check(_forced_run(m, w, wl, 3, batch=8), m, "reduced_q8_b8")
 
 
-def test_reduced_q4_parity():
-    # 4-bit blocks run on the per-op path: one and two streams on the GEMV,
+@pytest.mark.parametrize("flags", [0, qt.QT_F_OPS], ids=["frame", "ops"])
+def test_reduced_q4_parity(flags):
+    # 4-bit blocks: one stream on the persistent kernel (4-bit rows widened
+    # in LDS) or, with the per-op flag, on the GEMV; two streams on the GEMV;
     # a 358-row prompt's prefill chunks (128, 128, 102 rows) on the MFMA GEMM
     m = _reduced(synth.BIG_Q4)
     w = synth.make_weights(m, random_q8_scales=True)
     wl = dataclasses.replace(synth.WORKLOADS["q4_b1"], model=m, prompt=358)
     for batch in (1, 2):
-        say(f"[reduced q4 random scales] prompt 358, 4 frames, batch {batch}")
-        r = _forced_run(m, w, wl, 4, batch=batch)
-        assert r["d"].path == qt.QT_PATH_GRAPH
+        say(f"[reduced q4 random scales] flags {flags}, prompt 358, 4 frames, batch {batch}")
+        r = _forced_run(m, w, wl, 4, batch=batch, flags=flags)
+        assert r["d"].path == (qt.QT_PATH_FRAME if batch == 1 and not flags else qt.QT_PATH_GRAPH)
         _check(r, m, f"reduced_q4_b{batch}")
 
 
@@ -527,7 +534,9 @@ def test_full_q4_b1_parity():
     say("[q4_b1] weights")
     w = synth.make_weights(m)
     say("[q4_b1] prefill 128 + 4 frames")
-    _check(_forced_run(m, w, wl, 4), m, "q4_b1")
+    r = _forced_run(m, w, wl, 4)
+    assert r["d"].path == qt.QT_PATH_FRAME
+    _check(r, m, "q4_b1")
 
 
 @pytest.mark.timeout(900)
@@ -558,7 +567,9 @@ def test_full_q8_b1_parity():
     say("[q8_b1] weights")
     w = synth.make_weights(m)
     say("[q8_b1] prefill 128 + 4 frames")
-    _check(_forced_run(m, w, wl, 4), m, "q8_b1")
+    r = _forced_run(m, w, wl, 4)
+    assert r["d"].path == qt.QT_PATH_FRAME
+    _check(r, m, "q8_b1")
 
 
 @pytest.mark.timeout(900)
