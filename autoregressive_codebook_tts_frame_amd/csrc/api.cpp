@@ -39,7 +39,7 @@ struct Layout {
   size_t gcnt_bytes;
   size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
   // persistent frame kernel: weight tables, tagged exchange words, error flag
-  size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_part, f_err, f_trace;
+  size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_lgx, f_part, f_err, f_trace;
   size_t xch_words;  // words between copies of the exchange rows
   size_t f_xch_begin;
   size_t total;
@@ -116,6 +116,7 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.f_z = L.f_o + 8 * 2 * (size_t)d.qd;
   L.f_qkv = take(8 * 2 * (size_t)d.nqkv);
   L.f_amax = take(8 * 2 * (size_t)kMaxWG);
+  L.f_lgx = take(8 * (size_t)d.Vc);
   L.f_part = take(8 * (size_t)d.nq * (d.P / kTile) * (d.hd + 2));
   L.f_err = take(64);
   L.f_trace = take(8 * 8 * 1024);
@@ -505,11 +506,8 @@ int32_t qt_set_sampler(qt_ctx *c, float temperature, int32_t top_k, uint64_t see
   if (!(temperature >= 0.f) || isinf(temperature))
     return fail(c, QT_E_ARG, "temperature must be finite and >= 0");
   if (top_k < 0) return fail(c, QT_E_ARG, "top_k must be >= 0");
-  if (top_k > 0 && top_k < c->d.Vc) {
-    if (c->path == QT_PATH_FRAME)
-      return fail(c, QT_E_UNSUPPORTED, "top-k needs the per-op path (a context with QT_F_OPS or several streams)");
-    if (c->d.Vc > 2048) return fail(c, QT_E_UNSUPPORTED, "top-k supports codebooks of at most 2048 entries");
-  }
+  if (top_k > 0 && top_k < c->d.Vc && c->d.Vc > 2048)
+    return fail(c, QT_E_UNSUPPORTED, "top-k supports codebooks of at most 2048 entries");
   c->inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
   c->top_k = top_k;
   c->seed = seed;
@@ -696,6 +694,7 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
       fa.xq = c->A<uint64_t>(c->L.f_xq); fa.qkvb = c->A<uint64_t>(c->L.f_qkv);
       fa.ob = c->A<uint64_t>(c->L.f_o); fa.zb = c->A<uint64_t>(c->L.f_z);
       fa.amax = c->A<uint64_t>(c->L.f_amax); fa.part = c->A<uint64_t>(c->L.f_part);
+      fa.lgx = c->A<uint64_t>(c->L.f_lgx);
       fa.logits_t = c->A<float>(c->L.logits_t); fa.logits_p = c->A<float>(c->L.logits_p);
       fa.x0_dump = c->A<float>(c->L.x0_dump); fa.hidden_dump = c->A<float>(c->L.hidden_dump);
       fa.gather_dump = c->A<int32_t>(c->L.gather_dump); fa.tpos_dump = c->A<int32_t>(c->L.tpos_dump);
@@ -865,6 +864,7 @@ int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t 
       fa.xq = (uint64_t *)(base + c->L.f_xq); fa.qkvb = (uint64_t *)(base + c->L.f_qkv);
       fa.ob = (uint64_t *)(base + c->L.f_o); fa.zb = (uint64_t *)(base + c->L.f_z);
       fa.amax = (uint64_t *)(base + c->L.f_amax); fa.part = (uint64_t *)(base + c->L.f_part);
+      fa.lgx = (uint64_t *)(base + c->L.f_lgx);
       fa.err = (int32_t *)(base + c->L.f_err);
       HIPCHK(c, hipMemsetAsync(c->scratch, 0, c->L.f_err + 64 - c->L.f_xch_begin, s));
     } else if (c->path == QT_PATH_FRAME) {
@@ -891,6 +891,7 @@ int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t 
       fa.tag_base = c->tag_base;
       fa.inv_temp = c->inv_temp;
       fa.seed = c->seed;
+      fa.top_k = c->inv_temp != 0.f && c->top_k > 0 && c->top_k < d.Vc ? c->top_k : 0;
       c->tag_base += (uint32_t)span;
       HIPCHK(c, launch_frame_kernel(fa, s));
     } else {

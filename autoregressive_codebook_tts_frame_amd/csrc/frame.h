@@ -73,6 +73,8 @@ struct FrameArgs {
   uint64_t *trace;    // optional: [1024][8] stamps (rows < 768: first GEMV workgroup; rest: attention workgroup 0)
   float inv_temp;     // sampling (sampler.h): float(1/T), 0 = greedy
   uint64_t seed;
+  int32_t top_k;      // sampling: only the top_k largest logits compete (0: all; Vc <= 2048)
+  uint64_t *lgx;      // [Vc] tagged head logits, for top_k > 0
 };
 
 // Cooperative launch: every workgroup is resident at once, or the launch fails.

@@ -46,6 +46,7 @@ constexpr int NW = 5;            // compute waves of a GEMV workgroup
 constexpr int NT = 64 * NW;      // their threads
 constexpr int NLW = 3;           // loader waves (each keeps its own loads in flight)
 constexpr int MAXWB = 16;        // q4: 1 KB raw blocks per loader wave and slice
+constexpr int TKU = 7;           // top-k: logits per compute thread (Vc <= 2048 = 7 * 320 - 192)
 constexpr int NTB = NT + 64 * NLW;  // two waves per SIMD
 constexpr int ANT = 512;         // threads of an attention workgroup
 constexpr int ANW = ANT / 64;    // its waves
@@ -214,6 +215,8 @@ struct Common {
   uint32_t cbar;   // compute-wave barrier arrivals
   uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
   uint32_t lbar;   // loader-wave barrier arrivals (q4 widening)
+  uint32_t hist[256];       // top-k: radix-select histogram
+  uint32_t tsel[2];         // top-k: the threshold key and the last member's index
   uint64_t ltime;  // tracing: when a loader wave's part of the last slice had landed
   Share sh[PH_END];  // this GEMV workgroup's rows, per phase type
 };
@@ -231,7 +234,7 @@ __host__ __device__ inline Lds lds_layout(const FrameArgs &a) {
   const uint32_t base = up16(sizeof(Common));
   // GEMV role
   const int kop = imax(a.H, imax(a.nq * a.hd, a.F));
-  const int opw = imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg);
+  const int opw = imax(imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg), (a.Vc + 1) / 2);
   L.xres = base;
   L.opnd = up16(L.xres + 2u * a.H * 4u);
   L.res = up16(L.opnd + 2u * opw * 4u);
@@ -723,8 +726,112 @@ __device__ __forceinline__ void tab_pairs(const FrameArgs &a, const void *tab, s
 
 // argmax over the workgroups' partial maxima of the head with tag; lowest
 // index wins ties.  Compute waves; false on timeout.
+// Logit -> unsigned key in the same order (-0 and +0 equal, as they compare).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x == 0.f ? 0.f : x);
+  return b ^ ((b >> 31) ? 0xffffffffu : 0x80000000u);
+}
+
+// The sampled code under top-k.  Every compute thread polls its share of the
+// head's Vc logits into LDS (logit i = u * NT + tid is value u of the
+// thread).  The k-th largest key is found by a radix select, 8 bits per pass
+// from the top: every thread adds its keys to an LDS histogram, wave 0 scans
+// it, picks the digit and clears it for the next pass.  After the last pass
+// wave 0 also finds, among the logits equal to the threshold, the index of
+// the last member: equal logits count in index order, lower indices first
+// (the argmax's tie rule).  Then every thread scores the members among its
+// logits (code j of frame position q) and the best score wins; every other
+// logit scores -inf.  Values are read back from LDS at each use: this runs
+// inside the phase loop, where registers are scarce.
+__device__ __forceinline__ bool resolve_top_k(const FrameArgs &a, Common &cm, uint32_t &gen, uint32_t *scratch,
+                                              uint32_t tag, int q, int j) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, Vc = a.Vc;
+  if (tid < 256) cm.hist[tid] = 0;
+  if (!poll_lin(a, a.lgx, Vc, tag, scratch)) cm.abort = 1;
+  if (!cbar(a, cm, gen) || cm.abort) return false;
+  auto key_at = [&](int i) { return order_key(__uint_as_float(scratch[min(i, Vc - 1)])); };
+  uint32_t prefix = 0, need = (uint32_t)a.top_k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass ? 0xffffffffu << (shift + 8) : 0u;
+    for (int u = 0; u < TKU; ++u) {
+      const uint32_t key = key_at(u * NT + tid);
+      if (u * NT + tid < Vc && (key & hmask) == prefix) atomicAdd(&cm.hist[(key >> shift) & 255], 1u);
+    }
+    if (!cbar(a, cm, gen)) return false;
+    if (wave == 0) {
+      // lane l holds bins 255 - 4l .. 252 - 4l (descending); inclusive scan over lanes
+      uint32_t c[4], c4 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { c[e] = cm.hist[255 - 4 * lane - e]; c4 += c[e]; }
+      uint32_t cum = c4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(cum, o, 64);
+        if (lane >= o) cum += t;
+      }
+      const uint64_t hit = __ballot(cum >= need);
+      const int hl = (int)__ffsll((unsigned long long)hit) - 1;  // the lane whose bins reach the k-th
+      uint32_t bin = 0, rest = 0, run = cum - c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (run + c[e] >= need) { bin = (uint32_t)(255 - 4 * lane - e); rest = need - run; break; }
+        run += c[e];
+      }
+      prefix |= (uint32_t)__builtin_amdgcn_readlane((int)bin, hl) << shift;
+      need = (uint32_t)__builtin_amdgcn_readlane((int)rest, hl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cm.hist[4 * lane + e] = 0;  // (every lane has read its bins)
+      if (pass == 3) {
+        // the need-th logit equal to the threshold, in index order: the last member
+        int last = -1;
+        uint32_t seen = 0;
+        for (int i0 = 0; i0 < Vc && last < 0; i0 += 64) {
+          const uint64_t eq = __ballot(i0 + lane < Vc && key_at(i0 + lane) == prefix);
+          const uint32_t n = (uint32_t)__popcll(eq);
+          if (seen + n >= need) {
+            uint64_t m = eq;
+            for (uint32_t r = seen + 1; r < need; ++r) m &= m - 1;  // drop the lower need - seen - 1
+            last = i0 + (int)__ffsll((unsigned long long)m) - 1;
+          }
+          seen += n;
+        }
+        need = (uint32_t)last;
+      }
+      if (lane == 0) { cm.tsel[0] = prefix; cm.tsel[1] = need; }
+    }
+    if (!cbar(a, cm, gen)) return false;
+    prefix = cm.tsel[0];
+    need = cm.tsel[1];
+  }
+  const int last = (int)need;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int u = 0; u < TKU; ++u) {
+    const int i = u * NT + tid;
+    const uint32_t key = key_at(i);
+    if (i < Vc && (key > prefix || (key == prefix && i <= last)))
+      pick(bv, bi, sample_score(__uint_as_float(scratch[i]), a.inv_temp, a.seed, 0, q, j, i), i);
+  }
+  wave_argmax(bv, bi);
+  if (lane == 0) { cm.amv[wave] = bv; cm.ami[wave] = bi; }
+  if (!cbar(a, cm, gen)) return false;
+  float b2 = cm.amv[0];
+  int i2 = cm.ami[0];
+  for (int w = 1; w < NW; ++w) pick(b2, i2, cm.amv[w], cm.ami[w]);
+  cm.code = i2 == 0x7fffffff ? 0 : i2;  // every thread writes the same value
+  return true;
+}
+
+// The code a head decided: the best of the GEMV workgroups' (value, index)
+// words, or under top-k sampling the pick among all the head's logits (q, j:
+// the code's frame position and index, its sampling key).
+template <bool SMP>
 __device__ __forceinline__ bool resolve_code(const FrameArgs &a, Common &cm, uint32_t &gen, uint32_t *scratch,
-                                             int NG, uint32_t tag) {
+                                             int NG, uint32_t tag, int q, int j) {
+  if constexpr (SMP) {
+    if (a.top_k > 0) return resolve_top_k(a, cm, gen, scratch, tag, q, j);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (!poll_lin(a, a.amax, 2 * NG, tag, scratch)) cm.abort = 1;
   if (!cbar(a, cm, gen) || cm.abort) return false;  // each thread reduces words other threads polled
@@ -944,7 +1051,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   float *xres = (float *)(smem + L.xres);   // [2][H] residual rows
   uint32_t *opnd = (uint32_t *)(smem + L.opnd);
   const int kop = imax(a.H, imax(a.nq * a.hd, a.F));
-  const int opw = imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg);  // words per operand row
+  const int opw = imax(imax(a.act_bf16 ? kop / 2 : kop, 2 * a.nwg), (a.Vc + 1) / 2);  // words per operand row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gi = (int)blockIdx.x - a.n_attn, NG = a.nwg - a.n_attn;
   const int H = a.H, G = a.G;
@@ -980,6 +1087,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   int slot = 0;
   bool pending = false;  // the previous GEMV phase was a head
   int pending_idx = 0;   // the code index it decides (0: next frame's code 0)
+  int pending_q = 0;     // and that code's frame position (its sampling key, with the index)
   int ntr = 0;
 
   while (cur.type != PH_END) {
@@ -1014,7 +1122,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     bool ok = true;
     if (cur.type == PH_QKV && cur.layer == 0) {
       if (pending) {
-        if (!resolve_code(a, cm, gen, opnd, NG, tagp)) { cm.abort = 1; ok = false; }
+        if (!resolve_code<SMP>(a, cm, gen, opnd, NG, tagp, pending_q, pending_idx)) { cm.abort = 1; ok = false; }
         else {
           const int c = cm.code;
           if (pending_idx == 0) c0 = c;
@@ -1167,6 +1275,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
         const int n = s.r0 + it;
         if (lane == 0) st(lg + n, acc[0][0]);
         if constexpr (SMP) {
+          if (a.top_k > 0 && lane == 0) tputf(a.lgx + n, acc[0][0], tag);  // every logit, for the top-k pick
           // item it is this wave's ((it - wave) / NW)-th: its noise sits in that lane
           const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gnoise), (it - wave) / NW));
           pick(bv, bi, __fadd_rn(__fmul_rn(acc[0][0], a.inv_temp), g), n);
@@ -1183,6 +1292,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
       }
       pending = true;
       pending_idx = cur.stack ? 0 : cur.step + 1;
+      pending_q = cur.stack ? pos + 1 : pos;
     } else {
       const int type = cur.type, N = s.N;
       const bool hid = type == PH_D && cur.stack == 1 && a.dump;
@@ -1237,7 +1347,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   // the code picked by the last talker head becomes the slot's pending code 0
   if (lead) {
     if (pending) {
-      if (!cbar(a, cm, gen) || !resolve_code(a, cm, gen, opnd, NG, a.tag_base + seq - 1)) return;
+      if (!cbar(a, cm, gen) || !resolve_code<SMP>(a, cm, gen, opnd, NG, a.tag_base + seq - 1, pending_q, pending_idx))
+        return;
       if (tid == 0) st(a.c0, cm.code);
     }
     if (tid == 0) st(a.pos, pos0 + a.n_frames);

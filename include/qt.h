@@ -307,9 +307,10 @@ int32_t qt_time_kernel(qt_ctx *ctx, int32_t kernel, int32_t reps, double *avg_us
    is from softmax(l / T) restricted to them); equal logits at the boundary
    rank by lower index, as in the argmax.  top_k = 0 (or >= codebook_size):
    every logit.  Host only: no GPU call, no graph recapture.
+   Every decode path implements it (on the persistent kernel every
+   workgroup polls the head's logits and makes the same pick).
    Errors: QT_E_ARG (NULL ctx, temperature negative, NaN or infinite, top_k
-   negative), QT_E_UNSUPPORTED (top-k on a context whose decode path is
-   QT_PATH_FRAME, or codebook_size > 2048). */
+   negative), QT_E_UNSUPPORTED (top-k with codebook_size > 2048). */
 int32_t qt_set_sampler(qt_ctx *ctx, float temperature, int32_t top_k, uint64_t seed);
 
 /* Measurement hook (the library's own): the achievable HBM read bandwidth

@@ -377,28 +377,21 @@ def test_tiny_sampled_parity(tiny, flags):
     assert np.mean(rs["oout"]["codes"] != r["oout"]["codes"]) > 0.5
 
 
-@pytest.mark.parametrize("top_k", [1, 5, 200])
-def test_tiny_top_k_parity(tiny, top_k):
-    # top-k on the per-op path (radix select in the argmax kernel): F32 codes
-    # equal the oracle's free-running; top_k = 1 is the greedy decode
+@pytest.mark.parametrize("flags", [0, qt.QT_F_OPS], ids=["frame", "ops"])
+@pytest.mark.parametrize("top_k", [1, 5, 200, 255])
+def test_tiny_top_k_parity(tiny, top_k, flags):
+    # top-k on the persistent kernel (every workgroup polls the head's logits
+    # and runs the radix select) and on the per-op path (radix select in the
+    # argmax kernel): F32 codes equal the oracle's free-running; top_k = 1 is
+    # the greedy decode, 255 drops one logit of 256
     m, w, wl, r = tiny
-    say(f"[tiny top-k] k = {top_k}, 8 frames, T = 1.0")
-    rs = _forced_run(m, w, wl, 8, sampler=(1.0, 31, top_k), flags=qt.QT_F_OPS)
+    say(f"[tiny top-k] flags {flags}, k = {top_k}, 8 frames, T = 1.0")
+    rs = _forced_run(m, w, wl, 8, sampler=(1.0, 31, top_k), flags=flags)
+    assert rs["d"].path == (qt.QT_PATH_GRAPH if flags else qt.QT_PATH_FRAME)
     _check(rs, m, f"tiny_top{top_k}")
     assert np.array_equal(rs["g"]["codes"], rs["oout"]["codes"])
     if top_k == 1:
         assert np.array_equal(rs["oout"]["codes"], r["oout"]["codes"])
-
-
-def test_top_k_rejected_on_the_persistent_kernel(tiny):
-    m, w, wl, r = tiny
-    d = qt.Decoder(m, r["d"].dw, 1)
-    assert d.path == qt.QT_PATH_FRAME
-    with pytest.raises(qt.QtError) as e:
-        d.set_sampler(1.0, 0, top_k=5)
-    assert e.value.code == qt.QT_E_UNSUPPORTED
-    d.set_sampler(1.0, 0, top_k=0)  # temperature alone runs there
-    d.close()
 
 
 def test_tiny_sampled_batched_keys_by_slot(tiny):
@@ -451,8 +444,9 @@ def test_reduced_bf16_sampled_parity():
     for batch in (1, 8):
         say(f"[reduced bf16 sampled] 4 frames, batch {batch}, T = 0.8")
         _check(_forced_run(m, w, wl, 4, batch=batch, sampler=(0.8, 2024)), m, f"reduced_bf16_sampled_b{batch}")
-    say("[reduced bf16 top-k] 4 frames, batch 8, T = 0.8, k = 50")
-    _check(_forced_run(m, w, wl, 4, batch=8, sampler=(0.8, 2024, 50)), m, "reduced_bf16_top50_b8")
+    for batch in (1, 8):
+        say(f"[reduced bf16 top-k] 4 frames, batch {batch}, T = 0.8, k = 50")
+        _check(_forced_run(m, w, wl, 4, batch=batch, sampler=(0.8, 2024, 50)), m, f"reduced_bf16_top50_b{batch}")
 
 
 def test_reduced_q8_random_scales_parity():
@@ -727,8 +721,11 @@ def _tied_heads(m, w, wl, prompt):
     return w2, codes, ov, tied
 
 
+@pytest.mark.parametrize("sampler", [None, (1.0, 5, 1)], ids=["greedy", "top1"])
 @pytest.mark.parametrize("flags", [0, qt.QT_F_OPS], ids=["frame", "ops"])
-def test_exact_ties_pick_the_lowest_index(flags):
+def test_exact_ties_pick_the_lowest_index(flags, sampler):
+    # greedy, and top-k sampling with k = 1: of two equal largest logits only
+    # the lower index is a member, whatever the noise
     m = synth.TINY
     wl = synth.WORKLOADS["tiny_f32_b1"]
     w = synth.make_weights(m)
@@ -736,13 +733,16 @@ def test_exact_ties_pick_the_lowest_index(flags):
     w2, codes, ov, tied = _tied_heads(m, w, wl, prompt)
     assert len(tied) >= 8
     o = Oracle(m, w2, 1)
+    d = qt.Decoder(m, w2, 1, flags=flags)
+    if sampler:
+        o.set_sampler(*sampler)
+        d.set_sampler(sampler[0], sampler[1], top_k=sampler[2])
     o.prefill(0, *prompt)
     oc = o.decode(1, ov, forced=codes)["codes"]
-    d = qt.Decoder(m, w2, 1, flags=flags)
     assert d.path == (qt.QT_PATH_GRAPH if flags else qt.QT_PATH_FRAME)
     d.prefill(0, *prompt)
     gc = d.decode(1, ov, forced=codes)
-    say(f"[ties {flags}] tied decisions {tied}; codes", gc[0, 0].tolist())
+    say(f"[ties {flags} {sampler}] tied decisions {tied}; codes", gc[0, 0].tolist())
     assert all(oc[0, 0, j] == 0 for j in tied)  # the oracle's rule: lowest index
     assert np.array_equal(gc, oc)                # F32: every decision equal
     d.close()
