@@ -228,7 +228,8 @@ int32_t qt_decode_frame(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_id
    Errors: those of qt_decode_frame; QT_E_UNSUPPORTED if the context does not
    decode on the persistent kernel (qt_path() != QT_PATH_FRAME); QT_E_SIZE if
    the model's exchange region exceeds 512 KiB (the 28-layer, 1,024-wide
-   model needs 436 KiB). */
+   model with a 4,096-position ring needs 452 KiB; 8 KV heads with rings of
+   5,632 positions or more exceed it). */
 int32_t qt_decode_frame_noalloc(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_ids,
                                 int32_t *codes_out, const int32_t *forced_codes);
 

@@ -1,10 +1,9 @@
 """qt_decode_frame_noalloc (the entry point for callers that cannot allocate)
 against qt_decode_frame, through the C ABI on the GPU: the same codes,
 logits, bridge and state, bit for bit, on two calls in a row, the second
-with fewer frames; and its refusal without the persistent kernel.  (Its
-other refusal, an exchange region above the 512 KiB static maximum, has no
-model to exercise it: the largest region of any shape the persistent kernel
-plans is 493 KiB.)"""
+with fewer frames; and its refusals: without the persistent kernel, and
+for an exchange region above the 512 KiB static maximum (8 KV heads and a
+5,632-position ring: 525 KiB)."""
 import dataclasses
 
 import numpy as np
@@ -38,7 +37,7 @@ def test_noalloc_equals_decode_frame(which):
     if which == "tiny_f32":
         m = synth.TINY
         wl = synth.WORKLOADS["tiny_f32_b1"]
-    else:  # full widths and the 4,096-position ring: the 436 KiB exchange region
+    else:  # full widths and the 4,096-position ring: the 452 KiB exchange region
         m = dataclasses.replace(synth.BIG, Lt=2, Lp=1, Vt=4096, model_id=synth.BIG.model_id + 50)
         wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=40)
     w = synth.make_weights(m)
@@ -78,4 +77,21 @@ def test_noalloc_refusals():
     with pytest.raises(qt.QtError) as e:
         d.decode(1, synth.make_overlays(wl, 1), noalloc=True)
     assert e.value.code == qt.QT_E_UNSUPPORTED
+    d.close()
+    # one stream on the persistent kernel, but 22 attention tiles of 8 KV heads
+    # make its exchange region 525 KiB: refused before any launch, and the
+    # ordinary entry point still decodes from the unchanged state
+    m = dataclasses.replace(synth.BIG, Lt=2, Lp=1, Vt=4096, F=2048, P=5632, model_id=synth.BIG.model_id + 60)
+    wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=40)
+    d = qt.Decoder(m, synth.make_weights(m), 1)
+    assert d.path == qt.QT_PATH_FRAME
+    d.prefill(0, *synth.make_prompt(wl, 0))
+    st = d.get_state(0)
+    ov = synth.make_overlays(wl, 1)
+    print("[noalloc] 5,632-position ring: refusal", flush=True)
+    with pytest.raises(qt.QtError) as e:
+        d.decode(1, ov, noalloc=True)
+    assert e.value.code == qt.QT_E_SIZE
+    assert d.get_state(0)[:2] == st[:2]
+    assert d.decode(1, ov).shape == (1, 1, m.G)
     d.close()
