@@ -893,13 +893,21 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
     for (int q = 0; q < UPI; ++q) acc[q][0] = acc[q][1] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < MAXB; ++cb) {
-      if (cb >= bpr) break;
-      const int c = cb * 64 + lane;
+      // Every block's products are computed (past the row's end from the
+      // clamped block, then dropped by a select): with a branch here the
+      // compiler sinks each block's loads behind it, one LDS round trip per
+      // block instead of one per item.
+      const bool on = cb < bpr;
+      const int c = min(cb, bpr - 1) * 64 + lane;
 #pragma unroll
       for (int q = 0; q < UPI; ++q) {
         const uint8_t *scl = scb + (size_t)(it * UPI + q) * (s.K / 16);
-        acc[q][0] += chunk_dot<WT>(w[q][cb], x[0][cb], c, scl);
-        if (M > 1) acc[q][1] += chunk_dot<WT>(w[q][cb], x[1][cb], c, scl);
+        const float d0 = chunk_dot<WT>(w[q][cb], x[0][cb], c, scl);
+        acc[q][0] += on ? d0 : 0.f;
+        if (M > 1) {
+          const float d1 = chunk_dot<WT>(w[q][cb], x[1][cb], c, scl);
+          acc[q][1] += on ? d1 : 0.f;
+        }
       }
     }
 #pragma unroll
