@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
+#include <stddef.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -35,6 +36,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t rope_cos, rope_sin, pos, c0, bridge, ctl, overlay, cin, cout;
   size_t x, qkv, q, part, o, z, logits_t, logits_p;
+  size_t ptab;  // paged ring: pool row of (slot, position), int32 [B][P]
   size_t ssq, gpart, gcnt;  // batched projections: row sums of squares, split-K partials, tile counters
   size_t gcnt_bytes;
   size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
@@ -103,6 +105,7 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.tpos_dump = take(sizeof(int32_t) * B);
   L.pf_codes = take(sizeof(int32_t) * (size_t)d.P * d.G);
   L.pf_text = take(sizeof(int32_t) * (size_t)d.P);
+  L.ptab = take(sizeof(int32_t) * (size_t)B * d.P);
   L.f_tl = take(sizeof(qtk::LayerDev) * d.Lt);
   L.f_pl = take(sizeof(qtk::LayerDev) * d.Lp);
   L.f_heads = take(sizeof(void *) * d.G);
@@ -129,6 +132,8 @@ size_t kv_elem(const qt_model_desc &m) { return m.kv_bf16 ? 2 : 4; }
 size_t talker_ring_elems(const Dims &d, int32_t B) {
   return (size_t)B * d.Lt * 2 * d.kd * d.P;
 }
+// the paged talker ring: one pool of `rows` positions per (layer, K|V, head)
+size_t talker_pool_elems(const Dims &d, int32_t rows) { return (size_t)d.Lt * 2 * d.kd * rows; }
 size_t pred_ring_elems(const Dims &d, int32_t B) { return (size_t)B * d.Lp * 2 * d.kd * d.Q; }
 
 // Shapes the kernels implement; message on failure.
@@ -168,6 +173,12 @@ struct qt_ctx {
   std::vector<qt_layer_weights> tl, pl;
   // device memory
   uint8_t *ring, *arena;
+  // paged talker ring (QT_F_PAGED): pool rows, the host's free list and each
+  // slot's rows by position (mirrored on the device in the page table)
+  int32_t pool_rows = 0;
+  std::vector<int32_t> free_rows;
+  std::vector<std::vector<int32_t>> slot_rows;
+  size_t pu_ptab = 0;
   // host mirrors and staging
   std::vector<int32_t> pos_host;
   std::vector<uint8_t> ready;
@@ -192,6 +203,43 @@ struct qt_ctx {
 };
 
 namespace {
+
+// ----------------------------------------------------------------- paged ring
+//
+// With QT_F_PAGED the talker's K/V rows live in one pool shared by every slot,
+// page size 1: each (slot, position) gets a pool row of its own from a host
+// free list, and the device page table [B][P] (carried as data, like the
+// set_rows destinations of [QT-log]) maps positions to rows, so a captured
+// graph never changes.  Rows come from the free list as a slot's positions
+// are first written and go back when the slot is prefilled again.
+
+// Rows still to take for slot b to hold positions [0, upto).
+size_t rows_short(const qt_ctx *c, int b, int upto) {
+  const size_t have = c->slot_rows[b].size();
+  return (size_t)upto > have ? (size_t)upto - have : 0;
+}
+
+// Give slot b rows for positions [0, upto) (the free list holds them: checked
+// by the caller) and upload their table entries through `stage` (pinned).
+hipError_t grow_slot(qt_ctx *c, int b, int upto, int32_t *stage) {
+  std::vector<int32_t> &rows = c->slot_rows[b];
+  const int first = (int)rows.size();
+  if (upto <= first) return hipSuccess;
+  for (int p = first; p < upto; ++p) {
+    rows.push_back(c->free_rows.back());
+    c->free_rows.pop_back();
+    stage[p - first] = rows.back();
+  }
+  return hipMemcpyAsync(c->A<int32_t>(c->L.ptab) + (size_t)b * c->d.P + first, stage, sizeof(int32_t) * (upto - first),
+                        hipMemcpyHostToDevice, c->stream);
+}
+
+// Return slot b's rows to the free list (host only).
+void release_slot(qt_ctx *c, int b) {
+  std::vector<int32_t> &rows = c->slot_rows[b];
+  for (size_t i = rows.size(); i-- > 0;) c->free_rows.push_back(rows[i]);  // taken again in the same order
+  rows.clear();
+}
 
 int32_t fail(qt_ctx *c, int32_t code, const char *fmt, ...) {
   char buf[512];
@@ -229,6 +277,8 @@ struct Stack {
   int64_t kv_stride;
   int32_t P;              // positions per head
   int32_t tile, max_tiles;
+  const int32_t *ptab = nullptr;  // paged ring's page table (talker only)
+  int32_t rows_per_head = 0;
 };
 
 Stack talker_stack(const qt_ctx *c) {
@@ -236,10 +286,19 @@ Stack talker_stack(const qt_ctx *c) {
   Stack s;
   s.layers = &c->tl;
   s.ring = c->ring;
-  s.kv_stride = (int64_t)d.kd * d.P;
-  s.layer_stride = 2 * s.kv_stride;
-  s.slot_stride = s.layer_stride * d.Lt;
   s.P = d.P;
+  if (c->pool_rows) {  // paged: [Lt][2][nkv][pool rows][hd], rows from the page table
+    s.kv_stride = (int64_t)d.kd * c->pool_rows;
+    s.layer_stride = 2 * s.kv_stride;
+    s.slot_stride = 0;
+    s.ptab = c->A<int32_t>(c->L.ptab);
+    s.rows_per_head = c->pool_rows;
+  } else {
+    s.kv_stride = (int64_t)d.kd * d.P;
+    s.layer_stride = 2 * s.kv_stride;
+    s.slot_stride = s.layer_stride * d.Lt;
+    s.rows_per_head = d.P;
+  }
   s.tile = kTile;
   s.max_tiles = c->L.max_tiles;
   return s;
@@ -249,7 +308,8 @@ Stack pred_stack(const qt_ctx *c) {
   const Dims &d = c->d;
   Stack s;
   s.layers = &c->pl;
-  s.ring = c->ring + talker_ring_elems(d, c->B) * kv_elem(c->md);
+  s.ring = c->ring + (c->pool_rows ? talker_pool_elems(d, c->pool_rows) : talker_ring_elems(d, c->B)) * kv_elem(c->md);
+  s.rows_per_head = d.Q;
   s.kv_stride = (int64_t)d.kd * d.Q;
   s.layer_stride = 2 * s.kv_stride;
   s.slot_stride = s.layer_stride * d.Lp;
@@ -339,7 +399,7 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
     qa.q_gain = w.q_norm; qa.k_gain = w.k_norm; qa.gain_bf16 = md.tab_bf16; qa.eps = (float)md.eps;
     qa.rope_cos = c->A<float>(c->L.rope_cos); qa.rope_sin = c->A<float>(c->L.rope_sin);
     qa.q_out = q; qa.ring_layer = ring_layer; qa.slot_stride = st.slot_stride;
-    qa.kv_stride = st.kv_stride; qa.P = st.P;
+    qa.kv_stride = st.kv_stride; qa.P = st.P; qa.ptab = st.ptab; qa.rows_per_head = st.rows_per_head;
     if ((e = launch_qk_rope_kv(d.hd, md.kv_bf16, qa, s)) != hipSuccess) return e;
   }
 
@@ -353,6 +413,7 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   aa.q = q; aa.M = M; aa.rows = rows; aa.nq = d.nq; aa.nkv = d.nkv;
   aa.ring_layer = ring_layer; aa.slot_stride = st.slot_stride; aa.kv_stride = st.kv_stride;
   aa.P = st.P; aa.tile = st.tile; aa.max_tiles = st.max_tiles;
+  aa.ptab = st.ptab; aa.rows_per_head = st.rows_per_head;
   // rows with host-known positions (prefill chunks, the predictor) launch only
   // the tiles up to their last position, and skip the merge when that is one
   aa.grid_tiles = rows.pos_dev ? st.max_tiles
@@ -524,11 +585,20 @@ int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t fr
     return fail(nullptr, QT_E_ARG, "max_batch, frames_per_replay and max_frames_per_call must be positive");
   if (max_frames_per_call % frames_per_replay)
     return fail(nullptr, QT_E_ARG, "max_frames_per_call must be a multiple of frames_per_replay");
-  if (flags & ~(QT_F_DUMP | QT_F_EAGER | QT_F_OPS | QT_F_TRACE)) return fail(nullptr, QT_E_ARG, "unknown flags");
+  if (flags & ~(QT_F_DUMP | QT_F_EAGER | QT_F_OPS | QT_F_TRACE | QT_F_PAGED)) return fail(nullptr, QT_E_ARG, "unknown flags");
   if (const char *why = unsupported(*model)) return fail(nullptr, QT_E_UNSUPPORTED, "%s", why);
   const Dims d = dims_of(*model);
   *ring_bytes = (talker_ring_elems(d, max_batch) + pred_ring_elems(d, max_batch)) * kv_elem(*model);
   *arena_bytes = layout_of(d, max_batch, max_frames_per_call).total;
+  return QT_OK;
+}
+
+int32_t qt_query_paged_ring(const qt_model_desc *model, int32_t max_batch, int32_t pool_rows, size_t *ring_bytes) {
+  if (!model || !ring_bytes) return fail(nullptr, QT_E_ARG, "NULL argument");
+  if (max_batch <= 0 || pool_rows <= 0) return fail(nullptr, QT_E_ARG, "max_batch and pool_rows must be positive");
+  if (const char *why = unsupported(*model)) return fail(nullptr, QT_E_UNSUPPORTED, "%s", why);
+  const Dims d = dims_of(*model);
+  *ring_bytes = (talker_pool_elems(d, pool_rows) + pred_ring_elems(d, max_batch)) * kv_elem(*model);
   return QT_OK;
 }
 
@@ -541,17 +611,26 @@ void qt_free(qt_ctx *c) {
   delete c;
 }
 
-int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
-  if (!p || !out) return fail(nullptr, QT_E_ARG, "NULL argument");
-  if (p->abi_version < QT_ABI_MIN_VERSION || p->abi_version > QT_ABI_VERSION)
-    return fail(nullptr, QT_E_ABI, "abi_version %u outside [%d, %d]", p->abi_version,
+int32_t qt_init(const qt_init_params *params, qt_ctx **out) {
+  if (!params || !out) return fail(nullptr, QT_E_ARG, "NULL argument");
+  if (params->abi_version < QT_ABI_MIN_VERSION || params->abi_version > QT_ABI_VERSION)
+    return fail(nullptr, QT_E_ABI, "abi_version %u outside [%d, %d]", params->abi_version,
                 QT_ABI_MIN_VERSION, QT_ABI_VERSION);
-  if (p->struct_size != sizeof(qt_init_params))
-    return fail(nullptr, QT_E_ARG, "struct_size %u != %zu", p->struct_size, sizeof(qt_init_params));
+  // callers of ABI 1-3 pass the structure without pool_rows (a dense ring)
+  const size_t old_size = offsetof(qt_init_params, pool_rows);
+  if (params->struct_size != sizeof(qt_init_params) && params->struct_size != old_size)
+    return fail(nullptr, QT_E_ARG, "struct_size %u is neither %zu nor %zu", params->struct_size,
+                sizeof(qt_init_params), old_size);
+  qt_init_params pv = {};
+  memcpy(&pv, params, params->struct_size);
+  const qt_init_params *p = &pv;
+  const bool paged = (p->flags & QT_F_PAGED) != 0;
+  if (paged && p->pool_rows <= 0) return fail(nullptr, QT_E_ARG, "QT_F_PAGED needs pool_rows > 0");
   size_t ring_need, arena_need;
   int32_t rc = qt_query_sizes(&p->model, p->max_batch, p->frames_per_replay,
                               p->max_frames_per_call, p->flags, &ring_need, &arena_need);
   if (rc != QT_OK) return rc;
+  if (paged && (rc = qt_query_paged_ring(&p->model, p->max_batch, p->pool_rows, &ring_need)) != QT_OK) return rc;
   const qt_model_desc &m = p->model;
   const Dims d = dims_of(m);
   const qt_weights &w = p->weights;
@@ -602,6 +681,12 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
   c->arena = (uint8_t *)p->arena;
   c->pos_host.assign(c->B, 0);
   c->ready.assign(c->B, 0);
+  if (paged) {
+    c->pool_rows = p->pool_rows;
+    c->free_rows.resize(p->pool_rows);
+    for (int32_t i = 0; i < p->pool_rows; ++i) c->free_rows[i] = p->pool_rows - 1 - i;  // row 0 is taken first
+    c->slot_rows.assign(c->B, {});
+  }
 
   auto bail = [&](int32_t code) {
     g_err = c->err;
@@ -615,7 +700,8 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
   c->pu_pf_text = c->pu_forced + (size_t)c->maxF * c->B * d.G;
   c->pu_pf_codes = c->pu_pf_text + (size_t)d.P;
   c->pu_scalar = c->pu_pf_codes + (size_t)d.P * d.G;
-  c->pin_up_elems = c->pu_scalar + 16;
+  c->pu_ptab = c->pu_scalar + 16;  // paged: new table entries (a prefill's P, or maxF per slot per chunk)
+  c->pin_up_elems = c->pu_ptab + std::max((size_t)d.P, (size_t)c->maxF * c->B);
   c->pin_down_elems = (size_t)c->maxF * c->B * d.G;
   if (hipHostMalloc((void **)&c->pin_up, c->pin_up_elems * 4, hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void **)&c->pin_down, c->pin_down_elems * 4, hipHostMallocDefault) != hipSuccess)
@@ -643,7 +729,7 @@ int32_t qt_init(const qt_init_params *p, qt_ctx **out) {
     return bail(fail(c, QT_E_HIP, "counter clear failed"));
   // decode path: persistent frame kernel where it applies
   c->path = (c->flags & QT_F_EAGER) ? QT_PATH_EAGER : QT_PATH_GRAPH;
-  if (!(c->flags & (QT_F_EAGER | QT_F_OPS)) && !frame_unsupported(m, c->B)) {
+  if (!(c->flags & (QT_F_EAGER | QT_F_OPS | QT_F_PAGED)) && !frame_unsupported(m, c->B)) {
     int dev = 0, ncu = 0;
     const char *why = nullptr;
     int lds = 0;
@@ -731,6 +817,8 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
   if (T > d.P) return fail(c, QT_E_CONTEXT_FULL, "prompt of %d rows exceeds %d ring positions", T, d.P);
   if (!ids_ok(text_ids, T, d.Vt)) return fail(c, QT_E_RANGE, "text id outside [0, %d)", d.Vt);
   if (codes && !ids_ok(codes, (size_t)T * d.G, d.Vc)) return fail(c, QT_E_RANGE, "code id outside [0, %d)", d.Vc);
+  if (c->pool_rows && c->free_rows.size() + c->slot_rows[slot].size() < (size_t)T)
+    return fail(c, QT_E_CONTEXT_FULL, "paged ring: %zu free rows, the prompt needs %d", c->free_rows.size() + c->slot_rows[slot].size(), T);
 
   hipStream_t s = c->stream;
   // from the first launch on the slot's ring rows change: it counts as
@@ -742,6 +830,10 @@ int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, con
   if (codes) memcpy(up_codes, codes, sizeof(int32_t) * T * d.G);
   HIPCHK(c, hipMemcpyAsync(pf_text, up_text, sizeof(int32_t) * T, hipMemcpyHostToDevice, s));
   if (codes) HIPCHK(c, hipMemcpyAsync(pf_codes, up_codes, sizeof(int32_t) * T * d.G, hipMemcpyHostToDevice, s));
+  if (c->pool_rows) {  // the slot's rows back to the pool, then T rows for the prompt
+    release_slot(c, slot);
+    HIPCHK(c, grow_slot(c, slot, T, c->pin_up + c->pu_ptab));
+  }
 
   const int wt = wtype_of(md);
   float *x = c->A<float>(c->L.x);
@@ -811,11 +903,15 @@ int32_t decode_entry(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *
   const int B = c->B;
   if (n <= 0 || !overlay_ids || !codes_out) return fail(c, QT_E_ARG, "n_frames must be positive, pointers non-NULL");
   if (n % c->K) return fail(c, QT_E_ARG, "n_frames %d is not a multiple of frames_per_replay %d", n, c->K);
+  size_t short_rows = 0;  // paged: pool rows the new positions still need
   for (int b = 0; b < B; ++b) {
     if (!c->ready[b]) return fail(c, QT_E_STATE, "slot %d not prefilled", b);
     if (c->pos_host[b] + n > d.P)
       return fail(c, QT_E_CONTEXT_FULL, "slot %d: position %d + %d frames exceeds %d", b, c->pos_host[b], n, d.P);
+    if (c->pool_rows) short_rows += rows_short(c, b, c->pos_host[b] + n);
   }
+  if (short_rows > c->free_rows.size())
+    return fail(c, QT_E_CONTEXT_FULL, "paged ring: %zu free rows, %d frames need %zu", c->free_rows.size(), n, short_rows);
   if (!ids_ok(overlay_ids, (size_t)n * B, d.Vt)) return fail(c, QT_E_RANGE, "overlay id outside [0, %d)", d.Vt);
   if (forced && !ids_ok(forced, (size_t)n * B * d.G, d.Vc)) return fail(c, QT_E_RANGE, "forced code outside [0, %d)", d.Vc);
 
@@ -848,6 +944,9 @@ int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t 
     memcpy(ov, overlay_ids + (size_t)f0 * B, sizeof(int32_t) * nf * B);
     HIPCHK(c, hipMemcpyAsync(ctl, up, 16 * sizeof(int32_t), hipMemcpyHostToDevice, s));
     HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.overlay), ov, sizeof(int32_t) * nf * B, hipMemcpyHostToDevice, s));
+    if (c->pool_rows)  // rows for the positions this chunk writes (counted by decode_entry)
+      for (int b = 0; b < B; ++b)
+        HIPCHK(c, grow_slot(c, b, c->pos_host[b] + nf, c->pin_up + c->pu_ptab + (size_t)b * c->maxF));
     if (forced) {
       int32_t *fu = c->pin_up + c->pu_forced;
       memcpy(fu, forced + (size_t)f0 * B * d.G, sizeof(int32_t) * nf * B * d.G);
@@ -935,6 +1034,8 @@ int32_t qt_set_slot_state(qt_ctx *c, int32_t slot, int32_t pos, int32_t c0, cons
   if (slot < 0 || slot >= c->B || !bridge) return fail(c, QT_E_ARG, "bad slot or NULL bridge");
   if (pos < 1 || pos > c->d.P) return fail(c, QT_E_RANGE, "pos %d outside [1, %d]", pos, c->d.P);
   if (c0 < 0 || c0 >= c->d.Vc) return fail(c, QT_E_RANGE, "c0 %d outside [0, %d)", c0, c->d.Vc);
+  if (c->pool_rows && c->slot_rows[slot].size() < (size_t)pos)
+    return fail(c, QT_E_STATE, "paged ring: slot %d holds %zu rows, pos %d needs them all", slot, c->slot_rows[slot].size(), pos);
   c->ready[slot] = 0;  // until every part of the state is written
   HIPCHK(c, hipStreamSynchronize(c->stream));
   HIPCHK(c, hipMemcpy(c->A<int32_t>(c->L.pos) + slot, &pos, 4, hipMemcpyHostToDevice));

@@ -61,6 +61,10 @@ struct QkArgs {
   void *ring_layer;                  // this layer's (slot 0, K) block
   int64_t slot_stride, kv_stride;    // elements
   int32_t P;                         // positions per (slot, layer, K|V, head)
+  // Paged ring (page size 1): ptab[slot * P + pos] is the pool row of a
+  // position, rows_per_head the pool's rows; null: the dense ring (row = pos)
+  const int32_t *ptab;
+  int32_t rows_per_head;
 };
 
 struct AttnArgs {
@@ -71,6 +75,8 @@ struct AttnArgs {
   const void *ring_layer;
   int64_t slot_stride, kv_stride;
   int32_t P;
+  const int32_t *ptab;    // paged ring: pool row of (slot, position) at [slot * P + pos], or null
+  int32_t rows_per_head;  // rows of one (layer, K|V, head): P (dense) or the pool's
   int32_t tile;       // positions per tile (fixed absolute boundaries)
   int32_t max_tiles;  // tiles per row in the partial buffer
   int32_t grid_tiles; // grid z: tiles launched (rows' positions known to stay below grid_tiles * tile), or 0: max_tiles

@@ -56,6 +56,16 @@ __device__ __forceinline__ int row_slot(const RowMap &m, int r) { return m.slot_
 __device__ __forceinline__ int row_pos(const RowMap &m, int r) {
   return m.pos_dev ? m.pos_dev[row_slot(m, r)] : m.pos_base + r % m.rows_per_slot;
 }
+// Element offset of (slot, position) inside one (layer, K|V) block of the
+// ring, head kh: the dense ring [slot][head][P][hd], or the paged pool
+// [head][rows][hd] with the position's row from the page table (page size 1:
+// each position's row is placed independently, the table carried as data).
+template <int HD>
+__device__ __forceinline__ size_t ring_off(const int32_t *ptab, int64_t slot_stride, int P, int rows_per_head,
+                                           int slot, int kh, int pos) {
+  if (ptab) return ((size_t)kh * rows_per_head + (size_t)ptab[(size_t)slot * P + pos]) * HD;
+  return (size_t)slot * slot_stride + ((size_t)kh * P + pos) * HD;
+}
 
 // ------------------------------------------------------------------ GEMV
 //
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(64) void qk_rope_kv_kernel(QkArgs a) {
     dst[lane + HALF] = o1;
     return;
   }
-  const size_t off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD + (size_t)pos * HD;
+  const size_t off = ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, pos);
   const float *vsrc = row + qd + kd + kh * HD;
   const float v0 = vsrc[lane], v1 = vsrc[lane + HALF];
   if constexpr (KVB) {
@@ -406,7 +416,9 @@ __device__ __forceinline__ void kv_unpack(uint4 w, float *v) {
 // Lanes work in groups of CPR = one K/V row (16-byte chunk each): a row is one
 // coalesced read, PG = 256 / CPR rows per pass, and every chunk a thread needs
 // is requested before it is used.
-template <int HD, int G, bool KVB, bool FUSED>
+// PAGED: the tile's rows come through the page table (a separate
+// instantiation, so the dense ring's address arithmetic stays as it is).
+template <int HD, int G, bool KVB, bool FUSED, bool PAGED>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   constexpr int ESZ = KVB ? 2 : 4;
   constexpr int DPC = 16 / ESZ;   // values per chunk
@@ -484,15 +496,33 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
       }
     }
   }
+  // this thread's rows j = p * PG + pg of the tile (position j0 + j): K at
+  // ring + roff, V one K|V block further (dense: consecutive positions;
+  // paged: each row from the page table, all table entries read first)
   const size_t head_off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD;
   const uint8_t *kbase = (const uint8_t *)a.ring_layer + (head_off + (size_t)j0 * HD) * ESZ;
   const uint8_t *vbase = (const uint8_t *)a.ring_layer + (head_off + a.kv_stride + (size_t)j0 * HD) * ESZ;
+  size_t roff[PAGED ? NP : 1];  // paged: byte offset of each row's K chunk (V one K|V block further)
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int j = p * PG + pg;
+      roff[p] = ring_off<HD>(a.ptab, 0, a.P, a.rows_per_head, slot, kh, j0 + (j < jn ? j : 0)) * ESZ + cc * 16;
+    }
+  }
+  auto krow = [&](int p) -> const uint4 * {
+    const int j = p * PG + pg;
+    if constexpr (PAGED) return (const uint4 *)((const uint8_t *)a.ring_layer + roff[p]);
+    return (const uint4 *)(kbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
+  };
+  auto vrow = [&](int p) -> const uint4 * {
+    const int j = p * PG + pg;
+    if constexpr (PAGED) return (const uint4 *)((const uint8_t *)a.ring_layer + roff[p] + (size_t)a.kv_stride * ESZ);
+    return (const uint4 *)(vbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
+  };
   uint4 kc[NP], vc[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int j = p * PG + pg;
-    kc[p] = *(const uint4 *)(kbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
-  }
+  for (int p = 0; p < NP; ++p) kc[p] = *krow(p);
 
   if constexpr (FUSED) {
     const bool act = lane < HALF;
@@ -522,7 +552,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
       }
       if (rs0 + i == r) {
         // set_rows: the row's own workgroup (its last tile) writes its K/V row
-        const size_t off = (size_t)slot * a.slot_stride + (size_t)kh * a.P * HD + (size_t)pos * HD;
+        const size_t off = head_off + (size_t)pos * HD;  // (the fused prologue serves the dense predictor cache)
         if constexpr (KVB) {
           uint16_t *kr = (uint16_t *)a.ring_layer + off, *vr = kr + a.kv_stride;
           kr[lane] = bf16_bits(o0); kr[lane + HALF] = bf16_bits(o1);
@@ -542,10 +572,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   }
   // V rows, requested after the prologue (whose inputs are dead by now)
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int j = p * PG + pg;
-    vc[p] = *(const uint4 *)(vbase + (size_t)(j < jn ? j : 0) * HD * ESZ + cc * 16);
-  }
+  for (int p = 0; p < NP; ++p) vc[p] = *vrow(p);
 
   // Rows of the step's new positions come from the workgroup, not from the
   // ring: the loops below skip them, and they are added after each loop.  A
@@ -717,12 +744,15 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
 template <int HD, int G>
 static void attn_tile_g(int kv_bf16, const AttnArgs &a, hipStream_t s) {
   const dim3 grid(a.M, a.nkv, a.grid_tiles > 0 ? a.grid_tiles : a.max_tiles);
-  if (a.qkv) {
-    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, true>), grid, dim3(256), 0, s, a);
+  if (a.qkv) {  // (the predictor's dense cache: never paged)
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, true, false>), grid, dim3(256), 0, s, a);
+  } else if (a.ptab) {
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, true>), grid, dim3(256), 0, s, a);
   } else {
-    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false>), grid, dim3(256), 0, s, a);
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, false>), grid, dim3(256), 0, s, a);
   }
 }
 
@@ -736,6 +766,7 @@ static void attn_tile_hd(int kv_bf16, const AttnArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine, hipStream_t s) {
+  if (a.qkv && a.ptab) return hipErrorInvalidValue;  // the fused prologue writes the dense cache only
   if (hd == 128) attn_tile_hd<128>(kv_bf16, a, s);
   else attn_tile_hd<64>(kv_bf16, a, s);
   hipError_t e = hipGetLastError();

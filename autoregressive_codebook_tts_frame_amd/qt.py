@@ -20,12 +20,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqt.so")
 
 QT_ABI_MIN_VERSION = 1
-QT_ABI_VERSION = 3
+QT_ABI_VERSION = 4
 QT_OK = 0
 QT_E_ABI, QT_E_ARG, QT_E_SIZE, QT_E_RANGE = -1, -2, -3, -4
 QT_E_STATE, QT_E_CONTEXT_FULL, QT_E_HIP, QT_E_UNSUPPORTED = -5, -6, -7, -8
 QT_LIN_F32, QT_LIN_BF16, QT_LIN_Q8, QT_LIN_Q4 = 0, 1, 2, 3
-QT_F_DUMP, QT_F_EAGER, QT_F_OPS, QT_F_TRACE = 1, 2, 4, 8
+QT_F_DUMP, QT_F_EAGER, QT_F_OPS, QT_F_TRACE, QT_F_PAGED = 1, 2, 4, 8, 16
 QT_PATH_FRAME, QT_PATH_GRAPH, QT_PATH_EAGER = 1, 2, 3
 (QT_DUMP_TALKER_LOGITS, QT_DUMP_PRED_LOGITS, QT_DUMP_BRIDGE, QT_DUMP_X0, QT_DUMP_GATHER,
  QT_DUMP_TPOS, QT_DUMP_HIDDEN, QT_DUMP_TRACE) = range(1, 9)
@@ -35,7 +35,7 @@ QT_KERNEL_GEMV_GATE_UP = 1
 EXPORTS = ("qt_abi_version", "qt_query_sizes", "qt_init", "qt_prefill", "qt_decode_frame",
            "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_time_kernel",
            "qt_set_sampler", "qt_path", "qt_free", "qt_last_error", "qt_stream_read",
-           "qt_decode_frame_noalloc")
+           "qt_decode_frame_noalloc", "qt_query_paged_ring")
 
 
 class qt_model_desc(C.Structure):
@@ -71,7 +71,7 @@ class qt_init_params(C.Structure):
                 ("arena", C.c_void_p), ("arena_bytes", C.c_size_t),
                 ("max_batch", C.c_int32), ("frames_per_replay", C.c_int32),
                 ("max_frames_per_call", C.c_int32), ("flags", C.c_uint32),
-                ("stream", C.c_void_p)]
+                ("stream", C.c_void_p), ("pool_rows", C.c_int32)]
 
 
 def _load():
@@ -83,6 +83,8 @@ def _load():
     lib.qt_query_sizes.argtypes = [C.POINTER(qt_model_desc), i32, i32, i32, C.c_uint32,
                                    C.POINTER(sz), C.POINTER(sz)]
     lib.qt_query_sizes.restype = i32
+    lib.qt_query_paged_ring.argtypes = [C.POINTER(qt_model_desc), i32, i32, C.POINTER(sz)]
+    lib.qt_query_paged_ring.restype = i32
     lib.qt_init.argtypes = [C.POINTER(qt_init_params), C.POINTER(vp)]
     lib.qt_init.restype = i32
     lib.qt_prefill.argtypes = [vp, i32, i32, vp, vp]
@@ -152,6 +154,12 @@ def qt_query_sizes(desc: qt_model_desc, max_batch: int, frames_per_replay: int =
     _check(lib.qt_query_sizes(C.byref(desc), max_batch, frames_per_replay, max_frames_per_call,
                               flags, C.byref(rb), C.byref(ab)))
     return rb.value, ab.value
+
+
+def qt_query_paged_ring(desc: qt_model_desc, max_batch: int, pool_rows: int) -> int:
+    rb = C.c_size_t()
+    _check(lib.qt_query_paged_ring(C.byref(desc), max_batch, pool_rows, C.byref(rb)))
+    return rb.value
 
 
 def qt_init(params: qt_init_params):
@@ -273,7 +281,10 @@ class Decoder:
 
     def __init__(self, m: synth.Model, weights, batch: int, frames_per_replay: int = 1,
                  max_frames_per_call: int = 256, flags: int = 0, device="cuda",
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, pool_rows: int = 0):
+        """pool_rows > 0: a paged talker ring (QT_F_PAGED) of that many rows."""
+        if pool_rows:
+            flags |= QT_F_PAGED
         self.m = m
         self.B = batch
         self.K = frames_per_replay
@@ -281,6 +292,9 @@ class Decoder:
         self.dw = weights if isinstance(weights, DeviceWeights) else DeviceWeights(m, weights, device)
         self.desc = model_desc(m)
         rb, ab = qt_query_sizes(self.desc, batch, frames_per_replay, max_frames_per_call, flags)
+        if pool_rows:
+            rb = qt_query_paged_ring(self.desc, batch, pool_rows)
+        self.pool_rows = pool_rows
         self.ring = torch.zeros(rb, dtype=torch.uint8, device=device)
         self.arena = torch.zeros(ab, dtype=torch.uint8, device=device)
         self.stream = stream if stream is not None else torch.cuda.Stream(device=device)
@@ -296,6 +310,7 @@ class Decoder:
         p.max_frames_per_call = max_frames_per_call
         p.flags = flags
         p.stream = self.stream.cuda_stream
+        p.pool_rows = pool_rows
         self.params = p
         self.ctx = qt_init(p)
 
@@ -316,6 +331,7 @@ class Decoder:
 
     def talker_ring(self) -> torch.Tensor:
         """View [B][Lt][2][nkv][P][hd] (bf16 bits as int16, or float32)."""
+        assert not self.pool_rows, "a paged ring has no per-slot layout"
         m = self.m
         esz = 2 if m.kv_bf16 else 4
         n = self.B * m.Lt * 2 * m.nkv * m.P * m.hd
@@ -324,7 +340,7 @@ class Decoder:
     def predictor_ring(self) -> torch.Tensor:
         m = self.m
         esz = 2 if m.kv_bf16 else 4
-        n0 = self.B * m.Lt * 2 * m.nkv * m.P * m.hd
+        n0 = (self.pool_rows if self.pool_rows else self.B * m.P) * m.Lt * 2 * m.nkv * m.hd
         n = self.B * m.Lp * 2 * m.nkv * m.Q * m.hd
         return self.ring[n0 * esz:(n0 + n) * esz].view(self._kv_dtype()).view(
             self.B, m.Lp, 2, m.nkv, m.Q, m.hd)

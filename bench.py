@@ -159,15 +159,19 @@ def ttfa(args, d, m, wl, B):
     }
 
 
-def setup(qt, synth, wl, dw, nf, flags, args):
+def setup(qt, synth, wl, dw, nf, flags, args, paged=False):
     """A decoder for wl with every stream prefilled from its seeded prompt;
-    returns it, the context lengths, the slot states and the overlay ids."""
+    returns it, the context lengths, the slot states and the overlay ids.
+    paged: a paged talker ring holding exactly the prompts plus nf frames of
+    every stream (a step restores the states, so its rows are reused)."""
     B = wl.batch
-    d = qt.Decoder(wl.model, dw, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf, flags=flags)
+    ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
+    pool = int(sum(int(c) for c in ctx)) + B * nf if paged else 0
+    d = qt.Decoder(wl.model, dw, B, frames_per_replay=wl.frames_per_replay, max_frames_per_call=nf, flags=flags,
+                   pool_rows=pool)
     if args.temperature:
         d.set_sampler(args.temperature, args.seed, top_k=args.top_k)
     lens = []
-    ctx = synth.make_context_lengths(wl)  # ragged per-stream contexts where the workload has them
     for b in range(B):
         codes, text = synth.make_prompt(wl, b, T=int(ctx[b]))
         d.prefill(b, codes, text)
@@ -224,6 +228,8 @@ def main():
     ap.add_argument("--ttfa", action="store_true",
                     help="time to first frame instead: a step is the prompt prefill of every stream plus "
                          "one decoded frame")
+    ap.add_argument("--paged", action="store_true",
+                    help="decode on a paged talker ring holding exactly the streams' contexts (per-op path)")
     ap.add_argument("--no-b32", action="store_true",
                     help="skip the 32-stream leg that the default run times after the batch-1 workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -253,7 +259,7 @@ def main():
         import dataclasses
         wl = dataclasses.replace(wl, frames_per_replay=args.frames_per_replay)
     dw = qt.DeviceWeights(m, w, "cuda")
-    d, lens, states, ov = setup(qt, synth, wl, dw, nf, qt.QT_F_OPS if args.ops else 0, args)
+    d, lens, states, ov = setup(qt, synth, wl, dw, nf, qt.QT_F_OPS if args.ops else 0, args, paged=args.paged)
     if args.ttfa:
         print(json.dumps(ttfa(args, d, m, wl, B)), flush=True)
         d.close()
@@ -319,6 +325,18 @@ def main():
                "gpu_event_s": gpu32, "wall_s": wall32}
         log(f"{wl32.name}: {b32['value']:.1f} frames/s, {ms32:.3f} ms per frame-step, "
             f"{b32['frame_roofline']['frac']:.3f} of HBM peak")
+        dense_ring = int(d32.ring.numel())
+        d32.close()
+        # the same 32 streams on a paged ring (page size 1) holding exactly
+        # their contexts: its memory against the dense rings', and its rate
+        d32, lens32, states32, ov32 = setup(qt, synth, wl32, dw, nf32, 0, args, paged=True)
+        wallp, gpup = time_steps(d32, states32, ov32, nf32, args.steps, args.warmup)
+        b32["paged"] = {"value": wl32.batch * nf32 * args.steps / wallp, "unit": "frames/s",
+                        "ms_per_frame_step": 1e3 * wallp / (nf32 * args.steps), "pool_rows": d32.pool_rows,
+                        "ring_bytes": int(d32.ring.numel()), "dense_ring_bytes": dense_ring,
+                        "gpu_event_s": gpup, "wall_s": wallp}
+        log(f"{wl32.name} paged: {b32['paged']['value']:.1f} frames/s, ring {d32.ring.numel() / 2**30:.2f} GiB "
+            f"against {dense_ring / 2**30:.2f} GiB dense")
         d32.close()
 
     res = {

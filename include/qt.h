@@ -45,7 +45,7 @@ extern "C" {
    ([QT-tests], codec left context / ABI range entry: the range check rejects
    a version past either bound). */
 #define QT_ABI_MIN_VERSION 1
-#define QT_ABI_VERSION 3 /* 2: qt_set_sampler; 3: qt_stream_read */
+#define QT_ABI_VERSION 4 /* 2: qt_set_sampler; 3: qt_stream_read; 4: paged ring (QT_F_PAGED) */
 
 #define QT_OK 0
 #define QT_E_ABI (-1)          /* abi_version outside the closed range (checked first) */
@@ -75,6 +75,13 @@ extern "C" {
                          frame kernel applies (single stream); for comparisons */
 #define QT_F_TRACE 8u /* persistent kernel: workgroup 0 stamps every phase of the
                          first frame of a call (read with QT_DUMP_TRACE) */
+#define QT_F_PAGED 16u /* paged talker ring, page size 1 ([MC-opt] core table:
+                          paged KV for many streams): one pool of pool_rows
+                          rows per (layer, K|V, head) shared by every slot,
+                          rows handed out as positions are first written and
+                          returned when a slot is prefilled again; the page
+                          table (slot, position) -> row is device data, so the
+                          graph never changes.  Decodes on the per-op path. */
 
 typedef struct qt_model_desc {
   int32_t hidden;              /* H: width of talker and predictor */
@@ -153,6 +160,13 @@ typedef struct qt_init_params {
   int32_t max_frames_per_call; /* frames staged per upload; longer calls loop */
   uint32_t flags;              /* QT_F_* */
   void *stream;                /* hipStream_t, caller-owned; non-default unless QT_F_EAGER */
+  /* ABI 4: with QT_F_PAGED, the talker ring's rows per (layer, K|V, head),
+     shared by all slots (>= 1); the ring is then the pool
+     [Lt][2][nkv][pool_rows][hd] followed by the predictor cache
+     [B][Lp][2][nkv][Q][hd], sized by qt_query_paged_ring.  Callers of an
+     older ABI pass the structure without this field (struct_size up to
+     `stream`): a dense ring. */
+  int32_t pool_rows;
 } qt_init_params;
 
 typedef struct qt_ctx qt_ctx;
@@ -170,6 +184,14 @@ int32_t qt_abi_version(void);
 int32_t qt_query_sizes(const qt_model_desc *model, int32_t max_batch, int32_t frames_per_replay,
                        int32_t max_frames_per_call, uint32_t flags, size_t *ring_bytes,
                        size_t *arena_bytes);
+
+/* Ring bytes of a QT_F_PAGED context (the library's own helper; the arena is
+   the same as qt_query_sizes gives): talker pool Lt*2*nkv*pool_rows*hd*e plus
+   the predictor cache B*Lp*2*nkv*Q*hd*e.  A pool holding every slot's
+   longest context is the dense ring's size at most; ragged contexts need
+   their sum.  Errors: QT_E_ARG (NULL output, non-positive sizes),
+   QT_E_UNSUPPORTED. */
+int32_t qt_query_paged_ring(const qt_model_desc *model, int32_t max_batch, int32_t pool_rows, size_t *ring_bytes);
 
 /* Validates, binds caller memory, uploads the RoPE table, and (unless
    QT_F_EAGER) captures the K-frame graph on params->stream.  Everything a
@@ -191,8 +213,10 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out);
    sum_g code_emb[g][codes[p][g]] + text_emb[text_ids[p]] (codes may be NULL:
    text rows only).  Writes ring rows [0, T), sets the slot's bridge (final
    normed hidden of row T-1), c0 (argmax of the talker head) and pos = T.
-   codes: host [T][G] or NULL; text_ids: host [T].  Synchronous.
-   Errors: QT_E_ARG, QT_E_RANGE, QT_E_CONTEXT_FULL (T > P), QT_E_HIP. */
+   codes: host [T][G] or NULL; text_ids: host [T].  Synchronous.  Paged ring:
+   the slot's rows go back to the pool first, then it takes T rows.
+   Errors: QT_E_ARG, QT_E_RANGE, QT_E_CONTEXT_FULL (T > P, or a paged pool
+   without T free rows), QT_E_HIP. */
 int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
                    const int32_t *text_ids);
 
@@ -209,8 +233,9 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
    frame ([QT-log] set_rows / hot-loop entry).
    With a sampler set (qt_set_sampler) codes_out holds the sampled codes.
    Errors: QT_E_ARG (n_frames % K, NULLs), QT_E_RANGE, QT_E_STATE (a slot not
-   prefilled), QT_E_CONTEXT_FULL (pos + n_frames > P; checked before any
-   launch), QT_E_HIP. */
+   prefilled), QT_E_CONTEXT_FULL (pos + n_frames > P, or a paged pool
+   without the rows the new positions need; checked before any launch),
+   QT_E_HIP. */
 int32_t qt_decode_frame(qt_ctx *ctx, int32_t n_frames, const int32_t *overlay_ids,
                         int32_t *codes_out, const int32_t *forced_codes);
 
@@ -238,8 +263,10 @@ int32_t qt_decode_frame_noalloc(qt_ctx *ctx, int32_t n_frames, const int32_t *ov
    position, the pending code 0, and the bridge (host float [H]; the bridge
    is the [QT-log] set_rows entry's device-resident talker hidden).  The
    ring itself is caller memory at the documented layout.  set marks the slot
-   prefilled.
-   Errors: QT_E_ARG, QT_E_RANGE (pos outside [1, P], c0 outside [0, Vc)). */
+   prefilled.  Paged ring: set needs rows for positions [0, pos) already
+   given to the slot (by its prefill and decodes).
+   Errors: QT_E_ARG, QT_E_RANGE (pos outside [1, P], c0 outside [0, Vc)),
+   QT_E_STATE (paged: the slot holds fewer than pos rows). */
 int32_t qt_get_slot_state(qt_ctx *ctx, int32_t slot, int32_t *pos, int32_t *c0, float *bridge);
 int32_t qt_set_slot_state(qt_ctx *ctx, int32_t slot, int32_t pos, int32_t c0,
                           const float *bridge);

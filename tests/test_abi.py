@@ -67,8 +67,8 @@ def test_abi_range_both_bounds_reject():
 
 
 def test_struct_size_and_null_arguments():
-    rc, _ = _init_rc(_params(struct_size=C.sizeof(qt.qt_init_params) - 8))
-    assert rc == qt.QT_E_ARG
+    rc, _ = _init_rc(_params(struct_size=C.sizeof(qt.qt_init_params) - 4))
+    assert rc == qt.QT_E_ARG and "struct_size" in qt.qt_last_error()
     assert qt.lib.qt_init(None, None) == qt.QT_E_ARG
     rc, _ = _init_rc(_params())  # no ring / arena
     assert rc == qt.QT_E_ARG
@@ -113,3 +113,32 @@ def test_null_context_calls_fail_cleanly():
     assert qt.lib.qt_decode_frame(None, 1, None, None, None) == qt.QT_E_ARG
     assert qt.lib.qt_read_dump(None, 1, None, 0) == qt.QT_E_ARG
     qt.lib.qt_free(None)
+
+
+def test_older_callers_struct_without_pool_rows_is_accepted():
+    # ABI 1-3 callers pass the structure up to `stream`: it passes the size
+    # check and reaches the next validation (an undersized ring here)
+    rb, ab = qt.qt_query_sizes(qt.model_desc(synth.TINY), 1, 1, 8, qt.QT_F_EAGER)
+    fake = 1 << 40
+    old = qt.qt_init_params.pool_rows.offset
+    rc, _ = _init_rc(_params(struct_size=old, abi_version=3, ring=fake, ring_bytes=rb - 1, arena=fake, arena_bytes=ab))
+    assert rc == qt.QT_E_SIZE
+
+
+def test_paged_ring_sizes():
+    # pool [Lt][2][nkv][rows][hd] then the predictor cache [B][Lp][2][nkv][Q][hd]
+    m = synth.BIG
+    for B, rows in ((1, 1), (32, 35000), (8, 4096 * 8)):
+        rb = qt.qt_query_paged_ring(qt.model_desc(m), B, rows)
+        assert rb == (m.Lt * 2 * m.nkv * rows * m.hd + B * m.Lp * 2 * m.nkv * m.Q * m.hd) * 2
+    # a pool of B * P rows is the dense ring's size
+    dense, _ = qt.qt_query_sizes(qt.model_desc(m), 8)
+    assert qt.qt_query_paged_ring(qt.model_desc(m), 8, 8 * m.P) == dense
+    for args in ((0, 10), (1, 0)):
+        with pytest.raises(qt.QtError) as e:
+            qt.qt_query_paged_ring(qt.model_desc(m), *args)
+        assert e.value.code == qt.QT_E_ARG
+    # the flag is known to the size query; a paged context needs pool rows
+    qt.qt_query_sizes(qt.model_desc(synth.TINY), 1, 1, 8, qt.QT_F_PAGED)
+    rc, _ = _init_rc(_params(flags=qt.QT_F_EAGER | qt.QT_F_PAGED, pool_rows=0))
+    assert rc == qt.QT_E_ARG and "pool_rows" in qt.qt_last_error()

@@ -29,10 +29,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None, sampler=None, flags=0):
+def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None, sampler=None, flags=0, pool_rows=0,
+                order=None):
     """Oracle free run, then the GPU teacher-forced with the oracle's codes
     (one frame per call, dumps read after each) and free-running.
-    sampler: (temperature, seed) set on both sides before the prefill."""
+    sampler: (temperature, seed) set on both sides before the prefill.
+    pool_rows: a paged ring of that many rows; order: the GPU's prefill order."""
     prompts = prompts or [synth.make_prompt(wl, b) for b in range(batch)]
     ov = synth.make_overlays(wl, nframes, batch)
     o = Oracle(m, w, batch, pcap=max(len(p[1]) for p in prompts) + nframes + 1)
@@ -44,11 +46,11 @@ def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None, sam
     ostate = [o.get_state(b) for b in range(batch)]
     oout = o.decode(nframes, ov, dump=True, hidden=dump_hidden)
 
-    d = qt.Decoder(m, w, batch, flags=qt.QT_F_DUMP | flags)
+    d = qt.Decoder(m, w, batch, flags=qt.QT_F_DUMP | flags, pool_rows=pool_rows)
     if sampler:
         d.set_sampler(*sampler)
-    for b, (c, t) in enumerate(prompts):
-        d.prefill(b, c, t)
+    for b in (order or range(batch)):
+        d.prefill(b, *prompts[b])
     gstate = [d.get_state(b) for b in range(batch)]
     gpre = d.dump(qt.QT_DUMP_TALKER_LOGITS)
     g = {k: [] for k in ("codes", "talker_logits", "pred_logits", "bridge", "x0", "gather", "tpos", "hidden")}
@@ -65,7 +67,7 @@ def _forced_run(m, w, wl, nframes, batch=1, dump_hidden=False, prompts=None, sam
     g = {k: np.stack(v) for k, v in g.items() if v}
     return dict(o=o, d=d, ov=ov, prompts=prompts, pre_logits=pre_logits, ostate=ostate,
                 oout=oout, gstate=gstate, gpre=gpre, g=g, sampler=sampler, flags=flags,
-                q0=[len(t) for _, t in prompts])
+                q0=[len(t) for _, t in prompts], pool_rows=pool_rows)
 
 
 def _read_state(d, b, length):
@@ -209,7 +211,7 @@ def _check(r, m, label, free_run=True):
         assert np.array_equal(codes, oout["codes"]), f"{label}: free-run codes differ"
     elif free_run and not bad:
         # free running from the same prefill reproduces the oracle's codes
-        d2 = qt.Decoder(m, r["d"].dw, B, flags=r.get("flags", 0))
+        d2 = qt.Decoder(m, r["d"].dw, B, flags=r.get("flags", 0), pool_rows=r.get("pool_rows", 0))
         if r.get("sampler"):
             d2.set_sampler(*r["sampler"])
         for b, (c, t) in enumerate(r["prompts"]):
@@ -777,3 +779,89 @@ def test_exact_ties_bf16_full_width():
                     err = float(np.max(np.abs(gl[j - 1, b] - rl)))
                     assert margin(rl) <= 4 * err, f"code {j} differs away from a near tie"
         d.close()
+
+
+# ----------------------------------------------------------------- paged ring
+
+
+def _paged_vs_dense(m, w, prompts, frames, pool_rows, order, wl, sampler=None):
+    """A dense and a paged context decode the same prompts: the outputs must be
+    bitwise equal (the paged ring only moves rows).  Slots are prefilled in
+    `order`, so each slot's rows are scattered through the pool."""
+    B = len(prompts)
+    dd = qt.Decoder(m, w, B, flags=qt.QT_F_DUMP)
+    dp = qt.Decoder(m, dd.dw, B, flags=qt.QT_F_DUMP, pool_rows=pool_rows)
+    assert dd.path == dp.path == qt.QT_PATH_GRAPH
+    for d in (dd, dp):
+        if sampler:
+            d.set_sampler(*sampler)
+        for b in order:
+            d.prefill(b, *prompts[b])
+    return dd, dp
+
+
+def _same_outputs(dd, dp, n, ov):
+    cd = dd.decode(n, ov)
+    cp = dp.decode(n, ov)
+    assert np.array_equal(cd, cp)
+    for kind in (qt.QT_DUMP_TALKER_LOGITS, qt.QT_DUMP_PRED_LOGITS, qt.QT_DUMP_BRIDGE):
+        assert np.array_equal(dd.dump(kind).view(np.uint32), dp.dump(kind).view(np.uint32))
+    return cd
+
+
+@pytest.mark.parametrize("sampler", [None, (0.9, 11, 50)], ids=["greedy", "top50"])
+def test_paged_ring_equals_dense(sampler):
+    # four ragged streams (40 to 460 rows: one to two 256-position tiles),
+    # prefilled out of order, decoded in calls of 8, 4 and 4 frames; then one
+    # slot re-prefilled with a shorter prompt (its rows go back to the pool
+    # and are reused) and decoded again; the pool holds exactly what the
+    # streams need, so one more frame is refused
+    m = _reduced(synth.BIG)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
+    lens = [40, 300, 130, 460]
+    prompts = [synth.make_prompt(wl, b, T=t) for b, t in enumerate(lens)]
+    short = synth.make_prompt(wl, 7, T=70)
+    n = 16
+    pool = sum(lens) + len(lens) * n
+    say(f"[paged {sampler}] prompts {lens}, pool {pool} rows")
+    dd, dp = _paged_vs_dense(m, w, prompts, n, pool, [2, 0, 3, 1], wl, sampler)
+    ov = synth.make_overlays(wl, n, len(lens))
+    _same_outputs(dd, dp, 8, ov[:8])
+    _same_outputs(dd, dp, 4, ov[8:12])
+    for d in (dd, dp):  # slot 3 restarts: 460 rows back to the pool, 70 taken
+        d.prefill(3, *short)
+    _same_outputs(dd, dp, 4, ov[12:16])
+    # 4 x 16 frames + the prompts fill the pool but for what slot 3 gave back
+    st = [dp.get_state(b) for b in range(len(lens))]
+    free = pool - (lens[0] + lens[1] + lens[2] + 3 * n) - (70 + 4)
+    assert free == 460 + 12 - 70
+    # frames until the pool runs out: every slot needs a row per frame
+    k = free // len(lens)
+    _same_outputs(dd, dp, k, np.repeat(ov[:1], k, axis=0))
+    with pytest.raises(qt.QtError) as e:
+        dp.decode(len(lens), np.repeat(ov[:1], len(lens), axis=0))
+    assert e.value.code == qt.QT_E_CONTEXT_FULL
+    # refused before any launch: the state did not move
+    assert [dp.get_state(b)[0] for b in range(len(lens))] == [s[0] + k for s in st]
+    # a restored position needs the slot's rows to exist
+    with pytest.raises(qt.QtError) as e:
+        dp.set_state(0, st[0][0] + k + 1, *st[0][1:])
+    assert e.value.code == qt.QT_E_STATE
+    dd.close()
+    dp.close()
+
+
+def test_paged_ring_oracle_parity():
+    # the paged ring against the oracle, at the 1e-2 gates: three ragged
+    # streams (60, 270, 150 rows) prefilled out of order, so each stream's
+    # rows are scattered through the pool (its exact size)
+    m = _reduced(synth.BIG)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
+    lens = [60, 270, 150]
+    prompts = [synth.make_prompt(wl, b, T=t) for b, t in enumerate(lens)]
+    say(f"[paged oracle] prompts {lens}, 4 frames")
+    r = _forced_run(m, w, wl, 4, batch=3, prompts=prompts, pool_rows=sum(lens) + 3 * 4, order=[1, 2, 0])
+    assert r["d"].path == qt.QT_PATH_GRAPH and r["d"].pool_rows
+    _check(r, m, "paged_b3")
