@@ -189,6 +189,10 @@ struct qt_ctx {
   size_t pu_ctl = 0, pu_overlay = 0, pu_forced = 0, pu_pf_text = 0, pu_pf_codes = 0, pu_scalar = 0;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  // adaptive K: a 1-frame graph for the frames of a call past its last
+  // whole K-frame block (K > 1 only)
+  hipGraph_t graph1 = nullptr;
+  hipGraphExec_t exec1 = nullptr;
   int32_t path = QT_PATH_GRAPH;
   qtk::FrameArgs fa;       // persistent kernel arguments (path == QT_PATH_FRAME)
   int lds_limit = 0;       // LDS per workgroup on the device
@@ -525,11 +529,12 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
   return launch_argmax(am, s);
 }
 
-hipError_t enqueue_replay(qt_ctx *c) {
+// kf frames (a replay of the K-frame graph, or the 1-frame one)
+hipError_t enqueue_replay(qt_ctx *c, int kf) {
   hipError_t e;
-  for (int k = 0; k < c->K; ++k)
+  for (int k = 0; k < kf; ++k)
     if ((e = enqueue_frame(c, k)) != hipSuccess) return e;
-  return launch_advance(c->A<int32_t>(c->L.ctl), c->K, c->stream);
+  return launch_advance(c->A<int32_t>(c->L.ctl), kf, c->stream);
 }
 
 const char *frame_unsupported(const qt_model_desc &m, int B) {
@@ -606,6 +611,8 @@ void qt_free(qt_ctx *c) {
   if (!c) return;
   if (c->exec) (void)hipGraphExecDestroy(c->exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->exec1) (void)hipGraphExecDestroy(c->exec1);
+  if (c->graph1) (void)hipGraphDestroy(c->graph1);
   if (c->pin_up) (void)hipHostFree(c->pin_up);
   if (c->pin_down) (void)hipHostFree(c->pin_down);
   delete c;
@@ -795,14 +802,20 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out) {
     }
   }
   if (c->path == QT_PATH_GRAPH) {
-    hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
-    if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)));
-    hipError_t eq = enqueue_replay(c);
-    e = hipStreamEndCapture(c->stream, &c->graph);
-    if (eq != hipSuccess) return bail(fail(c, QT_E_HIP, "frame capture: %s", hipGetErrorString(eq)));
-    if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e)));
-    e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0);
-    if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e)));
+    // the K-frame graph, and for K > 1 a 1-frame one (the tail of a call)
+    for (const int kf : {c->K, 1}) {
+      if (kf == 1 && c->K == 1) break;
+      hipGraph_t &g = kf == c->K ? c->graph : c->graph1;
+      hipGraphExec_t &x = kf == c->K ? c->exec : c->exec1;
+      hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
+      if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)));
+      hipError_t eq = enqueue_replay(c, kf);
+      e = hipStreamEndCapture(c->stream, &g);
+      if (eq != hipSuccess) return bail(fail(c, QT_E_HIP, "frame capture: %s", hipGetErrorString(eq)));
+      if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e)));
+      e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+      if (e != hipSuccess) return bail(fail(c, QT_E_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e)));
+    }
   }
   *out = c;
   return QT_OK;
@@ -902,7 +915,6 @@ int32_t decode_entry(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *
   const Dims &d = c->d;
   const int B = c->B;
   if (n <= 0 || !overlay_ids || !codes_out) return fail(c, QT_E_ARG, "n_frames must be positive, pointers non-NULL");
-  if (n % c->K) return fail(c, QT_E_ARG, "n_frames %d is not a multiple of frames_per_replay %d", n, c->K);
   size_t short_rows = 0;  // paged: pool rows the new positions still need
   for (int b = 0; b < B; ++b) {
     if (!c->ready[b]) return fail(c, QT_E_STATE, "slot %d not prefilled", b);
@@ -994,9 +1006,14 @@ int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t 
       c->tag_base += (uint32_t)span;
       HIPCHK(c, launch_frame_kernel(fa, s));
     } else {
+      // adaptive K: whole K-frame blocks, then the rest one frame at a time
       for (int r = 0; r < nf / c->K; ++r) {
         if (c->exec) HIPCHK(c, hipGraphLaunch(c->exec, s));
-        else HIPCHK(c, enqueue_replay(c));
+        else HIPCHK(c, enqueue_replay(c, c->K));
+      }
+      for (int r = 0; r < nf % c->K; ++r) {
+        if (c->exec1) HIPCHK(c, hipGraphLaunch(c->exec1, s));
+        else HIPCHK(c, enqueue_replay(c, 1));
       }
     }
     HIPCHK(c, hipMemcpyAsync(c->pin_down, c->A<int32_t>(c->L.cout), sizeof(int32_t) * nf * B * d.G, hipMemcpyDeviceToHost, s));

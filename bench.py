@@ -114,13 +114,14 @@ def ttfa(args, d, m, wl, B):
     import numpy as np
     from autoregressive_codebook_tts_frame_amd import synth
 
-    prompts = [synth.make_prompt(wl, b) for b in range(B)]
-    ov = synth.make_overlays(wl, wl.frames_per_replay, B)
+    ctx = synth.make_context_lengths(wl)  # the workload's (ragged) prompt lengths
+    prompts = [synth.make_prompt(wl, b, T=int(ctx[b])) for b in range(B)]
+    ov = synth.make_overlays(wl, 1, B)
 
-    def step():
+    def step():  # one frame, whatever the frames per replay (adaptive K: a 1-frame graph)
         for b, (c, t) in enumerate(prompts):
             d.prefill(b, c, t)
-        d.decode(wl.frames_per_replay, ov)
+        d.decode(1, ov)
 
     for _ in range(args.warmup):
         step()
@@ -136,8 +137,8 @@ def ttfa(args, d, m, wl, B):
         for b, (c, t) in enumerate(prompts):
             d.prefill(b, c, t)
         pre.append(time.perf_counter() - t0)
-    T = len(prompts[0][1])
-    chunks = B * ((T + 127) // 128)
+    T = int(np.mean([len(t) for _, t in prompts]))  # (mean prompt rows, for the record)
+    chunks = sum((len(t) + 127) // 128 for _, t in prompts)
     wbytes = talker_weight_bytes(m)
     ms = 1e3 * float(np.median(times))
     pre_ms = 1e3 * float(np.median(pre))

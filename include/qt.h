@@ -156,7 +156,7 @@ typedef struct qt_init_params {
   void *arena;
   size_t arena_bytes;
   int32_t max_batch;           /* B: streams decoded together (slots 0..B-1) */
-  int32_t frames_per_replay;   /* K: frames per graph replay; n_frames % K == 0 */
+  int32_t frames_per_replay;   /* K: frames per graph replay (a call's tail replays a 1-frame graph) */
   int32_t max_frames_per_call; /* frames staged per upload; longer calls loop */
   uint32_t flags;              /* QT_F_* */
   void *stream;                /* hipStream_t, caller-owned; non-default unless QT_F_EAGER */
@@ -223,7 +223,11 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
 /* Decodes n_frames frames for all B slots.  With one slot (B = 1) and a shape
    the persistent kernel implements, one kernel launch runs every phase of the
    frames (qt_path() reports which path a context uses); otherwise each K-frame
-   block is one replay of a graph of per-op kernels.
+   block is one replay of a graph of per-op kernels, and the frames past the
+   call's last whole block replay a second, 1-frame graph (adaptive K: a short
+   call, such as a stream's first frame, is not held to K frames, while long
+   calls keep K-frame replays; [MC-opt] experiments table: K trades
+   throughput against time to first audio).  Any n_frames > 0.
    overlay_ids: host [n][B] (frame f's talker step adds text_emb row
    overlay_ids[f][b]).  codes_out: host [n][B][G]: codes_out[f][b][0] is the
    talker's greedy code for frame f, [1..G-1] the predictor's.  forced_codes:
@@ -232,7 +236,7 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
    codes are in codes_out on return.  Only ids cross the host boundary per
    frame ([QT-log] set_rows / hot-loop entry).
    With a sampler set (qt_set_sampler) codes_out holds the sampled codes.
-   Errors: QT_E_ARG (n_frames % K, NULLs), QT_E_RANGE, QT_E_STATE (a slot not
+   Errors: QT_E_ARG (n_frames <= 0, NULLs), QT_E_RANGE, QT_E_STATE (a slot not
    prefilled), QT_E_CONTEXT_FULL (pos + n_frames > P, or a paged pool
    without the rows the new positions need; checked before any launch),
    QT_E_HIP. */

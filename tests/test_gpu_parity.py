@@ -272,6 +272,25 @@ def test_tiny_repeat_runs_identical_and_multi_frame_call(tiny):
     assert np.array_equal(runs[0], r["oout"]["codes"])
 
 
+def test_tiny_adaptive_k_any_frame_count(tiny):
+    # four frames per graph replay, calls of 1, 3 and 6 frames (one 1-frame
+    # graph replay, three, then a 4-frame replay and two 1-frame ones): the
+    # codes of one 10-frame call with one frame per replay, bit for bit
+    m, w, wl, r = tiny
+    ov = synth.make_overlays(wl, 10)
+    prompt = synth.make_prompt(wl, 0)
+    d1 = qt.Decoder(m, r["d"].dw, 1, flags=qt.QT_F_OPS)
+    d1.prefill(0, *prompt)
+    ref = d1.decode(10, ov)
+    d4 = qt.Decoder(m, r["d"].dw, 1, frames_per_replay=4, max_frames_per_call=8, flags=qt.QT_F_OPS)
+    d4.prefill(0, *prompt)
+    got = np.concatenate([d4.decode(1, ov[:1]), d4.decode(3, ov[1:4]), d4.decode(6, ov[4:])])
+    say("[tiny adaptive K] calls of 1, 3, 6 frames at K = 4 (6 = a 4-frame replay + 2 single ones)")
+    assert np.array_equal(got, ref)
+    d1.close()
+    d4.close()
+
+
 def test_tiny_batched_equals_per_stream_and_permutation(tiny):
     m, w, wl, r = tiny
     wl3 = dataclasses.replace(wl, batch=3)
@@ -627,7 +646,7 @@ def test_full_bf16_b32_parity():
 
 
 @pytest.mark.timeout(900)
-def test_full_bf16_b32_replay_of_four_frames_equals_one():
+def test_full_bf16_b32_replay_of_four_frames_equals_one_and_adaptive_k():
     # four frames per graph replay (as the bench times the workload) decode
     # the same codes and last-frame logits as one frame per replay, bit for bit
     m = synth.BIG
@@ -638,16 +657,25 @@ def test_full_bf16_b32_replay_of_four_frames_equals_one():
     ov = synth.make_overlays(wl, 8)
     dw = qt.DeviceWeights(m, w, "cuda")
     out = {}
-    for K in (1, 4):
-        say(f"[bf16_b32 replay] K = {K}: 32 prefills, 8 frames")
+    for K, calls in ((1, [8]), (4, [8]), (4, [1, 2, 5])):
+        # (K = 4 in calls of 1, 2 and 5 frames: adaptive K replays the 1-frame
+        # graph for the frames past each call's last whole block)
+        say(f"[bf16_b32 replay] K = {K}: 32 prefills, calls of {calls} frames")
         d = qt.Decoder(m, dw, wl.batch, frames_per_replay=K, flags=qt.QT_F_DUMP)
         for b, (c, t) in enumerate(prompts):
             d.prefill(b, c, t)
-        out[K] = (d.decode(8, ov), d.dump(qt.QT_DUMP_TALKER_LOGITS), d.dump(qt.QT_DUMP_PRED_LOGITS))
+        codes, f0 = [], 0
+        for n in calls:
+            codes.append(d.decode(n, ov[f0:f0 + n]))
+            f0 += n
+        out[(K, len(calls))] = (np.concatenate(codes), d.dump(qt.QT_DUMP_TALKER_LOGITS),
+                                d.dump(qt.QT_DUMP_PRED_LOGITS))
         d.close()
-    assert np.array_equal(out[1][0], out[4][0])
-    assert np.array_equal(out[1][1].view(np.uint32), out[4][1].view(np.uint32))
-    assert np.array_equal(out[1][2].view(np.uint32), out[4][2].view(np.uint32))
+    ref = out[(1, 1)]
+    for key in ((4, 1), (4, 3)):
+        assert np.array_equal(ref[0], out[key][0])
+        assert np.array_equal(ref[1].view(np.uint32), out[key][1].view(np.uint32))
+        assert np.array_equal(ref[2].view(np.uint32), out[key][2].view(np.uint32))
 
 
 @pytest.mark.timeout(900)
