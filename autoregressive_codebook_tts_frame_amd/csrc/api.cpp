@@ -94,7 +94,8 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   }
   {
     const int nmax = d.nqkv > d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (d.F > d.Vc ? d.F : d.Vc);
-    L.gcnt_bytes = sizeof(uint32_t) * (size_t)(nmax / 32 + 1 + (d.H / 32));  // tiles of every projection
+    // a counter per (32-column tile, 64-row block) of every projection
+    L.gcnt_bytes = sizeof(uint32_t) * 2 * (size_t)(nmax / 32 + 1 + (d.H / 32));
     L.gcnt = take(L.gcnt_bytes);
   }
   L.logits_t = take(sizeof(float) * (R > (size_t)B ? R : B) * d.Vc);

@@ -147,9 +147,9 @@ struct ArgmaxArgs {
   int32_t q_prefill;
 };
 
-// Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 128 rows (two 64-row halves),
+// Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 128 rows (64-row blocks),
 // bf16, q8 or q4 weights with bf16 operands.  Tiles of 32 output columns (gated:
-// 32 gate + 32 up rows) x all rows x 256-wide K slices; the last workgroup of
+// 32 gate + 32 up rows) x 64 rows x 256-wide K slices; the last workgroup of
 // a tile to finish sums the K slices' partials in order and applies the
 // epilogue.
 struct GemmArgs {

@@ -780,7 +780,7 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
 
 // ------------------------------------------------------------------ batched projections (MFMA)
 //
-// y[M][N] = epi(x~ . W^T) for M <= 128 rows (in 64-row halves): x~ = bf16(x * rinv * gain) (or
+// y[M][N] = epi(x~ . W^T) for M <= 128 rows (two 64-row blocks): x~ = bf16(x * rinv * gain) (or
 // bf16(x)); weight rows in their storage format (bf16, or q8 / q4 codes
 // converted exactly to bf16 with the 32-wide block scale applied to each
 // block's product).
@@ -858,10 +858,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float *p) {
 }
 constexpr int CPOL_SC1 = 16;
 
-// MH: 64-row halves of the activation rows (1: up to 64 rows; 2: up to 128,
-// the second half staged and multiplied after the first with the same
-// weights, which stay in registers).
-template <int WT, int EPI, int MH>
+// Grid z: 64-row blocks of the activation rows, each its own workgroups (the
+// blocks of one tile read the same weights; their ids differ by a multiple of
+// 8, so they run on one XCD and share its L2).
+template <int WT, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // The tile's weight rows form NSUB blocks of 16; each block's K slice is
   // split over WPB waves, so every wave owns SPW 32-wide steps of one block
@@ -880,7 +880,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tn = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
   const int M = a.M, K = a.K, N = a.N;
-  const int M0 = M < 64 ? M : 64;  // rows of the first half
+  const int mb = 64 * blockIdx.z;                // first row of this block
+  const int M0 = M - mb < 64 ? M - mb : 64;      // its rows
   const int MT = (M0 + 15) / 16;
   const int k0 = ks * GBK;
   const int NP = EPI == EPI_GATED ? 2 * N : N;  // partial columns (gated: gate then up)
@@ -897,7 +898,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // used: a load under a branch makes the compiler wait for it at the join.
   const int sm = tid >> 2, sq4 = tid & 3;
   const bool norm_row = a.gain && sm < M0;
-  const float *ssp = a.gain ? a.ssq + (size_t)min(sm, M0 - 1) * a.ssq_stride : a.x;
+  const float *ssp = a.gain ? a.ssq + (size_t)(mb + min(sm, M0 - 1)) * a.ssq_stride : a.x;
   float sqv[8];  // slots sq4 + 4 i, i < 8 (hidden widths up to 1024; wider rows add a loop)
 #pragma unroll
   for (int i = 0; i < 8; ++i) sqv[i] = ssp[min(sq4 + 4 * i, K / 32 - 1)];
@@ -912,7 +913,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   for (int it = 0; it < IT; ++it) {
     const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
     if (it * 256 >= MT * 16 * (GBK / 8)) break;  // rows past the last 16-row block
-    const float *xr = a.x + (size_t)min(m, M0 - 1) * a.x_stride + k0 + 8 * c;
+    const float *xr = a.x + (size_t)(mb + min(m, M0 - 1)) * a.x_stride + k0 + 8 * c;
     xv[it][0] = *(const float4 *)xr;
     xv[it][1] = *(const float4 *)(xr + 4);
   }
@@ -977,7 +978,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         for (int i = 0; i < 8; ++i) v[i] = v[i] * r * gs[8 * c + i];
         if (a.normed_out && tn == 0)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a.normed_out[(size_t)m * K + k0 + 8 * c + i] = v[i];
+          for (int i = 0; i < 8; ++i) a.normed_out[(size_t)(mb + m) * K + k0 + 8 * c + i] = v[i];
       }
       o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
       o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
@@ -1034,118 +1035,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       const int m = mt * 16 + (lane & 15);
       if (mt < MT && m < M0 && nj < N)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc[mt]), prs,
-                                               (int)((((size_t)ks * M + m) * NP + (mat ? N : 0) + nj) * 4), 0,
+                                               (int)((((size_t)ks * M + mb + m) * NP + (mat ? N : 0) + nj) * 4), 0,
                                                CPOL_SC1);
-    }
-  }
-  if constexpr (MH == 2) {
-    if (M > 64) {
-      // rows 64 .. M-1: their sums of squares and operand slice, then the
-      // same steps as above through the weights still in registers
-      const int M1 = M - 64, MT1 = (M1 + 15) / 16;
-      const bool norm_row1 = a.gain && sm < M1;
-      const float *ssp1 = a.gain ? a.ssq + (size_t)(64 + min(sm, M1 - 1)) * a.ssq_stride : a.x;
-      float sqv1[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sqv1[i] = ssp1[min(sq4 + 4 * i, K / 32 - 1)];
-      float4 xv1[IT][2];
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
-        if (it * 256 >= MT1 * 16 * (GBK / 8)) break;
-        const float *xr = a.x + (size_t)(64 + min(m, M1 - 1)) * a.x_stride + k0 + 8 * c;
-        xv1[it][0] = *(const float4 *)xr;
-        xv1[it][1] = *(const float4 *)(xr + 4);
-      }
-      float sq1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sq1 += norm_row1 && sq4 + 4 * i < K / 32 ? sqv1[i] : 0.f;
-      if (norm_row1)
-        for (int i = sq4 + 32; i < K / 32; i += 4) sq1 += ssp1[i];
-      sq1 += __shfl_xor(sq1, 1, 64);
-      sq1 += __shfl_xor(sq1, 2, 64);
-      __syncthreads();  // every wave is done with the first half's xs, rinv and red
-      if (sq4 == 0) rinv[sm] = a.gain ? 1.0f / sqrtf(sq1 / (float)K + a.eps) : 1.f;
-      __syncthreads();
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
-        if (m >= MT1 * 16) break;
-        float v[8] = {xv1[it][0].x, xv1[it][0].y, xv1[it][0].z, xv1[it][0].w,
-                      xv1[it][1].x, xv1[it][1].y, xv1[it][1].z, xv1[it][1].w};
-        uint4 o = make_uint4(0u, 0u, 0u, 0u);
-        if (m < M1) {
-          if (a.gain) {
-            const float r = rinv[m];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = v[i] * r * gs[8 * c + i];
-            if (a.normed_out && tn == 0)
-#pragma unroll
-              for (int i = 0; i < 8; ++i) a.normed_out[(size_t)(64 + m) * K + k0 + 8 * c + i] = v[i];
-          }
-          o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-          o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
-          o.z = (uint32_t)bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
-          o.w = (uint32_t)bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
-        }
-        *(uint4 *)&xs[m * GXS + 8 * c] = o;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < SPW; ++s) {
-        const int kl = (kq * SPW + s) * 32;
-        const bf16x8_t av = gemm_w_bf16<WT>(wv[s]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          if (mt >= MT1) break;
-          const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + kl + (lane >> 4) * 8];
-          const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bx);
-          if constexpr (WT == W_BF16) {
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mt], 0, 0, 0);
-          } else {
-            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero, 0, 0, 0);
-            const float *sr = &scl[(nb * 16 + (lane >> 4) * 4) * NBLK + kl / 32];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[mt][j] += t[j] * sr[j * NBLK];
-          }
-        }
-      }
-      if constexpr (WPB > 1) {
-        if (kq > 0)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            if (mt < MT1) red[((nb * (WPB - 1) + kq - 1) * 4 + mt) * 64 + lane] = acc[mt];
-        __syncthreads();
-        if (kq == 0)
-#pragma unroll
-          for (int q = 1; q < WPB; ++q)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              if (mt < MT1) acc[mt] += red[((nb * (WPB - 1) + q - 1) * 4 + mt) * 64 + lane];
-      }
-      // row 64 + m
-      if (kq == 0) {
-        const int nj = nrow0 + (lane >> 4) * 4;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int m = mt * 16 + (lane & 15);
-          if (mt < MT1 && m < M1 && nj < N)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, acc[mt]), prs,
-                                                   (int)((((size_t)ks * M + 64 + m) * NP + (mat ? N : 0) + nj) * 4), 0,
-                                                   CPOL_SC1);
-        }
-      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.cnt + tn, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t *cn = a.cnt + blockIdx.z * gridDim.x + tn;
+    const uint32_t old = __hip_atomic_fetch_add(cn, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = old == (uint32_t)(KS - 1);
-    if (last) __hip_atomic_store(a.cnt + tn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) __hip_atomic_store(cn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!last) return;
@@ -1154,78 +1054,72 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // thread t covers row t / 4, columns (t % 4) * 8 .. + 8 of the tile.  The
   // residual row and every slice of a group (all of them for K <= 3072) are
   // requested before the first sum, so the epilogue waits for one round trip.
-  for (int h = 0; h < MH; ++h) {  // 64-row halves
-  const int m = h * 64 + (tid >> 2), c0 = (tid & 3) * 8;
-  const int nb0 = tn * GT + c0;
-  sq = 0.f;
-  if (m < M && nb0 < N) {
-    float *yr = a.y + (size_t)m * a.y_stride + nb0;
-    float yv[8];
-    if constexpr (EPI == EPI_RESID)
+  {  // this block's rows
+    const int m = mb + (tid >> 2), c0 = (tid & 3) * 8;
+    const int nb0 = tn * GT + c0;
+    sq = 0.f;
+    if (m < M && nb0 < N) {
+      float *yr = a.y + (size_t)m * a.y_stride + nb0;
+      float yv[8];
+      if constexpr (EPI == EPI_RESID)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) yv[i] = yr[i];
-    float g8[8], u8[8];
+        for (int i = 0; i < 8; ++i) yv[i] = yr[i];
+      float g8[8], u8[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g8[i] = u8[i] = 0.f;
-    constexpr int QG = EPI == EPI_GATED ? 6 : 12;  // slices per group
-    for (int q0 = 0; q0 < KS; q0 += QG) {
-      f32x4v_t lg[QG][2], lu[EPI == EPI_GATED ? QG : 1][2];
+      for (int i = 0; i < 8; ++i) g8[i] = u8[i] = 0.f;
+      constexpr int QG = EPI == EPI_GATED ? 6 : 12;  // slices per group
+      for (int q0 = 0; q0 < KS; q0 += QG) {
+        f32x4v_t lg[QG][2], lu[EPI == EPI_GATED ? QG : 1][2];
 #pragma unroll
-      for (int qq = 0; qq < QG; ++qq)
-        if (q0 + qq < KS) {
-          const int off = (int)((((size_t)(q0 + qq) * M + m) * NP + nb0) * 4);
-          lg[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, CPOL_SC1));
-          lg[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16, 0, CPOL_SC1));
-          if constexpr (EPI == EPI_GATED) {
-            lu[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4, 0, CPOL_SC1));
-            lu[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4 + 16, 0, CPOL_SC1));
+        for (int qq = 0; qq < QG; ++qq)
+          if (q0 + qq < KS) {
+            const int off = (int)((((size_t)(q0 + qq) * M + m) * NP + nb0) * 4);
+            lg[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, CPOL_SC1));
+            lg[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16, 0, CPOL_SC1));
+            if constexpr (EPI == EPI_GATED) {
+              lu[qq][0] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4, 0, CPOL_SC1));
+              lu[qq][1] = __builtin_bit_cast(f32x4v_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off + N * 4 + 16, 0, CPOL_SC1));
+            }
           }
+#pragma unroll
+        for (int qq = 0; qq < QG; ++qq)
+          if (q0 + qq < KS)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              g8[i] += lg[qq][i >> 2][i & 3];
+              if constexpr (EPI == EPI_GATED) u8[i] += lu[qq][i >> 2][i & 3];
+            }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = nb0 + i;
+        const float g = g8[i], u = u8[i];
+        if constexpr (EPI == EPI_STORE) {
+          yr[i] = g;
+        } else if constexpr (EPI == EPI_RESID) {
+          const float v = yv[i] + g;
+          yr[i] = v;
+          if (a.copy_out) a.copy_out[(size_t)m * a.copy_stride + n] = v;
+          sq += v * v;
+        } else {
+          yr[i] = silu(g) * u;
         }
-#pragma unroll
-      for (int qq = 0; qq < QG; ++qq)
-        if (q0 + qq < KS)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            g8[i] += lg[qq][i >> 2][i & 3];
-            if constexpr (EPI == EPI_GATED) u8[i] += lu[qq][i >> 2][i & 3];
-          }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = nb0 + i;
-      const float g = g8[i], u = u8[i];
-      if constexpr (EPI == EPI_STORE) {
-        yr[i] = g;
-      } else if constexpr (EPI == EPI_RESID) {
-        const float v = yv[i] + g;
-        yr[i] = v;
-        if (a.copy_out) a.copy_out[(size_t)m * a.copy_stride + n] = v;
-        sq += v * v;
-      } else {
-        yr[i] = silu(g) * u;
       }
     }
-  }
-  if (EPI == EPI_RESID && a.ssq_out) {
-    sq += __shfl_xor(sq, 1, 64);
-    sq += __shfl_xor(sq, 2, 64);
-    if ((tid & 3) == 0 && m < M) a.ssq_out[(size_t)m * (N / 32) + tn] = sq;
-  }
+    if (EPI == EPI_RESID && a.ssq_out) {
+      sq += __shfl_xor(sq, 1, 64);
+      sq += __shfl_xor(sq, 2, 64);
+      if ((tid & 3) == 0 && m < M) a.ssq_out[(size_t)m * (N / 32) + tn] = sq;
+    }
   }
 }
 
 template <int WT>
 static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
-  const dim3 grid((a.N + GT - 1) / GT, a.K / GBK);
-  if (a.M <= 64) {
-    if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE, 1>), grid, dim3(256), 0, s, a);
-    else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED, 1>), grid, dim3(256), 0, s, a);
-  } else {
-    if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE, 2>), grid, dim3(256), 0, s, a);
-    else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED, 2>), grid, dim3(256), 0, s, a);
-  }
+  const dim3 grid((a.N + GT - 1) / GT, a.K / GBK, (a.M + 63) / 64);
+  if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE>), grid, dim3(256), 0, s, a);
+  else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -451,7 +451,7 @@ def test_reduced_bf16_full_width_parity():
     m = _reduced(synth.BIG)
     w = synth.make_weights(m)
     # a 358-row prompt: prefill chunks of 128, 128 and 102 rows (the GEMM's
-    # two 64-row halves, the second one ragged at 38 rows), 2 attention tiles
+    # two 64-row blocks, the second one ragged at 38 rows), 2 attention tiles
     wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=358)
     say("[reduced bf16] prompt 358, 6 frames")
     _check(_forced_run(m, w, wl, 6, dump_hidden=True), m, "reduced_bf16")
