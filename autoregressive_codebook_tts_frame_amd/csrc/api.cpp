@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -25,6 +26,7 @@ namespace {
 thread_local std::string g_err;
 
 constexpr int kPrefillChunk = 128;  // prompt rows per prefill step (the batched GEMM takes up to 128)
+constexpr int kPfMinRows = 16;      // smallest token bucket of a prompt chunk
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
@@ -40,6 +42,7 @@ struct Layout {
   size_t ssq, gpart, gcnt;  // batched projections: row sums of squares, split-K partials, tile counters
   size_t gcnt_bytes;
   size_t x0_dump, hidden_dump, gather_dump, tpos_dump, pf_codes, pf_text;
+  size_t pf_desc, pf_xh, pf_lg, pf_br;  // prompt chunks: descriptor, head rows, logits, bridge rows
   // persistent frame kernel: weight tables, tagged exchange words, error flag
   size_t f_tl, f_pl, f_heads, f_heads_sc, f_xq, f_qkv, f_o, f_z, f_amax, f_lgx, f_part, f_err, f_trace;
   size_t xch_words;  // words between copies of the exchange rows
@@ -104,8 +107,14 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.hidden_dump = take(sizeof(float) * (size_t)d.Lt * B * d.H);
   L.gather_dump = take(sizeof(int32_t) * B * (d.G + 1));
   L.tpos_dump = take(sizeof(int32_t) * B);
-  L.pf_codes = take(sizeof(int32_t) * (size_t)d.P * d.G);
-  L.pf_text = take(sizeof(int32_t) * (size_t)d.P);
+  // a call's padded chunk ids: at most PF_MAXROWS streams x (P + one chunk)
+  const size_t pf_rows = (size_t)qtk::PF_MAXROWS * (d.P + kPrefillChunk);
+  L.pf_codes = take(sizeof(int32_t) * pf_rows * d.G);
+  L.pf_text = take(sizeof(int32_t) * pf_rows);
+  L.pf_desc = take(sizeof(int32_t) * qtk::PF_WORDS);
+  L.pf_xh = take(sizeof(float) * qtk::PF_MAXROWS * d.H);
+  L.pf_lg = take(sizeof(float) * qtk::PF_MAXROWS * d.Vc);
+  L.pf_br = take(sizeof(float) * qtk::PF_MAXROWS * d.H);
   L.ptab = take(sizeof(int32_t) * (size_t)B * d.P);
   L.f_tl = take(sizeof(qtk::LayerDev) * d.Lt);
   L.f_pl = take(sizeof(qtk::LayerDev) * d.Lp);
@@ -188,6 +197,9 @@ struct qt_ctx {
   int32_t *pin_up = nullptr, *pin_down = nullptr;
   size_t pin_up_elems = 0, pin_down_elems = 0;
   size_t pu_ctl = 0, pu_overlay = 0, pu_forced = 0, pu_pf_text = 0, pu_pf_codes = 0, pu_scalar = 0;
+  size_t pu_pf_desc = 0;  // one descriptor per prompt chunk of a call
+  // prompt-chunk graphs by (streams, rows per stream, attention tiles, codes, head)
+  std::map<uint32_t, std::pair<hipGraph_t, hipGraphExec_t>> pf_graphs;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   // adaptive K: a 1-frame graph for the frames of a call past its last
@@ -395,9 +407,10 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
 
   // 2. q/k norm + RoPE + K/V rows into the ring at the row's position: the
   // attention tile's prologue for the predictor's decode steps (one tile per
-  // row, latency-bound); a kernel of its own for prefill chunks and for the
-  // talker, whose long tiles stream K/V at a higher occupancy without it
-  const bool fused = rows.rows_per_slot <= 2 && st.max_tiles == 1;
+  // row, latency-bound); a kernel of its own for prefill chunks, for the
+  // talker, whose long tiles stream K/V at a higher occupancy without it, and
+  // for a paged ring (the fused prologue writes the dense cache only)
+  const bool fused = rows.rows_per_slot <= 2 && st.max_tiles == 1 && !st.ptab;
   if (!fused) {
     QkArgs qa = {};
     qa.qkv = qkv; qa.M = M; qa.rows = rows; qa.nq = d.nq; qa.nkv = d.nkv;
@@ -530,6 +543,70 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
   return launch_argmax(am, s);
 }
 
+// ----------------------------------------------------------------- prompt chunks
+//
+// A prompt is prefilled in chunks of up to 128 rows ([QT-log] per-layer K/V
+// ring entry: the prefill writes positions [0, T)).  One call takes 1-4
+// streams ([MC-opt] round-18 table, talker chunk-prefill graphs: a graph per
+// row count and token bucket): each chunk holds the same t positions
+// [r0, r0 + t) of every stream whose prompt is still going, t a token bucket
+// (16, 32, 64 or 128, at most 128 rows in all), a shorter prompt's rows past
+// its end being padding that reaches neither the ring nor the result.  The
+// chunk's ids, slots and positions live in a device descriptor, so one
+// captured graph per (streams, t, attention tiles, codes given, head)
+// serves every chunk of that shape; the chunk in which a stream's prompt
+// ends also runs the head and decides the stream's first code (c0).
+
+struct PfShape {
+  int n, t, r0, tiles;  // r0: the chunk start the capture sizes the attention grid from
+  bool codes, head;
+  uint32_t key() const {
+    return (uint32_t)n | (uint32_t)t << 3 | (uint32_t)tiles << 11 | (uint32_t)codes << 24 | (uint32_t)head << 25;
+  }
+};
+
+hipError_t enqueue_pf_chunk(qt_ctx *c, const PfShape &sh) {
+  const Dims &d = c->d;
+  const qt_model_desc &md = c->md;
+  hipStream_t s = c->stream;
+  const int32_t *pf = c->A<int32_t>(c->L.pf_desc);
+  float *x = c->A<float>(c->L.x);
+  const int M = sh.n * sh.t;
+  hipError_t e;
+  // gather-sum of the chunk's rows ([QT-log] AR inputs entry); the ids start
+  // at the descriptor's PF_IDOFF row
+  GatherArgs ga = {};
+  ga.code_emb = c->code_emb; ga.text_emb = c->text_emb; ga.tab_bf16 = md.tab_bf16;
+  ga.H = d.H; ga.Vc = d.Vc; ga.G = d.G;
+  ga.codes = sh.codes ? c->A<int32_t>(c->L.pf_codes) : nullptr; ga.codes_stride = d.G;
+  ga.text = c->A<int32_t>(c->L.pf_text); ga.text_stride = 1;
+  ga.ctl = pf; ga.frame_stride_codes = d.G; ga.frame_stride_text = 1;
+  ga.x = x; ga.M = M; ga.ssq = c->A<float>(c->L.ssq);
+  if ((e = launch_gather(ga, s)) != hipSuccess) return e;
+  const Stack ts = talker_stack(c);
+  RowMap rows{0, sh.t, sh.r0, nullptr};
+  rows.pf = pf;
+  for (int l = 0; l < d.Lt; ++l)
+    if ((e = enqueue_layer(c, ts, l, M, rows, nullptr)) != hipSuccess) return e;
+  if (!sh.head) return hipSuccess;
+  // final norm -> bridge, head, first code of the streams whose prompt ends here
+  float *xh = c->A<float>(c->L.pf_xh);
+  if ((e = launch_pf_rows(pf, x, xh, sh.n, d.H, s)) != hipSuccess) return e;
+  GemvArgs h = {};
+  h.seg[0] = lin(c->t_head); h.nseg = 1; h.seg_end[0] = d.Vc;
+  h.N = d.Vc; h.K = d.H; h.x = xh; h.x_stride = d.H; h.M = sh.n;
+  h.gain = c->t_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
+  h.normed_out = c->A<float>(c->L.pf_br);
+  h.y = c->A<float>(c->L.pf_lg); h.y_stride = d.Vc;
+  if ((e = launch_gemv(wtype_of(md), EPI_STORE, h, s)) != hipSuccess) return e;
+  ArgmaxArgs am = {};
+  am.logits = h.y; am.Vc = d.Vc; am.M = sh.n; am.mode = AM_PREFILL; am.ctl = pf;
+  am.c0_state = c->A<int32_t>(c->L.c0); am.pos = c->A<int32_t>(c->L.pos);
+  am.bridge_src = h.normed_out; am.bridge = c->A<float>(c->L.bridge); am.H = d.H;
+  am.logits_out = c->A<float>(c->L.logits_t);
+  return launch_argmax(am, s);
+}
+
 // kf frames (a replay of the K-frame graph, or the 1-frame one)
 hipError_t enqueue_replay(qt_ctx *c, int kf) {
   hipError_t e;
@@ -547,6 +624,8 @@ const char *frame_unsupported(const qt_model_desc &m, int B) {
   return nullptr;
 }
 
+int32_t prefill_rows(qt_ctx *c, int32_t n, const int32_t *slots, const int32_t *lens, const int32_t *codes,
+                     const int32_t *text_ids);
 int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
                       const int32_t *forced, bool static_scratch);
 int32_t decode_entry(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out, const int32_t *forced,
@@ -614,6 +693,10 @@ void qt_free(qt_ctx *c) {
   if (c->graph) (void)hipGraphDestroy(c->graph);
   if (c->exec1) (void)hipGraphExecDestroy(c->exec1);
   if (c->graph1) (void)hipGraphDestroy(c->graph1);
+  for (auto &kv : c->pf_graphs) {
+    (void)hipGraphExecDestroy(kv.second.second);
+    (void)hipGraphDestroy(kv.second.first);
+  }
   if (c->pin_up) (void)hipHostFree(c->pin_up);
   if (c->pin_down) (void)hipHostFree(c->pin_down);
   delete c;
@@ -705,11 +788,14 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out) {
   c->pu_ctl = 0;
   c->pu_overlay = 16;
   c->pu_forced = c->pu_overlay + (size_t)c->maxF * c->B;
+  const size_t pf_rows = (size_t)qtk::PF_MAXROWS * (d.P + kPrefillChunk);
   c->pu_pf_text = c->pu_forced + (size_t)c->maxF * c->B * d.G;
-  c->pu_pf_codes = c->pu_pf_text + (size_t)d.P;
-  c->pu_scalar = c->pu_pf_codes + (size_t)d.P * d.G;
-  c->pu_ptab = c->pu_scalar + 16;  // paged: new table entries (a prefill's P, or maxF per slot per chunk)
-  c->pin_up_elems = c->pu_ptab + std::max((size_t)d.P, (size_t)c->maxF * c->B);
+  c->pu_pf_codes = c->pu_pf_text + pf_rows;
+  c->pu_pf_desc = c->pu_pf_codes + pf_rows * d.G;
+  c->pu_scalar = c->pu_pf_desc + (size_t)(d.P / kPfMinRows + 2) * qtk::PF_WORDS;
+  // paged: new table entries (a prefill's streams' P each, or maxF per slot per decode chunk)
+  c->pu_ptab = c->pu_scalar + 16;
+  c->pin_up_elems = c->pu_ptab + std::max((size_t)qtk::PF_MAXROWS * d.P, (size_t)c->maxF * c->B);
   c->pin_down_elems = (size_t)c->maxF * c->B * d.G;
   if (hipHostMalloc((void **)&c->pin_up, c->pin_up_elems * 4, hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void **)&c->pin_down, c->pin_down_elems * 4, hipHostMallocDefault) != hipSuccess)
@@ -804,8 +890,8 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out) {
   }
   if (c->path == QT_PATH_GRAPH) {
     // the K-frame graph, and for K > 1 a 1-frame one (the tail of a call)
-    for (const int kf : {c->K, 1}) {
-      if (kf == 1 && c->K == 1) break;
+    for (int gi = 0; gi < (c->K > 1 ? 2 : 1); ++gi) {
+      const int kf = gi == 0 ? c->K : 1;
       hipGraph_t &g = kf == c->K ? c->graph : c->graph1;
       hipGraphExec_t &x = kf == c->K ? c->exec : c->exec1;
       hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
@@ -823,69 +909,12 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out) {
 }
 
 int32_t qt_prefill(qt_ctx *c, int32_t slot, int32_t T, const int32_t *codes, const int32_t *text_ids) {
-  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
-  const Dims &d = c->d;
-  const qt_model_desc &md = c->md;
-  if (slot < 0 || slot >= c->B) return fail(c, QT_E_ARG, "slot %d outside [0, %d)", slot, c->B);
-  if (T <= 0 || !text_ids) return fail(c, QT_E_ARG, "T must be positive and text_ids non-NULL");
-  if (T > d.P) return fail(c, QT_E_CONTEXT_FULL, "prompt of %d rows exceeds %d ring positions", T, d.P);
-  if (!ids_ok(text_ids, T, d.Vt)) return fail(c, QT_E_RANGE, "text id outside [0, %d)", d.Vt);
-  if (codes && !ids_ok(codes, (size_t)T * d.G, d.Vc)) return fail(c, QT_E_RANGE, "code id outside [0, %d)", d.Vc);
-  if (c->pool_rows && c->free_rows.size() + c->slot_rows[slot].size() < (size_t)T)
-    return fail(c, QT_E_CONTEXT_FULL, "paged ring: %zu free rows, the prompt needs %d", c->free_rows.size() + c->slot_rows[slot].size(), T);
+  return prefill_rows(c, 1, &slot, &T, codes, text_ids);
+}
 
-  hipStream_t s = c->stream;
-  // from the first launch on the slot's ring rows change: it counts as
-  // prefilled again only once the whole prompt has run
-  c->ready[slot] = 0;
-  int32_t *pf_codes = c->A<int32_t>(c->L.pf_codes), *pf_text = c->A<int32_t>(c->L.pf_text);
-  int32_t *up_text = c->pin_up + c->pu_pf_text, *up_codes = c->pin_up + c->pu_pf_codes;
-  memcpy(up_text, text_ids, sizeof(int32_t) * T);
-  if (codes) memcpy(up_codes, codes, sizeof(int32_t) * T * d.G);
-  HIPCHK(c, hipMemcpyAsync(pf_text, up_text, sizeof(int32_t) * T, hipMemcpyHostToDevice, s));
-  if (codes) HIPCHK(c, hipMemcpyAsync(pf_codes, up_codes, sizeof(int32_t) * T * d.G, hipMemcpyHostToDevice, s));
-  if (c->pool_rows) {  // the slot's rows back to the pool, then T rows for the prompt
-    release_slot(c, slot);
-    HIPCHK(c, grow_slot(c, slot, T, c->pin_up + c->pu_ptab));
-  }
-
-  const int wt = wtype_of(md);
-  float *x = c->A<float>(c->L.x);
-  const Stack ts = talker_stack(c);
-  for (int r0 = 0; r0 < T; r0 += kPrefillChunk) {
-    const int M = T - r0 < kPrefillChunk ? T - r0 : kPrefillChunk;
-    GatherArgs ga = {};
-    ga.code_emb = c->code_emb; ga.text_emb = c->text_emb; ga.tab_bf16 = md.tab_bf16;
-    ga.H = d.H; ga.Vc = d.Vc; ga.G = d.G;
-    ga.codes = codes ? pf_codes + (size_t)r0 * d.G : nullptr; ga.codes_stride = d.G;
-    ga.text = pf_text + r0; ga.text_stride = 1; ga.x = x; ga.M = M;
-    ga.ssq = c->A<float>(c->L.ssq);
-    HIPCHK(c, launch_gather(ga, s));
-    // rows of one slot at positions r0 .. r0+M-1, causal through the mask
-    const RowMap rows{slot, M, r0, nullptr};
-    for (int l = 0; l < d.Lt; ++l) HIPCHK(c, enqueue_layer(c, ts, l, M, rows, nullptr));
-    if (r0 + M == T) {
-      GemvArgs h = {};
-      h.seg[0] = lin(c->t_head); h.nseg = 1; h.seg_end[0] = d.Vc;
-      h.N = d.Vc; h.K = d.H; h.x = x + (size_t)(M - 1) * d.H; h.x_stride = d.H; h.M = 1;
-      h.gain = c->t_norm; h.gain_bf16 = md.tab_bf16; h.eps = (float)md.eps; h.act_bf16 = md.act_bf16;
-      h.normed_out = c->A<float>(c->L.bridge) + (size_t)slot * d.H;
-      h.y = c->A<float>(c->L.logits_t) + (size_t)slot * d.Vc; h.y_stride = d.Vc;
-      HIPCHK(c, launch_gemv(wt, EPI_STORE, h, s));
-      ArgmaxArgs am = {};
-      am.logits = h.y; am.Vc = d.Vc; am.M = 1; am.mode = AM_PREFILL; am.slot = slot;
-      am.c0_state = c->A<int32_t>(c->L.c0);
-      am.inv_temp = c->inv_temp; am.seed = c->seed; am.top_k = c->top_k; am.q_prefill = T;
-      HIPCHK(c, launch_argmax(am, s));
-    }
-  }
-  int32_t *up_pos = c->pin_up + c->pu_scalar;
-  up_pos[0] = T;
-  HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.pos) + slot, up_pos, sizeof(int32_t), hipMemcpyHostToDevice, s));
-  HIPCHK(c, hipStreamSynchronize(s));
-  c->pos_host[slot] = T;
-  c->ready[slot] = 1;
-  return QT_OK;
+int32_t qt_prefill_rows(qt_ctx *c, int32_t n, const int32_t *slots, const int32_t *lengths, const int32_t *codes,
+                        const int32_t *text_ids) {
+  return prefill_rows(c, n, slots, lengths, codes, text_ids);
 }
 
 int32_t qt_decode_frame(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,
@@ -934,6 +963,145 @@ int32_t decode_entry(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *
     // bridge, position), so they must be restored before the next decode
     for (int b = 0; b < B; ++b) c->ready[b] = 0;
   return rc;
+}
+
+int32_t prefill_rows(qt_ctx *c, int32_t n, const int32_t *slots, const int32_t *lens, const int32_t *codes,
+                     const int32_t *text_ids) {
+  if (!c) return fail(nullptr, QT_E_ARG, "NULL context");
+  const Dims &d = c->d;
+  if (n < 1 || n > PF_MAXROWS) return fail(c, QT_E_ARG, "streams per prefill call %d outside [1, %d]", n, PF_MAXROWS);
+  if (!slots || !lens || !text_ids) return fail(c, QT_E_ARG, "NULL slots, lengths or text_ids");
+  size_t total = 0, held = 0;
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= c->B) return fail(c, QT_E_ARG, "slot %d outside [0, %d)", slots[i], c->B);
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == slots[i]) return fail(c, QT_E_ARG, "slot %d given twice", slots[i]);
+    if (lens[i] <= 0) return fail(c, QT_E_ARG, "prompt length %d must be positive", lens[i]);
+    if (lens[i] > d.P) return fail(c, QT_E_CONTEXT_FULL, "prompt of %d rows exceeds %d ring positions", lens[i], d.P);
+    total += (size_t)lens[i];
+    if (c->pool_rows) held += c->slot_rows[slots[i]].size();
+  }
+  if (!ids_ok(text_ids, total, d.Vt)) return fail(c, QT_E_RANGE, "text id outside [0, %d)", d.Vt);
+  if (codes && !ids_ok(codes, total * d.G, d.Vc)) return fail(c, QT_E_RANGE, "code id outside [0, %d)", d.Vc);
+  if (c->pool_rows && c->free_rows.size() + held < total)
+    return fail(c, QT_E_CONTEXT_FULL, "paged ring: %zu free rows, the prompts need %zu", c->free_rows.size() + held, total);
+
+  // the chunks: positions [r0, r0 + t) of every stream still going
+  struct Chunk {
+    PfShape sh;
+    int idoff, src[PF_MAXROWS], len[PF_MAXROWS], head[PF_MAXROWS];
+  };
+  std::vector<Chunk> plan;
+  std::vector<size_t> first(n);  // each stream's first id row in text_ids
+  for (int i = 0, acc = 0; i < n; acc += lens[i], ++i) first[i] = (size_t)acc;
+  {
+    std::vector<int> act(n);
+    for (int i = 0; i < n; ++i) act[i] = i;
+    int r0 = 0, idoff = 0;
+    while (!act.empty()) {
+      const int na = (int)act.size();
+      int cap = kPrefillChunk;  // rows per stream so that na of them fit one chunk
+      while (cap * na > kPrefillChunk) cap /= 2;
+      int rem = 0;
+      for (int i : act) rem = std::max(rem, lens[i] - r0);
+      int t = kPfMinRows;
+      while (t < rem && t < cap) t *= 2;
+      if (r0 + t > d.P) t = d.P - r0;  // the ring's last positions
+      Chunk ch = {};
+      ch.sh.n = na; ch.sh.t = t; ch.sh.r0 = r0;
+      ch.sh.tiles = std::min(c->L.max_tiles, (r0 + t - 1) / kTile + 1);
+      ch.sh.codes = codes != nullptr;
+      ch.idoff = idoff;
+      for (int k = 0; k < na; ++k) {
+        const int i = act[k];
+        ch.src[k] = i;
+        ch.len[k] = std::min(t, lens[i] - r0);
+        ch.head[k] = lens[i] <= r0 + t ? k * t + ch.len[k] - 1 : -1;
+        ch.sh.head = ch.sh.head || ch.head[k] >= 0;
+      }
+      plan.push_back(ch);
+      idoff += na * t;
+      r0 += t;
+      act.erase(std::remove_if(act.begin(), act.end(), [&](int i) { return lens[i] <= r0; }), act.end());
+    }
+  }
+
+  hipStream_t s = c->stream;
+  const bool eager = c->flags & QT_F_EAGER;
+  // every shape's graph is captured before this call's first copy, on the
+  // idle stream (each earlier call ended with a synchronize)
+  if (!eager)
+    for (const Chunk &ch : plan) {
+      if (c->pf_graphs.count(ch.sh.key())) continue;
+      hipGraph_t g = nullptr;
+      hipGraphExec_t x = nullptr;
+      HIPCHK(c, hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed));
+      const hipError_t eq = enqueue_pf_chunk(c, ch.sh);
+      const hipError_t ec = hipStreamEndCapture(s, &g);
+      if (eq != hipSuccess || ec != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return fail(c, QT_E_HIP, "prompt chunk capture: %s", hipGetErrorString(eq != hipSuccess ? eq : ec));
+      }
+      const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+      if (ei != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return fail(c, QT_E_HIP, "hipGraphInstantiate: %s", hipGetErrorString(ei));
+      }
+      c->pf_graphs[ch.sh.key()] = {g, x};
+    }
+
+  // from the first copy on the slots' ring rows change: they count as
+  // prefilled again only once every chunk has run
+  for (int i = 0; i < n; ++i) c->ready[slots[i]] = 0;
+  // padded ids of every chunk, one upload
+  int32_t *up_text = c->pin_up + c->pu_pf_text, *up_codes = c->pin_up + c->pu_pf_codes;
+  size_t rows_total = 0;
+  for (const Chunk &ch : plan) {
+    for (int k = 0; k < ch.sh.n; ++k)
+      for (int j = 0; j < ch.sh.t; ++j) {
+        const size_t row = (size_t)ch.idoff + (size_t)k * ch.sh.t + j;
+        const bool on = j < ch.len[k];
+        const size_t src = first[ch.src[k]] + (size_t)(ch.sh.r0 + j);
+        up_text[row] = on ? text_ids[src] : 0;
+        if (codes)
+          for (int g = 0; g < d.G; ++g) up_codes[row * d.G + g] = on ? codes[src * d.G + g] : 0;
+      }
+    rows_total = (size_t)ch.idoff + (size_t)ch.sh.n * ch.sh.t;
+  }
+  HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.pf_text), up_text, sizeof(int32_t) * rows_total, hipMemcpyHostToDevice, s));
+  if (codes)
+    HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.pf_codes), up_codes, sizeof(int32_t) * rows_total * d.G,
+                             hipMemcpyHostToDevice, s));
+  if (c->pool_rows) {  // the slots' rows back to the pool, then rows for their prompts
+    for (int i = 0; i < n; ++i) release_slot(c, slots[i]);
+    for (int i = 0; i < n; ++i) HIPCHK(c, grow_slot(c, slots[i], lens[i], c->pin_up + c->pu_ptab + (size_t)i * d.P));
+  }
+  for (size_t ci = 0; ci < plan.size(); ++ci) {
+    const Chunk &ch = plan[ci];
+    int32_t *w = c->pin_up + c->pu_pf_desc + ci * PF_WORDS;
+    memset(w, 0, sizeof(int32_t) * PF_WORDS);
+    w[PF_IDOFF] = ch.idoff;
+    w[PF_R0] = ch.sh.r0;
+    memcpy(&w[PF_ITEMP], &c->inv_temp, sizeof(float));
+    w[PF_SEED_LO] = (int32_t)(uint32_t)c->seed;
+    w[PF_SEED_HI] = (int32_t)(uint32_t)(c->seed >> 32);
+    w[PF_TOPK] = c->top_k;
+    for (int k = 0; k < ch.sh.n; ++k) {
+      w[PF_SLOT + k] = slots[ch.src[k]];
+      w[PF_LEN + k] = ch.len[k];
+      w[PF_HEAD + k] = ch.head[k];
+      w[PF_T + k] = lens[ch.src[k]];
+    }
+    HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.pf_desc), w, sizeof(int32_t) * PF_WORDS, hipMemcpyHostToDevice, s));
+    if (eager) HIPCHK(c, enqueue_pf_chunk(c, ch.sh));
+    else HIPCHK(c, hipGraphLaunch(c->pf_graphs[ch.sh.key()].second, s));
+  }
+  HIPCHK(c, hipStreamSynchronize(s));
+  for (int i = 0; i < n; ++i) {
+    c->pos_host[slots[i]] = lens[i];
+    c->ready[slots[i]] = 1;
+  }
+  return QT_OK;
 }
 
 int32_t decode_chunks(qt_ctx *c, int32_t n, const int32_t *overlay_ids, int32_t *codes_out,

@@ -13,12 +13,32 @@ enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_GATED = 2 };
 
 // Row r of a step belongs to slot  slot_base + r / rows_per_slot  and sits at
 // position  pos_dev ? pos_dev[slot] : pos_base + r % rows_per_slot.
+// Prompt chunks carry a device descriptor instead (pf, the PF_* words below):
+// row r is row r % rows_per_slot of the chunk's stream i = r / rows_per_slot,
+// slot pf[PF_SLOT + i], position pf[PF_R0] + r % rows_per_slot, and a padding
+// row (not written to the ring) past the stream's pf[PF_LEN + i] rows;
+// pos_base then only sizes the launch (the chunk's start on the host).
 struct RowMap {
   int32_t slot_base;
   int32_t rows_per_slot;
   int32_t pos_base;
   const int32_t *pos_dev;
+  const int32_t *pf = nullptr;
 };
+
+// Prompt-chunk descriptor words (int32; sampler words as in the decode's
+// control block).  Up to PF_MAXROWS streams per chunk.
+enum PfWord {
+  PF_IDOFF = 0,  // first row of the chunk's ids in the staged id arrays
+  PF_R0 = 1,     // position of the chunk's first row (every stream)
+  PF_ITEMP = 2, PF_SEED_LO = 3, PF_SEED_HI = 4, PF_TOPK = 5,
+  PF_SLOT = 8,   // [i] slot of stream i
+  PF_LEN = 12,   // [i] prompt rows of stream i in the chunk (the rest is padding)
+  PF_HEAD = 16,  // [i] chunk row of stream i's last prompt row, -1: its prompt goes on
+  PF_T = 20,     // [i] stream i's prompt length
+  PF_WORDS = 32
+};
+constexpr int PF_MAXROWS = 4;
 
 struct Lin {
   const void *w;
@@ -136,15 +156,15 @@ struct ArgmaxArgs {
   int32_t tab_bf16, H;
   float *x_next;  // AM_PRED: row b <- E_{j+1}[code] when j+1 < G-1
   float *ssq;     // optional: x_next row sums of squares in 32-column slots [M][H/32]
-  int32_t slot;   // AM_PREFILL
-  // Sampling (sampler.h).  AM_PRED / AM_TALKER read it from the per-call
-  // control words: ctl[2] = float bits of 1/T (0: greedy), ctl[3], ctl[4] =
-  // seed low, high, ctl[5] = top_k (0: all; needs Vc <= 2048).  AM_PREFILL
-  // takes it here, with q = the prompt length.
-  float inv_temp;
-  uint64_t seed;
-  int32_t top_k;
-  int32_t q_prefill;
+  // AM_PREFILL: row r is stream r of a prompt chunk (ctl = its descriptor,
+  // PF_* words); a stream whose prompt ends in the chunk (PF_HEAD >= 0) gets
+  // c0, pos = its prompt length, its bridge row (bridge_src row r) and its
+  // logits row (logits_out row slot)
+  const float *bridge_src;
+  float *bridge, *logits_out;
+  // Sampling (sampler.h), read from the control words: ctl[2] = float bits
+  // of 1/T (0: greedy), ctl[3], ctl[4] = seed low, high, ctl[5] = top_k (0:
+  // all; needs Vc <= 2048); q = the prompt length for AM_PREFILL.
 };
 
 // Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= 128 rows (64-row blocks),
@@ -175,6 +195,11 @@ struct GemmArgs {
   uint32_t *cnt;       // [tiles] arrival counters, zero between launches
 };
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s);
+
+// Prompt chunks: row PF_HEAD[i] of x (or row 0 when negative) -> row i of xh,
+// for the chunk's n streams ([QT-log] TTFA entry: the first frame's code is
+// decided by the talker head over the prompt's last row).
+hipError_t launch_pf_rows(const int32_t *pf, const float *x, float *xh, int32_t n, int32_t H, hipStream_t s);
 
 hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s);
 hipError_t launch_qk_rope_kv(int hd, int kv_bf16, const QkArgs &a, hipStream_t s);

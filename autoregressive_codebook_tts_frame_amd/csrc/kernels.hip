@@ -52,9 +52,16 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-__device__ __forceinline__ int row_slot(const RowMap &m, int r) { return m.slot_base + r / m.rows_per_slot; }
+__device__ __forceinline__ int row_slot(const RowMap &m, int r) {
+  return m.pf ? m.pf[PF_SLOT + r / m.rows_per_slot] : m.slot_base + r / m.rows_per_slot;
+}
 __device__ __forceinline__ int row_pos(const RowMap &m, int r) {
+  if (m.pf) return m.pf[PF_R0] + r % m.rows_per_slot;
   return m.pos_dev ? m.pos_dev[row_slot(m, r)] : m.pos_base + r % m.rows_per_slot;
+}
+// false for a prompt chunk's padding rows (their stream's prompt has ended)
+__device__ __forceinline__ bool row_valid(const RowMap &m, int r) {
+  return !m.pf || r % m.rows_per_slot < m.pf[PF_LEN + r / m.rows_per_slot];
 }
 // Element offset of (slot, position) inside one (layer, K|V) block of the
 // ring, head kh: the dense ring [slot][head][P][hd], or the paged pool
@@ -324,6 +331,7 @@ template <int HD, bool KVB>
 __global__ __launch_bounds__(64) void qk_rope_kv_kernel(QkArgs a) {
   constexpr int HALF = HD / 2;
   const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  if (!row_valid(a.rows, r)) return;  // padding: nothing reaches the ring
   const int slot = row_slot(a.rows, r), pos = row_pos(a.rows, r);
   const int qd = a.nq * HD, kd = a.nkv * HD;
   const float *row = a.qkv + (size_t)r * (qd + 2 * kd);
@@ -426,6 +434,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   constexpr int PG = 256 / CPR;   // rows per pass
   constexpr int NP = 256 / PG;    // passes over a full tile
   const int r = blockIdx.x, kh = blockIdx.y, t = blockIdx.z;
+  if (!row_valid(a.rows, r)) return;  // padding rows attend to nothing
   const int slot = row_slot(a.rows, r), pos = row_pos(a.rows, r);
   const int j0 = t * a.tile;
   if (j0 > pos) return;
@@ -701,6 +710,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
 template <int HD>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
   const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  if (!row_valid(a.rows, r)) return;
   const int pos = row_pos(a.rows, r);
   const int ntiles = (pos + a.tile) / a.tile;
   if (ntiles == 1) return;
@@ -1322,14 +1332,17 @@ __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *lg = a.logits + (size_t)r * a.Vc;
   // The code's sampling key: stream, frame position, index in the frame
-  float inv_temp = a.inv_temp;
-  uint64_t seed = a.seed;
-  int slot = a.slot, q = a.q_prefill, jc = 0, top_k = a.top_k;
-  if (a.mode != AM_PREFILL) {
-    inv_temp = __int_as_float(a.ctl[2]);
-    seed = (uint64_t)(uint32_t)a.ctl[3] | ((uint64_t)(uint32_t)a.ctl[4] << 32);
-    top_k = a.ctl[5];
-    slot = r;
+  const float inv_temp = __int_as_float(a.ctl[2]);
+  const uint64_t seed = (uint64_t)(uint32_t)a.ctl[3] | ((uint64_t)(uint32_t)a.ctl[4] << 32);
+  const int top_k = a.ctl[5];
+  int slot = r, q, jc = 0;
+  if (a.mode == AM_PREFILL) {
+    if (a.ctl[PF_HEAD + r] < 0) return;  // this stream's prompt goes on in the next chunk
+    slot = a.ctl[PF_SLOT + r];
+    q = a.ctl[PF_T + r];
+    for (int i = tid; i < a.H; i += 256) a.bridge[(size_t)slot * a.H + i] = a.bridge_src[(size_t)r * a.H + i];
+    for (int i = tid; i < a.Vc; i += 256) a.logits_out[(size_t)slot * a.Vc + i] = lg[i];
+  } else {
     q = a.mode == AM_PRED ? a.pos[r] : a.pos[r] + 1;
     jc = a.mode == AM_PRED ? a.j + 1 : 0;
   }
@@ -1384,7 +1397,8 @@ __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
       if (a.tpos_dump) a.tpos_dump[r] = a.pos[r];
       a.pos[r] = a.pos[r] + 1;
     } else {
-      a.c0_state[a.slot] = b;
+      a.c0_state[slot] = b;
+      a.pos[slot] = q;
     }
     code = c;
   }
@@ -1408,6 +1422,16 @@ __global__ __launch_bounds__(256) void argmax_kernel(ArgmaxArgs a) {
     }
     if (a.ssq) put_ssq(a.ssq, a.H, r, 0, a.H, sq);
   }
+}
+
+__global__ __launch_bounds__(256) void pf_rows_kernel(const int32_t *pf, const float *x, float *xh, int32_t H) {
+  const int i = blockIdx.x, src = max(pf[PF_HEAD + i], 0);
+  for (int k = threadIdx.x; k < H; k += 256) xh[(size_t)i * H + k] = x[(size_t)src * H + k];
+}
+
+hipError_t launch_pf_rows(const int32_t *pf, const float *x, float *xh, int32_t n, int32_t H, hipStream_t s) {
+  hipLaunchKernelGGL(pf_rows_kernel, dim3(n), dim3(256), 0, s, pf, x, xh, H);
+  return hipGetLastError();
 }
 
 hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t s) {

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqt.so")
 
 QT_ABI_MIN_VERSION = 1
-QT_ABI_VERSION = 4
+QT_ABI_VERSION = 5
 QT_OK = 0
 QT_E_ABI, QT_E_ARG, QT_E_SIZE, QT_E_RANGE = -1, -2, -3, -4
 QT_E_STATE, QT_E_CONTEXT_FULL, QT_E_HIP, QT_E_UNSUPPORTED = -5, -6, -7, -8
@@ -35,7 +35,7 @@ QT_KERNEL_GEMV_GATE_UP = 1
 EXPORTS = ("qt_abi_version", "qt_query_sizes", "qt_init", "qt_prefill", "qt_decode_frame",
            "qt_get_slot_state", "qt_set_slot_state", "qt_read_dump", "qt_time_kernel",
            "qt_set_sampler", "qt_path", "qt_free", "qt_last_error", "qt_stream_read",
-           "qt_decode_frame_noalloc", "qt_query_paged_ring")
+           "qt_decode_frame_noalloc", "qt_query_paged_ring", "qt_prefill_rows")
 
 
 class qt_model_desc(C.Structure):
@@ -89,6 +89,8 @@ def _load():
     lib.qt_init.restype = i32
     lib.qt_prefill.argtypes = [vp, i32, i32, vp, vp]
     lib.qt_prefill.restype = i32
+    lib.qt_prefill_rows.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.qt_prefill_rows.restype = i32
     lib.qt_decode_frame.argtypes = [vp, i32, vp, vp, vp]
     lib.qt_decode_frame.restype = i32
     lib.qt_decode_frame_noalloc.argtypes = [vp, i32, vp, vp, vp]
@@ -172,6 +174,17 @@ def qt_prefill(ctx, slot: int, codes: Optional[np.ndarray], text_ids: np.ndarray
     text_ids = np.ascontiguousarray(text_ids, dtype=np.int32)
     codes = None if codes is None else np.ascontiguousarray(codes, dtype=np.int32)
     _check(lib.qt_prefill(ctx, slot, text_ids.shape[0], _np_ptr(codes), _np_ptr(text_ids)), ctx)
+
+
+def qt_prefill_rows(ctx, slots, codes, text_ids):
+    """Prefill of len(slots) streams in one call: codes / text_ids are lists
+    (one array per stream; codes None for text rows only), concatenated here."""
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    lens = np.ascontiguousarray([len(t) for t in text_ids], dtype=np.int32)
+    tx = np.ascontiguousarray(np.concatenate([np.asarray(t, dtype=np.int32) for t in text_ids]), dtype=np.int32)
+    cd = None if codes is None else np.ascontiguousarray(
+        np.concatenate([np.asarray(c, dtype=np.int32) for c in codes]), dtype=np.int32)
+    _check(lib.qt_prefill_rows(ctx, sl.shape[0], _np_ptr(sl), _np_ptr(lens), _np_ptr(cd), _np_ptr(tx)), ctx)
 
 
 def qt_decode_frame(ctx, n_frames: int, overlay_ids: np.ndarray, codes_out: np.ndarray,
@@ -348,6 +361,10 @@ class Decoder:
     # -- entry points --------------------------------------------------------
     def prefill(self, slot: int, codes, text):
         qt_prefill(self.ctx, slot, codes, text)
+
+    def prefill_rows(self, slots, codes, texts):
+        """qt_prefill_rows: codes None or one [T_i][G] array per stream."""
+        qt_prefill_rows(self.ctx, slots, codes, texts)
 
     def set_sampler(self, temperature: float, seed: int = 0, top_k: int = 0):
         qt_set_sampler(self.ctx, temperature, top_k, seed)

@@ -45,7 +45,7 @@ extern "C" {
    ([QT-tests], codec left context / ABI range entry: the range check rejects
    a version past either bound). */
 #define QT_ABI_MIN_VERSION 1
-#define QT_ABI_VERSION 4 /* 2: qt_set_sampler; 3: qt_stream_read; 4: paged ring (QT_F_PAGED) */
+#define QT_ABI_VERSION 5 /* 2: qt_set_sampler; 3: qt_stream_read; 4: paged ring (QT_F_PAGED); 5: qt_prefill_rows */
 
 #define QT_OK 0
 #define QT_E_ABI (-1)          /* abi_version outside the closed range (checked first) */
@@ -214,11 +214,36 @@ int32_t qt_init(const qt_init_params *params, qt_ctx **out);
    text rows only).  Writes ring rows [0, T), sets the slot's bridge (final
    normed hidden of row T-1), c0 (argmax of the talker head) and pos = T.
    codes: host [T][G] or NULL; text_ids: host [T].  Synchronous.  Paged ring:
-   the slot's rows go back to the pool first, then it takes T rows.
+   the slot's rows go back to the pool first, then it takes T rows.  The
+   same as qt_prefill_rows with one stream.
    Errors: QT_E_ARG, QT_E_RANGE, QT_E_CONTEXT_FULL (T > P, or a paged pool
    without T free rows), QT_E_HIP. */
 int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
                    const int32_t *text_ids);
+
+/* Prefill of n streams (1 <= n <= 4) in one call, each as qt_prefill would
+   ([MC-opt] round-18 table, talker chunk-prefill graphs: graphs per row count
+   1-4 and token bucket, first codes decided in the same call).  The prompts
+   run in chunks: a chunk holds the same positions [r0, r0 + t) of every
+   stream whose prompt is not yet done, t a token bucket (16, 32, 64 or 128,
+   at most 128 rows per chunk; the ring's last positions may make the final
+   chunk shorter); a shorter prompt's rows past its end are padding, which
+   writes no ring row and changes no result, so each slot ends exactly as
+   after qt_prefill of its own prompt (bit for bit).  Unless QT_F_EAGER,
+   every chunk replays a graph captured once per (streams, t, attention
+   tiles, codes given, last chunk of some prompt) on the context's stream
+   and kept until qt_free; the first call of a new shape captures it.
+   slots: host [n], distinct; lengths: host [n], each in [1, P]; codes: host
+   [sum(lengths)][G] (stream i's rows after streams 0..i-1's) or NULL (text
+   rows only, for every stream); text_ids: host [sum(lengths)], same order.
+   Synchronous.  Paged ring: the slots' rows go back to the pool first, then
+   each takes its prompt's rows.
+   Errors: QT_E_ARG (n outside [1, 4], NULLs, a slot outside [0, B) or given
+   twice, a length <= 0), QT_E_RANGE, QT_E_CONTEXT_FULL (a length > P, or a
+   paged pool without the rows), QT_E_HIP; every check is made before the
+   first launch, and after a QT_E_HIP the slots are un-prefilled. */
+int32_t qt_prefill_rows(qt_ctx *ctx, int32_t n, const int32_t *slots, const int32_t *lengths,
+                        const int32_t *codes, const int32_t *text_ids);
 
 /* Decodes n_frames frames for all B slots.  With one slot (B = 1) and a shape
    the persistent kernel implements, one kernel launch runs every phase of the

@@ -110,6 +110,7 @@ def test_block_formats_need_scales_and_whole_blocks():
 
 def test_null_context_calls_fail_cleanly():
     assert qt.lib.qt_prefill(None, 0, 1, None, None) == qt.QT_E_ARG
+    assert qt.lib.qt_prefill_rows(None, 1, None, None, None, None) == qt.QT_E_ARG
     assert qt.lib.qt_decode_frame(None, 1, None, None, None) == qt.QT_E_ARG
     assert qt.lib.qt_read_dump(None, 1, None, 0) == qt.QT_E_ARG
     qt.lib.qt_free(None)

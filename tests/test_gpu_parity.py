@@ -893,3 +893,89 @@ def test_paged_ring_oracle_parity():
     r = _forced_run(m, w, wl, 4, batch=3, prompts=prompts, pool_rows=sum(lens) + 3 * 4, order=[1, 2, 0])
     assert r["d"].path == qt.QT_PATH_GRAPH and r["d"].pool_rows
     _check(r, m, "paged_b3")
+
+
+# ----------------------------------------------------------------- prompts of several streams in one call
+
+
+def _ring_bytes(d, b, T):
+    return d.talker_ring()[b, :, :, :, :T, :].cpu().numpy().copy().view(np.uint8)
+
+
+@pytest.mark.parametrize("base", ["tiny", "reduced_bf16"])
+def test_prefill_rows_equals_per_stream(base, tiny):
+    # several streams' prompts in one qt_prefill_rows call (chunks of the same
+    # positions of every stream still going, ragged prompts padded and ending
+    # in different chunks, the chunk size growing as streams finish) leave
+    # every slot as its own qt_prefill does, bit for bit: ring rows, bridge,
+    # c0, position and the head's logits; the graph replays equal the eager
+    # launches of the same chunks; a paged ring decodes the same codes
+    if base == "tiny":
+        m, w, wl = tiny[0], tiny[3]["d"].dw, tiny[2]
+        lens, slots = [5, 37, 100, 16], [3, 0, 2, 1]
+    else:
+        m = _reduced(synth.BIG)
+        w = synth.make_weights(m)
+        wl = dataclasses.replace(synth.WORKLOADS["q8_b8"], model=m, prompt=40)
+        lens, slots = [300, 40, 129], [1, 2, 0]
+    B = len(lens)
+    wlb = dataclasses.replace(wl, batch=B)
+    prompts = [synth.make_prompt(wlb, 20 + i, T=t) for i, t in enumerate(lens)]
+    ov = synth.make_overlays(wlb, 3)
+    say(f"[prefill rows {base}] prompts {lens} into slots {slots}")
+    d_each = qt.Decoder(m, w, B, flags=qt.QT_F_DUMP | qt.QT_F_OPS)
+    for b, (c, t) in zip(slots, prompts):
+        d_each.prefill(b, c, t)
+    lg_each = d_each.dump(qt.QT_DUMP_TALKER_LOGITS)
+    outs = {}
+    for name, flags in (("graph", qt.QT_F_DUMP | qt.QT_F_OPS), ("eager", qt.QT_F_DUMP | qt.QT_F_EAGER)):
+        d = qt.Decoder(m, w, B, flags=flags)
+        d.prefill_rows(slots, [c for c, _ in prompts], [t for _, t in prompts])
+        for b, T in zip(slots, lens):
+            se, sr = d_each.get_state(b), d.get_state(b)
+            assert se[:2] == sr[:2], (name, b)
+            assert np.array_equal(se[2].view(np.uint32), sr[2].view(np.uint32)), (name, b)
+            assert np.array_equal(_ring_bytes(d_each, b, T), _ring_bytes(d, b, T)), (name, b)
+        assert np.array_equal(d.dump(qt.QT_DUMP_TALKER_LOGITS).view(np.uint32), lg_each.view(np.uint32)), name
+        outs[name] = d.decode(3, ov)
+        d.close()
+    ref = d_each.decode(3, ov)
+    assert np.array_equal(outs["graph"], ref) and np.array_equal(outs["eager"], ref)
+    dp = qt.Decoder(m, w, B, flags=qt.QT_F_OPS, pool_rows=sum(lens) + 3 * B)
+    dp.prefill_rows(slots, [c for c, _ in prompts], [t for _, t in prompts])
+    assert np.array_equal(dp.decode(3, ov), ref)
+    dp.close()
+    d_each.close()
+    if base == "tiny":  # F32: the oracle's codes exactly
+        o = Oracle(m, tiny[1], B)
+        for b, (c, t) in zip(slots, prompts):
+            o.prefill(b, c, t)
+        assert np.array_equal(o.decode(3, ov)["codes"], ref)
+
+
+def test_prefill_rows_refusals_leave_state(tiny):
+    m, w, wl = tiny[0], tiny[3]["d"].dw, tiny[2]
+    wl2 = dataclasses.replace(wl, batch=2)
+    prompts = [synth.make_prompt(wl2, b, T=12 + b) for b in range(2)]
+    ov = synth.make_overlays(wl2, 2)
+    d = qt.Decoder(m, w, 2, flags=qt.QT_F_OPS)
+    d.prefill_rows([0, 1], [c for c, _ in prompts], [t for _, t in prompts])
+    st = [d.get_state(b) for b in range(2)]
+    c, t = prompts[0]
+    cases = [([0, 0], [c, c], [t, t], qt.QT_E_ARG),            # a slot twice
+             ([0, 2], [c, c], [t, t], qt.QT_E_ARG),            # a slot outside [0, B)
+             ([0, 1, 0, 1, 0], [c] * 5, [t] * 5, qt.QT_E_ARG),  # more than 4 streams
+             ([1], [np.zeros((m.P + 1, m.G), np.int32)], [np.zeros(m.P + 1, np.int32)], qt.QT_E_CONTEXT_FULL),
+             ([1], [c], [np.full(len(t), m.Vt, np.int32)], qt.QT_E_RANGE)]
+    for sl, cs, ts, code in cases:
+        with pytest.raises(qt.QtError) as e:
+            d.prefill_rows(sl, cs, ts)
+        assert e.value.code == code, (sl, e.value.code)
+    assert qt.lib.qt_prefill_rows(d.ctx, 0, None, None, None, None) == qt.QT_E_ARG
+    assert [d.get_state(b)[:2] for b in range(2)] == [s[:2] for s in st]
+    ref = qt.Decoder(m, w, 2, flags=qt.QT_F_OPS)
+    for b, (c, t) in enumerate(prompts):
+        ref.prefill(b, c, t)
+    assert np.array_equal(d.decode(2, ov), ref.decode(2, ov))
+    d.close()
+    ref.close()
