@@ -25,7 +25,7 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kPrefillChunk = 128;  // prompt rows per prefill step (the batched GEMM takes up to 128)
+constexpr int kPrefillChunk = 512;  // prompt rows per prefill step (at most qtk::GEMM_MAX_ROWS)
 constexpr int kPfMinRows = 16;      // smallest token bucket of a prompt chunk
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
@@ -89,16 +89,16 @@ Layout layout_of(const Dims &d, int32_t B, int32_t maxF) {
   L.z = take(sizeof(float) * R * d.F);
   L.ssq = take(sizeof(float) * R * (d.H / 32 > 0 ? d.H / 32 : 1));
   {
-    // split-K partials of the largest projection: (K / 256) slices x 128 rows x columns
+    // split-K partials of the largest projection: (K / 256) slices x rows x columns
     const size_t a1 = (size_t)(d.H / 256) * (d.nqkv > 2 * d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (2 * d.F > d.Vc ? 2 * d.F : d.Vc));
     const size_t a2 = (size_t)(d.qd / 256) * d.H, a3 = (size_t)(d.F / 256) * d.H;
     const size_t mx = a1 > a2 ? (a1 > a3 ? a1 : a3) : (a2 > a3 ? a2 : a3);
-    L.gpart = take(sizeof(float) * 128 * (mx > 0 ? mx : 1));
+    L.gpart = take(sizeof(float) * L.rows * (mx > 0 ? mx : 1));
   }
   {
     const int nmax = d.nqkv > d.F ? (d.nqkv > d.Vc ? d.nqkv : d.Vc) : (d.F > d.Vc ? d.F : d.Vc);
     // a counter per (32-column tile, 64-row block) of every projection
-    L.gcnt_bytes = sizeof(uint32_t) * 2 * (size_t)(nmax / 32 + 1 + (d.H / 32));
+    L.gcnt_bytes = sizeof(uint32_t) * ((L.rows + 63) / 64) * (size_t)(nmax / 32 + 1 + (d.H / 32));
     L.gcnt = take(L.gcnt_bytes);
   }
   L.logits_t = take(sizeof(float) * (R > (size_t)B ? R : B) * d.Vc);
@@ -199,7 +199,7 @@ struct qt_ctx {
   size_t pu_ctl = 0, pu_overlay = 0, pu_forced = 0, pu_pf_text = 0, pu_pf_codes = 0, pu_scalar = 0;
   size_t pu_pf_desc = 0;  // one descriptor per prompt chunk of a call
   // prompt-chunk graphs by (streams, rows per stream, attention tiles, codes, head)
-  std::map<uint32_t, std::pair<hipGraph_t, hipGraphExec_t>> pf_graphs;
+  std::map<uint64_t, std::pair<hipGraph_t, hipGraphExec_t>> pf_graphs;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   // adaptive K: a 1-frame graph for the frames of a call past its last
@@ -337,7 +337,7 @@ Stack pred_stack(const qt_ctx *c) {
 }
 
 // One decoder layer over M rows (x in the arena's activation rows).
-// With bf16, q8 or q4 weights and bf16 operands, every projection of 1..128
+// With bf16, q8 or q4 weights and bf16 operands, every projection of 1..512
 // rows goes through the split-K MFMA GEMM: even at one row it spreads each
 // weight row's K over its workgroups, where the GEMV gives a row to one wave
 // (a 1,024-wide q4 row fills only half of it).  F32 models use the GEMV.
@@ -350,7 +350,9 @@ bool model_uses_gemm(const qt_model_desc &md, const Dims &d) {
   return md.lin_type != QT_LIN_F32 && md.act_bf16 && d.H % 256 == 0 && d.qd % 256 == 0 && d.F % 256 == 0 &&
          d.nqkv % 32 == 0 && d.Vc % 32 == 0;
 }
-bool use_gemm(const qt_ctx *c, int M) { return model_uses_gemm(c->md, c->d) && M >= 1 && M <= 128; }
+bool use_gemm(const qt_ctx *c, int M) {
+  return model_uses_gemm(c->md, c->d) && M >= 1 && M <= std::min(c->L.rows, qtk::GEMM_MAX_ROWS);
+}
 
 // One projection.  ssq_in: the input rows' sums of squares in 32-column slots
 // (row m at ssq_in + m * ssq_stride), needed by the GEMM's RMSNorm; ssq_out:
@@ -545,13 +547,15 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
 
 // ----------------------------------------------------------------- prompt chunks
 //
-// A prompt is prefilled in chunks of up to 128 rows ([QT-log] per-layer K/V
-// ring entry: the prefill writes positions [0, T)).  One call takes 1-4
-// streams ([MC-opt] round-18 table, talker chunk-prefill graphs: a graph per
-// row count and token bucket): each chunk holds the same t positions
-// [r0, r0 + t) of every stream whose prompt is still going, t a token bucket
-// (16, 32, 64 or 128, at most 128 rows in all), a shorter prompt's rows past
-// its end being padding that reaches neither the ring nor the result.  The
+// A prompt is prefilled in chunks of up to kPrefillChunk rows ([QT-log]
+// per-layer K/V ring entry: the prefill writes positions [0, T)).  One call
+// takes 1-4 streams ([MC-opt] round-18 table, talker chunk-prefill graphs: a
+// graph per row count and token bucket): each chunk holds the same t
+// positions [r0, r0 + t) of every stream whose prompt is still going, t a
+// token bucket (a power of two from 16, at most kPrefillChunk rows in all),
+// a shorter prompt's rows past its end being padding that reaches neither
+// the ring nor the result.  Every weight matrix is read once per chunk, so
+// long prompts take the largest chunks the batched GEMM holds.  The
 // chunk's ids, slots and positions live in a device descriptor, so one
 // captured graph per (streams, t, attention tiles, codes given, head)
 // serves every chunk of that shape; the chunk in which a stream's prompt
@@ -560,8 +564,8 @@ hipError_t enqueue_frame(qt_ctx *c, int k) {
 struct PfShape {
   int n, t, r0, tiles;  // r0: the chunk start the capture sizes the attention grid from
   bool codes, head;
-  uint32_t key() const {
-    return (uint32_t)n | (uint32_t)t << 3 | (uint32_t)tiles << 11 | (uint32_t)codes << 24 | (uint32_t)head << 25;
+  uint64_t key() const {  // fields wide enough for any n, t and tile count
+    return (uint64_t)n | (uint64_t)t << 8 | (uint64_t)tiles << 24 | (uint64_t)codes << 48 | (uint64_t)head << 49;
   }
 };
 
@@ -1277,7 +1281,7 @@ int32_t qt_time_kernel(qt_ctx *c, int32_t kernel, int32_t reps, double *avg_us, 
   gu.x = c->A<float>(c->L.x); gu.x_stride = d.H; gu.M = c->B;
   gu.y = c->A<float>(c->L.z); gu.y_stride = d.F;
   // as the per-op decode path runs it (project(): the split-K MFMA GEMM for
-  // bf16, q8 and q4 models whose widths are multiples of 256, at 1..128 rows,
+  // bf16, q8 and q4 models whose widths are multiples of 256, at 1..512 rows,
   // its row norms reading the sums of squares the last decode left; else the
   // GEMV)
   (void)wt;

@@ -790,7 +790,7 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
 
 // ------------------------------------------------------------------ batched projections (MFMA)
 //
-// y[M][N] = epi(x~ . W^T) for M <= 128 rows (two 64-row blocks): x~ = bf16(x * rinv * gain) (or
+// y[M][N] = epi(x~ . W^T) for M <= GEMM_MAX_ROWS rows in 64-row blocks: x~ = bf16(x * rinv * gain) (or
 // bf16(x)); weight rows in their storage format (bf16, or q8 / q4 codes
 // converted exactly to bf16 with the 32-wide block scale applied to each
 // block's product).
@@ -1134,7 +1134,7 @@ static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
-  if (a.M < 1 || a.M > 128 || a.K % GBK || a.N % GT || a.nseg < 1 || a.nseg > 3) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > GEMM_MAX_ROWS || a.K % GBK || a.N % GT || a.nseg < 1 || a.nseg > 3) return hipErrorInvalidValue;
   for (int i = 0; i + 1 < a.nseg; ++i)  // a 16-row weight block never straddles two segments
     if (a.seg_end[i] % 16) return hipErrorInvalidValue;
   if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);

@@ -225,9 +225,9 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
    ([MC-opt] round-18 table, talker chunk-prefill graphs: graphs per row count
    1-4 and token bucket, first codes decided in the same call).  The prompts
    run in chunks: a chunk holds the same positions [r0, r0 + t) of every
-   stream whose prompt is not yet done, t a token bucket (16, 32, 64 or 128,
-   at most 128 rows per chunk; the ring's last positions may make the final
-   chunk shorter); a shorter prompt's rows past its end are padding, which
+   stream whose prompt is not yet done, t a token bucket (a power of two from
+   16 to 512, at most 512 rows per chunk; the ring's last positions may make
+   the final chunk shorter); a shorter prompt's rows past its end are padding, which
    writes no ring row and changes no result, so each slot ends exactly as
    after qt_prefill of its own prompt (bit for bit).  Unless QT_F_EAGER,
    every chunk replays a graph captured once per (streams, t, attention
@@ -340,7 +340,7 @@ int32_t qt_read_dump(qt_ctx *ctx, int32_t kind, void *host_dst, size_t bytes);
      QT_KERNEL_GEMV_GATE_UP   RMSNorm + gate/up projection + SiLU-multiply (the
                               largest weight stream of a layer) as the per-op
                               decode path runs it for the context's batch: the
-                              split-K MFMA GEMM for 1..128 rows with bf16, q8 or
+                              split-K MFMA GEMM for 1..512 rows with bf16, q8 or
                               q4 weights, the GEMV for f32 weights or widths the
                               GEMM does not take
    Errors: QT_E_ARG, QT_E_HIP, QT_E_UNSUPPORTED. */
