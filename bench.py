@@ -107,20 +107,48 @@ def talker_weight_bytes(m) -> float:
     return m.Lt * layer + m.Vc * m.H * wb
 
 
+PF_CHUNK, PF_MIN, PF_STREAMS = 512, 16, 4  # the library's prompt-chunk rows, smallest bucket, streams per call
+
+
+def prompt_chunks(lens, P):
+    """Chunks (streams, rows per stream) of one qt_prefill_rows call, as the
+    library plans them: the same positions of every stream still going, a
+    power-of-two token bucket, at most PF_CHUNK rows in all."""
+    out, r0, act = [], 0, list(lens)
+    while act:
+        cap = PF_CHUNK
+        while cap * len(act) > PF_CHUNK:
+            cap //= 2
+        t = PF_MIN
+        while t < max(act) - r0 and t < cap:
+            t *= 2
+        t = min(t, P - r0)
+        out.append((len(act), t))
+        r0 += t
+        act = [L for L in act if L > r0]
+    return out
+
+
 def ttfa(args, d, m, wl, B):
-    """Time to first frame: qt_prefill of each stream's prompt (per-op path,
-    chunks of 128 rows on the MFMA GEMM) then one qt_decode_frame.  Host wall
-    clock around each step (both calls are synchronous)."""
+    """Time to first frame: the prompts' prefill (qt_prefill_rows, up to 4
+    streams of similar length per call, in prompt chunks that replay a graph
+    per shape) then one qt_decode_frame.  Host wall clock around each step
+    (both calls are synchronous)."""
     import numpy as np
     from autoregressive_codebook_tts_frame_amd import synth
 
     ctx = synth.make_context_lengths(wl)  # the workload's (ragged) prompt lengths
     prompts = [synth.make_prompt(wl, b, T=int(ctx[b])) for b in range(B)]
     ov = synth.make_overlays(wl, 1, B)
+    order = sorted(range(B), key=lambda b: len(prompts[b][1]))
+    groups = [order[i:i + PF_STREAMS] for i in range(0, B, PF_STREAMS)]
+
+    def prefill_all():
+        for g in groups:
+            d.prefill_rows(g, [prompts[b][0] for b in g], [prompts[b][1] for b in g])
 
     def step():  # one frame, whatever the frames per replay (adaptive K: a 1-frame graph)
-        for b, (c, t) in enumerate(prompts):
-            d.prefill(b, c, t)
+        prefill_all()
         d.decode(1, ov)
 
     for _ in range(args.warmup):
@@ -130,15 +158,14 @@ def ttfa(args, d, m, wl, B):
         t0 = time.perf_counter()
         step()
         times.append(time.perf_counter() - t0)
-    # the prefill alone, for its roofline: the talker weights once per 128-row chunk
+    # the prefill alone, for its roofline: the talker weights once per prompt chunk
     pre = []
     for _ in range(args.steps):
         t0 = time.perf_counter()
-        for b, (c, t) in enumerate(prompts):
-            d.prefill(b, c, t)
+        prefill_all()
         pre.append(time.perf_counter() - t0)
     T = int(np.mean([len(t) for _, t in prompts]))  # (mean prompt rows, for the record)
-    chunks = sum((len(t) + 127) // 128 for _, t in prompts)
+    chunks = sum(len(prompt_chunks([len(prompts[b][1]) for b in g], m.P)) for g in groups)
     wbytes = talker_weight_bytes(m)
     ms = 1e3 * float(np.median(times))
     pre_ms = 1e3 * float(np.median(pre))
@@ -148,13 +175,14 @@ def ttfa(args, d, m, wl, B):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": {0: "f32", 1: "bf16", 2: "q8_0+bf16", 3: "q4+bf16"}[m.lin],
         "data": "synthetic (seeded N(0,0.02) weights, uniform codes and text ids)",
-        "config": {"workload": wl.name + "_ttfa", "batch": B, "prompt": T, "prefill_chunk": 128,
+        "config": {"workload": wl.name + "_ttfa", "batch": B, "prompt": T, "prefill_chunk": PF_CHUNK,
+                   "prompt_chunks": chunks, "streams_per_prefill_call": min(B, PF_STREAMS),
                    "path": "per-op prefill + " + {1: "persistent frame kernel", 2: "per-op hipGraph",
                                                   3: "per-op eager"}[d.path]},
         "prefill_ms": pre_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "prefill (talker weights streamed once per 128-row chunk)",
+                     "kernel": "prefill (talker weights streamed once per prompt chunk)",
                      "bytes_per_launch": chunks * wbytes, "avg_launch_us": pre_ms * 1e3},
         "cpu_baseline": None,
     }

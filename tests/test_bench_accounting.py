@@ -51,6 +51,18 @@ def test_talker_weight_bytes_of_a_prefill_chunk():
     assert bench.talker_weight_bytes(m) == 28 * LAYER_PARAMS * 2 + 2048 * 1024 * 2
 
 
+def test_prompt_chunks_of_a_prefill_call():
+    # the same positions of every stream still going, a power-of-two bucket,
+    # at most 512 rows per chunk, the ring's end cutting the last one
+    assert bench.prompt_chunks([2048], 4096) == [(1, 512)] * 4
+    assert bench.prompt_chunks([128], 4096) == [(1, 128)]
+    assert bench.prompt_chunks([5, 37, 100, 16], 256) == [(4, 128)]
+    assert bench.prompt_chunks([600, 40], 4096) == [(2, 256), (1, 512)]
+    assert bench.prompt_chunks([300, 40, 129], 4096) == [(3, 128), (2, 256)]
+    assert bench.prompt_chunks([4088], 4096) == [(1, 512)] * 8
+    assert bench.prompt_chunks([250], 256) == [(1, 256)]
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
