@@ -440,7 +440,14 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
                                : std::min(st.max_tiles, (rows.pos_base + rows.rows_per_slot - 1) / st.tile + 1);
   aa.scale = (float)(1.0 / sqrt((double)d.hd));
   aa.o = o; aa.part = c->A<float>(c->L.part);
-  if ((e = launch_attention(d.hd, md.kv_bf16, aa, aa.grid_tiles > 1, s)) != hipSuccess) return e;
+  // prompt chunks: 16 query positions per workgroup on MFMA where the shape
+  // allows (hd 128, bf16 cache), else the decode tiles
+  const int gq = d.nq / d.nkv;
+  if (rows.pf && d.hd == 128 && md.kv_bf16 && (gq == 1 || gq == 2 || gq == 4)) {
+    if ((e = launch_attn_prompt(d.hd, md.kv_bf16, aa, M / rows.rows_per_slot, s)) != hipSuccess) return e;
+  } else if ((e = launch_attention(d.hd, md.kv_bf16, aa, aa.grid_tiles > 1, s)) != hipSuccess) {
+    return e;
+  }
 
   // 4. O projection, residual added in the epilogue
   GemvArgs go = g;

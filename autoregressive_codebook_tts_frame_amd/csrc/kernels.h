@@ -204,6 +204,10 @@ hipError_t launch_pf_rows(const int32_t *pf, const float *x, float *xh, int32_t 
 
 hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s);
 hipError_t launch_qk_rope_kv(int hd, int kv_bf16, const QkArgs &a, hipStream_t s);
+// Causal attention of a prompt chunk (a.rows.pf set; hd 128, bf16 K/V, GQA
+// group 1, 2 or 4; else hipErrorInvalidValue): 16 query positions x one KV
+// head's query heads per workgroup, MFMA with f32 operands, output in a.o.
+hipError_t launch_attn_prompt(int hd, int kv_bf16, const AttnArgs &a, int n_streams, hipStream_t s);
 hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_pred_input(const PredInArgs &a, hipStream_t s);

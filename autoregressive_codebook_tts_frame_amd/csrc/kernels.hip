@@ -787,6 +787,201 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ prompt-chunk attention (MFMA)
+//
+// Causal attention of a prompt chunk's rows ([QT-log] per-layer K/V ring
+// entry: a prompt row attends to every earlier position and its own).  The
+// decode tile kernel gives each query row a workgroup, which for a long
+// prompt reads every K/V tile once per row; here a workgroup takes 16 query
+// positions of one stream and the G query heads of one KV head, and reads
+// each K/V row of their range once.  The products run on MFMA with f32
+// operands (v_mfma_f32_16x16x4_f32: the bf16 K/V values and the f32 queries
+// and probabilities, multiplied and summed in f32 as the tile kernel does).
+// Waves (g, half): query head kh*G + g over the 64-position key blocks of
+// parity `half`, each with its own online softmax; the halves are merged at
+// the end in a fixed order, so every row's result depends on its position
+// only (chunks of any size give the same bits).
+//   S^T = K Q^T: A = K (lane: key l%16, d = 32 (l/16) + u at step u),
+//   B = Q^T (d likewise, query l%16); D[r] = score of key 4 (l/16) + r and
+//   query l%16.  O = P V: A = P (query l%16, key 4 (l/16) + r at step r: the
+//   lane's own D[r]), B = V (the same key, d = 16 db + l%16) from a d-major
+//   copy of the block in LDS; D[r] = O[query 4 (l/16) + r][d 16 db + l%16].
+constexpr int PKB = 64;  // key positions per block
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int G>
+__global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
+  constexpr int HD = 128;
+  constexpr int DPT = HD / G;  // d values each staging thread copies
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD][PKB + 4];  // V^T of each half's block (+4: banks)
+  __shared__ f32x4_t mo[G][8][64];                                       // half 1's O
+  __shared__ float ml[G][2][16];                                         // half 1's (m, l)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = wave % G, half = wave / G;
+  const int kh = blockIdx.y;
+  const int t = a.rows.rows_per_slot, nqb = (t + 15) / 16;
+  const int si = blockIdx.x / nqb, qoff = (blockIdx.x % nqb) * 16;
+  const int32_t *pf = a.rows.pf;
+  const int len = pf[PF_LEN + si];
+  if (qoff >= len) return;  // padding only (the whole workgroup)
+  const int nval = min(16, len - qoff);
+  const int slot = pf[PF_SLOT + si];
+  const int p0 = pf[PF_R0] + qoff, pmax = p0 + nval - 1;
+  const int nkb = pmax / PKB + 1, niter = (nkb + 1) / 2;
+  const int row0 = si * t + qoff;  // chunk row of query 0
+  const int h = kh * G + g;
+  const int ql = lane & 15, kq = lane >> 4;
+  const int qpos = p0 + ql;
+  const uint16_t *ring = (const uint16_t *)a.ring_layer;
+
+  float qv[32];  // this lane's query values, d = 32 kq + u
+  {
+    const float *qp = a.q + (size_t)(row0 + min(ql, nval - 1)) * a.nq * HD + (size_t)h * HD + 32 * kq;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 v = *(const float4 *)(qp + 4 * u);
+      qv[4 * u] = v.x; qv[4 * u + 1] = v.y; qv[4 * u + 2] = v.z; qv[4 * u + 3] = v.w;
+    }
+  }
+  const int ptid = g * 64 + lane;  // staging thread within the half
+  const int vk = ptid & (PKB - 1), vd0 = (ptid / PKB) * DPT;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t O[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int it = 0; it < niter; ++it) {
+    const int kb = 2 * it + half;
+    const bool active = kb < nkb;  // wave-uniform
+    if (active) {  // V^T of block kb (rows past the last query position: the last one, unused)
+      const int pos = min(kb * PKB + vk, pmax);
+      const uint16_t *vr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, pos) +
+                           a.kv_stride + vd0;
+      uint4 w[DPT / 8];
+#pragma unroll
+      for (int c = 0; c < DPT / 8; ++c) w[c] = *(const uint4 *)(vr + 8 * c);
+#pragma unroll
+      for (int c = 0; c < DPT / 8; ++c) {
+        const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vt[half][vd0 + 8 * c + 2 * e][vk] = (uint16_t)(ww[e] & 0xffffu);
+          vt[half][vd0 + 8 * c + 2 * e + 1][vk] = (uint16_t)(ww[e] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    if (active) {
+      // scores of the block's 4 sub-blocks of 16 keys
+      f32x4_t s[4];
+      uint4 kw[4][4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        const int kpos = min(kb * PKB + sb * 16 + ql, pmax);
+        const uint16_t *kr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, kpos) + 32 * kq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kw[sb][c] = *(const uint4 *)(kr + 8 * c);
+      }
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t ww[4] = {kw[sb][c].x, kw[sb][c].y, kw[sb][c].z, kw[sb][c].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_lo(ww[e]), qv[8 * c + 2 * e], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_hi(ww[e]), qv[8 * c + 2 * e + 1], acc, 0, 0, 0);
+          }
+        }
+        s[sb] = acc;
+      }
+      // online softmax: scale, causal mask, the block's maximum per query
+      float mb = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb * PKB + sb * 16 + 4 * kq + r;
+          const float v = key > qpos ? -INFINITY : s[sb][r] * a.scale;
+          s[sb][r] = v;
+          mb = fmaxf(mb, v);
+        }
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float m_new = fmaxf(m_run, mb);
+      const float corr = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = s[sb][r] == -INFINITY ? 0.f : expf(s[sb][r] - m_new);
+          s[sb][r] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
+      // O rows (query 4 kq + r) rescaled by their queries' corrections
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float cr = __shfl(corr, 4 * kq + r, 64);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[db][r] *= cr;
+      }
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const uint2 w = *(const uint2 *)&vt[half][16 * db + ql][sb * 16 + 4 * kq];
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][0], bf16_lo(w.x), O[db], 0, 0, 0);
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][1], bf16_hi(w.x), O[db], 0, 0, 0);
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][2], bf16_lo(w.y), O[db], 0, 0, 0);
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][3], bf16_hi(w.y), O[db], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // the next block's staging overwrites vt
+  }
+  // the halves merged (half 0's sums first), normalised, stored
+  if (half == 1) {
+    if (kq == 0) {
+      ml[g][0][ql] = m_run;
+      ml[g][1][ql] = l_run;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) mo[g][db][lane] = O[db];
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qq = 4 * kq + r;
+      const float m0 = __shfl(m_run, qq, 64), l0 = __shfl(l_run, qq, 64);
+      const float m1 = ml[g][0][qq], l1 = ml[g][1][qq];
+      const float m = fmaxf(m0, m1);
+      const float c0 = expf(m0 - m), c1 = m1 == -INFINITY ? 0.f : expf(m1 - m);
+      const float L = l0 * c0 + l1 * c1;
+      if (qq < nval) {
+        float *op = a.o + (size_t)(row0 + qq) * a.nq * HD + (size_t)h * HD + ql;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) op[16 * db] = (O[db][r] * c0 + mo[g][db][lane][r] * c1) / L;
+      }
+    }
+  }
+}
+
+hipError_t launch_attn_prompt(int hd, int kv_bf16, const AttnArgs &a, int n_streams, hipStream_t s) {
+  const int G = a.nq / a.nkv;
+  if (hd != 128 || !kv_bf16 || !a.rows.pf || a.qkv || !(G == 1 || G == 2 || G == 4)) return hipErrorInvalidValue;
+  const dim3 grid(n_streams * ((a.rows.rows_per_slot + 15) / 16), a.nkv);
+  if (G == 1) hipLaunchKernelGGL((attn_prompt_kernel<1>), grid, dim3(128), 0, s, a);
+  else if (G == 2) hipLaunchKernelGGL((attn_prompt_kernel<2>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_prompt_kernel<4>), grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 
 // ------------------------------------------------------------------ batched projections (MFMA)
 //
