@@ -794,20 +794,31 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
 // decode tile kernel gives each query row a workgroup, which for a long
 // prompt reads every K/V tile once per row; here a workgroup takes 16 query
 // positions of one stream and the G query heads of one KV head, and reads
-// each K/V row of their range once.  The products run on MFMA with f32
-// operands (v_mfma_f32_16x16x4_f32: the bf16 K/V values and the f32 queries
-// and probabilities, multiplied and summed in f32 as the tile kernel does).
+// each K/V row of their range once.  The products run on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) with f32 accumulation: the K/V rows are bf16
+// already, and each f32 query and probability enters as two bf16 terms, hi =
+// bf16(v) and lo = bf16(v - hi) (v - hi is exact), so a product carries 16
+// bits of the f32 operand where one bf16 term would carry 8.
 // Waves (g, half): query head kh*G + g over the 64-position key blocks of
 // parity `half`, each with its own online softmax; the halves are merged at
 // the end in a fixed order, so every row's result depends on its position
 // only (chunks of any size give the same bits).
-//   S^T = K Q^T: A = K (lane: key l%16, d = 32 (l/16) + u at step u),
-//   B = Q^T (d likewise, query l%16); D[r] = score of key 4 (l/16) + r and
-//   query l%16.  O = P V: A = P (query l%16, key 4 (l/16) + r at step r: the
-//   lane's own D[r]), B = V (the same key, d = 16 db + l%16) from a d-major
-//   copy of the block in LDS; D[r] = O[query 4 (l/16) + r][d 16 db + l%16].
+//   S^T = K Q^T per 16 keys: A = K (lane: key l%16, d = 32 st + 8 (l/16) ..
+//   + 8 at step st), B = Q^T (the same d, query l%16); D[r] = score of key
+//   4 (l/16) + r and query l%16.  O = P V per 32 keys (sub-blocks 2j, 2j+1):
+//   A = P (query l%16; its 8 k slots are the lane's own scores, keys
+//   4 (l/16) + r of both sub-blocks), B = V (the same keys, d = 16 db + l%16)
+//   from a d-major copy of the block in LDS; D[r] = O[query 4 (l/16) + r][d
+//   16 db + l%16].
 constexpr int PKB = 64;  // key positions per block
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// v as bf16 hi + lo terms (hi = nearest bf16, lo = nearest bf16 of the exact v - hi)
+__device__ __forceinline__ void split_bf16(const f32x8_t v, bf16x8_t &hi, bf16x8_t &lo) {
+  hi = __builtin_convertvector(v, bf16x8_t);
+  lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8_t), bf16x8_t);
+}
 
 template <int G>
 __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
@@ -834,13 +845,13 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
   const int qpos = p0 + ql;
   const uint16_t *ring = (const uint16_t *)a.ring_layer;
 
-  float qv[32];  // this lane's query values, d = 32 kq + u
+  bf16x8_t qhi[4], qlo[4];  // this lane's query values, d = 32 st + 8 kq .. + 8
   {
-    const float *qp = a.q + (size_t)(row0 + min(ql, nval - 1)) * a.nq * HD + (size_t)h * HD + 32 * kq;
+    const float *qp = a.q + (size_t)(row0 + min(ql, nval - 1)) * a.nq * HD + (size_t)h * HD + 8 * kq;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float4 v = *(const float4 *)(qp + 4 * u);
-      qv[4 * u] = v.x; qv[4 * u + 1] = v.y; qv[4 * u + 2] = v.z; qv[4 * u + 3] = v.w;
+    for (int st = 0; st < 4; ++st) {
+      const float4 v0 = *(const float4 *)(qp + 32 * st), v1 = *(const float4 *)(qp + 32 * st + 4);
+      split_bf16((f32x8_t){v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w}, qhi[st], qlo[st]);
     }
   }
   const int ptid = g * 64 + lane;  // staging thread within the half
@@ -874,25 +885,22 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
     if (active) {
       // scores of the block's 4 sub-blocks of 16 keys
       f32x4_t s[4];
-      uint4 kw[4][4];
+      uint4 kw[4][4];  // [sub-block][st]: key l%16 of the sub-block, d = 32 st + 8 kq .. + 8
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         const int kpos = min(kb * PKB + sb * 16 + ql, pmax);
-        const uint16_t *kr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, kpos) + 32 * kq;
+        const uint16_t *kr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, kpos) + 8 * kq;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kw[sb][c] = *(const uint4 *)(kr + 8 * c);
+        for (int st = 0; st < 4; ++st) kw[sb][st] = *(const uint4 *)(kr + 32 * st);
       }
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t ww[4] = {kw[sb][c].x, kw[sb][c].y, kw[sb][c].z, kw[sb][c].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_lo(ww[e]), qv[8 * c + 2 * e], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_hi(ww[e]), qv[8 * c + 2 * e + 1], acc, 0, 0, 0);
-          }
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, kw[sb][st]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qhi[st], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[st], acc, 0, 0, 0);
         }
         s[sb] = acc;
       }
@@ -932,15 +940,19 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
         for (int db = 0; db < 8; ++db) O[db][r] *= cr;
       }
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
+      for (int j = 0; j < 2; ++j) {  // keys of sub-blocks 2j and 2j+1
+        bf16x8_t phi, plo;
+        split_bf16((f32x8_t){s[2 * j][0], s[2 * j][1], s[2 * j][2], s[2 * j][3],
+                             s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]}, phi, plo);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const uint2 w = *(const uint2 *)&vt[half][16 * db + ql][sb * 16 + 4 * kq];
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][0], bf16_lo(w.x), O[db], 0, 0, 0);
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][1], bf16_hi(w.x), O[db], 0, 0, 0);
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][2], bf16_lo(w.y), O[db], 0, 0, 0);
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[sb][3], bf16_hi(w.y), O[db], 0, 0, 0);
+          const uint2 w0 = *(const uint2 *)&vt[half][16 * db + ql][32 * j + 4 * kq];
+          const uint2 w1 = *(const uint2 *)&vt[half][16 * db + ql][32 * j + 16 + 4 * kq];
+          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(w0.x, w0.y, w1.x, w1.y));
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[db], 0, 0, 0);
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[db], 0, 0, 0);
         }
+      }
     }
     __syncthreads();  // the next block's staging overwrites vt
   }
