@@ -52,16 +52,23 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// PFM: the rows are a prompt chunk's (m.pf set), a separate instantiation of
+// each kernel, so the decode steps' rows carry no descriptor reads or checks
+template <bool PFM>
 __device__ __forceinline__ int row_slot(const RowMap &m, int r) {
-  return m.pf ? m.pf[PF_SLOT + r / m.rows_per_slot] : m.slot_base + r / m.rows_per_slot;
+  if constexpr (PFM) return m.pf[PF_SLOT + r / m.rows_per_slot];
+  return m.slot_base + r / m.rows_per_slot;
 }
+template <bool PFM>
 __device__ __forceinline__ int row_pos(const RowMap &m, int r) {
-  if (m.pf) return m.pf[PF_R0] + r % m.rows_per_slot;
-  return m.pos_dev ? m.pos_dev[row_slot(m, r)] : m.pos_base + r % m.rows_per_slot;
+  if constexpr (PFM) return m.pf[PF_R0] + r % m.rows_per_slot;
+  return m.pos_dev ? m.pos_dev[row_slot<false>(m, r)] : m.pos_base + r % m.rows_per_slot;
 }
 // false for a prompt chunk's padding rows (their stream's prompt has ended)
+template <bool PFM>
 __device__ __forceinline__ bool row_valid(const RowMap &m, int r) {
-  return !m.pf || r % m.rows_per_slot < m.pf[PF_LEN + r / m.rows_per_slot];
+  if constexpr (PFM) return r % m.rows_per_slot < m.pf[PF_LEN + r / m.rows_per_slot];
+  return true;
 }
 // Element offset of (slot, position) inside one (layer, K|V) block of the
 // ring, head kh: the dense ring [slot][head][P][hd], or the paged pool
@@ -327,12 +334,12 @@ __device__ __forceinline__ void qk_norm_rope(float x0, float x1, float g0, float
   o1 = y1 * c + y0 * sn;
 }
 
-template <int HD, bool KVB>
+template <int HD, bool KVB, bool PFM>
 __global__ __launch_bounds__(64) void qk_rope_kv_kernel(QkArgs a) {
   constexpr int HALF = HD / 2;
   const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  if (!row_valid(a.rows, r)) return;  // padding: nothing reaches the ring
-  const int slot = row_slot(a.rows, r), pos = row_pos(a.rows, r);
+  if (!row_valid<PFM>(a.rows, r)) return;  // padding: nothing reaches the ring
+  const int slot = row_slot<PFM>(a.rows, r), pos = row_pos<PFM>(a.rows, r);
   const int qd = a.nq * HD, kd = a.nkv * HD;
   const float *row = a.qkv + (size_t)r * (qd + 2 * kd);
   const bool isq = h < a.nq;
@@ -374,12 +381,23 @@ __global__ __launch_bounds__(64) void qk_rope_kv_kernel(QkArgs a) {
 
 hipError_t launch_qk_rope_kv(int hd, int kv_bf16, const QkArgs &a, hipStream_t s) {
   const dim3 grid(a.M, a.nq + a.nkv);
+  const bool pf = a.rows.pf != nullptr;
   if (hd == 128) {
-    if (kv_bf16) hipLaunchKernelGGL((qk_rope_kv_kernel<128, true>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((qk_rope_kv_kernel<128, false>), grid, dim3(64), 0, s, a);
+    if (kv_bf16) {
+      if (pf) hipLaunchKernelGGL((qk_rope_kv_kernel<128, true, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((qk_rope_kv_kernel<128, true, false>), grid, dim3(64), 0, s, a);
+    } else {
+      if (pf) hipLaunchKernelGGL((qk_rope_kv_kernel<128, false, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((qk_rope_kv_kernel<128, false, false>), grid, dim3(64), 0, s, a);
+    }
   } else {
-    if (kv_bf16) hipLaunchKernelGGL((qk_rope_kv_kernel<64, true>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((qk_rope_kv_kernel<64, false>), grid, dim3(64), 0, s, a);
+    if (kv_bf16) {
+      if (pf) hipLaunchKernelGGL((qk_rope_kv_kernel<64, true, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((qk_rope_kv_kernel<64, true, false>), grid, dim3(64), 0, s, a);
+    } else {
+      if (pf) hipLaunchKernelGGL((qk_rope_kv_kernel<64, false, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((qk_rope_kv_kernel<64, false, false>), grid, dim3(64), 0, s, a);
+    }
   }
   return hipGetLastError();
 }
@@ -426,7 +444,7 @@ __device__ __forceinline__ void kv_unpack(uint4 w, float *v) {
 // is requested before it is used.
 // PAGED: the tile's rows come through the page table (a separate
 // instantiation, so the dense ring's address arithmetic stays as it is).
-template <int HD, int G, bool KVB, bool FUSED, bool PAGED>
+template <int HD, int G, bool KVB, bool FUSED, bool PAGED, bool PFM>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   constexpr int ESZ = KVB ? 2 : 4;
   constexpr int DPC = 16 / ESZ;   // values per chunk
@@ -434,8 +452,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   constexpr int PG = 256 / CPR;   // rows per pass
   constexpr int NP = 256 / PG;    // passes over a full tile
   const int r = blockIdx.x, kh = blockIdx.y, t = blockIdx.z;
-  if (!row_valid(a.rows, r)) return;  // padding rows attend to nothing
-  const int slot = row_slot(a.rows, r), pos = row_pos(a.rows, r);
+  if (!row_valid<PFM>(a.rows, r)) return;  // padding rows attend to nothing
+  const int slot = row_slot<PFM>(a.rows, r), pos = row_pos<PFM>(a.rows, r);
   const int j0 = t * a.tile;
   if (j0 > pos) return;
   const int jn = min(a.tile, pos + 1 - j0);
@@ -463,8 +481,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   if constexpr (FUSED) {
     const int rps = a.rows.rows_per_slot;
     rs0 = r - r % rps;
-    p0 = row_pos(a.rows, rs0);
-    p1 = rps > 1 ? row_pos(a.rows, rs0 + 1) : pos;
+    p0 = row_pos<PFM>(a.rows, rs0);
+    p1 = rps > 1 ? row_pos<PFM>(a.rows, rs0 + 1) : pos;
     need0 = p0 >= j0 && p0 - j0 < jn;  // inside this tile, at or before pos
     need1 = rps > 1 && p1 >= j0 && p1 - j0 < jn;
     const int ln = lane & (HALF - 1);
@@ -707,11 +725,11 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a) {
   }
 }
 
-template <int HD>
+template <int HD, bool PFM>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
   const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  if (!row_valid(a.rows, r)) return;
-  const int pos = row_pos(a.rows, r);
+  if (!row_valid<PFM>(a.rows, r)) return;
+  const int pos = row_pos<PFM>(a.rows, r);
   const int ntiles = (pos + a.tile) / a.tile;
   if (ntiles == 1) return;
   const float *p = a.part + ((size_t)r * a.nq + h) * a.max_tiles * (HD + 2);
@@ -754,15 +772,23 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
 template <int HD, int G>
 static void attn_tile_g(int kv_bf16, const AttnArgs &a, hipStream_t s) {
   const dim3 grid(a.M, a.nkv, a.grid_tiles > 0 ? a.grid_tiles : a.max_tiles);
-  if (a.qkv) {  // (the predictor's dense cache: never paged)
-    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, true, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, true, false>), grid, dim3(256), 0, s, a);
+  if (a.qkv) {  // (the predictor's dense cache: never paged, never a prompt chunk)
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, true, false, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, true, false, false>), grid, dim3(256), 0, s, a);
+  } else if (a.rows.pf) {  // prompt chunks of the shapes the MFMA kernel does not take
+    if (a.ptab) {
+      if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, true, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, true, true>), grid, dim3(256), 0, s, a);
+    } else {
+      if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, false, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, false, true>), grid, dim3(256), 0, s, a);
+    }
   } else if (a.ptab) {
-    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, true>), grid, dim3(256), 0, s, a);
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, true, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, false>), grid, dim3(256), 0, s, a);
+    if (kv_bf16) hipLaunchKernelGGL((attn_tile_kernel<HD, G, true, false, false, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_tile_kernel<HD, G, false, false, false, false>), grid, dim3(256), 0, s, a);
   }
 }
 
@@ -782,8 +808,13 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !combine) return e;
   const dim3 g2(a.M, a.nq);
-  if (hd == 128) hipLaunchKernelGGL((attn_combine_kernel<128>), g2, dim3(128), 0, s, a);
-  else hipLaunchKernelGGL((attn_combine_kernel<64>), g2, dim3(64), 0, s, a);
+  if (a.rows.pf) {
+    if (hd == 128) hipLaunchKernelGGL((attn_combine_kernel<128, true>), g2, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, true>), g2, dim3(64), 0, s, a);
+  } else {
+    if (hd == 128) hipLaunchKernelGGL((attn_combine_kernel<128, false>), g2, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, false>), g2, dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

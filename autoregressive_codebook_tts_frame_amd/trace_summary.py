@@ -2,6 +2,7 @@
 
     python -m autoregressive_codebook_tts_frame_amd.trace_summary DIR          one replay of the per-op graph
     python -m autoregressive_codebook_tts_frame_amd.trace_summary --stats DIR  every kernel of the trace
+    python -m autoregressive_codebook_tts_frame_amd.trace_summary --prefill DIR  the last prompt prefill
 
 The replay summary takes the last replay before the last advance_kernel and
 splits it into predictor and talker stages; --stats lists calls, total and
@@ -54,8 +55,31 @@ def stats(d: str) -> None:
         print("| `%s` | %d | %.1f | %.1f | %.2f |" % (k[:110], n, t, t / n, 100 * t / tot))
 
 
+def prefill(d: str) -> None:
+    db = glob.glob(d + "/**/*.db", recursive=True)[0]
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, start, end, grid_x, workgroup_x, grid_y, grid_z from kernels order by start").fetchall()
+    fk = [i for i, r in enumerate(rows) if "frame_kernel" in r[0]]
+    seg = rows[fk[-2] + 1:fk[-1]]
+    agg = collections.defaultdict(lambda: [0, 0.0])
+    for r in seg:
+        key = (r[0].split("(")[0].replace("void ", ""), "%dx%dx%d" % (r[3] // r[4], r[5], r[6]))
+        agg[key][0] += 1
+        agg[key][1] += (r[2] - r[1]) / 1e3
+    tot = sum(t for _, t in agg.values())
+    print("| kernel | grid | calls | average (us) | total (us) | % |")
+    print("|---|---|---:|---:|---:|---:|")
+    for k, (n, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
+        print("| `%s` | %s | %d | %.2f | %.1f | %.1f |" % (k[0], k[1], n, t / n, t, 100 * t / tot))
+    span = (seg[-1][2] - seg[0][1]) / 1e3
+    print("\nKernels in the prefill: %d; kernel time %.1f us, span %.1f us; the frame kernel that follows: %.1f us."
+          % (len(seg), tot, span, (rows[fk[-1]][2] - rows[fk[-1]][1]) / 1e3))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "--stats":
         stats(sys.argv[2])
+    elif sys.argv[1] == "--prefill":
+        prefill(sys.argv[2])
     else:
         main(sys.argv[1])
