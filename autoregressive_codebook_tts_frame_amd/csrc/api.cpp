@@ -27,6 +27,7 @@ thread_local std::string g_err;
 
 constexpr int kPrefillChunk = 512;  // prompt rows per prefill step (at most qtk::GEMM_MAX_ROWS)
 constexpr int kPfMinRows = 16;      // smallest token bucket of a prompt chunk
+constexpr size_t kPfMaxGraphs = 128; // prompt-chunk graphs a context keeps (further shapes launch eagerly)
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
@@ -1043,7 +1044,7 @@ int32_t prefill_rows(qt_ctx *c, int32_t n, const int32_t *slots, const int32_t *
   // idle stream (each earlier call ended with a synchronize)
   if (!eager)
     for (const Chunk &ch : plan) {
-      if (c->pf_graphs.count(ch.sh.key())) continue;
+      if (c->pf_graphs.count(ch.sh.key()) || c->pf_graphs.size() >= kPfMaxGraphs) continue;
       hipGraph_t g = nullptr;
       hipGraphExec_t x = nullptr;
       HIPCHK(c, hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed));
@@ -1104,8 +1105,9 @@ int32_t prefill_rows(qt_ctx *c, int32_t n, const int32_t *slots, const int32_t *
       w[PF_T + k] = lens[ch.src[k]];
     }
     HIPCHK(c, hipMemcpyAsync(c->A<int32_t>(c->L.pf_desc), w, sizeof(int32_t) * PF_WORDS, hipMemcpyHostToDevice, s));
-    if (eager) HIPCHK(c, enqueue_pf_chunk(c, ch.sh));
-    else HIPCHK(c, hipGraphLaunch(c->pf_graphs[ch.sh.key()].second, s));
+    const auto gi = eager ? c->pf_graphs.end() : c->pf_graphs.find(ch.sh.key());
+    if (gi == c->pf_graphs.end()) HIPCHK(c, enqueue_pf_chunk(c, ch.sh));
+    else HIPCHK(c, hipGraphLaunch(gi->second.second, s));
   }
   HIPCHK(c, hipStreamSynchronize(s));
   for (int i = 0; i < n; ++i) {

@@ -232,7 +232,9 @@ int32_t qt_prefill(qt_ctx *ctx, int32_t slot, int32_t T, const int32_t *codes,
    after qt_prefill of its own prompt (bit for bit).  Unless QT_F_EAGER,
    every chunk replays a graph captured once per (streams, t, attention
    tiles, codes given, last chunk of some prompt) on the context's stream
-   and kept until qt_free; the first call of a new shape captures it.
+   and kept until qt_free; the first call of a new shape captures it (a
+   context keeps up to 128 such graphs; chunks of further shapes launch their
+   kernels directly, with the same results).
    slots: host [n], distinct; lengths: host [n], each in [1, P]; codes: host
    [sum(lengths)][G] (stream i's rows after streams 0..i-1's) or NULL (text
    rows only, for every stream); text_ids: host [sum(lengths)], same order.

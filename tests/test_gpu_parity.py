@@ -902,8 +902,9 @@ def _ring_bytes(d, b, T):
     return d.talker_ring()[b, :, :, :, :T, :].cpu().numpy().copy().view(np.uint8)
 
 
-@pytest.mark.parametrize("base", ["tiny", "reduced_bf16"])
-def test_prefill_rows_equals_per_stream(base, tiny):
+@pytest.mark.parametrize("base,sampler", [("tiny", None), ("reduced_bf16", None), ("reduced_bf16", (0.8, 5, 40))],
+                         ids=["tiny", "reduced_bf16", "reduced_bf16_top40"])
+def test_prefill_rows_equals_per_stream(base, sampler, tiny):
     # several streams' prompts in one qt_prefill_rows call (chunks of the same
     # positions of every stream still going, ragged prompts padded and ending
     # in different chunks, the chunk size growing as streams finish) leave
@@ -922,14 +923,18 @@ def test_prefill_rows_equals_per_stream(base, tiny):
     wlb = dataclasses.replace(wl, batch=B)
     prompts = [synth.make_prompt(wlb, 20 + i, T=t) for i, t in enumerate(lens)]
     ov = synth.make_overlays(wlb, 3)
-    say(f"[prefill rows {base}] prompts {lens} into slots {slots}")
+    say(f"[prefill rows {base}] prompts {lens} into slots {slots}, sampler {sampler}")
     d_each = qt.Decoder(m, w, B, flags=qt.QT_F_DUMP | qt.QT_F_OPS)
+    if sampler:  # the first codes are drawn inside the prefill call
+        d_each.set_sampler(*sampler)
     for b, (c, t) in zip(slots, prompts):
         d_each.prefill(b, c, t)
     lg_each = d_each.dump(qt.QT_DUMP_TALKER_LOGITS)
     outs = {}
     for name, flags in (("graph", qt.QT_F_DUMP | qt.QT_F_OPS), ("eager", qt.QT_F_DUMP | qt.QT_F_EAGER)):
         d = qt.Decoder(m, w, B, flags=flags)
+        if sampler:
+            d.set_sampler(*sampler)
         d.prefill_rows(slots, [c for c, _ in prompts], [t for _, t in prompts])
         for b, T in zip(slots, lens):
             se, sr = d_each.get_state(b), d.get_state(b)
@@ -942,6 +947,8 @@ def test_prefill_rows_equals_per_stream(base, tiny):
     ref = d_each.decode(3, ov)
     assert np.array_equal(outs["graph"], ref) and np.array_equal(outs["eager"], ref)
     dp = qt.Decoder(m, w, B, flags=qt.QT_F_OPS, pool_rows=sum(lens) + 3 * B)
+    if sampler:
+        dp.set_sampler(*sampler)
     dp.prefill_rows(slots, [c for c, _ in prompts], [t for _, t in prompts])
     assert np.array_equal(dp.decode(3, ov), ref)
     dp.close()
