@@ -198,8 +198,10 @@ struct GemmArgs {
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s);
 
 // Prompt chunks: row PF_HEAD[i] of x (or row 0 when negative) -> row i of xh,
-// for the chunk's n streams ([QT-log] TTFA entry: the first frame's code is
-// decided by the talker head over the prompt's last row).
+// for the chunk's n streams: the last row of each prompt that ends in the
+// chunk, whose final-norm output is the bridge and whose head logits decide
+// frame 0's first code ([QT-log] per-layer K/V ring entry: a T-row prefill,
+// then one row per decode step).
 hipError_t launch_pf_rows(const int32_t *pf, const float *x, float *xh, int32_t n, int32_t H, hipStream_t s);
 
 hipError_t launch_gemv(int wtype, int epi, const GemvArgs &a, hipStream_t s);
