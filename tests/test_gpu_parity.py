@@ -681,9 +681,9 @@ def test_full_bf16_b32_replay_of_four_frames_equals_one_and_adaptive_k():
 @pytest.mark.timeout(900)
 def test_reduced_long_prefill_parity():
     # the 2,048-row prefill itself against the oracle's own prefill, on the
-    # full widths with two talker layers: 16 chunks of 128 rows, causal tiles
-    # across 8 attention tiles; last-row logits, bridge, code 0 and every
-    # cached K/V row
+    # full widths with two talker layers: 4 prompt chunks of 512 rows, causal
+    # tiles across 8 attention tiles; last-row logits, bridge, code 0 and
+    # every cached K/V row
     m = dataclasses.replace(_reduced(synth.BIG), P=4096)
     w = synth.make_weights(m)
     wl = dataclasses.replace(synth.WORKLOADS["bf16_long_b1"], model=m)
