@@ -28,6 +28,7 @@ thread_local std::string g_err;
 constexpr int kPrefillChunk = 512;  // prompt rows per prefill step (at most qtk::GEMM_MAX_ROWS)
 constexpr int kPfMinRows = 16;      // smallest token bucket of a prompt chunk
 constexpr size_t kPfMaxGraphs = 128; // prompt-chunk graphs a context keeps (further shapes launch eagerly)
+constexpr int kPfSlicesPerWg = 2;   // 256-wide K slices per GEMM workgroup in prompt chunks
 constexpr int kTile = 256;         // talker attention tile (window padding unit)
 constexpr size_t kAlign = 256;
 constexpr int kMaxWG = 1024;       // workgroups of the persistent kernel (>= CUs)
@@ -358,7 +359,10 @@ bool use_gemm(const qt_ctx *c, int M) {
 // One projection.  ssq_in: the input rows' sums of squares in 32-column slots
 // (row m at ssq_in + m * ssq_stride), needed by the GEMM's RMSNorm; ssq_out:
 // where a residual epilogue leaves the new rows' sums.
-hipError_t project(qt_ctx *c, int epi, const GemvArgs &g, const float *ssq_in, int ssq_stride, float *ssq_out) {
+// kpw: 256-wide K slices per GEMM workgroup (fewer split-K partials; taken
+// only where it divides the projection's K slices).
+hipError_t project(qt_ctx *c, int epi, const GemvArgs &g, const float *ssq_in, int ssq_stride, float *ssq_out,
+                   int kpw = 1) {
   const int wt = wtype_of(c->md);
   if (!use_gemm(c, g.M)) return launch_gemv(wt, epi, g, c->stream);
   GemmArgs a = {};
@@ -373,6 +377,7 @@ hipError_t project(qt_ctx *c, int epi, const GemvArgs &g, const float *ssq_in, i
   a.copy_out = g.copy_out; a.copy_stride = g.copy_stride;
   a.part = c->A<float>(c->L.gpart);
   a.cnt = c->A<uint32_t>(c->L.gcnt);
+  a.kpw = (g.K / 256) % kpw == 0 ? kpw : 1;
   return launch_gemm(wt, epi, a, c->stream);
 }
 
@@ -395,6 +400,9 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   g.act_bf16 = md.act_bf16;
   g.gain_bf16 = md.tab_bf16;
   g.eps = (float)md.eps;
+  // prompt chunks (16 to 512 rows) take two K slices per GEMM workgroup,
+  // every chunk alike, so a row's bits do not depend on how its prompt is cut
+  const int kpw = rows.pf ? kPfSlicesPerWg : 1;
 
   // 1. QKV with the attention RMSNorm prologue
   g.seg[0] = lin(w.wq); g.seg[1] = lin(w.wk); g.seg[2] = lin(w.wv);
@@ -406,7 +414,7 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   g.y = qkv; g.y_stride = d.nqkv;
   float *ssq = c->A<float>(c->L.ssq);
   const int ss = d.H / 32;
-  if ((e = project(c, EPI_STORE, g, ssq, ss, nullptr)) != hipSuccess) return e;
+  if ((e = project(c, EPI_STORE, g, ssq, ss, nullptr, kpw)) != hipSuccess) return e;
 
   // 2. q/k norm + RoPE + K/V rows into the ring at the row's position: the
   // attention tile's prologue for the predictor's decode steps (one tile per
@@ -455,14 +463,14 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   go.seg[0] = lin(w.wo); go.nseg = 1; go.seg_end[0] = d.H;
   go.N = d.H; go.K = d.qd; go.x = o; go.x_stride = d.qd; go.gain = nullptr;
   go.y = x; go.y_stride = d.H;
-  if ((e = project(c, EPI_RESID, go, nullptr, 0, ssq)) != hipSuccess) return e;
+  if ((e = project(c, EPI_RESID, go, nullptr, 0, ssq, kpw)) != hipSuccess) return e;
 
   // 5. gate/up with the MLP RMSNorm prologue, SiLU-multiply epilogue
   GemvArgs gu = g;
   gu.seg[0] = lin(w.wg); gu.up = lin(w.wu); gu.nseg = 1; gu.seg_end[0] = d.F;
   gu.N = d.F; gu.K = d.H; gu.x = x; gu.x_stride = d.H; gu.gain = w.mlp_norm;
   gu.y = z; gu.y_stride = d.F;
-  if ((e = project(c, EPI_GATED, gu, ssq, ss, nullptr)) != hipSuccess) return e;
+  if ((e = project(c, EPI_GATED, gu, ssq, ss, nullptr, kpw)) != hipSuccess) return e;
 
   // 6. down projection, residual added in the epilogue
   GemvArgs gd = g;
@@ -470,7 +478,7 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   gd.N = d.H; gd.K = d.F; gd.x = z; gd.x_stride = d.F; gd.gain = nullptr;
   gd.y = x; gd.y_stride = d.H;
   gd.copy_out = hidden_copy; gd.copy_stride = d.H;
-  return project(c, EPI_RESID, gd, nullptr, 0, ssq);
+  return project(c, EPI_RESID, gd, nullptr, 0, ssq, kpw);
 }
 
 // Frame k of a replay: predictor (codes 1..G-1) then the talker step.

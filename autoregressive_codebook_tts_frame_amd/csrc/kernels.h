@@ -194,6 +194,7 @@ struct GemmArgs {
   int32_t copy_stride;
   float *part;         // [K/256][M][N or 2N] split-K partials
   uint32_t *cnt;       // [tiles] arrival counters, zero between launches
+  int32_t kpw;         // 256-wide K slices per workgroup (0 or 1, or 2 where it divides K/256)
 };
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s);
 

@@ -1108,8 +1108,11 @@ constexpr int CPOL_SC1 = 16;
 
 // Grid z: 64-row blocks of the activation rows, each its own workgroups (the
 // blocks of one tile read the same weights; their ids differ by a multiple of
-// 8, so they run on one XCD and share its L2).
-template <int WT, int EPI>
+// 8, so they run on one XCD and share its L2).  KPW: consecutive 256-wide K
+// slices per workgroup (grid y = K / 256 / KPW), accumulated in the MFMA
+// registers slice after slice, so a tile has KPW times fewer split-K partials
+// for its last workgroup to read back; every slice's loads are issued first.
+template <int WT, int EPI, int KPW>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // The tile's weight rows form NSUB blocks of 16; each block's K slice is
   // split over WPB waves, so every wave owns SPW 32-wide steps of one block
@@ -1131,7 +1134,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int mb = 64 * blockIdx.z;                // first row of this block
   const int M0 = M - mb < 64 ? M - mb : 64;      // its rows
   const int MT = (M0 + 15) / 16;
-  const int k0 = ks * GBK;
+  const int kw = ks * KPW * GBK;                 // first K column of this workgroup's slices
   const int NP = EPI == EPI_GATED ? 2 * N : N;  // partial columns (gated: gate then up)
   const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.part);
   const int nb = wave / WPB, kq = wave % WPB;
@@ -1140,34 +1143,42 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
   // Loads first, in the order they are consumed, so that waiting for the
   // operand does not wait for the weights: the rows' sums of squares (thread
-  // t sums row t / 4's slots t % 4, t % 4 + 4, ...), the gain, the operand
-  // slice (eight columns per item), block scales, then the weights.  Every load
-  // is unconditional, from a clamped in-bounds address, and masked where it is
-  // used: a load under a branch makes the compiler wait for it at the join.
+  // t sums row t / 4's slots t % 4, t % 4 + 4, ...), the gains, the operand
+  // slices (eight columns per item), block scales, then the weights.  Every
+  // load is unconditional, from a clamped in-bounds address, and masked where
+  // it is used: a load under a branch makes the compiler wait for it at the
+  // join.
   const int sm = tid >> 2, sq4 = tid & 3;
   const bool norm_row = a.gain && sm < M0;
   const float *ssp = a.gain ? a.ssq + (size_t)(mb + min(sm, M0 - 1)) * a.ssq_stride : a.x;
   float sqv[8];  // slots sq4 + 4 i, i < 8 (hidden widths up to 1024; wider rows add a loop)
 #pragma unroll
   for (int i = 0; i < 8; ++i) sqv[i] = ssp[min(sq4 + 4 * i, K / 32 - 1)];
-  // the gain element as two 16-bit loads (bf16: the same half twice); without
-  // a norm, row 0 of x stands in as an in-bounds address
+  // each slice's gain element as two 16-bit loads (bf16: the same half
+  // twice); without a norm, row 0 of x stands in as an in-bounds address
   const uint16_t *gp = (const uint16_t *)(a.gain ? a.gain : (const void *)a.x);
-  const size_t gi = a.gain_bf16 ? (size_t)(k0 + tid) : 2 * (size_t)(k0 + tid);  // GBK == blockDim
-  const uint16_t glo = gp[gi], ghi = gp[a.gain_bf16 ? gi : gi + 1];
-  constexpr int IT = 64 * (GBK / 8) / 256;
-  float4 xv[IT][2];
+  uint16_t glo[KPW], ghi[KPW];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
-    if (it * 256 >= MT * 16 * (GBK / 8)) break;  // rows past the last 16-row block
-    const float *xr = a.x + (size_t)(mb + min(m, M0 - 1)) * a.x_stride + k0 + 8 * c;
-    xv[it][0] = *(const float4 *)xr;
-    xv[it][1] = *(const float4 *)(xr + 4);
+  for (int j = 0; j < KPW; ++j) {
+    const size_t gi = a.gain_bf16 ? (size_t)(kw + j * GBK + tid) : 2 * (size_t)(kw + j * GBK + tid);  // GBK == blockDim
+    glo[j] = gp[gi];
+    ghi[j] = gp[a.gain_bf16 ? gi : gi + 1];
   }
-  constexpr int NSC = NSUB * 16 * NBLK / 256;  // block scales per thread
+  constexpr int IT = 64 * (GBK / 8) / 256;
+  float4 xv[KPW][IT][2];
+#pragma unroll
+  for (int j = 0; j < KPW; ++j)
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
+      if (it * 256 >= MT * 16 * (GBK / 8)) break;  // rows past the last 16-row block
+      const float *xr = a.x + (size_t)(mb + min(m, M0 - 1)) * a.x_stride + kw + j * GBK + 8 * c;
+      xv[j][it][0] = *(const float4 *)xr;
+      xv[j][it][1] = *(const float4 *)(xr + 4);
+    }
+  constexpr int NSC = NSUB * 16 * NBLK / 256;  // block scales per thread and slice
   static_assert(NSUB * 16 * NBLK % 256 == 0 && 64 % NBLK == 0, "a wave's scales lie in one weight block");
-  uint16_t sv[NSC];
+  uint16_t sv[KPW][NSC];
   if constexpr (w_blocked(WT)) {
     // entry e: tile row r = e / NBLK (block r / 16, row r % 16 of it), scale
     // block e % NBLK; a wave's 64 entries are rows of one block
@@ -1178,11 +1189,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       const int rn0 = tn * GT + (EPI == EPI_GATED ? (rb % 2) : rb) * 16;
       const uint16_t *sp;
       (void)gemm_row<WT>(a, EPI == EPI_GATED ? rb / 2 : 0, rn0, sp);
-      sv[q] = sp[(size_t)(r % 16) * (K / 32) + k0 / 32 + b];
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) sv[j][q] = sp[(size_t)(r % 16) * (K / 32) + (kw + j * GBK) / 32 + b];
     }
   }
   typedef typename GemmW<WT>::V WVec;
-  WVec wv[SPW];
+  WVec wv[KPW][SPW];
   {
     // the block's 16 rows lie in one segment (segment ends are multiples of 16)
     const int n0 = __builtin_amdgcn_readfirstlane(nrow0);
@@ -1191,13 +1203,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int n = n0 + (lane & 15);  // the weight row this lane loads
     wr += (size_t)(n < N ? lane & 15 : 0) * row_bytes<WT>(K);
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const int k = k0 + (kq * SPW + s) * 32 + (lane >> 4) * 8;
-      wv[s] = *(const WVec *)(wr + row_bytes<WT>(k));
-    }
+    for (int j = 0; j < KPW; ++j)
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+        const int k = kw + j * GBK + (kq * SPW + s) * 32 + (lane >> 4) * 8;
+        wv[j][s] = *(const WVec *)(wr + row_bytes<WT>(k));
+      }
   }
 
-  // RMSNorm row scales, gain and block scales to LDS
+  // RMSNorm row scales to LDS
   float sq = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) sq += norm_row && sq4 + 4 * i < K / 32 ? sqv[i] : 0.f;
@@ -1206,58 +1220,64 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   sq += __shfl_xor(sq, 1, 64);
   sq += __shfl_xor(sq, 2, 64);
   if (sq4 == 0) rinv[sm] = a.gain ? 1.0f / sqrtf(sq / (float)K + a.eps) : 1.f;
-  gs[tid] = !a.gain ? 1.f : __uint_as_float(a.gain_bf16 ? (uint32_t)glo << 16 : ((uint32_t)ghi << 16) | glo);
-  if constexpr (w_blocked(WT))
-#pragma unroll
-    for (int q = 0; q < NSC; ++q) scl[tid + 256 * q] = f16_to_f32(sv[q]);
-  __syncthreads();
-  // operand slice in LDS as bf16: rows < MT * 16 (zero past M)
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
-    if (m >= MT * 16) break;
-    float v[8] = {xv[it][0].x, xv[it][0].y, xv[it][0].z, xv[it][0].w,
-                  xv[it][1].x, xv[it][1].y, xv[it][1].z, xv[it][1].w};
-    uint4 o = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M0) {
-      if (a.gain) {
-        const float r = rinv[m];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] * r * gs[8 * c + i];
-        if (a.normed_out && tn == 0)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a.normed_out[(size_t)(mb + m) * K + k0 + 8 * c + i] = v[i];
-      }
-      o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-      o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
-      o.z = (uint32_t)bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
-      o.w = (uint32_t)bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
-    }
-    *(uint4 *)&xs[m * GXS + 8 * c] = o;
-  }
-  __syncthreads();
 
-  // products of this wave's steps with every activation block
+  // products of this wave's steps with every activation block, slice by slice
   f32x4_t acc[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int kl = (kq * SPW + s) * 32;  // step's offset in the slice
-    const bf16x8_t av = gemm_w_bf16<WT>(wv[s]);
+  for (int j = 0; j < KPW; ++j) {
+    const int k0 = kw + j * GBK;
+    if (j > 0) __syncthreads();  // every wave is done with the last slice's operand, gain and scales
+    // the slice's gain and block scales to LDS
+    gs[tid] = !a.gain ? 1.f : __uint_as_float(a.gain_bf16 ? (uint32_t)glo[j] << 16 : ((uint32_t)ghi[j] << 16) | glo[j]);
+    if constexpr (w_blocked(WT))
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt >= MT) break;
-      const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + kl + (lane >> 4) * 8];
-      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bx);
-      if constexpr (WT == W_BF16) {
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mt], 0, 0, 0);
-      } else {
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero, 0, 0, 0);
-        const float *sr = &scl[(nb * 16 + (lane >> 4) * 4) * NBLK + kl / 32];
+      for (int q = 0; q < NSC; ++q) scl[tid + 256 * q] = f16_to_f32(sv[j][q]);
+    __syncthreads();
+    // operand slice in LDS as bf16: rows < MT * 16 (zero past M)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mt][j] += t[j] * sr[j * NBLK];
+    for (int it = 0; it < IT; ++it) {
+      const int e = tid + it * 256, m = e / (GBK / 8), c = e % (GBK / 8);
+      if (m >= MT * 16) break;
+      float v[8] = {xv[j][it][0].x, xv[j][it][0].y, xv[j][it][0].z, xv[j][it][0].w,
+                    xv[j][it][1].x, xv[j][it][1].y, xv[j][it][1].z, xv[j][it][1].w};
+      uint4 o = make_uint4(0u, 0u, 0u, 0u);
+      if (m < M0) {
+        if (a.gain) {
+          const float r = rinv[m];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = v[i] * r * gs[8 * c + i];
+          if (a.normed_out && tn == 0)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a.normed_out[(size_t)(mb + m) * K + k0 + 8 * c + i] = v[i];
+        }
+        o.x = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+        o.y = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+        o.z = (uint32_t)bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
+        o.w = (uint32_t)bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
+      }
+      *(uint4 *)&xs[m * GXS + 8 * c] = o;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int kl = (kq * SPW + s) * 32;  // step's offset in the slice
+      const bf16x8_t av = gemm_w_bf16<WT>(wv[j][s]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= MT) break;
+        const uint4 bx = *(const uint4 *)&xs[(mt * 16 + (lane & 15)) * GXS + kl + (lane >> 4) * 8];
+        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bx);
+        if constexpr (WT == W_BF16) {
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mt], 0, 0, 0);
+        } else {
+          const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+          const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero, 0, 0, 0);
+          const float *sr = &scl[(nb * 16 + (lane >> 4) * 4) * NBLK + kl / 32];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[mt][q] += t[q] * sr[q * NBLK];
+        }
       }
     }
   }
@@ -1362,17 +1382,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
 }
 
+template <int WT, int KPW>
+static hipError_t gemm_kpw(int epi, const GemmArgs &a, hipStream_t s) {
+  const dim3 grid((a.N + GT - 1) / GT, a.K / GBK / KPW, (a.M + 63) / 64);
+  if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE, KPW>), grid, dim3(256), 0, s, a);
+  else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID, KPW>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED, KPW>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 template <int WT>
 static hipError_t gemm_wt(int epi, const GemmArgs &a, hipStream_t s) {
-  const dim3 grid((a.N + GT - 1) / GT, a.K / GBK, (a.M + 63) / 64);
-  if (epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<WT, EPI_STORE>), grid, dim3(256), 0, s, a);
-  else if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_kernel<WT, EPI_RESID>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((gemm_kernel<WT, EPI_GATED>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return a.kpw == 2 ? gemm_kpw<WT, 2>(epi, a, s) : gemm_kpw<WT, 1>(epi, a, s);
 }
 
 hipError_t launch_gemm(int wtype, int epi, const GemmArgs &a, hipStream_t s) {
   if (a.M < 1 || a.M > GEMM_MAX_ROWS || a.K % GBK || a.N % GT || a.nseg < 1 || a.nseg > 3) return hipErrorInvalidValue;
+  if (a.kpw < 0 || a.kpw > 2 || (a.K / GBK) % (a.kpw > 1 ? a.kpw : 1)) return hipErrorInvalidValue;
   for (int i = 0; i + 1 < a.nseg; ++i)  // a 16-row weight block never straddles two segments
     if (a.seg_end[i] % 16) return hipErrorInvalidValue;
   if (wtype == W_BF16) return gemm_wt<W_BF16>(epi, a, s);
