@@ -830,10 +830,12 @@ hipError_t launch_attention(int hd, int kv_bf16, const AttnArgs &a, bool combine
 // already, and each f32 query and probability enters as two bf16 terms, hi =
 // bf16(v) and lo = bf16(v - hi) (v - hi is exact), so a product carries 16
 // bits of the f32 operand where one bf16 term would carry 8.
-// Waves (g, half): query head kh*G + g over the 64-position key blocks of
-// parity `half`, each with its own online softmax; the halves are merged at
-// the end in a fixed order, so every row's result depends on its position
-// only (chunks of any size give the same bits).
+// Waves (g, part): query head kh*G + g over the 64-position key blocks kb
+// with kb % NPART == part, each with its own online softmax; the parts are
+// merged at the end in a fixed order, so every row's result depends on its
+// position only (chunks of any size give the same bits).  A block's K rows go
+// straight to registers and its V rows through LDS (d-major), both requested
+// before the block's barrier.
 //   S^T = K Q^T per 16 keys: A = K (lane: key l%16, d = 32 st + 8 (l/16) ..
 //   + 8 at step st), B = Q^T (the same d, query l%16); D[r] = score of key
 //   4 (l/16) + r and query l%16.  O = P V per 32 keys (sub-blocks 2j, 2j+1):
@@ -851,15 +853,19 @@ __device__ __forceinline__ void split_bf16(const f32x8_t v, bf16x8_t &hi, bf16x8
   lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8_t), bf16x8_t);
 }
 
+// key-block partitions per workgroup: four for G = 1 and 2 (4 and 8 waves), two for G = 4 (8 waves)
+template <int G> struct PromptParts { static constexpr int v = G == 4 ? 2 : 4; };
+
 template <int G>
-__global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * G * PromptParts<G>::v) void attn_prompt_kernel(AttnArgs a) {
   constexpr int HD = 128;
+  constexpr int NPART = PromptParts<G>::v;
   constexpr int DPT = HD / G;  // d values each staging thread copies
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD][PKB + 4];  // V^T of each half's block (+4: banks)
-  __shared__ f32x4_t mo[G][8][64];                                       // half 1's O
-  __shared__ float ml[G][2][16];                                         // half 1's (m, l)
+  __shared__ __attribute__((aligned(16))) uint16_t vt[NPART][HD][PKB + 4];  // V^T of each part's block (+4: banks)
+  __shared__ f32x4_t mo[NPART - 1][G][8][64];                              // parts 1..'s O
+  __shared__ float ml[NPART - 1][G][2][16];                                // parts 1..'s (m, l)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = wave % G, half = wave / G;
+  const int g = wave % G, part = wave / G;
   const int kh = blockIdx.y;
   const int t = a.rows.rows_per_slot, nqb = (t + 15) / 16;
   const int si = blockIdx.x / nqb, qoff = (blockIdx.x % nqb) * 16;
@@ -869,7 +875,7 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
   const int nval = min(16, len - qoff);
   const int slot = pf[PF_SLOT + si];
   const int p0 = pf[PF_R0] + qoff, pmax = p0 + nval - 1;
-  const int nkb = pmax / PKB + 1, niter = (nkb + 1) / 2;
+  const int nkb = pmax / PKB + 1, niter = (nkb + NPART - 1) / NPART;
   const int row0 = si * t + qoff;  // chunk row of query 0
   const int h = kh * G + g;
   const int ql = lane & 15, kq = lane >> 4;
@@ -885,7 +891,7 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
       split_bf16((f32x8_t){v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w}, qhi[st], qlo[st]);
     }
   }
-  const int ptid = g * 64 + lane;  // staging thread within the half
+  const int ptid = g * 64 + lane;  // staging thread within the part
   const int vk = ptid & (PKB - 1), vd0 = (ptid / PKB) * DPT;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4_t O[8];
@@ -893,9 +899,12 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
   for (int db = 0; db < 8; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int it = 0; it < niter; ++it) {
-    const int kb = 2 * it + half;
+    const int kb = NPART * it + part;
     const bool active = kb < nkb;  // wave-uniform
-    if (active) {  // V^T of block kb (rows past the last query position: the last one, unused)
+    // the block's K rows (to registers) and V rows, requested together; rows
+    // past the last query position read that position's row (never used)
+    uint4 kw[4][4];  // [sub-block][st]: key l%16 of the sub-block, d = 32 st + 8 kq .. + 8
+    if (active) {
       const int pos = min(kb * PKB + vk, pmax);
       const uint16_t *vr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, pos) +
                            a.kv_stride + vd0;
@@ -903,12 +912,20 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
 #pragma unroll
       for (int c = 0; c < DPT / 8; ++c) w[c] = *(const uint4 *)(vr + 8 * c);
 #pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        const int kpos = min(kb * PKB + sb * 16 + ql, pmax);
+        const uint16_t *kr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, kpos) + 8 * kq;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) kw[sb][st] = *(const uint4 *)(kr + 32 * st);
+      }
+      // V^T of block kb
+#pragma unroll
       for (int c = 0; c < DPT / 8; ++c) {
         const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vt[half][vd0 + 8 * c + 2 * e][vk] = (uint16_t)(ww[e] & 0xffffu);
-          vt[half][vd0 + 8 * c + 2 * e + 1][vk] = (uint16_t)(ww[e] >> 16);
+          vt[part][vd0 + 8 * c + 2 * e][vk] = (uint16_t)(ww[e] & 0xffffu);
+          vt[part][vd0 + 8 * c + 2 * e + 1][vk] = (uint16_t)(ww[e] >> 16);
         }
       }
     }
@@ -916,14 +933,6 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
     if (active) {
       // scores of the block's 4 sub-blocks of 16 keys
       f32x4_t s[4];
-      uint4 kw[4][4];  // [sub-block][st]: key l%16 of the sub-block, d = 32 st + 8 kq .. + 8
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        const int kpos = min(kb * PKB + sb * 16 + ql, pmax);
-        const uint16_t *kr = ring + ring_off<HD>(a.ptab, a.slot_stride, a.P, a.rows_per_head, slot, kh, kpos) + 8 * kq;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) kw[sb][st] = *(const uint4 *)(kr + 32 * st);
-      }
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -977,8 +986,8 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
                              s[2 * j + 1][0], s[2 * j + 1][1], s[2 * j + 1][2], s[2 * j + 1][3]}, phi, plo);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const uint2 w0 = *(const uint2 *)&vt[half][16 * db + ql][32 * j + 4 * kq];
-          const uint2 w1 = *(const uint2 *)&vt[half][16 * db + ql][32 * j + 16 + 4 * kq];
+          const uint2 w0 = *(const uint2 *)&vt[part][16 * db + ql][32 * j + 4 * kq];
+          const uint2 w1 = *(const uint2 *)&vt[part][16 * db + ql][32 * j + 16 + 4 * kq];
           const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(w0.x, w0.y, w1.x, w1.y));
           O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, O[db], 0, 0, 0);
           O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, O[db], 0, 0, 0);
@@ -987,29 +996,43 @@ __global__ __launch_bounds__(128 * G) void attn_prompt_kernel(AttnArgs a) {
     }
     __syncthreads();  // the next block's staging overwrites vt
   }
-  // the halves merged (half 0's sums first), normalised, stored
-  if (half == 1) {
+  // the parts merged in order (part 0's sums first), normalised, stored;
+  // part 0 always holds block 0, whose keys every query sees
+  if (part > 0) {
     if (kq == 0) {
-      ml[g][0][ql] = m_run;
-      ml[g][1][ql] = l_run;
+      ml[part - 1][g][0][ql] = m_run;
+      ml[part - 1][g][1][ql] = l_run;
     }
 #pragma unroll
-    for (int db = 0; db < 8; ++db) mo[g][db][lane] = O[db];
+    for (int db = 0; db < 8; ++db) mo[part - 1][g][db][lane] = O[db];
   }
   __syncthreads();
-  if (half == 0) {
+  if (part == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int qq = 4 * kq + r;
       const float m0 = __shfl(m_run, qq, 64), l0 = __shfl(l_run, qq, 64);
-      const float m1 = ml[g][0][qq], l1 = ml[g][1][qq];
-      const float m = fmaxf(m0, m1);
-      const float c0 = expf(m0 - m), c1 = m1 == -INFINITY ? 0.f : expf(m1 - m);
-      const float L = l0 * c0 + l1 * c1;
+      float m = m0;
+#pragma unroll
+      for (int q = 0; q < NPART - 1; ++q) m = fmaxf(m, ml[q][g][0][qq]);
+      const float c0 = expf(m0 - m);
+      float cp[NPART - 1];
+      float L = l0 * c0;
+#pragma unroll
+      for (int q = 0; q < NPART - 1; ++q) {
+        const float mq = ml[q][g][0][qq];
+        cp[q] = mq == -INFINITY ? 0.f : expf(mq - m);
+        L += ml[q][g][1][qq] * cp[q];
+      }
       if (qq < nval) {
         float *op = a.o + (size_t)(row0 + qq) * a.nq * HD + (size_t)h * HD + ql;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) op[16 * db] = (O[db][r] * c0 + mo[g][db][lane][r] * c1) / L;
+        for (int db = 0; db < 8; ++db) {
+          float o = O[db][r] * c0;
+#pragma unroll
+          for (int q = 0; q < NPART - 1; ++q) o += mo[q][g][db][lane][r] * cp[q];
+          op[16 * db] = o / L;
+        }
       }
     }
   }
@@ -1019,9 +1042,9 @@ hipError_t launch_attn_prompt(int hd, int kv_bf16, const AttnArgs &a, int n_stre
   const int G = a.nq / a.nkv;
   if (hd != 128 || !kv_bf16 || !a.rows.pf || a.qkv || !(G == 1 || G == 2 || G == 4)) return hipErrorInvalidValue;
   const dim3 grid(n_streams * ((a.rows.rows_per_slot + 15) / 16), a.nkv);
-  if (G == 1) hipLaunchKernelGGL((attn_prompt_kernel<1>), grid, dim3(128), 0, s, a);
-  else if (G == 2) hipLaunchKernelGGL((attn_prompt_kernel<2>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_prompt_kernel<4>), grid, dim3(512), 0, s, a);
+  if (G == 1) hipLaunchKernelGGL((attn_prompt_kernel<1>), grid, dim3(64 * PromptParts<1>::v), 0, s, a);
+  else if (G == 2) hipLaunchKernelGGL((attn_prompt_kernel<2>), grid, dim3(128 * PromptParts<2>::v), 0, s, a);
+  else hipLaunchKernelGGL((attn_prompt_kernel<4>), grid, dim3(256 * PromptParts<4>::v), 0, s, a);
   return hipGetLastError();
 }
 
