@@ -980,7 +980,7 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
 // The loader waves: stream each GEMV phase's weight slice (a part each) into
 // its LDS slot one phase ahead, widen q4 slices to bf16 once they land,
 // and meet the compute waves once per phase, right after their inputs are in.
-template <int WT>
+template <int WT, bool TRC>
 __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, const Lds &L, unsigned char *smem) {
   uint8_t *const p0 = smem + L.slot0, *const p1 = smem + L.slot1;
   Ph cur{PH_QKV, 0, 0, 0, 0};
@@ -988,7 +988,7 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
   dma_slice<WT>(a, cm, cur, lds_addr(p0));
   wait_vm();
   if (!widen_slice<WT>(a, cm, cur, p0, lgen)) return;
-  if (a.trace) cm.ltime = wall_clock64();
+  if (TRC && a.trace) cm.ltime = wall_clock64();
   int slot = 0;
   uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
   uint32_t seq = 1;           // phase index of cur + 1 (its tag is tag_base + seq)
@@ -1034,7 +1034,7 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     // ng's slice (loaded now, or during the last phase) to bf16; a gate/up
     // slice loaded ahead waits for the next iteration
     if (ng.type != PH_END && !widen_slice<WT>(a, cm, ng, nslot, lgen)) break;
-    if (a.trace) cm.ltime = wall_clock64();
+    if (TRC && a.trace) cm.ltime = wall_clock64();
     if (a.two_slots) slot ^= 1;
     for (Ph q = next_phase(a, cur, a.pos0); ; q = next_phase(a, q, a.pos0)) {  // the phase index of ng
       ++seq;
@@ -1046,14 +1046,15 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
 }
 
 // SMP: the heads' codes are sampled (sampler.h), else greedy; a compile-time
-// switch, so the greedy kernel carries no sampling code.
-template <int WT, bool SMP>
+// switch, so the greedy kernel carries no sampling code.  TRC: the kernel
+// stamps its phases (QT_F_TRACE); the other kernels carry no stamp code.
+template <int WT, bool SMP, bool TRC>
 __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *smem) {
   constexpr int ESZ = WEsz<WT>::v;
   Common &cm = *reinterpret_cast<Common *>(smem);
   const Lds L = lds_layout(a);
   if (threadIdx.x >= NT) {
-    loader_role<WT>(a, cm, L, smem);
+    loader_role<WT, TRC>(a, cm, L, smem);
     return;
   }
   float *xres = (float *)(smem + L.xres);   // [2][H] residual rows
@@ -1101,7 +1102,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   while (cur.type != PH_END) {
     const Ph nxt = next_phase(a, cur, pos0);
     if (cur.type == PH_ATTN || cur.type == PH_COMB) { ++seq; cur = nxt; continue; }
-    const bool tracing = a.trace && lead && cur.frame == 0 && ntr < 767;
+    const bool tracing = TRC && a.trace && lead && cur.frame == 0 && ntr < 767;
     const uint64_t t0 = tracing ? wall_clock64() : 0;
     const uint32_t tag = a.tag_base + seq, tagp = tag - 1;
     const int f = cur.frame;
@@ -1351,7 +1352,7 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     ++seq;
     cur = nxt;
   }
-  if (a.trace && lead && tid == 0) st(a.trace + 8 * ntr, (uint64_t)255);
+  if (TRC && a.trace && lead && tid == 0) st(a.trace + 8 * ntr, (uint64_t)255);
   // the code picked by the last talker head becomes the slot's pending code 0
   if (lead) {
     if (pending) {
@@ -1406,7 +1407,7 @@ __device__ __forceinline__ void unpack16(uint4 w, float *v) {
   }
 }
 
-template <int HD, int GQ, bool KVB>
+template <int HD, int GQ, bool KVB, bool TRC>
 __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *smem) {
   constexpr int ESZ = KvT<KVB>::esz;
   constexpr int ROWB = HD * ESZ;           // bytes per K/V row
@@ -1480,7 +1481,7 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
     const bool mine = ev.valid && cur.type == PH_ATTN && cur.stack == ev.stack && cur.frame == ev.frame &&
                       cur.layer == ev.layer && (cur.stack == 1 || cur.step == ev.step);
     if (mine) {
-      const bool tracing = a.trace && wg == 0 && cur.frame == 0 && ntr < 255;
+      const bool tracing = TRC && a.trace && wg == 0 && cur.frame == 0 && ntr < 255;
       const uint64_t t0 = tracing ? wall_clock64() : 0;
       const int p = pos0 + cur.frame;
       const int M = (cur.stack == 0 && cur.step == 0) ? 2 : 1;
@@ -1712,12 +1713,12 @@ __device__ __forceinline__ void attn_role(const FrameArgs &a, unsigned char *sme
     ++seq;
     cur = nxt;
   }
-  if (a.trace && wg == 0 && tid == 0) st(a.trace + 8 * (768 + ntr), (uint64_t)255);
+  if (TRC && a.trace && wg == 0 && tid == 0) st(a.trace + 8 * (768 + ntr), (uint64_t)255);
 }
 
 // ------------------------------------------------------------ the kernel
 
-template <int WT, int HD, int GQ, bool KVB, bool SMP>
+template <int WT, int HD, int GQ, bool KVB, bool SMP, bool TRC>
 __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   Common &cm = *reinterpret_cast<Common *>(smem);
@@ -1743,9 +1744,9 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
     cm.sh[tid] = share_calc(a, tid, (int)blockIdx.x - a.n_attn, a.nwg - a.n_attn);
   __syncthreads();
   if ((int)blockIdx.x < a.n_attn) {
-    if (tid < ANT) attn_role<HD, GQ, KVB>(a, smem);  // the other waves end here
+    if (tid < ANT) attn_role<HD, GQ, KVB, TRC>(a, smem);  // the other waves end here
   } else {
-    gemv_role<WT, SMP>(a, smem);
+    gemv_role<WT, SMP, TRC>(a, smem);
   }
 }
 
@@ -1841,21 +1842,25 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   return true;
 }
 
-// The kernel instantiation of a plan (null if none).
-static const void *frame_fn(const FrameArgs &a, bool smp) {
+// The kernel instantiation of a plan (null if none): sampled or greedy
+// heads, with or without phase stamps.
+static const void *frame_fn(const FrameArgs &a, bool smp, bool trc) {
   const int g = a.nq / a.nkv;
-#define X1(W, HD_, G_, K_, S_) \
-  if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_ && smp == S_) return (const void *)frame_kernel<W, HD_, G_, K_, S_>;
+#define X2(W, HD_, G_, K_, S_, T_)                                                                     \
+  if (a.wt == W && a.hd == HD_ && g == G_ && (a.kv_bf16 != 0) == K_ && smp == S_ && trc == T_) \
+    return (const void *)frame_kernel<W, HD_, G_, K_, S_, T_>;
+#define X1(W, HD_, G_, K_, S_) X2(W, HD_, G_, K_, S_, false) X2(W, HD_, G_, K_, S_, true)
 #define X(W, HD_, G_, K_) X1(W, HD_, G_, K_, false) X1(W, HD_, G_, K_, true)
   QT_FRAME_VARIANTS(X)
 #undef X
 #undef X1
+#undef X2
   return nullptr;
 }
 
 bool frame_coresident(const FrameArgs &a, int ncu) {
-  for (const bool smp : {false, true}) {
-    const void *fn = frame_fn(a, smp);
+  for (const int v : {0, 1, 2, 3}) {
+    const void *fn = frame_fn(a, v & 1, v >> 1);
     int per_cu = 0;
     if (!fn || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTB, a.lds_bytes) != hipSuccess ||
@@ -1866,7 +1871,7 @@ bool frame_coresident(const FrameArgs &a, int ncu) {
 }
 
 hipError_t launch_frame_kernel(const FrameArgs &a, hipStream_t s) {
-  const void *fn = frame_fn(a, a.inv_temp != 0.f);
+  const void *fn = frame_fn(a, a.inv_temp != 0.f, a.trace != nullptr);
   if (!fn) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
   if (e != hipSuccess) return e;
