@@ -169,9 +169,9 @@ struct ArgmaxArgs {
 
 // Batched projection on MFMA: y = epi(act(norm(x)) . W^T) for M <= GEMM_MAX_ROWS rows (64-row blocks),
 // bf16, q8 or q4 weights with bf16 operands.  Tiles of 32 output columns (gated:
-// 32 gate + 32 up rows) x 64 rows x 256-wide K slices; the last workgroup of
-// a tile to finish sums the K slices' partials in order and applies the
-// epilogue.
+// 32 gate + 32 up rows) x 64 rows x kpw consecutive 256-wide K slices per
+// workgroup; the last workgroup of a tile to finish sums the workgroups'
+// partials in order and applies the epilogue.
 constexpr int GEMM_MAX_ROWS = 512;
 struct GemmArgs {
   Lin seg[3];          // row segments (q|k|v) ...
