@@ -450,9 +450,9 @@ hipError_t enqueue_layer(qt_ctx *c, const Stack &st, int l, int M, const RowMap 
   aa.scale = (float)(1.0 / sqrt((double)d.hd));
   aa.o = o; aa.part = c->A<float>(c->L.part);
   // prompt chunks: 16 query positions per workgroup on MFMA where the shape
-  // allows (hd 128, bf16 cache), else the decode tiles
+  // allows (hd 128, bf16 cache; the group is then 1 or 2), else the decode tiles
   const int gq = d.nq / d.nkv;
-  if (rows.pf && d.hd == 128 && md.kv_bf16 && (gq == 1 || gq == 2 || gq == 4)) {
+  if (rows.pf && d.hd == 128 && md.kv_bf16 && (gq == 1 || gq == 2)) {
     if ((e = launch_attn_prompt(d.hd, md.kv_bf16, aa, M / rows.rows_per_slot, s)) != hipSuccess) return e;
   } else if ((e = launch_attention(d.hd, md.kv_bf16, aa, aa.grid_tiles > 1, s)) != hipSuccess) {
     return e;

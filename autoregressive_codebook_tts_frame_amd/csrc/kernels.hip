@@ -853,13 +853,12 @@ __device__ __forceinline__ void split_bf16(const f32x8_t v, bf16x8_t &hi, bf16x8
   lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8_t), bf16x8_t);
 }
 
-// key-block partitions per workgroup: four for G = 1 and 2 (4 and 8 waves), two for G = 4 (8 waves)
-template <int G> struct PromptParts { static constexpr int v = G == 4 ? 2 : 4; };
+constexpr int PNPART = 4;  // key-block partitions per workgroup (G = 1: 4 waves, G = 2: 8)
 
 template <int G>
-__global__ __launch_bounds__(64 * G * PromptParts<G>::v) void attn_prompt_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * G * PNPART) void attn_prompt_kernel(AttnArgs a) {
   constexpr int HD = 128;
-  constexpr int NPART = PromptParts<G>::v;
+  constexpr int NPART = PNPART;
   constexpr int DPT = HD / G;  // d values each staging thread copies
   __shared__ __attribute__((aligned(16))) uint16_t vt[NPART][HD][PKB + 4];  // V^T of each part's block (+4: banks)
   __shared__ f32x4_t mo[NPART - 1][G][8][64];                              // parts 1..'s O
@@ -1040,11 +1039,10 @@ __global__ __launch_bounds__(64 * G * PromptParts<G>::v) void attn_prompt_kernel
 
 hipError_t launch_attn_prompt(int hd, int kv_bf16, const AttnArgs &a, int n_streams, hipStream_t s) {
   const int G = a.nq / a.nkv;
-  if (hd != 128 || !kv_bf16 || !a.rows.pf || a.qkv || !(G == 1 || G == 2 || G == 4)) return hipErrorInvalidValue;
+  if (hd != 128 || !kv_bf16 || !a.rows.pf || a.qkv || !(G == 1 || G == 2)) return hipErrorInvalidValue;
   const dim3 grid(n_streams * ((a.rows.rows_per_slot + 15) / 16), a.nkv);
-  if (G == 1) hipLaunchKernelGGL((attn_prompt_kernel<1>), grid, dim3(64 * PromptParts<1>::v), 0, s, a);
-  else if (G == 2) hipLaunchKernelGGL((attn_prompt_kernel<2>), grid, dim3(128 * PromptParts<2>::v), 0, s, a);
-  else hipLaunchKernelGGL((attn_prompt_kernel<4>), grid, dim3(256 * PromptParts<4>::v), 0, s, a);
+  if (G == 1) hipLaunchKernelGGL((attn_prompt_kernel<1>), grid, dim3(64 * PNPART), 0, s, a);
+  else hipLaunchKernelGGL((attn_prompt_kernel<2>), grid, dim3(128 * PNPART), 0, s, a);
   return hipGetLastError();
 }
 

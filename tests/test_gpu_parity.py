@@ -450,11 +450,29 @@ def _reduced(base, **kw):
 def test_reduced_bf16_full_width_parity():
     m = _reduced(synth.BIG)
     w = synth.make_weights(m)
-    # a 358-row prompt: prefill chunks of 128, 128 and 102 rows (the GEMM's
-    # two 64-row blocks, the second one ragged at 38 rows), 2 attention tiles
+    # a 358-row prompt: one prompt chunk (a 512-row bucket) whose last 64-row
+    # GEMM block is ragged at 38 rows; decode over 2 attention tiles
     wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m, prompt=358)
     say("[reduced bf16] prompt 358, 6 frames")
     _check(_forced_run(m, w, wl, 6, dump_hidden=True), m, "reduced_bf16")
+
+
+@pytest.mark.parametrize("nq,nkv,hd", [(8, 8, 128), (16, 4, 64)], ids=["group1_hd128", "group4_hd64"])
+def test_gqa_groups_parity(nq, nkv, hd):
+    # GQA groups other than the persistent kernel's (2): the per-op path with
+    # one query head per KV head (prompt chunks on the MFMA prompt attention)
+    # and four per KV head at head dim 64 (prompt chunks on the decode tiles);
+    # two streams, a 300-row and a 77-row prompt, 3 frames
+    m = dataclasses.replace(synth.BIG, Lt=2, Lp=1, Vt=4096, P=512, model_id=synth.BIG.model_id + 60 + nkv,
+                            nq=nq, nkv=nkv, hd=hd)
+    w = synth.make_weights(m)
+    wl = dataclasses.replace(synth.WORKLOADS["bf16_b1"], model=m)
+    prompts = [synth.make_prompt(wl, 0, T=300), synth.make_prompt(wl, 1, T=77)]
+    say(f"[gqa nq={nq} nkv={nkv} hd={hd}] prompts 300 and 77, 3 frames")
+    r = _forced_run(m, w, wl, 3, batch=2, prompts=prompts)
+    assert r["d"].path == qt.QT_PATH_GRAPH
+    _check(r, m, f"gqa_{nq}_{nkv}_{hd}")
+    r["d"].close()
 
 
 def test_reduced_bf16_sampled_parity():
