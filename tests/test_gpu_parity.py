@@ -242,6 +242,35 @@ def test_tiny_f32_parity(tiny):
     assert np.array_equal(r["g"]["codes"], r["oout"]["codes"])
 
 
+def test_tiny_traced_kernel_equals_plain():
+    # the QT_F_TRACE instantiation of the persistent kernel (phase stamps
+    # compiled in) decodes the same bits as the one without them, and stamps
+    # one row per GEMV phase of the call's first frame, in order
+    m = synth.TINY
+    w = synth.make_weights(m)
+    wl = synth.WORKLOADS["tiny_f32_b1"]
+    codes, text = synth.make_prompt(wl, 0)
+    ov = synth.make_overlays(wl, 4)
+    out, tr = {}, None
+    for trace in (False, True):
+        say(f"[tiny traced] trace {trace}")
+        d = qt.Decoder(m, w, 1, flags=qt.QT_F_DUMP | (qt.QT_F_TRACE if trace else 0))
+        assert d.path == qt.QT_PATH_FRAME
+        d.prefill(0, codes, text)
+        out[trace] = (d.decode(4, ov), d.dump(qt.QT_DUMP_TALKER_LOGITS), d.dump(qt.QT_DUMP_PRED_LOGITS),
+                      d.dump(qt.QT_DUMP_BRIDGE))
+        if trace:
+            tr = d.dump(qt.QT_DUMP_TRACE).astype(np.int64)
+        d.close()
+    assert np.array_equal(out[False][0], out[True][0])
+    for a, b in zip(out[False][1:], out[True][1:]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    n = next(i for i in range(768) if tr[i, 0] == 255)
+    assert n == (m.G - 1) * (4 * m.Lp + 1) + 4 * m.Lt + 1  # predictor steps, then the talker step
+    assert np.all(np.diff(tr[:n, 1]) > 0)  # phase starts in order
+    assert np.all(tr[:n, 2] >= tr[:n, 1]) and np.all(tr[:n, 3] >= tr[:n, 2])
+
+
 def test_tiny_graph_equals_eager_bitwise(tiny):
     m, w, wl, r = tiny
     c, t = r["prompts"][0]
