@@ -45,7 +45,6 @@ namespace {
 constexpr int NW = 5;            // compute waves of a GEMV workgroup
 constexpr int NT = 64 * NW;      // their threads
 constexpr int NLW = 3;           // loader waves (each keeps its own loads in flight)
-constexpr int MAXWB = 16;        // q4: 1 KB raw blocks per loader wave and slice
 constexpr int TKU = 7;           // top-k: logits per compute thread (Vc <= 2048 = 7 * 320 - 192)
 constexpr int NTB = NT + 64 * NLW;  // two waves per SIMD
 constexpr int ANT = 512;         // threads of an attention workgroup
@@ -214,7 +213,6 @@ struct Common {
   int abort;
   uint32_t cbar;   // compute-wave barrier arrivals
   uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
-  uint32_t lbar;   // loader-wave barrier arrivals (q4 widening)
   uint32_t hist[256];       // top-k: radix-select histogram
   uint32_t tsel[2];         // top-k: the threshold key and the last member's index
   uint64_t ltime;  // tracing: when a loader wave's part of the last slice had landed
@@ -401,24 +399,32 @@ __device__ __forceinline__ Share share_calc(const FrameArgs &a, int type, int gi
   return s;
 }
 
-// Bytes per weight in a weight slot in LDS: f32, bf16 and q8 rows stay as
-// they are in HBM (q8 codes are widened to bf16 pairs in registers, by the
-// GEMV); q4 rows are widened to bf16 by the loader waves once they land
-// (exact: |c - 8| <= 8).  The block scales stay beside the weights and are
-// applied to each chunk's dot product.
-template <int WT> struct WEsz { static constexpr int v = WT == W_F32 ? 4 : WT == W_Q8 ? 1 : 2; };
-// q4 slices are widened in LDS
-__host__ __device__ constexpr bool w_widened(int wt) { return wt == W_Q4; }
+// Weight rows in a weight slot in LDS keep their HBM format (f32, bf16, int8
+// codes or 4-bit codes, q4 rows padded to whole KB); the q8 and q4 block
+// scales stay beside the weights and multiply each chunk's dot product.  A
+// compute chunk is one lane's load: 16 bytes (4 f32, 8 bf16 or 16 int8
+// weights) or, for q4, 8 bytes (16 weights), so a block of 64 lanes spans
+// 256, 512 or 1,024 weights.  The GEMV widens q8 and q4 chunks to bf16 pairs
+// in registers (exact: |q| <= 128, |c - 8| <= 8).
+__host__ __device__ constexpr bool chunk16(int wt) { return wt == W_Q8 || wt == W_Q4; }  // 16 weights per chunk
 // Bytes of a weight row of width K as stored in HBM.
 __host__ __device__ constexpr int raw_rowb(int wt, int K) {
   return wt == W_F32 ? 4 * K : wt == W_BF16 ? 2 * K : wt == W_Q8 ? K : K / 2;
 }
-// 1 KB blocks a weight row of width H may span in LDS: its normalized operand
-// lives in registers (a q8 chunk takes twice the operand words of a bf16 one)
-__host__ __device__ constexpr int nb_hidden(int wt) { return wt == W_Q8 ? 1 : 2; }
-// 1 KB blocks of the O and down rows (widths nq*hd and F), whose operand
+// ... and in a weight slot
+__host__ __device__ constexpr int slot_rowb(int wt, int K) { return wt == W_Q4 ? (K / 2 + 1023) & ~1023 : raw_rowb(wt, K); }
+// weights of one compute block, and a row's compute blocks
+__host__ __device__ constexpr int block_weights(int wt) { return wt == W_F32 ? 256 : wt == W_BF16 ? 512 : 1024; }
+__host__ __device__ constexpr int row_blocks(int wt, int K) { return K / block_weights(wt); }
+// compute blocks a row of width H may span: its normalized operand lives in
+// registers (a 16-weight chunk takes twice the operand words of a bf16 one)
+__host__ __device__ constexpr int nb_hidden(int wt) { return chunk16(wt) ? 1 : 2; }
+// compute blocks of the O and down rows (widths nq*hd and F), whose operand
 // chunks are also held in registers per item
-__host__ __device__ constexpr int nb_wide(int wt) { return wt == W_Q8 ? 4 : 6; }
+__host__ __device__ constexpr int nb_wide(int wt) { return chunk16(wt) ? 4 : 6; }
+// one lane's weight chunk
+template <int WT> struct WChunk { typedef uint4 T; };
+template <> struct WChunk<W_Q4> { typedef uint2 T; };
 
 // weight row (bytes rb in HBM) and block-scale row of output row n, matrix mat
 __device__ __forceinline__ void wrow_of(const FrameArgs &a, const Common &cm, const Ph &p, int n, int mat,
@@ -451,19 +457,13 @@ __device__ __forceinline__ const void *gain_of(const FrameArgs &a, const Common 
   if (p.type == PH_HEAD) return p.stack ? a.t_norm : a.p_norm;
   return nullptr;
 }
-// slot layout: weights [R*NM rows] (in their LDS format), block scales
-// [R*NM][K/32] (q8 / q4, 1 KB aligned), gain [H].  A q4 slice lands in the
-// tail of the weight area (raw_off) and is widened in place.
-__device__ __forceinline__ uint32_t scales_off(const Share &s, int esz) { return (uint32_t)(s.R * s.NM) * s.K * esz; }
-__device__ __forceinline__ uint32_t gain_off(const Share &s, int esz, bool blocked) {
-  return scales_off(s, esz) + (blocked ? up1k((uint32_t)(s.R * s.NM) * (s.K / 16)) : 0u);
-}
-// q4 rows land 1 KB-padded (raw row stride bpr KB), at the end of the weight
-// area; the frame kernel's K (a multiple of 512) keeps that inside it
+// slot layout: weights [R*NM rows] (slot_rowb bytes each), block scales
+// [R*NM][K/32] (q8 / q4, 1 KB aligned), gain [H].
 template <int WT>
-__device__ __forceinline__ uint32_t raw_off(const Share &s) {
-  if constexpr (!w_widened(WT)) return 0u;
-  return (uint32_t)(s.R * s.NM) * (s.K * WEsz<WT>::v - ((raw_rowb(WT, s.K) + 1023) & ~1023));
+__device__ __forceinline__ uint32_t scales_off(const Share &s) { return (uint32_t)(s.R * s.NM) * slot_rowb(WT, s.K); }
+template <int WT>
+__device__ __forceinline__ uint32_t gain_off(const Share &s) {
+  return scales_off<WT>(s) + (w_blocked(WT) ? up1k((uint32_t)(s.R * s.NM) * (s.K / 16)) : 0u);
 }
 
 // Issue this loader wave's part of the direct-to-LDS loads of phase p's
@@ -473,29 +473,27 @@ __device__ __forceinline__ uint32_t raw_off(const Share &s) {
 // loads in flight, so several loader waves land a slice sooner.
 template <int WT>
 __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, const Ph &p, uint32_t slot) {
-  constexpr int ESZ = WEsz<WT>::v;
   const int lane = threadIdx.x & 63;
   const int li = (int)(threadIdx.x >> 6) - NW;
   const Share s = cm.sh[p.type];
-  // rows of rb bytes in 1 KB blocks, block b at raw_off + b KB; in a row's
-  // last block lanes past its end load its last chunk again (so that every
-  // lane of every load is on: a lane mask here slows the whole slice's issue)
+  // rows of rb bytes in 1 KB blocks, block b at b KB; in a q4 row's last
+  // block lanes past its end load its last chunk again (so that every lane
+  // of every load is on: a lane mask here slows the whole slice's issue)
   const int rb = raw_rowb(WT, s.K), bpr = (rb + 1023) >> 10, U = s.R * s.NM;
-  const uint32_t ro = slot + raw_off<WT>(s);
   const int nb = U * bpr, b1 = (li + 1) * nb / NLW;
   for (int b = li * nb / NLW; b < b1;) {
     const int u = b / bpr;
     const uint8_t *w, *sc;
     wrow_of(a, cm, p, s.r0 + u / s.NM, u % s.NM, s.K, rb, w, sc);
     for (int cb = b - u * bpr; cb < bpr && b < b1; ++cb, ++b) {
-      if constexpr (w_widened(WT)) dma16(w + min(cb * 1024 + lane * 16, rb - 16), ro + (uint32_t)b * 1024u);
-      else dma16(w + cb * 1024 + lane * 16, ro + (uint32_t)b * 1024u);
+      if constexpr (WT == W_Q4) dma16(w + min(cb * 1024 + lane * 16, rb - 16), slot + (uint32_t)b * 1024u);
+      else dma16(w + cb * 1024 + lane * 16, slot + (uint32_t)b * 1024u);
     }
   }
   if (li != NLW - 1) return;
   if constexpr (w_blocked(WT)) {
     const int spu = s.K / 256, n = U * spu;  // 16-byte scale chunks per row, in all
-    const uint32_t so = scales_off(s, ESZ);
+    const uint32_t so = scales_off<WT>(s);
     for (int sb = 0; sb * 64 < n; ++sb) {
       const int idx = min(sb * 64 + lane, n - 1);
       const int u = idx / spu, k = idx - u * spu;
@@ -507,7 +505,7 @@ __device__ __forceinline__ void dma_slice(const FrameArgs &a, const Common &cm, 
   const void *g = gain_of(a, cm, p);
   if (g) {
     const int n = a.H * (a.tab_bf16 ? 2 : 4) / 16;
-    const uint32_t go = gain_off(s, ESZ, w_blocked(WT));
+    const uint32_t go = gain_off<WT>(s);
     for (int gb = 0; gb * 64 < n; ++gb)
       dma16((const uint8_t *)g + min(gb * 64 + lane, n - 1) * 16, slot + go + (uint32_t)gb * 1024u);
   }
@@ -521,10 +519,14 @@ __device__ __forceinline__ uint32_t i8pair(uint32_t w, int b) {
   const float lo = (float)(int8_t)(w >> (8 * b)), hi = (float)(int8_t)(w >> (8 * b + 8));
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
+// 4-bit codes b, b+1 of w (low nibble first) as the bf16 pair c - 8 (exact)
+__device__ __forceinline__ uint32_t q4pair(uint32_t w, int b) {
+  const float lo = (float)((int)((w >> (4 * b)) & 15u) - 8), hi = (float)((int)((w >> (4 * b + 4)) & 15u) - 8);
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
 
-// The operand elements that meet one 16-byte weight chunk in LDS: 8 bf16
-// pairs for q8 (a, b), 4 pairs for bf16 and widened q4 (a), 4 floats for
-// f32 (a).
+// The operand elements that meet one weight chunk in LDS: 8 bf16 pairs for
+// q8 and q4 (a, b), 4 pairs for bf16 (a), 4 floats for f32 (a).
 struct OpC {
   uint4 a, b;
 };
@@ -532,7 +534,7 @@ struct OpC {
 template <int WT>
 __device__ __forceinline__ OpC op_lds(const uint32_t *op, int c) {
   OpC x;
-  if constexpr (WT == W_Q8) {
+  if constexpr (chunk16(WT)) {
     x.a = ((const uint4 *)op)[2 * c];
     x.b = ((const uint4 *)op)[2 * c + 1];
   } else {
@@ -542,11 +544,11 @@ __device__ __forceinline__ OpC op_lds(const uint32_t *op, int c) {
   return x;
 }
 
-// 16-byte weight chunk c of a row (in LDS) . its operand elements: a q8
-// chunk is 16 codes of half a block, a (widened) q4 chunk 8 bf16 weights of
-// a quarter block; the block scale multiplies the chunk's dot product
+// weight chunk c of a row (in LDS) . its operand elements: a q8 or q4 chunk
+// is 16 codes, half a 32-weight scale block, whose scale multiplies the
+// chunk's dot product
 template <int WT>
-__device__ __forceinline__ float chunk_dot(uint4 w, const OpC &x, int c, const uint8_t *scl) {
+__device__ __forceinline__ float chunk_dot(typename WChunk<WT>::T w, const OpC &x, int c, const uint8_t *scl) {
   if constexpr (WT == W_F32) {
     return __uint_as_float(w.x) * __uint_as_float(x.a.x) + __uint_as_float(w.y) * __uint_as_float(x.a.y) +
            __uint_as_float(w.z) * __uint_as_float(x.a.z) + __uint_as_float(w.w) * __uint_as_float(x.a.w);
@@ -560,72 +562,18 @@ __device__ __forceinline__ float chunk_dot(uint4 w, const OpC &x, int c, const u
     s = dot2(i8pair(w.w, 0), x.b.z, s);
     s = dot2(i8pair(w.w, 2), x.b.w, s);
     return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
+  } else if constexpr (WT == W_Q4) {
+    float s = dot2(q4pair(w.x, 0), x.a.x, 0.f);
+    s = dot2(q4pair(w.x, 2), x.a.y, s);
+    s = dot2(q4pair(w.x, 4), x.a.z, s);
+    s = dot2(q4pair(w.x, 6), x.a.w, s);
+    s = dot2(q4pair(w.y, 0), x.b.x, s);
+    s = dot2(q4pair(w.y, 2), x.b.y, s);
+    s = dot2(q4pair(w.y, 4), x.b.z, s);
+    s = dot2(q4pair(w.y, 6), x.b.w, s);
+    return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
   } else {
-    const float d = dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
-    if constexpr (w_blocked(WT)) return d * f16_to_f32(((const uint16_t *)scl)[c >> 2]);
-    return d;
-  }
-}
-
-// Barrier of the loader waves alone (an LDS counter; gen counts arrivals)
-__device__ __forceinline__ bool loader_barrier(const FrameArgs &a, Common &cm, uint32_t &gen) {
-  gen += NLW;
-  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(&cm.lbar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (uint32_t spins = 0; __hip_atomic_load(&cm.lbar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < gen; ++spins) {
-    if (spins > SPIN_LIMIT) { err_set(a.err); return false; }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  return true;
-}
-
-// Widen a landed q4 slice to bf16 rows in place (loader waves, each after
-// waiting for its own loads).  Each loader lane reads back the raw
-// 16-byte chunks that its own direct-to-LDS loads wrote (dma_slice's block
-// split), all of them before the one loader barrier, then writes each one's
-// weights as bf16: the chunk at byte o of raw row u becomes bf16 chunks
-// 4 (u rb + o) / 16 .. + 3 (rb raw row bytes).  The raw rows lie in the tail of the weight area, so these writes
-// overwrite raw bytes, but only after every lane has read its own.
-template <int WT>
-__device__ __forceinline__ bool widen_slice(const FrameArgs &a, Common &cm, const Ph &p, uint8_t *slot,
-                                            uint32_t &gen) {
-  if constexpr (!w_widened(WT)) {
-    return true;
-  } else {
-    constexpr int RHO = 4;  // bf16 chunks per raw chunk
-    const int lane = threadIdx.x & 63;
-    const int li = (int)(threadIdx.x >> 6) - NW;
-    const Share s = cm.sh[p.type];
-    const int rb = raw_rowb(WT, s.K), bpr = (rb + 1023) >> 10, nb = s.R * s.NM * bpr;
-    const int b0 = li * nb / NLW, n = (li + 1) * nb / NLW - b0;  // n <= MAXWB (frame_plan)
-    const uint8_t *raw = slot + raw_off<WT>(s);
-    uint4 v[MAXWB];
-    int off[MAXWB];  // unpadded raw offset u rb + o of this lane's chunk of each block (-1: none)
-#pragma unroll
-    for (int i = 0; i < MAXWB; ++i) {
-      const int bb = b0 + min(i, n - 1), u = bb / bpr, cb = bb - u * bpr;
-      const int o = cb * 1024 + lane * 16;
-      off[i] = i < n && o < rb ? u * rb + o : -1;
-      v[i] = *(const uint4 *)(raw + (bb < 0 ? 0 : bb * 1024 + lane * 16));
-    }
-    if (!loader_barrier(a, cm, gen)) return false;  // every lane's raw chunks are in registers
-#pragma unroll
-    for (int i = 0; i < MAXWB; ++i) {
-      if (off[i] < 0) continue;
-      const uint32_t r[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      uint4 *dst = (uint4 *)(slot + RHO * off[i]);
-#pragma unroll
-      for (int h = 0; h < RHO; ++h) {
-        uint32_t o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // byte k of word h: codes of weights 8 h + 2 k (low nibble) and 8 h + 2 k + 1, as c - 8
-          const uint32_t byte = (r[h] >> (8 * k)) & 0xffu;
-          o[k] = pack2((float)((int)(byte & 15u) - 8), (float)((int)(byte >> 4) - 8));
-        }
-        dst[h] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    }
-    return true;
+    return dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
   }
 }
 
@@ -681,7 +629,7 @@ __device__ __forceinline__ uint4 norm8(const FrameArgs &a, const float *x, const
 template <int WT>
 __device__ __forceinline__ OpC norm_chunk(const FrameArgs &a, const float *x, const uint8_t *g, float r, int c) {
   OpC o;
-  if constexpr (WT == W_Q8) {
+  if constexpr (chunk16(WT)) {
     o.a = norm8<true>(a, x, g, r, 16 * c);
     o.b = norm8<true>(a, x, g, r, 16 * c + 8);
   } else if constexpr (WT != W_F32) {
@@ -863,21 +811,21 @@ template <int WT, int UPI, int MAXB, int MC, class Op, class Out, class Pre = No
 __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Share &s, int Mrt, Out out,
                                            Pre pre = Pre(), int wv = -1, int nwv = NW) {
   const int M = MC ? MC : Mrt;
-  constexpr int ESZ = WEsz<WT>::v;
+  typedef typename WChunk<WT>::T WCh;
   const int lane = threadIdx.x & 63;
-  const int rowb = s.K * ESZ, bpr = rowb >> 10;
+  const int rowb = slot_rowb(WT, s.K), bpr = row_blocks(WT, s.K);
   const int nitems = s.R * s.NM / UPI;
-  const uint8_t *scb = slot + scales_off(s, ESZ);
+  const uint8_t *scb = slot + scales_off<WT>(s);
   for (int it = wv < 0 ? (int)(threadIdx.x >> 6) : wv; it < nitems; it += nwv) {
     // Every block's loads are unconditional, from block min(cb, bpr - 1)
     // past the row's end (read, never used): a load under a branch makes the
     // compiler wait for all outstanding LDS operations where the branch joins.
-    uint4 w[UPI][MAXB];
+    WCh w[UPI][MAXB];
 #pragma unroll
     for (int q = 0; q < UPI; ++q)
 #pragma unroll
       for (int cb = 0; cb < MAXB; ++cb)
-        w[q][cb] = ((const uint4 *)(slot + (size_t)(it * UPI + q) * rowb))[min(cb, bpr - 1) * 64 + lane];
+        w[q][cb] = ((const WCh *)(slot + (size_t)(it * UPI + q) * rowb))[min(cb, bpr - 1) * 64 + lane];
     const float pv = pre(it);
     // the operand chunks too, before any dot product (from LDS they would
     // otherwise wait one LDS round trip per block)
@@ -928,12 +876,11 @@ template <int WT, int MC>
 __device__ __forceinline__ void normed_items_m(const FrameArgs &a, const Common &cm, int type, const float *xres,
                                                const uint8_t *sp, uint32_t tag, int wv, int nwv) {
   constexpr int M = MC;  // operand rows, at compile time
-  constexpr int ESZ = WEsz<WT>::v;
   constexpr int NBH = nb_hidden(WT);
   const int lane = threadIdx.x & 63;
   const Share s = cm.sh[type];
-  const uint8_t *gain = sp + gain_off(s, ESZ, w_blocked(WT));
-  const int bpr = a.H * ESZ >> 10;
+  const uint8_t *gain = sp + gain_off<WT>(s);
+  const int bpr = row_blocks(WT, a.H);
   const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
   OpC xo[2][NBH];
 #pragma unroll
@@ -978,16 +925,14 @@ __device__ __forceinline__ void normed_items(const FrameArgs &a, const Common &c
 }
 
 // The loader waves: stream each GEMV phase's weight slice (a part each) into
-// its LDS slot one phase ahead, widen q4 slices to bf16 once they land,
-// and meet the compute waves once per phase, right after their inputs are in.
+// its LDS slot one phase ahead and meet the compute waves once per phase,
+// right after their inputs are in.
 template <int WT, bool TRC>
 __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, const Lds &L, unsigned char *smem) {
   uint8_t *const p0 = smem + L.slot0, *const p1 = smem + L.slot1;
   Ph cur{PH_QKV, 0, 0, 0, 0};
-  uint32_t lgen = 0;  // loader-barrier arrivals counted so far
   dma_slice<WT>(a, cm, cur, lds_addr(p0));
   wait_vm();
-  if (!widen_slice<WT>(a, cm, cur, p0, lgen)) return;
   if (TRC && a.trace) cm.ltime = wall_clock64();
   int slot = 0;
   uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
@@ -1028,12 +973,9 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
       const Ph n2 = next_gemv_phase(a, ng, a.pos0);
       if (!wait_gemv()) break;
       dma_slice<WT>(a, cm, n2, lds_addr(cslot));
-      have_next = true;  // not loaded again at the O phase's meeting; widened there (q4)
+      have_next = true;  // not loaded again at the O phase's meeting
     }
     wait_vm();
-    // ng's slice (loaded now, or during the last phase) to bf16; a gate/up
-    // slice loaded ahead waits for the next iteration
-    if (ng.type != PH_END && !widen_slice<WT>(a, cm, ng, nslot, lgen)) break;
     if (TRC && a.trace) cm.ltime = wall_clock64();
     if (a.two_slots) slot ^= 1;
     for (Ph q = next_phase(a, cur, a.pos0); ; q = next_phase(a, q, a.pos0)) {  // the phase index of ng
@@ -1050,7 +992,6 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
 // stamps its phases (QT_F_TRACE); the other kernels carry no stamp code.
 template <int WT, bool SMP, bool TRC>
 __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *smem) {
-  constexpr int ESZ = WEsz<WT>::v;
   Common &cm = *reinterpret_cast<Common *>(smem);
   const Lds L = lds_layout(a);
   if (threadIdx.x >= NT) {
@@ -1244,8 +1185,8 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
     constexpr int NBH = nb_hidden(WT);
     OpC xo[2][NBH];  // [row][block]
     if (normed && !(cur.type == PH_GU || (cur.type == PH_QKV && a.two_slots))) {  // (else inside normed_items)
-      const uint8_t *gain = sp + gain_off(s, ESZ, w_blocked(WT));
-      const int bpr = H * ESZ >> 10;
+      const uint8_t *gain = sp + gain_off<WT>(s);
+      const int bpr = row_blocks(WT, H);
       const float r0 = rms_inv(a, cm.pss[0]), r1 = M > 1 ? rms_inv(a, cm.pss[1]) : 0.f;
 #pragma unroll
       for (int cb = 0; cb < NBH; ++cb) {  // unconditional loads (see gemv_items)
@@ -1727,7 +1668,6 @@ __global__ __launch_bounds__(NTB) void frame_kernel(FrameArgs a) {
     cm.abort = 0;
     cm.cbar = 0;
     cm.gdone = 0;
-    cm.lbar = 0;
   }
   for (int l = tid; l < a.Lt + a.Lp; l += NT) {
     const LayerDev *src = l < a.Lt ? a.tl + l : a.pl + (l - a.Lt);
@@ -1788,7 +1728,6 @@ bool frame_variant_supported(int wt, int hd, int g, int kvb) {
 }
 
 bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
-  const int esz = a.wt == W_F32 ? 4 : a.wt == W_Q8 ? 1 : 2;  // bytes per weight in LDS (q4 rows widened to bf16)
   const bool blocked = a.wt == W_Q8 || a.wt == W_Q4;
   const int qd = a.nq * a.hd;
   a.tile = TILE;
@@ -1802,9 +1741,12 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   if (a.Lt + a.Lp > MAXLAYERS || a.G > MAXHEADS) { *why = "too many layers or codebooks"; return false; }
   if (a.nwg > 1024) { *why = "more than 1024 workgroups"; return false; }
   if (a.rep < 1 || a.rep > 32) { *why = "exchange copies outside 1..32"; return false; }
-  // GEMV rows held in registers per item: hidden-wide rows (gate/up pairs, heads)
-  // up to 2 KB (q8: 1 KB), the O and down rows up to 6 KB (q8: 4 KB)
-  if (a.H * esz > 1024 * nb_hidden(a.wt) || qd * esz > 1024 * nb_wide(a.wt) || a.F * esz > 1024 * nb_wide(a.wt)) {
+  // GEMV rows held in registers per item: hidden-wide rows (gate/up pairs,
+  // heads) up to 2 compute blocks (q8, q4: 1), the O and down rows up to 6
+  // (q8, q4: 4)
+  if (a.H % block_weights(a.wt) || qd % block_weights(a.wt) || a.F % block_weights(a.wt) ||
+      row_blocks(a.wt, a.H) > nb_hidden(a.wt) || row_blocks(a.wt, qd) > nb_wide(a.wt) ||
+      row_blocks(a.wt, a.F) > nb_wide(a.wt)) {
     *why = "GEMV rows too wide";
     return false;
   }
@@ -1815,18 +1757,13 @@ bool frame_plan(FrameArgs &a, int max_pos, int lds_limit, const char **why) {
   int slot = 0;
   for (int i = 0; i < 5; ++i) {
     const int N = NK[i][0], K = NK[i][1], nm = NK[i][2];
-    if ((K * esz) % 1024 || N % 2 || (blocked && K % 256)) { *why = "GEMV width not a multiple of 1 KB"; return false; }
+    if (K % block_weights(a.wt) || N % 2) { *why = "GEMV width not a whole number of compute blocks"; return false; }
     if (K > 3072) { *why = "GEMV width above 3072"; return false; }
     const int g = nm;  // gate/up (nm = 2) rows go in pairs
     const int R = g * ((N / g + NG - 1) / NG);
     if (R * nm > MAXR) { *why = "too many rows per workgroup"; return false; }
-    int b = R * nm * K * esz;
+    int b = R * nm * slot_rowb(a.wt, K);
     if (blocked) b += (int)up1k((uint32_t)(R * nm * (K / 16)));
-    if (w_widened(a.wt)) {
-      const int bpr = (raw_rowb(a.wt, K) + 1023) / 1024;  // raw blocks per row, widened from registers
-      if ((R * nm * bpr + NLW - 1) / NLW > MAXWB) { *why = "too many q4 blocks per loader wave"; return false; }
-      if (bpr * 1024 > 2 * K) { *why = "q4 rows narrower than 512"; return false; }  // (raw_off)
-    }
     if (i == 0 || i == 2 || i == 4) b += (int)up1k((uint32_t)(a.H * (a.tab_bf16 ? 2 : 4)));
     slot = imax(slot, (int)up1k((uint32_t)b));
   }
