@@ -519,10 +519,19 @@ __device__ __forceinline__ uint32_t i8pair(uint32_t w, int b) {
   const float lo = (float)(int8_t)(w >> (8 * b)), hi = (float)(int8_t)(w >> (8 * b + 8));
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
-// 4-bit codes b, b+1 of w (low nibble first) as the bf16 pair c - 8 (exact)
-__device__ __forceinline__ uint32_t q4pair(uint32_t w, int b) {
-  const float lo = (float)((int)((w >> (4 * b)) & 15u) - 8), hi = (float)((int)((w >> (4 * b + 4)) & 15u) - 8);
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+// The 8 4-bit codes of w (low nibble first) as 4 bf16 pairs c - 8 (exact):
+// each code c becomes the f32 2^23 + c by a byte permute (bits 0x4b0000cc),
+// 2^23 + 8 is subtracted (exact), and a pair keeps the two results' high
+// halves (small integers have no low mantissa bits).
+__device__ __forceinline__ void q4pairs8(uint32_t w, uint32_t *p) {
+  const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;  // codes 0, 2, 4, 6 and 1, 3, 5, 7 as bytes
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t sel = 0x070c0c00u | (uint32_t)k;  // byte k of the second source, 0, 0, 0x4b
+    const float lo = __uint_as_float(__builtin_amdgcn_perm(0x4b000000u, ev, sel)) - 8388616.0f;
+    const float hi = __uint_as_float(__builtin_amdgcn_perm(0x4b000000u, od, sel)) - 8388616.0f;
+    p[k] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
 }
 
 // The operand elements that meet one weight chunk in LDS: 8 bf16 pairs for
@@ -563,14 +572,17 @@ __device__ __forceinline__ float chunk_dot(typename WChunk<WT>::T w, const OpC &
     s = dot2(i8pair(w.w, 2), x.b.w, s);
     return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
   } else if constexpr (WT == W_Q4) {
-    float s = dot2(q4pair(w.x, 0), x.a.x, 0.f);
-    s = dot2(q4pair(w.x, 2), x.a.y, s);
-    s = dot2(q4pair(w.x, 4), x.a.z, s);
-    s = dot2(q4pair(w.x, 6), x.a.w, s);
-    s = dot2(q4pair(w.y, 0), x.b.x, s);
-    s = dot2(q4pair(w.y, 2), x.b.y, s);
-    s = dot2(q4pair(w.y, 4), x.b.z, s);
-    s = dot2(q4pair(w.y, 6), x.b.w, s);
+    uint32_t p[8];
+    q4pairs8(w.x, p);
+    q4pairs8(w.y, p + 4);
+    float s = dot2(p[0], x.a.x, 0.f);
+    s = dot2(p[1], x.a.y, s);
+    s = dot2(p[2], x.a.z, s);
+    s = dot2(p[3], x.a.w, s);
+    s = dot2(p[4], x.b.x, s);
+    s = dot2(p[5], x.b.y, s);
+    s = dot2(p[6], x.b.z, s);
+    s = dot2(p[7], x.b.w, s);
     return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
   } else {
     return dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
