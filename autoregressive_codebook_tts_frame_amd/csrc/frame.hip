@@ -553,11 +553,11 @@ __device__ __forceinline__ OpC op_lds(const uint32_t *op, int c) {
   return x;
 }
 
-// weight chunk c of a row (in LDS) . its operand elements: a q8 or q4 chunk
+// a weight chunk of a row (in LDS) . its operand elements: a q8 or q4 chunk
 // is 16 codes, half a 32-weight scale block, whose scale multiplies the
 // chunk's dot product
 template <int WT>
-__device__ __forceinline__ float chunk_dot(typename WChunk<WT>::T w, const OpC &x, int c, const uint8_t *scl) {
+__device__ __forceinline__ float chunk_dot(typename WChunk<WT>::T w, const OpC &x, float scale) {
   if constexpr (WT == W_F32) {
     return __uint_as_float(w.x) * __uint_as_float(x.a.x) + __uint_as_float(w.y) * __uint_as_float(x.a.y) +
            __uint_as_float(w.z) * __uint_as_float(x.a.z) + __uint_as_float(w.w) * __uint_as_float(x.a.w);
@@ -570,7 +570,7 @@ __device__ __forceinline__ float chunk_dot(typename WChunk<WT>::T w, const OpC &
     s = dot2(i8pair(w.z, 2), x.b.y, s);
     s = dot2(i8pair(w.w, 0), x.b.z, s);
     s = dot2(i8pair(w.w, 2), x.b.w, s);
-    return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
+    return s * scale;
   } else if constexpr (WT == W_Q4) {
     uint32_t p[8];
     q4pairs8(w.x, p);
@@ -583,7 +583,7 @@ __device__ __forceinline__ float chunk_dot(typename WChunk<WT>::T w, const OpC &
     s = dot2(p[5], x.b.y, s);
     s = dot2(p[6], x.b.z, s);
     s = dot2(p[7], x.b.w, s);
-    return s * f16_to_f32(((const uint16_t *)scl)[c >> 1]);
+    return s * scale;
   } else {
     return dot2(w.w, x.a.w, dot2(w.z, x.a.z, dot2(w.y, x.a.y, dot2(w.x, x.a.x, 0.f))));
   }
@@ -838,6 +838,20 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
 #pragma unroll
       for (int cb = 0; cb < MAXB; ++cb)
         w[q][cb] = ((const WCh *)(slot + (size_t)(it * UPI + q) * rowb))[min(cb, bpr - 1) * 64 + lane];
+    // q8 / q4: each chunk's block scale (chunk c of 16 codes: scale c / 2),
+    // requested with the weights
+    float scv[UPI][MAXB];
+#pragma unroll
+    for (int q = 0; q < UPI; ++q)
+#pragma unroll
+      for (int cb = 0; cb < MAXB; ++cb) {
+        if constexpr (w_blocked(WT)) {
+          const uint16_t *scl = (const uint16_t *)(scb + (size_t)(it * UPI + q) * (s.K / 16));
+          scv[q][cb] = f16_to_f32(scl[(min(cb, bpr - 1) * 64 + lane) >> 1]);
+        } else {
+          scv[q][cb] = 1.f;
+        }
+      }
     const float pv = pre(it);
     // the operand chunks too, before any dot product (from LDS they would
     // otherwise wait one LDS round trip per block)
@@ -858,14 +872,12 @@ __device__ __forceinline__ void gemv_items(const uint8_t *slot, Op op, const Sha
       // compiler sinks each block's loads behind it, one LDS round trip per
       // block instead of one per item.
       const bool on = cb < bpr;
-      const int c = min(cb, bpr - 1) * 64 + lane;
 #pragma unroll
       for (int q = 0; q < UPI; ++q) {
-        const uint8_t *scl = scb + (size_t)(it * UPI + q) * (s.K / 16);
-        const float d0 = chunk_dot<WT>(w[q][cb], x[0][cb], c, scl);
+        const float d0 = chunk_dot<WT>(w[q][cb], x[0][cb], scv[q][cb]);
         acc[q][0] += on ? d0 : 0.f;
         if (M > 1) {
-          const float d1 = chunk_dot<WT>(w[q][cb], x[1][cb], c, scl);
+          const float d1 = chunk_dot<WT>(w[q][cb], x[1][cb], scv[q][cb]);
           acc[q][1] += on ? d1 : 0.f;
         }
       }
