@@ -212,7 +212,7 @@ struct Common {
   int code;
   int abort;
   uint32_t cbar;   // compute-wave barrier arrivals
-  uint32_t gdone;  // compute-wave GEMV completions (one weight slot)
+  uint32_t gdone;  // GEMV completions (compute waves; loader waves where they take items)
   uint32_t hist[256];       // top-k: radix-select histogram
   uint32_t tsel[2];         // top-k: the threshold key and the last member's index
   uint64_t ltime;  // tracing: when a loader wave's part of the last slice had landed
@@ -959,10 +959,10 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
   wait_vm();
   if (TRC && a.trace) cm.ltime = wall_clock64();
   int slot = 0;
-  uint32_t done = 0;          // GEMV completions counted so far (NW per phase)
+  uint32_t done = 0;          // GEMV completions expected so far
   uint32_t seq = 1;           // phase index of cur + 1 (its tag is tag_base + seq)
   bool have_next = false;     // the next phase's slice was issued during the last phase
-  // until every compute wave has finished the current phase's GEMV
+  // until every wave has finished the current phase's GEMV items
   auto wait_gemv = [&]() -> bool {
     for (uint32_t spins = 0; __hip_atomic_load(&cm.gdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < done;
          ++spins) {
@@ -975,14 +975,17 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     const Ph ng = next_gemv_phase(a, cur, a.pos0);
     __syncthreads();  // the compute waves have this phase's inputs (and are done with the last phase's slot)
     if (cm.abort) break;
-    done += NW;
     uint8_t *const cslot = slot ? p1 : p0, *const nslot = a.two_slots && !slot ? p1 : p0;
-    if (a.two_slots && (cur.type == PH_GU || cur.type == PH_QKV)) {
+    const bool items = a.two_slots && (cur.type == PH_GU || cur.type == PH_QKV);
+    done += items ? NW + NLW : NW;  // this phase's GEMV completions (the loader waves' items too)
+    if (items) {
       // its items first (the next phase waits for every one of them), then
-      // the next slice
+      // the next slice; the count tells every loader wave when this slot's
+      // rows are no longer read
       const int M = cur.stack == 0 && cur.step == 0 ? 2 : 1;
       normed_items<WT>(a, cm, cur.type, (const float *)(smem + L.xres), cslot, M, a.tag_base + seq,
                        (int)(threadIdx.x >> 6), NW + NLW);
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(&cm.gdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     if (ng.type != PH_END && !have_next) {
       if (!a.two_slots && !wait_gemv()) break;  // one slot: it is free once this phase's GEMV is done
@@ -992,8 +995,9 @@ __device__ __forceinline__ void loader_role(const FrameArgs &a, Common &cm, cons
     if (a.two_slots && cur.type == PH_QKV && ng.type == PH_O) {
       // The attention window: the compute waves only poll until attention is
       // done, so the gate/up slice (the largest) streams into this phase's
-      // slot as soon as its GEMV is done, instead of competing later with the
-      // exchange before the gate/up phase.
+      // slot as soon as every GEMV of this phase is done (the loader waves'
+      // items included), instead of competing later with the exchange before
+      // the gate/up phase.
       const Ph n2 = next_gemv_phase(a, ng, a.pos0);
       if (!wait_gemv()) break;
       dma_slice<WT>(a, cm, n2, lds_addr(cslot));
