@@ -1023,6 +1023,10 @@ __device__ __forceinline__ void gemv_role(const FrameArgs &a, unsigned char *sme
   Common &cm = *reinterpret_cast<Common *>(smem);
   const Lds L = lds_layout(a);
   if (threadIdx.x >= NT) {
+    // The loader waves issue ahead of the compute wave that shares their
+    // SIMD: a weight slice's loads then leave as soon as they are issuable
+    // instead of waiting behind the compute waves' polls and dot products.
+    __builtin_amdgcn_s_setprio(1);
     loader_role<WT, TRC>(a, cm, L, smem);
     return;
   }
